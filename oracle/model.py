@@ -1,0 +1,165 @@
+"""fp64 oracle for the synthetic decoder blocks, run chunk by chunk.
+
+TEST INFRASTRUCTURE ONLY (see oracle.py): imported by tests, the smoke check and
+the CPU-baseline leg of the benchmark, never by the GPU library.
+
+The pages name the decoder's pieces (a causal per-layer state, nearest 2x
+spatial upsampling before a spatial conv, growth of the frame count) but print
+no layer list, channel count or weight.  The blocks below are the synthetic
+workloads built from those pieces:
+
+* ``ResBlock``  y = x + conv2(act(conv1(act(x)))), act = SiLU(RMSNorm(.)), each
+  conv with its own cache.
+* ``UpStage``   conv2(act(conv1(up2x(x)))) -- the 1080p-class and 1440p output
+  stages (conv1 reads the nearest-upsampled input).
+* ``Decoder``   conv_in, three stages of [nearest up (2x space; 2x time on
+  non-first frames for the first two) -> conv -> two ResBlocks], then a head:
+  act at low resolution -> nearest 2x -> conv to 3 channels.  Moving the act
+  before the upsample is exact because it works per position (the SwiftVR page,
+  "TemporalGrow: Compute Before Spatial Upsampling").
+
+``store`` is the storage rounding: with ``store=round_bf16`` every tensor that
+passes between layers is rounded to bfloat16, as a bf16 pipeline stores it
+(the conv output after bias and residual; the activation, computed from the
+stored conv output).  With ``store=None`` everything stays fp64.
+
+Weights are dicts of numpy arrays: ``w`` [Cout][Cin][kt][kh][kw], ``b`` [Cout]
+or None, ``g`` [C] (the RMSNorm gain applied to this conv's input, where it
+has one).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import oracle as O
+
+
+def _keep(x, store):
+    return x if store is None else store(x)
+
+
+class Conv:
+    """One causal conv layer with its cache (see oracle.CausalConvStream)."""
+
+    def __init__(self, p, mode=O.REPLICATE, up_s=1, up_t=1, nthreads=None):
+        self.s = O.CausalConvStream(p["w"], p.get("b"), mode, up_s, up_t, nthreads)
+
+    def reset(self):
+        self.s.reset()
+
+    def step(self, x):
+        return self.s.step(x)
+
+
+class ResBlock:
+    def __init__(self, p1, p2, eps=1e-6, mode=O.REPLICATE, store=None, nthreads=None):
+        self.c1 = Conv(p1, mode, nthreads=nthreads)
+        self.c2 = Conv(p2, mode, nthreads=nthreads)
+        self.g1, self.g2 = p1["g"], p2["g"]
+        self.eps, self.store = eps, store
+
+    def reset(self):
+        self.c1.reset()
+        self.c2.reset()
+
+    def step(self, x):
+        st = self.store
+        a1 = _keep(O.act(x, self.g1, self.eps), st)
+        h = _keep(self.c1.step(a1), st)
+        a2 = _keep(O.act(h, self.g2, self.eps), st)
+        return _keep(x + self.c2.step(a2), st)
+
+
+class UpStage:
+    """conv2(act(conv1(nearest_up(x)))): up_s on conv1's input."""
+
+    def __init__(self, p1, p2, eps=1e-6, mode=O.REPLICATE, up_s=2, store=None, nthreads=None):
+        self.c1 = Conv(p1, mode, up_s=up_s, nthreads=nthreads)
+        self.c2 = Conv(p2, mode, nthreads=nthreads)
+        self.g2 = p2["g"]
+        self.eps, self.store = eps, store
+
+    def reset(self):
+        self.c1.reset()
+        self.c2.reset()
+
+    def step(self, x):
+        st = self.store
+        h = _keep(self.c1.step(x), st)
+        a = _keep(O.act(h, self.g2, self.eps), st)
+        return _keep(self.c2.step(a), st)
+
+
+DECODER_STAGES = ((384, 2), (192, 2), (96, 1))  # (channels, temporal factor)
+
+
+def decoder_layer_shapes(c_latent=48, stages=DECODER_STAGES, c_out=3, k=3):
+    """(name, Cout, Cin, kt, kh, kw, has_gain) for every conv of the decoder,
+    in execution order.  ``has_gain``: the conv's input passes an RMSNorm."""
+    shapes = [("conv_in", stages[0][0], c_latent, k, k, k, False)]
+    cin = stages[0][0]
+    for si, (c, _) in enumerate(stages):
+        shapes.append(("s%d.up" % si, c, cin, k, k, k, False))
+        for r in range(2):
+            shapes.append(("s%d.rb%d.c1" % (si, r), c, c, k, k, k, True))
+            shapes.append(("s%d.rb%d.c2" % (si, r), c, c, k, k, k, True))
+        cin = c
+    shapes.append(("head", c_out, cin, k, k, k, True))
+    return shapes
+
+
+class Decoder:
+    def __init__(self, params, eps=1e-6, mode=O.REPLICATE, stages=DECODER_STAGES,
+                 store=None, nthreads=None):
+        self.eps, self.store = eps, store
+        self.conv_in = Conv(params["conv_in"], mode, nthreads=nthreads)
+        self.ups, self.blocks = [], []
+        for si, (_, up_t) in enumerate(stages):
+            self.ups.append(Conv(params["s%d.up" % si], mode, up_s=2, up_t=up_t,
+                                 nthreads=nthreads))
+            self.blocks.append([
+                ResBlock(params["s%d.rb%d.c1" % (si, r)], params["s%d.rb%d.c2" % (si, r)],
+                         eps, mode, store, nthreads) for r in range(2)])
+        self.head = Conv(params["head"], mode, up_s=2, nthreads=nthreads)
+        self.g_head = params["head"]["g"]
+
+    def reset(self):
+        self.conv_in.reset()
+        self.head.reset()
+        for u in self.ups:
+            u.reset()
+        for bl in self.blocks:
+            for b in bl:
+                b.reset()
+
+    def step(self, x):
+        st = self.store
+        h = _keep(self.conv_in.step(x), st)
+        for up, bl in zip(self.ups, self.blocks):
+            h = _keep(up.step(h), st)
+            for b in bl:
+                h = b.step(h)
+        a = _keep(O.act(h, self.g_head, self.eps), st)
+        return _keep(self.head.step(a), st)
+
+
+def output_frames(n_latent: int, temporal_factors=(2, 2)) -> int:
+    """Frames after temporal growth on non-first frames: n -> 1 + f (n - 1)."""
+    n = n_latent
+    for f in temporal_factors:
+        n = 1 + f * (n - 1) if n > 0 else 0
+    return n
+
+
+def clip_schedule(n_latent: int, first: int = 7, rest: int = 6):
+    """Latent chunk lengths: the first clip of ``first`` latents (25 frames after
+    two 2x temporal growths), then clips of ``rest`` (24 frames), the last one
+    holding what remains."""
+    out, left = [], n_latent
+    if left > 0:
+        out.append(min(first, left))
+        left -= out[-1]
+    while left > 0:
+        out.append(min(rest, left))
+        left -= out[-1]
+    return out

@@ -1,0 +1,262 @@
+"""Plain fp64 CPU oracle for the chunked causal 3-D convolution decode stack.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this module.  It shares no code
+with the GPU library (no kernels, headers, tables or helpers) and never
+imports the ``causal_convolution_x3x3_amd`` package.
+
+Every function computes what the pages define, in the order they state it, on
+float64 numpy arrays laid out [C][T][H][W] (one video, channels first):
+
+* causal conv -- the SwiftVR page, "ReAE: Causal Halo Exchange": each output
+  frame sees its own frame and earlier ones only; the page's MemoryBlock pairs
+  (current, previous) inputs, i.e. a temporal kernel of 2.  A 3x3x3 kernel takes
+  k_t-1 = 2 frames of history.  First-chunk history is zeros on that page; the
+  3x3x3 workloads replicate the first frame (both are modes here).
+* chunked form -- the same page, "From Pixels to Latents and Back": every layer
+  keeps boundary features across chunks; "ReAE: Causal Halo Exchange": a chunk
+  needs only the previous chunk's trailing input frames at each layer.
+* nearest 2x spatial upsample -- "TemporalGrow: Compute Before Spatial
+  Upsampling": nearest upsampling copies each position to four outputs, and
+  per-position ops commute with it.
+* 2x temporal growth on non-first frames, channel RMSNorm, SiLU, the residual
+  block and the stacks are the synthetic decoder workloads' own definitions
+  (the pages name the blocks but print no layer list); the readings taken where
+  the pages are silent are listed in the design doc.
+
+The dense sum itself runs in ``cc3d_oracle.c`` (plain nested loops, fp64).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "cc3d_oracle.c")
+_LIB = os.path.join(_HERE, "libcc3d_oracle.so")
+_lib_handle = None
+
+ZERO = "zero"
+REPLICATE = "replicate"
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared",
+             "-pthread", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _lib():
+    global _lib_handle
+    if _lib_handle is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i = ctypes.c_int
+        i64 = ctypes.c_int64
+        lib.cc3d_oracle_conv_valid.argtypes = [dp, i, i, i, i, dp, i, i, i, i, dp, dp, i]
+        lib.cc3d_oracle_conv_valid.restype = i
+        lib.cc3d_oracle_conv_points.argtypes = [
+            ctypes.POINTER(ctypes.c_float), i64, i64, i64, i64, i, i, i, i, i,
+            dp, i, i, i, i, dp, ctypes.POINTER(ctypes.c_int32), i64, dp, i]
+        lib.cc3d_oracle_conv_points.restype = i
+        _lib_handle = lib
+    return _lib_handle
+
+
+def default_threads() -> int:
+    return max(1, len(os.sched_getaffinity(0)))
+
+
+def _dptr(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+# ---------------------------------------------------------------- the conv --
+
+def conv_valid(xp: np.ndarray, w: np.ndarray, bias=None, nthreads: int | None = None) -> np.ndarray:
+    """Y[o,t] = B[o] + sum W[o,c,a,b,d] Xp[c,t+a,h+b-ph,w+d-pw] over an already
+    temporally padded sequence Xp [Cin][Tp][H][W]; spatial zero padding."""
+    xp = np.ascontiguousarray(xp, dtype=np.float64)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    cin, tp, h, wd = xp.shape
+    cout, cin_w, kt, kh, kw = w.shape
+    if cin_w != cin:
+        raise ValueError("weight Cin %d != input Cin %d" % (cin_w, cin))
+    if tp < kt:
+        raise ValueError("padded sequence shorter than the temporal kernel")
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float64)
+    y = np.empty((cout, tp - kt + 1, h, wd), dtype=np.float64)
+    rc = _lib().cc3d_oracle_conv_valid(
+        _dptr(xp), cin, tp, h, wd, _dptr(w), cout, kt, kh, kw,
+        None if b is None else _dptr(b), _dptr(y), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("cc3d_oracle_conv_valid rejected its arguments")
+    return y
+
+
+def conv_points(z: np.ndarray, w: np.ndarray, bias, pts: np.ndarray, up: int = 1,
+                nthreads: int | None = None) -> np.ndarray:
+    """The conv sum at output positions pts (n x 3: t, y, x) of the conv applied to
+    the nearest-upsampled (factor ``up``) padded sequence Z [Cin][Tz][H][W]
+    (any strides, float32 holding exact values).  Returns n x Cout fp64."""
+    if z.dtype != np.float32:
+        raise TypeError("conv_points reads a float32 input")
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    cin, tz, hin, win = z.shape
+    cout, cin_w, kt, kh, kw = w.shape
+    if cin_w != cin:
+        raise ValueError("weight Cin mismatch")
+    pts = np.ascontiguousarray(pts, dtype=np.int32).reshape(-1, 3)
+    out = np.empty((pts.shape[0], cout), dtype=np.float64)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float64)
+    st = [s // z.itemsize for s in z.strides]
+    rc = _lib().cc3d_oracle_conv_points(
+        z.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), st[0], st[1], st[2], st[3],
+        cin, tz, hin, win, up, _dptr(w), cout, kt, kh, kw,
+        None if b is None else _dptr(b),
+        pts.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), pts.shape[0], _dptr(out),
+        nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("cc3d_oracle_conv_points rejected its arguments")
+    return out
+
+
+def history(first_frame: np.ndarray, n: int, mode: str) -> np.ndarray:
+    """The n frames that stand before the first frame of the video: zeros (the
+    MemoryBlock rule: the first chunk uses zeros as its history) or n copies of
+    the first frame (replicate)."""
+    c, h, w = first_frame.shape
+    if mode == ZERO:
+        return np.zeros((c, n, h, w), dtype=np.float64)
+    if mode == REPLICATE:
+        return np.repeat(first_frame[:, None], n, axis=1).astype(np.float64)
+    raise ValueError("unknown temporal pad mode %r" % (mode,))
+
+
+def temporal_pad(x: np.ndarray, kt: int, mode: str) -> np.ndarray:
+    """X~ = history(k_t-1 frames) followed by X along time."""
+    return np.concatenate([history(x[:, 0], kt - 1, mode), x.astype(np.float64)], axis=1)
+
+
+def causal_conv3d(x: np.ndarray, w: np.ndarray, bias=None, mode: str = REPLICATE,
+                  nthreads: int | None = None) -> np.ndarray:
+    """One-shot causal conv over the whole sequence: conv_valid(temporal_pad(x))."""
+    return conv_valid(temporal_pad(x, w.shape[2], mode), w, bias, nthreads)
+
+
+# ------------------------------------------------------- composed pieces --
+
+def upsample_spatial(x: np.ndarray, s: int = 2) -> np.ndarray:
+    """Nearest upsample: U[c,t,h,w] = X[c,t,floor(h/s),floor(w/s)]."""
+    return np.repeat(np.repeat(x, s, axis=2), s, axis=3)
+
+
+def upsample_temporal(x: np.ndarray, first: bool) -> np.ndarray:
+    """Nearest 2x in time on non-first frames: V[0]=X[0]; V[2j-1]=V[2j]=X[j].
+    For a chunk that does not start the video every frame is doubled."""
+    if first:
+        return np.concatenate([x[:, :1], np.repeat(x[:, 1:], 2, axis=1)], axis=1)
+    return np.repeat(x, 2, axis=1)
+
+
+def rms_norm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """Channel RMSNorm per position: gamma_c * x_c / sqrt(mean_c x^2 + eps)."""
+    ms = np.mean(x * x, axis=0, keepdims=True)
+    g = np.asarray(gamma, dtype=np.float64).reshape((-1,) + (1,) * (x.ndim - 1))
+    return g * x / np.sqrt(ms + eps)
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """z * sigmoid(z) = z / (1 + e^-z)."""
+    return z / (1.0 + np.exp(-z))
+
+
+def act(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """Pre-activation: SiLU(RMSNorm(x))."""
+    return silu(rms_norm(x, gamma, eps))
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest bfloat16 (ties to even), returned as float64.
+    fp64 -> fp32 (nearest) -> bf16 (nearest even on the dropped 16 bits)."""
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------------- streaming --
+
+class CausalConvStream:
+    """A causal conv run chunk by chunk with a cache of the last k_t-1 frames
+    of its (logical, i.e. upsampled) input, equal to the one-shot conv.
+
+    Z = cache || chunk; the chunk's outputs use Z[t .. t+k_t-1]; the new cache is
+    the last k_t-1 frames of Z.  On the first chunk the cache is the history
+    rule (zeros or copies of the chunk's first frame).  The cache is held at the
+    input's own resolution; when ``up_s``/``up_t`` are set the chunk is first
+    upsampled (nearest, spatial; temporal growth on non-first frames).
+    """
+
+    def __init__(self, w, bias=None, mode: str = REPLICATE, up_s: int = 1, up_t: int = 1,
+                 nthreads: int | None = None):
+        self.w = np.asarray(w, dtype=np.float64)
+        self.bias = None if bias is None else np.asarray(bias, dtype=np.float64)
+        self.mode = mode
+        self.up_s = up_s
+        self.up_t = up_t
+        self.kt = self.w.shape[2]
+        self.nthreads = nthreads
+        self.reset()
+
+    def reset(self):
+        self.cache = None
+        self.frames_seen = 0
+
+    def logical_input(self, x: np.ndarray) -> np.ndarray:
+        v = np.asarray(x, dtype=np.float64)
+        if self.up_t == 2:
+            v = upsample_temporal(v, first=(self.frames_seen == 0))
+        return v
+
+    def step(self, x: np.ndarray) -> np.ndarray:
+        v = self.logical_input(x)  # low spatial resolution, grown in time
+        if self.frames_seen == 0:
+            self.cache = history(v[:, 0], self.kt - 1, self.mode)
+        z = np.concatenate([self.cache, v], axis=1)
+        zs = upsample_spatial(z, self.up_s) if self.up_s > 1 else z
+        y = conv_valid(zs, self.w, self.bias, self.nthreads)
+        self.cache = z[:, z.shape[1] - (self.kt - 1):].copy()
+        self.frames_seen += x.shape[1]
+        return y
+
+
+def one_shot(x, w, bias=None, mode=REPLICATE, up_s=1, up_t=1, nthreads=None):
+    """Upsample the whole video, then the one-shot causal conv."""
+    v = np.asarray(x, dtype=np.float64)
+    if up_t == 2:
+        v = upsample_temporal(v, first=True)
+    if up_s > 1:
+        v = upsample_spatial(v, up_s)
+    return causal_conv3d(v, w, bias, mode, nthreads)
+
+
+def chunked(x, w, bias=None, mode=REPLICATE, up_s=1, up_t=1, splits=None, nthreads=None):
+    """Run the stream over chunk lengths ``splits`` and concatenate the outputs."""
+    s = CausalConvStream(w, bias, mode, up_s, up_t, nthreads)
+    out, t0 = [], 0
+    for n in splits:
+        out.append(s.step(x[:, t0:t0 + n]))
+        t0 += n
+    if t0 != x.shape[1]:
+        raise ValueError("splits do not cover the sequence")
+    return np.concatenate(out, axis=1)

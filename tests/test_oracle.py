@@ -1,0 +1,344 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each pin is chosen so a plausible slip in the oracle -- a dropped bias, a
+reversed temporal or spatial tap, swapped Cin/Cout, a wrong history rule, a
+cache that keeps the wrong frames, an upsample that rounds instead of floors, a
+norm over the wrong axis -- fails at least one test.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import brute, model as M
+from oracle import oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    out = {}
+    with open(os.path.join(GOLD, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split(":", 1)
+            out[k.strip()] = v.strip()
+    return out
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ------------------------------------------------------------ brute force --
+
+KSHAPES = [(kt, kh, kw) for kt in (1, 2, 3) for kh in (1, 3) for kw in (1, 3)]
+
+
+@pytest.mark.parametrize("k", KSHAPES)
+@pytest.mark.parametrize("mode", [O.REPLICATE, O.ZERO])
+def test_conv_matches_brute_force(k, mode):
+    r = _rng(hash((k, mode)) % 2**32)
+    cin, cout, t, h, w = 3, 2, 5, 4, 5
+    x = r.standard_normal((cin, t, h, w))
+    wt = r.standard_normal((cout, cin) + k)
+    b = r.standard_normal(cout)
+    ref = brute.causal_conv3d_brute(x, wt, b, mode)
+    got = O.causal_conv3d(x, wt, b, mode)
+    assert got.shape == ref.shape
+    assert np.max(np.abs(got - ref)) <= 1e-13 * max(1.0, np.max(np.abs(ref)))
+
+
+@pytest.mark.parametrize("mode", [O.REPLICATE, O.ZERO])
+def test_conv_matches_torch_conv3d(mode):
+    """Library routine: torch CPU float64 conv3d (cross-correlation) on the
+    explicitly padded input (history frames + spatial zero border)."""
+    r = _rng(7)
+    cin, cout, t, h, w = 5, 7, 6, 9, 11
+    x = r.standard_normal((cin, t, h, w))
+    wt = r.standard_normal((cout, cin, 3, 3, 3))
+    b = r.standard_normal(cout)
+    xt = torch.from_numpy(x)
+    hist = torch.zeros_like(xt[:, :1]) if mode == O.ZERO else xt[:, :1]
+    xp = torch.cat([hist, hist, xt], dim=1)
+    xp = F.pad(xp, (1, 1, 1, 1))
+    ref = F.conv3d(xp[None], torch.from_numpy(wt), torch.from_numpy(b))[0].numpy()
+    got = O.causal_conv3d(x, wt, b, mode)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+# ---------------------------------------------------------- delta kernels --
+
+def _delta(c, kt, kh, kw, a, bb, d):
+    w = np.zeros((c, c, kt, kh, kw))
+    for i in range(c):
+        w[i, i, a, bb, d] = 1.0
+    return w
+
+
+def test_delta_identity():
+    x = _rng(1).standard_normal((3, 5, 6, 7))
+    y = O.causal_conv3d(x, _delta(3, 3, 3, 3, 2, 1, 1), None, O.REPLICATE)
+    assert np.array_equal(y, x)
+
+
+@pytest.mark.parametrize("mode", [O.REPLICATE, O.ZERO])
+def test_delta_oldest_tap_shifts_time(mode):
+    """k_t=3, delta at a=0: Y_t = X_{t-2} for t>=2; X_0 or 0 before."""
+    x = _rng(2).standard_normal((2, 6, 4, 5))
+    y = O.causal_conv3d(x, _delta(2, 3, 3, 3, 0, 1, 1), None, mode)
+    assert np.array_equal(y[:, 2:], x[:, :-2])
+    for t in range(2):
+        expect = x[:, 0] if mode == O.REPLICATE else np.zeros_like(x[:, 0])
+        assert np.array_equal(y[:, t], expect)
+
+
+def test_memoryblock_previous_tap_zero_history():
+    """k_t=2 previous-frame tap with zero history: Y_0 = 0, Y_t = X_{t-1}."""
+    x = _rng(3).standard_normal((2, 4, 3, 3))
+    y = O.causal_conv3d(x, _delta(2, 2, 3, 3, 0, 1, 1), None, O.ZERO)
+    assert np.array_equal(y[:, 0], np.zeros_like(x[:, 0]))
+    assert np.array_equal(y[:, 1:], x[:, :-1])
+
+
+def test_delta_spatial_shift_zero_border():
+    """delta at (b,d)=(0,2): Y[h,w] = X[h-1, w+1], zero outside the image."""
+    x = _rng(4).standard_normal((1, 2, 5, 6))
+    y = O.causal_conv3d(x, _delta(1, 1, 3, 3, 0, 0, 2), None, O.REPLICATE)
+    expect = np.zeros_like(x)
+    expect[:, :, 1:, :-1] = x[:, :, :-1, 1:]
+    assert np.array_equal(y, expect)
+
+
+def test_weight_axes_not_transposed():
+    """Cin != Cout and a weight that only links input channel 1 to output 0."""
+    x = _rng(5).standard_normal((3, 2, 3, 3))
+    w = np.zeros((2, 3, 1, 1, 1))
+    w[0, 1, 0, 0, 0] = 2.5
+    y = O.causal_conv3d(x, w, np.array([0.0, -1.0]), O.REPLICATE)
+    assert np.array_equal(y[0], 2.5 * x[1])
+    assert np.array_equal(y[1], -np.ones_like(x[0]))
+
+
+# ------------------------------------------------------------ closed form --
+
+@pytest.mark.parametrize("mode", [O.REPLICATE, O.ZERO])
+def test_constant_input_border_counts(mode):
+    c, cin, t, h, w = 1.5, 4, 5, 5, 6
+    x = np.full((cin, t, h, w), c)
+    wt = np.ones((2, cin, 3, 3, 3))
+    y = O.causal_conv3d(x, wt, None, mode)
+    nh = np.array([2] + [3] * (h - 2) + [2])
+    nw = np.array([2] + [3] * (w - 2) + [2])
+    for tt in range(t):
+        kt_eff = 3 if mode == O.REPLICATE else min(tt + 1, 3)
+        expect = c * cin * kt_eff * nh[:, None] * nw[None, :]
+        assert np.array_equal(y[0, tt], expect)
+        assert np.array_equal(y[1, tt], expect)
+
+
+def test_rmsnorm_silu_closed_forms():
+    g = np.array([0.5, 1.0, 1.5])
+    x = np.full((3, 2, 2, 2), 2.0)
+    eps = 1e-6
+    np.testing.assert_allclose(O.rms_norm(x, g, eps)[:, 0, 0, 0], g * 2.0 / np.sqrt(4.0 + eps),
+                               rtol=1e-15)
+    # mean over channels, not sum: a 1-hot vector of value v has rms = v / sqrt(C)
+    x1 = np.zeros((4, 1, 1, 1))
+    x1[2] = 3.0
+    np.testing.assert_allclose(O.rms_norm(x1, np.ones(4), 0.0)[2, 0, 0, 0], 2.0, rtol=1e-15)
+    z = np.linspace(-8, 8, 33)
+    assert O.silu(np.zeros(1))[0] == 0.0
+    np.testing.assert_allclose(O.silu(z) - O.silu(-z), z, atol=1e-14)
+    np.testing.assert_allclose(O.silu(np.array([50.0]))[0], 50.0, rtol=1e-15)
+
+
+def test_round_bf16_matches_torch():
+    r = _rng(9)
+    x = np.concatenate([r.standard_normal(4096) * 10 ** r.uniform(-6, 6, 4096),
+                        [0.0, -0.0, 1.0, 1.00390625, 1.01171875]])  # ties both ways
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.round_bf16(x), ref)
+
+
+# -------------------------------------------------------------- chunking --
+
+SPLITS = [[9], [1, 4, 4], [1] * 9, [2, 3, 1, 3], [4, 5]]
+
+
+@pytest.mark.parametrize("splits", SPLITS)
+@pytest.mark.parametrize("mode", [O.REPLICATE, O.ZERO])
+@pytest.mark.parametrize("up", [(1, 1), (2, 1), (2, 2)])
+def test_chunked_equals_one_shot(splits, mode, up):
+    r = _rng(11)
+    x = r.standard_normal((3, 9, 4, 5))
+    w = r.standard_normal((2, 3, 3, 3, 3))
+    b = r.standard_normal(2)
+    ref = O.one_shot(x, w, b, mode, up_s=up[0], up_t=up[1])
+    got = O.chunked(x, w, b, mode, up_s=up[0], up_t=up[1], splits=splits)
+    assert got.shape == ref.shape
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_cache_holds_last_frames_of_window():
+    """A first chunk of one frame: the new cache is (history frame, x0); after
+    it the next chunk sees x0 twice only in replicate mode."""
+    x = _rng(12).standard_normal((2, 3, 2, 2))
+    s = O.CausalConvStream(np.zeros((1, 2, 3, 3, 3)), mode=O.ZERO)
+    s.step(x[:, :1])
+    assert np.array_equal(s.cache[:, 0], np.zeros_like(x[:, 0]))
+    assert np.array_equal(s.cache[:, 1], x[:, 0])
+    s.step(x[:, 1:3])
+    assert np.array_equal(s.cache, x[:, 1:3])
+
+
+def test_memoryblock_golden_pairs():
+    g = _read_golden("memoryblock_pairs.txt")
+    assert g["current"].split() == ["A", "B", "C"]
+    assert g["previous"].split() == ["P", "A", "B"]
+    assert g["first_chunk_history"] == "zero"
+    vals = {"P": 1.0, "A": 2.0, "B": 3.0, "C": 4.0}
+    # k_t = 2, 1x1 spatial: out = 10*current + 1*previous, so each output
+    # spells its (current, previous) pair in base 10.
+    w = np.zeros((1, 1, 2, 1, 1))
+    w[0, 0, 0] = 1.0   # previous frame
+    w[0, 0, 1] = 10.0  # current frame
+    s = O.CausalConvStream(w, mode=O.ZERO)
+    y0 = s.step(np.full((1, 1, 1, 1), vals["P"]))
+    assert y0[0, 0, 0, 0] == 10 * vals["P"] + 0.0  # zero history
+    chunk = np.array([vals[k] for k in g["current"].split()]).reshape(1, 3, 1, 1)
+    y = s.step(chunk)[0, :, 0, 0]
+    for i, (cur, prev) in enumerate(zip(g["current"].split(), g["previous"].split())):
+        assert y[i] == 10 * vals[cur] + vals[prev]
+
+
+# ------------------------------------------------------------- causality --
+
+@pytest.mark.parametrize("up_t", [1, 2])
+def test_causality(up_t):
+    r = _rng(13)
+    x = r.standard_normal((2, 6, 4, 4))
+    w = r.standard_normal((2, 2, 3, 3, 3))
+    base = O.one_shot(x, w, None, O.REPLICATE, up_s=2, up_t=up_t)
+    for tp in range(1, 6):
+        x2 = x.copy()
+        x2[:, tp] += 1.0
+        y2 = O.one_shot(x2, w, None, O.REPLICATE, up_s=2, up_t=up_t)
+        first_changed = tp if up_t == 1 else 2 * tp - 1
+        assert np.array_equal(base[:, :first_changed], y2[:, :first_changed])
+        assert not np.array_equal(base[:, first_changed], y2[:, first_changed])
+
+
+# ---------------------------------------------------------------- upsample --
+
+def test_upsample_is_repeat_interleave():
+    x = _rng(14).standard_normal((2, 3, 4, 5))
+    ref = torch.from_numpy(x).repeat_interleave(2, dim=2).repeat_interleave(2, dim=3).numpy()
+    assert np.array_equal(O.upsample_spatial(x, 2), ref)
+    v = O.upsample_temporal(x, first=True)
+    assert v.shape[1] == 1 + 2 * (x.shape[1] - 1)
+    assert np.array_equal(v[:, 0], x[:, 0])
+    for j in range(1, x.shape[1]):
+        assert np.array_equal(v[:, 2 * j - 1], x[:, j]) and np.array_equal(v[:, 2 * j], x[:, j])
+
+
+def test_act_commutes_with_nearest_upsample_bitwise():
+    """Per-position ops before or after nearest 2x give identical bits (the
+    reorder the SwiftVR page reports as bitwise identical RGB)."""
+    r = _rng(15)
+    x = r.standard_normal((8, 2, 5, 6))
+    g = r.uniform(0.5, 1.5, 8)
+    a = O.upsample_spatial(O.act(x, g, 1e-6), 2)
+    b = O.act(O.upsample_spatial(x, 2), g, 1e-6)
+    assert np.array_equal(a, b)
+
+
+def test_conv_points_matches_full():
+    r = _rng(16)
+    x = r.standard_normal((3, 4, 5, 6)).astype(np.float32)
+    w = r.standard_normal((2, 3, 3, 3, 3))
+    b = r.standard_normal(2)
+    xp = O.temporal_pad(x.astype(np.float64), 3, O.REPLICATE)
+    full = O.conv_valid(O.upsample_spatial(xp, 2), w, b)
+    z = xp.astype(np.float32).transpose(1, 2, 3, 0).copy().transpose(3, 0, 1, 2)  # strided view
+    pts = np.array([[t, y, xx] for t in range(4) for y in (0, 3, 9) for xx in (0, 5, 11)])
+    got = O.conv_points(z, w, b, pts, up=2)
+    ref = np.stack([full[:, t, y, xx] for t, y, xx in pts])
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+# ----------------------------------------------------------------- blocks --
+
+def _params(r, cout, cin, gain=True, bias=False):
+    p = {"w": r.standard_normal((cout, cin, 3, 3, 3)) / np.sqrt(cin * 27)}
+    p["b"] = r.uniform(-0.1, 0.1, cout) if bias else None
+    if gain:
+        p["g"] = r.uniform(0.5, 1.5, cin)
+    return p
+
+
+def test_resblock_definition_and_chunking():
+    r = _rng(17)
+    c = 4
+    p1, p2 = _params(r, c, c, bias=True), _params(r, c, c, bias=True)
+    x = r.standard_normal((c, 6, 3, 4))
+    eps = 1e-6
+    a1 = O.act(x, p1["g"], eps)
+    h = O.causal_conv3d(a1, p1["w"], p1["b"])
+    ref = x + O.causal_conv3d(O.act(h, p2["g"], eps), p2["w"], p2["b"])
+    blk = M.ResBlock(p1, p2, eps)
+    got = np.concatenate([blk.step(x[:, i:i + 2]) for i in range(0, 6, 2)], axis=1)
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_decoder_shapes_and_causality():
+    r = _rng(18)
+    stages = ((6, 2), (5, 2), (4, 1))
+    shapes = M.decoder_layer_shapes(c_latent=3, stages=stages, c_out=3)
+    params = {}
+    for name, co, ci, kt, kh, kw, has_g in shapes:
+        params[name] = {"w": r.standard_normal((co, ci, kt, kh, kw)) / np.sqrt(ci * 27), "b": None,
+                        "g": r.uniform(0.5, 1.5, ci) if has_g else None}
+    x = r.standard_normal((3, 4, 2, 3))
+    dec = M.Decoder(params, stages=stages)
+    y = dec.step(x)
+    assert y.shape == (3, M.output_frames(4), 2 * 16, 3 * 16)
+    # chunked with per-layer caches == one shot
+    dec.reset()
+    yc = np.concatenate([dec.step(x[:, :1]), dec.step(x[:, 1:3]), dec.step(x[:, 3:])], axis=1)
+    assert np.max(np.abs(yc - y)) <= 1e-11
+    # latent t' leaves output frames < 4t'-3 unchanged
+    x2 = x.copy()
+    x2[:, 2] += 1.0
+    dec.reset()
+    y2 = dec.step(x2)
+    assert np.array_equal(y[:, :5], y2[:, :5])
+    assert not np.array_equal(y[:, 5], y2[:, 5])
+
+
+def test_chunk_schedule_golden():
+    g = _read_golden("chunk_schedule.txt")
+    sched = M.clip_schedule(91)
+    frames = []
+    done = 0
+    for n in sched:
+        # frames a clip adds: growth of the video prefix it completes
+        frames.append(M.output_frames(done + n) - M.output_frames(done))
+        done += n
+    assert len(sched) == int(g["n_chunks"])
+    assert frames[0] == int(g["first_chunk_read"]) - int(g["first_chunk_dropped"])
+    assert all(f == int(g["clip_len"]) for f in frames[1:])
+    assert sum(frames) == int(g["total_frames"]) == M.output_frames(91)
+    assert M.output_frames(2) - M.output_frames(1) == int(g["pixel_frames_per_latent"])
+
+
+def test_payload_golden():
+    g = _read_golden("payload_1440p.txt")
+    n = int(g["frames"]) * int(g["channels"]) * int(g["height"]) * int(g["width"])
+    assert round(2 * n / 2**30, 3) == float(g["bf16_gib"])
+    assert round(n / 2**30, 3) == float(g["uint8_gib"])
+    assert int(g["height"]) == 90 * 16 and int(g["width"]) == 160 * 16
