@@ -1,0 +1,294 @@
+"""Benchmark of the chunked causal Conv3d decode on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4|c3] [--no-cpu-baseline]
+
+Workloads (synthetic, seeded; the pages' test videos and trained weights are not
+available):
+  c4 (default): the decoder stack, latent 48 x 91 frames x 90x160 -> RGB
+      3 x 361 x 1440x2560, decoded in clips of 7 then 6 latents (25, then 24
+      output frames).  One step = one clip through every layer.
+  c3: the 1440p output stage, 128 ch x 720x1280 -> nearest 2x -> conv 128->96 ->
+      RMSNorm+SiLU -> conv 96->3, 361 frames streamed as 1 + 90 chunks of 4.
+      One step = one chunk.
+Inputs are resident in HBM before timing; outputs go to a device ring.
+
+Prints one JSON line: value = algorithmic conv TFLOP/s (2*Cin*Cout*27 FLOP per
+output voxel of every conv) over the timed steps; plus output frames/s, the
+dominant kernel's roofline (live HIP-event timing on the plan's stream) and the
+CPU oracle's rate on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0
+METRIC = "causal Conv3d decode TFLOP/s + output frames/s at 1440p, % of bf16 MFMA peak"
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def conv_flops_per_voxel(cin, cout, k=27):
+    return 2.0 * cin * cout * k
+
+
+def make_decoder(dev, synth, S, OMshapes):
+    params = {}
+    for i, (name, co, ci, kt, kh, kw, has_g) in enumerate(OMshapes):
+        w = synth.bf16(synth.conv_weight(co, ci, kt, kh, kw, synth.seed(4, 10 + 3 * i))).to(dev)
+        g = synth.gain(ci, synth.seed(4, 11 + 3 * i)).to(dev) if has_g else None
+        params[name] = {"w": w, "g": g, "b": None}
+    return params
+
+
+def decoder_layer_list(c_latent=48, stages=((384, 2), (192, 2), (96, 1)), c_out=3):
+    """(name, cout, cin, kt, kh, kw, has_gain) -- the decoder's conv list."""
+    out = [("conv_in", stages[0][0], c_latent, 3, 3, 3, False)]
+    cin = stages[0][0]
+    for si, (c, _) in enumerate(stages):
+        out.append(("s%d.up" % si, c, cin, 3, 3, 3, False))
+        for r in range(2):
+            out.append(("s%d.rb%d.c1" % (si, r), c, c, 3, 3, 3, True))
+            out.append(("s%d.rb%d.c2" % (si, r), c, c, 3, 3, 3, True))
+        cin = c
+    out.append(("head", c_out, cin, 3, 3, 3, True))
+    return out
+
+
+def grown(n, first):
+    return 2 * n - 1 if first else 2 * n
+
+
+def c4_step_flops(t_lat, first, h=90, w=160):
+    """Algorithmic conv FLOP of one clip of t_lat latents."""
+    f = 0.0
+    t = t_lat
+    f += conv_flops_per_voxel(48, 384) * t * h * w
+    cin = 384
+    for si, (c, up_t) in enumerate(((384, 2), (192, 2), (96, 1))):
+        h, w = 2 * h, 2 * w
+        if up_t == 2:
+            t = grown(t, first)
+        f += conv_flops_per_voxel(cin, c) * t * h * w
+        f += 4 * conv_flops_per_voxel(c, c) * t * h * w
+        cin = c
+    f += conv_flops_per_voxel(96, 3) * t * (2 * h) * (2 * w)
+    return f, t
+
+
+def setup_c4(dev, torch, synth, P, S):
+    lat_c, lat_t, lh, lw = 48, 91, 90, 160
+    layers = decoder_layer_list()
+    params = make_decoder(dev, synth, S, layers)
+    ops = S.decoder_ops(params)
+    plan = P.stack_plan(ops, lat_c, lh, lw, max_chunk_t=7, device=dev)
+    del params
+    log("c4 plan: %d ops, state %.2f GB, plan device memory %.2f GB" % (
+        len(ops), plan.state_bytes / 1e9, plan.device_bytes / 1e9))
+    x = synth.bf16(synth.video(lat_c, lat_t, lh, lw, synth.seed(4, 1)))
+    x_cl = x.permute(1, 2, 3, 0).contiguous().to(dev)
+    del x
+    sched = [7] + [6] * 14
+    starts = [0]
+    for n in sched[:-1]:
+        starts.append(starts[-1] + n)
+    clips = [(x_cl[s:s + n].contiguous(), s == 0) for s, n in zip(starts, sched)]
+    ring = [torch.empty((25, 1440, 2560, 3), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    work = []
+    for (xc, first), n in zip(clips, sched):
+        fl, tout = c4_step_flops(n, first)
+        work.append((xc, first, fl, tout))
+    desc = {"workload": "c4_decoder_bf16: latent 48x91x90x160 -> conv_in 48->384 -> 3 stages "
+                        "(384/192/96 ch; nearest 2x space, 2x time on non-first frames for stages 1-2; "
+                        "2 residual blocks each) -> head 96->3 at 1440x2560; clips of 7+14x6 latents",
+            "output": "3x361x1440x2560 bf16", "step": "one clip (24 output frames; 25 for the first)"}
+    return plan, work, ring, desc
+
+
+def setup_c3(dev, torch, synth, P, S):
+    cin, cmid, cout, h, w = 128, 96, 3, 720, 1280
+    w1 = synth.bf16(synth.conv_weight(cmid, cin, 3, 3, 3, synth.seed(3, 10))).to(dev)
+    w2 = synth.bf16(synth.conv_weight(cout, cmid, 3, 3, 3, synth.seed(3, 13))).to(dev)
+    g2 = synth.gain(cmid, synth.seed(3, 14)).to(dev)
+    plan = P.stack_plan(S.upstage_ops(cmid, cout, {"w": w1}, {"w": w2, "g": g2}), cin, h, w, max_chunk_t=4,
+                        device=dev)
+    pool = []
+    for k in range(8):  # distinct input chunks, cycled (content does not change the time)
+        x = synth.bf16(synth.video(cin, 4, h, w, synth.seed(3, 100 + k)))
+        pool.append(x.permute(1, 2, 3, 0).contiguous().to(dev))
+    sched = [1] + [4] * 90
+    fl_frame = (conv_flops_per_voxel(cin, cmid) + conv_flops_per_voxel(cmid, cout)) * 1440 * 2560
+    work = []
+    for i, n in enumerate(sched):
+        work.append((pool[i % 8][:n], i == 0, fl_frame * n, n))
+    ring = [torch.empty((4, 1440, 2560, 3), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    desc = {"workload": "c3_stage1440_bf16: 128x720x1280 -> nearest 2x -> conv 128->96 -> RMSNorm+SiLU -> "
+                        "conv 96->3 at 1440x2560; 361 frames as 1+90x4 chunks with caches",
+            "output": "3x361x1440x2560 bf16", "step": "one 4-frame chunk"}
+    return plan, work, ring, desc
+
+
+def cpu_baseline(workload):
+    """The fp64 oracle, as it stands, on a bounded crop of the same workload."""
+    import numpy as np
+
+    from causal_convolution_x3x3_amd import synth
+    from oracle import model as OM
+    from oracle import oracle as O
+
+    O.build()
+    threads = O.default_threads()
+    if workload == "c4":
+        lt, lh, lw = 2, 2, 3
+        shapes = OM.decoder_layer_shapes()
+        params = {}
+        for i, (name, co, ci, kt, kh, kw, has_g) in enumerate(shapes):
+            params[name] = {"w": synth.conv_weight(co, ci, kt, kh, kw, synth.seed(4, 10 + 3 * i)).double().numpy(),
+                            "g": synth.gain(ci, synth.seed(4, 11 + 3 * i)).double().numpy() if has_g else None,
+                            "b": None}
+        x = synth.video(48, lt, lh, lw, synth.seed(4, 1)).double().numpy()
+        dec = OM.Decoder(params, nthreads=threads)
+        t0 = time.perf_counter()
+        y = dec.step(x)
+        dt = time.perf_counter() - t0
+        fl, tout = c4_step_flops(lt, True, lh, lw)
+        sample = ("whole decoder, one first clip of %d latents on a %dx%d latent crop "
+                  "(-> %d frames of %dx%d), fp64, %d threads" % (lt, lh, lw, y.shape[1], y.shape[2], y.shape[3],
+                                                                threads))
+        frames_per_s = y.shape[1] / dt * (y.shape[2] * y.shape[3]) / (1440 * 2560)
+    else:
+        cin, cmid, rows, cols = 128, 96, 8, 64
+        w1 = synth.conv_weight(cmid, cin, 3, 3, 3, synth.seed(3, 10)).double().numpy()
+        w2 = synth.conv_weight(3, cmid, 3, 3, 3, synth.seed(3, 13)).double().numpy()
+        g2 = synth.gain(cmid, synth.seed(3, 14)).double().numpy()
+        st = OM.UpStage({"w": w1, "b": None}, {"w": w2, "b": None, "g": g2}, nthreads=threads)
+        x = synth.video(cin, 1, rows, cols, synth.seed(3, 100)).double().numpy()
+        t0 = time.perf_counter()
+        y = st.step(x)
+        dt = time.perf_counter() - t0
+        fl = (conv_flops_per_voxel(cin, cmid) + conv_flops_per_voxel(cmid, 3)) * y.shape[2] * y.shape[3]
+        sample = "1440p stage on one frame of a %dx%d crop (-> %dx%d), fp64, %d threads" % (
+            rows, cols, y.shape[2], y.shape[3], threads)
+        frames_per_s = 1.0 / dt * (y.shape[2] * y.shape[3]) / (1440 * 2560)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3), "frames_per_s_equiv": frames_per_s}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=15)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", choices=["c4", "c3"], default="c4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this decode path has no multi-GPU mode "
+              "(the shard design is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from causal_convolution_x3x3_amd import capi as C
+    from causal_convolution_x3x3_amd import plan as P
+    from causal_convolution_x3x3_amd import stacks as S
+    from causal_convolution_x3x3_amd import synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    C.lib()
+    setup = setup_c4 if args.workload == "c4" else setup_c3
+    plan, work, ring, desc = setup(dev, torch, synth, P, S)
+    stream = torch.cuda.current_stream()
+    states = [plan.new_state(), plan.new_state()]
+    cur = [0]
+
+    def step(i):
+        xc, first, fl, tout = work[i % len(work)]
+        if first:
+            plan.reset(states[cur[0]])
+        a, b = states[cur[0]], states[1 - cur[0]]
+        y = ring[i % 2][:tout]
+        plan.forward_chunk(xc, a, b, y=y)
+        cur[0] = 1 - cur[0]
+        return fl, tout
+
+    log("warmup %d steps" % args.warmup)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    C.check(C.lib().cc3d_profile_enable(plan._h, 1), "profile_enable")
+    log("timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    flops, frames = 0.0, 0
+    for i in range(args.warmup, args.warmup + args.steps):
+        fl, tout = step(i)
+        flops += fl
+        frames += tout
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    log("timed %.3f s" % dt)
+
+    # per-kernel event totals over the timed region
+    import ctypes
+    kern = {}
+    for op in range(C.lib().cc3d_plan_num_ops(plan._h)):
+        for part in range(3):
+            pr = C.OpProfile()
+            C.check(C.lib().cc3d_profile_read(plan._h, op, part, ctypes.byref(pr)), "profile_read")
+            if pr.launches == 0:
+                continue
+            k = kern.setdefault(pr.kernel.decode(), {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
+            k["launches"] += pr.launches
+            k["ms"] += pr.total_ms
+            k["flops"] += pr.flops
+            k["bytes"] += pr.bytes
+    C.check(C.lib().cc3d_profile_enable(plan._h, 0), "profile_enable")
+    total_kernel_ms = sum(k["ms"] for k in kern.values())
+    dom_name, dom = max(kern.items(), key=lambda kv: kv[1]["ms"])
+    avg_ms = dom["ms"] / dom["launches"]
+    if dom["flops"] > 0:
+        achieved = dom["flops"] / dom["launches"] / (avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        achieved = dom["bytes"] / dom["launches"] / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof.update({"traffic": None, "kernel": dom_name, "launches": dom["launches"],
+                 "avg_launch_ms": round(avg_ms, 4), "share_of_kernel_time": round(dom["ms"] / total_kernel_ms, 3)})
+    per_kernel = {}
+    for name, k in sorted(kern.items(), key=lambda kv: -kv[1]["ms"]):
+        e = {"ms": round(k["ms"], 3), "launches": k["launches"]}
+        if k["flops"] > 0:
+            e["tflops"] = round(k["flops"] / (k["ms"] * 1e-3) / 1e12, 1)
+        e["gbs"] = round(k["bytes"] / (k["ms"] * 1e-3) / 1e9, 1)
+        per_kernel[name] = e
+
+    value = flops / dt / 1e12
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(dt / args.steps * 1e3, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": desc, "frames_per_s": round(frames / dt, 2), "mfma_frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": roof, "kernels": per_kernel,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on a bounded sample)")
+        out["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

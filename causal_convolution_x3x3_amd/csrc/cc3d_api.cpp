@@ -1,0 +1,856 @@
+// Host runtime of the C ABI in include/cc3d.h: argument validation (always
+// before any device work), plan construction (weight repack, intermediate
+// slots, cache arena layout), and the per-chunk launch sequence.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/cc3d.h"
+#include "cc3d_kernels.h"
+
+namespace {
+
+thread_local char g_err[1024] = "";
+
+cc3d_status fail(cc3d_status st, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+void clear_err() { g_err[0] = 0; }
+
+constexpr uint32_t kPlanMagic = 0xCC3D0A11u;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Frame count of a slot for one chunk: T = mul * t_chunk + (first ? add_first : add_rest).
+struct FrameCount {
+    int64_t mul = 0, add_first = 0, add_rest = 0;
+    bool operator==(const FrameCount& o) const {
+        return mul == o.mul && add_first == o.add_first && add_rest == o.add_rest;
+    }
+    int64_t eval(int64_t t, bool first) const { return mul * t + (first ? add_first : add_rest); }
+    FrameCount grown() const {  // nearest 2x in time on non-first frames
+        FrameCount g;
+        g.mul = 2 * mul;
+        g.add_first = 2 * add_first - 1;
+        g.add_rest = 2 * add_rest;
+        return g;
+    }
+};
+
+struct Slot {
+    bool defined = false;
+    int c = 0, h = 0, w = 0;
+    FrameCount tc;
+    size_t bytes = 0;
+    void* ptr = nullptr;  // intermediates only
+};
+
+struct OpRt {
+    int kind = 0;
+    int cin = 0, cout = 0, kt = 1, kh = 1, kw = 1, up_s = 1, up_t = 1, tpad = 0;
+    int src = -1, res = -1, out = -1, act_out = -1;
+    int norm_src = -1;      // act computed by a separate norm pass reading this slot
+    int h_in = 0, w_in = 0, h_out = 0, w_out = 0;
+    void* wpk = nullptr;    // packed (bf16) or copied (f32) weights
+    float* bias = nullptr;
+    float* gamma = nullptr;
+    size_t cache_off = 0, cache_bytes = 0;
+    int ntile = 0, nblocks = 0, kchunks = 0;
+    bool fused_act = false;
+};
+
+}  // namespace
+
+struct cc3d_plan {
+    uint32_t magic = kPlanMagic;
+    int device = 0;
+    int dtype = CC3D_BF16;
+    int elem = 2;
+    int cin = 0, h = 0, w = 0;
+    int max_t = 1;
+    float eps = 1e-6f;
+    std::vector<Slot> slots;
+    std::vector<OpRt> ops;
+    size_t state_bytes = kAlign;
+    size_t device_bytes = 0;
+    bool uses_aux = false;
+    std::vector<void*> allocs;
+
+    // live event timing (cc3d_profile_*); mutable: forward_chunk takes a const plan
+    struct Pending {
+        hipEvent_t start, stop;
+        double flops, bytes;
+    };
+    struct ProfPart {
+        std::string kernel;
+        int64_t launches = 0;
+        double ms = 0.0, flops = 0.0, bytes = 0.0;
+        std::vector<Pending> pending;
+    };
+    mutable bool prof_on = false;
+    mutable std::vector<ProfPart> prof;  // ops.size() * 3
+    mutable std::vector<hipEvent_t> event_pool;
+};
+
+namespace {
+
+int test_fail_alloc_at()
+{
+    const char* s = getenv("CC3D_TEST_FAIL_ALLOC");
+    return s ? atoi(s) : 0;
+}
+
+struct Allocator {
+    cc3d_plan* p;
+    int count = 0;
+    int fail_at;
+    explicit Allocator(cc3d_plan* plan) : p(plan), fail_at(test_fail_alloc_at()) {}
+    cc3d_status alloc(void** out, size_t bytes, const char* what) {
+        ++count;
+        void* d = nullptr;
+        if (fail_at > 0 && count == fail_at)
+            return fail(CC3D_ENOMEM, "allocation %d (%s, %zu bytes) failed (injected by CC3D_TEST_FAIL_ALLOC)",
+                        count, what, bytes);
+        hipError_t e = hipMalloc(&d, bytes ? bytes : 1);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(CC3D_ENOMEM, "hipMalloc of %zu bytes for %s failed: %s", bytes, what,
+                        hipGetErrorString(e));
+        }
+        p->allocs.push_back(d);
+        p->device_bytes += bytes;
+        *out = d;
+        return CC3D_OK;
+    }
+};
+
+void release(cc3d_plan* p)
+{
+    if (!p) return;
+    int cur = 0;
+    bool switched = false;
+    if (hipGetDevice(&cur) == hipSuccess && cur != p->device) switched = hipSetDevice(p->device) == hipSuccess;
+    for (void* d : p->allocs) (void)hipFree(d);
+    p->allocs.clear();
+    for (auto& part : p->prof)
+        for (auto& e : part.pending) {
+            (void)hipEventDestroy(e.start);
+            (void)hipEventDestroy(e.stop);
+        }
+    for (hipEvent_t e : p->event_pool) (void)hipEventDestroy(e);
+    if (switched) (void)hipSetDevice(cur);
+    p->magic = 0;
+    delete p;
+}
+
+bool valid_dtype(int d) { return d == CC3D_F32 || d == CC3D_BF16; }
+bool valid_slot_ref(int s) { return s >= 0 && s < CC3D_MAX_SLOTS; }
+const char* kind_name(int k) { return k == CC3D_OP_CONV ? "CONV" : "NORM_ACT"; }
+
+// Geometry and wiring checks, no device work.
+cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
+{
+    if (!d) return fail(CC3D_EINVAL, "stack desc is NULL");
+    if (!valid_dtype(d->dtype)) return fail(CC3D_EDTYPE, "dtype %d not accepted (0 = F32, 1 = BF16)", d->dtype);
+    if (d->cin <= 0 || d->h <= 0 || d->w <= 0)
+        return fail(CC3D_ESHAPE, "input cin=%d h=%d w=%d: all must be >= 1", d->cin, d->h, d->w);
+    if (d->max_chunk_t < 1 || d->max_chunk_t > 4096)
+        return fail(CC3D_ESHAPE, "max_chunk_t=%d not in [1, 4096]", d->max_chunk_t);
+    if (!(d->eps >= 0.0f) || d->eps > 1.0f) return fail(CC3D_EINVAL, "eps=%g not in [0, 1]", (double)d->eps);
+    if (d->n_ops < 1 || d->n_ops > CC3D_MAX_OPS)
+        return fail(CC3D_EINVAL, "n_ops=%d not in [1, %d]", d->n_ops, CC3D_MAX_OPS);
+    if (!d->ops) return fail(CC3D_EINVAL, "ops is NULL");
+    const bool bf16 = d->dtype == CC3D_BF16;
+    if (bf16 && d->cin % 8 != 0)
+        return fail(CC3D_ESHAPE, "bf16 input channels %d: must be a multiple of 8", d->cin);
+
+    p->dtype = d->dtype;
+    p->elem = bf16 ? 2 : 4;
+    p->cin = d->cin;
+    p->h = d->h;
+    p->w = d->w;
+    p->max_t = d->max_chunk_t;
+    p->eps = d->eps;
+    p->slots.assign(CC3D_MAX_SLOTS, Slot());
+    Slot& x = p->slots[CC3D_SLOT_X];
+    x.defined = true;
+    x.c = d->cin;
+    x.h = d->h;
+    x.w = d->w;
+    x.tc.mul = 1;
+
+    auto define = [&](int slot, int c, int h, int w, const FrameCount& tc, int op) -> cc3d_status {
+        if (slot == CC3D_SLOT_X || slot == CC3D_SLOT_AUX)
+            return fail(CC3D_EINVAL, "op %d writes slot %d (the input x or the residual argument)", op, slot);
+        Slot& s = p->slots[slot];
+        if (s.defined) {
+            if (s.c != c || s.h != h || s.w != w || !(s.tc == tc))
+                return fail(CC3D_ESHAPE, "op %d writes slot %d as %dx%dx%d but it holds %dx%dx%d", op, slot, c, h,
+                            w, s.c, s.h, s.w);
+            return CC3D_OK;
+        }
+        s.defined = true;
+        s.c = c;
+        s.h = h;
+        s.w = w;
+        s.tc = tc;
+        return CC3D_OK;
+    };
+
+    size_t cache_off = 0;
+    for (int i = 0; i < d->n_ops; ++i) {
+        const cc3d_op_desc& o = d->ops[i];
+        OpRt r;
+        r.kind = o.kind;
+        if (o.kind != CC3D_OP_CONV && o.kind != CC3D_OP_NORM_ACT)
+            return fail(CC3D_EINVAL, "op %d: kind %d not accepted (0 = CONV, 1 = NORM_ACT)", i, o.kind);
+        if (!valid_slot_ref(o.src) || !p->slots[o.src].defined)
+            return fail(CC3D_EINVAL, "op %d: src slot %d is not defined by an earlier op", i, o.src);
+        for (int s : {o.res, o.out, o.act_out})
+            if (s != CC3D_SLOT_NONE && !valid_slot_ref(s))
+                return fail(CC3D_EINVAL, "op %d: slot %d not in [0, %d) or -1", i, s, CC3D_MAX_SLOTS);
+        if (o.out == CC3D_SLOT_NONE && o.act_out == CC3D_SLOT_NONE)
+            return fail(CC3D_EINVAL, "op %d: neither out nor act_out is set", i);
+        if (o.out != CC3D_SLOT_NONE && o.out == o.act_out)
+            return fail(CC3D_EINVAL, "op %d: out and act_out are the same slot %d", i, o.out);
+        if (o.out == o.src || o.act_out == o.src || (o.res != CC3D_SLOT_NONE && (o.res == o.out || o.res == o.act_out)))
+            return fail(CC3D_EINVAL, "op %d: an output slot is also an input slot", i);
+        const Slot src = p->slots[o.src];
+        r.src = o.src;
+        r.res = o.res;
+        r.out = o.out;
+        r.act_out = o.act_out;
+        r.cin = src.c;
+        r.h_in = src.h;
+        r.w_in = src.w;
+        FrameCount tc_out = src.tc;
+        if (o.kind == CC3D_OP_CONV) {
+            if (o.kt < 1 || o.kt > 3 || o.kh < 1 || o.kh > 3 || o.kw < 1 || o.kw > 3 || o.kh % 2 == 0 || o.kw % 2 == 0)
+                return fail(CC3D_ESHAPE, "op %d: kernel %dx%dx%d; accepted: kt 1..3, kh and kw 1 or 3", i, o.kt,
+                            o.kh, o.kw);
+            if ((o.up_s != 1 && o.up_s != 2) || (o.up_t != 1 && o.up_t != 2))
+                return fail(CC3D_ESHAPE, "op %d: up_s=%d up_t=%d; accepted 1 or 2", i, o.up_s, o.up_t);
+            if (o.tpad != CC3D_TPAD_REPLICATE && o.tpad != CC3D_TPAD_ZERO)
+                return fail(CC3D_EINVAL, "op %d: tpad %d not accepted (0 = REPLICATE, 1 = ZERO)", i, o.tpad);
+            if (o.cout < 1 || o.cout > 4096) return fail(CC3D_ESHAPE, "op %d: cout=%d not in [1, 4096]", i, o.cout);
+            if (!o.w) return fail(CC3D_EINVAL, "op %d: weights are NULL", i);
+            if (bf16) {
+                if (r.cin % 8 != 0)
+                    return fail(CC3D_ESHAPE, "op %d: bf16 conv input channels %d: must be a multiple of 8", i, r.cin);
+                if (o.kh != o.kw) return fail(CC3D_ESHAPE, "op %d: bf16 conv needs kh == kw (got %d, %d)", i, o.kh, o.kw);
+                if (!cc3d::bf16_conv_supported(o.cout, o.kh, o.kw, o.up_s))
+                    return fail(CC3D_ESHAPE, "op %d: bf16 conv cout=%d k=%d up_s=%d has no kernel", i, o.cout, o.kh,
+                                o.up_s);
+            }
+            if ((int64_t)r.h_in * o.up_s > 65535 || (int64_t)r.w_in * o.up_s > 65535)
+                return fail(CC3D_ESHAPE, "op %d: output frame %dx%d exceeds 65535", i, r.h_in * o.up_s, r.w_in * o.up_s);
+            r.cout = o.cout;
+            r.kt = o.kt;
+            r.kh = o.kh;
+            r.kw = o.kw;
+            r.up_s = o.up_s;
+            r.up_t = o.up_t;
+            r.tpad = o.tpad;
+            r.h_out = r.h_in * o.up_s;
+            r.w_out = r.w_in * o.up_s;
+            if (o.up_t == 2) tc_out = src.tc.grown();
+            r.cache_off = cache_off;
+            r.cache_bytes = (size_t)(o.kt - 1) * r.h_in * r.w_in * r.cin * p->elem;
+            cache_off += align_up(r.cache_bytes);
+            if (bf16) {
+                cc3d::bf16_conv_tiling(o.cout, &r.ntile, &r.nblocks);
+                r.kchunks = (r.cin + 31) / 32;
+            }
+        } else {
+            r.cout = r.cin;
+            r.h_out = r.h_in;
+            r.w_out = r.w_in;
+            if (r.cin % 4 != 0 || r.cin > 512)
+                return fail(CC3D_ESHAPE, "op %d: NORM_ACT channels %d; accepted a multiple of 4 up to 512", i, r.cin);
+        }
+        if (o.act_out != CC3D_SLOT_NONE) {
+            if (!o.gamma) return fail(CC3D_EINVAL, "op %d: act_out is set but gamma is NULL", i);
+            if (r.cout % 4 != 0 || r.cout > 512)
+                return fail(CC3D_ESHAPE, "op %d: act over %d channels; accepted a multiple of 4 up to 512", i, r.cout);
+        }
+        if (o.res != CC3D_SLOT_NONE) {
+            if (o.res == CC3D_SLOT_AUX && !p->slots[CC3D_SLOT_AUX].defined) {
+                Slot& a = p->slots[CC3D_SLOT_AUX];
+                a.defined = true;
+                a.c = r.cout;
+                a.h = r.h_out;
+                a.w = r.w_out;
+                a.tc = tc_out;
+            }
+            const Slot& rs = p->slots[o.res];
+            if (!rs.defined) return fail(CC3D_EINVAL, "op %d: residual slot %d is not defined", i, o.res);
+            if (rs.c != r.cout || rs.h != r.h_out || rs.w != r.w_out || !(rs.tc == tc_out))
+                return fail(CC3D_ESHAPE, "op %d: residual slot %d is %dx%dx%d, the result is %dx%dx%d", i, o.res, rs.c,
+                            rs.h, rs.w, r.cout, r.h_out, r.w_out);
+            if (o.res == CC3D_SLOT_AUX) p->uses_aux = true;
+        }
+        if (o.out != CC3D_SLOT_NONE) {
+            cc3d_status st = define(o.out, r.cout, r.h_out, r.w_out, tc_out, i);
+            if (st != CC3D_OK) return st;
+        }
+        if (o.act_out != CC3D_SLOT_NONE) {
+            cc3d_status st = define(o.act_out, r.cout, r.h_out, r.w_out, tc_out, i);
+            if (st != CC3D_OK) return st;
+        }
+        // The act is fused into the bf16 conv when one workgroup holds every
+        // output channel; otherwise a norm pass reads the stored result.
+        if (o.kind == CC3D_OP_CONV && o.act_out != CC3D_SLOT_NONE)
+            r.fused_act = bf16 && r.nblocks == 1;
+        p->ops.push_back(r);
+    }
+    if (!p->slots[CC3D_SLOT_Y].defined) return fail(CC3D_EINVAL, "no op writes the output slot %d", CC3D_SLOT_Y);
+    p->state_bytes = cache_off < kAlign ? kAlign : cache_off;
+    return CC3D_OK;
+}
+
+// Slots an unfused act needs: the conv result must be stored somewhere.
+cc3d_status assign_norm_temps(cc3d_plan* p)
+{
+    for (OpRt& r : p->ops) {
+        if (r.kind != CC3D_OP_CONV || r.act_out == CC3D_SLOT_NONE || r.fused_act) continue;
+        if (r.out != CC3D_SLOT_NONE) {
+            r.norm_src = r.out;
+            continue;
+        }
+        int tmp = -1;
+        for (int s = CC3D_MAX_SLOTS - 1; s > CC3D_SLOT_AUX; --s)
+            if (!p->slots[s].defined) {
+                tmp = s;
+                break;
+            }
+        if (tmp < 0) return fail(CC3D_EINVAL, "no free slot left for an unfused act (all %d in use)", CC3D_MAX_SLOTS);
+        Slot& t = p->slots[tmp];
+        const Slot& a = p->slots[r.act_out];
+        t = a;
+        t.defined = true;
+        r.norm_src = tmp;
+    }
+    return CC3D_OK;
+}
+
+cc3d_status hip_status(hipError_t e, const char* what)
+{
+    if (e == hipSuccess) return CC3D_OK;
+    (void)hipGetLastError();
+    return fail(CC3D_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = true;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) {
+            ok = false;
+            prev = -1;
+            return;
+        }
+        if (prev != dev) ok = hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+cc3d_status materialise(const cc3d_stack_desc* d, cc3d_plan* p, hipStream_t stream)
+{
+    Allocator al(p);
+    // intermediate slots
+    for (int s = CC3D_SLOT_AUX + 1; s < CC3D_MAX_SLOTS; ++s) {
+        Slot& sl = p->slots[s];
+        if (!sl.defined) continue;
+        const int64_t tmax = std::max(sl.tc.eval(p->max_t, true), sl.tc.eval(p->max_t, false));
+        sl.bytes = (size_t)tmax * sl.h * sl.w * sl.c * p->elem;
+        cc3d_status st = al.alloc(&sl.ptr, sl.bytes, "an intermediate slot");
+        if (st != CC3D_OK) return st;
+    }
+    for (size_t i = 0; i < p->ops.size(); ++i) {
+        OpRt& r = p->ops[i];
+        const cc3d_op_desc& o = d->ops[i];
+        if (r.kind == CC3D_OP_CONV) {
+            const size_t wbytes = (size_t)r.cout * r.cin * r.kt * r.kh * r.kw * p->elem;
+            if (p->dtype == CC3D_BF16) {
+                const size_t pk = cc3d::bf16_packed_elems(r.cout, r.cin, r.kt, r.kh, r.kw) * 2;
+                cc3d_status st = al.alloc(&r.wpk, pk, "packed weights");
+                if (st != CC3D_OK) return st;
+                st = hip_status(cc3d::launch_pack_bf16(o.w, r.wpk, r.cout, r.cin, r.kt, r.kh, r.kw, stream),
+                                "weight repack launch");
+                if (st != CC3D_OK) return st;
+            } else {
+                cc3d_status st = al.alloc(&r.wpk, wbytes, "weights");
+                if (st != CC3D_OK) return st;
+                st = hip_status(hipMemcpyAsync(r.wpk, o.w, wbytes, hipMemcpyDeviceToDevice, stream), "weight copy");
+                if (st != CC3D_OK) return st;
+            }
+            if (o.bias) {
+                void* b = nullptr;
+                cc3d_status st = al.alloc(&b, (size_t)r.cout * 4, "bias");
+                if (st != CC3D_OK) return st;
+                r.bias = (float*)b;
+                st = hip_status(hipMemcpyAsync(r.bias, o.bias, (size_t)r.cout * 4, hipMemcpyDeviceToDevice, stream),
+                                "bias copy");
+                if (st != CC3D_OK) return st;
+            }
+        }
+        if (r.act_out != CC3D_SLOT_NONE) {
+            void* g = nullptr;
+            cc3d_status st = al.alloc(&g, (size_t)r.cout * 4, "gamma");
+            if (st != CC3D_OK) return st;
+            r.gamma = (float*)g;
+            st = hip_status(hipMemcpyAsync(r.gamma, o.gamma, (size_t)r.cout * 4, hipMemcpyDeviceToDevice, stream),
+                            "gamma copy");
+            if (st != CC3D_OK) return st;
+        }
+    }
+    return hip_status(hipStreamSynchronize(stream), "plan set-up");
+}
+
+std::string conv_kernel_name(const cc3d_plan* p, const OpRt& r);
+
+cc3d_status create_common(const cc3d_stack_desc* d, void* stream, cc3d_plan** out)
+{
+    if (!out) return fail(CC3D_EINVAL, "out is NULL");
+    *out = nullptr;
+    cc3d_plan* p = new (std::nothrow) cc3d_plan();
+    if (!p) return fail(CC3D_ENOMEM, "host allocation of the plan failed");
+    cc3d_status st = build_graph(d, p);
+    if (st != CC3D_OK) {
+        release(p);
+        return st;
+    }
+    st = assign_norm_temps(p);
+    if (st != CC3D_OK) {
+        release(p);
+        return st;
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        release(p);
+        return hip_status(e, "hipGetDevice");
+    }
+    p->device = dev;
+    st = materialise(d, p, (hipStream_t)stream);
+    if (st != CC3D_OK) {
+        release(p);
+        return st;
+    }
+    p->prof.assign(p->ops.size() * 3, cc3d_plan::ProfPart());
+    const char* norm_name = p->dtype == CC3D_BF16 ? "norm_act_bf16" : "norm_act_f32";
+    for (size_t i = 0; i < p->ops.size(); ++i) {
+        const OpRt& r = p->ops[i];
+        if (r.kind == CC3D_OP_CONV) {
+            p->prof[i * 3 + 0].kernel = conv_kernel_name(p, r);
+            if (r.act_out != CC3D_SLOT_NONE && !r.fused_act) p->prof[i * 3 + 1].kernel = norm_name;
+            if (r.kt > 1) p->prof[i * 3 + 2].kernel = "cache_update";
+        } else {
+            p->prof[i * 3 + 0].kernel = norm_name;
+        }
+    }
+    *out = p;
+    clear_err();
+    return CC3D_OK;
+}
+
+bool plan_ok(const cc3d_plan* p) { return p && p->magic == kPlanMagic; }
+
+cc3d_status check_ptr(const void* ptr, int device, const char* what)
+{
+    hipPointerAttribute_t at;
+    hipError_t e = hipPointerGetAttributes(&at, ptr);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(CC3D_EDEVICE, "%s (%p) is not memory known to HIP: %s", what, ptr, hipGetErrorString(e));
+    }
+    if (at.type == hipMemoryTypeHost || at.type == hipMemoryTypeUnregistered)
+        return fail(CC3D_EDEVICE, "%s (%p) is host memory; a device pointer is required", what, ptr);
+    if (at.type == hipMemoryTypeDevice && at.device != device)
+        return fail(CC3D_EDEVICE, "%s (%p) is on device %d, the plan on device %d", what, ptr, at.device, device);
+    return CC3D_OK;
+}
+
+hipEvent_t take_event(const cc3d_plan* p)
+{
+    if (!p->event_pool.empty()) {
+        hipEvent_t e = p->event_pool.back();
+        p->event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    return e;
+}
+
+// Event pair around one launch; inactive when profiling is off or events run out.
+struct ProfScope {
+    const cc3d_plan* p;
+    size_t slot;
+    hipStream_t s;
+    hipEvent_t a = nullptr, b = nullptr;
+    double flops, bytes;
+    ProfScope(const cc3d_plan* plan, size_t op, int part, hipStream_t st, double f, double by)
+        : p(plan), slot(op * 3 + part), s(st), flops(f), bytes(by) {
+        if (!p->prof_on) return;
+        a = take_event(p);
+        b = take_event(p);
+        if (a && b) {
+            (void)hipEventRecord(a, s);
+        } else {
+            if (a) p->event_pool.push_back(a);
+            if (b) p->event_pool.push_back(b);
+            a = b = nullptr;
+        }
+    }
+    ~ProfScope() {
+        if (!a) return;
+        (void)hipEventRecord(b, s);
+        p->prof[slot].pending.push_back({a, b, flops, bytes});
+    }
+};
+
+std::string conv_kernel_name(const cc3d_plan* p, const OpRt& r)
+{
+    char buf[64];
+    if (p->dtype == CC3D_BF16)
+        snprintf(buf, sizeof buf, "conv_bf16_up%d_k%d_n%d", r.up_s, r.kh, r.ntile);
+    else
+        snprintf(buf, sizeof buf, "conv_f32");
+    return buf;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cc3d_version(void) { return CC3D_VERSION; }
+
+const char* cc3d_last_error(void) { return g_err; }
+
+cc3d_status cc3d_stack_plan_create(const cc3d_stack_desc* desc, void* stream, cc3d_plan** out)
+{
+    return create_common(desc, stream, out);
+}
+
+cc3d_status cc3d_plan_create(const cc3d_conv_desc* d, const void* w, const float* bias, const float* gamma,
+                             void* stream, cc3d_plan** out)
+{
+    if (out) *out = nullptr;
+    if (!d) return fail(CC3D_EINVAL, "conv desc is NULL");
+    if (d->epilogue & ~(CC3D_EPI_RESIDUAL | CC3D_EPI_ACT))
+        return fail(CC3D_EINVAL, "epilogue flags 0x%x; accepted CC3D_EPI_RESIDUAL | CC3D_EPI_ACT", d->epilogue);
+    if (d->cin <= 0) return fail(CC3D_ESHAPE, "cin=%d must be >= 1", d->cin);
+    cc3d_op_desc op;
+    memset(&op, 0, sizeof op);
+    op.kind = CC3D_OP_CONV;
+    op.cout = d->cout;
+    op.kt = d->kt;
+    op.kh = d->kh;
+    op.kw = d->kw;
+    op.up_s = d->up_s;
+    op.up_t = d->up_t;
+    op.tpad = d->tpad;
+    op.src = CC3D_SLOT_X;
+    op.res = (d->epilogue & CC3D_EPI_RESIDUAL) ? CC3D_SLOT_AUX : CC3D_SLOT_NONE;
+    op.out = (d->epilogue & CC3D_EPI_ACT) ? CC3D_SLOT_NONE : CC3D_SLOT_Y;
+    op.act_out = (d->epilogue & CC3D_EPI_ACT) ? CC3D_SLOT_Y : CC3D_SLOT_NONE;
+    op.w = w;
+    op.bias = bias;
+    op.gamma = gamma;
+    cc3d_stack_desc sd;
+    sd.dtype = d->dtype;
+    sd.cin = d->cin;
+    sd.h = d->h_in;
+    sd.w = d->w_in;
+    sd.max_chunk_t = d->max_chunk_t;
+    sd.eps = d->eps;
+    sd.n_ops = 1;
+    sd.ops = &op;
+    return create_common(&sd, stream, out);
+}
+
+void cc3d_plan_destroy(cc3d_plan* plan)
+{
+    if (plan_ok(plan)) release(plan);
+}
+
+size_t cc3d_state_bytes(const cc3d_plan* plan) { return plan_ok(plan) ? plan->state_bytes : 0; }
+
+size_t cc3d_plan_device_bytes(const cc3d_plan* plan) { return plan_ok(plan) ? plan->device_bytes : 0; }
+
+cc3d_status cc3d_output_shape(const cc3d_plan* p, int t_chunk, int first, int* c, int* t, int* h, int* w)
+{
+    if (!plan_ok(p)) return fail(CC3D_EINVAL, "plan is NULL or destroyed");
+    if (t_chunk < 1 || t_chunk > p->max_t)
+        return fail(CC3D_ESHAPE, "t_chunk=%d not in [1, %d]", t_chunk, p->max_t);
+    const Slot& y = p->slots[CC3D_SLOT_Y];
+    if (c) *c = y.c;
+    if (t) *t = (int)y.tc.eval(t_chunk, first != 0);
+    if (h) *h = y.h;
+    if (w) *w = y.w;
+    clear_err();
+    return CC3D_OK;
+}
+
+cc3d_status cc3d_reset(const cc3d_plan* p, cc3d_state* state, void* stream)
+{
+    if (!plan_ok(p)) return fail(CC3D_EINVAL, "plan is NULL or destroyed");
+    if (!state) return fail(CC3D_EINVAL, "state is NULL");
+    if (!state->arena) return fail(CC3D_EINVAL, "state arena is NULL");
+    DeviceGuard g(p->device);
+    if (!g.ok) return fail(CC3D_EDEVICE, "cannot make device %d current", p->device);
+    cc3d_status st = check_ptr(state->arena, p->device, "state arena");
+    if (st != CC3D_OK) return st;
+    st = hip_status(cc3d::launch_fill_zero(state->arena, p->state_bytes, (hipStream_t)stream), "arena clear");
+    if (st != CC3D_OK) return st;
+    state->frames_seen = 0;
+    clear_err();
+    return CC3D_OK;
+}
+
+cc3d_status cc3d_forward_chunk(const cc3d_plan* p, const void* x, int t_chunk, const cc3d_state* cache_in,
+                               cc3d_state* cache_out, const void* residual, void* y, void* stream)
+{
+    if (!plan_ok(p)) return fail(CC3D_EINVAL, "plan is NULL or destroyed");
+    if (!x) return fail(CC3D_EINVAL, "x is NULL");
+    if (!y) return fail(CC3D_EINVAL, "y is NULL");
+    if (t_chunk < 1 || t_chunk > p->max_t)
+        return fail(CC3D_ESHAPE, "t_chunk=%d not in [1, %d] (the plan's max_chunk_t)", t_chunk, p->max_t);
+    if (!cache_in || !cache_out) return fail(CC3D_EINVAL, "cache_in or cache_out is NULL");
+    if (!cache_in->arena || !cache_out->arena) return fail(CC3D_EINVAL, "a state arena is NULL");
+    if (cache_in->arena == cache_out->arena || cache_in == cache_out)
+        return fail(CC3D_ESTATE, "cache_in and cache_out share the arena %p; pass two arenas and alternate them",
+                    cache_in->arena);
+    if (cache_in->frames_seen < 0)
+        return fail(CC3D_ESTATE, "cache_in->frames_seen=%lld is negative", (long long)cache_in->frames_seen);
+    if (p->uses_aux && !residual) return fail(CC3D_EINVAL, "this plan adds a residual but residual is NULL");
+    if (!p->uses_aux && residual) return fail(CC3D_EINVAL, "this plan takes no residual; pass NULL");
+    const char* cin_b = (const char*)cache_in->arena;
+    const char* cout_b = (const char*)cache_out->arena;
+    if (cin_b < cout_b + p->state_bytes && cout_b < cin_b + p->state_bytes)
+        return fail(CC3D_ESTATE, "cache_in and cache_out arenas overlap");
+    if (((uintptr_t)x | (uintptr_t)y | (uintptr_t)residual | (uintptr_t)cache_in->arena |
+         (uintptr_t)cache_out->arena) & 15u)
+        return fail(CC3D_EINVAL, "x, y, residual and the state arenas must be 16-byte aligned");
+    const bool first = cache_in->frames_seen == 0;
+    const Slot& ys = p->slots[CC3D_SLOT_Y];
+    const size_t y_bytes = (size_t)ys.tc.eval(t_chunk, first) * ys.h * ys.w * ys.c * p->elem;
+    const size_t x_bytes = (size_t)t_chunk * p->h * p->w * p->cin * p->elem;
+    if ((const char*)x < (const char*)y + y_bytes && (const char*)y < (const char*)x + x_bytes)
+        return fail(CC3D_EINVAL, "x and y overlap");
+
+    DeviceGuard g(p->device);
+    if (!g.ok) return fail(CC3D_EDEVICE, "cannot make device %d current", p->device);
+    cc3d_status st;
+    if ((st = check_ptr(x, p->device, "x")) != CC3D_OK) return st;
+    if ((st = check_ptr(y, p->device, "y")) != CC3D_OK) return st;
+    if ((st = check_ptr(cache_in->arena, p->device, "cache_in arena")) != CC3D_OK) return st;
+    if ((st = check_ptr(cache_out->arena, p->device, "cache_out arena")) != CC3D_OK) return st;
+    if (residual && (st = check_ptr(residual, p->device, "residual")) != CC3D_OK) return st;
+
+    hipStream_t s = (hipStream_t)stream;
+    auto slot_ptr = [&](int slot) -> void* {
+        if (slot == CC3D_SLOT_X) return const_cast<void*>(x);
+        if (slot == CC3D_SLOT_Y) return y;
+        if (slot == CC3D_SLOT_AUX) return const_cast<void*>(residual);
+        if (slot < 0) return nullptr;
+        return p->slots[slot].ptr;
+    };
+    for (const OpRt& r : p->ops) {
+        const Slot& src = p->slots[r.src];
+        const int t_in = (int)src.tc.eval(t_chunk, first);
+        if (r.kind == CC3D_OP_CONV) {
+            cc3d::ConvArgs a;
+            memset(&a, 0, sizeof a);
+            a.z.x = slot_ptr(r.src);
+            a.z.cache = cin_b + r.cache_off;
+            a.z.frame_elems = (int64_t)r.h_in * r.w_in * r.cin;
+            a.z.kt = r.kt;
+            a.z.up_t = r.up_t;
+            a.z.first = first ? 1 : 0;
+            a.z.zero_hist = r.tpad == CC3D_TPAD_ZERO ? 1 : 0;
+            const int t_v = (r.up_t == 2) ? (first ? 2 * t_in - 1 : 2 * t_in) : t_in;
+            a.wpk = r.wpk;
+            a.bias = r.bias;
+            a.res = slot_ptr(r.res);
+            a.gamma = r.gamma;
+            a.eps = p->eps;
+            a.cin = r.cin;
+            a.cout = r.cout;
+            a.kt = r.kt;
+            a.kh = r.kh;
+            a.kw = r.kw;
+            a.h_in = r.h_in;
+            a.w_in = r.w_in;
+            a.up_s = r.up_s;
+            a.h_out = r.h_out;
+            a.w_out = r.w_out;
+            a.t_out = t_v;
+            a.kchunks = r.kchunks;
+            a.ntile = r.ntile;
+            a.nblocks = r.nblocks;
+            if (r.fused_act) {
+                a.out = slot_ptr(r.out);
+                a.act_out = slot_ptr(r.act_out);
+            } else {
+                a.out = r.act_out != CC3D_SLOT_NONE ? slot_ptr(r.norm_src) : slot_ptr(r.out);
+                a.act_out = nullptr;
+            }
+            const size_t oi = (size_t)(&r - p->ops.data());
+            const double vox = (double)t_v * r.h_out * r.w_out;
+            const double fr_in = (double)r.h_in * r.w_in * r.cin * p->elem;
+            const double fr_out = (double)r.h_out * r.w_out * r.cout * p->elem;
+            hipError_t e;
+            {
+                const int nstore = (a.out ? 1 : 0) + (a.act_out ? 1 : 0);
+                const double by = fr_in * (t_in + (first ? 0 : r.kt - 1)) +
+                                  (double)r.cout * r.cin * r.kt * r.kh * r.kw * p->elem +
+                                  t_v * fr_out * (nstore + (a.res ? 1 : 0));
+                ProfScope ps(p, oi, 0, s, 2.0 * r.cin * r.cout * r.kt * r.kh * r.kw * vox, by);
+                e = p->dtype == CC3D_BF16 ? cc3d::launch_conv_bf16(a, s) : cc3d::launch_conv_f32(a, s);
+            }
+            if ((st = hip_status(e, "conv launch")) != CC3D_OK) return st;
+            if (r.act_out != CC3D_SLOT_NONE && !r.fused_act) {
+                cc3d::NormArgs n;
+                memset(&n, 0, sizeof n);
+                n.src = slot_ptr(r.norm_src);
+                n.act_out = slot_ptr(r.act_out);
+                n.gamma = r.gamma;
+                n.eps = p->eps;
+                n.n_pix = (int64_t)t_v * r.h_out * r.w_out;
+                n.c = r.cout;
+                {
+                    ProfScope ps(p, oi, 1, s, 0.0, 2.0 * t_v * fr_out);
+                    e = cc3d::launch_norm_act(n, p->elem, s);
+                }
+                if ((st = hip_status(e, "norm launch")) != CC3D_OK) return st;
+            }
+            if (r.kt > 1) {
+                {
+                    ProfScope ps(p, oi, 2, s, 0.0, 2.0 * (r.kt - 1) * fr_in);
+                    e = cc3d::launch_cache_update(a.z, t_v, (char*)cache_out->arena + r.cache_off, p->elem, s);
+                }
+                if ((st = hip_status(e, "cache update launch")) != CC3D_OK) return st;
+            }
+        } else {
+            cc3d::NormArgs n;
+            memset(&n, 0, sizeof n);
+            n.src = slot_ptr(r.src);
+            n.res = slot_ptr(r.res);
+            n.out = slot_ptr(r.out);
+            n.act_out = slot_ptr(r.act_out);
+            n.gamma = r.gamma;
+            n.eps = p->eps;
+            n.n_pix = (int64_t)t_in * r.h_in * r.w_in;
+            n.c = r.cin;
+            const size_t oi = (size_t)(&r - p->ops.data());
+            const int nmove = 1 + (n.res ? 1 : 0) + (n.out ? 1 : 0) + (n.act_out ? 1 : 0);
+            hipError_t e;
+            {
+                ProfScope ps(p, oi, 0, s, 0.0, (double)n.n_pix * n.c * p->elem * nmove);
+                e = cc3d::launch_norm_act(n, p->elem, s);
+            }
+            if ((st = hip_status(e, "norm launch")) != CC3D_OK) return st;
+        }
+    }
+    cache_out->frames_seen = cache_in->frames_seen + t_chunk;
+    clear_err();
+    return CC3D_OK;
+}
+
+cc3d_status cc3d_profile_enable(cc3d_plan* p, int enable)
+{
+    if (!plan_ok(p)) return fail(CC3D_EINVAL, "plan is NULL or destroyed");
+    DeviceGuard g(p->device);
+    for (auto& part : p->prof) {
+        for (auto& e : part.pending) {
+            (void)hipEventSynchronize(e.stop);
+            p->event_pool.push_back(e.start);
+            p->event_pool.push_back(e.stop);
+        }
+        part.pending.clear();
+        part.launches = 0;
+        part.ms = part.flops = part.bytes = 0.0;
+    }
+    p->prof_on = enable != 0;
+    clear_err();
+    return CC3D_OK;
+}
+
+int cc3d_plan_num_ops(const cc3d_plan* p) { return plan_ok(p) ? (int)p->ops.size() : 0; }
+
+cc3d_status cc3d_profile_read(const cc3d_plan* p, int op, int part, cc3d_op_profile* out)
+{
+    if (!plan_ok(p)) return fail(CC3D_EINVAL, "plan is NULL or destroyed");
+    if (op < 0 || op >= (int)p->ops.size()) return fail(CC3D_EINVAL, "op %d not in [0, %zu)", op, p->ops.size());
+    if (part < 0 || part > 2) return fail(CC3D_EINVAL, "part %d not in [0, 2]", part);
+    if (!out) return fail(CC3D_EINVAL, "out is NULL");
+    DeviceGuard g(p->device);
+    auto& pp = p->prof[(size_t)op * 3 + part];
+    for (auto& e : pp.pending) {
+        hipError_t err = hipEventSynchronize(e.stop);
+        float ms = 0.f;
+        if (err == hipSuccess) err = hipEventElapsedTime(&ms, e.start, e.stop);
+        if (err != hipSuccess) return hip_status(err, "profile event");
+        pp.launches += 1;
+        pp.ms += ms;
+        pp.flops += e.flops;
+        pp.bytes += e.bytes;
+        p->event_pool.push_back(e.start);
+        p->event_pool.push_back(e.stop);
+    }
+    pp.pending.clear();
+    memset(out, 0, sizeof *out);
+    snprintf(out->kernel, sizeof out->kernel, "%s", pp.kernel.c_str());
+    out->launches = pp.launches;
+    out->total_ms = pp.ms;
+    out->flops = pp.flops;
+    out->bytes = pp.bytes;
+    clear_err();
+    return CC3D_OK;
+}
+
+cc3d_status cc3d_to_channels_last(const void* src, void* dst, int c, int t, int h, int w, int eb, void* stream)
+{
+    if (!src || !dst) return fail(CC3D_EINVAL, "src or dst is NULL");
+    if (c < 1 || t < 1 || h < 1 || w < 1) return fail(CC3D_ESHAPE, "c=%d t=%d h=%d w=%d must be >= 1", c, t, h, w);
+    if (eb != 2 && eb != 4) return fail(CC3D_EDTYPE, "elem_bytes=%d; accepted 2 or 4", eb);
+    cc3d_status st = hip_status(cc3d::launch_transpose(src, dst, c, (int64_t)t * h * w, eb, (hipStream_t)stream),
+                                "transpose launch");
+    if (st == CC3D_OK) clear_err();
+    return st;
+}
+
+cc3d_status cc3d_to_channels_first(const void* src, void* dst, int c, int t, int h, int w, int eb, void* stream)
+{
+    if (!src || !dst) return fail(CC3D_EINVAL, "src or dst is NULL");
+    if (c < 1 || t < 1 || h < 1 || w < 1) return fail(CC3D_ESHAPE, "c=%d t=%d h=%d w=%d must be >= 1", c, t, h, w);
+    if (eb != 2 && eb != 4) return fail(CC3D_EDTYPE, "elem_bytes=%d; accepted 2 or 4", eb);
+    cc3d_status st = hip_status(cc3d::launch_transpose(src, dst, (int64_t)t * h * w, c, eb, (hipStream_t)stream),
+                                "transpose launch");
+    if (st == CC3D_OK) clear_err();
+    return st;
+}
+
+}  // extern "C"

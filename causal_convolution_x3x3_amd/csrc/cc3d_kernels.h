@@ -1,0 +1,77 @@
+// Internal interface between the host runtime (cc3d_api.cpp) and the gfx950
+// kernels.  Not installed; the public C ABI is include/cc3d.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cc3d {
+
+// The window a causal conv reads for one chunk: Z = history (kt-1 frames) ||
+// V, where V is the chunk input grown in time (up_t = 2: first chunk V[0]=X[0],
+// V[2j-1]=V[2j]=X[j]; later chunks V[u]=X[u/2]).  History is cache_in's frames,
+// or on the video's first chunk zeros / copies of V[0].  Frames are at the
+// input's own (pre-spatial-upsample) size.
+struct ZWindow {
+    const void* x;        // [T_in][H][W][C] chunk input
+    const void* cache;    // [kt-1][H][W][C] cache_in frames (unused when first)
+    int64_t frame_elems;  // H*W*C
+    int kt;
+    int up_t;
+    int first;            // 1 on the video's first chunk
+    int zero_hist;        // first-chunk history: 1 = zeros, 0 = copies of V[0]
+};
+
+struct ConvArgs {
+    ZWindow z;
+    const void* wpk;      // packed weights (layout depends on the kernel family)
+    const float* bias;    // [cout] or null
+    const void* res;      // [t_out][h_out][w_out][cout] or null
+    void* out;            // result v = conv + bias (+ res), or null
+    void* act_out;        // SiLU(RMSNorm(v)), or null (only when fused)
+    const float* gamma;   // [cout]
+    float eps;
+    int cin, cout, kt, kh, kw;
+    int h_in, w_in, up_s, h_out, w_out, t_out;
+    int kchunks;          // bf16: ceil(cin / 32)
+    int ntile, nblocks;   // bf16: output channels per workgroup, number of such blocks
+};
+
+struct NormArgs {
+    const void* src;      // [n_pix][c]
+    const void* res;      // [n_pix][c] or null
+    void* out;            // v = src (+ res) or null
+    void* act_out;        // SiLU(RMSNorm(v)) or null
+    const float* gamma;
+    float eps;
+    int64_t n_pix;
+    int c;
+};
+
+// bf16 implicit-GEMM conv on MFMA.  Returns hipErrorInvalidValue for a shape
+// the kernel family does not take (the host checks bf16_conv_supported first).
+bool bf16_conv_supported(int cout, int kh, int kw, int up_s);
+void bf16_conv_tiling(int cout, int* ntile, int* nblocks);
+hipError_t launch_conv_bf16(const ConvArgs& a, hipStream_t s);
+// Repack [cout][cin][kt][kh][kw] bf16 weights into the MFMA operand blocks.
+size_t bf16_packed_elems(int cout, int cin, int kt, int kh, int kw);
+hipError_t launch_pack_bf16(const void* w, void* wpk, int cout, int cin, int kt, int kh, int kw,
+                            hipStream_t s);
+
+// fp32 direct conv (weights used in PyTorch order, copied by the host).
+hipError_t launch_conv_f32(const ConvArgs& a, hipStream_t s);
+
+// v = src (+res); out = v; act_out = SiLU(RMSNorm(v)).  elem_bytes 2 (bf16) or 4.
+hipError_t launch_norm_act(const NormArgs& a, int elem_bytes, hipStream_t s);
+
+// cache_out[i] = Z[t_v + i], i < kt-1.
+hipError_t launch_cache_update(const ZWindow& z, int t_v, void* dst, int elem_bytes,
+                               hipStream_t s);
+
+hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t s);
+
+// dst[c][r] = src[r][c] for an rows x cols matrix of elem_bytes elements.
+hipError_t launch_transpose(const void* src, void* dst, int64_t rows, int64_t cols,
+                            int elem_bytes, hipStream_t s);
+
+}  // namespace cc3d

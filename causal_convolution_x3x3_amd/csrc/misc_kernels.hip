@@ -1,0 +1,273 @@
+// Memory-bound kernels of the decode path: the fp32 direct conv (small fp32
+// layers), the standalone channel RMSNorm + SiLU (+ residual) epilogue, the
+// causal cache update, zero fill and the channels-first/last transposes.
+#include "cc3d_kernels.h"
+
+namespace cc3d {
+namespace {
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Frame zi of the causal window (see ZWindow), as bytes; null = a zero frame.
+__device__ __forceinline__ const char* zframe_bytes(const ZWindow& z, int zi, int eb)
+{
+    const int hist = z.kt - 1;
+    const int64_t fb = z.frame_elems * eb;
+    if (zi < hist) {
+        if (!z.first) return (const char*)z.cache + zi * fb;
+        return z.zero_hist ? nullptr : (const char*)z.x;
+    }
+    const int u = zi - hist;
+    const int src = (z.up_t == 2) ? ((u + z.first) >> 1) : u;
+    return (const char*)z.x + src * fb;
+}
+
+// ------------------------------------------------------------ fp32 conv ----
+// One thread per output element (channel fastest, so neighbouring threads share
+// their input reads); fp32 accumulation over taps, then channels.
+__global__ __launch_bounds__(256) void conv_f32_kernel(ConvArgs a)
+{
+    const int64_t total = (int64_t)a.t_out * a.h_out * a.w_out * a.cout;
+    const int ph = (a.kh - 1) / 2, pw = (a.kw - 1) / 2;
+    const int kvol = a.kt * a.kh * a.kw;
+    const float* w = (const float*)a.wpk;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int o = (int)(idx % a.cout);
+        int64_t p = idx / a.cout;
+        const int x = (int)(p % a.w_out);
+        p /= a.w_out;
+        const int y = (int)(p % a.h_out);
+        const int t = (int)(p / a.h_out);
+        float s = 0.f;
+        for (int ta = 0; ta < a.kt; ++ta) {
+            const float* fp = (const float*)zframe_bytes(a.z, t + ta, 4);
+            if (!fp) continue;
+            for (int tb = 0; tb < a.kh; ++tb) {
+                const int yu = y + tb - ph;
+                if (yu < 0 || yu >= a.h_out) continue;
+                const int sy = yu / a.up_s;
+                for (int td = 0; td < a.kw; ++td) {
+                    const int xu = x + td - pw;
+                    if (xu < 0 || xu >= a.w_out) continue;
+                    const int sx = xu / a.up_s;
+                    const float* px = fp + ((int64_t)sy * a.w_in + sx) * a.cin;
+                    const float* wp = w + (int64_t)o * a.cin * kvol + (ta * a.kh + tb) * a.kw + td;
+                    for (int c = 0; c < a.cin; ++c) s = fmaf(px[c], wp[(int64_t)c * kvol], s);
+                }
+            }
+        }
+        if (a.bias) s += a.bias[o];
+        if (a.res) s += ((const float*)a.res)[idx];
+        ((float*)a.out)[idx] = s;
+    }
+}
+
+// -------------------------------------------------------------- norm_act ---
+// 32 lanes per pixel; lane u holds channel units u, u+32, ... of 4 channels.
+constexpr int NORM_MAXU = 4;  // up to 512 channels
+
+template <typename T>
+struct Vec4;
+template <>
+struct Vec4<uint16_t> {
+    static __device__ __forceinline__ void load(const void* p, int64_t e, float v[4]) {
+        const uint2 r = *(const uint2*)((const uint16_t*)p + e);
+        v[0] = bf2f((uint16_t)(r.x & 0xffffu));
+        v[1] = bf2f((uint16_t)(r.x >> 16));
+        v[2] = bf2f((uint16_t)(r.y & 0xffffu));
+        v[3] = bf2f((uint16_t)(r.y >> 16));
+    }
+    static __device__ __forceinline__ void round(float v[4]) {
+        for (int i = 0; i < 4; ++i) v[i] = bf2f(f2bf(v[i]));
+    }
+    static __device__ __forceinline__ void store(void* p, int64_t e, const float v[4]) {
+        uint2 r;
+        r.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+        r.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+        *(uint2*)((uint16_t*)p + e) = r;
+    }
+};
+template <>
+struct Vec4<float> {
+    static __device__ __forceinline__ void load(const void* p, int64_t e, float v[4]) {
+        const float4 r = *(const float4*)((const float*)p + e);
+        v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+    }
+    static __device__ __forceinline__ void round(float*) {}
+    static __device__ __forceinline__ void store(void* p, int64_t e, const float v[4]) {
+        *(float4*)((float*)p + e) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void norm_act_kernel(NormArgs a)
+{
+    const int l32 = threadIdx.x & 31;
+    const int64_t pix = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 5;
+    const bool live = pix < a.n_pix;
+    const int nunits = a.c >> 2;
+    float v[NORM_MAXU][4];
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < NORM_MAXU; ++u) {
+        const int unit = l32 + 32 * u;
+        if (live && unit < nunits) {
+            const int64_t e = pix * a.c + unit * 4;
+            Vec4<T>::load(a.src, e, v[u]);
+            if (a.res) {
+                float r[4];
+                Vec4<T>::load(a.res, e, r);
+                for (int i = 0; i < 4; ++i) v[u][i] += r[i];
+                Vec4<T>::round(v[u]);
+            }
+            for (int i = 0; i < 4; ++i) ss += v[u][i] * v[u][i];
+        }
+    }
+    ss += __shfl_xor(ss, 1, 32);
+    ss += __shfl_xor(ss, 2, 32);
+    ss += __shfl_xor(ss, 4, 32);
+    ss += __shfl_xor(ss, 8, 32);
+    ss += __shfl_xor(ss, 16, 32);
+    const float inv = 1.0f / sqrtf(ss / (float)a.c + a.eps);
+#pragma unroll
+    for (int u = 0; u < NORM_MAXU; ++u) {
+        const int unit = l32 + 32 * u;
+        if (live && unit < nunits) {
+            const int64_t e = pix * a.c + unit * 4;
+            if (a.out) Vec4<T>::store(a.out, e, v[u]);
+            if (a.act_out) {
+                float o[4];
+                for (int i = 0; i < 4; ++i) {
+                    const float z = a.gamma[unit * 4 + i] * v[u][i] * inv;
+                    o[i] = z / (1.0f + expf(-z));
+                }
+                Vec4<T>::store(a.act_out, e, o);
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------- cache update --
+template <typename V>
+__global__ __launch_bounds__(256) void cache_update_kernel(ZWindow z, int t_v, void* dst, int eb)
+{
+    const int i = blockIdx.y;
+    const int64_t n = z.frame_elems * eb / (int64_t)sizeof(V);
+    const V* src = (const V*)zframe_bytes(z, t_v + i, eb);
+    V* d = (V*)dst + i * n;
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n;
+         k += (int64_t)gridDim.x * blockDim.x)
+        d[k] = src ? src[k] : V{};
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint4* d, int64_t n16, unsigned char* tail,
+                                                        int ntail)
+{
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n16;
+         k += (int64_t)gridDim.x * blockDim.x)
+        d[k] = make_uint4(0u, 0u, 0u, 0u);
+    if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+// -------------------------------------------------------------- transpose --
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* src, T* dst, int64_t rows,
+                                                        int64_t cols)
+{
+    __shared__ T tile[32][33];
+    const int64_t tiles_c = (cols + 31) / 32;
+    const int64_t ntiles = tiles_c * ((rows + 31) / 32);
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+    for (int64_t tb = blockIdx.x; tb < ntiles; tb += gridDim.x) {
+        const int64_t r0 = (tb / tiles_c) * 32, c0 = (tb % tiles_c) * 32;
+        __syncthreads();
+        for (int j = ty; j < 32; j += 8) {
+            const int64_t r = r0 + j, c = c0 + tx;
+            if (r < rows && c < cols) tile[j][tx] = src[r * cols + c];
+        }
+        __syncthreads();
+        for (int j = ty; j < 32; j += 8) {
+            const int64_t c = c0 + j, r = r0 + tx;
+            if (r < rows && c < cols) dst[c * rows + r] = tile[tx][j];
+        }
+    }
+}
+
+int grid_for(int64_t n, int per_block = 256, int cap = 1 << 20)
+{
+    int64_t b = (n + per_block - 1) / per_block;
+    if (b < 1) b = 1;
+    if (b > cap) b = cap;
+    return (int)b;
+}
+
+}  // namespace
+
+hipError_t launch_conv_f32(const ConvArgs& a, hipStream_t s)
+{
+    const int64_t total = (int64_t)a.t_out * a.h_out * a.w_out * a.cout;
+    hipLaunchKernelGGL(conv_f32_kernel, dim3(grid_for(total)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_act(const NormArgs& a, int elem_bytes, hipStream_t s)
+{
+    if (a.c % 4 != 0 || a.c > 4 * 32 * NORM_MAXU) return hipErrorInvalidValue;
+    const int64_t threads = a.n_pix * 32;
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (elem_bytes == 2)
+        hipLaunchKernelGGL(norm_act_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(norm_act_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_cache_update(const ZWindow& z, int t_v, void* dst, int eb, hipStream_t s)
+{
+    if (z.kt <= 1) return hipSuccess;
+    const int64_t bytes = z.frame_elems * eb;
+    if (bytes % 16 == 0) {
+        hipLaunchKernelGGL(cache_update_kernel<uint4>, dim3(grid_for(bytes / 16, 256, 4096), z.kt - 1),
+                           dim3(256), 0, s, z, t_v, dst, eb);
+    } else {
+        hipLaunchKernelGGL(cache_update_kernel<uint16_t>, dim3(grid_for(bytes / 2, 256, 4096), z.kt - 1),
+                           dim3(256), 0, s, z, t_v, dst, eb);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* dst, size_t bytes, hipStream_t s)
+{
+    const int64_t n16 = (int64_t)(bytes / 16);
+    const int ntail = (int)(bytes % 16);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n16, 256, 8192)), dim3(256), 0, s, (uint4*)dst,
+                       n16, (unsigned char*)dst + n16 * 16, ntail);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose(const void* src, void* dst, int64_t rows, int64_t cols, int eb,
+                            hipStream_t s)
+{
+    const int64_t ntiles = ((cols + 31) / 32) * ((rows + 31) / 32);
+    const dim3 grid((unsigned)(ntiles < (1 << 20) ? (ntiles > 0 ? ntiles : 1) : (1 << 20)));
+    if (eb == 2)
+        hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)src,
+                           (uint16_t*)dst, rows, cols);
+    else if (eb == 4)
+        hipLaunchKernelGGL(transpose_kernel<uint32_t>, grid, dim3(256), 0, s, (const uint32_t*)src,
+                           (uint32_t*)dst, rows, cols);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace cc3d

@@ -1,0 +1,196 @@
+"""Thin torch-facing wrappers over the C ABI: torch supplies device memory and the
+stream, the library does every step of the path.
+
+Activations are channels-last: a chunk is a [T, H, W, C] tensor (bf16 or fp32)
+on the plan's device.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import torch
+
+from . import capi as C
+
+_DT = {torch.bfloat16: C.BF16, torch.float32: C.F32}
+_TD = {C.BF16: torch.bfloat16, C.F32: torch.float32}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to the library must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class State:
+    """One causal state arena (device bytes) and its frame counter."""
+
+    def __init__(self, nbytes: int, device):
+        self.arena = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        self.frames_seen = 0
+
+    def _c(self) -> C.State:
+        return C.State(ctypes.c_void_p(self.arena.data_ptr()), self.frames_seen)
+
+    def copy_(self, other: "State") -> "State":
+        """Checkpoint/restore: copy another state's arena and counter."""
+        self.arena.copy_(other.arena)
+        self.frames_seen = other.frames_seen
+        return self
+
+
+@dataclass
+class Op:
+    """One op of a stack (see cc3d_op_desc)."""
+    kind: int = C.OP_CONV
+    cout: int = 0
+    k: tuple = (3, 3, 3)
+    up_s: int = 1
+    up_t: int = 1
+    tpad: int = C.TPAD_REPLICATE
+    src: int = C.SLOT_X
+    res: int = C.SLOT_NONE
+    out: int = C.SLOT_NONE
+    act_out: int = C.SLOT_NONE
+    w: Optional[torch.Tensor] = None
+    bias: Optional[torch.Tensor] = None
+    gamma: Optional[torch.Tensor] = None
+    name: str = field(default="")
+
+
+class Plan:
+    """A created plan (single conv or stack) with its forward/reset calls."""
+
+    def __init__(self, handle: ctypes.c_void_p, dtype: int, device):
+        self._h = handle
+        self.dtype = dtype
+        self.device = device
+        L = C.lib()
+        self.state_bytes = int(L.cc3d_state_bytes(self._h))
+        self.device_bytes = int(L.cc3d_plan_device_bytes(self._h))
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            try:
+                torch.cuda.synchronize(self.device)
+            except Exception:
+                pass
+            C.lib().cc3d_plan_destroy(h)
+            self._h = None
+
+    def new_state(self) -> State:
+        return State(self.state_bytes, self.device)
+
+    def output_shape(self, t_chunk: int, first: bool):
+        c, t, h, w = (ctypes.c_int() for _ in range(4))
+        C.check(C.lib().cc3d_output_shape(self._h, t_chunk, int(first), ctypes.byref(c), ctypes.byref(t),
+                                          ctypes.byref(h), ctypes.byref(w)), "cc3d_output_shape")
+        return (t.value, h.value, w.value, c.value)
+
+    def reset(self, state: State, stream=None):
+        cs = state._c()
+        C.check(C.lib().cc3d_reset(self._h, ctypes.byref(cs), _stream(stream)), "cc3d_reset")
+        state.frames_seen = cs.frames_seen
+
+    def forward_chunk(self, x: torch.Tensor, cache_in: State, cache_out: State,
+                      residual: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+        t_chunk = x.shape[0]
+        if y is None:
+            shape = self.output_shape(t_chunk, cache_in.frames_seen == 0)
+            y = torch.empty(shape, dtype=_TD[self.dtype], device=self.device)
+        ci, co = cache_in._c(), cache_out._c()
+        C.check(C.lib().cc3d_forward_chunk(self._h, _ptr(x), t_chunk, ctypes.byref(ci), ctypes.byref(co),
+                                           _ptr(residual), _ptr(y), _stream(stream)), "cc3d_forward_chunk")
+        cache_out.frames_seen = co.frames_seen
+        return y
+
+
+def conv_plan(w: torch.Tensor, h_in: int, w_in: int, *, bias=None, gamma=None, up_s=1, up_t=1,
+              max_chunk_t=8, tpad=C.TPAD_REPLICATE, residual=False, act=False, eps=1e-6,
+              stream=None) -> Plan:
+    """Plan for one causal conv; w is [Cout][Cin][kt][kh][kw] on the GPU (bf16 or fp32)."""
+    cout, cin, kt, kh, kw = w.shape
+    d = C.ConvDesc(cin=cin, cout=cout, kt=kt, kh=kh, kw=kw, h_in=h_in, w_in=w_in, up_s=up_s, up_t=up_t,
+                   max_chunk_t=max_chunk_t, dtype=_DT[w.dtype], tpad=tpad,
+                   epilogue=(C.EPI_RESIDUAL if residual else 0) | (C.EPI_ACT if act else 0), eps=eps)
+    h = ctypes.c_void_p()
+    with torch.cuda.device(w.device):
+        C.check(C.lib().cc3d_plan_create(ctypes.byref(d), _ptr(w), _ptr(bias), _ptr(gamma), _stream(stream),
+                                         ctypes.byref(h)), "cc3d_plan_create")
+    return Plan(h, d.dtype, w.device)
+
+
+def stack_plan(ops: List[Op], cin: int, h: int, w: int, *, dtype=torch.bfloat16, max_chunk_t=8,
+               eps=1e-6, device=None, stream=None) -> Plan:
+    arr = (C.OpDesc * len(ops))()
+    for i, o in enumerate(ops):
+        kt, kh, kw = o.k
+        arr[i] = C.OpDesc(kind=o.kind, cout=o.cout, kt=kt, kh=kh, kw=kw, up_s=o.up_s, up_t=o.up_t,
+                          tpad=o.tpad, src=o.src, res=o.res, out=o.out, act_out=o.act_out,
+                          w=_ptr(o.w), bias=_ptr(o.bias), gamma=_ptr(o.gamma))
+    d = C.StackDesc(dtype=_DT[dtype], cin=cin, h=h, w=w, max_chunk_t=max_chunk_t, eps=eps, n_ops=len(ops),
+                    ops=arr)
+    if device is None:
+        device = next((o.w.device for o in ops if o.w is not None), torch.device("cuda", 0))
+    hnd = ctypes.c_void_p()
+    with torch.cuda.device(device):
+        C.check(C.lib().cc3d_stack_plan_create(ctypes.byref(d), _stream(stream), ctypes.byref(hnd)),
+                "cc3d_stack_plan_create")
+    return Plan(hnd, d.dtype, device)
+
+
+class Stream:
+    """A video being decoded: a plan plus two state arenas used alternately
+    (the pages' ping-pong state buffers)."""
+
+    def __init__(self, plan: Plan, stream=None):
+        self.plan = plan
+        self.states = [plan.new_state(), plan.new_state()]
+        self.cur = 0
+        self.stream = stream
+        self.reset()
+
+    def reset(self):
+        for s in self.states:
+            self.plan.reset(s, self.stream)
+        self.cur = 0
+
+    @property
+    def frames_seen(self) -> int:
+        return self.states[self.cur].frames_seen
+
+    def step(self, x: torch.Tensor, residual=None, y=None) -> torch.Tensor:
+        a, b = self.states[self.cur], self.states[1 - self.cur]
+        out = self.plan.forward_chunk(x, a, b, residual=residual, y=y, stream=self.stream)
+        self.cur = 1 - self.cur
+        return out
+
+
+def to_channels_last(x_cthw: torch.Tensor, stream=None) -> torch.Tensor:
+    c, t, h, w = x_cthw.shape
+    out = torch.empty((t, h, w, c), dtype=x_cthw.dtype, device=x_cthw.device)
+    C.check(C.lib().cc3d_to_channels_last(_ptr(x_cthw), _ptr(out), c, t, h, w, x_cthw.element_size(),
+                                          _stream(stream)), "cc3d_to_channels_last")
+    return out
+
+
+def to_channels_first(x_thwc: torch.Tensor, stream=None) -> torch.Tensor:
+    t, h, w, c = x_thwc.shape
+    out = torch.empty((c, t, h, w), dtype=x_thwc.dtype, device=x_thwc.device)
+    C.check(C.lib().cc3d_to_channels_first(_ptr(x_thwc), _ptr(out), c, t, h, w, x_thwc.element_size(),
+                                           _stream(stream)), "cc3d_to_channels_first")
+    return out

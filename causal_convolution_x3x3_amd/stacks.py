@@ -1,0 +1,97 @@
+"""Op lists for the decoder blocks run by the stack runner.
+
+The pages name the decoder's pieces -- per-layer causal state, nearest 2x
+upsampling followed by a spatial conv, growth of the frame count (LightX2V blog,
+"SwiftVR Inference Optimization ...", sections "From Pixels to Latents and Back",
+"TemporalGrow: Compute Before Spatial Upsampling") -- but no layer list; these
+are the synthetic blocks built from them.  act = SiLU(RMSNorm(.)) is always
+produced by the op that writes its input (fused into the conv when one
+workgroup holds all output channels), and is computed once at the lower
+resolution when an upsample follows: it works per position, so it commutes with
+nearest upsampling.
+
+Parameter dicts hold device tensors: ``w`` [Cout][Cin][kt][kh][kw], ``b``
+[Cout] float32 or None, ``g`` [Cin] float32 (the RMSNorm gain of the conv's
+input) or None.
+"""
+from __future__ import annotations
+
+from typing import Dict, List
+
+from . import capi as C
+from .plan import Op
+
+X, Y = C.SLOT_X, C.SLOT_Y
+NONE = C.SLOT_NONE
+
+
+def resblock_ops(c: int, p1: Dict, p2: Dict, src: int = X, out: int = Y, first_tmp: int = 3,
+                 next_gain=None, act_out: int = NONE) -> List[Op]:
+    """y = x + conv2(act2(conv1(act1(x)))); x in ``src``.  Uses slots
+    first_tmp (act1 x) and first_tmp+1 (act2 of conv1).  With ``next_gain`` the
+    last conv also stores act(y) for what follows into ``act_out``."""
+    a1, a2 = first_tmp, first_tmp + 1
+    return [
+        Op(kind=C.OP_NORM_ACT, src=src, act_out=a1, gamma=p1["g"], name="rb.act1"),
+        Op(cout=c, w=p1["w"], bias=p1.get("b"), src=a1, act_out=a2, gamma=p2["g"], name="rb.conv1"),
+        Op(cout=c, w=p2["w"], bias=p2.get("b"), src=a2, res=src, out=out,
+           act_out=act_out if next_gain is not None else NONE, gamma=next_gain, name="rb.conv2"),
+    ]
+
+
+def upstage_ops(c_mid: int, c_out: int, p1: Dict, p2: Dict) -> List[Op]:
+    """conv2(act(conv1(nearest_up2(x)))) -- conv1 reads the upsampled input
+    through its operand load; its epilogue stores act for conv2."""
+    return [
+        Op(cout=c_mid, w=p1["w"], bias=p1.get("b"), up_s=2, src=X, act_out=3, gamma=p2["g"], name="up.conv1"),
+        Op(cout=c_out, w=p2["w"], bias=p2.get("b"), src=3, out=Y, name="up.conv2"),
+    ]
+
+
+DECODER_STAGES = ((384, 2), (192, 2), (96, 1))
+
+
+def decoder_ops(params: Dict[str, Dict], stages=DECODER_STAGES, c_out: int = 3) -> List[Op]:
+    """conv_in -> per stage [nearest up (2x space, 2x time on non-first frames
+    when the stage's factor is 2) + conv, two residual blocks] -> head (act at low
+    resolution, nearest 2x, conv to c_out).
+
+    Slots per stage s (base = 3 + 5 s): raw A, raw B (the residual stream
+    alternates between them), act A, act B, inner act.  Slot 3 + 5*len(stages)
+    holds conv_in's output."""
+    ops: List[Op] = []
+    h_in = 3 + 5 * len(stages)
+    ops.append(Op(cout=stages[0][0], w=params["conv_in"]["w"], bias=params["conv_in"].get("b"), src=X,
+                  out=h_in, name="conv_in"))
+    prev_raw = h_in
+    for si, (c, up_t) in enumerate(stages):
+        base = 3 + 5 * si
+        raw = [base, base + 1]
+        act = [base + 2, base + 3]
+        inner = base + 4
+        rb = [(params["s%d.rb%d.c1" % (si, r)], params["s%d.rb%d.c2" % (si, r)]) for r in range(2)]
+        up = params["s%d.up" % si]
+        # up conv: stores the raw result (residual of block 0) and act for block 0's conv1
+        ops.append(Op(cout=c, w=up["w"], bias=up.get("b"), up_s=2, up_t=up_t, src=prev_raw, out=raw[0],
+                      act_out=act[0], gamma=rb[0][0]["g"], name="s%d.up" % si))
+        cur = 0
+        for r in range(2):
+            p1, p2 = rb[r]
+            ops.append(Op(cout=c, w=p1["w"], bias=p1.get("b"), src=act[cur], act_out=inner, gamma=p2["g"],
+                          name="s%d.rb%d.c1" % (si, r)))
+            last_of_stack = si == len(stages) - 1 and r == 1
+            if r == 0:
+                nxt_g = rb[1][0]["g"]
+            elif last_of_stack:
+                nxt_g = params["head"]["g"]
+            else:
+                nxt_g = None  # the next stage's up conv reads the raw stream
+            ops.append(Op(cout=c, w=p2["w"], bias=p2.get("b"), src=inner, res=raw[cur], out=raw[1 - cur],
+                          act_out=act[1 - cur] if nxt_g is not None else NONE, gamma=nxt_g,
+                          name="s%d.rb%d.c2" % (si, r)))
+            cur = 1 - cur
+        prev_raw = raw[cur]
+        last_act = act[cur]
+    head = params["head"]
+    ops.append(Op(cout=c_out, w=head["w"], bias=head.get("b"), up_s=2, src=last_act, out=Y, name="head"))
+    return ops

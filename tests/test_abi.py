@@ -1,0 +1,119 @@
+"""C-ABI library checks that need no GPU: it loads, exports every function
+include/cc3d.h declares, and rejects bad arguments before any device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from causal_convolution_x3x3_amd import capi as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "cc3d.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(cc3d_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    L = C.lib()
+    declared = _header_functions()
+    assert declared, "no declarations parsed"
+    assert sorted(declared) == sorted(C.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.cc3d_version() == 100
+
+
+def _conv_desc(**kw):
+    d = dict(cin=16, cout=16, kt=3, kh=3, kw=3, h_in=8, w_in=8, up_s=1, up_t=1, max_chunk_t=4,
+             dtype=C.BF16, tpad=C.TPAD_REPLICATE, epilogue=0, eps=1e-6)
+    d.update(kw)
+    return C.ConvDesc(**d)
+
+
+DUMMY = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(kt=0), C.ESHAPE), (dict(kt=4), C.ESHAPE), (dict(kh=2), C.ESHAPE), (dict(up_s=3), C.ESHAPE),
+    (dict(up_t=0), C.ESHAPE), (dict(dtype=7), C.EDTYPE), (dict(tpad=5), C.EINVAL), (dict(cin=12), C.ESHAPE),
+    (dict(max_chunk_t=0), C.ESHAPE), (dict(h_in=0), C.ESHAPE), (dict(cout=0), C.ESHAPE),
+    (dict(epilogue=8), C.EINVAL), (dict(kh=3, kw=1), C.ESHAPE), (dict(eps=-1.0), C.EINVAL),
+])
+def test_plan_create_rejects_bad_descriptor(bad, status):
+    L = C.lib()
+    out = ctypes.c_void_p(123)
+    st = L.cc3d_plan_create(ctypes.byref(_conv_desc(**bad)), DUMMY, None, None, None, ctypes.byref(out))
+    assert st == status, C.last_error()
+    assert out.value is None
+    assert C.last_error()  # a message naming the value
+
+
+def test_plan_create_null_arguments():
+    L = C.lib()
+    out = ctypes.c_void_p()
+    assert L.cc3d_plan_create(None, DUMMY, None, None, None, ctypes.byref(out)) == C.EINVAL
+    assert L.cc3d_plan_create(ctypes.byref(_conv_desc()), None, None, None, None, ctypes.byref(out)) == C.EINVAL
+    assert "weights" in C.last_error()
+    # act epilogue without gamma
+    assert L.cc3d_plan_create(ctypes.byref(_conv_desc(epilogue=C.EPI_ACT)), DUMMY, None, None, None,
+                              ctypes.byref(out)) == C.EINVAL
+    assert "gamma" in C.last_error()
+
+
+def _stack(ops, **kw):
+    arr = (C.OpDesc * len(ops))(*ops)
+    d = dict(dtype=C.BF16, cin=16, h=8, w=8, max_chunk_t=4, eps=1e-6, n_ops=len(ops), ops=arr)
+    d.update(kw)
+    return C.StackDesc(**d), arr
+
+
+def _conv_op(**kw):
+    d = dict(kind=C.OP_CONV, cout=16, kt=3, kh=3, kw=3, up_s=1, up_t=1, tpad=0, src=C.SLOT_X,
+             res=C.SLOT_NONE, out=C.SLOT_Y, act_out=C.SLOT_NONE, w=DUMMY, bias=None, gamma=None)
+    d.update(kw)
+    return C.OpDesc(**d)
+
+
+@pytest.mark.parametrize("ops,status,needle", [
+    ([_conv_op(src=5)], C.EINVAL, "src slot"),
+    ([_conv_op(out=C.SLOT_NONE)], C.EINVAL, "neither"),
+    ([_conv_op(out=3)], C.EINVAL, "output slot"),
+    ([_conv_op(out=C.SLOT_X)], C.EINVAL, "output slot"),
+    ([_conv_op(res=C.SLOT_Y)], C.EINVAL, "also an input"),
+    ([_conv_op(out=3), _conv_op(src=3, res=C.SLOT_X, cout=8)], C.ESHAPE, "residual"),
+    ([_conv_op(out=3), _conv_op(src=3, out=3)], C.EINVAL, "output slot is also"),
+    ([_conv_op(kind=9)], C.EINVAL, "kind"),
+    ([_conv_op(act_out=3, out=C.SLOT_Y)], C.EINVAL, "gamma"),
+    ([_conv_op(out=3, cout=12), _conv_op(src=3)], C.ESHAPE, "multiple of 8"),
+])
+def test_stack_plan_rejects_bad_wiring(ops, status, needle):
+    L = C.lib()
+    d, keep = _stack(ops)
+    out = ctypes.c_void_p()
+    st = L.cc3d_stack_plan_create(ctypes.byref(d), None, ctypes.byref(out))
+    assert st == status, C.last_error()
+    assert needle in C.last_error(), C.last_error()
+    assert out.value is None
+
+
+def test_calls_on_null_plan():
+    L = C.lib()
+    s1 = C.State(DUMMY, 0)
+    s2 = C.State(ctypes.c_void_p(0x2000), 0)
+    assert L.cc3d_forward_chunk(None, DUMMY, 1, ctypes.byref(s1), ctypes.byref(s2), None, DUMMY, None) == C.EINVAL
+    assert L.cc3d_reset(None, ctypes.byref(s1), None) == C.EINVAL
+    assert L.cc3d_state_bytes(None) == 0
+    c = ctypes.c_int()
+    assert L.cc3d_output_shape(None, 1, 1, ctypes.byref(c), None, None, None) == C.EINVAL
+    L.cc3d_plan_destroy(None)  # accepted
+
+
+def test_transpose_argument_checks():
+    L = C.lib()
+    assert L.cc3d_to_channels_last(None, DUMMY, 1, 1, 1, 1, 2, None) == C.EINVAL
+    assert L.cc3d_to_channels_last(DUMMY, DUMMY, 0, 1, 1, 1, 2, None) == C.ESHAPE
+    assert L.cc3d_to_channels_first(DUMMY, DUMMY, 1, 1, 1, 1, 3, None) == C.EDTYPE

@@ -1,0 +1,263 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs, at sizes the oracle finishes in seconds that still span
+several tiles and ragged tails."""
+import numpy as np
+import pytest
+import torch
+
+from causal_convolution_x3x3_amd import capi as C
+from causal_convolution_x3x3_amd import plan as P
+from causal_convolution_x3x3_amd import stacks as S
+from causal_convolution_x3x3_amd import synth
+from oracle import model as OM
+from oracle import oracle as O
+
+from helpers import (assert_bf16_close, assert_fp32_close, from_device_cl, say, to_device_cl,
+                      to_oracle)
+
+pytestmark = pytest.mark.gpu
+
+TP = {C.TPAD_REPLICATE: O.REPLICATE, C.TPAD_ZERO: O.ZERO}
+
+
+def _run_chunks(plan, x_cl, splits, residual_cl=None):
+    st = P.Stream(plan)
+    outs, t0, r0 = [], 0, 0
+    for n in splits:
+        res = None
+        if residual_cl is not None:
+            first = st.frames_seen == 0
+            tn = plan.output_shape(n, first)[0]
+            res = residual_cl[r0:r0 + tn].contiguous()
+            r0 += tn
+        outs.append(st.step(x_cl[t0:t0 + n].contiguous(), residual=res))
+        t0 += n
+    torch.cuda.synchronize()
+    return torch.cat(outs, dim=0)
+
+
+# -------------------------------------------------------------- fp32 conv --
+
+@pytest.mark.parametrize("tpad", [C.TPAD_REPLICATE, C.TPAD_ZERO])
+@pytest.mark.parametrize("splits", [[9], [1, 4, 4], [1] * 9])
+def test_c0_fp32_conv_chunked(tpad, splits):
+    say("c0 fp32 tpad=%d splits=%s" % (tpad, splits))
+    wl = synth.WORKLOADS[0]
+    x = synth.video(wl["cin"], wl["t"], wl["h"], wl["w"], synth.seed(0, 1))
+    w = synth.conv_weight(wl["cout"], wl["cin"], 3, 3, 3, synth.seed(0, 2))
+    ref = O.causal_conv3d(to_oracle(x), to_oracle(w), None, TP[tpad])
+    plan = P.conv_plan(w.cuda(), wl["h"], wl["w"], max_chunk_t=9, tpad=tpad)
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits))
+    assert_fp32_close(got, ref, "c0")
+
+
+def test_fp32_memoryblock_zero_history_with_bias_and_upsample():
+    say("fp32 memoryblock kt=2")
+    x = synth.video(8, 5, 6, 7, synth.seed(0, 11))
+    w = synth.conv_weight(4, 8, 2, 3, 3, synth.seed(0, 12))
+    b = synth.bias(4, synth.seed(0, 13))
+    ref = O.one_shot(to_oracle(x), to_oracle(w), to_oracle(b), O.ZERO, up_s=2, up_t=2)
+    plan = P.conv_plan(w.cuda(), 6, 7, bias=b.cuda(), up_s=2, up_t=2, max_chunk_t=4, tpad=C.TPAD_ZERO)
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), [1, 2, 2]))
+    assert_fp32_close(got, ref, "memoryblock")
+
+
+# -------------------------------------------------------------- bf16 conv --
+
+BF16_CASES = [
+    # cin, cout, k, up_s, up_t, h, w, splits, tpad, bias
+    (32, 16, (3, 3, 3), 1, 1, 20, 36, [1, 3, 2], C.TPAD_REPLICATE, False),
+    (48, 96, (3, 3, 3), 1, 1, 18, 33, [2, 2], C.TPAD_REPLICATE, True),
+    (64, 128, (3, 3, 3), 2, 1, 9, 21, [1, 2], C.TPAD_REPLICATE, False),
+    (64, 192, (3, 3, 3), 1, 2, 10, 17, [1, 2, 1], C.TPAD_ZERO, True),
+    (32, 3, (3, 3, 3), 2, 1, 12, 20, [1, 2], C.TPAD_REPLICATE, True),
+    (128, 96, (3, 3, 3), 2, 1, 8, 40, [1, 3], C.TPAD_REPLICATE, False),
+    (384, 384, (3, 3, 3), 2, 2, 5, 6, [1, 1], C.TPAD_REPLICATE, False),
+    (16, 32, (2, 1, 1), 1, 1, 7, 19, [1, 2, 2], C.TPAD_ZERO, False),
+    (16, 64, (1, 3, 3), 2, 1, 7, 9, [2, 1], C.TPAD_REPLICATE, True),
+    (24, 16, (3, 1, 1), 1, 2, 5, 17, [2, 1], C.TPAD_ZERO, False),
+]
+
+
+@pytest.mark.parametrize("case", BF16_CASES, ids=lambda c: "ci%d_co%d_k%s_us%d_ut%d" % (c[0], c[1], "".join(map(str, c[2])), c[3], c[4]))
+def test_bf16_conv_vs_oracle(case):
+    cin, cout, k, up_s, up_t, h, w, splits, tpad, with_bias = case
+    say("bf16 conv %s" % (case,))
+    t = sum(splits)
+    x = synth.bf16(synth.video(cin, t, h, w, synth.seed(5, 1)))
+    wt = synth.bf16(synth.conv_weight(cout, cin, *k, synth.seed(5, 2)))
+    b = synth.bias(cout, synth.seed(5, 3)) if with_bias else None
+    ref = O.one_shot(to_oracle(x), to_oracle(wt), None if b is None else to_oracle(b), TP[tpad], up_s, up_t)
+    plan = P.conv_plan(wt.cuda(), h, w, bias=None if b is None else b.cuda(), up_s=up_s, up_t=up_t,
+                       max_chunk_t=max(splits), tpad=tpad)
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits))
+    assert_bf16_close(got, ref, "bf16 conv")
+
+
+@pytest.mark.parametrize("cout", [96, 192])
+@pytest.mark.parametrize("residual", [False, True])
+def test_bf16_conv_epilogue_act(cout, residual):
+    """v = conv + bias (+ residual), stored as bf16, then SiLU(RMSNorm(v)):
+    fused in the conv (96) or by the norm pass (192)."""
+    say("bf16 epilogue cout=%d residual=%s" % (cout, residual))
+    cin, h, w, splits = 32, 9, 20, [1, 2]
+    t = sum(splits)
+    x = synth.bf16(synth.video(cin, t, h, w, synth.seed(6, 1)))
+    wt = synth.bf16(synth.conv_weight(cout, cin, 3, 3, 3, synth.seed(6, 2)))
+    b = synth.bias(cout, synth.seed(6, 3))
+    g = synth.gain(cout, synth.seed(6, 4))
+    r = synth.bf16(synth.video(cout, t, h, w, synth.seed(6, 5))) if residual else None
+    v = O.causal_conv3d(to_oracle(x), to_oracle(wt), to_oracle(b), O.REPLICATE)
+    if residual:
+        v = v + to_oracle(r)
+    ref = O.act(O.round_bf16(v), to_oracle(g), 1e-6)
+    plan = P.conv_plan(wt.cuda(), h, w, bias=b.cuda(), gamma=g.cuda(), act=True, residual=residual,
+                       max_chunk_t=2)
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits,
+                                     residual_cl=to_device_cl(r) if residual else None))
+    assert_bf16_close(got, ref, "epilogue")
+
+
+# ------------------------------------------------------------- boundary --
+
+def _small_plan():
+    cin, cout, h, w = 32, 32, 10, 18
+    wt = synth.bf16(synth.conv_weight(cout, cin, 3, 3, 3, synth.seed(7, 2))).cuda()
+    return P.conv_plan(wt, h, w, max_chunk_t=4), (cin, h, w)
+
+
+def test_reset_pingpong_checkpoint_and_determinism():
+    say("boundary: reset / ping-pong / checkpoint")
+    plan, (cin, h, w) = _small_plan()
+    x = to_device_cl(synth.bf16(synth.video(cin, 10, h, w, synth.seed(7, 1))))
+    splits = [1, 4, 3, 2]
+    a = _run_chunks(plan, x, splits)
+    b = _run_chunks(plan, x, splits)
+    assert torch.equal(a, b), "replay is not bitwise identical"
+    # reset mid-stream == fresh stream
+    st = P.Stream(plan)
+    st.step(x[:3].contiguous())
+    st.reset()
+    c = torch.cat([st.step(x[i:i + n].contiguous()) for i, n in zip([0, 1, 5, 8], splits)])
+    assert torch.equal(a, c)
+    # checkpoint after two chunks, resume in a new stream
+    st = P.Stream(plan)
+    st.step(x[:1].contiguous())
+    st.step(x[1:5].contiguous())
+    saved = plan.new_state().copy_(st.states[st.cur])
+    tail_a = st.step(x[5:8].contiguous())
+    st2 = P.Stream(plan)
+    st2.states[0].copy_(saved)
+    st2.cur = 0
+    tail_b = st2.step(x[5:8].contiguous())
+    assert torch.equal(tail_a, tail_b)
+    torch.cuda.synchronize()
+
+
+def test_cache_in_untouched_and_aliasing_rejected():
+    say("boundary: cache_in untouched, aliasing")
+    plan, (cin, h, w) = _small_plan()
+    x = to_device_cl(synth.bf16(synth.video(cin, 3, h, w, synth.seed(7, 3))))
+    s0, s1 = plan.new_state(), plan.new_state()
+    plan.reset(s0)
+    plan.reset(s1)
+    plan.forward_chunk(x[:1].contiguous(), s0, s1)
+    before = s1.arena.clone()
+    s2 = plan.new_state()
+    plan.forward_chunk(x[1:3].contiguous(), s1, s2)
+    torch.cuda.synchronize()
+    assert torch.equal(before, s1.arena)
+    assert s2.frames_seen == 3
+    with pytest.raises(C.Cc3dError) as e:
+        plan.forward_chunk(x[:1].contiguous(), s1, s1)
+    assert e.value.status == C.ESTATE
+    with pytest.raises(C.Cc3dError) as e:
+        plan.forward_chunk(torch.empty((5, h, w, cin), dtype=torch.bfloat16, device="cuda"), s1, s2)
+    assert e.value.status == C.ESHAPE
+    # host memory is refused
+    with pytest.raises(ValueError):
+        plan.forward_chunk(x[:1].cpu().contiguous(), s1, s2)
+
+
+def test_transposes_roundtrip():
+    say("transposes")
+    for dt in (torch.bfloat16, torch.float32):
+        x = synth.video(5, 3, 7, 33, synth.seed(8, 1)).to(dt).cuda()
+        cl = P.to_channels_last(x)
+        assert torch.equal(cl, x.permute(1, 2, 3, 0).contiguous())
+        assert torch.equal(P.to_channels_first(cl), x)
+
+
+# ----------------------------------------------------------------- stacks --
+
+def _params(shapes, cfg, gain_for, with_bias=False):
+    """Seeded bf16 weights / fp32 gains and biases for (name, cout, cin, kt, kh, kw)."""
+    cpu, dev = {}, {}
+    for i, (name, co, ci, kt, kh, kw) in enumerate(shapes):
+        w = synth.bf16(synth.conv_weight(co, ci, kt, kh, kw, synth.seed(cfg, 10 + 3 * i)))
+        g = synth.gain(ci, synth.seed(cfg, 11 + 3 * i)) if gain_for(name) else None
+        b = synth.bias(co, synth.seed(cfg, 12 + 3 * i)) if with_bias else None
+        cpu[name] = {"w": to_oracle(w), "g": None if g is None else to_oracle(g),
+                     "b": None if b is None else to_oracle(b)}
+        dev[name] = {"w": w.cuda(), "g": None if g is None else g.cuda(), "b": None if b is None else b.cuda()}
+    return cpu, dev
+
+
+def test_c1_resblock_small():
+    say("c1 resblock small")
+    c, t, h, w = 32, 8, 12, 20
+    cpu, dev = _params([("c1", c, c, 3, 3, 3), ("c2", c, c, 3, 3, 3)], 1, lambda n: True, with_bias=True)
+    x = synth.bf16(synth.video(c, t, h, w, synth.seed(1, 1)))
+    ref_blk = OM.ResBlock(cpu["c1"], cpu["c2"], store=O.round_bf16)
+    ref = np.concatenate([ref_blk.step(to_oracle(x)[:, i:i + 4]) for i in range(0, t, 4)], axis=1)
+    plan = P.stack_plan(S.resblock_ops(c, dev["c1"], dev["c2"]), c, h, w, max_chunk_t=4)
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), [4, 4]))
+    assert_bf16_close(got, ref, "c1 block")
+
+
+@pytest.mark.parametrize("cfg,cin,cmid,cout", [(2, 64, 32, 32), (3, 32, 96, 3)])
+def test_upstage_small(cfg, cin, cmid, cout):
+    say("upstage small cfg=%d" % cfg)
+    t, h, w = 6, 7, 19
+    cpu, dev = _params([("c1", cmid, cin, 3, 3, 3), ("c2", cout, cmid, 3, 3, 3)], cfg, lambda n: n == "c2")
+    x = synth.bf16(synth.video(cin, t, h, w, synth.seed(cfg, 1)))
+    ref_st = OM.UpStage(cpu["c1"], cpu["c2"], store=O.round_bf16)
+    splits = [1, 4, 1] if cfg == 3 else [2, 4]
+    ref, t0 = [], 0
+    for n in splits:
+        ref.append(ref_st.step(to_oracle(x)[:, t0:t0 + n]))
+        t0 += n
+    ref = np.concatenate(ref, axis=1)
+    plan = P.stack_plan(S.upstage_ops(cmid, cout, dev["c1"], dev["c2"]), cin, h, w, max_chunk_t=4)
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits))
+    assert_bf16_close(got, ref, "upstage")
+
+
+def _decoder_case(c_latent, stages, t, h, w, splits, cfg=4):
+    shapes = [s[:6] for s in OM.decoder_layer_shapes(c_latent=c_latent, stages=stages)]
+    gains = {s[0]: s[6] for s in OM.decoder_layer_shapes(c_latent=c_latent, stages=stages)}
+    cpu, dev = _params(shapes, cfg, lambda n: gains[n])
+    x = synth.bf16(synth.video(c_latent, t, h, w, synth.seed(cfg, 1)))
+    dec = OM.Decoder(cpu, stages=stages, store=O.round_bf16)
+    ref, t0 = [], 0
+    for n in splits:
+        ref.append(dec.step(to_oracle(x)[:, t0:t0 + n]))
+        t0 += n
+    ref = np.concatenate(ref, axis=1)
+    plan = P.stack_plan(S.decoder_ops(dev, stages=stages), c_latent, h, w, max_chunk_t=max(splits))
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits))
+    return got, ref
+
+
+def test_decoder_small_channels():
+    say("decoder small channels")
+    got, ref = _decoder_case(16, ((64, 2), (32, 2), (16, 1)), t=6, h=3, w=5, splits=[2, 3, 1])
+    assert got.shape == (3, OM.output_frames(6), 48, 80)
+    assert_bf16_close(got, ref, "decoder small")
+
+
+def test_decoder_full_channels_tiny_frame():
+    say("decoder full channels tiny frame")
+    got, ref = _decoder_case(48, OM.DECODER_STAGES, t=5, h=2, w=3, splits=[3, 2])
+    assert got.shape == (3, OM.output_frames(5), 32, 48)
+    assert_bf16_close(got, ref, "decoder full channels")
