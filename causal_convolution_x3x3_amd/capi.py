@@ -24,7 +24,7 @@ EXPORTS = (
     "cc3d_plan_create", "cc3d_stack_plan_create", "cc3d_plan_destroy", "cc3d_state_bytes",
     "cc3d_plan_device_bytes", "cc3d_output_shape", "cc3d_reset", "cc3d_forward_chunk",
     "cc3d_to_channels_last", "cc3d_to_channels_first", "cc3d_last_error", "cc3d_version",
-    "cc3d_profile_enable", "cc3d_plan_num_ops", "cc3d_profile_read",
+    "cc3d_profile_enable", "cc3d_plan_num_ops", "cc3d_profile_read", "cc3d_slot_shape", "cc3d_slot_read",
 )
 
 
@@ -89,6 +89,8 @@ def lib():
             "cc3d_profile_enable": (i, [vp, i]),
             "cc3d_plan_num_ops": (i, [vp]),
             "cc3d_profile_read": (i, [vp, i, i, ctypes.POINTER(OpProfile)]),
+            "cc3d_slot_shape": (i, [vp, i, i, i, pi, pi, pi, pi]),
+            "cc3d_slot_read": (i, [vp, i, i, i, vp, sz, vp]),
             "cc3d_last_error": (ctypes.c_char_p, []),
             "cc3d_version": (i, []),
         }

@@ -779,6 +779,37 @@ cc3d_status cc3d_forward_chunk(const cc3d_plan* p, const void* x, int t_chunk, c
     return CC3D_OK;
 }
 
+cc3d_status cc3d_slot_shape(const cc3d_plan* p, int slot, int t_chunk, int first, int* c, int* t, int* h, int* w)
+{
+    if (!plan_ok(p)) return fail(CC3D_EINVAL, "plan is NULL or destroyed");
+    if (slot <= CC3D_SLOT_AUX || slot >= CC3D_MAX_SLOTS || !p->slots[slot].defined)
+        return fail(CC3D_EINVAL, "slot %d is not an intermediate slot of this plan", slot);
+    if (t_chunk < 1 || t_chunk > p->max_t) return fail(CC3D_ESHAPE, "t_chunk=%d not in [1, %d]", t_chunk, p->max_t);
+    const Slot& s = p->slots[slot];
+    if (c) *c = s.c;
+    if (t) *t = (int)s.tc.eval(t_chunk, first != 0);
+    if (h) *h = s.h;
+    if (w) *w = s.w;
+    clear_err();
+    return CC3D_OK;
+}
+
+cc3d_status cc3d_slot_read(const cc3d_plan* p, int slot, int t_chunk, int first, void* dst, size_t dst_bytes,
+                           void* stream)
+{
+    int c = 0, t = 0, h = 0, w = 0;
+    cc3d_status st = cc3d_slot_shape(p, slot, t_chunk, first, &c, &t, &h, &w);
+    if (st != CC3D_OK) return st;
+    if (!dst) return fail(CC3D_EINVAL, "dst is NULL");
+    const size_t bytes = (size_t)c * t * h * w * p->elem;
+    if (dst_bytes < bytes) return fail(CC3D_EINVAL, "dst_bytes=%zu < %zu needed", dst_bytes, bytes);
+    DeviceGuard g(p->device);
+    st = hip_status(hipMemcpyAsync(dst, p->slots[slot].ptr, bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream),
+                    "slot copy");
+    if (st == CC3D_OK) clear_err();
+    return st;
+}
+
 cc3d_status cc3d_profile_enable(cc3d_plan* p, int enable)
 {
     if (!plan_ok(p)) return fail(CC3D_EINVAL, "plan is NULL or destroyed");

@@ -100,6 +100,20 @@ class Plan:
                                           ctypes.byref(h), ctypes.byref(w)), "cc3d_output_shape")
         return (t.value, h.value, w.value, c.value)
 
+    def slot_shape(self, slot: int, t_chunk: int, first: bool):
+        c, t, h, w = (ctypes.c_int() for _ in range(4))
+        C.check(C.lib().cc3d_slot_shape(self._h, slot, t_chunk, int(first), ctypes.byref(c), ctypes.byref(t),
+                                        ctypes.byref(h), ctypes.byref(w)), "cc3d_slot_shape")
+        return (t.value, h.value, w.value, c.value)
+
+    def read_slot(self, slot: int, t_chunk: int, first: bool, stream=None) -> torch.Tensor:
+        """Copy of an intermediate slot as the last forward_chunk left it ([T][H][W][C])."""
+        shape = self.slot_shape(slot, t_chunk, first)
+        out = torch.empty(shape, dtype=_TD[self.dtype], device=self.device)
+        C.check(C.lib().cc3d_slot_read(self._h, slot, t_chunk, int(first), _ptr(out),
+                                       out.numel() * out.element_size(), _stream(stream)), "cc3d_slot_read")
+        return out
+
     def reset(self, state: State, stream=None):
         cs = state._c()
         C.check(C.lib().cc3d_reset(self._h, ctypes.byref(cs), _stream(stream)), "cc3d_reset")

@@ -51,47 +51,56 @@ def upstage_ops(c_mid: int, c_out: int, p1: Dict, p2: Dict) -> List[Op]:
 DECODER_STAGES = ((384, 2), (192, 2), (96, 1))
 
 
-def decoder_ops(params: Dict[str, Dict], stages=DECODER_STAGES, c_out: int = 3) -> List[Op]:
+def decoder_ops(params: Dict[str, Dict], stages=DECODER_STAGES, c_out: int = 3,
+                unique_slots: bool = False) -> List[Op]:
     """conv_in -> per stage [nearest up (2x space, 2x time on non-first frames
     when the stage's factor is 2) + conv, two residual blocks] -> head (act at low
     resolution, nearest 2x, conv to c_out).
 
     Slots per stage s (base = 3 + 5 s): raw A, raw B (the residual stream
     alternates between them), act A, act B, inner act.  Slot 3 + 5*len(stages)
-    holds conv_in's output."""
+    holds conv_in's output.  ``unique_slots`` gives every tensor a slot of its
+    own instead (same ops and kernels; every layer's input and output stay
+    readable after a chunk, for layer-wise checks)."""
+    nxt = [3]
+
+    def slot(fixed):
+        if not unique_slots:
+            return fixed
+        nxt[0] += 1
+        return nxt[0] - 1
+
     ops: List[Op] = []
-    h_in = 3 + 5 * len(stages)
+    h0 = slot(3 + 5 * len(stages))
     ops.append(Op(cout=stages[0][0], w=params["conv_in"]["w"], bias=params["conv_in"].get("b"), src=X,
-                  out=h_in, name="conv_in"))
-    prev_raw = h_in
+                  out=h0, name="conv_in"))
+    prev_raw, last_act = h0, NONE
     for si, (c, up_t) in enumerate(stages):
         base = 3 + 5 * si
-        raw = [base, base + 1]
-        act = [base + 2, base + 3]
-        inner = base + 4
+        raw_fixed = [base, base + 1]
+        act_fixed = [base + 2, base + 3]
         rb = [(params["s%d.rb%d.c1" % (si, r)], params["s%d.rb%d.c2" % (si, r)]) for r in range(2)]
         up = params["s%d.up" % si]
+        raw_cur, act_cur = slot(raw_fixed[0]), slot(act_fixed[0])
         # up conv: stores the raw result (residual of block 0) and act for block 0's conv1
-        ops.append(Op(cout=c, w=up["w"], bias=up.get("b"), up_s=2, up_t=up_t, src=prev_raw, out=raw[0],
-                      act_out=act[0], gamma=rb[0][0]["g"], name="s%d.up" % si))
+        ops.append(Op(cout=c, w=up["w"], bias=up.get("b"), up_s=2, up_t=up_t, src=prev_raw, out=raw_cur,
+                      act_out=act_cur, gamma=rb[0][0]["g"], name="s%d.up" % si))
         cur = 0
         for r in range(2):
             p1, p2 = rb[r]
-            ops.append(Op(cout=c, w=p1["w"], bias=p1.get("b"), src=act[cur], act_out=inner, gamma=p2["g"],
+            inner = slot(base + 4)
+            ops.append(Op(cout=c, w=p1["w"], bias=p1.get("b"), src=act_cur, act_out=inner, gamma=p2["g"],
                           name="s%d.rb%d.c1" % (si, r)))
-            last_of_stack = si == len(stages) - 1 and r == 1
-            if r == 0:
-                nxt_g = rb[1][0]["g"]
-            elif last_of_stack:
-                nxt_g = params["head"]["g"]
-            else:
-                nxt_g = None  # the next stage's up conv reads the raw stream
-            ops.append(Op(cout=c, w=p2["w"], bias=p2.get("b"), src=inner, res=raw[cur], out=raw[1 - cur],
-                          act_out=act[1 - cur] if nxt_g is not None else NONE, gamma=nxt_g,
-                          name="s%d.rb%d.c2" % (si, r)))
-            cur = 1 - cur
-        prev_raw = raw[cur]
-        last_act = act[cur]
+            # block 0 hands act(y) to block 1; the last block of the last stage hands
+            # it to the head; otherwise the next stage's up conv reads the raw stream
+            need_act = r == 0 or si == len(stages) - 1
+            nxt_g = (rb[1][0]["g"] if r == 0 else params["head"]["g"]) if need_act else None
+            new_raw = slot(raw_fixed[1 - cur])
+            new_act = slot(act_fixed[1 - cur]) if need_act else NONE
+            ops.append(Op(cout=c, w=p2["w"], bias=p2.get("b"), src=inner, res=raw_cur, out=new_raw,
+                          act_out=new_act, gamma=nxt_g, name="s%d.rb%d.c2" % (si, r)))
+            raw_cur, act_cur, cur = new_raw, new_act, 1 - cur
+        prev_raw, last_act = raw_cur, act_cur
     head = params["head"]
     ops.append(Op(cout=c_out, w=head["w"], bias=head.get("b"), up_s=2, src=last_act, out=Y, name="head"))
     return ops

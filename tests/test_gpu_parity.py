@@ -12,8 +12,8 @@ from causal_convolution_x3x3_amd import synth
 from oracle import model as OM
 from oracle import oracle as O
 
-from helpers import (assert_bf16_close, assert_fp32_close, from_device_cl, say, to_device_cl,
-                      to_oracle)
+from helpers import (assert_bf16_close, assert_fp32_close, assert_stack_close, from_device_cl, say,
+                     to_device_cl, to_oracle)
 
 pytestmark = pytest.mark.gpu
 
@@ -233,31 +233,76 @@ def test_upstage_small(cfg, cin, cmid, cout):
     assert_bf16_close(got, ref, "upstage")
 
 
-def _decoder_case(c_latent, stages, t, h, w, splits, cfg=4):
-    shapes = [s[:6] for s in OM.decoder_layer_shapes(c_latent=c_latent, stages=stages)]
-    gains = {s[0]: s[6] for s in OM.decoder_layer_shapes(c_latent=c_latent, stages=stages)}
-    cpu, dev = _params(shapes, cfg, lambda n: gains[n])
+def _decoder_layerwise(c_latent, stages, t, h, w, splits, cfg=4):
+    """Run the decoder twice on the GPU -- production slot wiring and the
+    unique-slot wiring -- and check (1) both give bitwise identical outputs,
+    (2) every layer of the unique-slot run against the oracle fed that layer's
+    own GPU input (the per-layer parity bound), (3) the whole stack against the
+    storage-rounded oracle run end to end (the stack bound)."""
+    full = OM.decoder_layer_shapes(c_latent=c_latent, stages=stages)
+    gains = {s_[0]: s_[6] for s_ in full}
+    cpu, dev = _params([s_[:6] for s_ in full], cfg, lambda n: gains[n])
     x = synth.bf16(synth.video(c_latent, t, h, w, synth.seed(cfg, 1)))
+    x_cl = to_device_cl(x)
+    ops_u = S.decoder_ops(dev, stages=stages, unique_slots=True)
+    plan_u = P.stack_plan(ops_u, c_latent, h, w, max_chunk_t=max(splits))
+    plan_p = P.stack_plan(S.decoder_ops(dev, stages=stages), c_latent, h, w, max_chunk_t=max(splits))
+    su, sp = P.Stream(plan_u), P.Stream(plan_p)
+    layer = {i: O.CausalConvStream(cpu[o.name]["w"], cpu[o.name]["b"], O.REPLICATE, o.up_s, o.up_t)
+             for i, o in enumerate(ops_u)}
+    outs, t0, worst = [], 0, {}
+    for n in splits:
+        first = su.frames_seen == 0
+        xc = x_cl[t0:t0 + n].contiguous()
+        yu, yp = su.step(xc), sp.step(xc)
+        torch.cuda.synchronize()
+        assert torch.equal(yu, yp), "production wiring differs from the unique-slot wiring"
+        outs.append(yu)
+        ten = {C.SLOT_X: xc, C.SLOT_Y: yu}
+        for o in ops_u:
+            for sl in (o.out, o.act_out):
+                if sl > C.SLOT_AUX:
+                    ten[sl] = plan_u.read_slot(sl, n, first)
+        torch.cuda.synchronize()
+        for i, o in enumerate(ops_u):
+            v = layer[i].step(from_device_cl(ten[o.src]))
+            if o.res != C.SLOT_NONE:
+                v = v + from_device_cl(ten[o.res])
+            if o.out != C.SLOT_NONE:
+                mx, mn = assert_bf16_close(from_device_cl(ten[o.out]), v, "%s out (chunk at %d)" % (o.name, t0))
+                worst[o.name] = max(worst.get(o.name, 0.0), mn)
+            if o.act_out != C.SLOT_NONE:
+                ref_act = O.act(O.round_bf16(v), cpu_gain(cpu, ops_u, o), 1e-6)
+                assert_bf16_close(from_device_cl(ten[o.act_out]), ref_act, "%s act (chunk at %d)" % (o.name, t0))
+        t0 += n
+    got = from_device_cl(torch.cat(outs, dim=0))
     dec = OM.Decoder(cpu, stages=stages, store=O.round_bf16)
     ref, t0 = [], 0
     for n in splits:
         ref.append(dec.step(to_oracle(x)[:, t0:t0 + n]))
         t0 += n
     ref = np.concatenate(ref, axis=1)
-    plan = P.stack_plan(S.decoder_ops(dev, stages=stages), c_latent, h, w, max_chunk_t=max(splits))
-    got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits))
-    return got, ref
+    return got, ref, worst
+
+
+def cpu_gain(cpu, ops, o):
+    """The oracle-side gain of the act an op stores: the RMSNorm gain of the conv
+    that reads it (the next block's conv1, the block's conv2, or the head)."""
+    for nxt in ops:
+        if nxt.src == o.act_out:
+            return cpu[nxt.name]["g"]
+    raise AssertionError("no op reads %s's act" % o.name)
 
 
 def test_decoder_small_channels():
     say("decoder small channels")
-    got, ref = _decoder_case(16, ((64, 2), (32, 2), (16, 1)), t=6, h=3, w=5, splits=[2, 3, 1])
+    got, ref, _ = _decoder_layerwise(16, ((64, 2), (32, 2), (16, 1)), t=6, h=3, w=5, splits=[2, 3, 1])
     assert got.shape == (3, OM.output_frames(6), 48, 80)
-    assert_bf16_close(got, ref, "decoder small")
+    assert_stack_close(got, ref, "decoder small")
 
 
 def test_decoder_full_channels_tiny_frame():
     say("decoder full channels tiny frame")
-    got, ref = _decoder_case(48, OM.DECODER_STAGES, t=5, h=2, w=3, splits=[3, 2])
+    got, ref, _ = _decoder_layerwise(48, OM.DECODER_STAGES, t=5, h=2, w=3, splits=[3, 2])
     assert got.shape == (3, OM.output_frames(5), 32, 48)
-    assert_bf16_close(got, ref, "decoder full channels")
+    assert_stack_close(got, ref, "decoder full channels")
