@@ -69,7 +69,7 @@ struct OpRt {
     float* bias = nullptr;
     float* gamma = nullptr;
     size_t cache_off = 0, cache_bytes = 0;
-    int ntile = 0, nblocks = 0, kchunks = 0;
+    int ntile = 0, nblocks = 0, kchunks = 0, family = 1;
     bool fused_act = false;
 };
 
@@ -274,6 +274,7 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
             if (bf16) {
                 cc3d::bf16_conv_tiling(o.cout, &r.ntile, &r.nblocks);
                 r.kchunks = (r.cin + 31) / 32;
+                r.family = cc3d::bf16_conv_family(r.ntile, o.kh, o.kw, o.up_s);
             }
         } else {
             r.cout = r.cin;
@@ -392,7 +393,7 @@ cc3d_status materialise(const cc3d_stack_desc* d, cc3d_plan* p, hipStream_t stre
                 const size_t pk = cc3d::bf16_packed_elems(r.cout, r.cin, r.kt, r.kh, r.kw) * 2;
                 cc3d_status st = al.alloc(&r.wpk, pk, "packed weights");
                 if (st != CC3D_OK) return st;
-                st = hip_status(cc3d::launch_pack_bf16(o.w, r.wpk, r.cout, r.cin, r.kt, r.kh, r.kw, stream),
+                st = hip_status(cc3d::launch_pack_bf16(o.w, r.wpk, r.cout, r.cin, r.kt, r.kh, r.kw, r.family, stream),
                                 "weight repack launch");
                 if (st != CC3D_OK) return st;
             } else {
@@ -534,7 +535,8 @@ std::string conv_kernel_name(const cc3d_plan* p, const OpRt& r)
 {
     char buf[64];
     if (p->dtype == CC3D_BF16)
-        snprintf(buf, sizeof buf, "conv_bf16_up%d_k%d_n%d", r.up_s, r.kh, r.ntile);
+        snprintf(buf, sizeof buf, "conv_bf16%s_up%d_k%d_n%d", r.family == 2 ? "_v2" : "", r.up_s, r.kh,
+                 r.ntile);
     else
         snprintf(buf, sizeof buf, "conv_f32");
     return buf;
@@ -710,6 +712,7 @@ cc3d_status cc3d_forward_chunk(const cc3d_plan* p, const void* x, int t_chunk, c
             a.kchunks = r.kchunks;
             a.ntile = r.ntile;
             a.nblocks = r.nblocks;
+            a.family = r.family;
             if (r.fused_act) {
                 a.out = slot_ptr(r.out);
                 a.act_out = slot_ptr(r.act_out);

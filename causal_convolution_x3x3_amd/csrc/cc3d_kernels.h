@@ -35,6 +35,7 @@ struct ConvArgs {
     int h_in, w_in, up_s, h_out, w_out, t_out;
     int kchunks;          // bf16: ceil(cin / 32)
     int ntile, nblocks;   // bf16: output channels per workgroup, number of such blocks
+    int family;           // bf16: kernel family (1 or 2) the weights were packed for
 };
 
 struct NormArgs {
@@ -56,7 +57,15 @@ hipError_t launch_conv_bf16(const ConvArgs& a, hipStream_t s);
 // Repack [cout][cin][kt][kh][kw] bf16 weights into the MFMA operand blocks.
 size_t bf16_packed_elems(int cout, int cin, int kt, int kh, int kw);
 hipError_t launch_pack_bf16(const void* w, void* wpk, int cout, int cin, int kt, int kh, int kw,
-                            hipStream_t s);
+                            int family, hipStream_t s);
+
+// Register-blocked 3x3 spatial kernels (conv_bf16_v2.hip) for 96/128-channel
+// output blocks; their weights are packed with the column tap outermost.
+bool v2_conv_applies(int ntile, int kh, int kw, int up_s);
+// Kernel family chosen for a bf16 conv: 2 = v2 where it applies, else 1.
+// CC3D_CONV_FAMILY=1 in the environment at plan creation keeps every conv on v1.
+int bf16_conv_family(int ntile, int kh, int kw, int up_s);
+hipError_t launch_conv_bf16_v2(const ConvArgs& a, hipStream_t s);
 
 // fp32 direct conv (weights used in PyTorch order, copied by the host).
 hipError_t launch_conv_f32(const ConvArgs& a, hipStream_t s);

@@ -24,6 +24,8 @@
 // MFMA operand layout (16x16x32): lane l supplies row (l & 15) of A / column
 // (l & 15) of B with 8 consecutive K values from K group (l >> 4); the result
 // lane l holds rows 4*(l >> 4) + i, column (l & 15).
+#include <cstdlib>
+
 #include "cc3d_kernels.h"
 
 namespace cc3d {
@@ -230,8 +232,12 @@ hipError_t launch_nf(const ConvArgs& a, hipStream_t s)
     }
 }
 
+// Packed layout per (channel block, temporal tap, 32-channel chunk): the
+// kh*kw spatial taps, each NTILE rows of 32 channels with the 16-byte chunks
+// swizzled as in LDS.  Spatial taps are ordered row-major (b, d), or column
+// major (d, b) for the v2 kernels, whose sub-steps take one column tap at a time.
 __global__ void pack_bf16_kernel(const uint16_t* w, uint16_t* wpk, int cout, int cin, int kt,
-                                 int kh, int kw, int ntile, int nblocks, int kchunks)
+                                 int kh, int kw, int ntile, int nblocks, int kchunks, int dmajor)
 {
     const int taps = kh * kw;
     const int64_t total = (int64_t)nblocks * kt * kchunks * taps * ntile * 32;
@@ -251,7 +257,8 @@ __global__ void pack_bf16_kernel(const uint16_t* w, uint16_t* wpk, int cout, int
         const int glog = gphys ^ swz(nl);
         const int n = nb * ntile + nl;
         const int c = kc * 32 + glog * 8 + el;
-        const int b = tap / kw, d = tap % kw;
+        const int b = dmajor ? tap % kh : tap / kw;
+        const int d = dmajor ? tap / kh : tap % kw;
         uint16_t v = 0;
         if (n < cout && c < cin) v = w[((((int64_t)n * cin + c) * kt + ta) * kh + b) * kw + d];
         wpk[idx] = v;
@@ -284,6 +291,13 @@ void bf16_conv_tiling(int cout, int* ntile, int* nblocks)
     *nblocks = nt ? (cout + nt - 1) / nt : 0;
 }
 
+int bf16_conv_family(int ntile, int kh, int kw, int up_s)
+{
+    const char* e = getenv("CC3D_CONV_FAMILY");
+    if (e && atoi(e) == 1) return 1;
+    return v2_conv_applies(ntile, kh, kw, up_s) ? 2 : 1;
+}
+
 size_t bf16_packed_elems(int cout, int cin, int kt, int kh, int kw)
 {
     int nt, nb;
@@ -293,7 +307,7 @@ size_t bf16_packed_elems(int cout, int cin, int kt, int kh, int kw)
 }
 
 hipError_t launch_pack_bf16(const void* w, void* wpk, int cout, int cin, int kt, int kh, int kw,
-                            hipStream_t s)
+                            int family, hipStream_t s)
 {
     int nt, nb;
     bf16_conv_tiling(cout, &nt, &nb);
@@ -301,14 +315,16 @@ hipError_t launch_pack_bf16(const void* w, void* wpk, int cout, int cin, int kt,
     const size_t total = bf16_packed_elems(cout, cin, kt, kh, kw);
     int blocks = (int)((total + 255) / 256);
     if (blocks > 65536) blocks = 65536;
+    const int dmajor = family == 2 ? 1 : 0;
     hipLaunchKernelGGL(pack_bf16_kernel, dim3(blocks), dim3(256), 0, s, (const uint16_t*)w,
-                       (uint16_t*)wpk, cout, cin, kt, kh, kw, nt, nb, kchunks);
+                       (uint16_t*)wpk, cout, cin, kt, kh, kw, nt, nb, kchunks, dmajor);
     return hipGetLastError();
 }
 
 hipError_t launch_conv_bf16(const ConvArgs& a, hipStream_t s)
 {
     if (a.kh != a.kw) return hipErrorInvalidValue;
+    if (a.family == 2) return launch_conv_bf16_v2(a, s);
     if (a.up_s == 1 && a.kh == 3) return launch_nf<1, 3>(a, s);
     if (a.up_s == 2 && a.kh == 3) return launch_nf<2, 3>(a, s);
     if (a.up_s == 1 && a.kh == 1) return launch_nf<1, 1>(a, s);

@@ -72,6 +72,9 @@ BF16_CASES = [
     (64, 192, (3, 3, 3), 1, 2, 10, 17, [1, 2, 1], C.TPAD_ZERO, True),
     (32, 3, (3, 3, 3), 2, 1, 12, 20, [1, 2], C.TPAD_REPLICATE, True),
     (128, 96, (3, 3, 3), 2, 1, 8, 40, [1, 3], C.TPAD_REPLICATE, False),
+    (32, 128, (3, 3, 3), 1, 1, 11, 70, [2, 1], C.TPAD_ZERO, True),
+    (96, 96, (3, 3, 3), 1, 1, 17, 131, [1, 2], C.TPAD_REPLICATE, False),
+    (192, 96, (3, 3, 3), 2, 1, 9, 35, [2, 1], C.TPAD_REPLICATE, True),
     (384, 384, (3, 3, 3), 2, 2, 5, 6, [1, 1], C.TPAD_REPLICATE, False),
     (16, 32, (2, 1, 1), 1, 1, 7, 19, [1, 2, 2], C.TPAD_ZERO, False),
     (16, 64, (1, 3, 3), 2, 1, 7, 9, [2, 1], C.TPAD_REPLICATE, True),
