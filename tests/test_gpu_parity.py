@@ -309,3 +309,23 @@ def test_decoder_full_channels_tiny_frame():
     got, ref, _ = _decoder_layerwise(48, OM.DECODER_STAGES, t=5, h=2, w=3, splits=[3, 2])
     assert got.shape == (3, OM.output_frames(5), 32, 48)
     assert_stack_close(got, ref, "decoder full channels")
+
+
+def test_plan_create_failure_releases_everything(monkeypatch):
+    """An allocation that fails part-way through plan creation returns ENOMEM,
+    leaves no plan and no device memory behind."""
+    say("boundary: injected allocation failure")
+    wt = synth.bf16(synth.conv_weight(96, 64, 3, 3, 3, synth.seed(7, 9))).cuda()
+    g = synth.gain(96, synth.seed(7, 10)).cuda()
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    for k in (1, 2, 3):
+        monkeypatch.setenv("CC3D_TEST_FAIL_ALLOC", str(k))
+        with pytest.raises(C.Cc3dError) as e:
+            P.conv_plan(wt, 64, 96, gamma=g, act=True, max_chunk_t=8)
+        assert e.value.status == C.ENOMEM
+    monkeypatch.delenv("CC3D_TEST_FAIL_ALLOC")
+    torch.cuda.synchronize()
+    assert torch.cuda.mem_get_info()[0] >= free0 - (2 << 20)
+    plan = P.conv_plan(wt, 64, 96, gamma=g, act=True, max_chunk_t=8)  # and it still works
+    assert plan.state_bytes > 0
