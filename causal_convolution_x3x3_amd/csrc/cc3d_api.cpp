@@ -252,6 +252,9 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
                 if (r.cin % 8 != 0)
                     return fail(CC3D_ESHAPE, "op %d: bf16 conv input channels %d: must be a multiple of 8", i, r.cin);
                 if (o.kh != o.kw) return fail(CC3D_ESHAPE, "op %d: bf16 conv needs kh == kw (got %d, %d)", i, o.kh, o.kw);
+                if ((int64_t)r.h_in * r.w_in * r.cin >= ((int64_t)1 << 30))
+                    return fail(CC3D_ESHAPE, "op %d: input frame of %lld elements; accepted below 2^30", i,
+                                (long long)r.h_in * r.w_in * r.cin);
                 if (!cc3d::bf16_conv_supported(o.cout, o.kh, o.kw, o.up_s))
                     return fail(CC3D_ESHAPE, "op %d: bf16 conv cout=%d k=%d up_s=%d has no kernel", i, o.cout, o.kh,
                                 o.up_s);

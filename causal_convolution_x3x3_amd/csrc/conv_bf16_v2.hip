@@ -87,8 +87,41 @@ struct Geo<2> {  // tile: 8 source rows x 16 source columns; M-wave w: source ro
     static constexpr int MF = 8;  // 2 rows x 4 phases
 };
 
+// Raw buffer descriptor (gfx9 family word 3) over `bytes` bytes at `base`; a
+// load whose offset lies past the end returns zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t OOB = 0x80000000u;  // an offset past every buffer used here
+
+// 16 bytes per lane from buffer offset `off` straight into LDS: lane l writes
+// the 16-byte slot lds_base + l (lds_base is the same for the whole wave).
+__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4* lds_base)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // WN = waves along N: the workgroup has 4*WN waves (two per SIMD when WN = 2);
 // wave (wm, wn) computes M-wave wm's pixels for the NF/WN fragments of half wn.
+//
+// Staging: the input tile and the weights go from global memory straight into
+// LDS (buffer loads with the LDS flag), so no registers or LDS stores are spent
+// on them.  A thread's 16-byte slots are fixed (slot = tid + NT*it); the byte
+// offset each slot reads inside a frame is computed once.  LDS rows of the input
+// tile are padded to a multiple of 8 pixels, so the chunk swizzle depends on the
+// column only and every fragment read is a base register plus a constant.
+// Weights are prefetched two sub-steps ahead (three LDS buffers; two, one
+// sub-step ahead, where three do not fit), the input tile one K step ahead.
 template <int UP, int NF, int WN>
 __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
 {
@@ -96,16 +129,32 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     constexpr int NT = 256 * WN;        // threads
     constexpr int NFW = NF / WN;        // N fragments per wave
     constexpr int LH = G::TS_H + 2, LW = G::TS_W + 2;
+    constexpr int LWP = (LW + 7) / 8 * 8;  // padded row (pixels)
+    constexpr int ROWB = LWP * 64;          // bytes per LDS row
     constexpr int NTILE = 16 * NF;
-    constexpr int A_CH = LH * LW * 4;   // 16-byte chunks of one input tile (32 channels)
-    constexpr int B_CH = 3 * NTILE * 4; // 16-byte chunks of one column tap's weights
+    constexpr int A_CH = LH * LWP * 4;      // 16-byte slots of one LDS tile buffer
+    constexpr int B_CH = 3 * NTILE * 4;     // 16-byte slots of one column tap's weights
     constexpr int A_IT = (A_CH + NT - 1) / NT;
     constexpr int B_IT = (B_CH + NT - 1) / NT;
+    // Load instructions every wave issues per tile / per weight block: only these
+    // full rounds are counted by the vmcnt waits (a wave that issued more younger
+    // loads then waits for some of them too, which is safe).
+    constexpr int A_FULL = A_CH / NT;
+    constexpr int B_FULL = B_CH / NT;
+    static_assert(A_FULL >= 1 && B_FULL >= 1, "every wave takes part in each load round");
     constexpr int MF = G::MF;
+    // weight buffers: 3 (prefetch distance 2) when they fit in LDS with the
+    // double-buffered tile, else 2 (distance 1)
+    constexpr int NBB = (2 * A_CH + 3 * B_CH) * 16 <= 160 * 1024 ? 3 : 2;
     static_assert(NF % WN == 0, "N fragments split evenly over the N waves");
 
-    __shared__ uint4 lds_a[2][A_CH];
-    __shared__ uint4 lds_b[2][B_CH];
+    // one LDS variable per buffer: the compiler then knows that loads into one
+    // buffer do not touch the buffer being read, and does not wait for them
+    __shared__ uint4 lds_a0[A_CH];
+    __shared__ uint4 lds_a1[A_CH];
+    __shared__ uint4 lds_b0[B_CH];
+    __shared__ uint4 lds_b1[B_CH];
+    __shared__ uint4 lds_b2[NBB == 3 ? B_CH : 1];
 
     const int tiles_w = (a.w_in + G::TS_W - 1) / G::TS_W;
     const int tiles_h = (a.h_in + G::TS_H - 1) / G::TS_H;
@@ -126,131 +175,171 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
 
     const int nsteps = a.kt * a.kchunks;
     const int nsub = nsteps * 3;
-    const uint4* wblk = (const uint4*)a.wpk + (size_t)nb * nsub * B_CH;
+    const uint32_t frame_bytes = (uint32_t)(a.z.frame_elems * 2);
+    const __amdgpu_buffer_rsrc_t wr =
+        make_rsrc((const uint4*)a.wpk + (size_t)nb * nsub * B_CH, (uint32_t)(nsub * B_CH * 16));
 
-    uint4 ra[A_IT];
-    uint4 rb[B_IT];
+    // Step-invariant load plan: byte offset inside a frame of the chunk slot
+    // (tid + NT*it) holds (OOB: zero, i.e. outside the image or a padding column),
+    // and the channel of its first element.
+    uint32_t a_off[A_IT];
+    int a_ch[A_IT];
+#pragma unroll
+    for (int it = 0; it < A_IT; ++it) {
+        const int slot = tid + NT * it;
+        a_off[it] = OOB;
+        a_ch[it] = 0;
+        if (slot < A_CH) {
+            const int pix = slot >> 2;
+            const int r = pix / LWP, c = pix - r * LWP;
+            const int gg = (slot & 3) ^ swz(c);
+            a_ch[it] = gg * 8;
+            const int gy = i0 + r - 1, gx = j0 + c - 1;
+            if (c < LW && gy >= 0 && gy < a.h_in && gx >= 0 && gx < a.w_in)
+                a_off[it] = (uint32_t)(((gy * a.w_in + gx) * a.cin + gg * 8) * 2);
+        }
+    }
 
-    auto fetch_a = [&](int step) {
+    auto issue_a = [&](int step, uint4* buf) {
         const int ta = step / a.kchunks, kc = step - ta * a.kchunks;
         const uint16_t* fp = zframe(a.z, t + ta);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(fp, fp ? frame_bytes : 0u);
+        const int ch0 = kc * 32;
 #pragma unroll
         for (int it = 0; it < A_IT; ++it) {
-            const int idx = tid + NT * it;
-            uint4 v = make_uint4(0u, 0u, 0u, 0u);
-            if (idx < A_CH) {
-                const int pix = idx >> 2, gg = idx & 3;
-                const int r = pix / LW, c = pix - r * LW;
-                const int gy = i0 + r - 1, gx = j0 + c - 1;
-                const int ch = kc * 32 + gg * 8;
-                if (fp && gy >= 0 && gy < a.h_in && gx >= 0 && gx < a.w_in && ch < a.cin)
-                    v = *(const uint4*)(fp + ((int64_t)gy * a.w_in + gx) * a.cin + ch);
-            }
-            ra[it] = v;
-        }
-    };
-    auto store_a = [&](int buf) {
-#pragma unroll
-        for (int it = 0; it < A_IT; ++it) {
-            const int idx = tid + NT * it;
-            if (idx < A_CH) {
-                const int pix = idx >> 2, gg = idx & 3;
-                lds_a[buf][pix * 4 + (gg ^ swz(pix))] = ra[it];
+            if (NT * it + wave * 64 < A_CH) {  // wave-uniform: the wave has slots in range
+                const uint32_t off = (ch0 + a_ch[it] < a.cin) ? a_off[it] + (uint32_t)(ch0 * 2) : OOB;
+                if (tid + NT * it < A_CH) load_to_lds(r, off, buf + NT * it + wave * 64);
             }
         }
     };
-    auto fetch_b = [&](int sub) {
-        const uint4* src = wblk + (size_t)sub * B_CH;
+    auto issue_b = [&](int sub, uint4* buf) {
 #pragma unroll
         for (int it = 0; it < B_IT; ++it) {
-            const int idx = tid + NT * it;
-            rb[it] = idx < B_CH ? src[idx] : make_uint4(0u, 0u, 0u, 0u);
+            if (NT * it + wave * 64 < B_CH) {
+                const uint32_t off = (uint32_t)((sub * B_CH + tid + NT * it) * 16);
+                if (tid + NT * it < B_CH) load_to_lds(wr, off, buf + NT * it + wave * 64);
+            }
         }
     };
-    auto store_b = [&](int buf) {
+    // byte offset of this lane's 16-byte chunk at LDS column `col` of row 0
+    auto col_off = [&](int col) -> int { return col * 64 + ((g ^ swz(col)) << 4); };
+    auto lds_frag = [&](const uint4* base, int byte_off) -> bf16x8 {
+        return as_bf16x8(*(const uint4*)((const char*)base + byte_off));
+    };
+    int b_off[NFW];
 #pragma unroll
-        for (int it = 0; it < B_IT; ++it) {
-            const int idx = tid + NT * it;
-            if (idx < B_CH) lds_b[buf][idx] = rb[it];
-        }
-    };
-    auto a_frag = [&](int buf, int ly, int lx) -> bf16x8 {
-        const int pix = ly * LW + lx;
-        return as_bf16x8(lds_a[buf][pix * 4 + (g ^ swz(pix))]);
-    };
+    for (int f = 0; f < NFW; ++f) {
+        const int nl = 16 * (wn * NFW + f) + k16;
+        b_off[f] = nl * 64 + ((g ^ swz(nl)) << 4);
+    }
 
-    // prologue: step 0's tile and sub-step 0's weights
-    fetch_a(0);
-    fetch_b(0);
-    store_a(0);
-    store_b(0);
-    __syncthreads();
+    // prologue: step 0's tile, the first NBB-1 sub-steps' weights
+    issue_a(0, lds_a0);
+    issue_b(0, lds_b0);
+    if (NBB == 3 && nsub > 1) issue_b(1, lds_b1);
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
 
-    for (int sub = 0; sub < nsub; ++sub) {
-        const int step = sub / 3, d = sub - step * 3;
-        const int abuf = step & 1, bbuf = sub & 1;
-        const bool more_b = sub + 1 < nsub;
+    // One K step = three sub-steps (column taps d = 0, 1, 2), unrolled so the tap
+    // and every LDS offset are compile-time constants; steps are taken in pairs
+    // so that every buffer a sub-step reads or fills is a fixed LDS variable.
+    // Sub-step `sub` reads weight buffer sub % NBB and input buffer step % 2.
+    auto k_step = [&](int step, const uint4* aread, uint4* awrite, const int par) {
         const bool more_a = step + 1 < nsteps;
-        if (more_b) fetch_b(sub + 1);
-        if (more_a && d == 0) fetch_a(step + 1);  // lands in LDS after sub-step d == 2
+        const int sub0 = 3 * step;
+#pragma unroll
+        for (int d = 0; d < 3; ++d) {
+            const int sub = sub0 + d;
+            // NBB = 3: sub % 3 == d; NBB = 2: sub % 2 == (par + d) % 2 with par = step % 2.
+            // The buffer written now, (sub + NBB - 1) % NBB, was last read in
+            // sub-step sub - 1 (retired by its barrier).
+            const int bcur = NBB == 3 ? d : ((par + d) & 1);
+            const int bnext = NBB == 3 ? (d + 2) % 3 : (bcur ^ 1);
+            const uint4* bread = bcur == 0 ? lds_b0 : (bcur == 1 ? lds_b1 : lds_b2);
+            uint4* bwrite = bnext == 0 ? lds_b0 : (bnext == 1 ? lds_b1 : lds_b2);
+            const bool ahead_b = sub + NBB - 1 < nsub;
+            if (ahead_b) issue_b(sub + NBB - 1, bwrite);
+            if (d == 0 && more_a) issue_a(step + 1, awrite);
 
-        // B fragments of taps (b, d), b = 0..2, for this wave's channels
-        bf16x8 bq[3][NFW];
+            // B fragments of taps (b, d), b = 0..2, for this wave's channels
+            bf16x8 bq[3][NFW];
 #pragma unroll
-        for (int b = 0; b < 3; ++b)
+            for (int b = 0; b < 3; ++b)
 #pragma unroll
-            for (int f = 0; f < NFW; ++f) {
-                const int nl = 16 * (wn * NFW + f) + k16;
-                bq[b][f] = as_bf16x8(lds_b[bbuf][(b * NTILE + nl) * 4 + (g ^ swz(nl))]);
-            }
+                for (int f = 0; f < NFW; ++f) bq[b][f] = lds_frag(bread, b_off[f] + b * NTILE * 64);
 
-        if (UP == 1) {
-            // LDS row s holds source row i0 + s - 1; output row r reads rows r+b.
+            if (UP == 1) {
+                // LDS row s holds source row i0 + s - 1; output row r reads rows r+b.
+                const int base = col_off(16 * wm + k16 + d);
 #pragma unroll
-            for (int s = 0; s < G::TS_H + 2; ++s) {
-                const bf16x8 av = a_frag(abuf, s, 16 * wm + k16 + d);
+                for (int s = 0; s < G::TS_H + 2; ++s) {
+                    const bf16x8 av = lds_frag(aread, base + s * ROWB);
 #pragma unroll
-                for (int b = 0; b < 3; ++b) {
-                    const int r = s - b;
-                    if (r >= 0 && r < G::TS_H) {
+                    for (int b = 0; b < 3; ++b) {
+                        const int r = s - b;
+                        if (r >= 0 && r < G::TS_H) {
 #pragma unroll
-                        for (int f = 0; f < NFW; ++f)
-                            acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[b][f], acc[r][f], 0, 0, 0);
+                            for (int f = 0; f < NFW; ++f)
+                                acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[b][f], acc[r][f], 0, 0, 0);
+                        }
+                    }
+                }
+            } else {
+                // M fragment m = rr*4 + p*2 + q: source row 2*wm + rr, phase (p, q).
+                // Column offsets of this d: q=0 -> floor((d-1)/2), q=1 -> floor(d/2).
+                const int ox0 = (d - 1) >> 1, ox1 = d >> 1;
+                const int base0 = col_off(k16 + ox0 + 1) + 2 * wm * ROWB;
+                const int base1 = col_off(k16 + ox1 + 1) + 2 * wm * ROWB;
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr) {
+#pragma unroll
+                    for (int oy = -1; oy <= 1; ++oy) {
+                        const int row = rr + oy + 1;  // plus 2*wm, folded into the bases
+                        const bf16x8 a0 = lds_frag(aread, base0 + row * ROWB);
+                        const bf16x8 a1 = (ox0 == ox1) ? a0 : lds_frag(aread, base1 + row * ROWB);
+#pragma unroll
+                        for (int p = 0; p < 2; ++p)
+#pragma unroll
+                            for (int b = 0; b < 3; ++b) {
+                                if (((p + b - 1) >> 1) != oy) continue;
+#pragma unroll
+                                for (int f = 0; f < NFW; ++f) {
+                                    acc[rr * 4 + p * 2 + 0][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                        a0, bq[b][f], acc[rr * 4 + p * 2 + 0][f], 0, 0, 0);
+                                    acc[rr * 4 + p * 2 + 1][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                        a1, bq[b][f], acc[rr * 4 + p * 2 + 1][f], 0, 0, 0);
+                                }
+                            }
                     }
                 }
             }
-        } else {
-            // M fragment m = rr*4 + p*2 + q: source row 2*wm + rr, phase (p, q).
-            // Column offsets used by this d: q=0 -> floor((d-1)/2), q=1 -> floor(d/2).
-#pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-#pragma unroll
-                for (int oy = -1; oy <= 1; ++oy) {
-                    const int ly = 2 * wm + rr + oy + 1;
-                    const int ox0 = (d - 1) >> 1;  // q = 0
-                    const int ox1 = d >> 1;        // q = 1
-                    const bf16x8 a0 = a_frag(abuf, ly, k16 + ox0 + 1);
-                    const bf16x8 a1 = (ox1 == ox0) ? a0 : a_frag(abuf, ly, k16 + ox1 + 1);
-#pragma unroll
-                    for (int p = 0; p < 2; ++p)
-#pragma unroll
-                        for (int b = 0; b < 3; ++b) {
-                            if (((p + b - 1) >> 1) != oy) continue;
-#pragma unroll
-                            for (int f = 0; f < NFW; ++f) {
-                                acc[rr * 4 + p * 2 + 0][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    a0, bq[b][f], acc[rr * 4 + p * 2 + 0][f], 0, 0, 0);
-                                acc[rr * 4 + p * 2 + 1][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    a1, bq[b][f], acc[rr * 4 + p * 2 + 1][f], 0, 0, 0);
-                            }
-                        }
-                }
-            }
-        }
 
-        if (more_b) store_b(bbuf ^ 1);
-        if (more_a && d == 2) store_a(abuf ^ 1);
-        __syncthreads();
+            // Before the barrier: the weights of sub + 1 (issued during sub - 1) and,
+            // at d == 2, the next tile (issued at d == 0) must have landed.  Loads
+            // complete in issue order; the waits leave the younger ones in flight.
+            if (NBB == 3) {
+                if (ahead_b && more_a) {
+                    if (d == 2) wait_vmcnt<B_FULL>();
+                    else wait_vmcnt<A_FULL + B_FULL>();
+                } else {
+                    wait_vmcnt<0>();
+                }
+            } else {
+                // the weights of sub + 1 were issued in this sub-step, before the tile
+                if (d == 0 && more_a) wait_vmcnt<A_FULL>();
+                else wait_vmcnt<0>();
+            }
+            // A bare barrier: the loads this barrier publishes were waited for just
+            // above, every LDS read of this sub-step has been consumed by its MFMA,
+            // and the loop issues no LDS stores, so __syncthreads' release fence
+            // (which would drain the loads still in flight) is not needed.
+            __builtin_amdgcn_s_barrier();
+        }
+    };
+    for (int step = 0; step < nsteps; step += 2) {
+        k_step(step, lds_a0, lds_a1, 0);
+        if (step + 1 < nsteps) k_step(step + 1, lds_a1, lds_a0, 1);
     }
 
     // ---------------------------------------------------------------- epilogue
@@ -262,7 +351,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     uint16_t* out = (uint16_t*)a.out;
     uint16_t* act = (uint16_t*)a.act_out;
     const uint16_t* res = (const uint16_t*)a.res;
-    float* red = (float*)&lds_a[0][0];  // [WN][4 M-waves][MF][16 pixels]
+    float* red = (float*)&lds_a0[0];  // [WN][4 M-waves][MF][16 pixels]
 
     auto pixel_of = [&](int m, int i, int& y, int& x) {
         const int k = 4 * g + i;  // pixel within the 16-pixel fragment

@@ -312,20 +312,30 @@ def test_decoder_full_channels_tiny_frame():
 
 
 def test_plan_create_failure_releases_everything(monkeypatch):
-    """An allocation that fails part-way through plan creation returns ENOMEM,
-    leaves no plan and no device memory behind."""
+    """Failing allocation k of plan creation (k = 1, 2, ... until creation needs
+    fewer) returns ENOMEM and leaves no plan and no device memory behind."""
     say("boundary: injected allocation failure")
-    wt = synth.bf16(synth.conv_weight(96, 64, 3, 3, 3, synth.seed(7, 9))).cuda()
-    g = synth.gain(96, synth.seed(7, 10)).cuda()
+    c, h, w = 32, 24, 40
+    ps = {n: {"w": synth.bf16(synth.conv_weight(c, c, 3, 3, 3, synth.seed(7, 20 + i))).cuda(),
+              "g": synth.gain(c, synth.seed(7, 30 + i)).cuda(), "b": synth.bias(c, synth.seed(7, 40 + i)).cuda()}
+          for i, n in enumerate(("c1", "c2"))}
+    ops = S.resblock_ops(c, ps["c1"], ps["c2"])
     torch.cuda.synchronize()
     free0 = torch.cuda.mem_get_info()[0]
-    for k in (1, 2, 3):
+    failures = 0
+    for k in range(1, 32):
         monkeypatch.setenv("CC3D_TEST_FAIL_ALLOC", str(k))
-        with pytest.raises(C.Cc3dError) as e:
-            P.conv_plan(wt, 64, 96, gamma=g, act=True, max_chunk_t=8)
-        assert e.value.status == C.ENOMEM
+        try:
+            plan = P.stack_plan(ops, c, h, w, max_chunk_t=4)
+        except C.Cc3dError as e:
+            assert e.status == C.ENOMEM
+            failures += 1
+            continue
+        del plan  # creation needed fewer than k allocations
+        break
+    assert failures >= 5  # slots, packed weights, biases, gains
     monkeypatch.delenv("CC3D_TEST_FAIL_ALLOC")
     torch.cuda.synchronize()
     assert torch.cuda.mem_get_info()[0] >= free0 - (2 << 20)
-    plan = P.conv_plan(wt, 64, 96, gamma=g, act=True, max_chunk_t=8)  # and it still works
+    plan = P.stack_plan(ops, c, h, w, max_chunk_t=4)  # and creation still works
     assert plan.state_bytes > 0
