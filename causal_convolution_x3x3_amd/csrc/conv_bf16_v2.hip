@@ -16,6 +16,9 @@
 //   sub-step's B and the next step's A are fetched into registers while the
 //   current sub-step runs, then written to the idle buffers: one barrier per
 //   sub-step.
+// * The weights are the MFMA's row operand and the pixels its column operand,
+//   so each lane's accumulators are four consecutive output channels of one
+//   pixel: the epilogue moves 8-byte vectors.
 // * A fragments are reused from registers.  up_s = 1: the fragment of LDS row s
 //   (shifted by d) serves output rows s-b for the three row taps b.  up_s = 2:
 //   with nearest upsampling, output phase (p, q) and tap (b, d) read source
@@ -42,6 +45,27 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
     if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
     u += 0x7fffu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
+}
+
+// Two floats to a bf16 pair (low half = lo), round to nearest even: gfx950's
+// v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
+// 1/sqrt(mean of squares + eps) and SiLU(z) = z / (1 + e^-z) on the hardware's
+// transcendental units (v_rsq_f32, v_exp_f32, v_rcp_f32; about 1 ulp of fp32
+// each, far below the bf16 rounding of the stored result).
+__device__ __forceinline__ float rms_scale(float mean_sq, float eps)
+{
+    return __builtin_amdgcn_rsqf(mean_sq + eps);
+}
+__device__ __forceinline__ float silu(float z)
+{
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
 }
 
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
@@ -281,7 +305,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
                         if (r >= 0 && r < G::TS_H) {
 #pragma unroll
                             for (int f = 0; f < NFW; ++f)
-                                acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[b][f], acc[r][f], 0, 0, 0);
+                                acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bq[b][f], av, acc[r][f], 0, 0, 0);
                         }
                     }
                 }
@@ -306,9 +330,9 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
 #pragma unroll
                                 for (int f = 0; f < NFW; ++f) {
                                     acc[rr * 4 + p * 2 + 0][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                        a0, bq[b][f], acc[rr * 4 + p * 2 + 0][f], 0, 0, 0);
+                                        bq[b][f], a0, acc[rr * 4 + p * 2 + 0][f], 0, 0, 0);
                                     acc[rr * 4 + p * 2 + 1][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                        a1, bq[b][f], acc[rr * 4 + p * 2 + 1][f], 0, 0, 0);
+                                        bq[b][f], a1, acc[rr * 4 + p * 2 + 1][f], 0, 0, 0);
                                 }
                             }
                     }
@@ -343,85 +367,142 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     }
 
     // ---------------------------------------------------------------- epilogue
-    // v = acc + bias (+ res), rounded to bf16 and stored.  act = SiLU(RMSNorm(v))
-    // from the rounded value: the channel sum of squares is reduced over the 16
-    // lanes that hold one pixel, then over the WN waves through LDS (the main
-    // loop's last barrier has retired every read of lds_a).
-    const int n0 = nb * NTILE + wn * NFW * 16;
+    // The MFMAs above take the weights as the row operand, so acc[m][f] holds
+    // D[channel][pixel]: lane (g, k16) has channels 16*F + 4g .. 16*F + 4g + 3
+    // (F = wn*NFW + f) of pixel k16 of fragment m -- four consecutive channels,
+    // moved with 8-byte loads and stores.
+    //
+    // v = acc + bias (+ res), rounded to bf16 and stored; the rounded value stays
+    // in acc.  act = SiLU(RMSNorm(v)) from it: the sum of squares over a pixel's
+    // channels is reduced in-lane, over the four lanes of that pixel (g), then
+    // over the WN waves through LDS (the main loop's loads have all landed and its
+    // reads retired, so lds_a0 is free).
+    wait_vmcnt<0>();
+    __syncthreads();
+    const int n0 = nb * NTILE + wn * NFW * 16 + 4 * g;  // first channel of this lane in fragment f = 0
     uint16_t* out = (uint16_t*)a.out;
     uint16_t* act = (uint16_t*)a.act_out;
     const uint16_t* res = (const uint16_t*)a.res;
     float* red = (float*)&lds_a0[0];  // [WN][4 M-waves][MF][16 pixels]
+    const bool vec_ok = (a.cout & 3) == 0;  // 4-channel groups never straddle cout
 
-    auto pixel_of = [&](int m, int i, int& y, int& x) {
-        const int k = 4 * g + i;  // pixel within the 16-pixel fragment
+    auto pixel_of = [&](int m, int& y, int& x) {
         if (UP == 1) {
             y = i0 + m;
-            x = j0 + 16 * wm + k;
+            x = j0 + 16 * wm + k16;
         } else {
             const int rr = m >> 2, p = (m >> 1) & 1, q = m & 1;
             y = 2 * (i0 + 2 * wm + rr) + p;
-            x = 2 * (j0 + k) + q;
+            x = 2 * (j0 + k16) + q;
         }
     };
-    auto value = [&](int m, int i, int f, int64_t pbase, bool valid) -> float {
-        const int n = n0 + 16 * f + k16;
-        if (n >= a.cout) return 0.f;
-        float v = acc[m][f][i];
-        if (a.bias) v += a.bias[n];
-        if (res && valid) v += bf2f(res[pbase + n]);
-        return bf2f(f2bf(v));
+    auto pixel_base = [&](int m, bool& valid) -> int64_t {
+        int y, x;
+        pixel_of(m, y, x);
+        valid = y < a.h_out && x < a.w_out;
+        return (((int64_t)t * a.h_out + y) * a.w_out + x) * a.cout;
     };
 
-    // pass 1: store v; per-pixel partial sums of squares for the act
-#pragma clang loop unroll(full)
-    for (int m = 0; m < MF; ++m) {
-#pragma clang loop unroll(full)
-        for (int i = 0; i < 4; ++i) {
-            int y, x;
-            pixel_of(m, i, y, x);
-            const bool valid = y < a.h_out && x < a.w_out;
-            const int64_t pbase = (((int64_t)t * a.h_out + y) * a.w_out + x) * a.cout;
-            float ss = 0.f;
+    // The residual is loaded for the whole tile before anything is stored: the
+    // compiler may not move a load of `res` past a store to `out` (they could
+    // alias as far as it knows), so interleaved loads would each pay the full
+    // memory latency.
+    uint2 rv[MF][NFW];
+#pragma unroll
+    for (int m = 0; m < MF; ++m)
+#pragma unroll
+        for (int f = 0; f < NFW; ++f) rv[m][f] = make_uint2(0u, 0u);
+    if (res && vec_ok) {
+#pragma unroll
+        for (int m = 0; m < MF; ++m) {
+            bool valid;
+            const int64_t pbase = pixel_base(m, valid);
 #pragma unroll
             for (int f = 0; f < NFW; ++f) {
-                const float v = value(m, i, f, pbase, valid);
-                const int n = n0 + 16 * f + k16;
-                if (out && valid && n < a.cout) out[pbase + n] = f2bf(v);
-                ss += v * v;
-            }
-            if (act) {
-                ss += __shfl_xor(ss, 1, 64);
-                ss += __shfl_xor(ss, 2, 64);
-                ss += __shfl_xor(ss, 4, 64);
-                ss += __shfl_xor(ss, 8, 64);
-                if (k16 == 0) red[((wn * 4 + wm) * MF + m) * 16 + 4 * g + i] = ss;
+                const int n = n0 + 16 * f;
+                if (valid && n < a.cout) rv[m][f] = *(const uint2*)(res + pbase + n);
             }
         }
     }
+
+    // pass 1: v, stored; per-pixel partial sums of squares
+#pragma clang loop unroll(full)
+    for (int m = 0; m < MF; ++m) {
+        bool valid;
+        const int64_t pbase = pixel_base(m, valid);
+        float ss = 0.f;
+#pragma unroll
+        for (int f = 0; f < NFW; ++f) {
+            const int n = n0 + 16 * f;  // channels n .. n+3
+            float v[4] = {acc[m][f][0], acc[m][f][1], acc[m][f][2], acc[m][f][3]};
+            if (n < a.cout && vec_ok) {
+                if (a.bias) {
+                    const float4 bv = *(const float4*)(a.bias + n);
+                    v[0] += bv.x; v[1] += bv.y; v[2] += bv.z; v[3] += bv.w;
+                }
+                if (res) {
+                    v[0] += bf2f((uint16_t)(rv[m][f].x & 0xffffu));
+                    v[1] += bf2f((uint16_t)(rv[m][f].x >> 16));
+                    v[2] += bf2f((uint16_t)(rv[m][f].y & 0xffffu));
+                    v[3] += bf2f((uint16_t)(rv[m][f].y >> 16));
+                }
+                const uint2 hb = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                v[0] = bf2f((uint16_t)(hb.x & 0xffffu));
+                v[1] = bf2f((uint16_t)(hb.x >> 16));
+                v[2] = bf2f((uint16_t)(hb.y & 0xffffu));
+                v[3] = bf2f((uint16_t)(hb.y >> 16));
+                if (out && valid) *(uint2*)(out + pbase + n) = hb;
+            } else if (n < a.cout) {  // cout not a multiple of 4: element by element
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (n + i >= a.cout) { v[i] = 0.f; continue; }
+                    if (a.bias) v[i] += a.bias[n + i];
+                    if (res && valid) v[i] += bf2f(res[pbase + n + i]);
+                    const uint16_t hb = f2bf(v[i]);
+                    v[i] = bf2f(hb);
+                    if (out && valid) out[pbase + n + i] = hb;
+                }
+            } else {
+                v[0] = v[1] = v[2] = v[3] = 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[m][f][i] = v[i];
+                ss += v[i] * v[i];
+            }
+        }
+        if (act) {
+            ss += __shfl_xor(ss, 16, 64);
+            ss += __shfl_xor(ss, 32, 64);
+            if (g == 0) red[((wn * 4 + wm) * MF + m) * 16 + k16] = ss;
+        }
+    }
     if (!act) return;
+    // act over 4-channel groups: act requires cout % 4 == 0 (checked on the host)
+    float4 gm[NFW];
+#pragma unroll
+    for (int f = 0; f < NFW; ++f) {
+        const int n = n0 + 16 * f;
+        gm[f] = n < a.cout ? *(const float4*)(a.gamma + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const float inv_c = 1.0f / (float)a.cout;
     __syncthreads();
     // pass 2: the act from the full channel sum
 #pragma clang loop unroll(full)
     for (int m = 0; m < MF; ++m) {
-#pragma clang loop unroll(full)
-        for (int i = 0; i < 4; ++i) {
-            int y, x;
-            pixel_of(m, i, y, x);
-            const bool valid = y < a.h_out && x < a.w_out;
-            const int64_t pbase = (((int64_t)t * a.h_out + y) * a.w_out + x) * a.cout;
-            float ss = 0.f;
+        bool valid;
+        const int64_t pbase = pixel_base(m, valid);
+        float ss = 0.f;
 #pragma unroll
-            for (int h = 0; h < WN; ++h) ss += red[((h * 4 + wm) * MF + m) * 16 + 4 * g + i];
-            const float inv = 1.0f / sqrtf(ss / (float)a.cout + a.eps);
+        for (int h = 0; h < WN; ++h) ss += red[((h * 4 + wm) * MF + m) * 16 + k16];
+        const float inv = rms_scale(ss * inv_c, a.eps);
 #pragma unroll
-            for (int f = 0; f < NFW; ++f) {
-                const int n = n0 + 16 * f + k16;
-                if (n < a.cout && valid) {
-                    const float zz = a.gamma[n] * value(m, i, f, pbase, valid) * inv;
-                    act[pbase + n] = f2bf(zz / (1.0f + expf(-zz)));
-                }
-            }
+        for (int f = 0; f < NFW; ++f) {
+            const int n = n0 + 16 * f;
+            if (!valid || n >= a.cout) continue;
+            const float z0 = silu(gm[f].x * acc[m][f][0] * inv), z1 = silu(gm[f].y * acc[m][f][1] * inv);
+            const float z2 = silu(gm[f].z * acc[m][f][2] * inv), z3 = silu(gm[f].w * acc[m][f][3] * inv);
+            *(uint2*)(act + pbase + n) = make_uint2(pack_bf16x2(z0, z1), pack_bf16x2(z2, z3));
         }
     }
 }

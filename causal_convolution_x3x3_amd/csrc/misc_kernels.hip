@@ -155,6 +155,133 @@ __global__ __launch_bounds__(256) void norm_act_kernel(NormArgs a)
     }
 }
 
+// ----------------------------------------------------- norm_act (bf16) ---
+// Two floats to a bf16 pair (low half = lo), round to nearest even
+// (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+__device__ __forceinline__ void unpack8(const uint4& r, float v[8])
+{
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ uint4 pack8(const float v[8])
+{
+    return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                      pack_bf16x2(v[6], v[7]));
+}
+// SiLU on the hardware's exp and reciprocal (about 1 ulp of fp32 each, far
+// below the bf16 rounding of the stored result).
+__device__ __forceinline__ float silu_fast(float z)
+{
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
+
+// LPP lanes per pixel, each holding U 16-byte chunks (8 channels) of it: chunk
+// l + LPP*u for lane l of the group, so C = 8 * LPP * U.  All loads of a thread
+// are issued before its first store.
+template <int LPP, int U>
+__global__ __launch_bounds__(256) void norm_act_bf16_kernel(NormArgs a)
+{
+    const int l = threadIdx.x & (LPP - 1);
+    const int64_t pix = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / LPP;
+    if (pix >= a.n_pix) return;  // whole LPP-lane groups leave together
+    const uint4* src = (const uint4*)a.src + pix * (LPP * U);
+    float v[U][8];
+    uint4 r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) r[u] = src[l + LPP * u];
+    if (a.res) {
+        const uint4* rs = (const uint4*)a.res + pix * (LPP * U);
+        uint4 q[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) q[u] = rs[l + LPP * u];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float w[8];
+            unpack8(r[u], v[u]);
+            unpack8(q[u], w);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[u][i] += w[i];
+            r[u] = pack8(v[u]);  // v is stored rounded; the act reads the rounded value
+        }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        unpack8(r[u], v[u]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss += v[u][i] * v[u][i];
+    }
+#pragma unroll
+    for (int o = 1; o < LPP; o <<= 1) ss += __shfl_xor(ss, o, LPP);
+    if (a.out) {
+        uint4* dst = (uint4*)a.out + pix * (LPP * U);
+#pragma unroll
+        for (int u = 0; u < U; ++u) dst[l + LPP * u] = r[u];
+    }
+    if (!a.act_out) return;
+    const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / (float)a.c) + a.eps);
+    uint4* dst = (uint4*)a.act_out + pix * (LPP * U);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int c0 = 8 * (l + LPP * u);
+        const float4 g0 = *(const float4*)(a.gamma + c0);
+        const float4 g1 = *(const float4*)(a.gamma + c0 + 4);
+        const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        float o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = silu_fast(gm[i] * v[u][i] * inv);
+        dst[l + LPP * u] = pack8(o);
+    }
+}
+
+// (lanes per pixel, chunks per lane) for a bf16 norm over c channels, or false
+// when c is not 8 * LPP * U with LPP in {4, 8, 16} and U <= 6.
+bool norm_bf16_shape(int c, int& lpp, int& u)
+{
+    if (c % 8 != 0) return false;
+    const int chunks = c / 8;
+    for (int cand : {4, 8, 16})
+        if (chunks % cand == 0 && chunks / cand <= 6) {
+            lpp = cand;
+            u = chunks / cand;
+            return true;
+        }
+    return false;
+}
+
+template <int LPP, int U>
+hipError_t launch_norm_bf16(const NormArgs& a, hipStream_t s)
+{
+    const int64_t blocks = (a.n_pix * LPP + 255) / 256;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((norm_act_bf16_kernel<LPP, U>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int LPP>
+hipError_t launch_norm_bf16_u(const NormArgs& a, int u, hipStream_t s)
+{
+    switch (u) {
+    case 1: return launch_norm_bf16<LPP, 1>(a, s);
+    case 2: return launch_norm_bf16<LPP, 2>(a, s);
+    case 3: return launch_norm_bf16<LPP, 3>(a, s);
+    case 4: return launch_norm_bf16<LPP, 4>(a, s);
+    case 5: return launch_norm_bf16<LPP, 5>(a, s);
+    case 6: return launch_norm_bf16<LPP, 6>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 // ----------------------------------------------------------- cache update --
 template <typename V>
 __global__ __launch_bounds__(256) void cache_update_kernel(ZWindow z, int t_v, void* dst, int eb)
@@ -224,6 +351,13 @@ hipError_t launch_norm_act(const NormArgs& a, int elem_bytes, hipStream_t s)
     const int64_t threads = a.n_pix * 32;
     const int64_t blocks = (threads + 255) / 256;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    int lpp = 0, u = 0;
+    const bool aligned = (((uintptr_t)a.src | (uintptr_t)a.res | (uintptr_t)a.out | (uintptr_t)a.act_out) & 15u) == 0;
+    if (elem_bytes == 2 && aligned && norm_bf16_shape(a.c, lpp, u)) {
+        if (lpp == 4) return launch_norm_bf16_u<4>(a, u, s);
+        if (lpp == 8) return launch_norm_bf16_u<8>(a, u, s);
+        return launch_norm_bf16_u<16>(a, u, s);
+    }
     if (elem_bytes == 2)
         hipLaunchKernelGGL(norm_act_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, s, a);
     else
