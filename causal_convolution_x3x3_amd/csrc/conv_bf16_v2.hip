@@ -12,10 +12,12 @@
 // * K is walked in steps of (temporal tap a, 32 channels); each step in three
 //   sub-steps, one per spatial column tap d.  A sub-step needs the step's input
 //   tile (A, in LDS for the whole step) and the weights of the three taps (b, d),
-//   b = 0..2 (B, 3 x NTILE x 32).  Both are double-buffered in LDS; the next
-//   sub-step's B and the next step's A are fetched into registers while the
-//   current sub-step runs, then written to the idle buffers: one barrier per
-//   sub-step.
+//   b = 0..2 (B, 3 x NTILE x 32).  The next step's A goes from global memory
+//   straight into an idle LDS buffer (buffer loads with the LDS flag) while the
+//   current step runs.  B takes one of two paths: through LDS the same way
+//   (three buffers, two sub-steps ahead; one barrier per sub-step), or straight
+//   into registers one sub-step ahead, every wave loading its own fragments
+//   from L2 (one barrier per K step).
 // * The weights are the MFMA's row operand and the pixels its column operand,
 //   so each lane's accumulators are four consecutive output channels of one
 //   pixel: the epilogue moves 8-byte vectors.
@@ -146,7 +148,7 @@ __device__ __forceinline__ void wait_vmcnt()
 // column only and every fragment read is a base register plus a constant.
 // Weights are prefetched two sub-steps ahead (three LDS buffers; two, one
 // sub-step ahead, where three do not fit), the input tile one K step ahead.
-template <int UP, int NF, int WN>
+template <int UP, int NF, int WN, bool BG>
 __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
 {
     using G = Geo<UP>;
@@ -174,11 +176,13 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
 
     // one LDS variable per buffer: the compiler then knows that loads into one
     // buffer do not touch the buffer being read, and does not wait for them
-    __shared__ uint4 lds_a0[A_CH];
-    __shared__ uint4 lds_a1[A_CH];
-    __shared__ uint4 lds_b0[B_CH];
-    __shared__ uint4 lds_b1[B_CH];
-    __shared__ uint4 lds_b2[NBB == 3 ? B_CH : 1];
+    // (BG: tile buffers padded to whole load rounds, so that every lane issues
+    // every round and no load sits behind a branch)
+    __shared__ uint4 lds_a0[BG ? A_IT * NT : A_CH];
+    __shared__ uint4 lds_a1[BG ? A_IT * NT : A_CH];
+    __shared__ uint4 lds_b0[BG ? 1 : B_CH];
+    __shared__ uint4 lds_b1[BG ? 1 : B_CH];
+    __shared__ uint4 lds_b2[(!BG && NBB == 3) ? B_CH : 1];
 
     const int tiles_w = (a.w_in + G::TS_W - 1) / G::TS_W;
     const int tiles_h = (a.h_in + G::TS_H - 1) / G::TS_H;
@@ -258,112 +262,193 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
         b_off[f] = nl * 64 + ((g ^ swz(nl)) << 4);
     }
 
-    // prologue: step 0's tile, the first NBB-1 sub-steps' weights
-    issue_a(0, lds_a0);
-    issue_b(0, lds_b0);
-    if (NBB == 3 && nsub > 1) issue_b(1, lds_b1);
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-
-    // One K step = three sub-steps (column taps d = 0, 1, 2), unrolled so the tap
-    // and every LDS offset are compile-time constants; steps are taken in pairs
-    // so that every buffer a sub-step reads or fills is a fixed LDS variable.
-    // Sub-step `sub` reads weight buffer sub % NBB and input buffer step % 2.
-    auto k_step = [&](int step, const uint4* aread, uint4* awrite, const int par) {
-        const bool more_a = step + 1 < nsteps;
-        const int sub0 = 3 * step;
+    // The MFMAs of one sub-step (column tap d) from input buffer `aread` and the
+    // B fragments bq[b][f] of taps (b, d).
+    auto mma = [&](const int d, const uint4* aread, const bf16x8 (&bq)[3][NFW]) {
+        if (UP == 1) {
+            // LDS row s holds source row i0 + s - 1; output row r reads rows r+b.
+            const int base = col_off(16 * wm + k16 + d);
 #pragma unroll
-        for (int d = 0; d < 3; ++d) {
-            const int sub = sub0 + d;
-            // NBB = 3: sub % 3 == d; NBB = 2: sub % 2 == (par + d) % 2 with par = step % 2.
-            // The buffer written now, (sub + NBB - 1) % NBB, was last read in
-            // sub-step sub - 1 (retired by its barrier).
-            const int bcur = NBB == 3 ? d : ((par + d) & 1);
-            const int bnext = NBB == 3 ? (d + 2) % 3 : (bcur ^ 1);
-            const uint4* bread = bcur == 0 ? lds_b0 : (bcur == 1 ? lds_b1 : lds_b2);
-            uint4* bwrite = bnext == 0 ? lds_b0 : (bnext == 1 ? lds_b1 : lds_b2);
-            const bool ahead_b = sub + NBB - 1 < nsub;
-            if (ahead_b) issue_b(sub + NBB - 1, bwrite);
-            if (d == 0 && more_a) issue_a(step + 1, awrite);
+            for (int s = 0; s < G::TS_H + 2; ++s) {
+                const bf16x8 av = lds_frag(aread, base + s * ROWB);
+#pragma unroll
+                for (int b = 0; b < 3; ++b) {
+                    const int r = s - b;
+                    if (r >= 0 && r < G::TS_H) {
+#pragma unroll
+                        for (int f = 0; f < NFW; ++f)
+                            acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bq[b][f], av, acc[r][f], 0, 0, 0);
+                    }
+                }
+            }
+        } else {
+            // M fragment m = rr*4 + p*2 + q: source row 2*wm + rr, phase (p, q).
+            // Column offsets of this d: q=0 -> floor((d-1)/2), q=1 -> floor(d/2).
+            const int ox0 = (d - 1) >> 1, ox1 = d >> 1;
+            const int base0 = col_off(k16 + ox0 + 1) + 2 * wm * ROWB;
+            const int base1 = col_off(k16 + ox1 + 1) + 2 * wm * ROWB;
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+#pragma unroll
+                for (int oy = -1; oy <= 1; ++oy) {
+                    const int row = rr + oy + 1;  // plus 2*wm, folded into the bases
+                    const bf16x8 a0 = lds_frag(aread, base0 + row * ROWB);
+                    const bf16x8 a1 = (ox0 == ox1) ? a0 : lds_frag(aread, base1 + row * ROWB);
+#pragma unroll
+                    for (int p = 0; p < 2; ++p)
+#pragma unroll
+                        for (int b = 0; b < 3; ++b) {
+                            if (((p + b - 1) >> 1) != oy) continue;
+#pragma unroll
+                            for (int f = 0; f < NFW; ++f) {
+                                acc[rr * 4 + p * 2 + 0][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    bq[b][f], a0, acc[rr * 4 + p * 2 + 0][f], 0, 0, 0);
+                                acc[rr * 4 + p * 2 + 1][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    bq[b][f], a1, acc[rr * 4 + p * 2 + 1][f], 0, 0, 0);
+                            }
+                        }
+                }
+            }
+        }
+    };
 
-            // B fragments of taps (b, d), b = 0..2, for this wave's channels
-            bf16x8 bq[3][NFW];
+    if constexpr (BG) {
+        // Weights straight from global memory (L2; every workgroup reads the same
+        // few hundred KB) into registers, one sub-step ahead; only the input tile
+        // goes through LDS, so the workgroup meets at one barrier per K step.
+        const uint4* wg = (const uint4*)a.wpk + (size_t)nb * nsub * B_CH;
+        int bidx[NFW];
+#pragma unroll
+        for (int f = 0; f < NFW; ++f) {
+            const int nl = 16 * (wn * NFW + f) + k16;
+            bidx[f] = nl * 4 + (g ^ swz(nl));
+        }
+        auto load_b = [&](int sub, bf16x8 (&dst)[3][NFW]) {
+            const uint4* p = wg + (size_t)sub * B_CH;
 #pragma unroll
             for (int b = 0; b < 3; ++b)
 #pragma unroll
-                for (int f = 0; f < NFW; ++f) bq[b][f] = lds_frag(bread, b_off[f] + b * NTILE * 64);
-
-            if (UP == 1) {
-                // LDS row s holds source row i0 + s - 1; output row r reads rows r+b.
-                const int base = col_off(16 * wm + k16 + d);
+                for (int f = 0; f < NFW; ++f) dst[b][f] = as_bf16x8(p[b * NTILE * 4 + bidx[f]]);
+        };
+        // Every load below is issued unconditionally (out-of-range slots read
+        // zeros into the padding; the last sub-step reloads its own weights, the
+        // last K step the first tile into the idle buffer): a load behind a branch
+        // makes the compiler's own waits assume it may be missing and wait for
+        // younger loads as well.
+        auto issue_a_all = [&](int step, uint4* buf) {
+            const int ta = step / a.kchunks, kc = step - ta * a.kchunks;
+            const uint16_t* fp = zframe(a.z, t + ta);
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(fp, fp ? frame_bytes : 0u);
+            const int ch0 = kc * 32;
 #pragma unroll
-                for (int s = 0; s < G::TS_H + 2; ++s) {
-                    const bf16x8 av = lds_frag(aread, base + s * ROWB);
-#pragma unroll
-                    for (int b = 0; b < 3; ++b) {
-                        const int r = s - b;
-                        if (r >= 0 && r < G::TS_H) {
-#pragma unroll
-                            for (int f = 0; f < NFW; ++f)
-                                acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bq[b][f], av, acc[r][f], 0, 0, 0);
-                        }
-                    }
-                }
-            } else {
-                // M fragment m = rr*4 + p*2 + q: source row 2*wm + rr, phase (p, q).
-                // Column offsets of this d: q=0 -> floor((d-1)/2), q=1 -> floor(d/2).
-                const int ox0 = (d - 1) >> 1, ox1 = d >> 1;
-                const int base0 = col_off(k16 + ox0 + 1) + 2 * wm * ROWB;
-                const int base1 = col_off(k16 + ox1 + 1) + 2 * wm * ROWB;
-#pragma unroll
-                for (int rr = 0; rr < 2; ++rr) {
-#pragma unroll
-                    for (int oy = -1; oy <= 1; ++oy) {
-                        const int row = rr + oy + 1;  // plus 2*wm, folded into the bases
-                        const bf16x8 a0 = lds_frag(aread, base0 + row * ROWB);
-                        const bf16x8 a1 = (ox0 == ox1) ? a0 : lds_frag(aread, base1 + row * ROWB);
-#pragma unroll
-                        for (int p = 0; p < 2; ++p)
-#pragma unroll
-                            for (int b = 0; b < 3; ++b) {
-                                if (((p + b - 1) >> 1) != oy) continue;
-#pragma unroll
-                                for (int f = 0; f < NFW; ++f) {
-                                    acc[rr * 4 + p * 2 + 0][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                        bq[b][f], a0, acc[rr * 4 + p * 2 + 0][f], 0, 0, 0);
-                                    acc[rr * 4 + p * 2 + 1][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                        bq[b][f], a1, acc[rr * 4 + p * 2 + 1][f], 0, 0, 0);
-                                }
-                            }
-                    }
-                }
+            for (int it = 0; it < A_IT; ++it) {
+                const uint32_t off = (ch0 + a_ch[it] < a.cin) ? a_off[it] + (uint32_t)(ch0 * 2) : OOB;
+                load_to_lds(r, off, buf + NT * it + wave * 64);
             }
-
-            // Before the barrier: the weights of sub + 1 (issued during sub - 1) and,
-            // at d == 2, the next tile (issued at d == 0) must have landed.  Loads
-            // complete in issue order; the waits leave the younger ones in flight.
-            if (NBB == 3) {
-                if (ahead_b && more_a) {
-                    if (d == 2) wait_vmcnt<B_FULL>();
-                    else wait_vmcnt<A_FULL + B_FULL>();
-                } else {
-                    wait_vmcnt<0>();
+        };
+        bf16x8 bq0[3][NFW], bq1[3][NFW];
+        issue_a_all(0, lds_a0);
+        load_b(0, bq0);
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        // Sub-step `sub` uses bq0 when sub is even; 3*step + d has the parity of
+        // step + d.
+        auto k_step = [&](int step, const uint4* aread, uint4* awrite, const int par) {
+            const int next_a = step + 1 < nsteps ? step + 1 : 0;
+            auto sub_step = [&](const int d, const bf16x8 (&cur)[3][NFW], bf16x8 (&nxt)[3][NFW]) {
+                const int sub = 3 * step + d;
+                load_b(sub + 1 < nsub ? sub + 1 : sub, nxt);
+                if (d == 0) issue_a_all(next_a, awrite);
+                // keep the scheduler from sinking these loads towards their first
+                // use in the next sub-step (it would, to shorten live ranges)
+                __builtin_amdgcn_sched_barrier(0);
+                mma(d, aread, cur);
+                if (d == 2) {
+                    // The next tile (issued at d == 0, before this sub-step's weight
+                    // loads) must have landed for every wave; loads complete in
+                    // issue order, so only those weight loads may stay in flight.
+                    wait_vmcnt<3 * NFW>();
+                    __builtin_amdgcn_s_barrier();
                 }
+            };
+            if (par == 0) {
+                sub_step(0, bq0, bq1);
+                sub_step(1, bq1, bq0);
+                sub_step(2, bq0, bq1);
             } else {
-                // the weights of sub + 1 were issued in this sub-step, before the tile
-                if (d == 0 && more_a) wait_vmcnt<A_FULL>();
-                else wait_vmcnt<0>();
+                sub_step(0, bq1, bq0);
+                sub_step(1, bq0, bq1);
+                sub_step(2, bq1, bq0);
             }
-            // A bare barrier: the loads this barrier publishes were waited for just
-            // above, every LDS read of this sub-step has been consumed by its MFMA,
-            // and the loop issues no LDS stores, so __syncthreads' release fence
-            // (which would drain the loads still in flight) is not needed.
-            __builtin_amdgcn_s_barrier();
+        };
+        for (int step = 0; step < nsteps; step += 2) {
+            k_step(step, lds_a0, lds_a1, 0);
+            if (step + 1 < nsteps) k_step(step + 1, lds_a1, lds_a0, 1);
         }
-    };
-    for (int step = 0; step < nsteps; step += 2) {
-        k_step(step, lds_a0, lds_a1, 0);
-        if (step + 1 < nsteps) k_step(step + 1, lds_a1, lds_a0, 1);
+    } else {
+        // prologue: step 0's tile, the first NBB-1 sub-steps' weights
+        issue_a(0, lds_a0);
+        issue_b(0, lds_b0);
+        if (NBB == 3 && nsub > 1) issue_b(1, lds_b1);
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+
+        // One K step = three sub-steps (column taps d = 0, 1, 2), unrolled so the tap
+        // and every LDS offset are compile-time constants; steps are taken in pairs
+        // so that every buffer a sub-step reads or fills is a fixed LDS variable.
+        // Sub-step `sub` reads weight buffer sub % NBB and input buffer step % 2.
+        auto k_step = [&](int step, const uint4* aread, uint4* awrite, const int par) {
+            const bool more_a = step + 1 < nsteps;
+            const int sub0 = 3 * step;
+    #pragma unroll
+            for (int d = 0; d < 3; ++d) {
+                const int sub = sub0 + d;
+                // NBB = 3: sub % 3 == d; NBB = 2: sub % 2 == (par + d) % 2 with par = step % 2.
+                // The buffer written now, (sub + NBB - 1) % NBB, was last read in
+                // sub-step sub - 1 (retired by its barrier).
+                const int bcur = NBB == 3 ? d : ((par + d) & 1);
+                const int bnext = NBB == 3 ? (d + 2) % 3 : (bcur ^ 1);
+                const uint4* bread = bcur == 0 ? lds_b0 : (bcur == 1 ? lds_b1 : lds_b2);
+                uint4* bwrite = bnext == 0 ? lds_b0 : (bnext == 1 ? lds_b1 : lds_b2);
+                const bool ahead_b = sub + NBB - 1 < nsub;
+                if (ahead_b) issue_b(sub + NBB - 1, bwrite);
+                if (d == 0 && more_a) issue_a(step + 1, awrite);
+
+                // B fragments of taps (b, d), b = 0..2, for this wave's channels
+                bf16x8 bq[3][NFW];
+    #pragma unroll
+                for (int b = 0; b < 3; ++b)
+    #pragma unroll
+                    for (int f = 0; f < NFW; ++f) bq[b][f] = lds_frag(bread, b_off[f] + b * NTILE * 64);
+
+                mma(d, aread, bq);
+
+                // Before the barrier: the weights of sub + 1 (issued during sub - 1) and,
+                // at d == 2, the next tile (issued at d == 0) must have landed.  Loads
+                // complete in issue order; the waits leave the younger ones in flight.
+                if (NBB == 3) {
+                    if (ahead_b && more_a) {
+                        if (d == 2) wait_vmcnt<B_FULL>();
+                        else wait_vmcnt<A_FULL + B_FULL>();
+                    } else {
+                        wait_vmcnt<0>();
+                    }
+                } else {
+                    // the weights of sub + 1 were issued in this sub-step, before the tile
+                    if (d == 0 && more_a) wait_vmcnt<A_FULL>();
+                    else wait_vmcnt<0>();
+                }
+                // A bare barrier: the loads this barrier publishes were waited for just
+                // above, every LDS read of this sub-step has been consumed by its MFMA,
+                // and the loop issues no LDS stores, so __syncthreads' release fence
+                // (which would drain the loads still in flight) is not needed.
+                __builtin_amdgcn_s_barrier();
+            }
+        };
+        for (int step = 0; step < nsteps; step += 2) {
+            k_step(step, lds_a0, lds_a1, 0);
+            if (step + 1 < nsteps) k_step(step + 1, lds_a1, lds_a0, 1);
+        }
     }
 
     // ---------------------------------------------------------------- epilogue
@@ -507,7 +592,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     }
 }
 
-template <int UP, int NF, int WN>
+template <int UP, int NF, int WN, bool BG>
 hipError_t launch_v2(const ConvArgs& a, hipStream_t s)
 {
     using G = Geo<UP>;
@@ -515,7 +600,7 @@ hipError_t launch_v2(const ConvArgs& a, hipStream_t s)
     const int64_t total = (int64_t)tiles * a.t_out * a.nblocks;
     if (total <= 0 || total > (int64_t)0x7fffffff - 8) return hipErrorInvalidValue;
     const int64_t grid = ((total + 7) / 8) * 8;
-    hipLaunchKernelGGL((conv3_v2_kernel<UP, NF, WN>), dim3((unsigned)grid), dim3(256 * WN), 0, s, a);
+    hipLaunchKernelGGL((conv3_v2_kernel<UP, NF, WN, BG>), dim3((unsigned)grid), dim3(256 * WN), 0, s, a);
     return hipGetLastError();
 }
 
@@ -529,8 +614,13 @@ bool v2_conv_applies(int ntile, int kh, int kw, int up_s)
 hipError_t launch_conv_bf16_v2(const ConvArgs& a, hipStream_t s)
 {
     if (!v2_conv_applies(a.ntile, a.kh, a.kw, a.up_s)) return hipErrorInvalidValue;
-    if (a.up_s == 1) return a.ntile == 96 ? launch_v2<1, 6, 2>(a, s) : launch_v2<1, 8, 2>(a, s);
-    return a.ntile == 96 ? launch_v2<2, 6, 2>(a, s) : launch_v2<2, 8, 2>(a, s);
+    // Weights through LDS for up_s = 1; straight to registers for the
+    // 96-channel up_s = 2 kernel (measured faster there: its input tile is a
+    // third of the size, and the workgroup meets at a third of the barriers).
+    // The 128-channel blocks keep the weights in LDS: with them in registers
+    // the kernel no longer fits 256 VGPRs.
+    if (a.up_s == 1) return a.ntile == 96 ? launch_v2<1, 6, 2, false>(a, s) : launch_v2<1, 8, 2, false>(a, s);
+    return a.ntile == 96 ? launch_v2<2, 6, 2, true>(a, s) : launch_v2<2, 8, 2, false>(a, s);
 }
 
 }  // namespace cc3d
