@@ -277,7 +277,7 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
             if (bf16) {
                 cc3d::bf16_conv_tiling(o.cout, &r.ntile, &r.nblocks);
                 r.kchunks = (r.cin + 31) / 32;
-                r.family = cc3d::bf16_conv_family(r.ntile, o.kh, o.kw, o.up_s);
+                r.family = cc3d::bf16_conv_family(o.cout, r.cin, o.kt, o.kh, o.kw, o.up_s);
             }
         } else {
             r.cout = r.cin;
@@ -393,7 +393,7 @@ cc3d_status materialise(const cc3d_stack_desc* d, cc3d_plan* p, hipStream_t stre
         if (r.kind == CC3D_OP_CONV) {
             const size_t wbytes = (size_t)r.cout * r.cin * r.kt * r.kh * r.kw * p->elem;
             if (p->dtype == CC3D_BF16) {
-                const size_t pk = cc3d::bf16_packed_elems(r.cout, r.cin, r.kt, r.kh, r.kw) * 2;
+                const size_t pk = cc3d::bf16_packed_elems(r.cout, r.cin, r.kt, r.kh, r.kw, r.family) * 2;
                 cc3d_status st = al.alloc(&r.wpk, pk, "packed weights");
                 if (st != CC3D_OK) return st;
                 st = hip_status(cc3d::launch_pack_bf16(o.w, r.wpk, r.cout, r.cin, r.kt, r.kh, r.kw, r.family, stream),
@@ -537,7 +537,9 @@ struct ProfScope {
 std::string conv_kernel_name(const cc3d_plan* p, const OpRt& r)
 {
     char buf[64];
-    if (p->dtype == CC3D_BF16)
+    if (p->dtype == CC3D_BF16 && r.family == 3)
+        snprintf(buf, sizeof buf, "conv_bf16_head_up%d_k%d_c%d", r.up_s, r.kh, r.cout);
+    else if (p->dtype == CC3D_BF16)
         snprintf(buf, sizeof buf, "conv_bf16%s_up%d_k%d_n%d", r.family == 2 ? "_v2" : "", r.up_s, r.kh,
                  r.ntile);
     else

@@ -35,7 +35,7 @@ struct ConvArgs {
     int h_in, w_in, up_s, h_out, w_out, t_out;
     int kchunks;          // bf16: ceil(cin / 32)
     int ntile, nblocks;   // bf16: output channels per workgroup, number of such blocks
-    int family;           // bf16: kernel family (1 or 2) the weights were packed for
+    int family;           // bf16: kernel family (1, 2 or 3) the weights were packed for
 };
 
 struct NormArgs {
@@ -54,18 +54,28 @@ struct NormArgs {
 bool bf16_conv_supported(int cout, int kh, int kw, int up_s);
 void bf16_conv_tiling(int cout, int* ntile, int* nblocks);
 hipError_t launch_conv_bf16(const ConvArgs& a, hipStream_t s);
-// Repack [cout][cin][kt][kh][kw] bf16 weights into the MFMA operand blocks.
-size_t bf16_packed_elems(int cout, int cin, int kt, int kh, int kw);
+// Repack [cout][cin][kt][kh][kw] bf16 weights into the MFMA operand blocks of
+// the given kernel family.
+size_t bf16_packed_elems(int cout, int cin, int kt, int kh, int kw, int family);
 hipError_t launch_pack_bf16(const void* w, void* wpk, int cout, int cin, int kt, int kh, int kw,
                             int family, hipStream_t s);
 
 // Register-blocked 3x3 spatial kernels (conv_bf16_v2.hip) for 96/128-channel
 // output blocks; their weights are packed with the column tap outermost.
 bool v2_conv_applies(int ntile, int kh, int kw, int up_s);
-// Kernel family chosen for a bf16 conv: 2 = v2 where it applies, else 1.
-// CC3D_CONV_FAMILY=1 in the environment at plan creation keeps every conv on v1.
-int bf16_conv_family(int ntile, int kh, int kw, int up_s);
+// Kernel family chosen for a bf16 conv: 3 = the output head (conv_head.hip)
+// where it applies, 2 = v2 where it applies, else 1.  CC3D_CONV_FAMILY=1 in the
+// environment at plan creation keeps every conv on v1.
+int bf16_conv_family(int cout, int cin, int kt, int kh, int kw, int up_s);
 hipError_t launch_conv_bf16_v2(const ConvArgs& a, hipStream_t s);
+
+// Output head (conv_head.hip): 3x3x3 conv to at most 3 channels of a nearest-2x
+// upsampled input, spatial taps in the GEMM's N dimension; weights packed per
+// (32-channel chunk, N fragment) as 64 lanes x 8 channels.
+bool head_conv_applies(int cout, int cin, int kt, int kh, int kw, int up_s);
+size_t head_packed_elems(int cin);
+hipError_t launch_pack_head(const void* w, void* wpk, int cout, int cin, hipStream_t s);
+hipError_t launch_conv_head(const ConvArgs& a, hipStream_t s);
 
 // fp32 direct conv (weights used in PyTorch order, copied by the host).
 hipError_t launch_conv_f32(const ConvArgs& a, hipStream_t s);

@@ -291,15 +291,19 @@ void bf16_conv_tiling(int cout, int* ntile, int* nblocks)
     *nblocks = nt ? (cout + nt - 1) / nt : 0;
 }
 
-int bf16_conv_family(int ntile, int kh, int kw, int up_s)
+int bf16_conv_family(int cout, int cin, int kt, int kh, int kw, int up_s)
 {
     const char* e = getenv("CC3D_CONV_FAMILY");
     if (e && atoi(e) == 1) return 1;
-    return v2_conv_applies(ntile, kh, kw, up_s) ? 2 : 1;
+    if (head_conv_applies(cout, cin, kt, kh, kw, up_s)) return 3;
+    int nt, nb;
+    bf16_conv_tiling(cout, &nt, &nb);
+    return v2_conv_applies(nt, kh, kw, up_s) ? 2 : 1;
 }
 
-size_t bf16_packed_elems(int cout, int cin, int kt, int kh, int kw)
+size_t bf16_packed_elems(int cout, int cin, int kt, int kh, int kw, int family)
 {
+    if (family == 3) return head_packed_elems(cin);
     int nt, nb;
     bf16_conv_tiling(cout, &nt, &nb);
     const int kchunks = (cin + 31) / 32;
@@ -309,10 +313,11 @@ size_t bf16_packed_elems(int cout, int cin, int kt, int kh, int kw)
 hipError_t launch_pack_bf16(const void* w, void* wpk, int cout, int cin, int kt, int kh, int kw,
                             int family, hipStream_t s)
 {
+    if (family == 3) return launch_pack_head(w, wpk, cout, cin, s);
     int nt, nb;
     bf16_conv_tiling(cout, &nt, &nb);
     const int kchunks = (cin + 31) / 32;
-    const size_t total = bf16_packed_elems(cout, cin, kt, kh, kw);
+    const size_t total = bf16_packed_elems(cout, cin, kt, kh, kw, family);
     int blocks = (int)((total + 255) / 256);
     if (blocks > 65536) blocks = 65536;
     const int dmajor = family == 2 ? 1 : 0;
@@ -324,6 +329,7 @@ hipError_t launch_pack_bf16(const void* w, void* wpk, int cout, int cin, int kt,
 hipError_t launch_conv_bf16(const ConvArgs& a, hipStream_t s)
 {
     if (a.kh != a.kw) return hipErrorInvalidValue;
+    if (a.family == 3) return launch_conv_head(a, s);
     if (a.family == 2) return launch_conv_bf16_v2(a, s);
     if (a.up_s == 1 && a.kh == 3) return launch_nf<1, 3>(a, s);
     if (a.up_s == 2 && a.kh == 3) return launch_nf<2, 3>(a, s);

@@ -1,0 +1,294 @@
+// Output-head conv on gfx950 MFMA: a 3x3x3 causal conv to at most three
+// channels (RGB) whose input is nearest-2x upsampled in space.
+//
+// With three output channels, the GEMM view of the other kernels (N = output
+// channels) leaves 13 of 16 MFMA columns idle.  Here the spatial taps go into N
+// instead: for every source pixel s of an input frame and every tap (a, b, d)
+// and channel o,
+//
+//     P[s][(a, b, d, o)] = sum_c X[s][c] * W[o][c][a][b][d]
+//
+// is one GEMM with M = source pixels, K = Cin, N = 3 temporal x 9 spatial taps
+// x 3 channels (27 per temporal tap, padded to 32).  An output pixel (y, x) of
+// frame t then sums, for each tap, one entry of P: spatial tap (b, d) of output
+// phase (p, q) = (y & 1, x & 1) reads source (y/2 + floor((p+b-1)/2),
+// x/2 + floor((q+d-1)/2)) -- nearest upsampling followed by zero padding of the
+// upsampled image is exactly "zero outside the source image" -- and temporal tap
+// a reads input frame t + a of the causal window.  Every product of the conv's
+// definition is formed once (in the MFMA) and every sum is taken in fp32, in a
+// different order from the direct form; no weights are pre-summed.
+//
+// A workgroup owns a tile of 8 x 16 source pixels (16 x 32 output pixels) and a
+// run of consecutive output frames.  It walks the input frames of that run
+// once: each frame's tile plus a one-pixel border (18 x 10 pixels, 12 M
+// fragments) is loaded straight into MFMA operand registers (the next frame's
+// while the current one is gathered), multiplied by the weights held in
+// registers for the whole run, and the partial sums P go to LDS.  Each thread
+// then gathers the taps of two horizontally adjacent output pixels and adds
+// them to a three-frame ring of fp32 accumulators in registers; output frame t
+// is complete, and stored, once input frame t + 2 has been added.
+#include "cc3d_kernels.h"
+
+namespace cc3d {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int TH = 8, TW = 16;                  // source tile
+constexpr int BH = TH + 2, BW = TW + 2;         // with the one-pixel border
+constexpr int BPIX = BH * BW;                   // 180
+constexpr int MFR = (BPIX + 15) / 16;           // 12 M fragments of 16 pixels
+constexpr int MFW = MFR / 4;                    // 3 per wave
+constexpr int NFR = 6;                          // 3 temporal taps x 32 columns
+constexpr int PSTR = 100;                       // floats per pixel in the P table (96 used)
+constexpr uint32_t OOB = 0x80000000u;           // an offset past every buffer used here
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+__device__ __forceinline__ uint16_t bf16_rne(float f)
+{
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ const uint16_t* zframe(const ZWindow& z, int zi)
+{
+    const int hist = z.kt - 1;
+    if (zi < hist) {
+        if (!z.first) return (const uint16_t*)z.cache + (int64_t)zi * z.frame_elems;
+        return z.zero_hist ? nullptr : (const uint16_t*)z.x;
+    }
+    const int u = zi - hist;
+    const int src = (z.up_t == 2) ? ((u + z.first) >> 1) : u;
+    return (const uint16_t*)z.x + (int64_t)src * z.frame_elems;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int KC>
+__global__ __launch_bounds__(256, 2) void conv_head_kernel(ConvArgs a, int fpw)
+{
+    __shared__ float ptab[MFR * 16 * PSTR];  // P[pixel of the bordered tile][n]
+
+    const int tiles_w = (a.w_in + TW - 1) / TW;
+    const int tiles_h = (a.h_in + TH - 1) / TH;
+    const int ntiles = tiles_w * tiles_h;
+    const int tgroups = (a.t_out + fpw - 1) / fpw;
+    // work items (tile, time group), dealt to the 8 XCDs in contiguous ranges
+    const int total = ntiles * tgroups;
+    const int per_xcd = (total + 7) >> 3;
+    const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if (w >= total) return;
+    const int tg = w % tgroups, tile = w / tgroups;
+    const int i0 = (tile / tiles_w) * TH, j0 = (tile % tiles_w) * TW;
+    const int t0 = tg * fpw;
+    const int t1 = min(t0 + fpw, a.t_out);
+    const int z0 = t0, z1 = t1 + 2;  // input frames of the causal window this run reads
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, k16 = lane & 15;
+
+    // weights (MFMA row operand): row 16 f + k16, channels 32 kc + 8 g .. + 7
+    bf16x8 wa[KC][NFR];
+    const uint4* wp = (const uint4*)a.wpk;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int f = 0; f < NFR; ++f) wa[kc][f] = __builtin_bit_cast(bf16x8, wp[(kc * NFR + f) * 64 + lane]);
+
+    // this lane's pixel in each of the wave's M fragments: byte offset inside a
+    // frame of its 8-channel group, OOB outside the image (loads return zeros)
+    uint32_t poff[MFW];
+#pragma unroll
+    for (int mm = 0; mm < MFW; ++mm) {
+        const int L = (wave * MFW + mm) * 16 + k16;
+        const int r = L / BW, c = L - r * BW;
+        const int gy = i0 + r - 1, gx = j0 + c - 1;
+        poff[mm] = (L < BPIX && gy >= 0 && gy < a.h_in && gx >= 0 && gx < a.w_in)
+                       ? (uint32_t)(((gy * a.w_in + gx) * a.cin + g * 8) * 2)
+                       : OOB;
+    }
+    const uint32_t frame_bytes = (uint32_t)(a.z.frame_elems * 2);
+    bf16x8 xb[KC][MFW];
+    auto load_frame = [&](int zi) {
+        const uint16_t* fp = zframe(a.z, zi);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(fp, fp ? frame_bytes : 0u);
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+            for (int mm = 0; mm < MFW; ++mm)
+                xb[kc][mm] = __builtin_bit_cast(
+                    bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(poff[mm] + (uint32_t)(kc * 64)), 0, 0));
+    };
+
+    // the two output pixels of this thread: row oy, columns ox and ox + 1 of the
+    // 16 x 32 output tile; source row si (phase p) and column sj of the tile
+    const int oy = tid >> 4, sj = tid & 15;
+    const int p = oy & 1, si = oy >> 1;
+    const int Y = 2 * i0 + oy, X = 2 * (j0 + sj);
+    const bool row_ok = Y < a.h_out;
+    const int cout = a.cout;
+
+    float ring[3][2][3];
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int o = 0; o < 3; ++o) ring[s][q][o] = 0.f;
+
+    auto store = [&](int t, const float (&v)[2][3]) {
+        if (!row_ok) return;
+        uint16_t* out = (uint16_t*)a.out;
+        const uint16_t* res = (const uint16_t*)a.res;
+        const int64_t base = (((int64_t)t * a.h_out + Y) * a.w_out + X) * cout;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            if (X + q >= a.w_out) continue;
+#pragma unroll
+            for (int o = 0; o < 3; ++o) {
+                if (o >= cout) continue;
+                float y = v[q][o];
+                if (a.bias) y += a.bias[o];
+                if (res) y += bf2f(res[base + q * cout + o]);
+                out[base + q * cout + o] = bf16_rne(y);
+            }
+        }
+    };
+
+    // One input frame zi at ring phase PH = (zi - z0) mod 3: output frame
+    // t = zi - a takes temporal tap a; its accumulator is ring slot (t - z0) mod 3.
+    auto frame = [&](const int zi, const int PH) {
+        f32x4 acc[MFW][NFR];
+#pragma unroll
+        for (int mm = 0; mm < MFW; ++mm)
+#pragma unroll
+            for (int f = 0; f < NFR; ++f) acc[mm][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+            for (int mm = 0; mm < MFW; ++mm)
+#pragma unroll
+                for (int f = 0; f < NFR; ++f)
+                    acc[mm][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[kc][f], xb[kc][mm], acc[mm][f], 0, 0, 0);
+        if (zi + 1 < z1) load_frame(zi + 1);
+        __syncthreads();  // the previous frame's gather has finished reading P
+        // acc[mm][f] = D[n][pixel]: lane (g, k16) holds n = 16 f + 4 g .. + 3 of pixel k16
+#pragma unroll
+        for (int mm = 0; mm < MFW; ++mm) {
+            const int L = (wave * MFW + mm) * 16 + k16;
+#pragma unroll
+            for (int f = 0; f < NFR; ++f) *(f32x4*)&ptab[L * PSTR + 16 * f + 4 * g] = acc[mm][f];
+        }
+        __syncthreads();
+        // gather: tap (a, b, d) of output pixel (oy, 2 sj + q) reads bordered-tile
+        // pixel (si + 1 + floor((p+b-1)/2), sj + 1 + floor((q+d-1)/2)):
+        //   q = 0: d = 0 -> column sj, d = 1, 2 -> sj + 1;  q = 1: d = 0, 1 -> sj + 1, d = 2 -> sj + 2
+#pragma unroll
+        for (int ta = 0; ta < 3; ++ta) {
+            const int t = zi - ta;
+            if (t < t0 || t >= t1) continue;
+            const int slot = ((PH - ta) % 3 + 3) % 3;
+#pragma unroll
+            for (int b = 0; b < 3; ++b) {
+                const int row = si + 1 + ((p + b - 1) >> 1);
+                const float* pr = &ptab[(row * BW + sj) * PSTR + ta * 32 + b * 9];
+#pragma unroll
+                for (int o = 0; o < 3; ++o) {
+                    ring[slot][0][o] += pr[o] + pr[PSTR + 3 + o] + pr[PSTR + 6 + o];
+                    ring[slot][1][o] += pr[PSTR + o] + pr[PSTR + 3 + o] + pr[2 * PSTR + 6 + o];
+                }
+            }
+            if (ta == 2) {  // output frame t has all its taps
+                store(t, ring[slot]);
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int o = 0; o < 3; ++o) ring[slot][q][o] = 0.f;
+            }
+        }
+    };
+
+    load_frame(z0);
+    for (int zb = z0; zb < z1; zb += 3) {
+        frame(zb, 0);
+        if (zb + 1 < z1) frame(zb + 1, 1);
+        if (zb + 2 < z1) frame(zb + 2, 2);
+    }
+}
+
+}  // namespace
+
+bool head_conv_applies(int cout, int cin, int kt, int kh, int kw, int up_s)
+{
+    return cout >= 1 && cout <= 3 && kt == 3 && kh == 3 && kw == 3 && up_s == 2 && cin % 32 == 0 &&
+           cin >= 32 && cin <= 96;
+}
+
+size_t head_packed_elems(int cin)
+{
+    return (size_t)(cin / 32) * NFR * 64 * 8;
+}
+
+namespace {
+// Packed head weights: for each (32-channel chunk kc, N fragment f), 64 lanes of
+// 8 channels: lane (g, k16) holds W[o][32 kc + 8 g + e][a][b][d] for row
+// n = 16 f + k16 = 32 a + 3 (3 b + d) + o (zero for n mod 32 >= 27 or o >= cout).
+__global__ void pack_head_kernel(const uint16_t* w, uint16_t* wpk, int cout, int cin)
+{
+    const int kcs = cin / 32;
+    const int total = kcs * NFR * 64 * 8;
+    for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += gridDim.x * blockDim.x) {
+        const int e = idx & 7;
+        const int lane = (idx >> 3) & 63;
+        const int f = (idx >> 9) % NFR;
+        const int kc = (idx >> 9) / NFR;
+        const int n = 16 * f + (lane & 15);
+        const int c = kc * 32 + (lane >> 4) * 8 + e;
+        const int ta = n / 32, r = n % 32;
+        uint16_t v = 0;
+        if (r < 27) {
+            const int tap = r / 3, o = r % 3;
+            const int b = tap / 3, d = tap % 3;
+            if (o < cout) v = w[((((int64_t)o * cin + c) * 3 + ta) * 3 + b) * 3 + d];
+        }
+        wpk[idx] = v;
+    }
+}
+}  // namespace
+
+hipError_t launch_pack_head(const void* w, void* wpk, int cout, int cin, hipStream_t s)
+{
+    const int total = (int)head_packed_elems(cin);
+    hipLaunchKernelGGL(pack_head_kernel, dim3((total + 255) / 256), dim3(256), 0, s, (const uint16_t*)w,
+                       (uint16_t*)wpk, cout, cin);
+    return hipGetLastError();
+}
+
+hipError_t launch_conv_head(const ConvArgs& a, hipStream_t s)
+{
+    if (!head_conv_applies(a.cout, a.cin, a.kt, a.kh, a.kw, a.up_s)) return hipErrorInvalidValue;
+    if (a.h_out != 2 * a.h_in || a.w_out != 2 * a.w_in || a.t_out < 1) return hipErrorInvalidValue;
+    const int64_t ntiles = (int64_t)((a.h_in + TH - 1) / TH) * ((a.w_in + TW - 1) / TW);
+    // a run of frames per workgroup: long runs read each input frame once; cut
+    // them when there are too few tiles to fill the chip twice over
+    int groups = (int)((2048 + ntiles - 1) / ntiles);
+    if (groups > a.t_out) groups = a.t_out;
+    if (groups < 1) groups = 1;
+    const int fpw = (a.t_out + groups - 1) / groups;
+    const int64_t total = ntiles * ((a.t_out + fpw - 1) / fpw);
+    if (total > (int64_t)0x7fffffff - 8) return hipErrorInvalidValue;
+    const int64_t grid = ((total + 7) / 8) * 8;
+    switch (a.cin / 32) {
+    case 1: hipLaunchKernelGGL((conv_head_kernel<1>), dim3((unsigned)grid), dim3(256), 0, s, a, fpw); break;
+    case 2: hipLaunchKernelGGL((conv_head_kernel<2>), dim3((unsigned)grid), dim3(256), 0, s, a, fpw); break;
+    case 3: hipLaunchKernelGGL((conv_head_kernel<3>), dim3((unsigned)grid), dim3(256), 0, s, a, fpw); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace cc3d

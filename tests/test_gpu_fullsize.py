@@ -1,0 +1,271 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times, on sampled outputs the fp64 oracle computes one by one.
+
+Each workload runs through the library at its real frame size and chunking
+(the first chunks of the stream: the first-chunk rule and at least one carried
+cache).  After every chunk, every conv and norm op is checked on sampled
+output positions -- the four corners, the first and last rows and columns, the
+first and last frame of the chunk (the chunk boundaries), plus seeded random
+positions -- against the oracle fed that op's own GPU input (the per-layer
+parity bound): ``oracle.conv_points`` evaluates the conv sum of the definition
+at each sampled position from the op's causal window.  The window is the op's
+input frames behind its history (copies of the first frame on the video's
+first chunk, else the last two frames of the previous window) after the
+temporal growth; only the rows the sampled positions read are copied to the
+host.
+"""
+import numpy as np
+import pytest
+import torch
+
+from causal_convolution_x3x3_amd import capi as C
+from causal_convolution_x3x3_amd import plan as P
+from causal_convolution_x3x3_amd import stacks as S
+from causal_convolution_x3x3_amd import synth
+from oracle import model as OM
+from oracle import oracle as O
+
+from helpers import BF16_MAX_REL, BF16_MEAN_REL, say, to_oracle
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-6
+
+
+def _grow(v, first):
+    """Nearest 2x in time on non-first frames, on a [T][H][W][C] device tensor."""
+    if first:
+        return torch.cat([v[:1], v[1:].repeat_interleave(2, dim=0)])
+    return v.repeat_interleave(2, dim=0)
+
+
+class Window:
+    """The causal window Z = history || V of one conv op, on the device."""
+
+    def __init__(self, kt, up_t):
+        self.kt, self.up_t, self.hist = kt, up_t, None
+
+    def step(self, x, first):
+        v = _grow(x, first) if self.up_t == 2 else x
+        if first:  # REPLICATE history: copies of the first frame
+            self.hist = v[:1].expand(self.kt - 1, *v.shape[1:])
+        z = torch.cat([self.hist, v])
+        self.hist = z[z.shape[0] - (self.kt - 1):].clone()
+        return z
+
+
+class Tally:
+    """Sampled |d| and |ref| sums for the parity bounds over all samples of a check."""
+
+    def __init__(self):
+        self.dmax = self.rmax = self.dsum = self.rsum = 0.0
+
+    def add(self, got, ref):
+        d = np.abs(got - ref)
+        self.dmax = max(self.dmax, float(d.max()))
+        self.rmax = max(self.rmax, float(np.abs(ref).max()))
+        self.dsum += float(d.mean())
+        self.rsum += float(np.abs(ref).mean())
+
+    def check(self, what):
+        mx, mn = self.dmax / max(self.rmax, 1e-30), self.dsum / max(self.rsum, 1e-30)
+        assert mx <= BF16_MAX_REL and mn <= BF16_MEAN_REL, "%s: sampled max-rel %.3g (<= %g), mean-rel %.3g (<= %g)" % (
+            what, mx, BF16_MAX_REL, mn, BF16_MEAN_REL)
+        return mx, mn
+
+
+def _samples(rng, t, h, w, nrows=6, ncols=48, nts=4):
+    rows = sorted(set([0, h - 1] + list(rng.randint(0, h, size=nrows - 2))))
+    cols = sorted(set([0, 1, w - 2, w - 1] + list(rng.randint(0, w, size=ncols - 4))))
+    ts = sorted(set([0, t - 1] + list(rng.randint(0, t, size=nts - 2))))
+    return rows, [c for c in cols if 0 <= c < w], ts
+
+
+def _gather(y, ts, row, cols):
+    """y[t, row, c, :] for t in ts, c in cols (device [T][H][W][C]) -> n x C float64."""
+    ti = torch.tensor(ts, device=y.device).repeat_interleave(len(cols))
+    ci = torch.tensor(cols, device=y.device).repeat(len(ts))
+    return y[ti, row][torch.arange(ti.numel(), device=y.device), ci].double().cpu().numpy()
+
+
+def check_conv(z, w, b, up, ts, rows, cols, out=None, res=None, act=None, gamma=None, tallies=None):
+    """Compare the op's stored result (out = conv + bias (+ res), bf16) and/or
+    its act (SiLU(RMSNorm(rounded result))) with the oracle at the sampled
+    positions.  z: [Tz][Hin][Win][Cin] device window; w, b: float64 numpy."""
+    hin = z.shape[1]
+    for y in rows:
+        r0 = max(0, (y - 1) // up)
+        r1 = min(hin - 1, (y + 1) // up)
+        zc = z[:, r0:r1 + 1].float().cpu().numpy().transpose(3, 0, 1, 2)  # [C][T][rows][W], a view
+        pts = np.array([(t, y - up * r0, c) for t in ts for c in cols], dtype=np.int32)
+        v = O.conv_points(zc, w, b, pts, up)  # n x Cout
+        if res is not None:
+            v = v + _gather(res, ts, y, cols)
+        if out is not None:
+            tallies["out"].add(_gather(out, ts, y, cols), v)
+        if act is not None:
+            ref = O.act(O.round_bf16(v).T, gamma, EPS).T
+            tallies["act"].add(_gather(act, ts, y, cols), ref)
+
+
+def check_norm(src, act, gamma, ts, rows, cols, res=None, out=None, tallies=None):
+    for y in rows:
+        v = _gather(src, ts, y, cols)
+        if res is not None:
+            v = O.round_bf16(v + _gather(res, ts, y, cols))
+            if out is not None:
+                tallies["out"].add(_gather(out, ts, y, cols), v)
+        tallies["act"].add(_gather(act, ts, y, cols), O.act(v.T, gamma, EPS).T)
+
+
+def run_stack_sampled(ops, params_cpu, x_cl, cin, h, w, splits, seed, max_pts_rows=6):
+    """Run `ops` chunk by chunk and check every op on sampled positions."""
+    plan = P.stack_plan(ops, cin, h, w, max_chunk_t=max(splits))
+    st = P.Stream(plan)
+    wins = {i: Window(o.k[0], o.up_t) for i, o in enumerate(ops) if o.kind == C.OP_CONV}
+    rng = np.random.RandomState(seed)
+    worst = {}
+    outs, t0 = [], 0
+    for n in splits:
+        first = st.frames_seen == 0
+        xc = x_cl[t0:t0 + n].contiguous()
+        say("  chunk at %d (%d frames)" % (t0, n))
+        y = st.step(xc)
+        torch.cuda.synchronize()
+        outs.append(y.cpu())
+
+        def slot(s):
+            if s == C.SLOT_X:
+                return xc
+            if s == C.SLOT_Y:
+                return y
+            if s == C.SLOT_NONE:
+                return None
+            return plan.read_slot(s, n, first)
+
+        for i, o in enumerate(ops):
+            src = slot(o.src)
+            res, out, act = slot(o.res), slot(o.out), slot(o.act_out)
+            ref_t = out if out is not None else act
+            tal = {"out": Tally(), "act": Tally()}
+            rows, cols, ts = _samples(rng, ref_t.shape[0], ref_t.shape[1], ref_t.shape[2], nrows=max_pts_rows)
+            if o.kind == C.OP_CONV:
+                z = wins[i].step(src, first)
+                p = params_cpu[o.name]
+                g = None
+                if act is not None:
+                    g = params_cpu["__gain_of_act_%d" % o.act_out]
+                check_conv(z, p["w"], p["b"], o.up_s, ts, rows, cols, out=out, res=res, act=act, gamma=g,
+                           tallies=tal)
+            else:
+                check_norm(src, act, to_oracle(o.gamma.cpu()), ts, rows, cols, res=res, out=out, tallies=tal)
+            for k in ("out", "act"):
+                if tal[k].rsum > 0:
+                    mx, mn = tal[k].check("%s %s (chunk at %d)" % (o.name or "op%d" % i, k, t0))
+                    key = "%s.%s" % (o.name or "op%d" % i, k)
+                    worst[key] = max(worst.get(key, 0.0), mn)
+            del src, res, out, act, ref_t
+        torch.cuda.synchronize()
+        t0 += n
+    say("  worst sampled mean-rel per op: " + ", ".join("%s %.2e" % kv for kv in sorted(worst.items())))
+    return torch.cat(outs), worst
+
+
+def _gains_of_acts(ops, params_cpu):
+    """For every act slot, the RMSNorm gain of the conv that produces it (the
+    gain that belongs to the conv reading it)."""
+    for o in ops:
+        if o.act_out != C.SLOT_NONE and o.gamma is not None:
+            params_cpu["__gain_of_act_%d" % o.act_out] = to_oracle(o.gamma.cpu())
+
+
+def _param_pair(cout, cin, cfg, i, with_gain):
+    w = synth.bf16(synth.conv_weight(cout, cin, 3, 3, 3, synth.seed(cfg, 10 + 3 * i)))
+    g = synth.gain(cin, synth.seed(cfg, 11 + 3 * i)) if with_gain else None
+    dev = {"w": w.cuda(), "g": None if g is None else g.cuda(), "b": None}
+    cpu = {"w": to_oracle(w), "g": None if g is None else to_oracle(g), "b": None}
+    return dev, cpu
+
+
+def test_c1_resblock_fullsize_sampled():
+    """128-channel residual block at 90x160, 16 frames in 4-frame chunks."""
+    wl = synth.WORKLOADS[1]
+    say("full size c1: %s" % wl)
+    c = wl["c"]
+    d1, c1 = _param_pair(c, c, 1, 0, True)
+    d2, c2 = _param_pair(c, c, 1, 1, True)
+    ops = S.resblock_ops(c, d1, d2)
+    ops[0].name, ops[1].name, ops[2].name = "act1", "conv1", "conv2"
+    cpu = {"conv1": c1, "conv2": c2}
+    _gains_of_acts(ops, cpu)
+    x = synth.bf16(synth.video(c, wl["t"], wl["h"], wl["w"], synth.seed(1, 1)))
+    x_cl = x.permute(1, 2, 3, 0).contiguous().cuda()
+    run_stack_sampled(ops, cpu, x_cl, c, wl["h"], wl["w"], [wl["chunk"]] * (wl["t"] // wl["chunk"]), seed=101)
+
+
+def test_c2_stage1080_fullsize_sampled():
+    """256 channels at 270x480 -> nearest 2x -> conv 256->128 -> act -> conv 128->128,
+    24 frames in 4-frame chunks."""
+    wl = synth.WORKLOADS[2]
+    say("full size c2: %s" % wl)
+    d1, c1 = _param_pair(wl["cmid"], wl["cin"], 2, 0, False)
+    d2, c2 = _param_pair(wl["cout"], wl["cmid"], 2, 1, True)
+    ops = S.upstage_ops(wl["cmid"], wl["cout"], d1, d2)
+    ops[0].name, ops[1].name = "conv1", "conv2"
+    cpu = {"conv1": c1, "conv2": c2}
+    _gains_of_acts(ops, cpu)
+    x = synth.bf16(synth.video(wl["cin"], wl["t"], wl["h"], wl["w"], synth.seed(2, 1)))
+    x_cl = x.permute(1, 2, 3, 0).contiguous().cuda()
+    del x
+    run_stack_sampled(ops, cpu, x_cl, wl["cin"], wl["h"], wl["w"], [wl["chunk"]] * (wl["t"] // wl["chunk"]),
+                      seed=202)
+
+
+def test_c3_stage1440_fullsize_sampled():
+    """128 channels at 720x1280 -> nearest 2x -> conv 128->96 -> act -> conv 96->3
+    at 2560x1440: the stream's first chunk (1 frame) and the two after it."""
+    wl = synth.WORKLOADS[3]
+    say("full size c3: %s" % wl)
+    d1, c1 = _param_pair(wl["cmid"], wl["cin"], 3, 0, False)
+    d2, c2 = _param_pair(wl["cout"], wl["cmid"], 3, 1, True)
+    ops = S.upstage_ops(wl["cmid"], wl["cout"], d1, d2)
+    ops[0].name, ops[1].name = "conv1", "conv2"
+    cpu = {"conv1": c1, "conv2": c2}
+    _gains_of_acts(ops, cpu)
+    splits = [wl["first_chunk"], wl["chunk"], wl["chunk"]]
+    x = synth.bf16(synth.video(wl["cin"], sum(splits), wl["h"], wl["w"], synth.seed(3, 1)))
+    x_cl = x.permute(1, 2, 3, 0).contiguous().cuda()
+    del x
+    run_stack_sampled(ops, cpu, x_cl, wl["cin"], wl["h"], wl["w"], splits, seed=303)
+
+
+def test_c4_decoder_fullsize_sampled():
+    """The whole decoder at the full latent size 48 x 90x160 -> 3 x 1440x2560:
+    the first two clips (7 then 6 latents -> 25 then 24 frames), every op
+    checked; then the benchmark's own slot wiring must give bitwise the same
+    RGB output."""
+    wl = synth.WORKLOADS[4]
+    say("full size c4: %s" % wl)
+    shapes = OM.decoder_layer_shapes()
+    dev, cpu = {}, {}
+    for i, (name, co, ci, kt, kh, kw, has_g) in enumerate(shapes):
+        d, c = _param_pair(co, ci, 4, i, has_g)
+        dev[name], cpu[name] = d, c
+    ops = S.decoder_ops(dev, unique_slots=True)
+    _gains_of_acts(ops, cpu)
+    splits = [wl["first_clip"], wl["clip"]]
+    x = synth.bf16(synth.video(wl["c_latent"], sum(splits), wl["h"], wl["w"], synth.seed(4, 1)))
+    x_cl = x.permute(1, 2, 3, 0).contiguous().cuda()
+    got, worst = run_stack_sampled(ops, cpu, x_cl, wl["c_latent"], wl["h"], wl["w"], splits, seed=404,
+                                   max_pts_rows=4)
+    assert got.shape == (OM.output_frames(sum(splits)), 1440, 2560, 3)
+    torch.cuda.empty_cache()
+    say("  production wiring")
+    plan = P.stack_plan(S.decoder_ops(dev), wl["c_latent"], wl["h"], wl["w"], max_chunk_t=max(splits))
+    st = P.Stream(plan)
+    t0, outs = 0, []
+    for n in splits:
+        outs.append(st.step(x_cl[t0:t0 + n].contiguous()).cpu())
+        t0 += n
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(outs), got), "production slot wiring differs from the unique-slot wiring"

@@ -28,7 +28,7 @@ def _run_chunks(plan, x_cl, splits, residual_cl=None):
         if residual_cl is not None:
             first = st.frames_seen == 0
             tn = plan.output_shape(n, first)[0]
-            res = residual_cl[r0:r0 + tn].contiguous()
+            res = residual_cl[r0:r0 + tn].clone()  # a fresh (16-byte aligned) buffer
             r0 += tn
         outs.append(st.step(x_cl[t0:t0 + n].contiguous(), residual=res))
         t0 += n
@@ -79,6 +79,11 @@ BF16_CASES = [
     (16, 32, (2, 1, 1), 1, 1, 7, 19, [1, 2, 2], C.TPAD_ZERO, False),
     (16, 64, (1, 3, 3), 2, 1, 7, 9, [2, 1], C.TPAD_REPLICATE, True),
     (24, 16, (3, 1, 1), 1, 2, 5, 17, [2, 1], C.TPAD_ZERO, False),
+    # output head (taps in the GEMM's N): ragged tiles, runs of frames, cout < 3
+    (96, 3, (3, 3, 3), 2, 1, 13, 37, [1, 4, 3], C.TPAD_REPLICATE, True),
+    (64, 2, (3, 3, 3), 2, 2, 9, 20, [1, 3, 2], C.TPAD_ZERO, True),
+    (96, 1, (3, 3, 3), 2, 1, 8, 16, [2, 5], C.TPAD_REPLICATE, False),
+    (32, 3, (3, 3, 3), 2, 1, 128, 1024, [2, 5], C.TPAD_REPLICATE, True),
 ]
 
 
@@ -119,6 +124,22 @@ def test_bf16_conv_epilogue_act(cout, residual):
     got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits,
                                      residual_cl=to_device_cl(r) if residual else None))
     assert_bf16_close(got, ref, "epilogue")
+
+
+def test_bf16_head_conv_residual():
+    """The output head (3 channels, nearest 2x) with bias and a residual added
+    before the bf16 store."""
+    say("bf16 head residual")
+    cin, cout, h, w, splits = 96, 3, 11, 21, [1, 3]
+    t = sum(splits)
+    x = synth.bf16(synth.video(cin, t, h, w, synth.seed(6, 11)))
+    wt = synth.bf16(synth.conv_weight(cout, cin, 3, 3, 3, synth.seed(6, 12)))
+    b = synth.bias(cout, synth.seed(6, 13))
+    r = synth.bf16(synth.video(cout, t, 2 * h, 2 * w, synth.seed(6, 14)))
+    ref = O.one_shot(to_oracle(x), to_oracle(wt), to_oracle(b), O.REPLICATE, up_s=2) + to_oracle(r)
+    plan = P.conv_plan(wt.cuda(), h, w, bias=b.cuda(), up_s=2, residual=True, max_chunk_t=3)
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits, residual_cl=to_device_cl(r)))
+    assert_bf16_close(got, ref, "head + residual")
 
 
 # ------------------------------------------------------------- boundary --
