@@ -101,7 +101,7 @@ __device__ __forceinline__ bool decode_work(int ntiles, int t_out, int nblocks, 
 }
 
 // Geometry of the two variants (per group of four waves along M); RH = output
-// rows per wave for up_s = 1.
+// rows per wave for up_s = 1, source rows per wave for up_s = 2.
 template <int UP, int RH>
 struct Geo;
 template <int RH>
@@ -110,9 +110,9 @@ struct Geo<1, RH> {  // tile: RH output rows x 64 columns; M-wave w: columns 16w
     static constexpr int MF = RH;  // M fragments per wave: one per row
 };
 template <int RH>
-struct Geo<2, RH> {  // tile: 8 source rows x 16 source columns; M-wave w: source rows 2w, 2w+1
-    static constexpr int TS_H = 8, TS_W = 16;
-    static constexpr int MF = 8;  // 2 rows x 4 phases
+struct Geo<2, RH> {  // tile: 4 RH source rows x 16 source columns; M-wave w: source rows RH w .. RH w + RH-1
+    static constexpr int TS_H = 4 * RH, TS_W = 16;
+    static constexpr int MF = 4 * RH;  // RH rows x 4 phases
 };
 
 // Raw buffer descriptor (gfx9 family word 3) over `bytes` bytes at `base`; a
@@ -284,18 +284,22 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
                 }
             }
         } else {
-            // M fragment m = rr*4 + p*2 + q: source row 2*wm + rr, phase (p, q).
+            // M fragment m = rr*4 + p*2 + q: source row R*wm + rr, phase (p, q).
             // Column offsets of this d: q=0 -> floor((d-1)/2), q=1 -> floor(d/2).
+            // Each LDS row is read once and applied to every (rr, row tap) that
+            // reads it: source row rr + oy with oy = floor((p+b-1)/2).
+            constexpr int R = MF / 4;
             const int ox0 = (d - 1) >> 1, ox1 = d >> 1;
-            const int base0 = col_off(k16 + ox0 + 1) + 2 * wm * ROWB;
-            const int base1 = col_off(k16 + ox1 + 1) + 2 * wm * ROWB;
+            const int base0 = col_off(k16 + ox0 + 1) + R * wm * ROWB;
+            const int base1 = col_off(k16 + ox1 + 1) + R * wm * ROWB;
 #pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
+            for (int srow = 0; srow < R + 2; ++srow) {  // LDS row R*wm + srow: source row R*wm + srow - 1
+                const bf16x8 a0 = lds_frag(aread, base0 + srow * ROWB);
+                const bf16x8 a1 = (ox0 == ox1) ? a0 : lds_frag(aread, base1 + srow * ROWB);
 #pragma unroll
-                for (int oy = -1; oy <= 1; ++oy) {
-                    const int row = rr + oy + 1;  // plus 2*wm, folded into the bases
-                    const bf16x8 a0 = lds_frag(aread, base0 + row * ROWB);
-                    const bf16x8 a1 = (ox0 == ox1) ? a0 : lds_frag(aread, base1 + row * ROWB);
+                for (int rr = 0; rr < R; ++rr) {
+                    const int oy = srow - 1 - rr;
+                    if (oy < -1 || oy > 1) continue;
 #pragma unroll
                     for (int p = 0; p < 2; ++p)
 #pragma unroll
@@ -479,7 +483,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
             x = j0 + 16 * wm + k16;
         } else {
             const int rr = m >> 2, p = (m >> 1) & 1, q = m & 1;
-            y = 2 * (i0 + 2 * wm + rr) + p;
+            y = 2 * (i0 + (MF / 4) * wm + rr) + p;
             x = 2 * (j0 + k16) + q;
         }
     };
@@ -626,7 +630,8 @@ hipError_t launch_conv_bf16_v2(const ConvArgs& a, hipStream_t s)
     // share each weight fetch and the tile border is a smaller share.  The
     // 128-channel blocks keep 8 rows (10 would not fit 256 VGPRs).
     if (a.up_s == 1) return a.ntile == 96 ? launch_v2<1, 6, 2, false, 10>(a, s) : launch_v2<1, 8, 2, false, 8>(a, s);
-    return a.ntile == 96 ? launch_v2<2, 6, 2, true>(a, s) : launch_v2<2, 8, 2, false>(a, s);
+    // up_s = 2: two source rows per wave (three measured no faster).
+    return a.ntile == 96 ? launch_v2<2, 6, 2, true, 2>(a, s) : launch_v2<2, 8, 2, false, 2>(a, s);
 }
 
 }  // namespace cc3d
