@@ -718,6 +718,7 @@ cc3d_status cc3d_forward_chunk(const cc3d_plan* p, const void* x, int t_chunk, c
             a.ntile = r.ntile;
             a.nblocks = r.nblocks;
             a.family = r.family;
+            a.rot_taps = 1;
             if (r.fused_act) {
                 a.out = slot_ptr(r.out);
                 a.act_out = slot_ptr(r.act_out);

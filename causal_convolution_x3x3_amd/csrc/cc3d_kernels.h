@@ -36,6 +36,7 @@ struct ConvArgs {
     int kchunks;          // bf16: ceil(cin / 32)
     int ntile, nblocks;   // bf16: output channels per workgroup, number of such blocks
     int family;           // bf16: kernel family (1, 2 or 3) the weights were packed for
+    int rot_taps;         // bf16 v2: rotate the temporal-tap order by the output frame
 };
 
 struct NormArgs {

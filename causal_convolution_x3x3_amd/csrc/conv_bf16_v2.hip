@@ -86,18 +86,13 @@ __device__ __forceinline__ const uint16_t* zframe(const ZWindow& z, int zi) {
     return (const uint16_t*)z.x + (int64_t)src * z.frame_elems;
 }
 
-// Work item of this workgroup: contiguous ranges of (tile, frame, channel block)
-// per XCD (workgroups are dealt to the XCDs round-robin).
-__device__ __forceinline__ bool decode_work(int ntiles, int t_out, int nblocks, int& tile, int& t, int& nb) {
-    const int total = ntiles * t_out * nblocks;
-    const int per_xcd = (total + 7) >> 3;
-    const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-    if (w >= total) return false;
+// (tile, frame, channel block) of work item w; the channel block varies fastest.
+__device__ __forceinline__ void decode_item(int w, int t_out, int nblocks, int& tile, int& t, int& nb)
+{
     nb = w % nblocks;
     const int rest = w / nblocks;
     t = rest % t_out;
     tile = rest / t_out;
-    return true;
 }
 
 // Geometry of the two variants (per group of four waves along M); RH = output
@@ -131,6 +126,12 @@ __device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t o
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
 }
 
+// 4 bytes per lane from buffer offset `off` into LDS at lds_base + 4 * lane.
+__device__ __forceinline__ void load_to_lds4(__amdgpu_buffer_rsrc_t r, uint32_t off, char* lds_base)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4, off, 0, 0, 0);
+}
+
 // s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left at their maxima)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
@@ -162,34 +163,40 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     constexpr int NTILE = 16 * NF;
     constexpr int A_CH = LH * LWP * 4;      // 16-byte slots of one LDS tile buffer
     constexpr int B_CH = 3 * NTILE * 4;     // 16-byte slots of one column tap's weights
-    constexpr int A_IT = (A_CH + NT - 1) / NT;
-    constexpr int B_IT = (B_CH + NT - 1) / NT;
-    // Load instructions every wave issues per tile / per weight block: only these
-    // full rounds are counted by the vmcnt waits (a wave that issued more younger
-    // loads then waits for some of them too, which is safe).
-    constexpr int A_FULL = A_CH / NT;
-    constexpr int B_FULL = B_CH / NT;
-    static_assert(A_FULL >= 1 && B_FULL >= 1, "every wave takes part in each load round");
+    constexpr int A_IT = (A_CH + NT - 1) / NT;  // tile load rounds (16 bytes per lane)
+    constexpr int A_PAD = A_IT * NT;            // tile buffer slots: whole rounds
+    constexpr int B_BYTES = B_CH * 16;          // one column tap's weights
+    constexpr int RB16 = B_CH / NT;             // weight load rounds of 16 bytes per lane ...
+    constexpr int RB4 = (B_CH % NT) * 16 / (NT * 4);  // ... and of 4 bytes per lane for the rest
+    static_assert(RB4 * NT * 4 == (B_CH % NT) * 16, "weight blocks split into whole load rounds");
+    constexpr int RB = RB16 + RB4;              // weight load instructions per wave
     constexpr int MF = G::MF;
+    constexpr int RED = WN * 4 * MF * 16;       // epilogue reduction floats
     // weight buffers: 3 (prefetch distance 2) when they fit in LDS with the
     // double-buffered tile, else 2 (distance 1)
-    constexpr int NBB = (2 * A_CH + 3 * B_CH) * 16 <= 160 * 1024 ? 3 : 2;
+    constexpr int NBB = (2 * A_PAD + 3 * B_CH) * 16 + RED * 4 <= 160 * 1024 ? 3 : 2;
     static_assert(NF % WN == 0, "N fragments split evenly over the N waves");
 
-    // one LDS variable per buffer: the compiler then knows that loads into one
-    // buffer do not touch the buffer being read, and does not wait for them
-    // (BG: tile buffers padded to whole load rounds, so that every lane issues
-    // every round and no load sits behind a branch)
-    __shared__ uint4 lds_a0[BG ? A_IT * NT : A_CH];
-    __shared__ uint4 lds_a1[BG ? A_IT * NT : A_CH];
+    // One LDS variable per buffer, and every load of the main loop issued
+    // unconditionally (tile buffers padded to whole rounds; out-of-range slots
+    // read zeros into the padding; the last steps reload instead of skipping):
+    // the compiler's own waits then see exactly which loads are in flight, know
+    // that the buffer being read is not one being filled, and add no waits.
+    __shared__ uint4 lds_a0[A_PAD];
+    __shared__ uint4 lds_a1[A_PAD];
     __shared__ uint4 lds_b0[BG ? 1 : B_CH];
     __shared__ uint4 lds_b1[BG ? 1 : B_CH];
     __shared__ uint4 lds_b2[(!BG && NBB == 3) ? B_CH : 1];
+    __shared__ float lds_red[RED];  // epilogue: per-pixel partial sums of squares
 
     const int tiles_w = (a.w_in + G::TS_W - 1) / G::TS_W;
     const int tiles_h = (a.h_in + G::TS_H - 1) / G::TS_H;
+    const int total = tiles_w * tiles_h * a.t_out * a.nblocks;
+
+  // One work item (tile, frame, channel block): main loop and epilogue.
+  auto process = [&](const int w) {
     int tile, t, nb;
-    if (!decode_work(tiles_w * tiles_h, a.t_out, a.nblocks, tile, t, nb)) return;
+    decode_item(w, a.t_out, a.nblocks, tile, t, nb);
     const int i0 = (tile / tiles_w) * G::TS_H;  // source tile origin
     const int j0 = (tile % tiles_w) * G::TS_W;
 
@@ -230,27 +237,40 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
         }
     }
 
-    auto issue_a = [&](int step, uint4* buf) {
+    // K steps take the temporal taps in an order rotated by the output frame:
+    // loop step (ta, kc) reads tap (ta + rot) mod kt, rot = -t mod kt, so the
+    // workgroups of frames t, t+1, t+2 -- which run at the same time -- read the
+    // same input frame in the same step and share it in L2.
+    const int rot = a.rot_taps ? (a.kt - t % a.kt) % a.kt : 0;
+    auto phys_step = [&](int step) -> int {
+        const int ta = step / a.kchunks, kc = step - ta * a.kchunks;
+        const int tr = ta + rot < a.kt ? ta + rot : ta + rot - a.kt;
+        return tr * a.kchunks + kc;
+    };
+    auto phys_sub = [&](int sub) -> int { return phys_step(sub / 3) * 3 + sub % 3; };
+    auto issue_a = [&](int lstep, uint4* buf) {
+        const int step = phys_step(lstep);
         const int ta = step / a.kchunks, kc = step - ta * a.kchunks;
         const uint16_t* fp = zframe(a.z, t + ta);
         const __amdgpu_buffer_rsrc_t r = make_rsrc(fp, fp ? frame_bytes : 0u);
         const int ch0 = kc * 32;
 #pragma unroll
         for (int it = 0; it < A_IT; ++it) {
-            if (NT * it + wave * 64 < A_CH) {  // wave-uniform: the wave has slots in range
-                const uint32_t off = (ch0 + a_ch[it] < a.cin) ? a_off[it] + (uint32_t)(ch0 * 2) : OOB;
-                if (tid + NT * it < A_CH) load_to_lds(r, off, buf + NT * it + wave * 64);
-            }
+            const uint32_t off = (ch0 + a_ch[it] < a.cin) ? a_off[it] + (uint32_t)(ch0 * 2) : OOB;
+            load_to_lds(r, off, buf + NT * it + wave * 64);
         }
     };
-    auto issue_b = [&](int sub, uint4* buf) {
+    // a column tap's weights, copied as they are packed: RB16 rounds of 16 bytes
+    // per lane, then RB4 rounds of 4 bytes for what is left
+    auto issue_b = [&](int lsub, uint4* buf) {
+        const int sub = phys_sub(lsub);
 #pragma unroll
-        for (int it = 0; it < B_IT; ++it) {
-            if (NT * it + wave * 64 < B_CH) {
-                const uint32_t off = (uint32_t)((sub * B_CH + tid + NT * it) * 16);
-                if (tid + NT * it < B_CH) load_to_lds(wr, off, buf + NT * it + wave * 64);
-            }
-        }
+        for (int it = 0; it < RB16; ++it)
+            load_to_lds(wr, (uint32_t)((sub * B_CH + it * NT + tid) * 16), buf + it * NT + wave * 64);
+#pragma unroll
+        for (int it = 0; it < RB4; ++it)
+            load_to_lds4(wr, (uint32_t)(sub * B_BYTES + RB16 * NT * 16 + (it * NT + tid) * 4),
+                         (char*)buf + RB16 * NT * 16 + (it * NT + wave * 64) * 4);
     };
     // byte offset of this lane's 16-byte chunk at LDS column `col` of row 0
     auto col_off = [&](int col) -> int { return col * 64 + ((g ^ swz(col)) << 4); };
@@ -329,31 +349,15 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
             const int nl = 16 * (wn * NFW + f) + k16;
             bidx[f] = nl * 4 + (g ^ swz(nl));
         }
-        auto load_b = [&](int sub, bf16x8 (&dst)[3][NFW]) {
-            const uint4* p = wg + (size_t)sub * B_CH;
+        auto load_b = [&](int lsub, bf16x8 (&dst)[3][NFW]) {
+            const uint4* p = wg + (size_t)phys_sub(lsub) * B_CH;
 #pragma unroll
             for (int b = 0; b < 3; ++b)
 #pragma unroll
                 for (int f = 0; f < NFW; ++f) dst[b][f] = as_bf16x8(p[b * NTILE * 4 + bidx[f]]);
         };
-        // Every load below is issued unconditionally (out-of-range slots read
-        // zeros into the padding; the last sub-step reloads its own weights, the
-        // last K step the first tile into the idle buffer): a load behind a branch
-        // makes the compiler's own waits assume it may be missing and wait for
-        // younger loads as well.
-        auto issue_a_all = [&](int step, uint4* buf) {
-            const int ta = step / a.kchunks, kc = step - ta * a.kchunks;
-            const uint16_t* fp = zframe(a.z, t + ta);
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(fp, fp ? frame_bytes : 0u);
-            const int ch0 = kc * 32;
-#pragma unroll
-            for (int it = 0; it < A_IT; ++it) {
-                const uint32_t off = (ch0 + a_ch[it] < a.cin) ? a_off[it] + (uint32_t)(ch0 * 2) : OOB;
-                load_to_lds(r, off, buf + NT * it + wave * 64);
-            }
-        };
         bf16x8 bq0[3][NFW], bq1[3][NFW];
-        issue_a_all(0, lds_a0);
+        issue_a(0, lds_a0);
         load_b(0, bq0);
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
@@ -364,7 +368,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
             auto sub_step = [&](const int d, const bf16x8 (&cur)[3][NFW], bf16x8 (&nxt)[3][NFW]) {
                 const int sub = 3 * step + d;
                 load_b(sub + 1 < nsub ? sub + 1 : sub, nxt);
-                if (d == 0) issue_a_all(next_a, awrite);
+                if (d == 0) issue_a(next_a, awrite);
                 // keep the scheduler from sinking these loads towards their first
                 // use in the next sub-step (it would, to shorten live ranges)
                 __builtin_amdgcn_sched_barrier(0);
@@ -395,59 +399,57 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
         // prologue: step 0's tile, the first NBB-1 sub-steps' weights
         issue_a(0, lds_a0);
         issue_b(0, lds_b0);
-        if (NBB == 3 && nsub > 1) issue_b(1, lds_b1);
+        if (NBB == 3) issue_b(nsub > 1 ? 1 : 0, lds_b1);
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
 
-        // One K step = three sub-steps (column taps d = 0, 1, 2), unrolled so the tap
-        // and every LDS offset are compile-time constants; steps are taken in pairs
-        // so that every buffer a sub-step reads or fills is a fixed LDS variable.
-        // Sub-step `sub` reads weight buffer sub % NBB and input buffer step % 2.
+        // One K step = three sub-steps (column taps d = 0, 1, 2), unrolled so the
+        // tap and every LDS offset are compile-time constants; steps are taken in
+        // pairs so that every buffer a sub-step reads or fills is a fixed LDS
+        // variable.  Sub-step `sub` reads weight buffer sub % NBB and tile buffer
+        // step % 2; it fills weight buffer (sub + NBB - 1) % NBB, last read in
+        // sub-step sub - 1 (retired by its barrier), and at d = 0 the other tile
+        // buffer, last read in the previous step.
         auto k_step = [&](int step, const uint4* aread, uint4* awrite, const int par) {
-            const bool more_a = step + 1 < nsteps;
+            const int next_a = step + 1 < nsteps ? step + 1 : 0;
             const int sub0 = 3 * step;
-    #pragma unroll
+#pragma unroll
             for (int d = 0; d < 3; ++d) {
                 const int sub = sub0 + d;
                 // NBB = 3: sub % 3 == d; NBB = 2: sub % 2 == (par + d) % 2 with par = step % 2.
-                // The buffer written now, (sub + NBB - 1) % NBB, was last read in
-                // sub-step sub - 1 (retired by its barrier).
                 const int bcur = NBB == 3 ? d : ((par + d) & 1);
                 const int bnext = NBB == 3 ? (d + 2) % 3 : (bcur ^ 1);
                 const uint4* bread = bcur == 0 ? lds_b0 : (bcur == 1 ? lds_b1 : lds_b2);
                 uint4* bwrite = bnext == 0 ? lds_b0 : (bnext == 1 ? lds_b1 : lds_b2);
-                const bool ahead_b = sub + NBB - 1 < nsub;
-                if (ahead_b) issue_b(sub + NBB - 1, bwrite);
-                if (d == 0 && more_a) issue_a(step + 1, awrite);
+                issue_b(sub + NBB - 1 < nsub ? sub + NBB - 1 : nsub - 1, bwrite);
+                if (d == 0) issue_a(next_a, awrite);
 
                 // B fragments of taps (b, d), b = 0..2, for this wave's channels
                 bf16x8 bq[3][NFW];
-    #pragma unroll
+#pragma unroll
                 for (int b = 0; b < 3; ++b)
-    #pragma unroll
+#pragma unroll
                     for (int f = 0; f < NFW; ++f) bq[b][f] = lds_frag(bread, b_off[f] + b * NTILE * 64);
-
                 mma(d, aread, bq);
 
-                // Before the barrier: the weights of sub + 1 (issued during sub - 1) and,
-                // at d == 2, the next tile (issued at d == 0) must have landed.  Loads
-                // complete in issue order; the waits leave the younger ones in flight.
+                // Before the barrier: the weights of sub + 1 and, at d == 2, the
+                // next tile must have landed.  Loads complete in issue order; the
+                // loads issued after the ones needed may stay in flight.
                 if (NBB == 3) {
-                    if (ahead_b && more_a) {
-                        if (d == 2) wait_vmcnt<B_FULL>();
-                        else wait_vmcnt<A_FULL + B_FULL>();
-                    } else {
-                        wait_vmcnt<0>();
-                    }
+                    // the weights of sub + 1 were issued in sub - 1, before
+                    // sub's weights (RB) and, at d <= 1, before the tile (A_IT)
+                    if (d == 2) wait_vmcnt<RB>();
+                    else wait_vmcnt<RB + A_IT>();
                 } else {
                     // the weights of sub + 1 were issued in this sub-step, before the tile
-                    if (d == 0 && more_a) wait_vmcnt<A_FULL>();
+                    if (d == 0) wait_vmcnt<A_IT>();
                     else wait_vmcnt<0>();
                 }
-                // A bare barrier: the loads this barrier publishes were waited for just
-                // above, every LDS read of this sub-step has been consumed by its MFMA,
-                // and the loop issues no LDS stores, so __syncthreads' release fence
-                // (which would drain the loads still in flight) is not needed.
+                // A bare barrier: the loads this barrier publishes were waited for
+                // just above, every LDS read of this sub-step has been consumed by
+                // its MFMA, and the loop issues no LDS stores, so __syncthreads'
+                // release fence (which would drain the loads still in flight) is
+                // not needed.
                 __builtin_amdgcn_s_barrier();
             }
         };
@@ -474,7 +476,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     uint16_t* out = (uint16_t*)a.out;
     uint16_t* act = (uint16_t*)a.act_out;
     const uint16_t* res = (const uint16_t*)a.res;
-    float* red = (float*)&lds_a0[0];  // [WN][4 M-waves][MF][16 pixels]
+    float* red = lds_red;  // [WN][4 M-waves][MF][16 pixels]
     const bool vec_ok = (a.cout & 3) == 0;  // 4-channel groups never straddle cout
 
     auto pixel_of = [&](int m, int& y, int& x) {
@@ -596,9 +598,17 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
             *(uint2*)(act + pbase + n) = make_uint2(pack_bf16x2(z0, z1), pack_bf16x2(z2, z3));
         }
     }
+  };
+
+    // Work items are dealt to the 8 XCDs in contiguous ranges (workgroups are
+    // dealt to the XCDs round-robin), so neighbouring tiles and consecutive
+    // frames run under the same L2.
+    const int per_xcd = (total + 7) >> 3;
+    const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if (w < total) process(w);
 }
 
-template <int UP, int NF, int WN, bool BG, int RH = 8>
+template <int UP, int NF, int WN, bool BG, int RH>
 hipError_t launch_v2(const ConvArgs& a, hipStream_t s)
 {
     using G = Geo<UP, RH>;
