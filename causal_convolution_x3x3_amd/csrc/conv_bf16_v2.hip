@@ -6,7 +6,7 @@
 //
 // * One workgroup of 8 waves per CU, two per SIMD so that one wave's LDS and
 //   barrier waits are covered by the other's MFMAs.  Four waves along M each own
-//   RH output rows x 16 columns (up_s = 1; RH = 10 for 96-channel blocks, 8 for
+//   RH output rows x 16 columns (up_s = 1; RH = 9 for 96-channel blocks, 8 for
 //   128) or 2 source rows x 16 source columns at all four output phases
 //   (up_s = 2, 128 output pixels); the two waves along N split the NTILE output
 //   channels.
@@ -146,11 +146,10 @@ __device__ __forceinline__ void wait_vmcnt()
 // Staging: the input tile and the weights go from global memory straight into
 // LDS (buffer loads with the LDS flag), so no registers or LDS stores are spent
 // on them.  A thread's 16-byte slots are fixed (slot = tid + NT*it); the byte
-// offset each slot reads inside a frame is computed once.  LDS rows of the input
-// tile are padded to a multiple of 8 pixels, so the chunk swizzle depends on the
-// column only and every fragment read is a base register plus a constant.
-// Weights are prefetched two sub-steps ahead (three LDS buffers; two, one
-// sub-step ahead, where three do not fit), the input tile one K step ahead.
+// offset each slot reads inside a frame is computed once.  Every fragment read
+// is a base register plus a constant (the chunk swizzle depends on the column
+// only).  Weights are prefetched two sub-steps ahead (three LDS buffers; two,
+// one sub-step ahead, where three do not fit), the input tile one K step ahead.
 template <int UP, int NF, int WN, bool BG, int RH>
 __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
 {
@@ -158,7 +157,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     constexpr int NT = 256 * WN;        // threads
     constexpr int NFW = NF / WN;        // N fragments per wave
     constexpr int LH = G::TS_H + 2, LW = G::TS_W + 2;
-    constexpr int LWP = (LW + 7) / 8 * 8;  // padded row (pixels)
+    constexpr int LWP = (LW + 1) / 2 * 2;  // row pitch (pixels)
     constexpr int ROWB = LWP * 64;          // bytes per LDS row
     constexpr int NTILE = 16 * NF;
     constexpr int A_CH = LH * LWP * 4;      // 16-byte slots of one LDS tile buffer
@@ -635,11 +634,12 @@ hipError_t launch_conv_bf16_v2(const ConvArgs& a, hipStream_t s)
     // third of the size, and the workgroup meets at a third of the barriers).
     // The 128-channel blocks keep the weights in LDS: with them in registers
     // the kernel no longer fits 256 VGPRs.
-    // up_s = 1, 96-channel blocks: 10 output rows per wave (a 10 x 64 tile per
-    // workgroup; 224 VGPRs), measured 4-10% faster than 8 rows -- more pixels
-    // share each weight fetch and the tile border is a smaller share.  The
-    // 128-channel blocks keep 8 rows (10 would not fit 256 VGPRs).
-    if (a.up_s == 1) return a.ntile == 96 ? launch_v2<1, 6, 2, false, 10>(a, s) : launch_v2<1, 8, 2, false, 8>(a, s);
+    // up_s = 1, 96-channel blocks: 9 output rows per wave (a 9 x 64 tile per
+    // workgroup, weights three buffers deep in LDS).  Measured against 8 rows
+    // (4-10% slower: fewer pixels per weight fetch, larger border share) and 10
+    // rows (about 1% slower: the tile leaves room for two weight buffers only).
+    // The 128-channel blocks keep 8 rows (more would not fit 256 VGPRs).
+    if (a.up_s == 1) return a.ntile == 96 ? launch_v2<1, 6, 2, false, 9>(a, s) : launch_v2<1, 8, 2, false, 8>(a, s);
     // up_s = 2: two source rows per wave (three measured no faster).
     return a.ntile == 96 ? launch_v2<2, 6, 2, true, 2>(a, s) : launch_v2<2, 8, 2, false, 2>(a, s);
 }
