@@ -7,18 +7,16 @@
 // * One workgroup of 8 waves per CU, two per SIMD so that one wave's LDS and
 //   barrier waits are covered by the other's MFMAs.  Four waves along M each own
 //   RH output rows x 16 columns (up_s = 1; RH = 9 for 96-channel blocks, 8 for
-//   128) or 2 source rows x 16 source columns at all four output phases
-//   (up_s = 2, 128 output pixels); the two waves along N split the NTILE output
-//   channels.
+//   128) or RH source rows x 16 source columns at all four output phases
+//   (up_s = 2; RH = 3 for 96-channel blocks, 2 for 128); the two waves along N
+//   split the NTILE output channels.
 // * K is walked in steps of (temporal tap a, 32 channels); each step in three
 //   sub-steps, one per spatial column tap d.  A sub-step needs the step's input
 //   tile (A, in LDS for the whole step) and the weights of the three taps (b, d),
 //   b = 0..2 (B, 3 x NTILE x 32).  The next step's A goes from global memory
 //   straight into an idle LDS buffer (buffer loads with the LDS flag) while the
-//   current step runs.  B takes one of two paths: through LDS the same way
-//   (three buffers, two sub-steps ahead; one barrier per sub-step), or straight
-//   into registers one sub-step ahead, every wave loading its own fragments
-//   from L2 (one barrier per K step).
+//   current step runs; B goes through LDS the same way, two sub-steps ahead
+//   where three buffers fit (else one); one barrier per sub-step.
 // * The weights are the MFMA's row operand and the pixels its column operand,
 //   so each lane's accumulators are four consecutive output channels of one
 //   pixel: the epilogue moves 8-byte vectors.
@@ -150,7 +148,7 @@ __device__ __forceinline__ void wait_vmcnt()
 // is a base register plus a constant (the chunk swizzle depends on the column
 // only).  Weights are prefetched two sub-steps ahead (three LDS buffers; two,
 // one sub-step ahead, where three do not fit), the input tile one K step ahead.
-template <int UP, int NF, int WN, bool BG, int RH>
+template <int UP, int NF, int WN, int RH>
 __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
 {
     using G = Geo<UP, RH>;
@@ -183,9 +181,9 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     // that the buffer being read is not one being filled, and add no waits.
     __shared__ uint4 lds_a0[A_PAD];
     __shared__ uint4 lds_a1[A_PAD];
-    __shared__ uint4 lds_b0[BG ? 1 : B_CH];
-    __shared__ uint4 lds_b1[BG ? 1 : B_CH];
-    __shared__ uint4 lds_b2[(!BG && NBB == 3) ? B_CH : 1];
+    __shared__ uint4 lds_b0[B_CH];
+    __shared__ uint4 lds_b1[B_CH];
+    __shared__ uint4 lds_b2[NBB == 3 ? B_CH : 1];
     __shared__ float lds_red[RED];  // epilogue: per-pixel partial sums of squares
 
     const int tiles_w = (a.w_in + G::TS_W - 1) / G::TS_W;
@@ -337,125 +335,66 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
         }
     };
 
-    if constexpr (BG) {
-        // Weights straight from global memory (L2; every workgroup reads the same
-        // few hundred KB) into registers, one sub-step ahead; only the input tile
-        // goes through LDS, so the workgroup meets at one barrier per K step.
-        const uint4* wg = (const uint4*)a.wpk + (size_t)nb * nsub * B_CH;
-        int bidx[NFW];
+    // prologue: step 0's tile, the first NBB-1 sub-steps' weights
+    issue_a(0, lds_a0);
+    issue_b(0, lds_b0);
+    if (NBB == 3) issue_b(nsub > 1 ? 1 : 0, lds_b1);
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+
+    // One K step = three sub-steps (column taps d = 0, 1, 2), unrolled so the
+    // tap and every LDS offset are compile-time constants; steps are taken in
+    // pairs so that every buffer a sub-step reads or fills is a fixed LDS
+    // variable.  Sub-step `sub` reads weight buffer sub % NBB and tile buffer
+    // step % 2; it fills weight buffer (sub + NBB - 1) % NBB, last read in
+    // sub-step sub - 1 (retired by its barrier), and at d = 0 the other tile
+    // buffer, last read in the previous step.
+    auto k_step = [&](int step, const uint4* aread, uint4* awrite, const int par) {
+        const int next_a = step + 1 < nsteps ? step + 1 : 0;
+        const int sub0 = 3 * step;
 #pragma unroll
-        for (int f = 0; f < NFW; ++f) {
-            const int nl = 16 * (wn * NFW + f) + k16;
-            bidx[f] = nl * 4 + (g ^ swz(nl));
-        }
-        auto load_b = [&](int lsub, bf16x8 (&dst)[3][NFW]) {
-            const uint4* p = wg + (size_t)phys_sub(lsub) * B_CH;
+        for (int d = 0; d < 3; ++d) {
+            const int sub = sub0 + d;
+            // NBB = 3: sub % 3 == d; NBB = 2: sub % 2 == (par + d) % 2 with par = step % 2.
+            const int bcur = NBB == 3 ? d : ((par + d) & 1);
+            const int bnext = NBB == 3 ? (d + 2) % 3 : (bcur ^ 1);
+            const uint4* bread = bcur == 0 ? lds_b0 : (bcur == 1 ? lds_b1 : lds_b2);
+            uint4* bwrite = bnext == 0 ? lds_b0 : (bnext == 1 ? lds_b1 : lds_b2);
+            issue_b(sub + NBB - 1 < nsub ? sub + NBB - 1 : nsub - 1, bwrite);
+            if (d == 0) issue_a(next_a, awrite);
+
+            // B fragments of taps (b, d), b = 0..2, for this wave's channels
+            bf16x8 bq[3][NFW];
 #pragma unroll
             for (int b = 0; b < 3; ++b)
 #pragma unroll
-                for (int f = 0; f < NFW; ++f) dst[b][f] = as_bf16x8(p[b * NTILE * 4 + bidx[f]]);
-        };
-        bf16x8 bq0[3][NFW], bq1[3][NFW];
-        issue_a(0, lds_a0);
-        load_b(0, bq0);
-        wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        // Sub-step `sub` uses bq0 when sub is even; 3*step + d has the parity of
-        // step + d.
-        auto k_step = [&](int step, const uint4* aread, uint4* awrite, const int par) {
-            const int next_a = step + 1 < nsteps ? step + 1 : 0;
-            auto sub_step = [&](const int d, const bf16x8 (&cur)[3][NFW], bf16x8 (&nxt)[3][NFW]) {
-                const int sub = 3 * step + d;
-                load_b(sub + 1 < nsub ? sub + 1 : sub, nxt);
-                if (d == 0) issue_a(next_a, awrite);
-                // keep the scheduler from sinking these loads towards their first
-                // use in the next sub-step (it would, to shorten live ranges)
-                __builtin_amdgcn_sched_barrier(0);
-                mma(d, aread, cur);
-                if (d == 2) {
-                    // The next tile (issued at d == 0, before this sub-step's weight
-                    // loads) must have landed for every wave; loads complete in
-                    // issue order, so only those weight loads may stay in flight.
-                    wait_vmcnt<3 * NFW>();
-                    __builtin_amdgcn_s_barrier();
-                }
-            };
-            if (par == 0) {
-                sub_step(0, bq0, bq1);
-                sub_step(1, bq1, bq0);
-                sub_step(2, bq0, bq1);
+                for (int f = 0; f < NFW; ++f) bq[b][f] = lds_frag(bread, b_off[f] + b * NTILE * 64);
+            mma(d, aread, bq);
+
+            // Before the barrier: the weights of sub + 1 and, at d == 2, the
+            // next tile must have landed.  Loads complete in issue order; the
+            // loads issued after the ones needed may stay in flight.
+            if (NBB == 3) {
+                // the weights of sub + 1 were issued in sub - 1, before
+                // sub's weights (RB) and, at d <= 1, before the tile (A_IT)
+                if (d == 2) wait_vmcnt<RB>();
+                else wait_vmcnt<RB + A_IT>();
             } else {
-                sub_step(0, bq1, bq0);
-                sub_step(1, bq0, bq1);
-                sub_step(2, bq1, bq0);
+                // the weights of sub + 1 were issued in this sub-step, before the tile
+                if (d == 0) wait_vmcnt<A_IT>();
+                else wait_vmcnt<0>();
             }
-        };
-        for (int step = 0; step < nsteps; step += 2) {
-            k_step(step, lds_a0, lds_a1, 0);
-            if (step + 1 < nsteps) k_step(step + 1, lds_a1, lds_a0, 1);
+            // A bare barrier: the loads this barrier publishes were waited for
+            // just above, every LDS read of this sub-step has been consumed by
+            // its MFMA, and the loop issues no LDS stores, so __syncthreads'
+            // release fence (which would drain the loads still in flight) is
+            // not needed.
+            __builtin_amdgcn_s_barrier();
         }
-    } else {
-        // prologue: step 0's tile, the first NBB-1 sub-steps' weights
-        issue_a(0, lds_a0);
-        issue_b(0, lds_b0);
-        if (NBB == 3) issue_b(nsub > 1 ? 1 : 0, lds_b1);
-        wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-
-        // One K step = three sub-steps (column taps d = 0, 1, 2), unrolled so the
-        // tap and every LDS offset are compile-time constants; steps are taken in
-        // pairs so that every buffer a sub-step reads or fills is a fixed LDS
-        // variable.  Sub-step `sub` reads weight buffer sub % NBB and tile buffer
-        // step % 2; it fills weight buffer (sub + NBB - 1) % NBB, last read in
-        // sub-step sub - 1 (retired by its barrier), and at d = 0 the other tile
-        // buffer, last read in the previous step.
-        auto k_step = [&](int step, const uint4* aread, uint4* awrite, const int par) {
-            const int next_a = step + 1 < nsteps ? step + 1 : 0;
-            const int sub0 = 3 * step;
-#pragma unroll
-            for (int d = 0; d < 3; ++d) {
-                const int sub = sub0 + d;
-                // NBB = 3: sub % 3 == d; NBB = 2: sub % 2 == (par + d) % 2 with par = step % 2.
-                const int bcur = NBB == 3 ? d : ((par + d) & 1);
-                const int bnext = NBB == 3 ? (d + 2) % 3 : (bcur ^ 1);
-                const uint4* bread = bcur == 0 ? lds_b0 : (bcur == 1 ? lds_b1 : lds_b2);
-                uint4* bwrite = bnext == 0 ? lds_b0 : (bnext == 1 ? lds_b1 : lds_b2);
-                issue_b(sub + NBB - 1 < nsub ? sub + NBB - 1 : nsub - 1, bwrite);
-                if (d == 0) issue_a(next_a, awrite);
-
-                // B fragments of taps (b, d), b = 0..2, for this wave's channels
-                bf16x8 bq[3][NFW];
-#pragma unroll
-                for (int b = 0; b < 3; ++b)
-#pragma unroll
-                    for (int f = 0; f < NFW; ++f) bq[b][f] = lds_frag(bread, b_off[f] + b * NTILE * 64);
-                mma(d, aread, bq);
-
-                // Before the barrier: the weights of sub + 1 and, at d == 2, the
-                // next tile must have landed.  Loads complete in issue order; the
-                // loads issued after the ones needed may stay in flight.
-                if (NBB == 3) {
-                    // the weights of sub + 1 were issued in sub - 1, before
-                    // sub's weights (RB) and, at d <= 1, before the tile (A_IT)
-                    if (d == 2) wait_vmcnt<RB>();
-                    else wait_vmcnt<RB + A_IT>();
-                } else {
-                    // the weights of sub + 1 were issued in this sub-step, before the tile
-                    if (d == 0) wait_vmcnt<A_IT>();
-                    else wait_vmcnt<0>();
-                }
-                // A bare barrier: the loads this barrier publishes were waited for
-                // just above, every LDS read of this sub-step has been consumed by
-                // its MFMA, and the loop issues no LDS stores, so __syncthreads'
-                // release fence (which would drain the loads still in flight) is
-                // not needed.
-                __builtin_amdgcn_s_barrier();
-            }
-        };
-        for (int step = 0; step < nsteps; step += 2) {
-            k_step(step, lds_a0, lds_a1, 0);
-            if (step + 1 < nsteps) k_step(step + 1, lds_a1, lds_a0, 1);
-        }
+    };
+    for (int step = 0; step < nsteps; step += 2) {
+        k_step(step, lds_a0, lds_a1, 0);
+        if (step + 1 < nsteps) k_step(step + 1, lds_a1, lds_a0, 1);
     }
 
     // ---------------------------------------------------------------- epilogue
@@ -607,7 +546,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     if (w < total) process(w);
 }
 
-template <int UP, int NF, int WN, bool BG, int RH>
+template <int UP, int NF, int WN, int RH>
 hipError_t launch_v2(const ConvArgs& a, hipStream_t s)
 {
     using G = Geo<UP, RH>;
@@ -615,7 +554,7 @@ hipError_t launch_v2(const ConvArgs& a, hipStream_t s)
     const int64_t total = (int64_t)tiles * a.t_out * a.nblocks;
     if (total <= 0 || total > (int64_t)0x7fffffff - 8) return hipErrorInvalidValue;
     const int64_t grid = ((total + 7) / 8) * 8;
-    hipLaunchKernelGGL((conv3_v2_kernel<UP, NF, WN, BG, RH>), dim3((unsigned)grid), dim3(256 * WN), 0, s, a);
+    hipLaunchKernelGGL((conv3_v2_kernel<UP, NF, WN, RH>), dim3((unsigned)grid), dim3(256 * WN), 0, s, a);
     return hipGetLastError();
 }
 
@@ -629,19 +568,16 @@ bool v2_conv_applies(int ntile, int kh, int kw, int up_s)
 hipError_t launch_conv_bf16_v2(const ConvArgs& a, hipStream_t s)
 {
     if (!v2_conv_applies(a.ntile, a.kh, a.kw, a.up_s)) return hipErrorInvalidValue;
-    // Weights through LDS for up_s = 1; straight to registers for the
-    // 96-channel up_s = 2 kernel (measured faster there: its input tile is a
-    // third of the size, and the workgroup meets at a third of the barriers).
-    // The 128-channel blocks keep the weights in LDS: with them in registers
-    // the kernel no longer fits 256 VGPRs.
     // up_s = 1, 96-channel blocks: 9 output rows per wave (a 9 x 64 tile per
     // workgroup, weights three buffers deep in LDS).  Measured against 8 rows
     // (4-10% slower: fewer pixels per weight fetch, larger border share) and 10
     // rows (about 1% slower: the tile leaves room for two weight buffers only).
     // The 128-channel blocks keep 8 rows (more would not fit 256 VGPRs).
-    if (a.up_s == 1) return a.ntile == 96 ? launch_v2<1, 6, 2, false, 9>(a, s) : launch_v2<1, 8, 2, false, 8>(a, s);
-    // up_s = 2: two source rows per wave (three measured no faster).
-    return a.ntile == 96 ? launch_v2<2, 6, 2, true, 2>(a, s) : launch_v2<2, 8, 2, false, 2>(a, s);
+    if (a.up_s == 1) return a.ntile == 96 ? launch_v2<1, 6, 2, 9>(a, s) : launch_v2<1, 8, 2, 8>(a, s);
+    // up_s = 2, 96-channel blocks: three source rows per wave (measured 4%
+    // faster than two rows; streaming the weights from L2 into registers instead
+    // of LDS was slower in every variant: four waves then fetch the same weights).
+    return a.ntile == 96 ? launch_v2<2, 6, 2, 3>(a, s) : launch_v2<2, 8, 2, 2>(a, s);
 }
 
 }  // namespace cc3d
