@@ -15,14 +15,14 @@ OK, EINVAL, ESHAPE, EDTYPE, ESTATE, ENOMEM, EDEVICE = range(7)
 STATUS_NAMES = {0: "OK", 1: "EINVAL", 2: "ESHAPE", 3: "EDTYPE", 4: "ESTATE", 5: "ENOMEM", 6: "EDEVICE"}
 F32, BF16 = 0, 1
 TPAD_REPLICATE, TPAD_ZERO = 0, 1
-EPI_NONE, EPI_RESIDUAL, EPI_ACT = 0, 1, 2
+EPI_NONE, EPI_RESIDUAL, EPI_ACT, EPI_U8 = 0, 1, 2, 4
 SLOT_NONE, SLOT_X, SLOT_Y, SLOT_AUX = -1, 0, 1, 2
 MAX_SLOTS, MAX_OPS = 64, 256
 OP_CONV, OP_NORM_ACT = 0, 1
 
 EXPORTS = (
     "cc3d_plan_create", "cc3d_stack_plan_create", "cc3d_plan_destroy", "cc3d_state_bytes",
-    "cc3d_plan_device_bytes", "cc3d_output_shape", "cc3d_reset", "cc3d_forward_chunk",
+    "cc3d_plan_device_bytes", "cc3d_output_elem_bytes", "cc3d_output_shape", "cc3d_reset", "cc3d_forward_chunk",
     "cc3d_to_channels_last", "cc3d_to_channels_first", "cc3d_last_error", "cc3d_version",
     "cc3d_profile_enable", "cc3d_plan_num_ops", "cc3d_profile_read", "cc3d_slot_shape", "cc3d_slot_read",
 )
@@ -41,7 +41,7 @@ class State(ctypes.Structure):
 class OpDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "kind", "cout", "kt", "kh", "kw", "up_s", "up_t", "tpad", "src", "res", "out", "act_out")] + [
-        ("w", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("gamma", ctypes.c_void_p)]
+        ("w", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("gamma", ctypes.c_void_p), ("out_u8", ctypes.c_int)]
 
 
 class StackDesc(ctypes.Structure):
@@ -81,6 +81,7 @@ def lib():
             "cc3d_plan_destroy": (None, [vp]),
             "cc3d_state_bytes": (sz, [vp]),
             "cc3d_plan_device_bytes": (sz, [vp]),
+            "cc3d_output_elem_bytes": (i, [vp]),
             "cc3d_output_shape": (i, [vp, i, i, pi, pi, pi, pi]),
             "cc3d_reset": (i, [vp, ctypes.POINTER(State), vp]),
             "cc3d_forward_chunk": (i, [vp, vp, i, ctypes.POINTER(State), ctypes.POINTER(State), vp, vp, vp]),

@@ -71,6 +71,7 @@ struct OpRt {
     size_t cache_off = 0, cache_bytes = 0;
     int ntile = 0, nblocks = 0, kchunks = 0, family = 1;
     bool fused_act = false;
+    bool out_u8 = false;  // y as 8-bit codes
 };
 
 }  // namespace
@@ -82,6 +83,7 @@ struct cc3d_plan {
     int elem = 2;
     int cin = 0, h = 0, w = 0;
     int max_t = 1;
+    int y_elem = 2;  // bytes per element of y (1 with 8-bit output)
     float eps = 1e-6f;
     std::vector<Slot> slots;
     std::vector<OpRt> ops;
@@ -212,6 +214,7 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
     };
 
     size_t cache_off = 0;
+    int y_u8_seen = -1;  // -1: no op writes y yet; else whether it is 8-bit
     for (int i = 0; i < d->n_ops; ++i) {
         const cc3d_op_desc& o = d->ops[i];
         OpRt r;
@@ -291,6 +294,20 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
             if (r.cout % 4 != 0 || r.cout > 512)
                 return fail(CC3D_ESHAPE, "op %d: act over %d channels; accepted a multiple of 4 up to 512", i, r.cout);
         }
+        if (o.out_u8) {
+            if (o.kind != CC3D_OP_CONV || o.out != CC3D_SLOT_Y || o.act_out != CC3D_SLOT_NONE)
+                return fail(CC3D_EINVAL, "op %d: out_u8 is accepted on a CONV op that writes only the output slot", i);
+            if (!bf16) return fail(CC3D_EDTYPE, "op %d: 8-bit output needs a bf16 plan", i);
+            if (r.family == 2)
+                return fail(CC3D_ESHAPE,
+                            "op %d: 8-bit output is not written by the 3x3 kernel for 96/128-channel blocks "
+                            "(cout=%d); accepted: cout <= 64, or the 3x3x3 upsampling head to <= 3 channels", i,
+                            r.cout);
+            r.out_u8 = true;
+        }
+        if (o.out == CC3D_SLOT_Y && (y_u8_seen >= 0) && (y_u8_seen != (o.out_u8 ? 1 : 0)))
+            return fail(CC3D_EINVAL, "op %d: the output slot is written both as 8-bit codes and as the plan dtype", i);
+        if (o.out == CC3D_SLOT_Y) y_u8_seen = o.out_u8 ? 1 : 0;
         if (o.res != CC3D_SLOT_NONE) {
             if (o.res == CC3D_SLOT_AUX && !p->slots[CC3D_SLOT_AUX].defined) {
                 Slot& a = p->slots[CC3D_SLOT_AUX];
@@ -322,6 +339,10 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
         p->ops.push_back(r);
     }
     if (!p->slots[CC3D_SLOT_Y].defined) return fail(CC3D_EINVAL, "no op writes the output slot %d", CC3D_SLOT_Y);
+    p->y_elem = y_u8_seen == 1 ? 1 : p->elem;
+    for (const OpRt& r : p->ops)
+        if (r.kind == CC3D_OP_NORM_ACT && (r.out == CC3D_SLOT_Y || r.act_out == CC3D_SLOT_Y) && p->y_elem == 1)
+            return fail(CC3D_EINVAL, "the output slot is written both as 8-bit codes and as the plan dtype");
     p->state_bytes = cache_off < kAlign ? kAlign : cache_off;
     return CC3D_OK;
 }
@@ -565,8 +586,11 @@ cc3d_status cc3d_plan_create(const cc3d_conv_desc* d, const void* w, const float
 {
     if (out) *out = nullptr;
     if (!d) return fail(CC3D_EINVAL, "conv desc is NULL");
-    if (d->epilogue & ~(CC3D_EPI_RESIDUAL | CC3D_EPI_ACT))
-        return fail(CC3D_EINVAL, "epilogue flags 0x%x; accepted CC3D_EPI_RESIDUAL | CC3D_EPI_ACT", d->epilogue);
+    if (d->epilogue & ~(CC3D_EPI_RESIDUAL | CC3D_EPI_ACT | CC3D_EPI_U8))
+        return fail(CC3D_EINVAL, "epilogue flags 0x%x; accepted CC3D_EPI_RESIDUAL | CC3D_EPI_ACT | CC3D_EPI_U8",
+                    d->epilogue);
+    if ((d->epilogue & CC3D_EPI_ACT) && (d->epilogue & CC3D_EPI_U8))
+        return fail(CC3D_EINVAL, "CC3D_EPI_U8 cannot be combined with CC3D_EPI_ACT");
     if (d->cin <= 0) return fail(CC3D_ESHAPE, "cin=%d must be >= 1", d->cin);
     cc3d_op_desc op;
     memset(&op, 0, sizeof op);
@@ -585,6 +609,7 @@ cc3d_status cc3d_plan_create(const cc3d_conv_desc* d, const void* w, const float
     op.w = w;
     op.bias = bias;
     op.gamma = gamma;
+    op.out_u8 = (d->epilogue & CC3D_EPI_U8) ? 1 : 0;
     cc3d_stack_desc sd;
     sd.dtype = d->dtype;
     sd.cin = d->cin;
@@ -605,6 +630,8 @@ void cc3d_plan_destroy(cc3d_plan* plan)
 size_t cc3d_state_bytes(const cc3d_plan* plan) { return plan_ok(plan) ? plan->state_bytes : 0; }
 
 size_t cc3d_plan_device_bytes(const cc3d_plan* plan) { return plan_ok(plan) ? plan->device_bytes : 0; }
+
+int cc3d_output_elem_bytes(const cc3d_plan* plan) { return plan_ok(plan) ? plan->y_elem : 0; }
 
 cc3d_status cc3d_output_shape(const cc3d_plan* p, int t_chunk, int first, int* c, int* t, int* h, int* w)
 {
@@ -662,7 +689,7 @@ cc3d_status cc3d_forward_chunk(const cc3d_plan* p, const void* x, int t_chunk, c
         return fail(CC3D_EINVAL, "x, y, residual and the state arenas must be 16-byte aligned");
     const bool first = cache_in->frames_seen == 0;
     const Slot& ys = p->slots[CC3D_SLOT_Y];
-    const size_t y_bytes = (size_t)ys.tc.eval(t_chunk, first) * ys.h * ys.w * ys.c * p->elem;
+    const size_t y_bytes = (size_t)ys.tc.eval(t_chunk, first) * ys.h * ys.w * ys.c * p->y_elem;
     const size_t x_bytes = (size_t)t_chunk * p->h * p->w * p->cin * p->elem;
     if ((const char*)x < (const char*)y + y_bytes && (const char*)y < (const char*)x + x_bytes)
         return fail(CC3D_EINVAL, "x and y overlap");
@@ -719,6 +746,7 @@ cc3d_status cc3d_forward_chunk(const cc3d_plan* p, const void* x, int t_chunk, c
             a.nblocks = r.nblocks;
             a.family = r.family;
             a.rot_taps = 1;
+            a.out_u8 = r.out_u8 ? 1 : 0;
             if (r.fused_act) {
                 a.out = slot_ptr(r.out);
                 a.act_out = slot_ptr(r.act_out);
@@ -733,9 +761,10 @@ cc3d_status cc3d_forward_chunk(const cc3d_plan* p, const void* x, int t_chunk, c
             hipError_t e;
             {
                 const int nstore = (a.out ? 1 : 0) + (a.act_out ? 1 : 0);
+                const double store_scale = r.out_u8 ? 1.0 / p->elem : 1.0;  // 8-bit codes
                 const double by = fr_in * (t_in + (first ? 0 : r.kt - 1)) +
                                   (double)r.cout * r.cin * r.kt * r.kh * r.kw * p->elem +
-                                  t_v * fr_out * (nstore + (a.res ? 1 : 0));
+                                  t_v * fr_out * (nstore * store_scale + (a.res ? 1 : 0));
                 ProfScope ps(p, oi, 0, s, 2.0 * r.cin * r.cout * r.kt * r.kh * r.kw * vox, by);
                 e = p->dtype == CC3D_BF16 ? cc3d::launch_conv_bf16(a, s) : cc3d::launch_conv_f32(a, s);
             }

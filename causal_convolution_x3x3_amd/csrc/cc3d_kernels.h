@@ -37,7 +37,14 @@ struct ConvArgs {
     int ntile, nblocks;   // bf16: output channels per workgroup, number of such blocks
     int family;           // bf16: kernel family (1, 2 or 3) the weights were packed for
     int rot_taps;         // bf16 v2: rotate the temporal-tap order by the output frame
+    int out_u8;           // bf16 families 1 and 3: out holds 8-bit codes of the fp32 result
 };
+
+// 8-bit output code of an fp32 result v: rint(clamp((v + 1) * 127.5, 0, 255)).
+__device__ __forceinline__ uint8_t rgb8_code(float v)
+{
+    return (uint8_t)rintf(fminf(fmaxf((v + 1.0f) * 127.5f, 0.0f), 255.0f));
+}
 
 struct NormArgs {
     const void* src;      // [n_pix][c]

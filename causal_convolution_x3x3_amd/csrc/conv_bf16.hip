@@ -17,7 +17,8 @@
 // image is exactly "source pixel outside the image".  The temporal growth and the
 // causal history are resolved per frame by the ZWindow map.
 //
-// Epilogue (fp32): + bias, + residual, round to bf16 and store; optionally the
+// Epilogue (fp32): + bias, + residual, round to bf16 and store (or store the
+// 8-bit code of the fp32 result, see rgb8_code); optionally the
 // channel RMSNorm + SiLU of the stored value, reduced across the 16 lanes that
 // hold one pixel's channels (only when one workgroup holds every channel).
 //
@@ -182,9 +183,10 @@ __global__ __launch_bounds__(256) void conv_bf16_kernel(ConvArgs a)
                     v = acc[m][f][i];
                     if (a.bias) v += a.bias[n];
                     if (res && valid) v += bf2f(res[pbase + n]);
+                    if (a.out_u8 && out && valid) ((uint8_t*)out)[pbase + n] = rgb8_code(v);
                     const uint16_t hb = f2bf(v);
                     v = bf2f(hb);
-                    if (out && valid) out[pbase + n] = hb;
+                    if (out && valid && !a.out_u8) out[pbase + n] = hb;
                 }
                 vr[f] = v;
                 ss += v * v;

@@ -26,7 +26,8 @@
 // registers for the whole run, and the partial sums P go to LDS.  Each thread
 // then gathers the taps of two horizontally adjacent output pixels and adds
 // them to a three-frame ring of fp32 accumulators in registers; output frame t
-// is complete, and stored, once input frame t + 2 has been added.
+// is complete, and stored (bf16, or the 8-bit code of the fp32 value), once
+// input frame t + 2 has been added.
 #include "cc3d_kernels.h"
 
 namespace cc3d {
@@ -154,7 +155,10 @@ __global__ __launch_bounds__(256, 2) void conv_head_kernel(ConvArgs a, int fpw)
                 float y = v[q][o];
                 if (a.bias) y += a.bias[o];
                 if (res) y += bf2f(res[base + q * cout + o]);
-                out[base + q * cout + o] = bf16_rne(y);
+                if (a.out_u8)
+                    ((uint8_t*)a.out)[base + q * cout + o] = rgb8_code(y);
+                else
+                    out[base + q * cout + o] = bf16_rne(y);
             }
         }
     };

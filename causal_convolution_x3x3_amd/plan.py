@@ -67,6 +67,7 @@ class Op:
     w: Optional[torch.Tensor] = None
     bias: Optional[torch.Tensor] = None
     gamma: Optional[torch.Tensor] = None
+    out_u8: bool = False  # CONV writing the output slot: y as 8-bit codes
     name: str = field(default="")
 
 
@@ -80,6 +81,7 @@ class Plan:
         L = C.lib()
         self.state_bytes = int(L.cc3d_state_bytes(self._h))
         self.device_bytes = int(L.cc3d_plan_device_bytes(self._h))
+        self.out_dtype = torch.uint8 if L.cc3d_output_elem_bytes(self._h) == 1 else _TD[dtype]
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -125,7 +127,7 @@ class Plan:
         t_chunk = x.shape[0]
         if y is None:
             shape = self.output_shape(t_chunk, cache_in.frames_seen == 0)
-            y = torch.empty(shape, dtype=_TD[self.dtype], device=self.device)
+            y = torch.empty(shape, dtype=self.out_dtype, device=self.device)
         ci, co = cache_in._c(), cache_out._c()
         C.check(C.lib().cc3d_forward_chunk(self._h, _ptr(x), t_chunk, ctypes.byref(ci), ctypes.byref(co),
                                            _ptr(residual), _ptr(y), _stream(stream)), "cc3d_forward_chunk")
@@ -134,13 +136,14 @@ class Plan:
 
 
 def conv_plan(w: torch.Tensor, h_in: int, w_in: int, *, bias=None, gamma=None, up_s=1, up_t=1,
-              max_chunk_t=8, tpad=C.TPAD_REPLICATE, residual=False, act=False, eps=1e-6,
+              max_chunk_t=8, tpad=C.TPAD_REPLICATE, residual=False, act=False, out_u8=False, eps=1e-6,
               stream=None) -> Plan:
     """Plan for one causal conv; w is [Cout][Cin][kt][kh][kw] on the GPU (bf16 or fp32)."""
     cout, cin, kt, kh, kw = w.shape
     d = C.ConvDesc(cin=cin, cout=cout, kt=kt, kh=kh, kw=kw, h_in=h_in, w_in=w_in, up_s=up_s, up_t=up_t,
                    max_chunk_t=max_chunk_t, dtype=_DT[w.dtype], tpad=tpad,
-                   epilogue=(C.EPI_RESIDUAL if residual else 0) | (C.EPI_ACT if act else 0), eps=eps)
+                   epilogue=(C.EPI_RESIDUAL if residual else 0) | (C.EPI_ACT if act else 0) |
+                   (C.EPI_U8 if out_u8 else 0), eps=eps)
     h = ctypes.c_void_p()
     with torch.cuda.device(w.device):
         C.check(C.lib().cc3d_plan_create(ctypes.byref(d), _ptr(w), _ptr(bias), _ptr(gamma), _stream(stream),
@@ -155,7 +158,7 @@ def stack_plan(ops: List[Op], cin: int, h: int, w: int, *, dtype=torch.bfloat16,
         kt, kh, kw = o.k
         arr[i] = C.OpDesc(kind=o.kind, cout=o.cout, kt=kt, kh=kh, kw=kw, up_s=o.up_s, up_t=o.up_t,
                           tpad=o.tpad, src=o.src, res=o.res, out=o.out, act_out=o.act_out,
-                          w=_ptr(o.w), bias=_ptr(o.bias), gamma=_ptr(o.gamma))
+                          w=_ptr(o.w), bias=_ptr(o.bias), gamma=_ptr(o.gamma), out_u8=int(o.out_u8))
     d = C.StackDesc(dtype=_DT[dtype], cin=cin, h=h, w=w, max_chunk_t=max_chunk_t, eps=eps, n_ops=len(ops),
                     ops=arr)
     if device is None:

@@ -52,7 +52,7 @@ DECODER_STAGES = ((384, 2), (192, 2), (96, 1))
 
 
 def decoder_ops(params: Dict[str, Dict], stages=DECODER_STAGES, c_out: int = 3,
-                unique_slots: bool = False) -> List[Op]:
+                unique_slots: bool = False, out_u8: bool = False) -> List[Op]:
     """conv_in -> per stage [nearest up (2x space, 2x time on non-first frames
     when the stage's factor is 2) + conv, two residual blocks] -> head (act at low
     resolution, nearest 2x, conv to c_out).
@@ -61,7 +61,8 @@ def decoder_ops(params: Dict[str, Dict], stages=DECODER_STAGES, c_out: int = 3,
     alternates between them), act A, act B, inner act.  Slot 3 + 5*len(stages)
     holds conv_in's output.  ``unique_slots`` gives every tensor a slot of its
     own instead (same ops and kernels; every layer's input and output stay
-    readable after a chunk, for layer-wise checks)."""
+    readable after a chunk, for layer-wise checks).  ``out_u8``: the head stores
+    8-bit RGB codes instead of bf16."""
     nxt = [3]
 
     def slot(fixed):
@@ -102,5 +103,6 @@ def decoder_ops(params: Dict[str, Dict], stages=DECODER_STAGES, c_out: int = 3,
             raw_cur, act_cur, cur = new_raw, new_act, 1 - cur
         prev_raw, last_act = raw_cur, act_cur
     head = params["head"]
-    ops.append(Op(cout=c_out, w=head["w"], bias=head.get("b"), up_s=2, src=last_act, out=Y, name="head"))
+    ops.append(Op(cout=c_out, w=head["w"], bias=head.get("b"), up_s=2, src=last_act, out=Y, out_u8=out_u8,
+                  name="head"))
     return ops

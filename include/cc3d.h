@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define CC3D_VERSION 100 /* 1.0.0 */
+#define CC3D_VERSION 101 /* 1.0.1: 8-bit RGB output */
 
 typedef enum {
     CC3D_OK = 0,
@@ -83,6 +83,21 @@ typedef enum {
 #define CC3D_EPI_NONE 0
 #define CC3D_EPI_RESIDUAL 1 /* forward_chunk's residual (shape of y) is added */
 #define CC3D_EPI_ACT 2      /* store SiLU(RMSNorm(result)) using gamma [Cout] */
+#define CC3D_EPI_U8 4       /* store y as 8-bit codes (see "8-bit output" below) */
+
+/* 8-bit output (CC3D_EPI_U8, or out_u8 on the stack op that writes y): the
+ * output is delivered as uint8 codes instead of the plan dtype, as a video
+ * decoder hands RGB frames to an encoder (LightX2V blog "SwiftVR Inference
+ * Optimization ...", section "Other Engineering Optimizations": the output is
+ * converted to uint8 on the GPU, halving the payload sent to the host).  The page
+ * does not state the mapping; the one used here is the usual one for a decoder
+ * whose output range is [-1, 1]:
+ *   q = rint(clamp((v + 1) * 127.5, 0, 255))   (rint: round half to even)
+ * taken from the fp32 result v (conv + bias + residual) before any rounding to
+ * the plan dtype.  bf16 plans only, and not for 3x3 spatial convs whose output
+ * channels are split into 96- or 128-channel blocks (cout in 65..128, or a
+ * multiple of 96 or 128 above that; CC3D_ESHAPE); it cannot be combined with
+ * an act. */
 
 typedef struct {
     int cin, cout;        /* channels; bf16 plans need cin % 8 == 0 */
@@ -148,6 +163,7 @@ typedef struct {
     const void* w;     /* CONV: device weights [cout][cin][kt][kh][kw], plan dtype */
     const float* bias; /* CONV: device float32 [cout] or NULL */
     const float* gamma;/* device float32 [channels of v]; required when act_out is set */
+    int out_u8;        /* CONV writing CC3D_SLOT_Y only: 1 = y as 8-bit codes (CC3D_EPI_U8) */
 } cc3d_op_desc;
 
 typedef struct {
@@ -173,6 +189,10 @@ size_t cc3d_state_bytes(const cc3d_plan* plan);
 
 /* Device bytes the plan holds (packed weights and intermediates). */
 size_t cc3d_plan_device_bytes(const cc3d_plan* plan);
+
+/* Bytes per element of y: 1 with 8-bit output, else that of the plan dtype
+ * (0 for an invalid plan). */
+int cc3d_output_elem_bytes(const cc3d_plan* plan);
 
 /* Output shape of one forward_chunk: y is [*t][*h][*w][*c].  first != 0 for the
  * video's first chunk (frames grow by 2t-1 instead of 2t at each up_t = 2). */

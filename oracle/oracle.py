@@ -194,6 +194,23 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
+def quantize_rgb8(y: np.ndarray) -> np.ndarray:
+    """8-bit output codes: q = rint(clip((y + 1) * 127.5, 0, 255)), rint rounding
+    half to even.  The SwiftVR page ("Other Engineering Optimizations") converts
+    the decoder output to uint8 on the GPU before the host copy; it does not state
+    the mapping, and this is the usual one for an output range of [-1, 1]."""
+    return np.rint(np.clip((np.asarray(y, dtype=np.float64) + 1.0) * 127.5, 0.0, 255.0)).astype(np.uint8)
+
+
+def rgb8_ambiguous(y: np.ndarray, margin: float = 0.002) -> np.ndarray:
+    """Positions whose code a different summation order may legitimately change:
+    (y + 1) * 127.5 lies within ``margin`` of a rounding boundary k + 0.5 inside
+    [0, 255]."""
+    t = (np.asarray(y, dtype=np.float64) + 1.0) * 127.5
+    f = t - np.floor(t)
+    return (np.abs(f - 0.5) < margin) & (t > -margin) & (t < 255.0 + margin)
+
+
 # ------------------------------------------------------------- streaming --
 
 class CausalConvStream:

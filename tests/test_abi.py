@@ -24,7 +24,7 @@ def test_library_exports_every_declared_function():
     assert sorted(declared) == sorted(C.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.cc3d_version() == 100
+    assert L.cc3d_version() == 101
 
 
 def _conv_desc(**kw):
@@ -41,7 +41,7 @@ DUMMY = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
     (dict(kt=0), C.ESHAPE), (dict(kt=4), C.ESHAPE), (dict(kh=2), C.ESHAPE), (dict(up_s=3), C.ESHAPE),
     (dict(up_t=0), C.ESHAPE), (dict(dtype=7), C.EDTYPE), (dict(tpad=5), C.EINVAL), (dict(cin=12), C.ESHAPE),
     (dict(max_chunk_t=0), C.ESHAPE), (dict(h_in=0), C.ESHAPE), (dict(cout=0), C.ESHAPE),
-    (dict(epilogue=8), C.EINVAL), (dict(kh=3, kw=1), C.ESHAPE), (dict(eps=-1.0), C.EINVAL),
+    (dict(epilogue=8), C.EINVAL), (dict(epilogue=C.EPI_ACT | C.EPI_U8), C.EINVAL), (dict(kh=3, kw=1), C.ESHAPE), (dict(eps=-1.0), C.EINVAL),
 ])
 def test_plan_create_rejects_bad_descriptor(bad, status):
     L = C.lib()

@@ -360,3 +360,95 @@ def test_plan_create_failure_releases_everything(monkeypatch):
     assert torch.cuda.mem_get_info()[0] >= free0 - (2 << 20)
     plan = P.stack_plan(ops, c, h, w, max_chunk_t=4)  # and creation still works
     assert plan.state_bytes > 0
+
+
+# ------------------------------------------------------------ 8-bit output --
+
+def assert_rgb8_matches(got_u8, y_ref, what):
+    """Codes equal the oracle's quantization of its fp64 result, except where that
+    result lies within a hair of a rounding boundary (a different summation order
+    may flip those by one code); such positions must be rare."""
+    ref = O.quantize_rgb8(y_ref)
+    amb = O.rgb8_ambiguous(y_ref)
+    got = np.asarray(got_u8).astype(np.int64)
+    d = np.abs(got - ref.astype(np.int64))
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(d[~amb] == 0), "%s: %d codes differ away from a rounding boundary" % (what, int((d[~amb] > 0).sum()))
+    assert np.all(d[amb] <= 1), what
+    assert amb.mean() < 0.01, "%s: %.3f of the positions are ambiguous" % (what, amb.mean())
+    # the codes span the range (not a degenerate all-0 / all-255 output)
+    assert ref.min() < 64 and ref.max() > 192, (what, ref.min(), ref.max())
+
+
+@pytest.mark.parametrize("case", [
+    # cin, cout, up_s, h, w, splits, residual
+    (96, 3, 2, 13, 37, [1, 4, 3], False),   # output head kernel
+    (64, 3, 2, 9, 20, [2, 3], True),         # output head kernel + residual
+    (96, 3, 1, 20, 36, [2, 3], False),       # small-output kernel (1440p stage's last conv)
+    (32, 16, 1, 11, 40, [1, 2], True),       # small-output kernel, 16 channels
+], ids=lambda c: "ci%d_co%d_us%d_res%d" % (c[0], c[1], c[2], c[6]))
+def test_conv_rgb8_output(case):
+    cin, cout, up_s, h, w, splits, residual = case
+    say("rgb8 conv %s" % (case,))
+    t = sum(splits)
+    x = synth.bf16(synth.video(cin, t, h, w, synth.seed(6, 21)))
+    # weights scaled so the output spans [-1, 1] and beyond (clamping exercised)
+    wt = synth.bf16(synth.conv_weight(cout, cin, 3, 3, 3, synth.seed(6, 22)) * 0.6)
+    b = synth.bias(cout, synth.seed(6, 23))
+    r = synth.bf16(synth.video(cout, t, h * up_s, w * up_s, synth.seed(6, 24)) * 0.3) if residual else None
+    y = O.one_shot(to_oracle(x), to_oracle(wt), to_oracle(b), O.REPLICATE, up_s=up_s)
+    if residual:
+        y = y + to_oracle(r)
+    plan = P.conv_plan(wt.cuda(), h, w, bias=b.cuda(), up_s=up_s, residual=residual, out_u8=True,
+                       max_chunk_t=max(splits))
+    assert plan.out_dtype == torch.uint8
+    got = _run_chunks(plan, to_device_cl(x), splits, residual_cl=to_device_cl(r) if residual else None)
+    assert got.dtype == torch.uint8
+    assert_rgb8_matches(got.cpu().permute(3, 0, 1, 2).numpy(), y, "rgb8 conv")
+
+
+def test_rgb8_rejected_where_unsupported():
+    """The 3x3 kernel for 96/128-channel blocks has no 8-bit store: plan creation
+    fails with ESHAPE before any device work; an act cannot be 8-bit."""
+    wt = synth.bf16(synth.conv_weight(96, 32, 3, 3, 3, synth.seed(6, 30))).cuda()
+    with pytest.raises(C.Cc3dError) as e:
+        P.conv_plan(wt, 8, 16, out_u8=True)
+    assert e.value.status == C.ESHAPE
+    w3 = synth.bf16(synth.conv_weight(4, 32, 3, 3, 3, synth.seed(6, 31))).cuda()
+    with pytest.raises(C.Cc3dError) as e:
+        P.conv_plan(w3, 8, 16, out_u8=True, act=True, gamma=torch.ones(4, device="cuda"))
+    assert e.value.status == C.EINVAL
+
+
+def test_decoder_rgb8_output_matches_bf16_head():
+    """The decoder with 8-bit output: the same kernels up to the head, whose codes
+    match the oracle's quantization of the head conv fed the GPU's own head input."""
+    say("decoder rgb8")
+    stages = ((64, 2), (32, 2), (16, 1))
+    full = OM.decoder_layer_shapes(c_latent=16, stages=stages)
+    gains = {s_[0]: s_[6] for s_ in full}
+    cpu, dev = _params([s_[:6] for s_ in full], 4, lambda n: gains[n])
+    t, h, w, splits = 5, 3, 5, [2, 3]
+    x = synth.bf16(synth.video(16, t, h, w, synth.seed(4, 1)))
+    x_cl = to_device_cl(x)
+    ops = S.decoder_ops(dev, stages=stages, unique_slots=True, out_u8=True)
+    plan = P.stack_plan(ops, 16, h, w, max_chunk_t=max(splits))
+    ops_b = S.decoder_ops(dev, stages=stages, unique_slots=True)
+    plan_b = P.stack_plan(ops_b, 16, h, w, max_chunk_t=max(splits))
+    st, st_b = P.Stream(plan), P.Stream(plan_b)
+    head = ops[-1]
+    ref_head = O.CausalConvStream(cpu["head"]["w"], cpu["head"]["b"], O.REPLICATE, 2, 1)
+    t0 = 0
+    for n in splits:
+        first = st.frames_seen == 0
+        xc = x_cl[t0:t0 + n].contiguous()
+        y8, yb = st.step(xc), st_b.step(xc)
+        torch.cuda.synchronize()
+        hin = plan.read_slot(head.src, n, first)
+        assert torch.equal(hin, plan_b.read_slot(ops_b[-1].src, n, first)), "layers before the head differ"
+        y_ref = ref_head.step(from_device_cl(hin))
+        assert_rgb8_matches(y8.cpu().permute(3, 0, 1, 2).numpy(), y_ref, "decoder head rgb8 (chunk at %d)" % t0)
+        # the bf16 output and the codes describe the same values
+        assert np.abs(O.quantize_rgb8(from_device_cl(yb)).astype(int) -
+                      y8.cpu().permute(3, 0, 1, 2).numpy().astype(int)).max() <= 1
+        t0 += n

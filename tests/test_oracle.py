@@ -369,3 +369,21 @@ def test_stack_rounding_divergence():
     mx, mn = d.max() / np.abs(ref).max(), d.mean() / np.abs(ref).mean()
     assert mn > 2e-3          # a single-layer mean bound cannot hold end to end
     assert mx < 1e-2 * 3 and mn < 5e-3 * 3  # the stack bound (3x) leaves room for it
+
+
+def test_rgb8_quantizer_closed_forms():
+    """The 8-bit output map at its fixed points: -1 -> 0, +1 -> 255, 0 -> 128
+    (127.5 rounds half to even), clamping outside [-1, 1], and the code of every
+    integer level k is recovered from y = k / 127.5 - 1."""
+    y = np.array([-1.0, 1.0, 0.0, -3.0, 5.0, np.nextafter(-1.0, 0.0), 1.0 / 255.0])
+    assert O.quantize_rgb8(y).tolist() == [0, 255, 128, 0, 255, 0, 128]
+    k = np.arange(256)
+    assert np.array_equal(O.quantize_rgb8(k / 127.5 - 1.0), k.astype(np.uint8))
+    # y = 0 is the one exactly half-way input (t = 127.5): it rounds to the even
+    # code 128; just below it rounds down
+    assert O.quantize_rgb8(np.array([-1e-9, 1e-9])).tolist() == [127, 128]
+    # monotone non-decreasing
+    ys = np.linspace(-1.2, 1.2, 10001)
+    assert np.all(np.diff(O.quantize_rgb8(ys).astype(int)) >= 0)
+    amb = O.rgb8_ambiguous(np.array([0.5 / 127.5 - 1.0, 0.0, 0.25, 0.01 / 127.5]))
+    assert amb.tolist() == [True, True, False, False]
