@@ -1,6 +1,7 @@
 """Benchmark of the chunked causal Conv3d decode on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4|c3] [--no-cpu-baseline]
+                    [--no-delivery]
 
 Workloads (synthetic, seeded; the pages' test videos and trained weights are not
 available):
@@ -14,8 +15,10 @@ Inputs are resident in HBM before timing; outputs go to a device ring.
 
 Prints one JSON line: value = algorithmic conv TFLOP/s (2*Cin*Cout*27 FLOP per
 output voxel of every conv) over the timed steps; plus output frames/s, the
-dominant kernel's roofline (live HIP-event timing on the plan's stream) and the
-CPU oracle's rate on a bounded sample of the same workload.
+dominant kernel's roofline (live HIP-event timing on the plan's stream), the
+host-delivery rate (c4: every clip's output copied to pinned host memory on a
+second stream, bf16 and 8-bit; never the headline value) and the CPU oracle's
+rate on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -86,11 +89,11 @@ def c4_step_flops(t_lat, first, h=90, w=160):
     return f, t
 
 
-def setup_c4(dev, torch, synth, P, S):
+def setup_c4(dev, torch, synth, P, S, out_u8=False):
     lat_c, lat_t, lh, lw = 48, 91, 90, 160
     layers = decoder_layer_list()
     params = make_decoder(dev, synth, S, layers)
-    ops = S.decoder_ops(params)
+    ops = S.decoder_ops(params, out_u8=out_u8)
     plan = P.stack_plan(ops, lat_c, lh, lw, max_chunk_t=7, device=dev)
     del params
     log("c4 plan: %d ops, state %.2f GB, plan device memory %.2f GB" % (
@@ -160,6 +163,61 @@ def recorded_traffic(kernel_name):
     return None
 
 
+def delivery_rate(torch, plan, work, steps, warmup, dev):
+    """Frames/s of the decode with every clip's output copied to pinned host
+    memory on a second stream (the SwiftVR page's overlap of output transfer with
+    compute, "Other Engineering Optimizations"): device output ring of two,
+    pinned host ring of two, the copy of clip i overlapping the decode of clip
+    i+1; timed to the end of the last copy.  Returns (frames/s, host GB/s of
+    the copies alone, bytes per clip)."""
+    copy_stream = torch.cuda.Stream(device=dev)
+    comp = torch.cuda.current_stream(dev)
+    shape = (25, 1440, 2560, 3)
+    ring = [torch.empty(shape, dtype=plan.out_dtype, device=dev) for _ in range(2)]
+    host = [torch.empty(shape, dtype=plan.out_dtype, pin_memory=True) for _ in range(2)]
+    produced = [torch.cuda.Event() for _ in range(2)]
+    copied = [torch.cuda.Event() for _ in range(2)]
+    timing = []  # (start, end) events of every timed copy, read after the run
+    states = [plan.new_state(), plan.new_state()]
+    cur = [0]
+    nbytes = [0]
+
+    def clip(i, timed):
+        xc, first, fl, tout = work[i % len(work)]
+        k = i % 2
+        if i >= 2:
+            comp.wait_event(copied[k])  # the copy out of this ring slot is done
+        if first:
+            plan.reset(states[cur[0]])
+        plan.forward_chunk(xc, states[cur[0]], states[1 - cur[0]], y=ring[k][:tout])
+        cur[0] = 1 - cur[0]
+        produced[k].record(comp)
+        copy_stream.wait_event(produced[k])
+        with torch.cuda.stream(copy_stream):
+            if timed:
+                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                ev[0].record(copy_stream)
+            host[k][:tout].copy_(ring[k][:tout], non_blocking=True)
+            copied[k].record(copy_stream)
+            if timed:
+                ev[1].record(copy_stream)
+                timing.append(ev)
+                nbytes[0] += ring[k][:tout].numel() * ring[k].element_size()
+        return tout
+
+    for i in range(warmup):
+        clip(i, False)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    frames = 0
+    for i in range(warmup, warmup + steps):
+        frames += clip(i, True)
+    torch.cuda.synchronize(dev)
+    dt = time.perf_counter() - t0
+    copy_ms = sum(a.elapsed_time(b) for a, b in timing)
+    return frames / dt, nbytes[0] / (copy_ms * 1e-3) / 1e9, nbytes[0] / steps
+
+
 def cpu_baseline(workload):
     """The fp64 oracle, as it stands, on a bounded crop of the same workload."""
     import numpy as np
@@ -213,6 +271,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", choices=["c4", "c3"], default="c4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-delivery", action="store_true",
+                    help="skip the host-delivery measurement (c4: output copied to pinned host memory)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this decode path has no multi-GPU mode "
@@ -306,6 +366,22 @@ def main():
         "config": desc, "frames_per_s": round(frames / dt, 2), "mfma_frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": roof, "kernels": per_kernel,
     }
+    if args.workload == "c4" and not args.no_delivery:
+        # Host delivery: the same decode with every clip's RGB copied to pinned host
+        # memory, overlapped with the next clip; bf16 output, then 8-bit codes.
+        # PCIe-inclusive, so never the headline value.
+        deliv = {}
+        out_dtype_names = {False: "bf16", True: "uint8"}
+        for u8 in (False, True):
+            if u8:
+                del plan
+                torch.cuda.empty_cache()
+                plan, work, ring, _ = setup_c4(dev, torch, synth, P, S, out_u8=True)
+            log("delivery to pinned host memory, %s output" % out_dtype_names[u8])
+            fps, gbs, per_clip = delivery_rate(torch, plan, work, args.steps, args.warmup, dev)
+            deliv[out_dtype_names[u8]] = {"frames_per_s": round(fps, 2), "copy_gbs": round(gbs, 1),
+                                          "bytes_per_clip": per_clip}
+        out["delivery"] = deliv
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
         out["cpu_baseline"] = cpu_baseline(args.workload)

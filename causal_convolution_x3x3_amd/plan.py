@@ -18,6 +18,13 @@ _DT = {torch.bfloat16: C.BF16, torch.float32: C.F32}
 _TD = {C.BF16: torch.bfloat16, C.F32: torch.float32}
 
 
+def _numel(shape) -> int:
+    n = 1
+    for d in shape:
+        n *= int(d)
+    return n
+
+
 def _ptr(t: Optional[torch.Tensor]):
     if t is None:
         return None
@@ -125,9 +132,12 @@ class Plan:
                       residual: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
                       stream=None) -> torch.Tensor:
         t_chunk = x.shape[0]
+        shape = self.output_shape(t_chunk, cache_in.frames_seen == 0)
         if y is None:
-            shape = self.output_shape(t_chunk, cache_in.frames_seen == 0)
             y = torch.empty(shape, dtype=self.out_dtype, device=self.device)
+        elif y.dtype != self.out_dtype or y.numel() < _numel(shape):
+            raise ValueError("y must hold %s elements of %s for this chunk, got %s of %s"
+                             % (_numel(shape), self.out_dtype, y.numel(), y.dtype))
         ci, co = cache_in._c(), cache_out._c()
         C.check(C.lib().cc3d_forward_chunk(self._h, _ptr(x), t_chunk, ctypes.byref(ci), ctypes.byref(co),
                                            _ptr(residual), _ptr(y), _stream(stream)), "cc3d_forward_chunk")
