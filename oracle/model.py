@@ -17,6 +17,13 @@ workloads built from those pieces:
   act at low resolution -> nearest 2x -> conv to 3 channels.  Moving the act
   before the upsample is exact because it works per position (the SwiftVR page,
   "TemporalGrow: Compute Before Spatial Upsampling").
+* ``TemporalGrow`` (same section): a 1x1 spatial projection followed by a
+  causal temporal conv with a 3x1x1 kernel, both per position; it grows the
+  frame count (the nearest 2x rule above, applied to the projection's output
+  before the temporal conv).  With ``temporal_grow`` the decoder has one per
+  stage, growth (2, 2, 1), taking over the stage's temporal growth: "before"
+  runs it at the stage's input size, ahead of the upsample conv; "after" runs it
+  on the upsampled positions, between the upsample and the spatial conv.
 
 ``store`` is the storage rounding: with ``store=round_bf16`` every tensor that
 passes between layers is rounded to bfloat16, as a bf16 pipeline stores it
@@ -41,8 +48,8 @@ def _keep(x, store):
 class Conv:
     """One causal conv layer with its cache (see oracle.CausalConvStream)."""
 
-    def __init__(self, p, mode=O.REPLICATE, up_s=1, up_t=1, nthreads=None):
-        self.s = O.CausalConvStream(p["w"], p.get("b"), mode, up_s, up_t, nthreads)
+    def __init__(self, p, mode=O.REPLICATE, up_s=1, up_t=1, nthreads=None, aligned=False):
+        self.s = O.CausalConvStream(p["w"], p.get("b"), mode, up_s, up_t, nthreads, aligned)
 
     def reset(self):
         self.s.reset()
@@ -90,15 +97,44 @@ class UpStage:
         return _keep(self.c2.step(a), st)
 
 
+class TemporalGrow:
+    """q = tconv(grow(proj(x))): proj a 1x1x1 conv, grow the nearest temporal
+    rule (factor 1 or 2), tconv a causal 3x1x1 conv with its own cache.  With
+    up_s = 2 the projection reads the nearest-upsampled input (the "after"
+    order: the block then runs on every upsampled position)."""
+
+    def __init__(self, p_proj, p_t, factor, mode=O.REPLICATE, up_s=1, store=None, nthreads=None,
+                 aligned=False):
+        self.proj = Conv(p_proj, mode, up_s=up_s, nthreads=nthreads)
+        self.tconv = Conv(p_t, mode, up_t=factor, nthreads=nthreads, aligned=aligned)
+        self.store = store
+
+    def reset(self):
+        self.proj.reset()
+        self.tconv.reset()
+
+    def step(self, x):
+        p = _keep(self.proj.step(x), self.store)
+        return _keep(self.tconv.step(p), self.store)
+
+
 DECODER_STAGES = ((384, 2), (192, 2), (96, 1))  # (channels, temporal factor)
+TG_ORDERS = (None, "before", "after")
 
 
-def decoder_layer_shapes(c_latent=48, stages=DECODER_STAGES, c_out=3, k=3):
+def decoder_layer_shapes(c_latent=48, stages=DECODER_STAGES, c_out=3, k=3, temporal_grow=None):
     """(name, Cout, Cin, kt, kh, kw, has_gain) for every conv of the decoder,
-    in execution order.  ``has_gain``: the conv's input passes an RMSNorm."""
+    in execution order.  ``has_gain``: the conv's input passes an RMSNorm.
+    With ``temporal_grow`` each stage starts with a TemporalGrow on its input
+    channels: "s<i>.tg.p" (1x1x1) and "s<i>.tg.t" (3x1x1)."""
+    if temporal_grow not in TG_ORDERS:
+        raise ValueError("temporal_grow must be one of %r" % (TG_ORDERS,))
     shapes = [("conv_in", stages[0][0], c_latent, k, k, k, False)]
     cin = stages[0][0]
     for si, (c, _) in enumerate(stages):
+        if temporal_grow:
+            shapes.append(("s%d.tg.p" % si, cin, cin, 1, 1, 1, False))
+            shapes.append(("s%d.tg.t" % si, cin, cin, 3, 1, 1, False))
         shapes.append(("s%d.up" % si, c, cin, k, k, k, False))
         for r in range(2):
             shapes.append(("s%d.rb%d.c1" % (si, r), c, c, k, k, k, True))
@@ -109,14 +145,29 @@ def decoder_layer_shapes(c_latent=48, stages=DECODER_STAGES, c_out=3, k=3):
 
 
 class Decoder:
+    """``temporal_grow``: None (the stage's up conv grows time), "before" or
+    "after" (a TemporalGrow per stage does, see the module docstring).
+    ``aligned``: the first chunk is grown like every later one (every frame
+    doubled), the reading of the 28-frame first chunk that drops 3 frames."""
+
     def __init__(self, params, eps=1e-6, mode=O.REPLICATE, stages=DECODER_STAGES,
-                 store=None, nthreads=None):
+                 store=None, nthreads=None, temporal_grow=None, aligned=False):
+        if temporal_grow not in TG_ORDERS:
+            raise ValueError("temporal_grow must be one of %r" % (TG_ORDERS,))
         self.eps, self.store = eps, store
         self.conv_in = Conv(params["conv_in"], mode, nthreads=nthreads)
-        self.ups, self.blocks = [], []
+        self.ups, self.blocks, self.tgs = [], [], []
         for si, (_, up_t) in enumerate(stages):
-            self.ups.append(Conv(params["s%d.up" % si], mode, up_s=2, up_t=up_t,
-                                 nthreads=nthreads))
+            if temporal_grow:
+                after = temporal_grow == "after"
+                self.tgs.append(TemporalGrow(params["s%d.tg.p" % si], params["s%d.tg.t" % si], up_t, mode,
+                                             up_s=2 if after else 1, store=store, nthreads=nthreads,
+                                             aligned=aligned))
+                self.ups.append(Conv(params["s%d.up" % si], mode, up_s=1 if after else 2, nthreads=nthreads))
+            else:
+                self.tgs.append(None)
+                self.ups.append(Conv(params["s%d.up" % si], mode, up_s=2, up_t=up_t,
+                                     nthreads=nthreads, aligned=aligned))
             self.blocks.append([
                 ResBlock(params["s%d.rb%d.c1" % (si, r)], params["s%d.rb%d.c2" % (si, r)],
                          eps, mode, store, nthreads) for r in range(2)])
@@ -128,6 +179,9 @@ class Decoder:
         self.head.reset()
         for u in self.ups:
             u.reset()
+        for g in self.tgs:
+            if g is not None:
+                g.reset()
         for bl in self.blocks:
             for b in bl:
                 b.reset()
@@ -135,7 +189,9 @@ class Decoder:
     def step(self, x):
         st = self.store
         h = _keep(self.conv_in.step(x), st)
-        for up, bl in zip(self.ups, self.blocks):
+        for tg, up, bl in zip(self.tgs, self.ups, self.blocks):
+            if tg is not None:
+                h = tg.step(h)
             h = _keep(up.step(h), st)
             for b in bl:
                 h = b.step(h)
@@ -143,11 +199,15 @@ class Decoder:
         return _keep(self.head.step(a), st)
 
 
-def output_frames(n_latent: int, temporal_factors=(2, 2)) -> int:
-    """Frames after temporal growth on non-first frames: n -> 1 + f (n - 1)."""
+def output_frames(n_latent: int, temporal_factors=(2, 2), aligned: bool = False) -> int:
+    """Frames after temporal growth on non-first frames: n -> 1 + f (n - 1);
+    with ``aligned`` (every frame grown): n -> f n."""
     n = n_latent
     for f in temporal_factors:
-        n = 1 + f * (n - 1) if n > 0 else 0
+        if aligned:
+            n = f * n
+        else:
+            n = 1 + f * (n - 1) if n > 0 else 0
     return n
 
 

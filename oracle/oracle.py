@@ -23,6 +23,11 @@ float64 numpy arrays laid out [C][T][H][W] (one video, channels first):
   block and the stacks are the synthetic decoder workloads' own definitions
   (the pages name the blocks but print no layer list); the readings taken where
   the pages are silent are listed in the design doc.
+* aligned first chunk -- "From Pixels to Latents and Back": the first chunk
+  reads 28 frames and drops 3 after decoding.  Read here as a growth rule that
+  doubles every frame, the first chunk's included (``aligned=True``); with
+  copies of the first frame as history it puts the first output frame three
+  extra times in front of the other rule's output.
 
 The dense sum itself runs in ``cc3d_oracle.c`` (plain nested loops, fp64).
 """
@@ -160,10 +165,11 @@ def upsample_spatial(x: np.ndarray, s: int = 2) -> np.ndarray:
     return np.repeat(np.repeat(x, s, axis=2), s, axis=3)
 
 
-def upsample_temporal(x: np.ndarray, first: bool) -> np.ndarray:
+def upsample_temporal(x: np.ndarray, first: bool, aligned: bool = False) -> np.ndarray:
     """Nearest 2x in time on non-first frames: V[0]=X[0]; V[2j-1]=V[2j]=X[j].
-    For a chunk that does not start the video every frame is doubled."""
-    if first:
+    For a chunk that does not start the video every frame is doubled, and so is
+    every frame of the first chunk with ``aligned`` (V[2j]=V[2j+1]=X[j])."""
+    if first and not aligned:
         return np.concatenate([x[:, :1], np.repeat(x[:, 1:], 2, axis=1)], axis=1)
     return np.repeat(x, 2, axis=1)
 
@@ -221,16 +227,18 @@ class CausalConvStream:
     the last k_t-1 frames of Z.  On the first chunk the cache is the history
     rule (zeros or copies of the chunk's first frame).  The cache is held at the
     input's own resolution; when ``up_s``/``up_t`` are set the chunk is first
-    upsampled (nearest, spatial; temporal growth on non-first frames).
+    upsampled (nearest, spatial; temporal growth on non-first frames, or on
+    every frame with ``aligned``).
     """
 
     def __init__(self, w, bias=None, mode: str = REPLICATE, up_s: int = 1, up_t: int = 1,
-                 nthreads: int | None = None):
+                 nthreads: int | None = None, aligned: bool = False):
         self.w = np.asarray(w, dtype=np.float64)
         self.bias = None if bias is None else np.asarray(bias, dtype=np.float64)
         self.mode = mode
         self.up_s = up_s
         self.up_t = up_t
+        self.aligned = aligned
         self.kt = self.w.shape[2]
         self.nthreads = nthreads
         self.reset()
@@ -242,7 +250,7 @@ class CausalConvStream:
     def logical_input(self, x: np.ndarray) -> np.ndarray:
         v = np.asarray(x, dtype=np.float64)
         if self.up_t == 2:
-            v = upsample_temporal(v, first=(self.frames_seen == 0))
+            v = upsample_temporal(v, first=(self.frames_seen == 0), aligned=self.aligned)
         return v
 
     def step(self, x: np.ndarray) -> np.ndarray:
@@ -257,19 +265,20 @@ class CausalConvStream:
         return y
 
 
-def one_shot(x, w, bias=None, mode=REPLICATE, up_s=1, up_t=1, nthreads=None):
+def one_shot(x, w, bias=None, mode=REPLICATE, up_s=1, up_t=1, nthreads=None, aligned=False):
     """Upsample the whole video, then the one-shot causal conv."""
     v = np.asarray(x, dtype=np.float64)
     if up_t == 2:
-        v = upsample_temporal(v, first=True)
+        v = upsample_temporal(v, first=True, aligned=aligned)
     if up_s > 1:
         v = upsample_spatial(v, up_s)
     return causal_conv3d(v, w, bias, mode, nthreads)
 
 
-def chunked(x, w, bias=None, mode=REPLICATE, up_s=1, up_t=1, splits=None, nthreads=None):
+def chunked(x, w, bias=None, mode=REPLICATE, up_s=1, up_t=1, splits=None, nthreads=None,
+            aligned=False):
     """Run the stream over chunk lengths ``splits`` and concatenate the outputs."""
-    s = CausalConvStream(w, bias, mode, up_s, up_t, nthreads)
+    s = CausalConvStream(w, bias, mode, up_s, up_t, nthreads, aligned)
     out, t0 = [], 0
     for n in splits:
         out.append(s.step(x[:, t0:t0 + n]))

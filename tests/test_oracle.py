@@ -387,3 +387,124 @@ def test_rgb8_quantizer_closed_forms():
     assert np.all(np.diff(O.quantize_rgb8(ys).astype(int)) >= 0)
     amb = O.rgb8_ambiguous(np.array([0.5 / 127.5 - 1.0, 0.0, 0.25, 0.01 / 127.5]))
     assert amb.tolist() == [True, True, False, False]
+
+
+# ------------------------------------- TemporalGrow and the aligned first chunk --
+
+def _tg_params(r, c, bias=False):
+    pp = {"w": r.standard_normal((c, c, 1, 1, 1)) / np.sqrt(c), "b": r.uniform(-0.1, 0.1, c) if bias else None}
+    pt = {"w": r.standard_normal((c, c, 3, 1, 1)) / np.sqrt(3 * c), "b": r.uniform(-0.1, 0.1, c) if bias else None}
+    return pp, pt
+
+
+@pytest.mark.parametrize("aligned", [False, True])
+@pytest.mark.parametrize("mode", [O.REPLICATE, O.ZERO])
+def test_tg_delta_weights_closed_form(mode, aligned):
+    """Identity projection; a temporal delta at the current tap gives the grown
+    sequence itself, at the oldest tap the grown sequence two frames back (the
+    history rule before it) -- across chunk boundaries too."""
+    x = _rng(30).standard_normal((3, 5, 2, 3))
+    proj = {"w": _delta(3, 1, 1, 1, 0, 0, 0), "b": None}
+    for tap in (2, 0):
+        tg = M.TemporalGrow(proj, {"w": _delta(3, 3, 1, 1, tap, 0, 0), "b": None}, 2, mode, aligned=aligned)
+        y = np.concatenate([tg.step(x[:, :2]), tg.step(x[:, 2:3]), tg.step(x[:, 3:])], axis=1)
+        if aligned:
+            v = np.repeat(x, 2, axis=1)                                  # V[2j] = V[2j+1] = X[j]
+        else:
+            v = np.concatenate([x[:, :1], np.repeat(x[:, 1:], 2, axis=1)], axis=1)  # V[0]=X[0]
+        assert y.shape == v.shape
+        if tap == 2:
+            assert np.array_equal(y, v)
+        else:
+            assert np.array_equal(y[:, 2:], v[:, :-2])
+            for u in range(2):
+                expect = v[:, 0] if mode == O.REPLICATE else np.zeros_like(v[:, 0])
+                assert np.array_equal(y[:, u], expect)
+
+
+def test_tg_projection_mixes_channels_only():
+    """Projection = the channel matrix at every position and frame (a library
+    matmul); factor 1 with a delta at the current tap leaves the frame count."""
+    r = _rng(31)
+    x = r.standard_normal((4, 3, 2, 5))
+    pp, _ = _tg_params(r, 4, bias=True)
+    tg = M.TemporalGrow(pp, {"w": _delta(4, 3, 1, 1, 2, 0, 0), "b": None}, 1)
+    ref = np.einsum("oc,cthw->othw", pp["w"][:, :, 0, 0, 0], x) + pp["b"][:, None, None, None]
+    assert np.max(np.abs(tg.step(x) - ref)) <= 1e-14
+
+
+@pytest.mark.parametrize("store", [None, O.round_bf16])
+def test_tg_commutes_with_nearest_upsample_bitwise(store):
+    """TemporalGrow at the input size then nearest 2x == nearest 2x then
+    TemporalGrow, bit for bit (it never mixes positions) -- the reorder the
+    SwiftVR page reports as bitwise identical."""
+    r = _rng(32)
+    x = r.standard_normal((5, 4, 3, 4))
+    pp, pt = _tg_params(r, 5, bias=True)
+    before = M.TemporalGrow(pp, pt, 2, store=store)
+    after = M.TemporalGrow(pp, pt, 2, up_s=2, store=store)
+    for lo, hi in ((0, 2), (2, 4)):
+        a = O.upsample_spatial(before.step(x[:, lo:hi]), 2)
+        b = after.step(x[:, lo:hi])
+        assert np.array_equal(a, b)
+
+
+def _decoder_params(r, stages, c_latent, temporal_grow):
+    shapes = M.decoder_layer_shapes(c_latent=c_latent, stages=stages, temporal_grow=temporal_grow)
+    return {n: {"w": r.standard_normal((co, ci, kt, kh, kw)) / np.sqrt(ci * kt * kh * kw),
+                "b": r.uniform(-0.1, 0.1, co), "g": r.uniform(0.5, 1.5, ci) if g else None}
+            for n, co, ci, kt, kh, kw, g in shapes}
+
+
+def test_decoder_tg_orders_bitwise_and_chunked():
+    r = _rng(33)
+    stages = ((6, 2), (5, 2), (4, 1))
+    params = _decoder_params(r, stages, 3, "before")
+    x = r.standard_normal((3, 4, 2, 3))
+    outs = {}
+    for order in ("before", "after"):
+        d = M.Decoder(params, stages=stages, temporal_grow=order, store=O.round_bf16)
+        outs[order] = np.concatenate([d.step(x[:, :1]), d.step(x[:, 1:3]), d.step(x[:, 3:])], axis=1)
+    assert outs["before"].shape == (3, M.output_frames(4), 32, 48)
+    assert np.array_equal(outs["before"], outs["after"])
+    d = M.Decoder(params, stages=stages, temporal_grow="before", store=O.round_bf16)
+    assert np.array_equal(d.step(x), outs["before"])
+    with pytest.raises(ValueError):
+        M.Decoder(params, stages=stages, temporal_grow="sideways")
+
+
+@pytest.mark.parametrize("temporal_grow", [None, "before"])
+def test_aligned_first_chunk_drops_to_the_same_video(temporal_grow):
+    """Aligned growth (every frame doubled from the start) with copies of the
+    first frame as history: the decoded video is the other rule's video with
+    its first frame three extra times in front -- dropping 3 frames of the
+    first chunk gives it back exactly.  With zero history it does not."""
+    r = _rng(34)
+    stages = ((6, 2), (5, 2), (4, 1))
+    params = _decoder_params(r, stages, 3, temporal_grow)
+    x = r.standard_normal((3, 5, 2, 3))
+    g = _read_golden("chunk_schedule.txt")
+    drop = int(g["first_chunk_dropped"])
+
+    def run(aligned, mode):
+        d = M.Decoder(params, stages=stages, temporal_grow=temporal_grow, aligned=aligned, mode=mode,
+                      store=O.round_bf16)
+        return [d.step(x[:, :3]), d.step(x[:, 3:])]
+
+    once, al = run(False, O.REPLICATE), run(True, O.REPLICATE)
+    assert al[0].shape[1] == M.output_frames(3, aligned=True) == M.output_frames(3) + drop
+    assert al[1].shape == once[1].shape
+    assert np.array_equal(al[0][:, drop:], once[0]) and np.array_equal(al[1], once[1])
+    for u in range(drop):
+        assert np.array_equal(al[0][:, u], once[0][:, 0])
+    z_once, z_al = run(False, O.ZERO), run(True, O.ZERO)
+    assert not np.array_equal(z_al[0][:, drop:], z_once[0])
+
+
+def test_aligned_schedule_golden():
+    """The reader's 28-frame first chunk is 7 latents grown by 4 with no frame
+    kept single; dropping 3 leaves the 25 frames of the other rule."""
+    g = _read_golden("chunk_schedule.txt")
+    assert M.output_frames(7, aligned=True) == int(g["first_chunk_read"])
+    assert M.output_frames(7, aligned=True) - int(g["first_chunk_dropped"]) == M.output_frames(7)
+    assert M.output_frames(6, aligned=True) == int(g["clip_len"])
