@@ -16,6 +16,7 @@ STATUS_NAMES = {0: "OK", 1: "EINVAL", 2: "ESHAPE", 3: "EDTYPE", 4: "ESTATE", 5: 
 F32, BF16 = 0, 1
 TPAD_REPLICATE, TPAD_ZERO = 0, 1
 EPI_NONE, EPI_RESIDUAL, EPI_ACT, EPI_U8 = 0, 1, 2, 4
+GROW_ONCE, GROW_ALIGNED = 0, 1
 SLOT_NONE, SLOT_X, SLOT_Y, SLOT_AUX = -1, 0, 1, 2
 MAX_SLOTS, MAX_OPS = 64, 256
 OP_CONV, OP_NORM_ACT = 0, 1
@@ -31,7 +32,7 @@ EXPORTS = (
 class ConvDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "cin", "cout", "kt", "kh", "kw", "h_in", "w_in", "up_s", "up_t", "max_chunk_t",
-        "dtype", "tpad", "epilogue")] + [("eps", ctypes.c_float)]
+        "dtype", "tpad", "epilogue")] + [("eps", ctypes.c_float), ("grow", ctypes.c_int)]
 
 
 class State(ctypes.Structure):
@@ -47,7 +48,7 @@ class OpDesc(ctypes.Structure):
 class StackDesc(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int), ("cin", ctypes.c_int), ("h", ctypes.c_int),
                 ("w", ctypes.c_int), ("max_chunk_t", ctypes.c_int), ("eps", ctypes.c_float),
-                ("n_ops", ctypes.c_int), ("ops", ctypes.POINTER(OpDesc))]
+                ("n_ops", ctypes.c_int), ("ops", ctypes.POINTER(OpDesc)), ("grow", ctypes.c_int)]
 
 
 class OpProfile(ctypes.Structure):

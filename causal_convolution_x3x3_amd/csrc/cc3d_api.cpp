@@ -42,10 +42,11 @@ struct FrameCount {
         return mul == o.mul && add_first == o.add_first && add_rest == o.add_rest;
     }
     int64_t eval(int64_t t, bool first) const { return mul * t + (first ? add_first : add_rest); }
-    FrameCount grown() const {  // nearest 2x in time on non-first frames
+    // nearest 2x in time on non-first frames (every frame with the aligned rule)
+    FrameCount grown(bool aligned) const {
         FrameCount g;
         g.mul = 2 * mul;
-        g.add_first = 2 * add_first - 1;
+        g.add_first = 2 * add_first - (aligned ? 0 : 1);
         g.add_rest = 2 * add_rest;
         return g;
     }
@@ -84,6 +85,7 @@ struct cc3d_plan {
     int cin = 0, h = 0, w = 0;
     int max_t = 1;
     int y_elem = 2;  // bytes per element of y (1 with 8-bit output)
+    bool grow_aligned = false;  // CC3D_GROW_ALIGNED: the first chunk grows every frame
     float eps = 1e-6f;
     std::vector<Slot> slots;
     std::vector<OpRt> ops;
@@ -176,6 +178,8 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
     if (d->n_ops < 1 || d->n_ops > CC3D_MAX_OPS)
         return fail(CC3D_EINVAL, "n_ops=%d not in [1, %d]", d->n_ops, CC3D_MAX_OPS);
     if (!d->ops) return fail(CC3D_EINVAL, "ops is NULL");
+    if (d->grow != CC3D_GROW_ONCE && d->grow != CC3D_GROW_ALIGNED)
+        return fail(CC3D_EINVAL, "grow=%d not accepted (0 = CC3D_GROW_ONCE, 1 = CC3D_GROW_ALIGNED)", d->grow);
     const bool bf16 = d->dtype == CC3D_BF16;
     if (bf16 && d->cin % 8 != 0)
         return fail(CC3D_ESHAPE, "bf16 input channels %d: must be a multiple of 8", d->cin);
@@ -187,6 +191,7 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
     p->w = d->w;
     p->max_t = d->max_chunk_t;
     p->eps = d->eps;
+    p->grow_aligned = d->grow == CC3D_GROW_ALIGNED;
     p->slots.assign(CC3D_MAX_SLOTS, Slot());
     Slot& x = p->slots[CC3D_SLOT_X];
     x.defined = true;
@@ -273,7 +278,7 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
             r.tpad = o.tpad;
             r.h_out = r.h_in * o.up_s;
             r.w_out = r.w_in * o.up_s;
-            if (o.up_t == 2) tc_out = src.tc.grown();
+            if (o.up_t == 2) tc_out = src.tc.grown(p->grow_aligned);
             r.cache_off = cache_off;
             r.cache_bytes = (size_t)(o.kt - 1) * r.h_in * r.w_in * r.cin * p->elem;
             cache_off += align_up(r.cache_bytes);
@@ -617,6 +622,7 @@ cc3d_status cc3d_plan_create(const cc3d_conv_desc* d, const void* w, const float
     sd.w = d->w_in;
     sd.max_chunk_t = d->max_chunk_t;
     sd.eps = d->eps;
+    sd.grow = d->grow;
     sd.n_ops = 1;
     sd.ops = &op;
     return create_common(&sd, stream, out);
@@ -724,7 +730,8 @@ cc3d_status cc3d_forward_chunk(const cc3d_plan* p, const void* x, int t_chunk, c
             a.z.up_t = r.up_t;
             a.z.first = first ? 1 : 0;
             a.z.zero_hist = r.tpad == CC3D_TPAD_ZERO ? 1 : 0;
-            const int t_v = (r.up_t == 2) ? (first ? 2 * t_in - 1 : 2 * t_in) : t_in;
+            a.z.t_shift = (first && !p->grow_aligned) ? 1 : 0;
+            const int t_v = (r.up_t == 2) ? 2 * t_in - a.z.t_shift : t_in;
             a.wpk = r.wpk;
             a.bias = r.bias;
             a.res = slot_ptr(r.res);

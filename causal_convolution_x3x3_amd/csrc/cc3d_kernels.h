@@ -8,10 +8,11 @@
 namespace cc3d {
 
 // The window a causal conv reads for one chunk: Z = history (kt-1 frames) ||
-// V, where V is the chunk input grown in time (up_t = 2: first chunk V[0]=X[0],
-// V[2j-1]=V[2j]=X[j]; later chunks V[u]=X[u/2]).  History is cache_in's frames,
-// or on the video's first chunk zeros / copies of V[0].  Frames are at the
-// input's own (pre-spatial-upsample) size.
+// V, where V is the chunk input grown in time (up_t = 2: V[u] = X[(u + t_shift)/2],
+// i.e. first chunk V[0]=X[0], V[2j-1]=V[2j]=X[j] with t_shift = 1; later chunks,
+// and the first one under the aligned rule, V[u]=X[u/2] with t_shift = 0).
+// History is cache_in's frames, or on the video's first chunk zeros / copies of
+// V[0].  Frames are at the input's own (pre-spatial-upsample) size.
 struct ZWindow {
     const void* x;        // [T_in][H][W][C] chunk input
     const void* cache;    // [kt-1][H][W][C] cache_in frames (unused when first)
@@ -20,6 +21,7 @@ struct ZWindow {
     int up_t;
     int first;            // 1 on the video's first chunk
     int zero_hist;        // first-chunk history: 1 = zeros, 0 = copies of V[0]
+    int t_shift;          // up_t = 2: V[u] = X[(u + t_shift) / 2]
 };
 
 struct ConvArgs {

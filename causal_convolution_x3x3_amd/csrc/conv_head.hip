@@ -60,7 +60,7 @@ __device__ __forceinline__ const uint16_t* zframe(const ZWindow& z, int zi)
         return z.zero_hist ? nullptr : (const uint16_t*)z.x;
     }
     const int u = zi - hist;
-    const int src = (z.up_t == 2) ? ((u + z.first) >> 1) : u;
+    const int src = (z.up_t == 2) ? ((u + z.t_shift) >> 1) : u;
     return (const uint16_t*)z.x + (int64_t)src * z.frame_elems;
 }
 

@@ -25,7 +25,7 @@ __device__ __forceinline__ const char* zframe_bytes(const ZWindow& z, int zi, in
         return z.zero_hist ? nullptr : (const char*)z.x;
     }
     const int u = zi - hist;
-    const int src = (z.up_t == 2) ? ((u + z.first) >> 1) : u;
+    const int src = (z.up_t == 2) ? ((u + z.t_shift) >> 1) : u;
     return (const char*)z.x + src * fb;
 }
 

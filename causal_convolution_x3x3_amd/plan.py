@@ -60,10 +60,11 @@ class State:
 
 @dataclass
 class Op:
-    """One op of a stack (see cc3d_op_desc)."""
+    """One op of a stack (see cc3d_op_desc).  A CONV op's kernel size ``k`` is
+    taken from its weights [Cout][Cin][kt][kh][kw]."""
     kind: int = C.OP_CONV
     cout: int = 0
-    k: tuple = (3, 3, 3)
+    k: tuple = (1, 1, 1)
     up_s: int = 1
     up_t: int = 1
     tpad: int = C.TPAD_REPLICATE
@@ -76,6 +77,13 @@ class Op:
     gamma: Optional[torch.Tensor] = None
     out_u8: bool = False  # CONV writing the output slot: y as 8-bit codes
     name: str = field(default="")
+
+    def __post_init__(self):
+        if self.kind == C.OP_CONV and self.w is not None:
+            if self.w.dim() != 5 or self.w.shape[0] != self.cout:
+                raise ValueError("op %s: weights %s are not [cout=%d][cin][kt][kh][kw]"
+                                 % (self.name, tuple(self.w.shape), self.cout))
+            self.k = tuple(int(d) for d in self.w.shape[2:])
 
 
 class Plan:
@@ -147,13 +155,14 @@ class Plan:
 
 def conv_plan(w: torch.Tensor, h_in: int, w_in: int, *, bias=None, gamma=None, up_s=1, up_t=1,
               max_chunk_t=8, tpad=C.TPAD_REPLICATE, residual=False, act=False, out_u8=False, eps=1e-6,
-              stream=None) -> Plan:
-    """Plan for one causal conv; w is [Cout][Cin][kt][kh][kw] on the GPU (bf16 or fp32)."""
+              aligned=False, stream=None) -> Plan:
+    """Plan for one causal conv; w is [Cout][Cin][kt][kh][kw] on the GPU (bf16 or fp32).
+    ``aligned``: the first chunk doubles every frame at up_t = 2 (CC3D_GROW_ALIGNED)."""
     cout, cin, kt, kh, kw = w.shape
     d = C.ConvDesc(cin=cin, cout=cout, kt=kt, kh=kh, kw=kw, h_in=h_in, w_in=w_in, up_s=up_s, up_t=up_t,
                    max_chunk_t=max_chunk_t, dtype=_DT[w.dtype], tpad=tpad,
                    epilogue=(C.EPI_RESIDUAL if residual else 0) | (C.EPI_ACT if act else 0) |
-                   (C.EPI_U8 if out_u8 else 0), eps=eps)
+                   (C.EPI_U8 if out_u8 else 0), eps=eps, grow=C.GROW_ALIGNED if aligned else C.GROW_ONCE)
     h = ctypes.c_void_p()
     with torch.cuda.device(w.device):
         C.check(C.lib().cc3d_plan_create(ctypes.byref(d), _ptr(w), _ptr(bias), _ptr(gamma), _stream(stream),
@@ -161,8 +170,30 @@ def conv_plan(w: torch.Tensor, h_in: int, w_in: int, *, bias=None, gamma=None, u
     return Plan(h, d.dtype, w.device)
 
 
+def _check_weights(ops: List[Op], cin: int):
+    """Each CONV op's weights must hold exactly [cout][channels of its src][k]
+    (the library reads that many elements through the pointer)."""
+    ch = {C.SLOT_X: cin}
+    for i, o in enumerate(ops):
+        c_src = ch.get(o.src)
+        if o.kind == C.OP_CONV:
+            if o.w is None:
+                raise ValueError("op %d (%s): weights are missing" % (i, o.name))
+            want = (o.cout, c_src) + tuple(o.k)
+            if c_src is not None and tuple(o.w.shape) != want:
+                raise ValueError("op %d (%s): weights %s, expected %s" % (i, o.name, tuple(o.w.shape), want))
+            c_out = o.cout
+        else:
+            c_out = c_src
+        for sl in (o.out, o.act_out):
+            if sl != C.SLOT_NONE and c_out is not None:
+                ch[sl] = c_out
+
+
 def stack_plan(ops: List[Op], cin: int, h: int, w: int, *, dtype=torch.bfloat16, max_chunk_t=8,
-               eps=1e-6, device=None, stream=None) -> Plan:
+               eps=1e-6, aligned=False, device=None, stream=None) -> Plan:
+    """Plan for an op list; ``aligned`` as in conv_plan, for every up_t = 2 op."""
+    _check_weights(ops, cin)
     arr = (C.OpDesc * len(ops))()
     for i, o in enumerate(ops):
         kt, kh, kw = o.k
@@ -170,7 +201,7 @@ def stack_plan(ops: List[Op], cin: int, h: int, w: int, *, dtype=torch.bfloat16,
                           tpad=o.tpad, src=o.src, res=o.res, out=o.out, act_out=o.act_out,
                           w=_ptr(o.w), bias=_ptr(o.bias), gamma=_ptr(o.gamma), out_u8=int(o.out_u8))
     d = C.StackDesc(dtype=_DT[dtype], cin=cin, h=h, w=w, max_chunk_t=max_chunk_t, eps=eps, n_ops=len(ops),
-                    ops=arr)
+                    ops=arr, grow=C.GROW_ALIGNED if aligned else C.GROW_ONCE)
     if device is None:
         device = next((o.w.device for o in ops if o.w is not None), torch.device("cuda", 0))
     hnd = ctypes.c_void_p()

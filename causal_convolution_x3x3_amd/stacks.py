@@ -51,18 +51,44 @@ def upstage_ops(c_mid: int, c_out: int, p1: Dict, p2: Dict) -> List[Op]:
 DECODER_STAGES = ((384, 2), (192, 2), (96, 1))
 
 
+TG_ORDERS = (None, "before", "after")
+
+
+def temporal_grow_ops(c: int, p_proj: Dict, p_t: Dict, factor: int, src: int, p_slot: int, out: int,
+                      up_s: int = 1, name: str = "tg") -> List[Op]:
+    """TemporalGrow (SwiftVR page, "TemporalGrow: Compute Before Spatial
+    Upsampling"): a 1x1x1 projection, then a causal 3x1x1 temporal conv that
+    reads the projection grown in time (nearest 2x when ``factor`` is 2).  Both
+    work per position.  ``up_s`` = 2 makes the projection read the nearest-
+    upsampled input, so the block runs on the upsampled positions."""
+    return [
+        Op(cout=c, w=p_proj["w"], bias=p_proj.get("b"), up_s=up_s, src=src, out=p_slot, name=name + ".p"),
+        Op(cout=c, w=p_t["w"], bias=p_t.get("b"), up_t=factor, src=p_slot, out=out, name=name + ".t"),
+    ]
+
+
 def decoder_ops(params: Dict[str, Dict], stages=DECODER_STAGES, c_out: int = 3,
-                unique_slots: bool = False, out_u8: bool = False) -> List[Op]:
+                unique_slots: bool = False, out_u8: bool = False, temporal_grow=None) -> List[Op]:
     """conv_in -> per stage [nearest up (2x space, 2x time on non-first frames
     when the stage's factor is 2) + conv, two residual blocks] -> head (act at low
     resolution, nearest 2x, conv to c_out).
 
+    ``temporal_grow`` = "before" or "after": each stage's time growth moves into
+    a TemporalGrow (params "s<i>.tg.p" [C][C][1][1][1], "s<i>.tg.t"
+    [C][C][3][1][1]) on the stage input, run at the input size ahead of the
+    upsample conv ("before", the reordered decoder) or on the upsampled
+    positions between the upsample and the spatial conv ("after", the original
+    order).  The two give bitwise the same TemporalGrow output.
+
     Slots per stage s (base = 3 + 5 s): raw A, raw B (the residual stream
     alternates between them), act A, act B, inner act.  Slot 3 + 5*len(stages)
-    holds conv_in's output.  ``unique_slots`` gives every tensor a slot of its
-    own instead (same ops and kernels; every layer's input and output stay
-    readable after a chunk, for layer-wise checks).  ``out_u8``: the head stores
-    8-bit RGB codes instead of bf16."""
+    holds conv_in's output; slots 4 + 5*len(stages) + 2 s and the next hold a
+    stage's TemporalGrow projection and output.  ``unique_slots`` gives every
+    tensor a slot of its own instead (same ops and kernels; every layer's input
+    and output stay readable after a chunk, for layer-wise checks).  ``out_u8``:
+    the head stores 8-bit RGB codes instead of bf16."""
+    if temporal_grow not in TG_ORDERS:
+        raise ValueError("temporal_grow must be one of %r" % (TG_ORDERS,))
     nxt = [3]
 
     def slot(fixed):
@@ -76,16 +102,26 @@ def decoder_ops(params: Dict[str, Dict], stages=DECODER_STAGES, c_out: int = 3,
     ops.append(Op(cout=stages[0][0], w=params["conv_in"]["w"], bias=params["conv_in"].get("b"), src=X,
                   out=h0, name="conv_in"))
     prev_raw, last_act = h0, NONE
+    c_in = stages[0][0]
     for si, (c, up_t) in enumerate(stages):
         base = 3 + 5 * si
         raw_fixed = [base, base + 1]
         act_fixed = [base + 2, base + 3]
         rb = [(params["s%d.rb%d.c1" % (si, r)], params["s%d.rb%d.c2" % (si, r)]) for r in range(2)]
         up = params["s%d.up" % si]
+        up_s_conv, up_t_conv = 2, up_t
+        if temporal_grow:
+            tg_base = 4 + 5 * len(stages) + 2 * si
+            tg_p, tg_q = slot(tg_base), slot(tg_base + 1)
+            tg_up = 2 if temporal_grow == "after" else 1
+            ops += temporal_grow_ops(c_in, params["s%d.tg.p" % si], params["s%d.tg.t" % si], up_t, prev_raw,
+                                     tg_p, tg_q, up_s=tg_up, name="s%d.tg" % si)
+            prev_raw = tg_q
+            up_s_conv, up_t_conv = 2 // tg_up, 1
         raw_cur, act_cur = slot(raw_fixed[0]), slot(act_fixed[0])
         # up conv: stores the raw result (residual of block 0) and act for block 0's conv1
-        ops.append(Op(cout=c, w=up["w"], bias=up.get("b"), up_s=2, up_t=up_t, src=prev_raw, out=raw_cur,
-                      act_out=act_cur, gamma=rb[0][0]["g"], name="s%d.up" % si))
+        ops.append(Op(cout=c, w=up["w"], bias=up.get("b"), up_s=up_s_conv, up_t=up_t_conv, src=prev_raw,
+                      out=raw_cur, act_out=act_cur, gamma=rb[0][0]["g"], name="s%d.up" % si))
         cur = 0
         for r in range(2):
             p1, p2 = rb[r]
@@ -102,6 +138,7 @@ def decoder_ops(params: Dict[str, Dict], stages=DECODER_STAGES, c_out: int = 3,
                           act_out=new_act, gamma=nxt_g, name="s%d.rb%d.c2" % (si, r)))
             raw_cur, act_cur, cur = new_raw, new_act, 1 - cur
         prev_raw, last_act = raw_cur, act_cur
+        c_in = c
     head = params["head"]
     ops.append(Op(cout=c_out, w=head["w"], bias=head.get("b"), up_s=2, src=last_act, out=Y, out_u8=out_u8,
                   name="head"))

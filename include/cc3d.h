@@ -27,7 +27,8 @@
  * History is zeros (CC3D_TPAD_ZERO) or copies of the first frame
  * (CC3D_TPAD_REPLICATE).  With up_s = 2 the conv reads the nearest-upsampled
  * input U[h,w] = X[h/2, w/2]; with up_t = 2 it reads the input grown in time on
- * non-first frames: V[0] = X[0], V[2j-1] = V[2j] = X[j].  The epilogue adds the
+ * non-first frames: V[0] = X[0], V[2j-1] = V[2j] = X[j] (or, under the aligned
+ * growth rule below, every frame: V[2j] = V[2j+1] = X[j]).  The epilogue adds the
  * bias and an optional residual, and can store SiLU(RMSNorm(.)) of the result:
  *   RMSNorm(v)_c = gamma_c * v_c / sqrt(mean_c v^2 + eps),  SiLU(z) = z / (1 + e^-z).
  *
@@ -57,7 +58,7 @@
 extern "C" {
 #endif
 
-#define CC3D_VERSION 101 /* 1.0.1: 8-bit RGB output */
+#define CC3D_VERSION 102 /* 1.0.2: aligned first-chunk growth rule */
 
 typedef enum {
     CC3D_OK = 0,
@@ -75,6 +76,17 @@ typedef enum {
     CC3D_TPAD_REPLICATE = 0, /* history = copies of the first frame */
     CC3D_TPAD_ZERO = 1       /* history = zeros (the MemoryBlock rule) */
 } cc3d_tpad;
+
+/* Temporal growth of the video's first chunk at every up_t = 2 conv.
+ * CC3D_GROW_ONCE: its first frame is not doubled (T -> 2T-1; later chunks 2T).
+ * CC3D_GROW_ALIGNED: every frame is doubled (T -> 2T), as for later chunks.  This
+ * is the first chunk of the SwiftVR page ("From Pixels to Latents and Back"):
+ * the reader takes 28 frames (7 latents, 4 frames each) and drops the 3 frames
+ * used for temporal alignment after decoding.  With two up_t = 2 stages and
+ * replicate history, the aligned video is the ONCE video with its first frame
+ * three extra times in front, so dropping y's first 3 frames of the first chunk
+ * gives the ONCE video.  The caller drops them (y holds all 2T.. frames). */
+typedef enum { CC3D_GROW_ONCE = 0, CC3D_GROW_ALIGNED = 1 } cc3d_grow;
 
 /* ----------------------------------------------------------------------------
  * Single conv plan (the causal conv3d plan).
@@ -109,6 +121,7 @@ typedef struct {
     int tpad;             /* cc3d_tpad */
     int epilogue;         /* CC3D_EPI_* flags */
     float eps;            /* RMSNorm epsilon (CC3D_EPI_ACT) */
+    int grow;             /* cc3d_grow (first chunk at up_t = 2) */
 } cc3d_conv_desc;
 
 typedef struct cc3d_plan cc3d_plan;
@@ -173,6 +186,7 @@ typedef struct {
     float eps;          /* RMSNorm epsilon for every act */
     int n_ops;          /* 1 .. CC3D_MAX_OPS */
     const cc3d_op_desc* ops;
+    int grow;           /* cc3d_grow for every up_t = 2 conv of the stack */
 } cc3d_stack_desc;
 
 /* Create a stack plan (same ownership, failure and synchronisation rules as
@@ -195,7 +209,8 @@ size_t cc3d_plan_device_bytes(const cc3d_plan* plan);
 int cc3d_output_elem_bytes(const cc3d_plan* plan);
 
 /* Output shape of one forward_chunk: y is [*t][*h][*w][*c].  first != 0 for the
- * video's first chunk (frames grow by 2t-1 instead of 2t at each up_t = 2). */
+ * video's first chunk (frames grow by 2t-1 instead of 2t at each up_t = 2, unless
+ * the plan uses CC3D_GROW_ALIGNED). */
 cc3d_status cc3d_output_shape(const cc3d_plan* plan, int t_chunk, int first, int* c, int* t,
                               int* h, int* w);
 

@@ -24,7 +24,7 @@ def test_library_exports_every_declared_function():
     assert sorted(declared) == sorted(C.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.cc3d_version() == 101
+    assert L.cc3d_version() == 102
 
 
 def _conv_desc(**kw):
@@ -42,6 +42,7 @@ DUMMY = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
     (dict(up_t=0), C.ESHAPE), (dict(dtype=7), C.EDTYPE), (dict(tpad=5), C.EINVAL), (dict(cin=12), C.ESHAPE),
     (dict(max_chunk_t=0), C.ESHAPE), (dict(h_in=0), C.ESHAPE), (dict(cout=0), C.ESHAPE),
     (dict(epilogue=8), C.EINVAL), (dict(epilogue=C.EPI_ACT | C.EPI_U8), C.EINVAL), (dict(kh=3, kw=1), C.ESHAPE), (dict(eps=-1.0), C.EINVAL),
+    (dict(grow=2), C.EINVAL), (dict(grow=-1), C.EINVAL),
 ])
 def test_plan_create_rejects_bad_descriptor(bad, status):
     L = C.lib()
@@ -117,3 +118,57 @@ def test_transpose_argument_checks():
     assert L.cc3d_to_channels_last(None, DUMMY, 1, 1, 1, 1, 2, None) == C.EINVAL
     assert L.cc3d_to_channels_last(DUMMY, DUMMY, 0, 1, 1, 1, 2, None) == C.ESHAPE
     assert L.cc3d_to_channels_first(DUMMY, DUMMY, 1, 1, 1, 1, 3, None) == C.EDTYPE
+
+
+def _op_descs(ops):
+    """OpDesc array for a Python op list, with placeholder pointers (creation is
+    stopped by a bad final op before anything is dereferenced)."""
+    arr = (C.OpDesc * (len(ops) + 1))()
+    for i, o in enumerate(ops):
+        kt, kh, kw = o.k
+        arr[i] = C.OpDesc(kind=o.kind, cout=o.cout, kt=kt, kh=kh, kw=kw, up_s=o.up_s, up_t=o.up_t, tpad=o.tpad,
+                          src=o.src, res=o.res, out=o.out, act_out=o.act_out, w=DUMMY if o.w is not None else None,
+                          bias=None, gamma=DUMMY if o.gamma is not None else None, out_u8=int(o.out_u8))
+    arr[len(ops)] = _conv_op(kind=9)
+    return arr
+
+
+@pytest.mark.parametrize("temporal_grow", [None, "before", "after"])
+@pytest.mark.parametrize("aligned", [False, True])
+def test_decoder_wiring_passes_library_checks(temporal_grow, aligned):
+    """The decoder op lists (with and without TemporalGrow, either growth rule)
+    pass every shape and wiring check of the library: creation fails only at
+    the bad op appended after them."""
+    import torch
+    from causal_convolution_x3x3_amd import plan as P
+    from causal_convolution_x3x3_amd import stacks as S
+    from oracle import model as OM
+    stages = ((64, 2), (32, 2), (16, 1))
+    params = {}
+    for name, co, ci, kt, kh, kw, g in OM.decoder_layer_shapes(c_latent=16, stages=stages,
+                                                               temporal_grow=temporal_grow):
+        params[name] = {"w": torch.empty((co, ci, kt, kh, kw), dtype=torch.bfloat16),
+                        "g": torch.empty(ci) if g else None}
+    ops = S.decoder_ops(params, stages=stages, temporal_grow=temporal_grow)
+    P._check_weights(ops, 16)
+    tg_ops = [o for o in ops if ".tg." in o.name]
+    assert len(tg_ops) == (6 if temporal_grow else 0)
+    for o in tg_ops:
+        assert o.k == ((1, 1, 1) if o.name.endswith(".p") else (3, 1, 1))
+    arr = _op_descs(ops)
+    d = C.StackDesc(dtype=C.BF16, cin=16, h=3, w=5, max_chunk_t=4, eps=1e-6, n_ops=len(ops) + 1, ops=arr,
+                    grow=C.GROW_ALIGNED if aligned else C.GROW_ONCE)
+    out = ctypes.c_void_p()
+    st = C.lib().cc3d_stack_plan_create(ctypes.byref(d), None, ctypes.byref(out))
+    assert st == C.EINVAL and ("op %d: kind 9" % len(ops)) in C.last_error(), C.last_error()
+
+
+def test_weight_shape_mismatch_is_caught_by_the_binding():
+    import torch
+    from causal_convolution_x3x3_amd import plan as P
+    w = torch.empty((16, 8, 3, 3, 3), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        P._check_weights([P.Op(cout=16, w=w, out=C.SLOT_Y)], 16)
+    with pytest.raises(ValueError):
+        P.Op(cout=8, w=w, out=C.SLOT_Y)
+    assert P.Op(cout=16, w=torch.empty((16, 16, 3, 1, 1)), out=C.SLOT_Y).k == (3, 1, 1)

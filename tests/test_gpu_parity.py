@@ -79,6 +79,11 @@ BF16_CASES = [
     (16, 32, (2, 1, 1), 1, 1, 7, 19, [1, 2, 2], C.TPAD_ZERO, False),
     (16, 64, (1, 3, 3), 2, 1, 7, 9, [2, 1], C.TPAD_REPLICATE, True),
     (24, 16, (3, 1, 1), 1, 2, 5, 17, [2, 1], C.TPAD_ZERO, False),
+    # TemporalGrow shapes: 1x1x1 projection (also on upsampled positions), 3x1x1 growing temporal conv
+    (384, 384, (1, 1, 1), 1, 1, 5, 9, [1, 2], C.TPAD_REPLICATE, True),
+    (192, 192, (1, 1, 1), 2, 1, 5, 7, [2, 1], C.TPAD_REPLICATE, False),
+    (384, 384, (3, 1, 1), 1, 2, 4, 9, [1, 2, 1], C.TPAD_REPLICATE, True),
+    (192, 192, (3, 1, 1), 1, 1, 7, 5, [2, 2], C.TPAD_ZERO, False),
     # output head (taps in the GEMM's N): ragged tiles, runs of frames, cout < 3
     (96, 3, (3, 3, 3), 2, 1, 13, 37, [1, 4, 3], C.TPAD_REPLICATE, True),
     (64, 2, (3, 3, 3), 2, 2, 9, 20, [1, 3, 2], C.TPAD_ZERO, True),
@@ -100,6 +105,22 @@ def test_bf16_conv_vs_oracle(case):
                        max_chunk_t=max(splits), tpad=tpad)
     got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits))
     assert_bf16_close(got, ref, "bf16 conv")
+
+
+@pytest.mark.parametrize("k,up_s", [((3, 1, 1), 1), ((3, 3, 3), 2)])
+def test_bf16_conv_aligned_growth(k, up_s):
+    """CC3D_GROW_ALIGNED: the first chunk doubles every frame at up_t = 2
+    (2T frames out of T), later chunks as usual."""
+    say("bf16 conv aligned growth k=%s up_s=%d" % (k, up_s))
+    cin, cout, h, w, splits = 32, 32, 6, 13, [3, 1, 2]
+    x = synth.bf16(synth.video(cin, sum(splits), h, w, synth.seed(5, 11)))
+    wt = synth.bf16(synth.conv_weight(cout, cin, *k, synth.seed(5, 12)))
+    ref = O.one_shot(to_oracle(x), to_oracle(wt), None, O.REPLICATE, up_s, 2, aligned=True)
+    plan = P.conv_plan(wt.cuda(), h, w, up_s=up_s, up_t=2, max_chunk_t=3, aligned=True)
+    assert plan.output_shape(3, True)[0] == 6
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits))
+    assert got.shape[1] == 2 * sum(splits)
+    assert_bf16_close(got, ref, "aligned growth")
 
 
 @pytest.mark.parametrize("cout", [96, 192])
@@ -257,24 +278,29 @@ def test_upstage_small(cfg, cin, cmid, cout):
     assert_bf16_close(got, ref, "upstage")
 
 
-def _decoder_layerwise(c_latent, stages, t, h, w, splits, cfg=4):
+def _decoder_layerwise(c_latent, stages, t, h, w, splits, cfg=4, temporal_grow=None, aligned=False,
+                       keep_slots=False):
     """Run the decoder twice on the GPU -- production slot wiring and the
     unique-slot wiring -- and check (1) both give bitwise identical outputs,
     (2) every layer of the unique-slot run against the oracle fed that layer's
     own GPU input (the per-layer parity bound), (3) the whole stack against the
-    storage-rounded oracle run end to end (the stack bound)."""
-    full = OM.decoder_layer_shapes(c_latent=c_latent, stages=stages)
+    storage-rounded oracle run end to end (the stack bound).  ``keep_slots``:
+    also return every op's output tensors per chunk (op name -> list)."""
+    full = OM.decoder_layer_shapes(c_latent=c_latent, stages=stages, temporal_grow=temporal_grow)
     gains = {s_[0]: s_[6] for s_ in full}
     cpu, dev = _params([s_[:6] for s_ in full], cfg, lambda n: gains[n])
     x = synth.bf16(synth.video(c_latent, t, h, w, synth.seed(cfg, 1)))
     x_cl = to_device_cl(x)
-    ops_u = S.decoder_ops(dev, stages=stages, unique_slots=True)
-    plan_u = P.stack_plan(ops_u, c_latent, h, w, max_chunk_t=max(splits))
-    plan_p = P.stack_plan(S.decoder_ops(dev, stages=stages), c_latent, h, w, max_chunk_t=max(splits))
+    ops_u = S.decoder_ops(dev, stages=stages, unique_slots=True, temporal_grow=temporal_grow)
+    plan_u = P.stack_plan(ops_u, c_latent, h, w, max_chunk_t=max(splits), aligned=aligned)
+    plan_p = P.stack_plan(S.decoder_ops(dev, stages=stages, temporal_grow=temporal_grow), c_latent, h, w,
+                          max_chunk_t=max(splits), aligned=aligned)
     su, sp = P.Stream(plan_u), P.Stream(plan_p)
-    layer = {i: O.CausalConvStream(cpu[o.name]["w"], cpu[o.name]["b"], O.REPLICATE, o.up_s, o.up_t)
+    layer = {i: O.CausalConvStream(cpu[o.name]["w"], cpu[o.name]["b"], O.REPLICATE, o.up_s, o.up_t,
+                                   aligned=aligned)
              for i, o in enumerate(ops_u)}
     outs, t0, worst = [], 0, {}
+    kept = {}
     for n in splits:
         first = su.frames_seen == 0
         xc = x_cl[t0:t0 + n].contiguous()
@@ -288,6 +314,10 @@ def _decoder_layerwise(c_latent, stages, t, h, w, splits, cfg=4):
                 if sl > C.SLOT_AUX:
                     ten[sl] = plan_u.read_slot(sl, n, first)
         torch.cuda.synchronize()
+        if keep_slots:
+            for o in ops_u:
+                if o.out != C.SLOT_NONE:
+                    kept.setdefault(o.name, []).append(ten[o.out])
         for i, o in enumerate(ops_u):
             v = layer[i].step(from_device_cl(ten[o.src]))
             if o.res != C.SLOT_NONE:
@@ -300,12 +330,14 @@ def _decoder_layerwise(c_latent, stages, t, h, w, splits, cfg=4):
                 assert_bf16_close(from_device_cl(ten[o.act_out]), ref_act, "%s act (chunk at %d)" % (o.name, t0))
         t0 += n
     got = from_device_cl(torch.cat(outs, dim=0))
-    dec = OM.Decoder(cpu, stages=stages, store=O.round_bf16)
+    dec = OM.Decoder(cpu, stages=stages, store=O.round_bf16, temporal_grow=temporal_grow, aligned=aligned)
     ref, t0 = [], 0
     for n in splits:
         ref.append(dec.step(to_oracle(x)[:, t0:t0 + n]))
         t0 += n
     ref = np.concatenate(ref, axis=1)
+    if keep_slots:
+        return got, ref, worst, kept
     return got, ref, worst
 
 
@@ -330,6 +362,58 @@ def test_decoder_full_channels_tiny_frame():
     got, ref, _ = _decoder_layerwise(48, OM.DECODER_STAGES, t=5, h=2, w=3, splits=[3, 2])
     assert got.shape == (3, OM.output_frames(5), 32, 48)
     assert_stack_close(got, ref, "decoder full channels")
+
+
+SMALL_STAGES = ((64, 2), (32, 2), (16, 1))
+
+
+@pytest.mark.parametrize("order", ["before", "after"])
+def test_decoder_temporal_grow_layerwise(order):
+    """TemporalGrow (1x1x1 projection, causal 3x1x1 temporal conv on the grown
+    sequence) in either order: every layer against the oracle, the stack end to
+    end."""
+    say("decoder temporal grow %s" % order)
+    got, ref, _ = _decoder_layerwise(16, SMALL_STAGES, t=6, h=3, w=5, splits=[2, 3, 1], temporal_grow=order)
+    assert got.shape == (3, OM.output_frames(6), 48, 80)
+    assert_stack_close(got, ref, "decoder tg %s" % order)
+
+
+def test_temporal_grow_orders_bitwise():
+    """The reorder: TemporalGrow at the stage input size, then nearest 2x, gives
+    bit for bit the TemporalGrow output computed on the upsampled positions (the
+    SwiftVR page reports bitwise identical results).  The decoders that follow
+    read the same values; their spatial convs fold the upsample or not, so the
+    RGB is held to the stack bound."""
+    say("temporal grow: before vs after, bitwise")
+    runs = {}
+    for order in ("before", "after"):
+        runs[order] = _decoder_layerwise(16, SMALL_STAGES, t=5, h=3, w=5, splits=[3, 2], temporal_grow=order,
+                                         keep_slots=True)
+    kb, ka = runs["before"][3], runs["after"][3]
+    for si in range(len(SMALL_STAGES)):
+        name = "s%d.tg.t" % si
+        for lo, hi in zip(kb[name], ka[name]):
+            up = lo.repeat_interleave(2, dim=1).repeat_interleave(2, dim=2)
+            assert up.shape == hi.shape
+            assert torch.equal(up, hi), "%s: TemporalGrow output differs between the orders" % name
+    mx, mn = assert_stack_close(runs["before"][0], runs["after"][0], "rgb before vs after")
+    say("  rgb before vs after: max-rel %.3g mean-rel %.3g, bitwise %s" % (
+        mx, mn, np.array_equal(runs["before"][0], runs["after"][0])))
+
+
+@pytest.mark.parametrize("temporal_grow", [None, "before"])
+def test_decoder_aligned_first_chunk(temporal_grow):
+    """Aligned growth (the 28-frame first chunk): layer-wise against the
+    oracle's aligned rule, and after dropping the first chunk's first 3 frames
+    the same video as the default rule, to the stack bound."""
+    say("decoder aligned first chunk, temporal_grow=%s" % temporal_grow)
+    splits = [3, 2]
+    got, ref, _ = _decoder_layerwise(16, SMALL_STAGES, t=5, h=3, w=5, splits=splits, temporal_grow=temporal_grow,
+                                     aligned=True)
+    assert got.shape[1] == OM.output_frames(5, aligned=True) == OM.output_frames(5) + 3
+    assert_stack_close(got, ref, "aligned decoder")
+    once, _, _ = _decoder_layerwise(16, SMALL_STAGES, t=5, h=3, w=5, splits=splits, temporal_grow=temporal_grow)
+    assert_stack_close(got[:, 3:], once, "aligned minus 3 frames vs default rule")
 
 
 def test_plan_create_failure_releases_everything(monkeypatch):
