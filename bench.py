@@ -1,13 +1,17 @@
 """Benchmark of the chunked causal Conv3d decode on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4|c3] [--no-cpu-baseline]
-                    [--no-delivery]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4|c4tg|c3]
+                    [--tg-order before|after] [--no-cpu-baseline] [--no-delivery]
 
 Workloads (synthetic, seeded; the pages' test videos and trained weights are not
 available):
   c4 (default): the decoder stack, latent 48 x 91 frames x 90x160 -> RGB
       3 x 361 x 1440x2560, decoded in clips of 7 then 6 latents (25, then 24
       output frames).  One step = one clip through every layer.
+  c4tg: the same decoder with each stage's time growth done by a TemporalGrow
+      (1x1x1 projection + causal 3x1x1 temporal conv) on the stage input, run
+      before the upsample conv (--tg-order before, the reordered decoder) or on
+      the upsampled positions (--tg-order after, the original order).
   c3: the 1440p output stage, 128 ch x 720x1280 -> nearest 2x -> conv 128->96 ->
       RMSNorm+SiLU -> conv 96->3, 361 frames streamed as 1 + 90 chunks of 4.
       One step = one chunk.
@@ -54,11 +58,15 @@ def make_decoder(dev, synth, S, OMshapes):
     return params
 
 
-def decoder_layer_list(c_latent=48, stages=((384, 2), (192, 2), (96, 1)), c_out=3):
-    """(name, cout, cin, kt, kh, kw, has_gain) -- the decoder's conv list."""
+def decoder_layer_list(c_latent=48, stages=((384, 2), (192, 2), (96, 1)), c_out=3, temporal_grow=None):
+    """(name, cout, cin, kt, kh, kw, has_gain) -- the decoder's conv list
+    (with a TemporalGrow's projection and temporal conv ahead of each stage)."""
     out = [("conv_in", stages[0][0], c_latent, 3, 3, 3, False)]
     cin = stages[0][0]
     for si, (c, _) in enumerate(stages):
+        if temporal_grow:
+            out.append(("s%d.tg.p" % si, cin, cin, 1, 1, 1, False))
+            out.append(("s%d.tg.t" % si, cin, cin, 3, 1, 1, False))
         out.append(("s%d.up" % si, c, cin, 3, 3, 3, False))
         for r in range(2):
             out.append(("s%d.rb%d.c1" % (si, r), c, c, 3, 3, 3, True))
@@ -72,13 +80,17 @@ def grown(n, first):
     return 2 * n - 1 if first else 2 * n
 
 
-def c4_step_flops(t_lat, first, h=90, w=160):
+def c4_step_flops(t_lat, first, h=90, w=160, temporal_grow=None):
     """Algorithmic conv FLOP of one clip of t_lat latents."""
     f = 0.0
     t = t_lat
     f += conv_flops_per_voxel(48, 384) * t * h * w
     cin = 384
     for si, (c, up_t) in enumerate(((384, 2), (192, 2), (96, 1))):
+        if temporal_grow:
+            pos = h * w * (4 if temporal_grow == "after" else 1)
+            t_g = grown(t, first) if up_t == 2 else t
+            f += conv_flops_per_voxel(cin, cin, 1) * t * pos + conv_flops_per_voxel(cin, cin, 3) * t_g * pos
         h, w = 2 * h, 2 * w
         if up_t == 2:
             t = grown(t, first)
@@ -89,11 +101,11 @@ def c4_step_flops(t_lat, first, h=90, w=160):
     return f, t
 
 
-def setup_c4(dev, torch, synth, P, S, out_u8=False):
+def setup_c4(dev, torch, synth, P, S, out_u8=False, temporal_grow=None):
     lat_c, lat_t, lh, lw = 48, 91, 90, 160
-    layers = decoder_layer_list()
+    layers = decoder_layer_list(temporal_grow=temporal_grow)
     params = make_decoder(dev, synth, S, layers)
-    ops = S.decoder_ops(params, out_u8=out_u8)
+    ops = S.decoder_ops(params, out_u8=out_u8, temporal_grow=temporal_grow)
     plan = P.stack_plan(ops, lat_c, lh, lw, max_chunk_t=7, device=dev)
     del params
     log("c4 plan: %d ops, state %.2f GB, plan device memory %.2f GB" % (
@@ -109,12 +121,22 @@ def setup_c4(dev, torch, synth, P, S, out_u8=False):
     ring = [torch.empty((25, 1440, 2560, 3), dtype=torch.bfloat16, device=dev) for _ in range(2)]
     work = []
     for (xc, first), n in zip(clips, sched):
-        fl, tout = c4_step_flops(n, first)
+        fl, tout = c4_step_flops(n, first, temporal_grow=temporal_grow)
         work.append((xc, first, fl, tout))
-    desc = {"workload": "c4_decoder_bf16: latent 48x91x90x160 -> conv_in 48->384 -> 3 stages "
-                        "(384/192/96 ch; nearest 2x space, 2x time on non-first frames for stages 1-2; "
-                        "2 residual blocks each) -> head 96->3 at 1440x2560; clips of 7+14x6 latents",
-            "output": "3x361x1440x2560 bf16", "step": "one clip (24 output frames; 25 for the first)"}
+    if temporal_grow:
+        name = ("c4tg_decoder_bf16: latent 48x91x90x160 -> conv_in 48->384 -> 3 stages (384/192/96 ch; "
+                "TemporalGrow [1x1x1 projection + causal 3x1x1 temporal conv, 2x time on non-first frames "
+                "for stages 1-2] %s the nearest 2x spatial upsample, then conv; 2 residual blocks each) -> "
+                "head 96->3 at 1440x2560; clips of 7+14x6 latents" % (
+                    "before" if temporal_grow == "before" else "after"))
+    else:
+        name = ("c4_decoder_bf16: latent 48x91x90x160 -> conv_in 48->384 -> 3 stages "
+                "(384/192/96 ch; nearest 2x space, 2x time on non-first frames for stages 1-2; "
+                "2 residual blocks each) -> head 96->3 at 1440x2560; clips of 7+14x6 latents")
+    desc = {"workload": name, "output": "3x361x1440x2560 bf16",
+            "step": "one clip (24 output frames; 25 for the first)"}
+    if temporal_grow:
+        desc["plan_device_gb"] = round(plan.device_bytes / 1e9, 3)
     return plan, work, ring, desc
 
 
@@ -218,7 +240,7 @@ def delivery_rate(torch, plan, work, steps, warmup, dev):
     return frames / dt, nbytes[0] / (copy_ms * 1e-3) / 1e9, nbytes[0] / steps
 
 
-def cpu_baseline(workload):
+def cpu_baseline(workload, temporal_grow=None):
     """The fp64 oracle, as it stands, on a bounded crop of the same workload."""
     import numpy as np
 
@@ -228,20 +250,20 @@ def cpu_baseline(workload):
 
     O.build()
     threads = O.default_threads()
-    if workload == "c4":
+    if workload in ("c4", "c4tg"):
         lt, lh, lw = 3, 6, 10
-        shapes = OM.decoder_layer_shapes()
+        shapes = OM.decoder_layer_shapes(temporal_grow=temporal_grow)
         params = {}
         for i, (name, co, ci, kt, kh, kw, has_g) in enumerate(shapes):
             params[name] = {"w": synth.conv_weight(co, ci, kt, kh, kw, synth.seed(4, 10 + 3 * i)).double().numpy(),
                             "g": synth.gain(ci, synth.seed(4, 11 + 3 * i)).double().numpy() if has_g else None,
                             "b": None}
         x = synth.video(48, lt, lh, lw, synth.seed(4, 1)).double().numpy()
-        dec = OM.Decoder(params, nthreads=threads)
+        dec = OM.Decoder(params, nthreads=threads, temporal_grow=temporal_grow)
         t0 = time.perf_counter()
         y = dec.step(x)
         dt = time.perf_counter() - t0
-        fl, tout = c4_step_flops(lt, True, lh, lw)
+        fl, tout = c4_step_flops(lt, True, lh, lw, temporal_grow=temporal_grow)
         sample = ("whole decoder, one first clip of %d latents on a %dx%d latent crop "
                   "(-> %d frames of %dx%d), fp64, %d threads" % (lt, lh, lw, y.shape[1], y.shape[2], y.shape[3],
                                                                 threads))
@@ -269,7 +291,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=15)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", choices=["c4", "c3"], default="c4")
+    ap.add_argument("--workload", choices=["c4", "c4tg", "c3"], default="c4")
+    ap.add_argument("--tg-order", choices=["before", "after"], default="before",
+                    help="c4tg: TemporalGrow before (reordered) or after (original) the spatial upsample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-delivery", action="store_true",
                     help="skip the host-delivery measurement (c4: output copied to pinned host memory)")
@@ -289,8 +313,11 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     C.lib()
-    setup = setup_c4 if args.workload == "c4" else setup_c3
-    plan, work, ring, desc = setup(dev, torch, synth, P, S)
+    tg = args.tg_order if args.workload == "c4tg" else None
+    if args.workload == "c3":
+        plan, work, ring, desc = setup_c3(dev, torch, synth, P, S)
+    else:
+        plan, work, ring, desc = setup_c4(dev, torch, synth, P, S, temporal_grow=tg)
     stream = torch.cuda.current_stream()
     states = [plan.new_state(), plan.new_state()]
     cur = [0]
@@ -384,7 +411,7 @@ def main():
         out["delivery"] = deliv
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
-        out["cpu_baseline"] = cpu_baseline(args.workload)
+        out["cpu_baseline"] = cpu_baseline(args.workload, tg)
     print(json.dumps(out), flush=True)
 
 

@@ -285,7 +285,9 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
             if (bf16) {
                 cc3d::bf16_conv_tiling(o.cout, &r.ntile, &r.nblocks);
                 r.kchunks = (r.cin + 31) / 32;
-                r.family = cc3d::bf16_conv_family(o.cout, r.cin, o.kt, o.kh, o.kw, o.up_s);
+                const int plain = o.act_out == CC3D_SLOT_NONE && !o.out_u8;
+                r.family = cc3d::bf16_conv_family(o.cout, r.cin, o.kt, o.kh, o.kw, o.up_s, plain);
+                if (r.family == 4) cc3d::pw_conv_tiling(o.cout, &r.ntile, &r.nblocks);
             }
         } else {
             r.cout = r.cin;
@@ -565,6 +567,8 @@ std::string conv_kernel_name(const cc3d_plan* p, const OpRt& r)
     char buf[64];
     if (p->dtype == CC3D_BF16 && r.family == 3)
         snprintf(buf, sizeof buf, "conv_bf16_head_up%d_k%d_c%d", r.up_s, r.kh, r.cout);
+    else if (p->dtype == CC3D_BF16 && r.family == 4)
+        snprintf(buf, sizeof buf, "conv_bf16_pw_up%d_kt%d_n%d", r.up_s, r.kt, r.ntile);
     else if (p->dtype == CC3D_BF16)
         snprintf(buf, sizeof buf, "conv_bf16%s_up%d_k%d_n%d", r.family == 2 ? "_v2" : "", r.up_s, r.kh,
                  r.ntile);

@@ -1,0 +1,365 @@
+// bf16 causal conv with a 1x1 spatial kernel (k_t x 1 x 1) on gfx950 MFMA:
+// the pointwise ("pw") family.
+//
+// A conv whose spatial kernel is 1x1 mixes channels at each position and, for
+// k_t > 1, across the frames of its causal window -- TemporalGrow's projection
+// (1x1x1) and temporal conv (3x1x1) (LightX2V blog "SwiftVR Inference
+// Optimization ...", section "TemporalGrow: Compute Before Spatial
+// Upsampling").  Per output frame t this is a plain GEMM
+//   Y[t][pos][n] = sum_{a, c} W[n][c][a] * Z[t + a][src(pos)][c]
+// with M = the frame's positions, N = output channels, K = k_t x Cin, where Z is
+// the causal window (history || input grown in time) and src() maps an output
+// position to its source position (identity, or the nearest 2x upsample).
+//
+// * A work item is (a run of TP consecutive output positions of frame t, a block
+//   of NTILE output channels).  8 waves, two per SIMD: four along M (16*MW
+//   positions each) and two along N.  The weights are the MFMA's row operand, so
+//   a lane's accumulators are four consecutive channels of one position and the
+//   epilogue moves 8-byte vectors.
+// * K is walked in steps of (temporal tap, 64 channels).  Both operands go from
+//   global memory straight into LDS (buffer loads with the LDS flag), one step
+//   ahead into the idle half of a double buffer; one barrier per step.  Every
+//   lane's 16-byte slot of the position tile has a fixed source offset, so the
+//   nearest upsample (and any ragged tail past the frame, read as zeros) costs
+//   nothing in the loop.
+// * Temporal taps are taken in an order rotated by the output frame, and work
+//   items run frame-major within a tile, so the workgroups of frames t, t+1, t+2
+//   read the same input frame at the same time and share it in L2.  Items are
+//   dealt to the 8 XCDs in contiguous ranges.
+// * Epilogue: + bias, + residual, round to bf16 (nearest even) and store.  The
+//   op's act and 8-bit output are not done here; the host picks this family only
+//   for convs without them.
+#include "cc3d_kernels.h"
+
+namespace cc3d {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Two floats to a bf16 pair (low half = lo), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 16-byte chunk swizzle inside a 128-byte LDS row (one position or one weight
+// row, 64 channels): the 16 rows one ds_read_b128 quarter touches spread over
+// all eight chunk positions.
+__device__ __forceinline__ int swz8(int row) { return row & 7; }
+
+__device__ __forceinline__ const uint16_t* zframe(const ZWindow& z, int zi)
+{
+    const int hist = z.kt - 1;
+    if (zi < hist) {
+        if (!z.first) return (const uint16_t*)z.cache + (int64_t)zi * z.frame_elems;
+        return z.zero_hist ? nullptr : (const uint16_t*)z.x;
+    }
+    const int u = zi - hist;
+    const int src = (z.up_t == 2) ? ((u + z.t_shift) >> 1) : u;
+    return (const uint16_t*)z.x + (int64_t)src * z.frame_elems;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t OOB = 0x80000000u;  // an offset past every buffer used here
+
+// 16 (or 4) bytes per lane from buffer offset `off` into LDS slot lds_base + lane.
+__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4* lds_base)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void load_to_lds4(__amdgpu_buffer_rsrc_t r, uint32_t off, char* lds_base)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4, off, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(0) (gfx9 encoding; expcnt and lgkmcnt left at their maxima)
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+
+constexpr int KC = 64;  // channels per K step
+
+template <int UP, int NF, int MW>
+__global__ __launch_bounds__(512, 1) void conv_pw_kernel(ConvArgs a)
+{
+    constexpr int WN = 2, NT = 512;
+    constexpr int NFW = NF / WN;          // N fragments per wave
+    constexpr int NTILE = 16 * NF;
+    constexpr int TP = 4 * 16 * MW;       // positions per work item
+    constexpr int A_CH = TP * (KC / 8);   // 16-byte slots of one position-tile buffer
+    constexpr int A_IT = A_CH / NT;
+    constexpr int B_CH = NTILE * (KC / 8);  // 16-byte slots of one step's weights
+    constexpr int B_BYTES = B_CH * 16;
+    constexpr int RB16 = B_CH / NT;                   // weight rounds of 16 bytes per lane ...
+    constexpr int RB4 = (B_CH % NT) * 16 / (NT * 4);  // ... then of 4 bytes for the rest
+    static_assert(A_IT * NT == A_CH, "position tile in whole load rounds");
+    static_assert(RB4 * NT * 4 == (B_CH % NT) * 16, "weight block in whole load rounds");
+    static_assert(NF % WN == 0, "N fragments split evenly over the N waves");
+
+    __shared__ uint4 lds_a0[A_CH];
+    __shared__ uint4 lds_a1[A_CH];
+    __shared__ uint4 lds_b0[B_CH];
+    __shared__ uint4 lds_b1[B_CH];
+
+    const int hw_out = a.h_out * a.w_out;
+    const int tiles = (hw_out + TP - 1) / TP;
+    const int total = tiles * a.t_out * a.nblocks;
+    const int per_xcd = (total + 7) >> 3;
+    const int w = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if (w >= total) return;
+    // (tile, frame, channel block) of item w; the channel block varies fastest,
+    // then the frame
+    const int nb = w % a.nblocks;
+    const int t = (w / a.nblocks) % a.t_out;
+    const int tile = w / a.nblocks / a.t_out;
+    const int p0 = tile * TP;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 3, wn = wave >> 2;
+    const int g = lane >> 4, k16 = lane & 15;
+
+    const int kc_n = (a.cin + KC - 1) / KC;
+    const int nsteps = a.kt * kc_n;
+    const uint32_t frame_bytes = (uint32_t)(a.z.frame_elems * 2);
+    const __amdgpu_buffer_rsrc_t wr =
+        make_rsrc((const uint4*)a.wpk + (size_t)nb * nsteps * B_CH, (uint32_t)(nsteps * B_BYTES));
+
+    // Step-invariant load plan: source byte offset inside a frame of the chunk
+    // slot (tid + NT*it) holds (OOB past the frame's last position), and the
+    // first channel of that chunk.
+    uint32_t a_off[A_IT];
+    int a_ch[A_IT];
+#pragma unroll
+    for (int it = 0; it < A_IT; ++it) {
+        const int slot = tid + NT * it;
+        const int pos = slot >> 3;
+        const int chunk = (slot & 7) ^ swz8(pos);
+        const int op = p0 + pos;
+        a_ch[it] = chunk * 8;
+        a_off[it] = OOB;
+        if (op < hw_out) {
+            int src = op;
+            if (UP == 2) {
+                const int y = op / a.w_out, x = op - y * a.w_out;
+                src = (y >> 1) * a.w_in + (x >> 1);
+            }
+            a_off[it] = (uint32_t)(((int64_t)src * a.cin + chunk * 8) * 2);
+        }
+    }
+
+    // loop step (ta, kc) reads temporal tap (ta + rot) mod kt, rot = -t mod kt
+    const int rot = a.rot_taps ? (a.kt - t % a.kt) % a.kt : 0;
+    auto phys_step = [&](int step) -> int {
+        const int ta = step / kc_n, kc = step - ta * kc_n;
+        const int tr = ta + rot < a.kt ? ta + rot : ta + rot - a.kt;
+        return tr * kc_n + kc;
+    };
+    auto issue = [&](int lstep, uint4* abuf, uint4* bbuf) {
+        const int step = phys_step(lstep);
+        const int ta = step / kc_n, kc = step - ta * kc_n;
+        const uint16_t* fp = zframe(a.z, t + ta);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(fp, fp ? frame_bytes : 0u);
+        const int ch0 = kc * KC;
+#pragma unroll
+        for (int it = 0; it < A_IT; ++it) {
+            const uint32_t off = (ch0 + a_ch[it] < a.cin) ? a_off[it] + (uint32_t)(ch0 * 2) : OOB;
+            load_to_lds(r, off, abuf + NT * it + wave * 64);
+        }
+#pragma unroll
+        for (int it = 0; it < RB16; ++it)
+            load_to_lds(wr, (uint32_t)((step * B_CH + it * NT + tid) * 16), bbuf + it * NT + wave * 64);
+#pragma unroll
+        for (int it = 0; it < RB4; ++it)
+            load_to_lds4(wr, (uint32_t)(step * B_BYTES + RB16 * NT * 16 + (it * NT + tid) * 4),
+                         (char*)bbuf + RB16 * NT * 16 + (it * NT + wave * 64) * 4);
+    };
+
+    // byte offsets of this lane's fragments for K half h = 0 (h = 1: chunk ^ 4)
+    int a_frag[MW], b_frag[NFW];
+#pragma unroll
+    for (int m = 0; m < MW; ++m) {
+        const int pos = 64 * wm + 16 * m + k16;
+        a_frag[m] = pos * 128;
+    }
+#pragma unroll
+    for (int f = 0; f < NFW; ++f) {
+        const int nl = 16 * (wn * NFW + f) + k16;
+        b_frag[f] = nl * 128;
+    }
+    // the chunk of K group g in half h of row `row`: (4h + g) ^ swz8(row); rows
+    // of one lane differ by multiples of 16, so swz8 is that of k16
+    const int c0 = (g ^ swz8(k16)) << 4, c1 = ((4 + g) ^ swz8(k16)) << 4;
+
+    f32x4 acc[MW][NFW];
+#pragma unroll
+    for (int m = 0; m < MW; ++m)
+#pragma unroll
+        for (int f = 0; f < NFW; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto mma = [&](const uint4* abuf, const uint4* bbuf) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int co = h ? c1 : c0;
+            bf16x8 bq[NFW];
+#pragma unroll
+            for (int f = 0; f < NFW; ++f) bq[f] = as_bf16x8(*(const uint4*)((const char*)bbuf + b_frag[f] + co));
+#pragma unroll
+            for (int m = 0; m < MW; ++m) {
+                const bf16x8 av = as_bf16x8(*(const uint4*)((const char*)abuf + a_frag[m] + co));
+#pragma unroll
+                for (int f = 0; f < NFW; ++f)
+                    acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bq[f], av, acc[m][f], 0, 0, 0);
+            }
+        }
+    };
+
+    issue(0, lds_a0, lds_b0);
+    wait_vmcnt0();
+    __builtin_amdgcn_s_barrier();
+    // Step s reads buffer s % 2 and fills the other one (last read in step s - 1,
+    // retired by its barrier) with step s + 1 -- the last step reloads itself (an
+    // L2 hit), so every load is unconditional and the compiler's own waits stay
+    // exact.  Steps go in pairs so that every buffer is a fixed LDS variable.
+    auto k_step = [&](int step, const uint4* ar, const uint4* br, uint4* aw, uint4* bw) {
+        issue(step + 1 < nsteps ? step + 1 : nsteps - 1, aw, bw);
+        mma(ar, br);
+        wait_vmcnt0();
+        // bare barrier: the loads it publishes were waited for just above and
+        // the loop makes no LDS stores
+        __builtin_amdgcn_s_barrier();
+    };
+    for (int step = 0; step < nsteps; step += 2) {
+        k_step(step, lds_a0, lds_b0, lds_a1, lds_b1);
+        if (step + 1 < nsteps) k_step(step + 1, lds_a1, lds_b1, lds_a0, lds_b0);
+    }
+
+    // ---------------------------------------------------------------- epilogue
+    // acc[m][f] holds D[channel][position]: lane (g, k16) has channels
+    // n0 + 16 f .. + 3 of position p0 + 64 wm + 16 m + k16.
+    const int n0 = nb * NTILE + wn * NFW * 16 + 4 * g;
+    uint16_t* out = (uint16_t*)a.out;
+    const uint16_t* res = (const uint16_t*)a.res;
+#pragma unroll
+    for (int m = 0; m < MW; ++m) {
+        const int pos = p0 + 64 * wm + 16 * m + k16;
+        if (pos >= hw_out) continue;
+        const int64_t pbase = ((int64_t)t * hw_out + pos) * a.cout;
+        // this row's residual before its stores (a load of `res` may not move
+        // past a store to `out`, which could alias it as far as the compiler knows)
+        uint2 rv[NFW];
+#pragma unroll
+        for (int f = 0; f < NFW; ++f) {
+            const int n = n0 + 16 * f;
+            rv[f] = make_uint2(0u, 0u);
+            if (res && n < a.cout) rv[f] = *(const uint2*)(res + pbase + n);
+        }
+#pragma unroll
+        for (int f = 0; f < NFW; ++f) {
+            const int n = n0 + 16 * f;
+            if (n >= a.cout) continue;
+            float v[4] = {acc[m][f][0], acc[m][f][1], acc[m][f][2], acc[m][f][3]};
+            if (a.bias) {
+                const float4 bv = *(const float4*)(a.bias + n);
+                v[0] += bv.x; v[1] += bv.y; v[2] += bv.z; v[3] += bv.w;
+            }
+            if (res) {
+                v[0] += bf2f((uint16_t)(rv[f].x & 0xffffu));
+                v[1] += bf2f((uint16_t)(rv[f].x >> 16));
+                v[2] += bf2f((uint16_t)(rv[f].y & 0xffffu));
+                v[3] += bf2f((uint16_t)(rv[f].y >> 16));
+            }
+            *(uint2*)(out + pbase + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+    }
+}
+
+template <int UP, int NF>
+hipError_t launch_pw(const ConvArgs& a, hipStream_t s)
+{
+    constexpr int MW = 4;
+    constexpr int TP = 4 * 16 * MW;
+    const int64_t hw = (int64_t)a.h_out * a.w_out;
+    const int64_t total = (hw + TP - 1) / TP * a.t_out * a.nblocks;
+    if (total <= 0 || total > (int64_t)0x7fffffff - 8) return hipErrorInvalidValue;
+    const int64_t grid = ((total + 7) / 8) * 8;
+    hipLaunchKernelGGL((conv_pw_kernel<UP, NF, MW>), dim3((unsigned)grid), dim3(512), 0, s, a);
+    return hipGetLastError();
+}
+
+// Packed layout per (channel block, temporal tap, 64-channel chunk): NTILE rows
+// of 64 channels, the 16-byte chunks of row nl swizzled by swz8(nl) as in LDS;
+// zero past cout and cin.
+__global__ void pack_pw_kernel(const uint16_t* w, uint16_t* wpk, int cout, int cin, int kt, int ntile,
+                               int nblocks, int kc_n)
+{
+    const int64_t total = (int64_t)nblocks * kt * kc_n * ntile * KC;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int e = (int)(idx % KC);
+        int64_t row = idx / KC;
+        const int nl = (int)(row % ntile);
+        row /= ntile;
+        const int kc = (int)(row % kc_n);
+        row /= kc_n;
+        const int ta = (int)(row % kt);
+        const int nb = (int)(row / kt);
+        const int chunk = (e >> 3) ^ swz8(nl);
+        const int c = kc * KC + chunk * 8 + (e & 7);
+        const int n = nb * ntile + nl;
+        uint16_t v = 0;
+        if (n < cout && c < cin) v = w[((int64_t)n * cin + c) * kt + ta];
+        wpk[idx] = v;
+    }
+}
+
+}  // namespace
+
+bool pw_conv_applies(int cout, int kh, int kw, int up_s)
+{
+    return kh == 1 && kw == 1 && (up_s == 1 || up_s == 2) && cout % 96 == 0;
+}
+
+void pw_conv_tiling(int cout, int* ntile, int* nblocks)
+{
+    const int nt = cout % 192 == 0 ? 192 : 96;
+    *ntile = nt;
+    *nblocks = cout / nt;
+}
+
+size_t pw_packed_elems(int cout, int cin, int kt)
+{
+    int nt, nb;
+    pw_conv_tiling(cout, &nt, &nb);
+    return (size_t)nb * kt * ((cin + KC - 1) / KC) * nt * KC;
+}
+
+hipError_t launch_pack_pw(const void* w, void* wpk, int cout, int cin, int kt, hipStream_t s)
+{
+    int nt, nb;
+    pw_conv_tiling(cout, &nt, &nb);
+    const size_t total = pw_packed_elems(cout, cin, kt);
+    int blocks = (int)((total + 255) / 256);
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(pack_pw_kernel, dim3(blocks), dim3(256), 0, s, (const uint16_t*)w, (uint16_t*)wpk, cout,
+                       cin, kt, nt, nb, (cin + KC - 1) / KC);
+    return hipGetLastError();
+}
+
+hipError_t launch_conv_pw(const ConvArgs& a, hipStream_t s)
+{
+    if (!pw_conv_applies(a.cout, a.kh, a.kw, a.up_s) || a.act_out || a.out_u8 || !a.out) return hipErrorInvalidValue;
+    if (a.ntile == 192) return a.up_s == 1 ? launch_pw<1, 12>(a, s) : launch_pw<2, 12>(a, s);
+    if (a.ntile == 96) return a.up_s == 1 ? launch_pw<1, 6>(a, s) : launch_pw<2, 6>(a, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace cc3d

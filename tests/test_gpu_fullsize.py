@@ -179,8 +179,8 @@ def _gains_of_acts(ops, params_cpu):
             params_cpu["__gain_of_act_%d" % o.act_out] = to_oracle(o.gamma.cpu())
 
 
-def _param_pair(cout, cin, cfg, i, with_gain):
-    w = synth.bf16(synth.conv_weight(cout, cin, 3, 3, 3, synth.seed(cfg, 10 + 3 * i)))
+def _param_pair(cout, cin, cfg, i, with_gain, k=(3, 3, 3)):
+    w = synth.bf16(synth.conv_weight(cout, cin, *k, synth.seed(cfg, 10 + 3 * i)))
     g = synth.gain(cin, synth.seed(cfg, 11 + 3 * i)) if with_gain else None
     dev = {"w": w.cuda(), "g": None if g is None else g.cuda(), "b": None}
     cpu = {"w": to_oracle(w), "g": None if g is None else to_oracle(g), "b": None}
@@ -237,6 +237,28 @@ def test_c3_stage1440_fullsize_sampled():
     x_cl = x.permute(1, 2, 3, 0).contiguous().cuda()
     del x
     run_stack_sampled(ops, cpu, x_cl, wl["cin"], wl["h"], wl["w"], splits, seed=303)
+
+
+def test_c4tg_decoder_fullsize_sampled():
+    """The decoder with a TemporalGrow (1x1x1 projection + causal 3x1x1 temporal
+    conv) ahead of each stage's upsample conv, at full size: the first two
+    clips, every op checked on sampled positions."""
+    wl = synth.WORKLOADS[4]
+    say("full size c4tg: %s" % wl)
+    shapes = OM.decoder_layer_shapes(temporal_grow="before")
+    dev, cpu = {}, {}
+    for i, (name, co, ci, kt, kh, kw, has_g) in enumerate(shapes):
+        d, c = _param_pair(co, ci, 4, i, has_g, k=(kt, kh, kw))
+        dev[name], cpu[name] = d, c
+    ops = S.decoder_ops(dev, unique_slots=True, temporal_grow="before")
+    _gains_of_acts(ops, cpu)
+    splits = [wl["first_clip"], wl["clip"]]
+    x = synth.bf16(synth.video(wl["c_latent"], sum(splits), wl["h"], wl["w"], synth.seed(4, 1)))
+    x_cl = x.permute(1, 2, 3, 0).contiguous().cuda()
+    got, worst = run_stack_sampled(ops, cpu, x_cl, wl["c_latent"], wl["h"], wl["w"], splits, seed=414,
+                                   max_pts_rows=4)
+    assert got.shape == (OM.output_frames(sum(splits)), 1440, 2560, 3)
+    assert any(k.startswith("s2.tg.t") for k in worst)
 
 
 def test_c4_decoder_fullsize_sampled():

@@ -84,6 +84,11 @@ BF16_CASES = [
     (192, 192, (1, 1, 1), 2, 1, 5, 7, [2, 1], C.TPAD_REPLICATE, False),
     (384, 384, (3, 1, 1), 1, 2, 4, 9, [1, 2, 1], C.TPAD_REPLICATE, True),
     (192, 192, (3, 1, 1), 1, 1, 7, 5, [2, 2], C.TPAD_ZERO, False),
+    # pointwise kernel: ragged last position tile, Cin not a multiple of 64, three
+    # 96-channel blocks with nearest 2x and zero history, a growing 3x1x1 conv
+    (104, 96, (1, 1, 1), 1, 1, 37, 41, [2, 1], C.TPAD_REPLICATE, True),
+    (64, 288, (2, 1, 1), 2, 1, 13, 19, [1, 2], C.TPAD_ZERO, True),
+    (192, 384, (3, 1, 1), 1, 2, 11, 23, [1, 3], C.TPAD_REPLICATE, False),
     # output head (taps in the GEMM's N): ragged tiles, runs of frames, cout < 3
     (96, 3, (3, 3, 3), 2, 1, 13, 37, [1, 4, 3], C.TPAD_REPLICATE, True),
     (64, 2, (3, 3, 3), 2, 2, 9, 20, [1, 3, 2], C.TPAD_ZERO, True),
@@ -105,6 +110,22 @@ def test_bf16_conv_vs_oracle(case):
                        max_chunk_t=max(splits), tpad=tpad)
     got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits))
     assert_bf16_close(got, ref, "bf16 conv")
+
+
+@pytest.mark.parametrize("k,up_s", [((1, 1, 1), 2), ((3, 1, 1), 1)])
+def test_bf16_pointwise_conv_residual(k, up_s):
+    """The pointwise kernel's epilogue: + bias + residual, stored as bf16."""
+    say("bf16 pointwise conv + residual k=%s up_s=%d" % (k, up_s))
+    cin, cout, h, w, splits = 96, 192, 9, 30, [1, 2]
+    t = sum(splits)
+    x = synth.bf16(synth.video(cin, t, h, w, synth.seed(5, 21)))
+    wt = synth.bf16(synth.conv_weight(cout, cin, *k, synth.seed(5, 22)))
+    b = synth.bias(cout, synth.seed(5, 23))
+    r = synth.bf16(synth.video(cout, t, h * up_s, w * up_s, synth.seed(5, 24)))
+    ref = O.one_shot(to_oracle(x), to_oracle(wt), to_oracle(b), O.REPLICATE, up_s) + to_oracle(r)
+    plan = P.conv_plan(wt.cuda(), h, w, bias=b.cuda(), up_s=up_s, residual=True, max_chunk_t=2)
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits, residual_cl=to_device_cl(r)))
+    assert_bf16_close(got, ref, "pointwise + residual")
 
 
 @pytest.mark.parametrize("k,up_s", [((3, 1, 1), 1), ((3, 3, 3), 2)])
@@ -376,6 +397,13 @@ def test_decoder_temporal_grow_layerwise(order):
     got, ref, _ = _decoder_layerwise(16, SMALL_STAGES, t=6, h=3, w=5, splits=[2, 3, 1], temporal_grow=order)
     assert got.shape == (3, OM.output_frames(6), 48, 80)
     assert_stack_close(got, ref, "decoder tg %s" % order)
+
+
+def test_decoder_temporal_grow_full_channels_tiny_frame():
+    say("decoder temporal grow, full channels, tiny frame")
+    got, ref, _ = _decoder_layerwise(48, OM.DECODER_STAGES, t=5, h=2, w=3, splits=[3, 2], temporal_grow="before")
+    assert got.shape == (3, OM.output_frames(5), 32, 48)
+    assert_stack_close(got, ref, "decoder tg full channels")
 
 
 def test_temporal_grow_orders_bitwise():
