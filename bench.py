@@ -1,7 +1,7 @@
 """Benchmark of the chunked causal Conv3d decode on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4|c4tg|c3]
-                    [--tg-order before|after] [--no-cpu-baseline] [--no-delivery]
+                    [--tg-order before|after] [--frame-batch B] [--no-cpu-baseline] [--no-delivery]
 
 Workloads (synthetic, seeded; the pages' test videos and trained weights are not
 available):
@@ -12,6 +12,8 @@ available):
       (1x1x1 projection + causal 3x1x1 temporal conv) on the stage input, run
       before the upsample conv (--tg-order before, the reordered decoder) or on
       the upsampled positions (--tg-order after, the original order).
+  --frame-batch B (c4, c4tg): the last stage and the head run over batches of B
+      frames of their input (frame batching); reports the plan's device memory.
   c3: the 1440p output stage, 128 ch x 720x1280 -> nearest 2x -> conv 128->96 ->
       RMSNorm+SiLU -> conv 96->3, 361 frames streamed as 1 + 90 chunks of 4.
       One step = one chunk.
@@ -101,12 +103,13 @@ def c4_step_flops(t_lat, first, h=90, w=160, temporal_grow=None):
     return f, t
 
 
-def setup_c4(dev, torch, synth, P, S, out_u8=False, temporal_grow=None):
+def setup_c4(dev, torch, synth, P, S, out_u8=False, temporal_grow=None, frame_batch=0):
     lat_c, lat_t, lh, lw = 48, 91, 90, 160
     layers = decoder_layer_list(temporal_grow=temporal_grow)
     params = make_decoder(dev, synth, S, layers)
     ops = S.decoder_ops(params, out_u8=out_u8, temporal_grow=temporal_grow)
-    plan = P.stack_plan(ops, lat_c, lh, lw, max_chunk_t=7, device=dev)
+    g0 = next(i for i, o in enumerate(ops) if o.name == ("s2.tg.p" if temporal_grow else "s2.up"))
+    plan = P.stack_plan(ops, lat_c, lh, lw, max_chunk_t=7, device=dev, batch_from=g0, frame_batch=frame_batch)
     del params
     log("c4 plan: %d ops, state %.2f GB, plan device memory %.2f GB" % (
         len(ops), plan.state_bytes / 1e9, plan.device_bytes / 1e9))
@@ -135,7 +138,9 @@ def setup_c4(dev, torch, synth, P, S, out_u8=False, temporal_grow=None):
                 "2 residual blocks each) -> head 96->3 at 1440x2560; clips of 7+14x6 latents")
     desc = {"workload": name, "output": "3x361x1440x2560 bf16",
             "step": "one clip (24 output frames; 25 for the first)"}
-    if temporal_grow:
+    if frame_batch:
+        desc["frame_batch"] = "%d frames of the last stage's input through the last stage and the head" % frame_batch
+    if temporal_grow or frame_batch:
         desc["plan_device_gb"] = round(plan.device_bytes / 1e9, 3)
     return plan, work, ring, desc
 
@@ -294,6 +299,8 @@ def main():
     ap.add_argument("--workload", choices=["c4", "c4tg", "c3"], default="c4")
     ap.add_argument("--tg-order", choices=["before", "after"], default="before",
                     help="c4tg: TemporalGrow before (reordered) or after (original) the spatial upsample")
+    ap.add_argument("--frame-batch", type=int, default=0,
+                    help="c4/c4tg: run the last stage and the head over batches of this many frames (0: whole clips)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-delivery", action="store_true",
                     help="skip the host-delivery measurement (c4: output copied to pinned host memory)")
@@ -317,7 +324,7 @@ def main():
     if args.workload == "c3":
         plan, work, ring, desc = setup_c3(dev, torch, synth, P, S)
     else:
-        plan, work, ring, desc = setup_c4(dev, torch, synth, P, S, temporal_grow=tg)
+        plan, work, ring, desc = setup_c4(dev, torch, synth, P, S, temporal_grow=tg, frame_batch=args.frame_batch)
     stream = torch.cuda.current_stream()
     states = [plan.new_state(), plan.new_state()]
     cur = [0]
@@ -393,7 +400,7 @@ def main():
         "config": desc, "frames_per_s": round(frames / dt, 2), "mfma_frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": roof, "kernels": per_kernel,
     }
-    if args.workload == "c4" and not args.no_delivery:
+    if args.workload == "c4" and not args.no_delivery and not args.frame_batch:
         # Host delivery: the same decode with every clip's RGB copied to pinned host
         # memory, overlapped with the next clip; bf16 output, then 8-bit codes.
         # PCIe-inclusive, so never the headline value.

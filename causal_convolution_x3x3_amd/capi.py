@@ -48,7 +48,8 @@ class OpDesc(ctypes.Structure):
 class StackDesc(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int), ("cin", ctypes.c_int), ("h", ctypes.c_int),
                 ("w", ctypes.c_int), ("max_chunk_t", ctypes.c_int), ("eps", ctypes.c_float),
-                ("n_ops", ctypes.c_int), ("ops", ctypes.POINTER(OpDesc)), ("grow", ctypes.c_int)]
+                ("n_ops", ctypes.c_int), ("ops", ctypes.POINTER(OpDesc)), ("grow", ctypes.c_int),
+                ("batch_from", ctypes.c_int), ("frame_batch", ctypes.c_int)]
 
 
 class OpProfile(ctypes.Structure):

@@ -58,6 +58,9 @@ struct Slot {
     FrameCount tc;
     size_t bytes = 0;
     void* ptr = nullptr;  // intermediates only
+    int writer = -1;      // first op that writes it (-1: the input x or the residual argument)
+    bool grouped = false; // written inside the frame-batched group: holds one batch
+    FrameCount rel;       // grouped (and the slots the group reads): frames per batch of the group input
 };
 
 struct OpRt {
@@ -86,6 +89,9 @@ struct cc3d_plan {
     int max_t = 1;
     int y_elem = 2;  // bytes per element of y (1 with 8-bit output)
     bool grow_aligned = false;  // CC3D_GROW_ALIGNED: the first chunk grows every frame
+    int batch_from = 0;         // frame-batched group: ops batch_from .. n_ops-1 ...
+    int frame_batch = 0;        // ... run over batches of this many frames of the group input (0: off)
+    FrameCount g_in;            // frame count of the group input (the slots it reads from before it)
     float eps = 1e-6f;
     std::vector<Slot> slots;
     std::vector<OpRt> ops;
@@ -165,6 +171,8 @@ bool valid_dtype(int d) { return d == CC3D_F32 || d == CC3D_BF16; }
 bool valid_slot_ref(int s) { return s >= 0 && s < CC3D_MAX_SLOTS; }
 const char* kind_name(int k) { return k == CC3D_OP_CONV ? "CONV" : "NORM_ACT"; }
 
+cc3d_status build_group(const cc3d_stack_desc* d, cc3d_plan* p);
+
 // Geometry and wiring checks, no device work.
 cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
 {
@@ -215,6 +223,7 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
         s.h = h;
         s.w = w;
         s.tc = tc;
+        s.writer = op;
         return CC3D_OK;
     };
 
@@ -326,7 +335,10 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
             }
             const Slot& rs = p->slots[o.res];
             if (!rs.defined) return fail(CC3D_EINVAL, "op %d: residual slot %d is not defined", i, o.res);
-            if (rs.c != r.cout || rs.h != r.h_out || rs.w != r.w_out || !(rs.tc == tc_out))
+            if (rs.c == r.cout && rs.h == r.h_out && rs.w == r.w_out && !(rs.tc == tc_out))
+                return fail(CC3D_ESHAPE, "op %d: residual slot %d has another frame count than the result "
+                            "(one is grown in time)", i, o.res);
+            if (rs.c != r.cout || rs.h != r.h_out || rs.w != r.w_out)
                 return fail(CC3D_ESHAPE, "op %d: residual slot %d is %dx%dx%d, the result is %dx%dx%d", i, o.res, rs.c,
                             rs.h, rs.w, r.cout, r.h_out, r.w_out);
             if (o.res == CC3D_SLOT_AUX) p->uses_aux = true;
@@ -351,6 +363,62 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
         if (r.kind == CC3D_OP_NORM_ACT && (r.out == CC3D_SLOT_Y || r.act_out == CC3D_SLOT_Y) && p->y_elem == 1)
             return fail(CC3D_EINVAL, "the output slot is written both as 8-bit codes and as the plan dtype");
     p->state_bytes = cache_off < kAlign ? kAlign : cache_off;
+    return build_group(d, p);
+}
+
+// Frame-batched group (frame_batch > 0): ops batch_from.. run over batches of
+// frame_batch frames of the group input, the slots they read from before the
+// group, which must all have one frame count.  Their own slots hold one batch;
+// frame counts inside the group are kept relative to the group input.
+cc3d_status build_group(const cc3d_stack_desc* d, cc3d_plan* p)
+{
+    if (d->frame_batch < 0 || d->frame_batch > 4096)
+        return fail(CC3D_EINVAL, "frame_batch=%d not in [0, 4096]", d->frame_batch);
+    if (d->frame_batch == 0) return CC3D_OK;
+    const int n = (int)p->ops.size();
+    if (d->batch_from < 0 || d->batch_from >= n)
+        return fail(CC3D_EINVAL, "batch_from=%d not in [0, %d) (the op list)", d->batch_from, n);
+    p->batch_from = d->batch_from;
+    p->frame_batch = d->frame_batch;
+    bool have = false;
+    for (int i = d->batch_from; i < n; ++i) {
+        const OpRt& r = p->ops[i];
+        for (int sl : {r.src, r.res}) {
+            if (sl == CC3D_SLOT_NONE) continue;
+            if (sl == CC3D_SLOT_AUX)
+                return fail(CC3D_EINVAL, "op %d of the frame-batched group reads the residual argument", i);
+            Slot& in = p->slots[sl];
+            if (in.writer >= d->batch_from) continue;  // written inside the group
+            if (!have) {
+                p->g_in = in.tc;
+                have = true;
+            } else if (!(in.tc == p->g_in)) {
+                return fail(CC3D_ESHAPE, "the frame-batched group reads slots of different frame counts (op %d, slot %d)",
+                            i, sl);
+            }
+            in.rel = FrameCount();
+            in.rel.mul = 1;
+        }
+        for (int sl : {r.out, r.act_out}) {
+            if (sl == CC3D_SLOT_NONE) continue;
+            if (p->slots[sl].writer < d->batch_from)
+                return fail(CC3D_EINVAL, "op %d of the frame-batched group writes slot %d, also written before the group",
+                            i, sl);
+        }
+    }
+    if (!have) return fail(CC3D_EINVAL, "the frame-batched group reads nothing computed before it");
+    if (p->slots[CC3D_SLOT_Y].writer < d->batch_from)
+        return fail(CC3D_EINVAL, "the output slot must be written inside the frame-batched group");
+    for (int i = d->batch_from; i < n; ++i) {
+        const OpRt& r = p->ops[i];
+        const FrameCount rel_in = p->slots[r.src].rel;
+        const FrameCount rel_out = (r.kind == CC3D_OP_CONV && r.up_t == 2) ? rel_in.grown(p->grow_aligned) : rel_in;
+        for (int sl : {r.out, r.act_out}) {
+            if (sl == CC3D_SLOT_NONE) continue;
+            p->slots[sl].grouped = true;
+            p->slots[sl].rel = rel_out;
+        }
+    }
     return CC3D_OK;
 }
 
@@ -410,7 +478,8 @@ cc3d_status materialise(const cc3d_stack_desc* d, cc3d_plan* p, hipStream_t stre
     for (int s = CC3D_SLOT_AUX + 1; s < CC3D_MAX_SLOTS; ++s) {
         Slot& sl = p->slots[s];
         if (!sl.defined) continue;
-        const int64_t tmax = std::max(sl.tc.eval(p->max_t, true), sl.tc.eval(p->max_t, false));
+        const int64_t tmax = sl.grouped ? std::max(sl.rel.eval(p->frame_batch, true), sl.rel.eval(p->frame_batch, false))
+                                        : std::max(sl.tc.eval(p->max_t, true), sl.tc.eval(p->max_t, false));
         sl.bytes = (size_t)tmax * sl.h * sl.w * sl.c * p->elem;
         cc3d_status st = al.alloc(&sl.ptr, sl.bytes, "an intermediate slot");
         if (st != CC3D_OK) return st;
@@ -620,6 +689,7 @@ cc3d_status cc3d_plan_create(const cc3d_conv_desc* d, const void* w, const float
     op.gamma = gamma;
     op.out_u8 = (d->epilogue & CC3D_EPI_U8) ? 1 : 0;
     cc3d_stack_desc sd;
+    memset(&sd, 0, sizeof sd);
     sd.dtype = d->dtype;
     sd.cin = d->cin;
     sd.h = d->h_in;
@@ -714,21 +784,43 @@ cc3d_status cc3d_forward_chunk(const cc3d_plan* p, const void* x, int t_chunk, c
     if (residual && (st = check_ptr(residual, p->device, "residual")) != CC3D_OK) return st;
 
     hipStream_t s = (hipStream_t)stream;
-    auto slot_ptr = [&](int slot) -> void* {
-        if (slot == CC3D_SLOT_X) return const_cast<void*>(x);
-        if (slot == CC3D_SLOT_Y) return y;
-        if (slot == CC3D_SLOT_AUX) return const_cast<void*>(residual);
-        if (slot < 0) return nullptr;
-        return p->slots[slot].ptr;
+    // One pass of ops over `t` frames of their base input: the chunk input (the
+    // whole chunk), or one batch of the frame-batched group's input.
+    struct Pass {
+        int t;               // frames of the base input
+        bool first;          // these are the video's first frames
+        const char* cache_rd;  // arena the convs read their history from ...
+        char* cache_wr;        // ... and the one their cache updates write
+        bool group;          // frame counts relative to the group input
+        int64_t in_off;      // group: frame offset into the slots it reads from before the group
+        int64_t y_off;       // group: frame offset into y
     };
-    for (const OpRt& r : p->ops) {
-        const Slot& src = p->slots[r.src];
-        const int t_in = (int)src.tc.eval(t_chunk, first);
+    auto frames_of = [&](int slot, const Pass& ps) -> int {
+        const Slot& sl = p->slots[slot];
+        return (int)(ps.group ? sl.rel.eval(ps.t, ps.first) : sl.tc.eval(ps.t, ps.first));
+    };
+    auto slot_ptr = [&](int slot, const Pass& ps) -> void* {
+        if (slot < 0) return nullptr;
+        const Slot& sl = p->slots[slot];
+        if (slot == CC3D_SLOT_Y)
+            return (char*)y + ps.y_off * ((int64_t)sl.h * sl.w * sl.c * p->y_elem);
+        char* base = slot == CC3D_SLOT_X ? (char*)const_cast<void*>(x)
+                   : slot == CC3D_SLOT_AUX ? (char*)const_cast<void*>(residual) : (char*)sl.ptr;
+        if (ps.group && !sl.grouped) base += ps.in_off * ((int64_t)sl.h * sl.w * sl.c * p->elem);
+        return base;
+    };
+    // rot0: frames of this op's output produced by earlier batches of the chunk
+    // (the kernels' temporal-tap rotation follows the frame's place in the chunk,
+    // so a batched run sums in the same order as a whole-chunk one)
+    auto run_op = [&](const OpRt& r, const Pass& ps, int64_t rot0, int64_t* frames_out) -> cc3d_status {
+        cc3d_status st;
+        const int t_in = frames_of(r.src, ps);
+        const bool first = ps.first;
         if (r.kind == CC3D_OP_CONV) {
             cc3d::ConvArgs a;
             memset(&a, 0, sizeof a);
-            a.z.x = slot_ptr(r.src);
-            a.z.cache = cin_b + r.cache_off;
+            a.z.x = slot_ptr(r.src, ps);
+            a.z.cache = ps.cache_rd + r.cache_off;
             a.z.frame_elems = (int64_t)r.h_in * r.w_in * r.cin;
             a.z.kt = r.kt;
             a.z.up_t = r.up_t;
@@ -736,9 +828,10 @@ cc3d_status cc3d_forward_chunk(const cc3d_plan* p, const void* x, int t_chunk, c
             a.z.zero_hist = r.tpad == CC3D_TPAD_ZERO ? 1 : 0;
             a.z.t_shift = (first && !p->grow_aligned) ? 1 : 0;
             const int t_v = (r.up_t == 2) ? 2 * t_in - a.z.t_shift : t_in;
+            *frames_out = t_v;
             a.wpk = r.wpk;
             a.bias = r.bias;
-            a.res = slot_ptr(r.res);
+            a.res = slot_ptr(r.res, ps);
             a.gamma = r.gamma;
             a.eps = p->eps;
             a.cin = r.cin;
@@ -757,12 +850,13 @@ cc3d_status cc3d_forward_chunk(const cc3d_plan* p, const void* x, int t_chunk, c
             a.nblocks = r.nblocks;
             a.family = r.family;
             a.rot_taps = 1;
+            a.t_rot0 = (int)rot0;
             a.out_u8 = r.out_u8 ? 1 : 0;
             if (r.fused_act) {
-                a.out = slot_ptr(r.out);
-                a.act_out = slot_ptr(r.act_out);
+                a.out = slot_ptr(r.out, ps);
+                a.act_out = slot_ptr(r.act_out, ps);
             } else {
-                a.out = r.act_out != CC3D_SLOT_NONE ? slot_ptr(r.norm_src) : slot_ptr(r.out);
+                a.out = r.act_out != CC3D_SLOT_NONE ? slot_ptr(r.norm_src, ps) : slot_ptr(r.out, ps);
                 a.act_out = nullptr;
             }
             const size_t oi = (size_t)(&r - p->ops.data());
@@ -776,51 +870,80 @@ cc3d_status cc3d_forward_chunk(const cc3d_plan* p, const void* x, int t_chunk, c
                 const double by = fr_in * (t_in + (first ? 0 : r.kt - 1)) +
                                   (double)r.cout * r.cin * r.kt * r.kh * r.kw * p->elem +
                                   t_v * fr_out * (nstore * store_scale + (a.res ? 1 : 0));
-                ProfScope ps(p, oi, 0, s, 2.0 * r.cin * r.cout * r.kt * r.kh * r.kw * vox, by);
+                ProfScope prof(p, oi, 0, s, 2.0 * r.cin * r.cout * r.kt * r.kh * r.kw * vox, by);
                 e = p->dtype == CC3D_BF16 ? cc3d::launch_conv_bf16(a, s) : cc3d::launch_conv_f32(a, s);
             }
             if ((st = hip_status(e, "conv launch")) != CC3D_OK) return st;
             if (r.act_out != CC3D_SLOT_NONE && !r.fused_act) {
                 cc3d::NormArgs n;
                 memset(&n, 0, sizeof n);
-                n.src = slot_ptr(r.norm_src);
-                n.act_out = slot_ptr(r.act_out);
+                n.src = slot_ptr(r.norm_src, ps);
+                n.act_out = slot_ptr(r.act_out, ps);
                 n.gamma = r.gamma;
                 n.eps = p->eps;
                 n.n_pix = (int64_t)t_v * r.h_out * r.w_out;
                 n.c = r.cout;
                 {
-                    ProfScope ps(p, oi, 1, s, 0.0, 2.0 * t_v * fr_out);
+                    ProfScope prof(p, oi, 1, s, 0.0, 2.0 * t_v * fr_out);
                     e = cc3d::launch_norm_act(n, p->elem, s);
                 }
                 if ((st = hip_status(e, "norm launch")) != CC3D_OK) return st;
             }
             if (r.kt > 1) {
                 {
-                    ProfScope ps(p, oi, 2, s, 0.0, 2.0 * (r.kt - 1) * fr_in);
-                    e = cc3d::launch_cache_update(a.z, t_v, (char*)cache_out->arena + r.cache_off, p->elem, s);
+                    ProfScope prof(p, oi, 2, s, 0.0, 2.0 * (r.kt - 1) * fr_in);
+                    e = cc3d::launch_cache_update(a.z, t_v, ps.cache_wr + r.cache_off, p->elem, s);
                 }
                 if ((st = hip_status(e, "cache update launch")) != CC3D_OK) return st;
             }
         } else {
             cc3d::NormArgs n;
             memset(&n, 0, sizeof n);
-            n.src = slot_ptr(r.src);
-            n.res = slot_ptr(r.res);
-            n.out = slot_ptr(r.out);
-            n.act_out = slot_ptr(r.act_out);
+            n.src = slot_ptr(r.src, ps);
+            n.res = slot_ptr(r.res, ps);
+            n.out = slot_ptr(r.out, ps);
+            n.act_out = slot_ptr(r.act_out, ps);
             n.gamma = r.gamma;
             n.eps = p->eps;
             n.n_pix = (int64_t)t_in * r.h_in * r.w_in;
             n.c = r.cin;
+            *frames_out = t_in;
             const size_t oi = (size_t)(&r - p->ops.data());
             const int nmove = 1 + (n.res ? 1 : 0) + (n.out ? 1 : 0) + (n.act_out ? 1 : 0);
             hipError_t e;
             {
-                ProfScope ps(p, oi, 0, s, 0.0, (double)n.n_pix * n.c * p->elem * nmove);
+                ProfScope prof(p, oi, 0, s, 0.0, (double)n.n_pix * n.c * p->elem * nmove);
                 e = cc3d::launch_norm_act(n, p->elem, s);
             }
             if ((st = hip_status(e, "norm launch")) != CC3D_OK) return st;
+        }
+        return CC3D_OK;
+    };
+
+    const int n_ops = (int)p->ops.size();
+    const int g0 = p->frame_batch > 0 ? p->batch_from : n_ops;
+    const Pass whole{t_chunk, first, cin_b, (char*)cache_out->arena, false, 0, 0};
+    for (int i = 0; i < g0; ++i) {
+        int64_t nf = 0;
+        if ((st = run_op(p->ops[i], whole, 0, &nf)) != CC3D_OK) return st;
+    }
+    if (g0 < n_ops) {
+        // The group in batches.  The first batch reads the caches from cache_in,
+        // later ones continue the caches the previous batch left in cache_out
+        // (the cache update is safe in place).
+        const int64_t tg = p->g_in.eval(t_chunk, first);
+        std::vector<int64_t> done(n_ops, 0);
+        int64_t y_done = 0;
+        for (int64_t f0 = 0; f0 < tg; f0 += p->frame_batch) {
+            const int tb = (int)std::min<int64_t>(p->frame_batch, tg - f0);
+            const bool bfirst = first && f0 == 0;
+            const Pass ps{tb, bfirst, f0 == 0 ? cin_b : cout_b, (char*)cache_out->arena, true, f0, y_done};
+            for (int i = g0; i < n_ops; ++i) {
+                int64_t nf = 0;
+                if ((st = run_op(p->ops[i], ps, done[i], &nf)) != CC3D_OK) return st;
+                done[i] += nf;
+            }
+            y_done += p->slots[CC3D_SLOT_Y].rel.eval(tb, bfirst);
         }
     }
     cache_out->frames_seen = cache_in->frames_seen + t_chunk;
@@ -835,6 +958,8 @@ cc3d_status cc3d_slot_shape(const cc3d_plan* p, int slot, int t_chunk, int first
         return fail(CC3D_EINVAL, "slot %d is not an intermediate slot of this plan", slot);
     if (t_chunk < 1 || t_chunk > p->max_t) return fail(CC3D_ESHAPE, "t_chunk=%d not in [1, %d]", t_chunk, p->max_t);
     const Slot& s = p->slots[slot];
+    if (s.grouped)
+        return fail(CC3D_EINVAL, "slot %d belongs to the frame-batched group and holds only the last batch", slot);
     if (c) *c = s.c;
     if (t) *t = (int)s.tc.eval(t_chunk, first != 0);
     if (h) *h = s.h;

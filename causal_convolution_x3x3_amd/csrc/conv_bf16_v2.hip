@@ -235,10 +235,12 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     }
 
     // K steps take the temporal taps in an order rotated by the output frame:
-    // loop step (ta, kc) reads tap (ta + rot) mod kt, rot = -t mod kt, so the
+    // loop step (ta, kc) reads tap (ta + rot) mod kt, rot = -(t_rot0 + t) mod kt
+    // (the frame's place in its chunk, so a frame-batched run sums in the same
+    // order as a whole-chunk one), so the
     // workgroups of frames t, t+1, t+2 -- which run at the same time -- read the
     // same input frame in the same step and share it in L2.
-    const int rot = a.rot_taps ? (a.kt - t % a.kt) % a.kt : 0;
+    const int rot = a.rot_taps ? (a.kt - (a.t_rot0 + t) % a.kt) % a.kt : 0;
     auto phys_step = [&](int step) -> int {
         const int ta = step / a.kchunks, kc = step - ta * a.kchunks;
         const int tr = ta + rot < a.kt ? ta + rot : ta + rot - a.kt;

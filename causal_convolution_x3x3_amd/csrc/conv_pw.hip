@@ -156,8 +156,9 @@ __global__ __launch_bounds__(512, 1) void conv_pw_kernel(ConvArgs a)
         }
     }
 
-    // loop step (ta, kc) reads temporal tap (ta + rot) mod kt, rot = -t mod kt
-    const int rot = a.rot_taps ? (a.kt - t % a.kt) % a.kt : 0;
+    // loop step (ta, kc) reads temporal tap (ta + rot) mod kt, rot = -(t_rot0 + t)
+    // mod kt: the frame's place in its chunk
+    const int rot = a.rot_taps ? (a.kt - (a.t_rot0 + t) % a.kt) % a.kt : 0;
     auto phys_step = [&](int step) -> int {
         const int ta = step / kc_n, kc = step - ta * kc_n;
         const int tr = ta + rot < a.kt ? ta + rot : ta + rot - a.kt;

@@ -283,16 +283,21 @@ hipError_t launch_norm_bf16_u(const NormArgs& a, int u, hipStream_t s)
 }
 
 // ----------------------------------------------------------- cache update --
+// dst[i] = Z[t_v + i] for i = 0 .. kt-2.  One thread moves element k of every
+// frame, in ascending i, so dst may be the window's own cache (a frame batch
+// that continues the cache it read): frame i is written after frame t_v + i > i
+// was read, in the same thread.
 template <typename V>
 __global__ __launch_bounds__(256) void cache_update_kernel(ZWindow z, int t_v, void* dst, int eb)
 {
-    const int i = blockIdx.y;
     const int64_t n = z.frame_elems * eb / (int64_t)sizeof(V);
-    const V* src = (const V*)zframe_bytes(z, t_v + i, eb);
-    V* d = (V*)dst + i * n;
     for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n;
-         k += (int64_t)gridDim.x * blockDim.x)
-        d[k] = src ? src[k] : V{};
+         k += (int64_t)gridDim.x * blockDim.x) {
+        for (int i = 0; i < z.kt - 1; ++i) {
+            const V* src = (const V*)zframe_bytes(z, t_v + i, eb);
+            ((V*)dst)[i * n + k] = src ? src[k] : V{};
+        }
+    }
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(uint4* d, int64_t n16, unsigned char* tail,
@@ -370,11 +375,11 @@ hipError_t launch_cache_update(const ZWindow& z, int t_v, void* dst, int eb, hip
     if (z.kt <= 1) return hipSuccess;
     const int64_t bytes = z.frame_elems * eb;
     if (bytes % 16 == 0) {
-        hipLaunchKernelGGL(cache_update_kernel<uint4>, dim3(grid_for(bytes / 16, 256, 4096), z.kt - 1),
-                           dim3(256), 0, s, z, t_v, dst, eb);
+        hipLaunchKernelGGL(cache_update_kernel<uint4>, dim3(grid_for(bytes / 16, 256, 8192)), dim3(256), 0, s, z,
+                           t_v, dst, eb);
     } else {
-        hipLaunchKernelGGL(cache_update_kernel<uint16_t>, dim3(grid_for(bytes / 2, 256, 4096), z.kt - 1),
-                           dim3(256), 0, s, z, t_v, dst, eb);
+        hipLaunchKernelGGL(cache_update_kernel<uint16_t>, dim3(grid_for(bytes / 2, 256, 8192)), dim3(256), 0, s, z,
+                           t_v, dst, eb);
     }
     return hipGetLastError();
 }

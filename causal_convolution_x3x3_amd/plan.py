@@ -191,8 +191,10 @@ def _check_weights(ops: List[Op], cin: int):
 
 
 def stack_plan(ops: List[Op], cin: int, h: int, w: int, *, dtype=torch.bfloat16, max_chunk_t=8,
-               eps=1e-6, aligned=False, device=None, stream=None) -> Plan:
-    """Plan for an op list; ``aligned`` as in conv_plan, for every up_t = 2 op."""
+               eps=1e-6, aligned=False, batch_from=0, frame_batch=0, device=None, stream=None) -> Plan:
+    """Plan for an op list; ``aligned`` as in conv_plan, for every up_t = 2 op.
+    ``frame_batch`` > 0: ops[batch_from:] run in batches of that many frames of
+    their input (frame batching, see cc3d_stack_desc)."""
     _check_weights(ops, cin)
     arr = (C.OpDesc * len(ops))()
     for i, o in enumerate(ops):
@@ -201,7 +203,8 @@ def stack_plan(ops: List[Op], cin: int, h: int, w: int, *, dtype=torch.bfloat16,
                           tpad=o.tpad, src=o.src, res=o.res, out=o.out, act_out=o.act_out,
                           w=_ptr(o.w), bias=_ptr(o.bias), gamma=_ptr(o.gamma), out_u8=int(o.out_u8))
     d = C.StackDesc(dtype=_DT[dtype], cin=cin, h=h, w=w, max_chunk_t=max_chunk_t, eps=eps, n_ops=len(ops),
-                    ops=arr, grow=C.GROW_ALIGNED if aligned else C.GROW_ONCE)
+                    ops=arr, grow=C.GROW_ALIGNED if aligned else C.GROW_ONCE, batch_from=batch_from,
+                    frame_batch=frame_batch)
     if device is None:
         device = next((o.w.device for o in ops if o.w is not None), torch.device("cuda", 0))
     hnd = ctypes.c_void_p()

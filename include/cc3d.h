@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define CC3D_VERSION 102 /* 1.0.2: aligned first-chunk growth rule */
+#define CC3D_VERSION 103 /* 1.0.3: frame-batched group execution */
 
 typedef enum {
     CC3D_OK = 0,
@@ -187,7 +187,23 @@ typedef struct {
     int n_ops;          /* 1 .. CC3D_MAX_OPS */
     const cc3d_op_desc* ops;
     int grow;           /* cc3d_grow for every up_t = 2 conv of the stack */
+    int batch_from;     /* frame batching (see below): first op of the group */
+    int frame_batch;    /* frames per batch of the group input; 0 = off */
 } cc3d_stack_desc;
+
+/* Frame batching (LightX2V blog "SwiftVR Inference Optimization ...", section
+ * "ReAE Frame Batching": a small batch of frames passes through a whole group of
+ * consecutive layers before the next batch starts, so only that batch's
+ * intermediate features are held, and every batch writes its part of one output
+ * buffer; causal layers keep their state rules).  With frame_batch > 0, ops
+ * batch_from .. n_ops-1 run once per batch of frame_batch frames of the group
+ * input -- the slots the group reads from ops before it (or x), which must all
+ * have the same frame count -- and the slots those ops write hold one batch
+ * (frames, and device memory, per batch instead of per chunk).  Each conv of the
+ * group carries its cache from batch to batch.  The output equals the
+ * whole-chunk run bit for bit.  The group must write y and must not read the
+ * residual argument or write a slot written before it; cc3d_slot_shape and
+ * cc3d_slot_read reject the group's slots (CC3D_EINVAL). */
 
 /* Create a stack plan (same ownership, failure and synchronisation rules as
  * cc3d_plan_create).  The plan allocates its intermediate slots for

@@ -24,7 +24,7 @@ def test_library_exports_every_declared_function():
     assert sorted(declared) == sorted(C.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.cc3d_version() == 102
+    assert L.cc3d_version() == 103
 
 
 def _conv_desc(**kw):
@@ -172,3 +172,55 @@ def test_weight_shape_mismatch_is_caught_by_the_binding():
     with pytest.raises(ValueError):
         P.Op(cout=8, w=w, out=C.SLOT_Y)
     assert P.Op(cout=16, w=torch.empty((16, 16, 3, 1, 1)), out=C.SLOT_Y).k == (3, 1, 1)
+
+
+def _group_desc(ops, batch_from, frame_batch):
+    # placeholder pointers: only for descriptors that validation rejects, and
+    # never where a GPU could take one that slipped through
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("descriptor checks with placeholder pointers run without a GPU")
+    d, keep = _stack(ops, batch_from=batch_from, frame_batch=frame_batch)
+    return d, keep
+
+
+@pytest.mark.parametrize("batch_from,frame_batch,ops,status,needle", [
+    (0, -1, [_conv_op()], C.EINVAL, "frame_batch"),
+    (0, 5000, [_conv_op()], C.EINVAL, "frame_batch"),
+    (1, 2, [_conv_op()], C.EINVAL, "batch_from"),
+    (-1, 2, [_conv_op()], C.EINVAL, "batch_from"),
+    # the output is written before the group
+    (2, 2, [_conv_op(out=3), _conv_op(src=3, out=C.SLOT_Y), _conv_op(src=3, out=4)], C.EINVAL, "output slot"),
+    # the group reads two slots of different frame counts (x, and a slot grown in time)
+    (2, 2, [_conv_op(out=3, up_t=2), _conv_op(out=4), _conv_op(src=3, out=5),
+            _conv_op(src=4, out=C.SLOT_Y)], C.ESHAPE, "different frame counts"),
+    # the group writes a slot also written before it
+    (1, 2, [_conv_op(out=3), _conv_op(src=3, out=4), _conv_op(src=4, out=3), _conv_op(src=3, out=C.SLOT_Y)],
+     C.EINVAL, "also written before"),
+    # the group reads the residual argument
+    (1, 2, [_conv_op(out=3), _conv_op(src=3, res=C.SLOT_AUX, out=C.SLOT_Y)], C.EINVAL, "residual argument"),
+])
+def test_frame_batch_rejects_bad_groups(batch_from, frame_batch, ops, status, needle):
+    L = C.lib()
+    d, keep = _group_desc(ops, batch_from, frame_batch)
+    out = ctypes.c_void_p()
+    st = L.cc3d_stack_plan_create(ctypes.byref(d), None, ctypes.byref(out))
+    assert st == status, C.last_error()
+    assert needle in C.last_error(), C.last_error()
+    assert out.value is None
+
+
+def test_valid_descriptors_pass_validation():
+    """A valid single-conv descriptor (every field the header defines set, the
+    rest of the stack descriptor built inside the library) passes validation:
+    without a GPU, creation fails only when it reaches the device."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("placeholder pointers: run without a GPU")
+    L = C.lib()
+    out = ctypes.c_void_p()
+    for kw in (dict(), dict(up_s=2, up_t=2, grow=C.GROW_ALIGNED), dict(kt=3, kh=1, kw=1, cout=192, cin=96)):
+        st = L.cc3d_plan_create(ctypes.byref(_conv_desc(**kw)), DUMMY, None, None, None, ctypes.byref(out))
+        assert st == C.EDEVICE, C.last_error()
+    d, keep = _stack([_conv_op(out=3), _conv_op(src=3, out=C.SLOT_Y)], batch_from=1, frame_batch=2)
+    assert L.cc3d_stack_plan_create(ctypes.byref(d), None, ctypes.byref(out)) == C.EDEVICE, C.last_error()

@@ -261,6 +261,41 @@ def test_c4tg_decoder_fullsize_sampled():
     assert any(k.startswith("s2.tg.t") for k in worst)
 
 
+def test_c4_decoder_fullsize_frame_batching():
+    """The benchmark's decoder wiring with the last stage and the head run one
+    frame at a time (frame batching): bitwise the same RGB as whole clips, on
+    the first two clips at full size, in less plan memory."""
+    wl = synth.WORKLOADS[4]
+    say("full size c4: frame batching of the last stage + head")
+    shapes = OM.decoder_layer_shapes()
+    dev = {}
+    for i, (name, co, ci, kt, kh, kw, has_g) in enumerate(shapes):
+        dev[name], _ = _param_pair(co, ci, 4, i, has_g)
+    ops = S.decoder_ops(dev)
+    g0 = next(i for i, o in enumerate(ops) if o.name == "s2.up")
+    splits = [wl["first_clip"], wl["clip"]]
+    x = synth.bf16(synth.video(wl["c_latent"], sum(splits), wl["h"], wl["w"], synth.seed(4, 1)))
+    x_cl = x.permute(1, 2, 3, 0).contiguous().cuda()
+    outs = {}
+    mem = {}
+    for fb in (0, 1):
+        plan = P.stack_plan(ops, wl["c_latent"], wl["h"], wl["w"], max_chunk_t=max(splits), batch_from=g0,
+                            frame_batch=fb)
+        mem[fb] = plan.device_bytes
+        st = P.Stream(plan)
+        t0, ys = 0, []
+        for n in splits:
+            ys.append(st.step(x_cl[t0:t0 + n].contiguous()).cpu())
+            t0 += n
+        torch.cuda.synchronize()
+        outs[fb] = torch.cat(ys)
+        del plan, st
+        torch.cuda.empty_cache()
+    assert torch.equal(outs[0], outs[1]), "frame-batched RGB differs from whole clips"
+    say("  plan device memory %.2f GB -> %.2f GB" % (mem[0] / 1e9, mem[1] / 1e9))
+    assert mem[1] < mem[0]
+
+
 def test_c4_decoder_fullsize_sampled():
     """The whole decoder at the full latent size 48 x 90x160 -> 3 x 1440x2560:
     the first two clips (7 then 6 latents -> 25 then 24 frames), every op

@@ -444,6 +444,45 @@ def test_decoder_aligned_first_chunk(temporal_grow):
     assert_stack_close(got[:, 3:], once, "aligned minus 3 frames vs default rule")
 
 
+def _op_index(ops, name):
+    return next(i for i, o in enumerate(ops) if o.name == name)
+
+
+@pytest.mark.parametrize("temporal_grow,group,fb,aligned", [
+    (None, "s2.up", 1, False),        # the last stage + head, one frame at a time
+    (None, "s2.up", 3, False),        # batches that do not divide the chunk
+    ("before", "s1.tg.p", 2, False),  # time grows inside the group
+    ("before", "s1.tg.p", 1, True),   # ... with the aligned first chunk
+    (None, "conv_in", 2, False),      # the whole stack (the group reads x)
+])
+def test_decoder_frame_batching_bitwise(temporal_grow, group, fb, aligned):
+    """Frame batching: the group of ops from `group` on runs over batches of
+    `fb` frames of its input with its caches carried from batch to batch; the
+    output equals the whole-chunk run bit for bit, with less plan memory."""
+    say("frame batching tg=%s group=%s fb=%d aligned=%s" % (temporal_grow, group, fb, aligned))
+    full = OM.decoder_layer_shapes(c_latent=16, stages=SMALL_STAGES, temporal_grow=temporal_grow)
+    gains = {s_[0]: s_[6] for s_ in full}
+    _, dev = _params([s_[:6] for s_ in full], 4, lambda n: gains[n])
+    ops = S.decoder_ops(dev, stages=SMALL_STAGES, temporal_grow=temporal_grow)
+    h, w, splits = 3, 5, [3, 2]
+    x = synth.bf16(synth.video(16, sum(splits), h, w, synth.seed(4, 1)))
+    x_cl = to_device_cl(x)
+    plan_w = P.stack_plan(ops, 16, h, w, max_chunk_t=3, aligned=aligned)
+    plan_b = P.stack_plan(ops, 16, h, w, max_chunk_t=3, aligned=aligned, batch_from=_op_index(ops, group),
+                          frame_batch=fb)
+    sw, sb = P.Stream(plan_w), P.Stream(plan_b)
+    t0 = 0
+    for n in splits:
+        xc = x_cl[t0:t0 + n].contiguous()
+        yw, yb = sw.step(xc), sb.step(xc)
+        torch.cuda.synchronize()
+        assert yw.shape == yb.shape
+        assert torch.equal(yw, yb), "chunk at %d: frame-batched output differs" % t0
+        t0 += n
+    assert plan_b.device_bytes < plan_w.device_bytes
+    say("  plan device bytes %d -> %d" % (plan_w.device_bytes, plan_b.device_bytes))
+
+
 def test_plan_create_failure_releases_everything(monkeypatch):
     """Failing allocation k of plan creation (k = 1, 2, ... until creation needs
     fewer) returns ENOMEM and leaves no plan and no device memory behind."""
