@@ -1,0 +1,95 @@
+"""CPU checks of the benchmark's own accounting: the FLOP and frame counts its
+headline value divides by, its layer list, the traffic record lookup, and the
+one-GPU contract."""
+import hashlib
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+from oracle import model as OM
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+STAGES = OM.DECODER_STAGES
+
+
+def _layer_sizes(t_lat, first, temporal_grow, h=90, w=160):
+    """(name, frames, height, width) of every conv's output for one clip, walked
+    stage by stage; frame growth from the oracle's rule (first chunk) or 2x."""
+    def frames_after(factors):
+        if first:
+            return OM.output_frames(t_lat, factors)
+        n = t_lat
+        for f in factors:
+            n *= f
+        return n
+
+    out = [("conv_in", t_lat, h, w)]
+    factors = []
+    for si, (c, f) in enumerate(STAGES):
+        t_in = frames_after(factors)
+        factors.append(f)
+        t_out = frames_after(factors)
+        if temporal_grow:
+            sh, sw = (2 * h, 2 * w) if temporal_grow == "after" else (h, w)
+            out.append(("s%d.tg.p" % si, t_in, sh, sw))
+            out.append(("s%d.tg.t" % si, t_out, sh, sw))
+        h, w = 2 * h, 2 * w
+        out.append(("s%d.up" % si, t_out, h, w))
+        for r in range(2):
+            out.append(("s%d.rb%d.c1" % (si, r), t_out, h, w))
+            out.append(("s%d.rb%d.c2" % (si, r), t_out, h, w))
+    out.append(("head", frames_after(factors), 2 * h, 2 * w))
+    return out
+
+
+@pytest.mark.parametrize("temporal_grow", [None, "before", "after"])
+@pytest.mark.parametrize("t_lat,first", [(7, True), (6, False), (1, True), (3, False)])
+def test_step_flops_match_a_per_layer_count(temporal_grow, t_lat, first):
+    shapes = {n: (co, ci, kt, kh, kw) for n, co, ci, kt, kh, kw, _ in
+              OM.decoder_layer_shapes(temporal_grow=temporal_grow)}
+    sizes = _layer_sizes(t_lat, first, temporal_grow)
+    assert [s[0] for s in sizes] == list(shapes)
+    want = 0
+    for name, t, h, w in sizes:
+        co, ci, kt, kh, kw = shapes[name]
+        want += 2 * ci * co * kt * kh * kw * t * h * w
+    got, t_out = bench.c4_step_flops(t_lat, first, temporal_grow=temporal_grow)
+    assert got == want
+    assert t_out == sizes[-1][1]
+
+
+@pytest.mark.parametrize("temporal_grow", [None, "before"])
+def test_bench_layer_list_is_the_decoder(temporal_grow):
+    assert bench.decoder_layer_list(temporal_grow=temporal_grow) == OM.decoder_layer_shapes(
+        temporal_grow=temporal_grow)
+
+
+def test_clip_schedule_covers_the_video():
+    sched = [7] + [6] * 14
+    assert sched == OM.clip_schedule(91)
+    frames = [bench.c4_step_flops(n, i == 0)[1] for i, n in enumerate(sched)]
+    assert frames[0] == 25 and set(frames[1:]) == {24} and sum(frames) == OM.output_frames(91) == 361
+
+
+def test_traffic_record_follows_the_source(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("kernel source\n")
+    sha = hashlib.sha256(src.read_bytes()).hexdigest()[:16]
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "x.md").write_text("traffic_record: kernel=kk source=k.hip source_sha256_16=%s bytes_per_launch=123.5\n" % sha)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.recorded_traffic("kk") == 123.5
+    assert bench.recorded_traffic("other") is None
+    src.write_text("kernel source, changed\n")
+    assert bench.recorded_traffic("kk") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
