@@ -346,14 +346,18 @@ def main():
     C.check(C.lib().cc3d_profile_enable(plan._h, 1), "profile_enable")
     log("timing %d steps" % args.steps)
     torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
     flops, frames = 0.0, 0
+    marks[0].record()
     for i in range(args.warmup, args.warmup + args.steps):
         fl, tout = step(i)
+        marks[i - args.warmup + 1].record()
         flops += fl
         frames += tout
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    step_ms = sorted(marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps))
     log("timed %.3f s" % dt)
 
     # per-kernel event totals over the timed region
@@ -399,6 +403,10 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": desc, "frames_per_s": round(frames / dt, 2), "mfma_frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": roof, "kernels": per_kernel,
+        # per-step GPU time between events on the stream (the first clip is the
+        # 25-frame one only when it falls in the timed steps)
+        "step_ms": {"min": round(step_ms[0], 3), "mean": round(sum(step_ms) / len(step_ms), 3),
+                    "p99": round(step_ms[min(len(step_ms) - 1, int(0.99 * len(step_ms)))], 3)},
     }
     if args.workload == "c4" and not args.no_delivery and not args.frame_batch:
         # Host delivery: the same decode with every clip's RGB copied to pinned host

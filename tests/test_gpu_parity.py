@@ -399,6 +399,16 @@ def test_decoder_temporal_grow_layerwise(order):
     assert_stack_close(got, ref, "decoder tg %s" % order)
 
 
+def test_decoder_full_channels_two_clips():
+    """The whole decoder end to end at reduced spatial size: latent 48 x 13 x
+    4x6 in the benchmark's clips (7 then 6 latents) -> RGB 3 x 49 x 64x96, every
+    layer against the oracle, the stack against the storage-rounded oracle."""
+    say("decoder full channels, two clips 7+6 at 4x6")
+    got, ref, _ = _decoder_layerwise(48, OM.DECODER_STAGES, t=13, h=4, w=6, splits=[7, 6])
+    assert got.shape == (3, 49, 64, 96)
+    assert_stack_close(got, ref, "decoder two clips")
+
+
 def test_decoder_temporal_grow_full_channels_tiny_frame():
     say("decoder temporal grow, full channels, tiny frame")
     got, ref, _ = _decoder_layerwise(48, OM.DECODER_STAGES, t=5, h=2, w=3, splits=[3, 2], temporal_grow="before")
