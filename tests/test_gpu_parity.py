@@ -1,6 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
 same seeded inputs, at sizes the oracle finishes in seconds that still span
 several tiles and ragged tails."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -491,6 +493,30 @@ def test_decoder_frame_batching_bitwise(temporal_grow, group, fb, aligned):
         t0 += n
     assert plan_b.device_bytes < plan_w.device_bytes
     say("  plan device bytes %d -> %d" % (plan_w.device_bytes, plan_b.device_bytes))
+
+
+def test_conv_family_override_keeps_v1(monkeypatch):
+    """CC3D_CONV_FAMILY=1 at plan creation keeps a conv the register-blocked
+    kernel would take on the generic kernel: the profiled kernel name says so
+    and its result matches the oracle."""
+    say("family override: 96-channel 3x3x3 conv on the generic kernel")
+    cin, cout, h, w, splits = 96, 96, 11, 70, [2, 1]
+    x = synth.bf16(synth.video(cin, sum(splits), h, w, synth.seed(5, 31)))
+    wt = synth.bf16(synth.conv_weight(cout, cin, 3, 3, 3, synth.seed(5, 32)))
+    ref = O.one_shot(to_oracle(x), to_oracle(wt), None, O.REPLICATE)
+    names = {}
+    for fam in (None, "1"):
+        if fam:
+            monkeypatch.setenv("CC3D_CONV_FAMILY", fam)
+        plan = P.conv_plan(wt.cuda(), h, w, max_chunk_t=2)
+        monkeypatch.delenv("CC3D_CONV_FAMILY", raising=False)
+        C.check(C.lib().cc3d_profile_enable(plan._h, 1), "profile_enable")
+        got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits))
+        pr = C.OpProfile()
+        C.check(C.lib().cc3d_profile_read(plan._h, 0, 0, ctypes.byref(pr)), "profile_read")
+        names[fam] = pr.kernel.decode()
+        assert_bf16_close(got, ref, "family %s" % fam)
+    assert names[None] == "conv_bf16_v2_up1_k3_n96" and names["1"] == "conv_bf16_up1_k3_n96", names
 
 
 def test_plan_create_failure_releases_everything(monkeypatch):
