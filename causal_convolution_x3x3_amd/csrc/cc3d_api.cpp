@@ -317,7 +317,7 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
             if (r.family == 2)
                 return fail(CC3D_ESHAPE,
                             "op %d: 8-bit output is not written by the 3x3 kernel for 96/128-channel blocks "
-                            "(cout=%d); accepted: cout <= 64, or the 3x3x3 upsampling head to <= 3 channels", i,
+                            "(cout=%d); accepted: cout <= 64, or the 3x3x3 head to <= 3 channels", i,
                             r.cout);
             r.out_u8 = true;
         }

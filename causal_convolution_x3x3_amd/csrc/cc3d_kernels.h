@@ -82,9 +82,10 @@ bool v2_conv_applies(int ntile, int kh, int kw, int up_s);
 int bf16_conv_family(int cout, int cin, int kt, int kh, int kw, int up_s, int plain);
 hipError_t launch_conv_bf16_v2(const ConvArgs& a, hipStream_t s);
 
-// Output head (conv_head.hip): 3x3x3 conv to at most 3 channels of a nearest-2x
-// upsampled input, spatial taps in the GEMM's N dimension; weights packed per
-// (32-channel chunk, N fragment) as 64 lanes x 8 channels.
+// Output head (conv_head.hip): 3x3x3 conv to at most 3 channels, of a nearest-2x
+// upsampled input or at the input's own size, spatial taps in the GEMM's N
+// dimension; weights packed per (32-channel chunk, N fragment) as 64 lanes x 8
+// channels.
 bool head_conv_applies(int cout, int cin, int kt, int kh, int kw, int up_s);
 size_t head_packed_elems(int cin);
 hipError_t launch_pack_head(const void* w, void* wpk, int cout, int cin, hipStream_t s);

@@ -1,5 +1,6 @@
 // Output-head conv on gfx950 MFMA: a 3x3x3 causal conv to at most three
-// channels (RGB) whose input is nearest-2x upsampled in space.
+// channels (RGB), on a nearest-2x upsampled input (UP = 2) or at the input's own
+// size (UP = 1).
 //
 // With three output channels, the GEMM view of the other kernels (N = output
 // channels) leaves 13 of 16 MFMA columns idle.  Here the spatial taps go into N
@@ -10,22 +11,24 @@
 //
 // is one GEMM with M = source pixels, K = Cin, N = 3 temporal x 9 spatial taps
 // x 3 channels (27 per temporal tap, padded to 32).  An output pixel (y, x) of
-// frame t then sums, for each tap, one entry of P: spatial tap (b, d) of output
-// phase (p, q) = (y & 1, x & 1) reads source (y/2 + floor((p+b-1)/2),
-// x/2 + floor((q+d-1)/2)) -- nearest upsampling followed by zero padding of the
-// upsampled image is exactly "zero outside the source image" -- and temporal tap
-// a reads input frame t + a of the causal window.  Every product of the conv's
+// frame t then sums, for each tap, one entry of P: with UP = 2, spatial tap
+// (b, d) of output phase (p, q) = (y & 1, x & 1) reads source (y/2 +
+// floor((p+b-1)/2), x/2 + floor((q+d-1)/2)) -- nearest upsampling followed by
+// zero padding of the upsampled image is exactly "zero outside the source
+// image"; with UP = 1 it reads (y + b - 1, x + d - 1).  Temporal tap a reads
+// input frame t + a of the causal window.  Every product of the conv's
 // definition is formed once (in the MFMA) and every sum is taken in fp32, in a
 // different order from the direct form; no weights are pre-summed.
 //
-// A workgroup owns a tile of 8 x 16 source pixels (16 x 32 output pixels) and a
-// run of consecutive output frames.  It walks the input frames of that run
+// A workgroup owns a tile of 8 x 16 source pixels (16 x 32 output pixels, or
+// 8 x 16 with UP = 1) and a run of consecutive output frames.  It walks the input frames of that run
 // once: each frame's tile plus a one-pixel border (18 x 10 pixels, 12 M
 // fragments) is loaded straight into MFMA operand registers (the next frame's
 // while the current one is gathered), multiplied by the weights held in
 // registers for the whole run, and the partial sums P go to LDS.  Each thread
-// then gathers the taps of two horizontally adjacent output pixels and adds
-// them to a three-frame ring of fp32 accumulators in registers; output frame t
+// then gathers the taps of two horizontally adjacent output pixels (UP = 1: one
+// pixel, threads 0..127) and adds them to a three-frame ring of fp32
+// accumulators in registers; output frame t
 // is complete, and stored (bf16, or the 8-bit code of the fp32 value), once
 // input frame t + 2 has been added.
 #include "cc3d_kernels.h"
@@ -69,9 +72,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-template <int KC>
+template <int UP, int KC>
 __global__ __launch_bounds__(256, 2) void conv_head_kernel(ConvArgs a, int fpw)
 {
+    constexpr int NQ = UP;  // output pixels per thread (horizontal neighbours)
     __shared__ float ptab[MFR * 16 * PSTR];  // P[pixel of the bordered tile][n]
 
     const int tiles_w = (a.w_in + TW - 1) / TW;
@@ -125,29 +129,30 @@ __global__ __launch_bounds__(256, 2) void conv_head_kernel(ConvArgs a, int fpw)
                     bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(poff[mm] + (uint32_t)(kc * 64)), 0, 0));
     };
 
-    // the two output pixels of this thread: row oy, columns ox and ox + 1 of the
-    // 16 x 32 output tile; source row si (phase p) and column sj of the tile
+    // UP = 2: the two output pixels of this thread are row oy, columns 2 sj and
+    // 2 sj + 1 of the 16 x 32 output tile (source row si, phase p = oy & 1).
+    // UP = 1: threads 0..127 own output pixel (si, sj) of the 8 x 16 tile.
     const int oy = tid >> 4, sj = tid & 15;
-    const int p = oy & 1, si = oy >> 1;
-    const int Y = 2 * i0 + oy, X = 2 * (j0 + sj);
-    const bool row_ok = Y < a.h_out;
+    const int p = oy & 1, si = UP == 2 ? oy >> 1 : oy;
+    const int Y = UP == 2 ? 2 * i0 + oy : i0 + oy, X = UP == 2 ? 2 * (j0 + sj) : j0 + sj;
+    const bool row_ok = Y < a.h_out && (UP == 2 || tid < TH * TW);
     const int cout = a.cout;
 
-    float ring[3][2][3];
+    float ring[3][NQ][3];
 #pragma unroll
     for (int s = 0; s < 3; ++s)
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+        for (int q = 0; q < NQ; ++q)
 #pragma unroll
             for (int o = 0; o < 3; ++o) ring[s][q][o] = 0.f;
 
-    auto store = [&](int t, const float (&v)[2][3]) {
+    auto store = [&](int t, const float (&v)[NQ][3]) {
         if (!row_ok) return;
         uint16_t* out = (uint16_t*)a.out;
         const uint16_t* res = (const uint16_t*)a.res;
         const int64_t base = (((int64_t)t * a.h_out + Y) * a.w_out + X) * cout;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             if (X + q >= a.w_out) continue;
 #pragma unroll
             for (int o = 0; o < 3; ++o) {
@@ -188,28 +193,35 @@ __global__ __launch_bounds__(256, 2) void conv_head_kernel(ConvArgs a, int fpw)
             for (int f = 0; f < NFR; ++f) *(f32x4*)&ptab[L * PSTR + 16 * f + 4 * g] = acc[mm][f];
         }
         __syncthreads();
-        // gather: tap (a, b, d) of output pixel (oy, 2 sj + q) reads bordered-tile
-        // pixel (si + 1 + floor((p+b-1)/2), sj + 1 + floor((q+d-1)/2)):
-        //   q = 0: d = 0 -> column sj, d = 1, 2 -> sj + 1;  q = 1: d = 0, 1 -> sj + 1, d = 2 -> sj + 2
+        // gather.  UP = 2: tap (a, b, d) of output pixel (oy, 2 sj + q) reads
+        // bordered-tile pixel (si + 1 + floor((p+b-1)/2), sj + 1 + floor((q+d-1)/2)):
+        //   q = 0: d = 0 -> column sj, d = 1, 2 -> sj + 1;  q = 1: d = 0, 1 -> sj + 1, d = 2 -> sj + 2.
+        // UP = 1: tap (a, b, d) of output pixel (si, sj) reads (si + b, sj + d).
 #pragma unroll
         for (int ta = 0; ta < 3; ++ta) {
             const int t = zi - ta;
             if (t < t0 || t >= t1) continue;
             const int slot = ((PH - ta) % 3 + 3) % 3;
+            if (UP == 2 || tid < TH * TW) {
 #pragma unroll
-            for (int b = 0; b < 3; ++b) {
-                const int row = si + 1 + ((p + b - 1) >> 1);
-                const float* pr = &ptab[(row * BW + sj) * PSTR + ta * 32 + b * 9];
+                for (int b = 0; b < 3; ++b) {
+                    const int row = UP == 2 ? si + 1 + ((p + b - 1) >> 1) : si + b;
+                    const float* pr = &ptab[(row * BW + sj) * PSTR + ta * 32 + b * 9];
 #pragma unroll
-                for (int o = 0; o < 3; ++o) {
-                    ring[slot][0][o] += pr[o] + pr[PSTR + 3 + o] + pr[PSTR + 6 + o];
-                    ring[slot][1][o] += pr[PSTR + o] + pr[PSTR + 3 + o] + pr[2 * PSTR + 6 + o];
+                    for (int o = 0; o < 3; ++o) {
+                        if (UP == 2) {
+                            ring[slot][0][o] += pr[o] + pr[PSTR + 3 + o] + pr[PSTR + 6 + o];
+                            ring[slot][NQ - 1][o] += pr[PSTR + o] + pr[PSTR + 3 + o] + pr[2 * PSTR + 6 + o];
+                        } else {
+                            ring[slot][0][o] += pr[o] + pr[PSTR + 3 + o] + pr[2 * PSTR + 6 + o];
+                        }
+                    }
                 }
             }
             if (ta == 2) {  // output frame t has all its taps
                 store(t, ring[slot]);
 #pragma unroll
-                for (int q = 0; q < 2; ++q)
+                for (int q = 0; q < NQ; ++q)
 #pragma unroll
                     for (int o = 0; o < 3; ++o) ring[slot][q][o] = 0.f;
             }
@@ -228,7 +240,7 @@ __global__ __launch_bounds__(256, 2) void conv_head_kernel(ConvArgs a, int fpw)
 
 bool head_conv_applies(int cout, int cin, int kt, int kh, int kw, int up_s)
 {
-    return cout >= 1 && cout <= 3 && kt == 3 && kh == 3 && kw == 3 && up_s == 2 && cin % 32 == 0 &&
+    return cout >= 1 && cout <= 3 && kt == 3 && kh == 3 && kw == 3 && (up_s == 1 || up_s == 2) && cin % 32 == 0 &&
            cin >= 32 && cin <= 96;
 }
 
@@ -275,7 +287,7 @@ hipError_t launch_pack_head(const void* w, void* wpk, int cout, int cin, hipStre
 hipError_t launch_conv_head(const ConvArgs& a, hipStream_t s)
 {
     if (!head_conv_applies(a.cout, a.cin, a.kt, a.kh, a.kw, a.up_s)) return hipErrorInvalidValue;
-    if (a.h_out != 2 * a.h_in || a.w_out != 2 * a.w_in || a.t_out < 1) return hipErrorInvalidValue;
+    if (a.h_out != a.up_s * a.h_in || a.w_out != a.up_s * a.w_in || a.t_out < 1) return hipErrorInvalidValue;
     const int64_t ntiles = (int64_t)((a.h_in + TH - 1) / TH) * ((a.w_in + TW - 1) / TW);
     // a run of frames per workgroup: long runs read each input frame once; cut
     // them when there are too few tiles to fill the chip twice over
@@ -286,11 +298,18 @@ hipError_t launch_conv_head(const ConvArgs& a, hipStream_t s)
     const int64_t total = ntiles * ((a.t_out + fpw - 1) / fpw);
     if (total > (int64_t)0x7fffffff - 8) return hipErrorInvalidValue;
     const int64_t grid = ((total + 7) / 8) * 8;
-    switch (a.cin / 32) {
-    case 1: hipLaunchKernelGGL((conv_head_kernel<1>), dim3((unsigned)grid), dim3(256), 0, s, a, fpw); break;
-    case 2: hipLaunchKernelGGL((conv_head_kernel<2>), dim3((unsigned)grid), dim3(256), 0, s, a, fpw); break;
-    case 3: hipLaunchKernelGGL((conv_head_kernel<3>), dim3((unsigned)grid), dim3(256), 0, s, a, fpw); break;
-    default: return hipErrorInvalidValue;
+    const dim3 gd((unsigned)grid), bd(256);
+    const int kc = a.cin / 32;
+    if (a.up_s == 2) {
+        if (kc == 1) hipLaunchKernelGGL((conv_head_kernel<2, 1>), gd, bd, 0, s, a, fpw);
+        else if (kc == 2) hipLaunchKernelGGL((conv_head_kernel<2, 2>), gd, bd, 0, s, a, fpw);
+        else if (kc == 3) hipLaunchKernelGGL((conv_head_kernel<2, 3>), gd, bd, 0, s, a, fpw);
+        else return hipErrorInvalidValue;
+    } else {
+        if (kc == 1) hipLaunchKernelGGL((conv_head_kernel<1, 1>), gd, bd, 0, s, a, fpw);
+        else if (kc == 2) hipLaunchKernelGGL((conv_head_kernel<1, 2>), gd, bd, 0, s, a, fpw);
+        else if (kc == 3) hipLaunchKernelGGL((conv_head_kernel<1, 3>), gd, bd, 0, s, a, fpw);
+        else return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

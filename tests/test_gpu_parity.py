@@ -96,6 +96,11 @@ BF16_CASES = [
     (64, 2, (3, 3, 3), 2, 2, 9, 20, [1, 3, 2], C.TPAD_ZERO, True),
     (96, 1, (3, 3, 3), 2, 1, 8, 16, [2, 5], C.TPAD_REPLICATE, False),
     (32, 3, (3, 3, 3), 2, 1, 128, 1024, [2, 5], C.TPAD_REPLICATE, True),
+    # ... at the input's own size (the 1440p stage's last conv)
+    (96, 3, (3, 3, 3), 1, 1, 13, 37, [1, 4, 3], C.TPAD_REPLICATE, True),
+    (64, 2, (3, 3, 3), 1, 1, 9, 20, [1, 3, 2], C.TPAD_ZERO, True),
+    (32, 3, (3, 3, 3), 1, 2, 17, 33, [2, 3], C.TPAD_REPLICATE, False),
+    (96, 1, (3, 3, 3), 1, 1, 16, 16, [3], C.TPAD_REPLICATE, False),
 ]
 
 
