@@ -43,6 +43,7 @@ DUMMY = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
     (dict(max_chunk_t=0), C.ESHAPE), (dict(h_in=0), C.ESHAPE), (dict(cout=0), C.ESHAPE),
     (dict(epilogue=8), C.EINVAL), (dict(epilogue=C.EPI_ACT | C.EPI_U8), C.EINVAL), (dict(kh=3, kw=1), C.ESHAPE), (dict(eps=-1.0), C.EINVAL),
     (dict(grow=2), C.EINVAL), (dict(grow=-1), C.EINVAL),
+    (dict(cin=384, h_in=1440, w_in=1942), C.ESHAPE),  # 2^30 elements per input frame or more
 ])
 def test_plan_create_rejects_bad_descriptor(bad, status):
     L = C.lib()

@@ -187,6 +187,37 @@ def _param_pair(cout, cin, cfg, i, with_gain, k=(3, 3, 3)):
     return dev, cpu
 
 
+def test_max_frame_size_sampled():
+    """The largest input frame a plan accepts (just under 2^30 elements: 384
+    channels x 1440 x 1940, 2.1 GB per frame), two one-frame chunks (the history
+    rule, then the carried cache), checked on sampled outputs that include the
+    last rows and columns -- where a 32-bit byte offset would wrap."""
+    cin, cout, h, w = 384, 96, 1440, 1940
+    assert cin * h * w < 2 ** 30 <= cin * h * (w + 2)
+    say("max frame size: %d x %d x %d" % (cin, h, w))
+    wt = synth.bf16(synth.conv_weight(cout, cin, 3, 3, 3, synth.seed(11, 2)))
+    gen = torch.Generator(device="cuda").manual_seed(11001)
+    x = torch.randn((2, h, w, cin), device="cuda", generator=gen).to(torch.bfloat16)
+    plan = P.stack_plan([P.Op(cout=cout, w=wt.cuda(), out=C.SLOT_Y, name="conv")], cin, h, w, max_chunk_t=1)
+    st = P.Stream(plan)
+    win = Window(3, 1)
+    rng = np.random.RandomState(1101)
+    wt64 = to_oracle(wt)
+    for t0 in range(2):
+        first = t0 == 0
+        xc = x[t0:t0 + 1].contiguous()
+        y = st.step(xc)
+        torch.cuda.synchronize()
+        z = win.step(xc, first)
+        rows, cols, ts = _samples(rng, 1, h, w, nrows=5, ncols=40, nts=2)
+        tal = {"out": Tally(), "act": Tally()}
+        check_conv(z, wt64, None, 1, ts, sorted(set(rows + [h - 2])), cols, out=y, tallies=tal)
+        mx, mn = tal["out"].check("max frame, chunk %d" % t0)
+        say("  chunk %d: sampled max-rel %.2e mean-rel %.2e" % (t0, mx, mn))
+        del y, z
+    torch.cuda.empty_cache()
+
+
 def test_c1_resblock_fullsize_sampled():
     """128-channel residual block at 90x160, 16 frames in 4-frame chunks."""
     wl = synth.WORKLOADS[1]

@@ -247,6 +247,10 @@ def test_cache_in_untouched_and_aliasing_rejected():
     with pytest.raises(C.Cc3dError) as e:
         plan.forward_chunk(torch.empty((5, h, w, cin), dtype=torch.bfloat16, device="cuda"), s1, s2)
     assert e.value.status == C.ESHAPE
+    # an empty chunk is refused
+    with pytest.raises(C.Cc3dError) as e:
+        plan.forward_chunk(x[:0].contiguous(), s1, s2)
+    assert e.value.status == C.ESHAPE
     # host memory is refused
     with pytest.raises(ValueError):
         plan.forward_chunk(x[:1].cpu().contiguous(), s1, s2)
