@@ -47,6 +47,13 @@
  * void*; NULL = the null stream) and return without synchronising the host.
  * Inputs must stay alive until that work completes.  One plan and one state
  * must not be used by two calls at once (a plan owns its intermediate buffers).
+ *
+ * Graphs (CDA-VSR page, "CUDA Graph inference").  cc3d_forward_chunk and
+ * cc3d_reset only launch kernels on the stream (no allocation, no host
+ * synchronisation, no memset nodes) and may be captured into a HIP graph, with
+ * profiling off.  Which rule a chunk takes (first chunk or not) is decided from
+ * cache_in->frames_seen when the call is made, so a captured call replays that
+ * rule: run the video's first chunk eagerly, then replay captured chunks. 
  */
 #ifndef CC3D_H
 #define CC3D_H
