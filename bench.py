@@ -171,7 +171,8 @@ def setup_c3(dev, torch, synth, P, S):
 def recorded_traffic(kernel_name):
     """HBM bytes per launch of `kernel_name` from a committed PMC summary in
     profiles/ (FETCH_SIZE + WRITE_SIZE runs, copy-calibrated), or None when no
-    record exists or the kernel's source changed since the counters were taken."""
+    record exists or a source it names (comma-separated: the kernel, and the op
+    list that sets its launches) changed since the counters were taken."""
     import glob
     import hashlib
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
@@ -181,11 +182,13 @@ def recorded_traffic(kernel_name):
             kv = dict(item.split("=", 1) for item in line.split()[1:])
             if kv.get("kernel") != kernel_name:
                 continue
-            src = os.path.join(ROOT, kv["source"])
-            if not os.path.exists(src):
+            srcs = [os.path.join(ROOT, f) for f in kv["source"].split(",")]
+            if not all(os.path.exists(f) for f in srcs):
                 continue
-            sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-            if sha == kv.get("source_sha256_16"):
+            h = hashlib.sha256()
+            for f in srcs:
+                h.update(open(f, "rb").read())
+            if h.hexdigest()[:16] == kv.get("source_sha256_16"):
                 return float(kv["bytes_per_launch"])
     return None
 

@@ -132,7 +132,9 @@ def decoder_ops(params: Dict[str, Dict], stages=DECODER_STAGES, c_out: int = 3,
             # it to the head; otherwise the next stage's up conv reads the raw stream
             need_act = r == 0 or si == len(stages) - 1
             nxt_g = (rb[1][0]["g"] if r == 0 else params["head"]["g"]) if need_act else None
-            new_raw = slot(raw_fixed[1 - cur])
+            # the last block's raw sum is read by nothing (the head reads its act)
+            last = r == 1 and si == len(stages) - 1
+            new_raw = NONE if last else slot(raw_fixed[1 - cur])
             new_act = slot(act_fixed[1 - cur]) if need_act else NONE
             ops.append(Op(cout=c, w=p2["w"], bias=p2.get("b"), src=inner, res=raw_cur, out=new_raw,
                           act_out=new_act, gamma=nxt_g, name="s%d.rb%d.c2" % (si, r)))

@@ -86,6 +86,15 @@ def test_traffic_record_follows_the_source(tmp_path, monkeypatch):
     assert bench.recorded_traffic("other") is None
     src.write_text("kernel source, changed\n")
     assert bench.recorded_traffic("kk") is None
+    # two sources: the hash covers both, in order
+    other = tmp_path / "ops.py"
+    other.write_text("op list\n")
+    sha2 = hashlib.sha256(src.read_bytes() + other.read_bytes()).hexdigest()[:16]
+    (prof / "x.md").write_text("traffic_record: kernel=kk source=k.hip,ops.py source_sha256_16=%s "
+                               "bytes_per_launch=7\n" % sha2)
+    assert bench.recorded_traffic("kk") == 7.0
+    other.write_text("op list, changed\n")
+    assert bench.recorded_traffic("kk") is None
 
 
 def test_more_than_one_gpu_is_refused():
