@@ -135,6 +135,18 @@ def test_bf16_pointwise_conv_residual(k, up_s):
     assert_bf16_close(got, ref, "pointwise + residual")
 
 
+def test_fp32_conv_aligned_growth():
+    """The fp32 kernel under CC3D_GROW_ALIGNED, against the oracle to the fp32 bound."""
+    say("fp32 conv aligned growth")
+    cin, cout, h, w, splits = 16, 16, 9, 13, [2, 1, 3]
+    x = synth.video(cin, sum(splits), h, w, synth.seed(0, 21))
+    wt = synth.conv_weight(cout, cin, 3, 3, 3, synth.seed(0, 22))
+    ref = O.one_shot(to_oracle(x), to_oracle(wt), None, O.REPLICATE, 2, 2, aligned=True)
+    plan = P.conv_plan(wt.cuda(), h, w, up_s=2, up_t=2, max_chunk_t=3, aligned=True)
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits))
+    assert_fp32_close(got, ref, "fp32 aligned growth")
+
+
 @pytest.mark.parametrize("k,up_s", [((3, 1, 1), 1), ((3, 3, 3), 2)])
 def test_bf16_conv_aligned_growth(k, up_s):
     """CC3D_GROW_ALIGNED: the first chunk doubles every frame at up_t = 2
@@ -389,10 +401,13 @@ def test_decoder_small_channels():
     assert_stack_close(got, ref, "decoder small")
 
 
-def test_decoder_full_channels_tiny_frame():
-    say("decoder full channels tiny frame")
-    got, ref, _ = _decoder_layerwise(48, OM.DECODER_STAGES, t=5, h=2, w=3, splits=[3, 2])
-    assert got.shape == (3, OM.output_frames(5), 32, 48)
+@pytest.mark.parametrize("aligned", [False, True])
+def test_decoder_full_channels_tiny_frame(aligned):
+    """Full channel counts (the register-blocked kernels and the head), both
+    first-chunk growth rules."""
+    say("decoder full channels tiny frame, aligned=%s" % aligned)
+    got, ref, _ = _decoder_layerwise(48, OM.DECODER_STAGES, t=5, h=2, w=3, splits=[3, 2], aligned=aligned)
+    assert got.shape == (3, OM.output_frames(5, aligned=aligned), 32, 48)
     assert_stack_close(got, ref, "decoder full channels")
 
 
@@ -469,22 +484,23 @@ def _op_index(ops, name):
     return next(i for i, o in enumerate(ops) if o.name == name)
 
 
-@pytest.mark.parametrize("temporal_grow,group,fb,aligned", [
-    (None, "s2.up", 1, False),        # the last stage + head, one frame at a time
-    (None, "s2.up", 3, False),        # batches that do not divide the chunk
-    ("before", "s1.tg.p", 2, False),  # time grows inside the group
-    ("before", "s1.tg.p", 1, True),   # ... with the aligned first chunk
-    (None, "conv_in", 2, False),      # the whole stack (the group reads x)
+@pytest.mark.parametrize("temporal_grow,group,fb,aligned,out_u8", [
+    (None, "s2.up", 1, False, False),        # the last stage + head, one frame at a time
+    (None, "s2.up", 2, False, True),         # ... writing 8-bit RGB
+    (None, "s2.up", 3, False, False),        # batches that do not divide the chunk
+    ("before", "s1.tg.p", 2, False, False),  # time grows inside the group
+    ("before", "s1.tg.p", 1, True, False),   # ... with the aligned first chunk
+    (None, "conv_in", 2, False, False),      # the whole stack (the group reads x)
 ])
-def test_decoder_frame_batching_bitwise(temporal_grow, group, fb, aligned):
+def test_decoder_frame_batching_bitwise(temporal_grow, group, fb, aligned, out_u8):
     """Frame batching: the group of ops from `group` on runs over batches of
     `fb` frames of its input with its caches carried from batch to batch; the
     output equals the whole-chunk run bit for bit, with less plan memory."""
-    say("frame batching tg=%s group=%s fb=%d aligned=%s" % (temporal_grow, group, fb, aligned))
+    say("frame batching tg=%s group=%s fb=%d aligned=%s u8=%s" % (temporal_grow, group, fb, aligned, out_u8))
     full = OM.decoder_layer_shapes(c_latent=16, stages=SMALL_STAGES, temporal_grow=temporal_grow)
     gains = {s_[0]: s_[6] for s_ in full}
     _, dev = _params([s_[:6] for s_ in full], 4, lambda n: gains[n])
-    ops = S.decoder_ops(dev, stages=SMALL_STAGES, temporal_grow=temporal_grow)
+    ops = S.decoder_ops(dev, stages=SMALL_STAGES, temporal_grow=temporal_grow, out_u8=out_u8)
     h, w, splits = 3, 5, [3, 2]
     x = synth.bf16(synth.video(16, sum(splits), h, w, synth.seed(4, 1)))
     x_cl = to_device_cl(x)
