@@ -74,7 +74,9 @@ class Tally:
         return mx, mn
 
 
-def _samples(rng, t, h, w, nrows=6, ncols=48, nts=4):
+def _samples(rng, t, h, w, nrows=8, ncols=128, nts=4):
+    """Rows (first, last, random), columns (the first two, the last two, random)
+    and frames (first, last, random): up to nrows x ncols x nts positions."""
     rows = sorted(set([0, h - 1] + list(rng.randint(0, h, size=nrows - 2))))
     cols = sorted(set([0, 1, w - 2, w - 1] + list(rng.randint(0, w, size=ncols - 4))))
     ts = sorted(set([0, t - 1] + list(rng.randint(0, t, size=nts - 2))))
@@ -118,7 +120,7 @@ def check_norm(src, act, gamma, ts, rows, cols, res=None, out=None, tallies=None
         tallies["act"].add(_gather(act, ts, y, cols), O.act(v.T, gamma, EPS).T)
 
 
-def run_stack_sampled(ops, params_cpu, x_cl, cin, h, w, splits, seed, max_pts_rows=6):
+def run_stack_sampled(ops, params_cpu, x_cl, cin, h, w, splits, seed, max_pts_rows=8):
     """Run `ops` chunk by chunk and check every op on sampled positions."""
     plan = P.stack_plan(ops, cin, h, w, max_chunk_t=max(splits))
     st = P.Stream(plan)
@@ -209,7 +211,7 @@ def test_max_frame_size_sampled():
         y = st.step(xc)
         torch.cuda.synchronize()
         z = win.step(xc, first)
-        rows, cols, ts = _samples(rng, 1, h, w, nrows=5, ncols=40, nts=2)
+        rows, cols, ts = _samples(rng, 1, h, w, nrows=8, ncols=128, nts=2)
         tal = {"out": Tally(), "act": Tally()}
         check_conv(z, wt64, None, 1, ts, sorted(set(rows + [h - 2])), cols, out=y, tallies=tal)
         mx, mn = tal["out"].check("max frame, chunk %d" % t0)
@@ -287,7 +289,7 @@ def test_c4tg_decoder_fullsize_sampled():
     x = synth.bf16(synth.video(wl["c_latent"], sum(splits), wl["h"], wl["w"], synth.seed(4, 1)))
     x_cl = x.permute(1, 2, 3, 0).contiguous().cuda()
     got, worst = run_stack_sampled(ops, cpu, x_cl, wl["c_latent"], wl["h"], wl["w"], splits, seed=414,
-                                   max_pts_rows=4)
+                                   max_pts_rows=8)
     assert got.shape == (OM.output_frames(sum(splits)), 1440, 2560, 3)
     assert any(k.startswith("s2.tg.t") for k in worst)
 
@@ -345,7 +347,7 @@ def test_c4_decoder_fullsize_sampled():
     x = synth.bf16(synth.video(wl["c_latent"], sum(splits), wl["h"], wl["w"], synth.seed(4, 1)))
     x_cl = x.permute(1, 2, 3, 0).contiguous().cuda()
     got, worst = run_stack_sampled(ops, cpu, x_cl, wl["c_latent"], wl["h"], wl["w"], splits, seed=404,
-                                   max_pts_rows=4)
+                                   max_pts_rows=8)
     assert got.shape == (OM.output_frames(sum(splits)), 1440, 2560, 3)
     torch.cuda.empty_cache()
     say("  production wiring")
