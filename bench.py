@@ -1,7 +1,8 @@
 """Benchmark of the chunked causal Conv3d decode on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4|c4tg|c3]
-                    [--tg-order before|after] [--frame-batch B] [--no-cpu-baseline] [--no-delivery]
+                    [--tg-order before|after] [--frame-batch B] [--fold-upsample] [--no-cpu-baseline]
+                    [--no-delivery]
 
 Workloads (synthetic, seeded; the pages' test videos and trained weights are not
 available):
@@ -14,6 +15,9 @@ available):
       the upsampled positions (--tg-order after, the original order).
   --frame-batch B (c4, c4tg): the last stage and the head run over batches of B
       frames of their input (frame batching); reports the plan's device memory.
+  --fold-upsample: the upsampling 3x3x3 convs run phase-folded (7/9 of their MFMA
+      work); value stays the definition's FLOP rate, executed_tflops and
+      mfma_frac count the MFMA work actually done.
   c3: the 1440p output stage, 128 ch x 720x1280 -> nearest 2x -> conv 128->96 ->
       RMSNorm+SiLU -> conv 96->3, 361 frames streamed as 1 + 90 chunks of 4.
       One step = one chunk.
@@ -103,13 +107,26 @@ def c4_step_flops(t_lat, first, h=90, w=160, temporal_grow=None):
     return f, t
 
 
-def setup_c4(dev, torch, synth, P, S, out_u8=False, temporal_grow=None, frame_batch=0):
+def c4_up_flops(t_lat, first, h=90, w=160):
+    """Algorithmic FLOP of the three upsampling convs (up_s = 2) of one clip."""
+    f, t, cin = 0.0, t_lat, 384
+    for c, up_t in ((384, 2), (192, 2), (96, 1)):
+        h, w = 2 * h, 2 * w
+        if up_t == 2:
+            t = grown(t, first)
+        f += conv_flops_per_voxel(cin, c) * t * h * w
+        cin = c
+    return f
+
+
+def setup_c4(dev, torch, synth, P, S, out_u8=False, temporal_grow=None, frame_batch=0, fold=False):
     lat_c, lat_t, lh, lw = 48, 91, 90, 160
     layers = decoder_layer_list(temporal_grow=temporal_grow)
     params = make_decoder(dev, synth, S, layers)
     ops = S.decoder_ops(params, out_u8=out_u8, temporal_grow=temporal_grow)
     g0 = next(i for i, o in enumerate(ops) if o.name == ("s2.tg.p" if temporal_grow else "s2.up"))
-    plan = P.stack_plan(ops, lat_c, lh, lw, max_chunk_t=7, device=dev, batch_from=g0, frame_batch=frame_batch)
+    plan = P.stack_plan(ops, lat_c, lh, lw, max_chunk_t=7, device=dev, batch_from=g0, frame_batch=frame_batch,
+                        fold_upsample=fold)
     del params
     log("c4 plan: %d ops, state %.2f GB, plan device memory %.2f GB" % (
         len(ops), plan.state_bytes / 1e9, plan.device_bytes / 1e9))
@@ -125,7 +142,9 @@ def setup_c4(dev, torch, synth, P, S, out_u8=False, temporal_grow=None, frame_ba
     work = []
     for (xc, first), n in zip(clips, sched):
         fl, tout = c4_step_flops(n, first, temporal_grow=temporal_grow)
-        work.append((xc, first, fl, tout))
+        # executed MFMA FLOP: the folded upsample convs do 7/9 of their taps
+        ex = fl - (2.0 / 9.0) * c4_up_flops(n, first) if fold and temporal_grow != "after" else fl
+        work.append((xc, first, fl, tout, ex))
     if temporal_grow:
         name = ("c4tg_decoder_bf16: latent 48x91x90x160 -> conv_in 48->384 -> 3 stages (384/192/96 ch; "
                 "TemporalGrow [1x1x1 projection + causal 3x1x1 temporal conv, 2x time on non-first frames "
@@ -138,6 +157,8 @@ def setup_c4(dev, torch, synth, P, S, out_u8=False, temporal_grow=None, frame_ba
                 "2 residual blocks each) -> head 96->3 at 1440x2560; clips of 7+14x6 latents")
     desc = {"workload": name, "output": "3x361x1440x2560 bf16",
             "step": "one clip (24 output frames; 25 for the first)"}
+    if fold:
+        desc["fold_upsample"] = "upsampling 3x3x3 convs phase-folded (hi/lo bf16 weights, 7/9 of their MFMA work)"
     if frame_batch:
         desc["frame_batch"] = "%d frames of the last stage's input through the last stage and the head" % frame_batch
     if temporal_grow or frame_batch:
@@ -145,26 +166,30 @@ def setup_c4(dev, torch, synth, P, S, out_u8=False, temporal_grow=None, frame_ba
     return plan, work, ring, desc
 
 
-def setup_c3(dev, torch, synth, P, S):
+def setup_c3(dev, torch, synth, P, S, fold=False):
     cin, cmid, cout, h, w = 128, 96, 3, 720, 1280
     w1 = synth.bf16(synth.conv_weight(cmid, cin, 3, 3, 3, synth.seed(3, 10))).to(dev)
     w2 = synth.bf16(synth.conv_weight(cout, cmid, 3, 3, 3, synth.seed(3, 13))).to(dev)
     g2 = synth.gain(cmid, synth.seed(3, 14)).to(dev)
     plan = P.stack_plan(S.upstage_ops(cmid, cout, {"w": w1}, {"w": w2, "g": g2}), cin, h, w, max_chunk_t=4,
-                        device=dev)
+                        device=dev, fold_upsample=fold)
     pool = []
     for k in range(8):  # distinct input chunks, cycled (content does not change the time)
         x = synth.bf16(synth.video(cin, 4, h, w, synth.seed(3, 100 + k)))
         pool.append(x.permute(1, 2, 3, 0).contiguous().to(dev))
     sched = [1] + [4] * 90
-    fl_frame = (conv_flops_per_voxel(cin, cmid) + conv_flops_per_voxel(cmid, cout)) * 1440 * 2560
+    fl_up = conv_flops_per_voxel(cin, cmid) * 1440 * 2560
+    fl_frame = fl_up + conv_flops_per_voxel(cmid, cout) * 1440 * 2560
+    ex_frame = fl_frame - (2.0 / 9.0) * fl_up if fold else fl_frame
     work = []
     for i, n in enumerate(sched):
-        work.append((pool[i % 8][:n], i == 0, fl_frame * n, n))
+        work.append((pool[i % 8][:n], i == 0, fl_frame * n, n, ex_frame * n))
     ring = [torch.empty((4, 1440, 2560, 3), dtype=torch.bfloat16, device=dev) for _ in range(2)]
     desc = {"workload": "c3_stage1440_bf16: 128x720x1280 -> nearest 2x -> conv 128->96 -> RMSNorm+SiLU -> "
                         "conv 96->3 at 1440x2560; 361 frames as 1+90x4 chunks with caches",
             "output": "3x361x1440x2560 bf16", "step": "one 4-frame chunk"}
+    if fold:
+        desc["fold_upsample"] = "the upsampling conv phase-folded (hi/lo bf16 weights, 7/9 of its MFMA work)"
     return plan, work, ring, desc
 
 
@@ -213,7 +238,7 @@ def delivery_rate(torch, plan, work, steps, warmup, dev):
     nbytes = [0]
 
     def clip(i, timed):
-        xc, first, fl, tout = work[i % len(work)]
+        xc, first, fl, tout, _ = work[i % len(work)]
         k = i % 2
         if i >= 2:
             comp.wait_event(copied[k])  # the copy out of this ring slot is done
@@ -304,6 +329,8 @@ def main():
                     help="c4tg: TemporalGrow before (reordered) or after (original) the spatial upsample")
     ap.add_argument("--frame-batch", type=int, default=0,
                     help="c4/c4tg: run the last stage and the head over batches of this many frames (0: whole clips)")
+    ap.add_argument("--fold-upsample", action="store_true",
+                    help="phase-folded upsampling convs (value stays algorithmic; executed FLOP reported)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-delivery", action="store_true",
                     help="skip the host-delivery measurement (c4: output copied to pinned host memory)")
@@ -325,22 +352,23 @@ def main():
     C.lib()
     tg = args.tg_order if args.workload == "c4tg" else None
     if args.workload == "c3":
-        plan, work, ring, desc = setup_c3(dev, torch, synth, P, S)
+        plan, work, ring, desc = setup_c3(dev, torch, synth, P, S, fold=args.fold_upsample)
     else:
-        plan, work, ring, desc = setup_c4(dev, torch, synth, P, S, temporal_grow=tg, frame_batch=args.frame_batch)
+        plan, work, ring, desc = setup_c4(dev, torch, synth, P, S, temporal_grow=tg, frame_batch=args.frame_batch,
+                                          fold=args.fold_upsample)
     stream = torch.cuda.current_stream()
     states = [plan.new_state(), plan.new_state()]
     cur = [0]
 
     def step(i):
-        xc, first, fl, tout = work[i % len(work)]
+        xc, first, fl, tout, ex = work[i % len(work)]
         if first:
             plan.reset(states[cur[0]])
         a, b = states[cur[0]], states[1 - cur[0]]
         y = ring[i % 2][:tout]
         plan.forward_chunk(xc, a, b, y=y)
         cur[0] = 1 - cur[0]
-        return fl, tout
+        return fl, tout, ex
 
     log("warmup %d steps" % args.warmup)
     for i in range(args.warmup):
@@ -351,12 +379,13 @@ def main():
     torch.cuda.synchronize()
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    flops, frames = 0.0, 0
+    flops, frames, executed = 0.0, 0, 0.0
     marks[0].record()
     for i in range(args.warmup, args.warmup + args.steps):
-        fl, tout = step(i)
+        fl, tout, ex = step(i)
         marks[i - args.warmup + 1].record()
         flops += fl
+        executed += ex
         frames += tout
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
@@ -404,14 +433,17 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(dt / args.steps * 1e3, 3), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": desc, "frames_per_s": round(frames / dt, 2), "mfma_frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
+        "config": desc, "frames_per_s": round(frames / dt, 2),
+        "mfma_frac": round(executed / dt / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": roof, "kernels": per_kernel,
         # per-step GPU time between events on the stream (the first clip is the
         # 25-frame one only when it falls in the timed steps)
         "step_ms": {"min": round(step_ms[0], 3), "mean": round(sum(step_ms) / len(step_ms), 3),
                     "p99": round(step_ms[min(len(step_ms) - 1, int(0.99 * len(step_ms)))], 3)},
     }
-    if args.workload == "c4" and not args.no_delivery and not args.frame_batch:
+    if args.fold_upsample:
+        out["executed_tflops"] = round(executed / dt / 1e12, 2)
+    if args.workload == "c4" and not args.no_delivery and not args.frame_batch and not args.fold_upsample:
         # Host delivery: the same decode with every clip's RGB copied to pinned host
         # memory, overlapped with the next clip; bf16 output, then 8-bit codes.
         # PCIe-inclusive, so never the headline value.

@@ -26,7 +26,7 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-I" + os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
-SOURCES = ["conv_bf16.hip", "conv_bf16_v2.hip", "conv_head.hip", "conv_pw.hip", "misc_kernels.hip", "cc3d_api.cpp"]
+SOURCES = ["conv_bf16.hip", "conv_bf16_v2.hip", "conv_head.hip", "conv_pw.hip", "conv_phase.hip", "misc_kernels.hip", "cc3d_api.cpp"]
 
 
 def _compile(src: str) -> str:

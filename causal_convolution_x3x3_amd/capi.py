@@ -32,7 +32,8 @@ EXPORTS = (
 class ConvDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "cin", "cout", "kt", "kh", "kw", "h_in", "w_in", "up_s", "up_t", "max_chunk_t",
-        "dtype", "tpad", "epilogue")] + [("eps", ctypes.c_float), ("grow", ctypes.c_int)]
+        "dtype", "tpad", "epilogue")] + [("eps", ctypes.c_float), ("grow", ctypes.c_int),
+                                         ("fold_upsample", ctypes.c_int)]
 
 
 class State(ctypes.Structure):
@@ -49,7 +50,7 @@ class StackDesc(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int), ("cin", ctypes.c_int), ("h", ctypes.c_int),
                 ("w", ctypes.c_int), ("max_chunk_t", ctypes.c_int), ("eps", ctypes.c_float),
                 ("n_ops", ctypes.c_int), ("ops", ctypes.POINTER(OpDesc)), ("grow", ctypes.c_int),
-                ("batch_from", ctypes.c_int), ("frame_batch", ctypes.c_int)]
+                ("batch_from", ctypes.c_int), ("frame_batch", ctypes.c_int), ("fold_upsample", ctypes.c_int)]
 
 
 class OpProfile(ctypes.Structure):

@@ -186,6 +186,8 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
     if (d->n_ops < 1 || d->n_ops > CC3D_MAX_OPS)
         return fail(CC3D_EINVAL, "n_ops=%d not in [1, %d]", d->n_ops, CC3D_MAX_OPS);
     if (!d->ops) return fail(CC3D_EINVAL, "ops is NULL");
+    if (d->fold_upsample != 0 && d->fold_upsample != 1)
+        return fail(CC3D_EINVAL, "fold_upsample=%d not accepted (0 or 1)", d->fold_upsample);
     if (d->grow != CC3D_GROW_ONCE && d->grow != CC3D_GROW_ALIGNED)
         return fail(CC3D_EINVAL, "grow=%d not accepted (0 = CC3D_GROW_ONCE, 1 = CC3D_GROW_ALIGNED)", d->grow);
     const bool bf16 = d->dtype == CC3D_BF16;
@@ -295,7 +297,8 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
                 cc3d::bf16_conv_tiling(o.cout, &r.ntile, &r.nblocks);
                 r.kchunks = (r.cin + 31) / 32;
                 const int plain = o.act_out == CC3D_SLOT_NONE && !o.out_u8;
-                r.family = cc3d::bf16_conv_family(o.cout, r.cin, o.kt, o.kh, o.kw, o.up_s, plain);
+                r.family = cc3d::bf16_conv_family(o.cout, r.cin, o.kt, o.kh, o.kw, o.up_s, plain,
+                                                  d->fold_upsample && !o.out_u8);
                 if (r.family == 4) cc3d::pw_conv_tiling(o.cout, &r.ntile, &r.nblocks);
             }
         } else {
@@ -636,6 +639,8 @@ std::string conv_kernel_name(const cc3d_plan* p, const OpRt& r)
     char buf[64];
     if (p->dtype == CC3D_BF16 && r.family == 3)
         snprintf(buf, sizeof buf, "conv_bf16_head_up%d_k%d_c%d", r.up_s, r.kh, r.cout);
+    else if (p->dtype == CC3D_BF16 && r.family == 5)
+        snprintf(buf, sizeof buf, "conv_bf16_phase_up%d_k%d_n%d", r.up_s, r.kh, r.ntile);
     else if (p->dtype == CC3D_BF16 && r.family == 4)
         snprintf(buf, sizeof buf, "conv_bf16_pw_up%d_kt%d_n%d", r.up_s, r.kt, r.ntile);
     else if (p->dtype == CC3D_BF16)
@@ -697,6 +702,7 @@ cc3d_status cc3d_plan_create(const cc3d_conv_desc* d, const void* w, const float
     sd.max_chunk_t = d->max_chunk_t;
     sd.eps = d->eps;
     sd.grow = d->grow;
+    sd.fold_upsample = d->fold_upsample;
     sd.n_ops = 1;
     sd.ops = &op;
     return create_common(&sd, stream, out);

@@ -37,7 +37,7 @@ struct ConvArgs {
     int h_in, w_in, up_s, h_out, w_out, t_out;
     int kchunks;          // bf16: ceil(cin / 32)
     int ntile, nblocks;   // bf16: output channels per workgroup, number of such blocks
-    int family;           // bf16: kernel family (1 to 4) the weights were packed for
+    int family;           // bf16: kernel family (1 to 5) the weights were packed for
     int rot_taps;         // bf16 v2 and pointwise: rotate the temporal-tap order by the output frame
     int t_rot0;           // ... counted from this frame (the launch's first frame in its chunk)
     int out_u8;           // bf16 families 1 and 3: out holds 8-bit codes of the fp32 result
@@ -75,11 +75,12 @@ hipError_t launch_pack_bf16(const void* w, void* wpk, int cout, int cin, int kt,
 // output blocks; their weights are packed with the column tap outermost.
 bool v2_conv_applies(int ntile, int kh, int kw, int up_s);
 // Kernel family chosen for a bf16 conv: 3 = the output head (conv_head.hip)
-// where it applies, 2 = v2 where it applies, 4 = the pointwise kernel
-// (conv_pw.hip) for 1x1 spatial kernels whose epilogue is plain (no act, no
-// 8-bit output: `plain` != 0), else 1.  CC3D_CONV_FAMILY=1 in the environment at
-// plan creation keeps every conv on v1.
-int bf16_conv_family(int cout, int cin, int kt, int kh, int kw, int up_s, int plain);
+// where it applies, 5 = the phase-decomposed upsample conv (conv_phase.hip)
+// where it applies and `fold` != 0, 2 = v2 where it applies, 4 = the pointwise
+// kernel (conv_pw.hip) for 1x1 spatial kernels whose epilogue is plain (no act,
+// no 8-bit output: `plain` != 0), else 1.  CC3D_CONV_FAMILY=1 in the environment
+// at plan creation keeps every conv on v1.
+int bf16_conv_family(int cout, int cin, int kt, int kh, int kw, int up_s, int plain, int fold);
 hipError_t launch_conv_bf16_v2(const ConvArgs& a, hipStream_t s);
 
 // Output head (conv_head.hip): 3x3x3 conv to at most 3 channels, of a nearest-2x
@@ -98,6 +99,13 @@ void pw_conv_tiling(int cout, int* ntile, int* nblocks);
 size_t pw_packed_elems(int cout, int cin, int kt);
 hipError_t launch_pack_pw(const void* w, void* wpk, int cout, int cin, int kt, hipStream_t s);
 hipError_t launch_conv_pw(const ConvArgs& a, hipStream_t s);
+
+// Phase-decomposed upsample conv (conv_phase.hip): 3x3 spatial, up_s = 2,
+// 96-channel blocks; weights folded per output phase into hi/lo bf16 pairs.
+bool phase_conv_applies(int ntile, int kh, int kw, int up_s);
+size_t phase_packed_elems(int cout, int cin, int kt);
+hipError_t launch_pack_phase(const void* w, void* wpk, int cout, int cin, int kt, hipStream_t s);
+hipError_t launch_conv_phase(const ConvArgs& a, hipStream_t s);
 
 // fp32 direct conv (weights used in PyTorch order, copied by the host).
 hipError_t launch_conv_f32(const ConvArgs& a, hipStream_t s);

@@ -293,7 +293,7 @@ void bf16_conv_tiling(int cout, int* ntile, int* nblocks)
     *nblocks = nt ? (cout + nt - 1) / nt : 0;
 }
 
-int bf16_conv_family(int cout, int cin, int kt, int kh, int kw, int up_s, int plain)
+int bf16_conv_family(int cout, int cin, int kt, int kh, int kw, int up_s, int plain, int fold)
 {
     const char* e = getenv("CC3D_CONV_FAMILY");
     if (e && atoi(e) == 1) return 1;
@@ -301,6 +301,7 @@ int bf16_conv_family(int cout, int cin, int kt, int kh, int kw, int up_s, int pl
     if (plain && pw_conv_applies(cout, kh, kw, up_s)) return 4;
     int nt, nb;
     bf16_conv_tiling(cout, &nt, &nb);
+    if (fold && phase_conv_applies(nt, kh, kw, up_s)) return 5;
     return v2_conv_applies(nt, kh, kw, up_s) ? 2 : 1;
 }
 
@@ -308,6 +309,7 @@ size_t bf16_packed_elems(int cout, int cin, int kt, int kh, int kw, int family)
 {
     if (family == 3) return head_packed_elems(cin);
     if (family == 4) return pw_packed_elems(cout, cin, kt);
+    if (family == 5) return phase_packed_elems(cout, cin, kt);
     int nt, nb;
     bf16_conv_tiling(cout, &nt, &nb);
     const int kchunks = (cin + 31) / 32;
@@ -319,6 +321,7 @@ hipError_t launch_pack_bf16(const void* w, void* wpk, int cout, int cin, int kt,
 {
     if (family == 3) return launch_pack_head(w, wpk, cout, cin, s);
     if (family == 4) return launch_pack_pw(w, wpk, cout, cin, kt, s);
+    if (family == 5) return launch_pack_phase(w, wpk, cout, cin, kt, s);
     int nt, nb;
     bf16_conv_tiling(cout, &nt, &nb);
     const int kchunks = (cin + 31) / 32;
@@ -336,6 +339,7 @@ hipError_t launch_conv_bf16(const ConvArgs& a, hipStream_t s)
     if (a.kh != a.kw) return hipErrorInvalidValue;
     if (a.family == 3) return launch_conv_head(a, s);
     if (a.family == 4) return launch_conv_pw(a, s);
+    if (a.family == 5) return launch_conv_phase(a, s);
     if (a.family == 2) return launch_conv_bf16_v2(a, s);
     if (a.up_s == 1 && a.kh == 3) return launch_nf<1, 3>(a, s);
     if (a.up_s == 2 && a.kh == 3) return launch_nf<2, 3>(a, s);

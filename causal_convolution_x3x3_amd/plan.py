@@ -155,14 +155,16 @@ class Plan:
 
 def conv_plan(w: torch.Tensor, h_in: int, w_in: int, *, bias=None, gamma=None, up_s=1, up_t=1,
               max_chunk_t=8, tpad=C.TPAD_REPLICATE, residual=False, act=False, out_u8=False, eps=1e-6,
-              aligned=False, stream=None) -> Plan:
+              aligned=False, fold_upsample=False, stream=None) -> Plan:
     """Plan for one causal conv; w is [Cout][Cin][kt][kh][kw] on the GPU (bf16 or fp32).
-    ``aligned``: the first chunk doubles every frame at up_t = 2 (CC3D_GROW_ALIGNED)."""
+    ``aligned``: the first chunk doubles every frame at up_t = 2 (CC3D_GROW_ALIGNED).
+    ``fold_upsample``: phase-folded kernel for an upsampling 3x3 conv where it applies."""
     cout, cin, kt, kh, kw = w.shape
     d = C.ConvDesc(cin=cin, cout=cout, kt=kt, kh=kh, kw=kw, h_in=h_in, w_in=w_in, up_s=up_s, up_t=up_t,
                    max_chunk_t=max_chunk_t, dtype=_DT[w.dtype], tpad=tpad,
                    epilogue=(C.EPI_RESIDUAL if residual else 0) | (C.EPI_ACT if act else 0) |
-                   (C.EPI_U8 if out_u8 else 0), eps=eps, grow=C.GROW_ALIGNED if aligned else C.GROW_ONCE)
+                   (C.EPI_U8 if out_u8 else 0), eps=eps, grow=C.GROW_ALIGNED if aligned else C.GROW_ONCE,
+                   fold_upsample=int(fold_upsample))
     h = ctypes.c_void_p()
     with torch.cuda.device(w.device):
         C.check(C.lib().cc3d_plan_create(ctypes.byref(d), _ptr(w), _ptr(bias), _ptr(gamma), _stream(stream),
@@ -191,10 +193,12 @@ def _check_weights(ops: List[Op], cin: int):
 
 
 def stack_plan(ops: List[Op], cin: int, h: int, w: int, *, dtype=torch.bfloat16, max_chunk_t=8,
-               eps=1e-6, aligned=False, batch_from=0, frame_batch=0, device=None, stream=None) -> Plan:
+               eps=1e-6, aligned=False, batch_from=0, frame_batch=0, fold_upsample=False, device=None,
+               stream=None) -> Plan:
     """Plan for an op list; ``aligned`` as in conv_plan, for every up_t = 2 op.
     ``frame_batch`` > 0: ops[batch_from:] run in batches of that many frames of
-    their input (frame batching, see cc3d_stack_desc)."""
+    their input (frame batching, see cc3d_stack_desc).  ``fold_upsample``: the
+    phase-folded kernel for every upsampling 3x3 conv it applies to."""
     _check_weights(ops, cin)
     arr = (C.OpDesc * len(ops))()
     for i, o in enumerate(ops):
@@ -204,7 +208,7 @@ def stack_plan(ops: List[Op], cin: int, h: int, w: int, *, dtype=torch.bfloat16,
                           w=_ptr(o.w), bias=_ptr(o.bias), gamma=_ptr(o.gamma), out_u8=int(o.out_u8))
     d = C.StackDesc(dtype=_DT[dtype], cin=cin, h=h, w=w, max_chunk_t=max_chunk_t, eps=eps, n_ops=len(ops),
                     ops=arr, grow=C.GROW_ALIGNED if aligned else C.GROW_ONCE, batch_from=batch_from,
-                    frame_batch=frame_batch)
+                    frame_batch=frame_batch, fold_upsample=int(fold_upsample))
     if device is None:
         device = next((o.w.device for o in ops if o.w is not None), torch.device("cuda", 0))
     hnd = ctypes.c_void_p()

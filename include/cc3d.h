@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define CC3D_VERSION 103 /* 1.0.3: frame-batched group execution */
+#define CC3D_VERSION 104 /* 1.0.4: phase-folded upsample convs */
 
 typedef enum {
     CC3D_OK = 0,
@@ -129,6 +129,7 @@ typedef struct {
     int epilogue;         /* CC3D_EPI_* flags */
     float eps;            /* RMSNorm epsilon (CC3D_EPI_ACT) */
     int grow;             /* cc3d_grow (first chunk at up_t = 2) */
+    int fold_upsample;    /* 1: phase-folded upsample conv where it applies (see below) */
 } cc3d_conv_desc;
 
 typedef struct cc3d_plan cc3d_plan;
@@ -196,7 +197,19 @@ typedef struct {
     int grow;           /* cc3d_grow for every up_t = 2 conv of the stack */
     int batch_from;     /* frame batching (see below): first op of the group */
     int frame_batch;    /* frames per batch of the group input; 0 = off */
+    int fold_upsample;  /* 1: phase-folded upsample convs where they apply (see below) */
 } cc3d_stack_desc;
+
+/* Phase-folded upsample convs (fold_upsample = 1; bf16, 3x3 spatial kernels with
+ * up_s = 2 whose output channels are taken in 96-channel blocks, not with 8-bit
+ * output).  Nearest 2x upsampling followed by a 3x3 conv is, at each output
+ * phase (y & 1, x & 1), a 2x2 conv of the source image (the taps that read the
+ * same source pixel are summed first; the SwiftVR page's "compute once, then
+ * copy" reasoning, section "TemporalGrow: Compute Before Spatial Upsampling",
+ * applied to the weights).  Each folded weight is kept as a bf16 hi/lo pair
+ * (about 2^-17 relative), so the result equals the conv up to fp32 rounding while
+ * the executed MFMA work is 7/9 of the definition's; profiling still reports the
+ * definition's (algorithmic) FLOP. */
 
 /* Frame batching (LightX2V blog "SwiftVR Inference Optimization ...", section
  * "ReAE Frame Batching": a small batch of frames passes through a whole group of

@@ -24,7 +24,7 @@ def test_library_exports_every_declared_function():
     assert sorted(declared) == sorted(C.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.cc3d_version() == 103
+    assert L.cc3d_version() == 104
 
 
 def _conv_desc(**kw):
@@ -42,7 +42,7 @@ DUMMY = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
     (dict(up_t=0), C.ESHAPE), (dict(dtype=7), C.EDTYPE), (dict(tpad=5), C.EINVAL), (dict(cin=12), C.ESHAPE),
     (dict(max_chunk_t=0), C.ESHAPE), (dict(h_in=0), C.ESHAPE), (dict(cout=0), C.ESHAPE),
     (dict(epilogue=8), C.EINVAL), (dict(epilogue=C.EPI_ACT | C.EPI_U8), C.EINVAL), (dict(kh=3, kw=1), C.ESHAPE), (dict(eps=-1.0), C.EINVAL),
-    (dict(grow=2), C.EINVAL), (dict(grow=-1), C.EINVAL),
+    (dict(grow=2), C.EINVAL), (dict(grow=-1), C.EINVAL), (dict(fold_upsample=2), C.EINVAL),
     (dict(cin=384, h_in=1440, w_in=1942), C.ESHAPE),  # 2^30 elements per input frame or more
 ])
 def test_plan_create_rejects_bad_descriptor(bad, status):

@@ -135,6 +135,59 @@ def test_bf16_pointwise_conv_residual(k, up_s):
     assert_bf16_close(got, ref, "pointwise + residual")
 
 
+PHASE_CASES = [
+    # cin, cout, up_t, h, w, splits, tpad, bias: ragged tiles, temporal growth,
+    # zero history, two and four 96-channel blocks
+    (192, 96, 1, 10, 70, [1, 2], C.TPAD_REPLICATE, True),
+    (128, 96, 2, 9, 40, [1, 2, 1], C.TPAD_ZERO, False),
+    (96, 192, 1, 7, 130, [2, 1], C.TPAD_REPLICATE, True),
+    (384, 384, 2, 5, 6, [1, 1], C.TPAD_REPLICATE, False),
+]
+
+
+@pytest.mark.parametrize("case", PHASE_CASES, ids=lambda c: "ci%d_co%d_ut%d" % c[:3])
+def test_phase_folded_upsample_conv(case):
+    """fold_upsample: the nearest-2x 3x3x3 conv computed per output phase from
+    folded hi/lo weights (7/9 of the MFMA work) matches the definition."""
+    cin, cout, up_t, h, w, splits, tpad, with_bias = case
+    say("phase-folded upsample conv %s" % (case,))
+    x = synth.bf16(synth.video(cin, sum(splits), h, w, synth.seed(13, 1)))
+    wt = synth.bf16(synth.conv_weight(cout, cin, 3, 3, 3, synth.seed(13, 2)))
+    b = synth.bias(cout, synth.seed(13, 3)) if with_bias else None
+    ref = O.one_shot(to_oracle(x), to_oracle(wt), None if b is None else to_oracle(b), TP[tpad], 2, up_t)
+    plan = P.conv_plan(wt.cuda(), h, w, bias=None if b is None else b.cuda(), up_s=2, up_t=up_t,
+                       max_chunk_t=max(splits), tpad=tpad, fold_upsample=True)
+    C.check(C.lib().cc3d_profile_enable(plan._h, 1), "profile_enable")
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits))
+    pr = C.OpProfile()
+    C.check(C.lib().cc3d_profile_read(plan._h, 0, 0, ctypes.byref(pr)), "profile_read")
+    assert pr.kernel.decode() == "conv_bf16_phase_up2_k3_n96", pr.kernel
+    assert_bf16_close(got, ref, "phase-folded conv")
+
+
+@pytest.mark.parametrize("residual", [False, True])
+def test_phase_folded_conv_fused_act(residual):
+    """The phase kernel's epilogue: bias (+ residual) stored as bf16 and the
+    fused SiLU(RMSNorm(.)) of the stored value."""
+    say("phase-folded conv, fused act, residual=%s" % residual)
+    cin, cout, h, w, splits = 64, 96, 9, 30, [1, 2]
+    t = sum(splits)
+    x = synth.bf16(synth.video(cin, t, h, w, synth.seed(13, 11)))
+    wt = synth.bf16(synth.conv_weight(cout, cin, 3, 3, 3, synth.seed(13, 12)))
+    b = synth.bias(cout, synth.seed(13, 13))
+    g = synth.gain(cout, synth.seed(13, 14))
+    r = synth.bf16(synth.video(cout, t, 2 * h, 2 * w, synth.seed(13, 15))) if residual else None
+    v = O.one_shot(to_oracle(x), to_oracle(wt), to_oracle(b), O.REPLICATE, 2)
+    if residual:
+        v = v + to_oracle(r)
+    ref = O.act(O.round_bf16(v), to_oracle(g), 1e-6)
+    plan = P.conv_plan(wt.cuda(), h, w, bias=b.cuda(), gamma=g.cuda(), act=True, residual=residual, up_s=2,
+                       max_chunk_t=2, fold_upsample=True)
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits,
+                                     residual_cl=to_device_cl(r) if residual else None))
+    assert_bf16_close(got, ref, "phase-folded epilogue")
+
+
 def test_fp32_conv_aligned_growth():
     """The fp32 kernel under CC3D_GROW_ALIGNED, against the oracle to the fp32 bound."""
     say("fp32 conv aligned growth")
@@ -323,7 +376,7 @@ def test_upstage_small(cfg, cin, cmid, cout):
 
 
 def _decoder_layerwise(c_latent, stages, t, h, w, splits, cfg=4, temporal_grow=None, aligned=False,
-                       keep_slots=False):
+                       keep_slots=False, fold_upsample=False):
     """Run the decoder twice on the GPU -- production slot wiring and the
     unique-slot wiring -- and check (1) both give bitwise identical outputs,
     (2) every layer of the unique-slot run against the oracle fed that layer's
@@ -336,9 +389,10 @@ def _decoder_layerwise(c_latent, stages, t, h, w, splits, cfg=4, temporal_grow=N
     x = synth.bf16(synth.video(c_latent, t, h, w, synth.seed(cfg, 1)))
     x_cl = to_device_cl(x)
     ops_u = S.decoder_ops(dev, stages=stages, unique_slots=True, temporal_grow=temporal_grow)
-    plan_u = P.stack_plan(ops_u, c_latent, h, w, max_chunk_t=max(splits), aligned=aligned)
+    plan_u = P.stack_plan(ops_u, c_latent, h, w, max_chunk_t=max(splits), aligned=aligned,
+                          fold_upsample=fold_upsample)
     plan_p = P.stack_plan(S.decoder_ops(dev, stages=stages, temporal_grow=temporal_grow), c_latent, h, w,
-                          max_chunk_t=max(splits), aligned=aligned)
+                          max_chunk_t=max(splits), aligned=aligned, fold_upsample=fold_upsample)
     su, sp = P.Stream(plan_u), P.Stream(plan_p)
     layer = {i: O.CausalConvStream(cpu[o.name]["w"], cpu[o.name]["b"], O.REPLICATE, o.up_s, o.up_t,
                                    aligned=aligned)
@@ -401,12 +455,13 @@ def test_decoder_small_channels():
     assert_stack_close(got, ref, "decoder small")
 
 
-@pytest.mark.parametrize("aligned", [False, True])
-def test_decoder_full_channels_tiny_frame(aligned):
+@pytest.mark.parametrize("aligned,fold", [(False, False), (True, False), (False, True)])
+def test_decoder_full_channels_tiny_frame(aligned, fold):
     """Full channel counts (the register-blocked kernels and the head), both
-    first-chunk growth rules."""
-    say("decoder full channels tiny frame, aligned=%s" % aligned)
-    got, ref, _ = _decoder_layerwise(48, OM.DECODER_STAGES, t=5, h=2, w=3, splits=[3, 2], aligned=aligned)
+    first-chunk growth rules, and the phase-folded upsample convs."""
+    say("decoder full channels tiny frame, aligned=%s fold=%s" % (aligned, fold))
+    got, ref, _ = _decoder_layerwise(48, OM.DECODER_STAGES, t=5, h=2, w=3, splits=[3, 2], aligned=aligned,
+                                     fold_upsample=fold)
     assert got.shape == (3, OM.output_frames(5, aligned=aligned), 32, 48)
     assert_stack_close(got, ref, "decoder full channels")
 
