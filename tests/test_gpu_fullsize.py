@@ -120,9 +120,9 @@ def check_norm(src, act, gamma, ts, rows, cols, res=None, out=None, tallies=None
         tallies["act"].add(_gather(act, ts, y, cols), O.act(v.T, gamma, EPS).T)
 
 
-def run_stack_sampled(ops, params_cpu, x_cl, cin, h, w, splits, seed, max_pts_rows=8):
+def run_stack_sampled(ops, params_cpu, x_cl, cin, h, w, splits, seed, max_pts_rows=8, fold_upsample=False):
     """Run `ops` chunk by chunk and check every op on sampled positions."""
-    plan = P.stack_plan(ops, cin, h, w, max_chunk_t=max(splits))
+    plan = P.stack_plan(ops, cin, h, w, max_chunk_t=max(splits), fold_upsample=fold_upsample)
     st = P.Stream(plan)
     wins = {i: Window(o.k[0], o.up_t) for i, o in enumerate(ops) if o.kind == C.OP_CONV}
     rng = np.random.RandomState(seed)
@@ -254,11 +254,13 @@ def test_c2_stage1080_fullsize_sampled():
                       seed=202)
 
 
-def test_c3_stage1440_fullsize_sampled():
+@pytest.mark.parametrize("fold", [False, True])
+def test_c3_stage1440_fullsize_sampled(fold):
     """128 channels at 720x1280 -> nearest 2x -> conv 128->96 -> act -> conv 96->3
-    at 2560x1440: the stream's first chunk (1 frame) and the two after it."""
+    at 2560x1440: the stream's first chunk (1 frame) and the two after it; with
+    `fold`, the upsampling conv phase-folded."""
     wl = synth.WORKLOADS[3]
-    say("full size c3: %s" % wl)
+    say("full size c3 (fold=%s): %s" % (fold, wl))
     d1, c1 = _param_pair(wl["cmid"], wl["cin"], 3, 0, False)
     d2, c2 = _param_pair(wl["cout"], wl["cmid"], 3, 1, True)
     ops = S.upstage_ops(wl["cmid"], wl["cout"], d1, d2)
@@ -269,7 +271,7 @@ def test_c3_stage1440_fullsize_sampled():
     x = synth.bf16(synth.video(wl["cin"], sum(splits), wl["h"], wl["w"], synth.seed(3, 1)))
     x_cl = x.permute(1, 2, 3, 0).contiguous().cuda()
     del x
-    run_stack_sampled(ops, cpu, x_cl, wl["cin"], wl["h"], wl["w"], splits, seed=303)
+    run_stack_sampled(ops, cpu, x_cl, wl["cin"], wl["h"], wl["w"], splits, seed=303, fold_upsample=fold)
 
 
 def test_c4tg_decoder_fullsize_sampled():
