@@ -27,8 +27,9 @@ Prints one JSON line: value = algorithmic conv TFLOP/s (2*Cin*Cout*27 FLOP per
 output voxel of every conv) over the timed steps; plus output frames/s, the
 dominant kernel's roofline (live HIP-event timing on the plan's stream), the
 host-delivery rate (c4: every clip's output copied to pinned host memory on a
-second stream, bf16 and 8-bit; never the headline value) and the CPU oracle's
-rate on a bounded sample of the same workload.
+second stream, bf16 and 8-bit; never the headline value), the phase-folded
+decode's frames/s and executed MFMA rate (c4: fold_upsample) and the CPU
+oracle's rate on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -218,6 +219,44 @@ def recorded_traffic(kernel_name):
     return None
 
 
+def timed_decode(torch, plan, work, ring, steps, warmup, before_timed=None):
+    """Decode `warmup` clips untimed, then time `steps` clips (inputs resident,
+    outputs to the device ring).  Returns (seconds, algorithmic FLOP, frames,
+    executed MFMA FLOP, sorted per-step GPU ms)."""
+    states = [plan.new_state(), plan.new_state()]
+    cur = [0]
+
+    def step(i):
+        xc, first, fl, tout, ex = work[i % len(work)]
+        if first:
+            plan.reset(states[cur[0]])
+        a, b = states[cur[0]], states[1 - cur[0]]
+        plan.forward_chunk(xc, a, b, y=ring[i % 2][:tout])
+        cur[0] = 1 - cur[0]
+        return fl, tout, ex
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if before_timed:
+        before_timed()
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    flops, frames, executed = 0.0, 0, 0.0
+    marks[0].record()
+    for i in range(warmup, warmup + steps):
+        fl, tout, ex = step(i)
+        marks[i - warmup + 1].record()
+        flops += fl
+        executed += ex
+        frames += tout
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    step_ms = sorted(marks[k].elapsed_time(marks[k + 1]) for k in range(steps))
+    return dt, flops, frames, executed, step_ms
+
+
 def delivery_rate(torch, plan, work, steps, warmup, dev):
     """Frames/s of the decode with every clip's output copied to pinned host
     memory on a second stream (the SwiftVR page's overlap of output transfer with
@@ -356,40 +395,10 @@ def main():
     else:
         plan, work, ring, desc = setup_c4(dev, torch, synth, P, S, temporal_grow=tg, frame_batch=args.frame_batch,
                                           fold=args.fold_upsample)
-    stream = torch.cuda.current_stream()
-    states = [plan.new_state(), plan.new_state()]
-    cur = [0]
-
-    def step(i):
-        xc, first, fl, tout, ex = work[i % len(work)]
-        if first:
-            plan.reset(states[cur[0]])
-        a, b = states[cur[0]], states[1 - cur[0]]
-        y = ring[i % 2][:tout]
-        plan.forward_chunk(xc, a, b, y=y)
-        cur[0] = 1 - cur[0]
-        return fl, tout, ex
-
-    log("warmup %d steps" % args.warmup)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    C.check(C.lib().cc3d_profile_enable(plan._h, 1), "profile_enable")
-    log("timing %d steps" % args.steps)
-    torch.cuda.synchronize()
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    t0 = time.perf_counter()
-    flops, frames, executed = 0.0, 0, 0.0
-    marks[0].record()
-    for i in range(args.warmup, args.warmup + args.steps):
-        fl, tout, ex = step(i)
-        marks[i - args.warmup + 1].record()
-        flops += fl
-        executed += ex
-        frames += tout
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    step_ms = sorted(marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps))
+    log("warmup %d steps, timing %d steps" % (args.warmup, args.steps))
+    dt, flops, frames, executed, step_ms = timed_decode(
+        torch, plan, work, ring, args.steps, args.warmup,
+        before_timed=lambda: C.check(C.lib().cc3d_profile_enable(plan._h, 1), "profile_enable"))
     log("timed %.3f s" % dt)
 
     # per-kernel event totals over the timed region
@@ -459,6 +468,17 @@ def main():
             deliv[out_dtype_names[u8]] = {"frames_per_s": round(fps, 2), "copy_gbs": round(gbs, 1),
                                           "bytes_per_clip": per_clip}
         out["delivery"] = deliv
+        # The same decode with the upsampling convs phase-folded (7/9 of their MFMA
+        # work, results equal to the definition up to fp32 rounding): frames/s and
+        # the MFMA work actually done; the headline value stays the exact path's.
+        del plan
+        torch.cuda.empty_cache()
+        plan, work, ring, _ = setup_c4(dev, torch, synth, P, S, fold=True)
+        log("phase-folded upsample convs")
+        fdt, _, fframes, fexec, fstep = timed_decode(torch, plan, work, ring, args.steps, args.warmup)
+        out["fold_upsample"] = {"frames_per_s": round(fframes / fdt, 2), "ms_per_step": round(fdt / args.steps * 1e3, 3),
+                                "executed_tflops": round(fexec / fdt / 1e12, 2),
+                                "mfma_frac": round(fexec / fdt / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
         out["cpu_baseline"] = cpu_baseline(args.workload, tg)
