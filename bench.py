@@ -16,8 +16,9 @@ available):
   --frame-batch B (c4, c4tg): the last stage and the head run over batches of B
       frames of their input (frame batching); reports the plan's device memory.
   --fold-upsample: the upsampling 3x3x3 convs run phase-folded (7/9 of their MFMA
-      work); value stays the definition's FLOP rate, executed_tflops and
-      mfma_frac count the MFMA work actually done.
+      work; about 16/27 where the conv also doubles time); value stays the
+      definition's FLOP rate, executed_tflops and mfma_frac count the MFMA work
+      actually done.
   c3: the 1440p output stage, 128 ch x 720x1280 -> nearest 2x -> conv 128->96 ->
       RMSNorm+SiLU -> conv 96->3, 361 frames streamed as 1 + 90 chunks of 4.
       One step = one chunk.
@@ -108,16 +109,45 @@ def c4_step_flops(t_lat, first, h=90, w=160, temporal_grow=None):
     return f, t
 
 
-def c4_up_flops(t_lat, first, h=90, w=160):
-    """Algorithmic FLOP of the three upsampling convs (up_s = 2) of one clip."""
-    f, t, cin = 0.0, t_lat, 384
+def folded_up_units(t_in, first, up_t):
+    """MFMA work of one phase-folded upsampling 3x3x3 conv (replicate history, the
+    default growth rule) for t_in input frames, in units of one spatial tap per
+    output pixel (27 per frame unfolded).  Per output frame and temporal tap: 7
+    (four folded offsets, a hi each, a lo for the three that sum several taps).
+    A conv that doubles time groups the taps that read one input frame: 8 per
+    group (every lo applied)."""
+    if up_t == 1:
+        return 21 * t_in
+    ts = 1 if first else 0  # V[u] = X[(u + ts) // 2]
+    t_v = 2 * t_in - ts
+
+    def frame(zi):  # what window frame zi reads: a cache slot or an input frame
+        if zi < 2:
+            return ("x", 0) if first else ("cache", zi)
+        return ("x", (zi - 2 + ts) >> 1)
+    units = 0
+    for t in range(t_v):
+        z = [frame(t + k) for k in range(3)]
+        units += 8 * (1 + (z[1] != z[0]) + (z[2] != z[1]))
+    return units
+
+
+def c4_up_flops(t_lat, first, h=90, w=160, grown_in_conv=True):
+    """(algorithmic, executed-when-phase-folded) FLOP of the three upsampling convs
+    (up_s = 2) of one clip; grown_in_conv False: the time growth happened before
+    them (a TemporalGrow), so they see the grown frame count with up_t = 1."""
+    f, ex, t, cin = 0.0, 0.0, t_lat, 384
     for c, up_t in ((384, 2), (192, 2), (96, 1)):
         h, w = 2 * h, 2 * w
+        t_in = t
         if up_t == 2:
             t = grown(t, first)
-        f += conv_flops_per_voxel(cin, c) * t * h * w
+        per_frame = conv_flops_per_voxel(cin, c) * h * w
+        f += per_frame * t
+        units = folded_up_units(t_in, first, up_t) if grown_in_conv else 21 * t
+        ex += per_frame / 27.0 * units
         cin = c
-    return f
+    return f, ex
 
 
 def setup_c4(dev, torch, synth, P, S, out_u8=False, temporal_grow=None, frame_batch=0, fold=False):
@@ -143,8 +173,10 @@ def setup_c4(dev, torch, synth, P, S, out_u8=False, temporal_grow=None, frame_ba
     work = []
     for (xc, first), n in zip(clips, sched):
         fl, tout = c4_step_flops(n, first, temporal_grow=temporal_grow)
-        # executed MFMA FLOP: the folded upsample convs do 7/9 of their taps
-        ex = fl - (2.0 / 9.0) * c4_up_flops(n, first) if fold and temporal_grow != "after" else fl
+        ex = fl
+        if fold and temporal_grow != "after":  # executed MFMA FLOP of the folded upsample convs
+            up, up_ex = c4_up_flops(n, first, grown_in_conv=not temporal_grow)
+            ex = fl - up + up_ex
         work.append((xc, first, fl, tout, ex))
     if temporal_grow:
         name = ("c4tg_decoder_bf16: latent 48x91x90x160 -> conv_in 48->384 -> 3 stages (384/192/96 ch; "
@@ -159,7 +191,8 @@ def setup_c4(dev, torch, synth, P, S, out_u8=False, temporal_grow=None, frame_ba
     desc = {"workload": name, "output": "3x361x1440x2560 bf16",
             "step": "one clip (24 output frames; 25 for the first)"}
     if fold:
-        desc["fold_upsample"] = "upsampling 3x3x3 convs phase-folded (hi/lo bf16 weights, 7/9 of their MFMA work)"
+        desc["fold_upsample"] = ("upsampling 3x3x3 convs phase-folded (hi/lo bf16 weights; 7/9 of their MFMA work, "
+                                 "about 16/27 where time doubles)")
     if frame_batch:
         desc["frame_batch"] = "%d frames of the last stage's input through the last stage and the head" % frame_batch
     if temporal_grow or frame_batch:

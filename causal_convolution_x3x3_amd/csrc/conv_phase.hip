@@ -12,11 +12,22 @@
 // 7/9 of the MFMA work of the definition, with results equal to it up to fp32
 // rounding.
 //
+// The same holds in time: where two or three temporal taps of an output frame
+// read the same input frame of the causal window (the nearest 2x temporal
+// growth repeats every frame; a first chunk's history repeats its first frame),
+// which the window's frame pointers show, their weights are summed too.  Weights
+// are packed for every tap alone, for the pairs (0, 1) and (1, 2) and for the
+// three together; each work item groups its taps by frame and walks the groups.
+// A group of several taps makes every lo non-zero, so the grouping variant
+// (launched for convs that double the frame count, where nearly every output
+// frame has one pair and one single tap) applies all eight operands per group:
+// 16 of the 27 operand applications per output pixel instead of 21.
+//
 // The kernel is the register-blocked conv of conv_bf16_v2.hip at the source
 // resolution (RH source rows x 64 source columns per workgroup, 8 waves: 4
 // along M, 2 along N), with one output phase per work item: work items are
 // (tile, frame, channel block, phase), phase fastest, so the four phases of a
-// tile read the same input tile from L2.  A K step (temporal tap, 32 channels)
+// tile read the same input tile from L2.  A K step (temporal group, 32 channels)
 // has two sub-steps, one per source column offset, each applying up to four
 // operands (hi and lo of the two row offsets) to the LDS rows of the tile.
 // Staging (buffer loads straight into LDS, one step ahead for the tile, one
@@ -104,7 +115,22 @@ __host__ __device__ constexpr int fold_count(int ph, int k) { return (k == ph) ?
 
 constexpr int NOP = 4;  // operands per sub-step: hi and lo of the two row offsets
 
-template <int NF, int RH>
+// Temporal weight sets: taps 0 .. kt-1 alone, then (kt = 2) the pair (0, 1), or
+// (kt = 3) the pairs (0, 1) and (1, 2) and the triple (0, 1, 2).
+__host__ __device__ constexpr int num_wsets(int kt) { return kt == 3 ? 6 : (kt == 2 ? 3 : 1); }
+__host__ __device__ inline void wset_taps(int kt, int w, int& a0, int& a1)
+{
+    a0 = a1 = w;
+    if (w < kt) return;
+    if (kt == 2) { a0 = 0; a1 = 1; return; }
+    if (w == 3) { a0 = 0; a1 = 1; }
+    else if (w == 4) { a0 = 1; a1 = 2; }
+    else { a0 = 0; a1 = 2; }
+}
+
+// TF: group temporal taps that read the same frame (launched for convs that grow
+// time; without it every tap is its own group and no branch is compiled in).
+template <int NF, int RH, bool TF>
 __global__ __launch_bounds__(512, 1) void conv_phase_kernel(ConvArgs a)
 {
     constexpr int WN = 2, NT = 512;
@@ -146,11 +172,31 @@ __global__ __launch_bounds__(512, 1) void conv_phase_kernel(ConvArgs a)
     const int wm = wave & 3, wn = wave >> 2;
     const int g = lane >> 4, k16 = lane & 15;
 
-    const int nsteps = a.kt * a.kchunks;
+    // Temporal taps grouped by the input frame they read (equal frame pointers
+    // are equal data): group i starts at tap g_taps >> 4i & 15 and uses weight set
+    // g_sets >> 4i & 15 (bit fields rather than a table, which the compiler would
+    // place in per-lane memory).
+    int ng = a.kt;
+    uint32_t g_taps = 0x210u, g_sets = 0x210u;
+    if (TF) {
+        const uint16_t* z0 = zframe(a.z, t);
+        const uint16_t* z1 = a.kt > 1 ? zframe(a.z, t + 1) : nullptr;
+        const uint16_t* z2 = a.kt > 2 ? zframe(a.z, t + 2) : nullptr;
+        if (a.kt == 3) {
+            if (z0 == z1 && z1 == z2) { ng = 1; g_taps = 0x0u; g_sets = 0x5u; }
+            else if (z0 == z1) { ng = 2; g_taps = 0x20u; g_sets = 0x23u; }
+            else if (z1 == z2) { ng = 2; g_taps = 0x10u; g_sets = 0x40u; }
+        } else if (a.kt == 2 && z0 == z1) {
+            ng = 1; g_taps = 0x0u; g_sets = 0x2u;
+        }
+    }
+    const int nws = num_wsets(a.kt);
+    const int nsteps = ng * a.kchunks;
     const int nsub = nsteps * 2;
+    const int wsub = nws * a.kchunks * 2;  // packed sub-steps of one (channel block, phase)
     const uint32_t frame_bytes = (uint32_t)(a.z.frame_elems * 2);
     const __amdgpu_buffer_rsrc_t wr =
-        make_rsrc((const uint4*)a.wpk + (size_t)(cb * 4 + ph) * nsub * B_CH, (uint32_t)(nsub * B_CH * 16));
+        make_rsrc((const uint4*)a.wpk + (size_t)(cb * 4 + ph) * wsub * B_CH, (uint32_t)(wsub * B_CH * 16));
 
     uint32_t a_off[A_IT];
     int a_ch[A_IT];
@@ -169,17 +215,24 @@ __global__ __launch_bounds__(512, 1) void conv_phase_kernel(ConvArgs a)
                 a_off[it] = (uint32_t)(((gy * a.w_in + gx) * a.cin + gg * 8) * 2);
         }
     }
-    // temporal taps rotated by the output frame's place in the chunk (L2 sharing
-    // between the workgroups of neighbouring frames)
+    // groups taken in an order rotated by the output frame's place in the chunk
+    // (from the group holding tap -(t_rot0 + t) mod kt), so the workgroups of
+    // neighbouring frames read the same input frame at about the same time
     const int rot = a.rot_taps ? (a.kt - (a.t_rot0 + t) % a.kt) % a.kt : 0;
-    auto phys_step = [&](int step) -> int {
-        const int ta = step / a.kchunks, kc = step - ta * a.kchunks;
-        const int tr = ta + rot < a.kt ? ta + rot : ta + rot - a.kt;
-        return tr * a.kchunks + kc;
+    // the group holding tap rot: the number of later groups' first taps <= rot
+    const int g_first = !TF ? rot
+                            : (ng > 1 && rot >= (int)(g_taps >> 4 & 15u)) + (ng > 2 && rot >= (int)(g_taps >> 8 & 15u));
+    auto group_of = [&](int step, int& tap, int& set, int& kc) {
+        const int gl = step / a.kchunks;
+        kc = step - gl * a.kchunks;
+        int gi = g_first + gl;
+        if (gi >= ng) gi -= ng;
+        tap = (int)(g_taps >> (4 * gi) & 15u);
+        set = (int)(g_sets >> (4 * gi) & 15u);
     };
     auto issue_a = [&](int lstep, uint4* buf) {
-        const int step = phys_step(lstep);
-        const int ta = step / a.kchunks, kc = step - ta * a.kchunks;
+        int ta, set, kc;
+        group_of(lstep, ta, set, kc);
         const uint16_t* fp = zframe(a.z, t + ta);
         const __amdgpu_buffer_rsrc_t r = make_rsrc(fp, fp ? frame_bytes : 0u);
         const int ch0 = kc * 32;
@@ -190,7 +243,9 @@ __global__ __launch_bounds__(512, 1) void conv_phase_kernel(ConvArgs a)
         }
     };
     auto issue_b = [&](int lsub, uint4* buf) {
-        const int sub = phys_step(lsub >> 1) * 2 + (lsub & 1);
+        int ta, set, kc;
+        group_of(lsub >> 1, ta, set, kc);
+        const int sub = (set * a.kchunks + kc) * 2 + (lsub & 1);
 #pragma unroll
         for (int it = 0; it < RB; ++it)
             load_to_lds(wr, (uint32_t)((sub * B_CH + it * NT + tid) * 16), buf + it * NT + wave * 64);
@@ -216,9 +271,12 @@ __global__ __launch_bounds__(512, 1) void conv_phase_kernel(ConvArgs a)
     // ox = Q - 1 + s (LDS column shift Q + s); LDS row srow serves output row
     // r = srow - bs for the row shifts bs = P and P + 1 (row offset bs - 1).
     // Operands of a sub-step: 0 = hi and 1 = lo of row shift P, 2 = hi and 3 =
-    // lo of row shift P + 1; a lo is zero, and skipped, where one tap folds.
+    // lo of row shift P + 1; a lo is zero, and skipped, where one tap (one
+    // temporal tap and one spatial tap) folds.
     auto main_loop = [&](auto PC, auto QC) {
         constexpr int P = decltype(PC)::value, Q = decltype(QC)::value;
+        // with temporal grouping every lo is applied: a group of several taps
+        // makes each lo non-zero, and a test per step would split the MFMA chain
         auto mma = [&](auto SC, const uint4* aread, const bf16x8 (&bq)[NOP][NFW]) {
             constexpr int S = decltype(SC)::value;
             const int base = col_off(16 * wm + k16 + Q + S);
@@ -232,7 +290,7 @@ __global__ __launch_bounds__(512, 1) void conv_phase_kernel(ConvArgs a)
 #pragma unroll
                     for (int f = 0; f < NFW; ++f)
                         acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bq[2 * k][f], av, acc[r][f], 0, 0, 0);
-                    if (fold_count(P, k) * fold_count(Q, S) > 1) {
+                    if (TF || fold_count(P, k) * fold_count(Q, S) > 1) {
 #pragma unroll
                         for (int f = 0; f < NFW; ++f)
                             acc[r][f] =
@@ -398,16 +456,17 @@ __global__ __launch_bounds__(512, 1) void conv_phase_kernel(ConvArgs a)
     }
 }
 
-// Packed weights per (channel block, phase, temporal tap, 32-channel chunk,
-// sub-step s, operand o): NTILE rows of 32 channels, 16-byte chunks swizzled as
-// in LDS.  Phase ph = 2 P + Q; sub-step s is source column offset Q - 1 + s;
-// operand o = 2 k + l is the folded weight of row offset P - 1 + k, hi (l = 0)
-// or lo (l = 1): W' = the fp32 sum of the taps (b, d) that read that offset,
-// hi = bf16(W'), lo = bf16(W' - hi).
+// Packed weights per (channel block, phase, temporal weight set, 32-channel
+// chunk, sub-step s, operand o): NTILE rows of 32 channels, 16-byte chunks
+// swizzled as in LDS.  Phase ph = 2 P + Q; sub-step s is source column offset
+// Q - 1 + s; operand o = 2 k + l is the folded weight of row offset P - 1 + k,
+// hi (l = 0) or lo (l = 1): W' = the fp32 sum over the set's temporal taps and
+// the spatial taps (b, d) that read that offset, hi = bf16(W'), lo = bf16(W' - hi).
 __global__ void pack_phase_kernel(const uint16_t* w, uint16_t* wpk, int cout, int cin, int kt, int ntile,
                                   int nblocks, int kchunks)
 {
-    const int64_t total = (int64_t)nblocks * 4 * kt * kchunks * 2 * NOP * ntile * 32;
+    const int nws = num_wsets(kt);
+    const int64_t total = (int64_t)nblocks * 4 * nws * kchunks * 2 * NOP * ntile * 32;
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * blockDim.x) {
         const int e = (int)(idx & 31);
@@ -420,8 +479,8 @@ __global__ void pack_phase_kernel(const uint16_t* w, uint16_t* wpk, int cout, in
         row /= 2;
         const int kc = (int)(row % kchunks);
         row /= kchunks;
-        const int ta = (int)(row % kt);
-        row /= kt;
+        const int ws = (int)(row % nws);
+        row /= nws;
         const int ph = (int)(row % 4);
         const int cb = (int)(row / 4);
         const int P = ph >> 1, Q = ph & 1;
@@ -431,14 +490,17 @@ __global__ void pack_phase_kernel(const uint16_t* w, uint16_t* wpk, int cout, in
         const int n = cb * ntile + nl;
         uint16_t v = 0;
         if (n < cout && c < cin) {
+            int a0, a1;
+            wset_taps(kt, ws, a0, a1);
             float sum = 0.f;
-            for (int b = 0; b < 3; ++b) {
-                if (((P + b - 1) >> 1) != oy) continue;
-                for (int d = 0; d < 3; ++d) {
-                    if (((Q + d - 1) >> 1) != ox) continue;
-                    sum += bf2f(w[((((int64_t)n * cin + c) * kt + ta) * 3 + b) * 3 + d]);
+            for (int ta = a0; ta <= a1; ++ta)
+                for (int b = 0; b < 3; ++b) {
+                    if (((P + b - 1) >> 1) != oy) continue;
+                    for (int d = 0; d < 3; ++d) {
+                        if (((Q + d - 1) >> 1) != ox) continue;
+                        sum += bf2f(w[((((int64_t)n * cin + c) * kt + ta) * 3 + b) * 3 + d]);
+                    }
                 }
-            }
             const uint16_t hi = f2bf(sum);
             v = lo ? f2bf(sum - bf2f(hi)) : hi;
         }
@@ -457,7 +519,7 @@ size_t phase_packed_elems(int cout, int cin, int kt)
 {
     int nt, nb;
     bf16_conv_tiling(cout, &nt, &nb);
-    return (size_t)nb * 4 * kt * ((cin + 31) / 32) * 2 * NOP * nt * 32;
+    return (size_t)nb * 4 * num_wsets(kt) * ((cin + 31) / 32) * 2 * NOP * nt * 32;
 }
 
 hipError_t launch_pack_phase(const void* w, void* wpk, int cout, int cin, int kt, hipStream_t s)
@@ -476,12 +538,15 @@ hipError_t launch_conv_phase(const ConvArgs& a, hipStream_t s)
 {
     if (!phase_conv_applies(a.ntile, a.kh, a.kw, a.up_s) || a.kt > 3 || a.out_u8) return hipErrorInvalidValue;
     if (a.h_out != 2 * a.h_in || a.w_out != 2 * a.w_in) return hipErrorInvalidValue;
+    const bool tf = a.z.up_t == 2;
     constexpr int RH = 9;
-    const int64_t tiles = (int64_t)((a.h_in + RH - 1) / RH) * ((a.w_in + 63) / 64);
+    const int rh = RH;
+    const int64_t tiles = (int64_t)((a.h_in + rh - 1) / rh) * ((a.w_in + 63) / 64);
     const int64_t total = tiles * a.t_out * a.nblocks * 4;
     if (total <= 0 || total > (int64_t)0x7fffffff - 8) return hipErrorInvalidValue;
     const int64_t grid = ((total + 7) / 8) * 8;
-    hipLaunchKernelGGL((conv_phase_kernel<6, RH>), dim3((unsigned)grid), dim3(512), 0, s, a);
+    if (tf) hipLaunchKernelGGL((conv_phase_kernel<6, RH, true>), dim3((unsigned)grid), dim3(512), 0, s, a);
+    else hipLaunchKernelGGL((conv_phase_kernel<6, RH, false>), dim3((unsigned)grid), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 

@@ -206,10 +206,13 @@ typedef struct {
  * phase (y & 1, x & 1), a 2x2 conv of the source image (the taps that read the
  * same source pixel are summed first; the SwiftVR page's "compute once, then
  * copy" reasoning, section "TemporalGrow: Compute Before Spatial Upsampling",
- * applied to the weights).  Each folded weight is kept as a bf16 hi/lo pair
- * (about 2^-17 relative), so the result equals the conv up to fp32 rounding while
- * the executed MFMA work is 7/9 of the definition's; profiling still reports the
- * definition's (algorithmic) FLOP. */
+ * applied to the weights).  Where the conv also doubles time (up_t = 2), the
+ * temporal taps that read the same input frame are summed the same way (two of
+ * the three taps of almost every output frame).  Each folded weight is kept as a
+ * bf16 hi/lo pair (about 2^-17 relative), so the result equals the conv up to
+ * fp32 rounding while the executed MFMA work is 7/9 of the definition's (about
+ * 16/27 with time doubled); profiling still reports the definition's
+ * (algorithmic) FLOP. */
 
 /* Frame batching (LightX2V blog "SwiftVR Inference Optimization ...", section
  * "ReAE Frame Batching": a small batch of frames passes through a whole group of

@@ -67,6 +67,29 @@ def test_bench_layer_list_is_the_decoder(temporal_grow):
         temporal_grow=temporal_grow)
 
 
+@pytest.mark.parametrize("t_in,first,want", [
+    # first chunk, 7 frames grown to 13: frame 0's taps all read X[0] (replicated
+    # history, then X[0]): one group; every later frame has one pair: two groups
+    (7, True, 8 * (1 + 2 * 12)),
+    # later chunk, 6 frames grown to 12: frame 0 reads two cache frames and X[0]:
+    # three groups; the rest two
+    (6, False, 8 * (3 + 2 * 11)),
+    (1, True, 8 * 1),
+    (1, False, 8 * (3 + 2)),
+])
+def test_folded_upsample_units_count_temporal_groups(t_in, first, want):
+    assert bench.folded_up_units(t_in, first, 2) == want
+    assert bench.folded_up_units(t_in, first, 1) == 21 * t_in
+
+
+def test_folded_upsample_flops_are_below_the_algorithmic_count():
+    for n, first in ((7, True), (6, False)):
+        alg, ex = bench.c4_up_flops(n, first)
+        assert 16.0 / 27.0 * alg < ex < 7.0 / 9.0 * alg
+        alg2, ex2 = bench.c4_up_flops(n, first, grown_in_conv=False)
+        assert alg2 == alg and ex2 == pytest.approx(7.0 / 9.0 * alg)
+
+
 def test_clip_schedule_covers_the_video():
     sched = [7] + [6] * 14
     assert sched == OM.clip_schedule(91)

@@ -136,27 +136,36 @@ def test_bf16_pointwise_conv_residual(k, up_s):
 
 
 PHASE_CASES = [
-    # cin, cout, up_t, h, w, splits, tpad, bias: ragged tiles, temporal growth,
-    # zero history, two and four 96-channel blocks
-    (192, 96, 1, 10, 70, [1, 2], C.TPAD_REPLICATE, True),
-    (128, 96, 2, 9, 40, [1, 2, 1], C.TPAD_ZERO, False),
-    (96, 192, 1, 7, 130, [2, 1], C.TPAD_REPLICATE, True),
-    (384, 384, 2, 5, 6, [1, 1], C.TPAD_REPLICATE, False),
+    # cin, cout, up_t, h, w, splits, tpad, bias, kt, aligned: ragged tiles, two and
+    # four 96-channel blocks; with time doubled the temporal taps that read one
+    # frame are grouped: zero history (the two history taps read nothing), the
+    # replicated first frame (all three taps read X[0]), the two cached frames,
+    # pairs of taps in either place, kt = 2 and 1, the aligned growth rule
+    (192, 96, 1, 10, 70, [1, 2], C.TPAD_REPLICATE, True, 3, False),
+    (128, 96, 2, 9, 40, [1, 2, 1], C.TPAD_ZERO, False, 3, False),
+    (96, 192, 1, 7, 130, [2, 1], C.TPAD_REPLICATE, True, 3, False),
+    (384, 384, 2, 5, 6, [1, 1], C.TPAD_REPLICATE, False, 3, False),
+    (96, 96, 2, 6, 20, [2, 3], C.TPAD_REPLICATE, True, 2, False),
+    (64, 96, 2, 5, 9, [1, 2], C.TPAD_ZERO, False, 1, False),
+    (160, 96, 2, 8, 17, [3, 1, 2], C.TPAD_ZERO, True, 3, True),
 ]
 
 
-@pytest.mark.parametrize("case", PHASE_CASES, ids=lambda c: "ci%d_co%d_ut%d" % c[:3])
+@pytest.mark.parametrize("case", PHASE_CASES, ids=lambda c: "ci%d_co%d_ut%d_kt%d%s" % (
+    c[:3] + (c[8], "_aligned" if c[9] else "")))
 def test_phase_folded_upsample_conv(case):
     """fold_upsample: the nearest-2x 3x3x3 conv computed per output phase from
-    folded hi/lo weights (7/9 of the MFMA work) matches the definition."""
-    cin, cout, up_t, h, w, splits, tpad, with_bias = case
+    folded hi/lo weights (spatial taps, and temporal taps that read one frame,
+    summed) matches the definition."""
+    cin, cout, up_t, h, w, splits, tpad, with_bias, kt, aligned = case
     say("phase-folded upsample conv %s" % (case,))
     x = synth.bf16(synth.video(cin, sum(splits), h, w, synth.seed(13, 1)))
-    wt = synth.bf16(synth.conv_weight(cout, cin, 3, 3, 3, synth.seed(13, 2)))
+    wt = synth.bf16(synth.conv_weight(cout, cin, kt, 3, 3, synth.seed(13, 2)))
     b = synth.bias(cout, synth.seed(13, 3)) if with_bias else None
-    ref = O.one_shot(to_oracle(x), to_oracle(wt), None if b is None else to_oracle(b), TP[tpad], 2, up_t)
+    ref = O.one_shot(to_oracle(x), to_oracle(wt), None if b is None else to_oracle(b), TP[tpad], 2, up_t,
+                     aligned=aligned)
     plan = P.conv_plan(wt.cuda(), h, w, bias=None if b is None else b.cuda(), up_s=2, up_t=up_t,
-                       max_chunk_t=max(splits), tpad=tpad, fold_upsample=True)
+                       max_chunk_t=max(splits), tpad=tpad, aligned=aligned, fold_upsample=True)
     C.check(C.lib().cc3d_profile_enable(plan._h, 1), "profile_enable")
     got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits))
     pr = C.OpProfile()
