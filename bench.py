@@ -26,7 +26,8 @@ Inputs are resident in HBM before timing; outputs go to a device ring.
 
 Prints one JSON line: value = algorithmic conv TFLOP/s (2*Cin*Cout*27 FLOP per
 output voxel of every conv) over the timed steps; plus output frames/s, the
-dominant kernel's roofline (live HIP-event timing on the plan's stream), the
+dominant kernel's roofline (live HIP-event timing on the plan's stream), every
+kernel's algorithmic rates and fraction of the roof that bounds it, the
 host-delivery rate (c4: every clip's output copied to pinned host memory on a
 second stream, bf16 and 8-bit; never the headline value), the phase-folded
 decode's frames/s and executed MFMA rate (c4: fold_upsample) and the CPU
@@ -462,12 +463,21 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
     roof.update({"traffic": recorded_traffic(dom_name), "kernel": dom_name, "launches": dom["launches"],
                  "avg_launch_ms": round(avg_ms, 4), "share_of_kernel_time": round(dom["ms"] / total_kernel_ms, 3)})
+    # per kernel: algorithmic rates and the fraction of the roof that bounds it
+    # (MFMA where its FLOP per algorithmic byte reach the ridge point, else HBM)
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     per_kernel = {}
     for name, k in sorted(kern.items(), key=lambda kv: -kv[1]["ms"]):
         e = {"ms": round(k["ms"], 3), "launches": k["launches"]}
+        tf = k["flops"] / (k["ms"] * 1e-3) / 1e12
+        gbs = k["bytes"] / (k["ms"] * 1e-3) / 1e9
         if k["flops"] > 0:
-            e["tflops"] = round(k["flops"] / (k["ms"] * 1e-3) / 1e12, 1)
-        e["gbs"] = round(k["bytes"] / (k["ms"] * 1e-3) / 1e9, 1)
+            e["tflops"] = round(tf, 1)
+        e["gbs"] = round(gbs, 1)
+        if k["flops"] > 0 and k["flops"] >= ridge * k["bytes"]:
+            e["bound"], e["frac"] = "mfma", round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+        else:
+            e["bound"], e["frac"] = "hbm", round(gbs / HBM_PEAK_GBS, 4)
         per_kernel[name] = e
 
     value = flops / dt / 1e12

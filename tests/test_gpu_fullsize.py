@@ -361,3 +361,25 @@ def test_c4_decoder_fullsize_sampled():
         t0 += n
     torch.cuda.synchronize()
     assert torch.equal(torch.cat(outs), got), "production slot wiring differs from the unique-slot wiring"
+
+
+def test_c4_decoder_fullsize_folded_sampled():
+    """The whole decoder at full size with phase-folded upsample convs (the two
+    that double time group their temporal taps): the first two clips, every op
+    checked on sampled positions to the same bound as the exact path."""
+    wl = synth.WORKLOADS[4]
+    say("full size c4, folded upsample convs: %s" % wl)
+    shapes = OM.decoder_layer_shapes()
+    dev, cpu = {}, {}
+    for i, (name, co, ci, kt, kh, kw, has_g) in enumerate(shapes):
+        d, c = _param_pair(co, ci, 4, i, has_g)
+        dev[name], cpu[name] = d, c
+    ops = S.decoder_ops(dev, unique_slots=True)
+    _gains_of_acts(ops, cpu)
+    splits = [wl["first_clip"], wl["clip"]]
+    x = synth.bf16(synth.video(wl["c_latent"], sum(splits), wl["h"], wl["w"], synth.seed(4, 1)))
+    x_cl = x.permute(1, 2, 3, 0).contiguous().cuda()
+    got, worst = run_stack_sampled(ops, cpu, x_cl, wl["c_latent"], wl["h"], wl["w"], splits, seed=424,
+                                   max_pts_rows=8, fold_upsample=True)
+    assert got.shape == (OM.output_frames(sum(splits)), 1440, 2560, 3)
+    assert all("%s.out" % k in worst for k in ("s0.up", "s1.up", "s2.up"))
