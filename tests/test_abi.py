@@ -225,3 +225,10 @@ def test_valid_descriptors_pass_validation():
         assert st == C.EDEVICE, C.last_error()
     d, keep = _stack([_conv_op(out=3), _conv_op(src=3, out=C.SLOT_Y)], batch_from=1, frame_batch=2)
     assert L.cc3d_stack_plan_create(ctypes.byref(d), None, ctypes.byref(out)) == C.EDEVICE, C.last_error()
+    # norm-only stack: act of x into an internal slot, then v = act + x stored
+    # and the act of v as the output
+    norm = dict(kind=C.OP_NORM_ACT, cout=0, kt=0, kh=0, kw=0, up_s=1, up_t=1, tpad=0, res=C.SLOT_NONE,
+                out=C.SLOT_NONE, w=None, bias=None, gamma=DUMMY)
+    d, keep = _stack([C.OpDesc(**dict(norm, src=C.SLOT_X, act_out=3)),
+                      C.OpDesc(**dict(norm, src=3, res=C.SLOT_X, out=4, act_out=C.SLOT_Y))])
+    assert L.cc3d_stack_plan_create(ctypes.byref(d), None, ctypes.byref(out)) == C.EDEVICE, C.last_error()

@@ -249,6 +249,31 @@ def test_bf16_conv_epilogue_act(cout, residual):
     assert_bf16_close(got, ref, "epilogue")
 
 
+@pytest.mark.parametrize("c", [16, 24, 32, 64, 96, 128, 192, 256, 320, 384, 512])
+def test_norm_act_pass_lane_layouts(c):
+    """The standalone norm pass (NORM_ACT ops) in every layout it picks for c
+    channels (lanes per pixel x 16-byte chunks per lane; 16 and 24 channels fit
+    none and take the element-wise kernel): act = SiLU(RMSNorm(x)),
+    then v = act + x stored (bitwise: the sum of two bf16 values rounded once)
+    and SiLU(RMSNorm(v))."""
+    say("norm pass c=%d" % c)
+    t, h, w = 3, 5, 7
+    x = synth.bf16(synth.video(c, t, h, w, synth.seed(16, c)))
+    g = synth.gain(c, synth.seed(16, c + 1))
+    s_a, s_v = C.SLOT_AUX + 1, C.SLOT_AUX + 2  # internal slots
+    ops = [P.Op(kind=C.OP_NORM_ACT, src=C.SLOT_X, act_out=s_a, gamma=g.cuda(), name="n1"),
+           P.Op(kind=C.OP_NORM_ACT, src=s_a, res=C.SLOT_X, out=s_v, act_out=C.SLOT_Y, gamma=g.cuda(), name="n2")]
+    plan = P.stack_plan(ops, c, h, w, max_chunk_t=t)
+    st = P.Stream(plan)
+    y = st.step(to_device_cl(x))
+    torch.cuda.synchronize()
+    a1 = from_device_cl(plan.read_slot(s_a, t, True))
+    v2 = from_device_cl(plan.read_slot(s_v, t, True))
+    assert_bf16_close(a1, O.act(to_oracle(x), to_oracle(g), 1e-6), "act")
+    assert np.array_equal(v2, O.round_bf16(a1 + to_oracle(x))), "stored v = bf16(act + x)"
+    assert_bf16_close(from_device_cl(y), O.act(v2, to_oracle(g), 1e-6), "act of v")
+
+
 def test_bf16_head_conv_residual():
     """The output head (3 channels, nearest 2x) with bias and a residual added
     before the bf16 store."""
