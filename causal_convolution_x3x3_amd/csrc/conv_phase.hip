@@ -538,10 +538,11 @@ hipError_t launch_conv_phase(const ConvArgs& a, hipStream_t s)
 {
     if (!phase_conv_applies(a.ntile, a.kh, a.kw, a.up_s) || a.kt > 3 || a.out_u8) return hipErrorInvalidValue;
     if (a.h_out != 2 * a.h_in || a.w_out != 2 * a.w_in) return hipErrorInvalidValue;
+    // temporal taps can read one frame only where the conv doubles time (or on a
+    // first chunk's history, which the ungrouped variant simply reads again)
     const bool tf = a.z.up_t == 2;
     constexpr int RH = 9;
-    const int rh = RH;
-    const int64_t tiles = (int64_t)((a.h_in + rh - 1) / rh) * ((a.w_in + 63) / 64);
+    const int64_t tiles = (int64_t)((a.h_in + RH - 1) / RH) * ((a.w_in + 63) / 64);
     const int64_t total = tiles * a.t_out * a.nblocks * 4;
     if (total <= 0 || total > (int64_t)0x7fffffff - 8) return hipErrorInvalidValue;
     const int64_t grid = ((total + 7) / 8) * 8;

@@ -500,6 +500,37 @@ def test_decoder_full_channels_tiny_frame(aligned, fold):
     assert_stack_close(got, ref, "decoder full channels")
 
 
+@pytest.mark.parametrize("t_prime,aligned,fold", [(1, False, False), (3, False, False), (4, False, True),
+                                                   (3, True, False), (2, True, True)])
+def test_decoder_causality_bitwise(t_prime, aligned, fold):
+    """Causality of the whole decoder on the GPU: changing latent t' leaves every
+    output frame that latents 0 .. t'-1 alone produce (OM.output_frames(t'):
+    4t'-3, or 4t' with the aligned rule) bitwise unchanged, in chunks that put
+    t' on either side of a chunk boundary, and changes the next frame."""
+    say("decoder causality t'=%d aligned=%s fold=%s" % (t_prime, aligned, fold))
+    c_latent, t, h, w, splits = 48, 5, 2, 3, [3, 2]
+    full = OM.decoder_layer_shapes(c_latent=c_latent)
+    gains = {s_[0]: s_[6] for s_ in full}
+    _, dev = _params([s_[:6] for s_ in full], 4, lambda n: gains[n])
+    x = synth.bf16(synth.video(c_latent, t, h, w, synth.seed(4, 1)))
+    x2 = x.clone()
+    x2[:, t_prime] = synth.bf16(x2[:, t_prime].float() + 1.0)
+    plan = P.stack_plan(S.decoder_ops(dev), c_latent, h, w, max_chunk_t=max(splits), aligned=aligned,
+                        fold_upsample=fold)
+    ys = []
+    for xv in (x, x2):
+        st, x_cl, t0, out = P.Stream(plan), to_device_cl(xv), 0, []
+        for n in splits:
+            out.append(st.step(x_cl[t0:t0 + n].contiguous()).clone())
+            t0 += n
+        torch.cuda.synchronize()
+        ys.append(torch.cat(out))
+    cut = OM.output_frames(t_prime, aligned=aligned)
+    assert ys[0].shape[0] == OM.output_frames(t, aligned=aligned) > cut
+    assert torch.equal(ys[0][:cut], ys[1][:cut]), "an output frame before %d changed" % cut
+    assert not torch.equal(ys[0][cut], ys[1][cut]), "output frame %d did not see latent %d" % (cut, t_prime)
+
+
 SMALL_STAGES = ((64, 2), (32, 2), (16, 1))
 
 
