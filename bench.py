@@ -228,11 +228,11 @@ def setup_c3(dev, torch, synth, P, S, fold=False):
     return plan, work, ring, desc
 
 
-def recorded_traffic(kernel_name):
-    """HBM bytes per launch of `kernel_name` from a committed PMC summary in
-    profiles/ (FETCH_SIZE + WRITE_SIZE runs, copy-calibrated), or None when no
-    record exists or a source it names (comma-separated: the kernel, and the op
-    list that sets its launches) changed since the counters were taken."""
+def _counter_record(kernel_name):
+    """The fields of `kernel_name`'s record in a committed PMC summary in
+    profiles/ (a "traffic_record:" line), or None when no record exists or a
+    source it names (comma-separated: the kernel, and the op list that sets its
+    launches) changed since the counters were taken."""
     import glob
     import hashlib
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
@@ -249,8 +249,22 @@ def recorded_traffic(kernel_name):
             for f in srcs:
                 h.update(open(f, "rb").read())
             if h.hexdigest()[:16] == kv.get("source_sha256_16"):
-                return float(kv["bytes_per_launch"])
+                return kv
     return None
+
+
+def recorded_traffic(kernel_name):
+    """HBM bytes per launch of `kernel_name` (FETCH_SIZE + WRITE_SIZE runs,
+    copy-calibrated), or None (see _counter_record)."""
+    kv = _counter_record(kernel_name)
+    return float(kv["bytes_per_launch"]) if kv else None
+
+
+def recorded_clock(kernel_name):
+    """Mean shader clock in GHz over `kernel_name`'s dispatches in the counter
+    run (GRBM_GUI_ACTIVE per XCD / dispatch time), or None."""
+    kv = _counter_record(kernel_name)
+    return float(kv["clock_ghz"]) if kv and "clock_ghz" in kv else None
 
 
 def timed_decode(torch, plan, work, ring, steps, warmup, before_timed=None):
@@ -468,6 +482,13 @@ def main():
         achieved = dom["bytes"] / dom["launches"] / (avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    clock = recorded_clock(dom_name)
+    if clock and roof["bound"] == "mfma":
+        # the part runs below its 2.4 GHz peak clock under this load (power): the
+        # same rate against the dense peak at the clock the counters saw
+        roof["clock_ghz"] = clock
+        roof["peak_at_clock"] = round(MFMA_BF16_PEAK_TFLOPS * clock / 2.4, 1)
+        roof["frac_at_clock"] = round(achieved / roof["peak_at_clock"], 4)
     if dom["exec_flops"] != dom["flops"]:
         roof["flop_basis"] = "the folded kernel's own MFMA work (27-tap equivalent: %.1f TFLOP/s)" % (
             dom["flops"] / dom["launches"] / (avg_ms * 1e-3) / 1e12)

@@ -116,8 +116,14 @@ def test_traffic_record_follows_the_source(tmp_path, monkeypatch):
     (prof / "x.md").write_text("traffic_record: kernel=kk source=k.hip,ops.py source_sha256_16=%s "
                                "bytes_per_launch=7\n" % sha2)
     assert bench.recorded_traffic("kk") == 7.0
+    assert bench.recorded_clock("kk") is None
     other.write_text("op list, changed\n")
     assert bench.recorded_traffic("kk") is None
+    # the counter run's clock rides on the same record
+    sha3 = hashlib.sha256(src.read_bytes() + other.read_bytes()).hexdigest()[:16]
+    (prof / "x.md").write_text("traffic_record: kernel=kk source=k.hip,ops.py source_sha256_16=%s "
+                               "bytes_per_launch=7 clock_ghz=1.994\n" % sha3)
+    assert bench.recorded_clock("kk") == 1.994 and bench.recorded_traffic("kk") == 7.0
 
 
 def test_more_than_one_gpu_is_refused():
