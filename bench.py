@@ -115,16 +115,17 @@ def folded_up_units(t_in, first, up_t):
     default growth rule) for t_in input frames, in units of one spatial tap per
     output pixel (27 per frame unfolded).  Per output frame and temporal tap: 7
     (four folded offsets, a hi each, a lo for the three that sum several taps).
-    A conv that doubles time groups the taps that read one input frame: 8 per
-    group (every lo applied)."""
+    A conv that doubles time groups the taps that read one source frame: 8 per
+    group (every lo applied); on a later chunk its two history frames are one
+    source frame (the previous window's last grown pair)."""
     if up_t == 1:
         return 21 * t_in
     ts = 1 if first else 0  # V[u] = X[(u + ts) // 2]
     t_v = 2 * t_in - ts
 
-    def frame(zi):  # what window frame zi reads: a cache slot or an input frame
+    def frame(zi):  # the source frame window frame zi holds
         if zi < 2:
-            return ("x", 0) if first else ("cache", zi)
+            return ("x", 0) if first else ("previous",)
         return ("x", (zi - 2 + ts) >> 1)
     units = 0
     for t in range(t_v):

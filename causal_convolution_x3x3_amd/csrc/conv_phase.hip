@@ -172,16 +172,25 @@ __global__ __launch_bounds__(512, 1) void conv_phase_kernel(ConvArgs a)
     const int wm = wave & 3, wn = wave >> 2;
     const int g = lane >> 4, k16 = lane & 15;
 
-    // Temporal taps grouped by the input frame they read (equal frame pointers
-    // are equal data): group i starts at tap g_taps >> 4i & 15 and uses weight set
-    // g_sets >> 4i & 15 (bit fields rather than a table, which the compiler would
-    // place in per-lane memory).
+    // Temporal taps grouped by the input frame they read: group i starts at tap
+    // g_taps >> 4i & 15 and uses weight set g_sets >> 4i & 15 (bit fields rather
+    // than a table, which the compiler would place in per-lane memory).  Window
+    // frames are told apart by the source frame they hold, not by address: frame
+    // zi >= kt-1 holds input frame (zi - (kt-1) + t_shift) / 2; the history holds
+    // the first input frame (replicated first chunk), zeros, or the previous
+    // window's last frames -- copies of one source frame where hist_same says so,
+    // never one of this window's.  A frame-batched run, which reads from the cache
+    // what a whole-chunk run reads from the input, then groups alike.
     int ng = a.kt;
     uint32_t g_taps = 0x210u, g_sets = 0x210u;
     if (TF) {
-        const uint16_t* z0 = zframe(a.z, t);
-        const uint16_t* z1 = a.kt > 1 ? zframe(a.z, t + 1) : nullptr;
-        const uint16_t* z2 = a.kt > 2 ? zframe(a.z, t + 2) : nullptr;
+        const int hist = a.kt - 1;
+        auto fid = [&](int zi) -> int {
+            if (zi >= hist) return (zi - hist + a.z.t_shift) >> 1;
+            if (a.z.first) return a.z.zero_hist ? -1 : 0;
+            return a.z.hist_same ? -2 : -2 - zi;
+        };
+        const int z0 = fid(t), z1 = fid(t + 1), z2 = fid(t + 2);
         if (a.kt == 3) {
             if (z0 == z1 && z1 == z2) { ng = 1; g_taps = 0x0u; g_sets = 0x5u; }
             else if (z0 == z1) { ng = 2; g_taps = 0x20u; g_sets = 0x23u; }

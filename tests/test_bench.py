@@ -71,11 +71,11 @@ def test_bench_layer_list_is_the_decoder(temporal_grow):
     # first chunk, 7 frames grown to 13: frame 0's taps all read X[0] (replicated
     # history, then X[0]): one group; every later frame has one pair: two groups
     (7, True, 8 * (1 + 2 * 12)),
-    # later chunk, 6 frames grown to 12: frame 0 reads two cache frames and X[0]:
-    # three groups; the rest two
-    (6, False, 8 * (3 + 2 * 11)),
+    # later chunk, 6 frames grown to 12: frame 0 reads the two history frames (one
+    # source frame, the previous chunk's last) and X[0]: two groups, as every frame
+    (6, False, 8 * 2 * 12),
     (1, True, 8 * 1),
-    (1, False, 8 * (3 + 2)),
+    (1, False, 8 * 2 * 2),
 ])
 def test_folded_upsample_units_count_temporal_groups(t_in, first, want):
     assert bench.folded_up_units(t_in, first, 2) == want

@@ -640,6 +640,60 @@ def test_decoder_frame_batching_bitwise(temporal_grow, group, fb, aligned, out_u
     say("  plan device bytes %d -> %d" % (plan_w.device_bytes, plan_b.device_bytes))
 
 
+@pytest.mark.parametrize("group,fb,aligned", [("s0.up", 1, False), ("s0.up", 2, True), ("conv_in", 3, False)])
+def test_decoder_frame_batching_folded_bitwise(group, fb, aligned):
+    """Frame batching with phase-folded upsample convs, the two that double time
+    inside the group: a batch reads from the cache the frames a whole-chunk run
+    reads from the input, and groups their temporal taps alike (by source frame),
+    so the output still equals the whole-chunk run bit for bit."""
+    say("frame batching, folded: group=%s fb=%d aligned=%s" % (group, fb, aligned))
+    full = OM.decoder_layer_shapes(c_latent=48)
+    gains = {s_[0]: s_[6] for s_ in full}
+    _, dev = _params([s_[:6] for s_ in full], 4, lambda n: gains[n])
+    ops = S.decoder_ops(dev)
+    h, w, splits = 2, 3, [3, 2, 1]
+    x_cl = to_device_cl(synth.bf16(synth.video(48, sum(splits), h, w, synth.seed(4, 1))))
+    plan_w = P.stack_plan(ops, 48, h, w, max_chunk_t=3, aligned=aligned, fold_upsample=True)
+    plan_b = P.stack_plan(ops, 48, h, w, max_chunk_t=3, aligned=aligned, fold_upsample=True,
+                          batch_from=_op_index(ops, group), frame_batch=fb)
+    sw, sb = P.Stream(plan_w), P.Stream(plan_b)
+    t0 = 0
+    for n in splits:
+        xc = x_cl[t0:t0 + n].contiguous()
+        yw, yb = sw.step(xc), sb.step(xc)
+        torch.cuda.synchronize()
+        assert torch.equal(yw, yb), "chunk at %d: frame-batched folded output differs" % t0
+        t0 += n
+
+
+@pytest.mark.parametrize("tpad", [C.TPAD_ZERO, C.TPAD_REPLICATE])
+def test_folded_growing_conv_batched_history(tpad):
+    """A phase-folded conv that doubles time, alone in a frame-batched group: a
+    one-frame first chunk leaves a history of two different frames under zero
+    padding (the zero frame and the first input frame) and two copies of one
+    frame under replication; batches of one frame then read every history from
+    the cache.  Batched equals whole chunks bit for bit, and both match the
+    definition."""
+    say("folded growing conv, batched history, tpad=%d" % tpad)
+    c, h, w, splits = 96, 5, 9, [1, 1, 3, 2]
+    x = synth.bf16(synth.video(c, sum(splits), h, w, synth.seed(13, 31)))
+    wt = synth.bf16(synth.conv_weight(c, c, 3, 3, 3, synth.seed(13, 32)))
+    ref = O.one_shot(to_oracle(x), to_oracle(wt), None, TP[tpad], 2, 2)
+    ops = [P.Op(cout=c, w=wt.cuda(), up_s=2, up_t=2, tpad=tpad, src=C.SLOT_X, out=C.SLOT_Y, name="up")]
+    plan_w = P.stack_plan(ops, c, h, w, max_chunk_t=3, fold_upsample=True)
+    plan_b = P.stack_plan(ops, c, h, w, max_chunk_t=3, fold_upsample=True, batch_from=0, frame_batch=1)
+    sw, sb = P.Stream(plan_w), P.Stream(plan_b)
+    x_cl, t0, outs = to_device_cl(x), 0, []
+    for n in splits:
+        xc = x_cl[t0:t0 + n].contiguous()
+        yw, yb = sw.step(xc), sb.step(xc)
+        torch.cuda.synchronize()
+        assert torch.equal(yw, yb), "chunk at %d: frame-batched output differs" % t0
+        outs.append(yw.clone())
+        t0 += n
+    assert_bf16_close(from_device_cl(torch.cat(outs)), ref, "folded growing conv")
+
+
 def test_conv_family_override_keeps_v1(monkeypatch):
     """CC3D_CONV_FAMILY=1 at plan creation keeps a conv the register-blocked
     kernel would take on the generic kernel: the profiled kernel name says so
