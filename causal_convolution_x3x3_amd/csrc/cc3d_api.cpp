@@ -835,23 +835,6 @@ cc3d_status cc3d_forward_chunk(const cc3d_plan* p, const void* x, int t_chunk, c
             a.z.t_shift = (first && !p->grow_aligned) ? 1 : 0;
             const int t_v = (r.up_t == 2) ? 2 * t_in - a.z.t_shift : t_in;
             *frames_out = t_v;
-            // The history of a conv that doubles time is the previous window's last
-            // two frames: copies of one source frame, unless the video so far grew
-            // to a single frame over zero history.  The conv's input frames so far
-            // are counted as one first chunk (later chunks add only mul * t).
-            if (r.up_t == 2 && !first) {
-                const int64_t seen = cache_in->frames_seen;
-                int64_t src_before;
-                if (ps.group) {
-                    const int64_t n = (seen > 0 ? p->g_in.eval(seen, true) : 0) + ps.in_off;
-                    src_before = n > 0 ? p->slots[r.src].rel.eval(n, true) : 0;
-                } else {
-                    src_before = seen > 0 ? p->slots[r.src].tc.eval(seen, true) : 0;
-                }
-                const int64_t v_before =
-                    src_before == 0 ? 0 : (p->grow_aligned ? 2 * src_before : 2 * src_before - 1);
-                a.z.hist_same = (a.z.zero_hist && v_before == 1) ? 0 : 1;
-            }
             a.wpk = r.wpk;
             a.bias = r.bias;
             a.res = slot_ptr(r.res, ps);

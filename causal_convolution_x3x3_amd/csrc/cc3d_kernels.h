@@ -22,7 +22,6 @@ struct ZWindow {
     int first;            // 1 on the video's first chunk
     int zero_hist;        // first-chunk history: 1 = zeros, 0 = copies of V[0]
     int t_shift;          // up_t = 2: V[u] = X[(u + t_shift) / 2]
-    int hist_same;        // not first: the kt-1 history frames are copies of one source frame
 };
 
 struct ConvArgs {

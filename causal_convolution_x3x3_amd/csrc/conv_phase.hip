@@ -176,19 +176,20 @@ __global__ __launch_bounds__(512, 1) void conv_phase_kernel(ConvArgs a)
     // g_taps >> 4i & 15 and uses weight set g_sets >> 4i & 15 (bit fields rather
     // than a table, which the compiler would place in per-lane memory).  Window
     // frames are told apart by the source frame they hold, not by address: frame
-    // zi >= kt-1 holds input frame (zi - (kt-1) + t_shift) / 2; the history holds
-    // the first input frame (replicated first chunk), zeros, or the previous
-    // window's last frames -- copies of one source frame where hist_same says so,
-    // never one of this window's.  A frame-batched run, which reads from the cache
-    // what a whole-chunk run reads from the input, then groups alike.
+    // zi >= kt-1 holds input frame (zi - (kt-1) + t_shift) / 2; with replicated
+    // history the history frames hold the first input frame (first chunk) or the
+    // previous window's last grown pair, one source frame that no frame of this
+    // window holds.  A frame-batched run, which reads from the cache what a
+    // whole-chunk run reads from the input, then groups alike.  Under zero history
+    // whether the two history frames hold one source frame depends on how the
+    // video began, which a replayed graph could not follow: no grouping there.
     int ng = a.kt;
     uint32_t g_taps = 0x210u, g_sets = 0x210u;
-    if (TF) {
+    if (TF && !a.z.zero_hist) {
         const int hist = a.kt - 1;
         auto fid = [&](int zi) -> int {
             if (zi >= hist) return (zi - hist + a.z.t_shift) >> 1;
-            if (a.z.first) return a.z.zero_hist ? -1 : 0;
-            return a.z.hist_same ? -2 : -2 - zi;
+            return a.z.first ? 0 : -1;
         };
         const int z0 = fid(t), z1 = fid(t + 1), z2 = fid(t + 2);
         if (a.kt == 3) {

@@ -53,11 +53,7 @@
  * synchronisation, no memset nodes) and may be captured into a HIP graph, with
  * profiling off.  Which rule a chunk takes (first chunk or not) is decided from
  * cache_in->frames_seen when the call is made, so a captured call replays that
- * rule: run the video's first chunk eagerly, then replay captured chunks.  (So is
- * one more choice, for a phase-folded conv that doubles time under zero temporal
- * padding: whether its two history frames are one source frame, which they are
- * not only on the chunk after a first chunk that grew to a single frame.  Taking
- * them apart is also correct, and changes only the fp32 summation order.)
+ * rule: run the video's first chunk eagerly, then replay captured chunks.
  */
 #ifndef CC3D_H
 #define CC3D_H
