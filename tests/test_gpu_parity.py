@@ -718,28 +718,36 @@ def test_conv_family_override_keeps_v1(monkeypatch):
     assert names[None] == "conv_bf16_v2_up1_k3_n96" and names["1"] == "conv_bf16_up1_k3_n96", names
 
 
-def test_graph_capture_replays_chunks():
+@pytest.mark.parametrize("kind", ["resblock", "growing_folded"])
+def test_graph_capture_replays_chunks(kind):
     """CDA-VSR page, "CUDA Graph inference": a chunk decode captured into a graph
     (fixed shapes, the two state arenas used alternately, no allocation, no host
     synchronisation) replays the eager decode bit for bit.  The first chunk runs
     eagerly (its first-chunk rule is fixed when a launch is recorded); two graphs
     (state A -> B and B -> A) are then replayed in turn, with eager copies and a
-    synchronisation between replays, and every replay is checked."""
-    say("graph capture of forward_chunk")
+    synchronisation between replays, and every replay is checked.  Stacks: a
+    residual block, and a phase-folded conv that doubles space and time."""
+    say("graph capture of forward_chunk: %s" % kind)
     c, h, w, n, nch = 96, 10, 40, 4, 7
-    cpu, dev = _params([("c1", c, c, 3, 3, 3), ("c2", c, c, 3, 3, 3)], 12, lambda n_: True, with_bias=True)
-    ops = S.resblock_ops(c, dev["c1"], dev["c2"])
-    plan = P.stack_plan(ops, c, h, w, max_chunk_t=n)
+    if kind == "resblock":
+        cpu, dev = _params([("c1", c, c, 3, 3, 3), ("c2", c, c, 3, 3, 3)], 12, lambda n_: True, with_bias=True)
+        plan = P.stack_plan(S.resblock_ops(c, dev["c1"], dev["c2"]), c, h, w, max_chunk_t=n)
+    else:
+        wt = synth.bf16(synth.conv_weight(c, c, 3, 3, 3, synth.seed(12, 7))).cuda()
+        ops = [P.Op(cout=c, w=wt, up_s=2, up_t=2, src=C.SLOT_X, out=C.SLOT_Y, name="up")]
+        plan = P.stack_plan(ops, c, h, w, max_chunk_t=n, fold_upsample=True)
     x = to_device_cl(synth.bf16(synth.video(c, n * nch, h, w, synth.seed(12, 1))))
     chunks = [x[i * n:(i + 1) * n].contiguous() for i in range(nch)]
     eager = _run_chunks(plan, x, [n] * nch)
+    t1, t_rest = plan.output_shape(n, True)[0], plan.output_shape(n, False)[0]
     st = P.Stream(plan)
     x_s = torch.empty_like(chunks[0])
-    y_s = torch.empty((n, h, w, c), dtype=torch.bfloat16, device="cuda")
+    y_1 = torch.empty((t1,) + tuple(eager.shape[1:]), dtype=torch.bfloat16, device="cuda")
+    y_s = torch.empty((t_rest,) + tuple(eager.shape[1:]), dtype=torch.bfloat16, device="cuda")
     x_s.copy_(chunks[0])
-    st.step(x_s, y=y_s)
+    st.step(x_s, y=y_1)
     torch.cuda.synchronize()
-    assert torch.equal(y_s, eager[:n])
+    assert torch.equal(y_1, eager[:t1])
     a, b = st.states[st.cur], st.states[1 - st.cur]
     graphs = []
     for cin_, cout_ in ((a, b), (b, a)):
@@ -751,7 +759,8 @@ def test_graph_capture_replays_chunks():
         x_s.copy_(chunks[i])
         graphs[(i - 1) % 2].replay()
         torch.cuda.synchronize()
-        assert torch.equal(y_s, eager[i * n:(i + 1) * n]), "replay %d differs from the eager decode" % i
+        f0 = t1 + (i - 1) * t_rest
+        assert torch.equal(y_s, eager[f0:f0 + t_rest]), "replay %d differs from the eager decode" % i
 
 
 def test_plan_create_failure_releases_everything(monkeypatch):
