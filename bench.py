@@ -372,7 +372,7 @@ def cpu_baseline(workload, temporal_grow=None):
     O.build()
     threads = O.default_threads()
     if workload in ("c4", "c4tg"):
-        lt, lh, lw = 3, 6, 10
+        lt, lh, lw = 3, 6, 20  # about 15 s on 16 host threads
         shapes = OM.decoder_layer_shapes(temporal_grow=temporal_grow)
         params = {}
         for i, (name, co, ci, kt, kh, kw, has_g) in enumerate(shapes):
