@@ -424,8 +424,8 @@ def main():
                     help="skip the host-delivery measurement (c4: output copied to pinned host memory)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this decode path has no multi-GPU mode "
-              "(the shard design is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: this decode path has no multi-GPU mode; "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -21,8 +21,9 @@ float64 numpy arrays laid out [C][T][H][W] (one video, channels first):
   per-position ops commute with it.
 * 2x temporal growth on non-first frames, channel RMSNorm, SiLU, the residual
   block and the stacks are the synthetic decoder workloads' own definitions
-  (the pages name the blocks but print no layer list); the readings taken where
-  the pages are silent are listed in the design doc.
+  (the pages name the blocks but print no layer list): where the pages are
+  silent, the plainest reading -- zero spatial padding at the upsampled size,
+  replicated history for the 3x3x3 convs, RMSNorm without mean subtraction.
 * aligned first chunk -- "From Pixels to Latents and Back": the first chunk
   reads 28 frames and drops 3 after decoding.  Read here as a growth rule that
   doubles every frame, the first chunk's included (``aligned=True``); with
