@@ -16,12 +16,14 @@
 //   positions each) and two along N.  The weights are the MFMA's row operand, so
 //   a lane's accumulators are four consecutive channels of one position and the
 //   epilogue moves 8-byte vectors.
-// * K is walked in steps of (temporal tap, 64 channels).  Both operands go from
-//   global memory straight into LDS (buffer loads with the LDS flag), one step
-//   ahead into the idle half of a double buffer; one barrier per step.  Every
-//   lane's 16-byte slot of the position tile has a fixed source offset, so the
-//   nearest upsample (and any ragged tail past the frame, read as zeros) costs
-//   nothing in the loop.
+// * K is walked in steps of (temporal tap, 32 channels): one MFMA deep.  Both
+//   operands go from global memory straight into LDS (buffer loads with the LDS
+//   flag), NB - 1 steps ahead into a ring of NB buffer sets; one barrier per
+//   step, which waits only for the next step's loads.  A step's MFMAs take well
+//   under a microsecond, less than the loads' latency, so a deep ring is what
+//   keeps the pipe fed.  Every lane's 16-byte slot of the position tile has a
+//   fixed source offset, so the nearest upsample (and any ragged tail past the
+//   frame, read as zeros) costs nothing in the loop.
 // * Temporal taps are taken in an order rotated by the output frame, and work
 //   items run frame-major within a tile, so the workgroups of frames t, t+1, t+2
 //   read the same input frame at the same time and share it in L2.  Items are
@@ -38,6 +40,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+template <int V>
+struct IC {
+    static constexpr int value = V;
+};
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
@@ -49,10 +55,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// 16-byte chunk swizzle inside a 128-byte LDS row (one position or one weight
-// row, 64 channels): the 16 rows one ds_read_b128 quarter touches spread over
-// all eight chunk positions.
-__device__ __forceinline__ int swz8(int row) { return row & 7; }
+// 16-byte chunk swizzle inside a 64-byte LDS row (one position or one weight
+// row, 32 channels): the 16 rows one fragment read touches spread over the
+// banks.
+__device__ __forceinline__ int swz4(int row) { return (row >> 1) & 3; }
 
 __device__ __forceinline__ const uint16_t* zframe(const ZWindow& z, int zi)
 {
@@ -83,10 +89,16 @@ __device__ __forceinline__ void load_to_lds4(__amdgpu_buffer_rsrc_t r, uint32_t 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4, off, 0, 0, 0);
 }
 
-// s_waitcnt vmcnt(0) (gfx9 encoding; expcnt and lgkmcnt left at their maxima)
-__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
-constexpr int KC = 64;  // channels per K step
+constexpr int KC = 32;  // channels per K step
+constexpr int NB = 5;   // buffer sets in the ring: loads NB - 1 steps ahead
 
 template <int UP, int NF, int MW>
 __global__ __launch_bounds__(512, 1) void conv_pw_kernel(ConvArgs a)
@@ -104,11 +116,22 @@ __global__ __launch_bounds__(512, 1) void conv_pw_kernel(ConvArgs a)
     static_assert(A_IT * NT == A_CH, "position tile in whole load rounds");
     static_assert(RB4 * NT * 4 == (B_CH % NT) * 16, "weight block in whole load rounds");
     static_assert(NF % WN == 0, "N fragments split evenly over the N waves");
+    constexpr int LI = A_IT + RB16 + RB4;  // load instructions per step and lane
+    static_assert((NB - 2) * LI < 64, "vmcnt range");
+    static_assert(NB * (A_CH + B_CH) * 16 <= 160 * 1024, "LDS budget");
 
-    __shared__ uint4 lds_a0[A_CH];
-    __shared__ uint4 lds_a1[A_CH];
-    __shared__ uint4 lds_b0[B_CH];
-    __shared__ uint4 lds_b1[B_CH];
+    // one LDS variable per buffer (the compiler then sees which one a load fills)
+    __shared__ uint4 lds_a0[A_CH], lds_a1[A_CH], lds_a2[A_CH], lds_a3[A_CH], lds_a4[A_CH];
+    __shared__ uint4 lds_b0[B_CH], lds_b1[B_CH], lds_b2[B_CH], lds_b3[B_CH], lds_b4[B_CH];
+    static_assert(NB == 5, "five buffer sets declared");
+    auto abuf = [&](auto J) -> uint4* {
+        constexpr int j = decltype(J)::value;
+        return j == 0 ? lds_a0 : j == 1 ? lds_a1 : j == 2 ? lds_a2 : j == 3 ? lds_a3 : lds_a4;
+    };
+    auto bbuf = [&](auto J) -> uint4* {
+        constexpr int j = decltype(J)::value;
+        return j == 0 ? lds_b0 : j == 1 ? lds_b1 : j == 2 ? lds_b2 : j == 3 ? lds_b3 : lds_b4;
+    };
 
     const int hw_out = a.h_out * a.w_out;
     const int tiles = (hw_out + TP - 1) / TP;
@@ -141,8 +164,8 @@ __global__ __launch_bounds__(512, 1) void conv_pw_kernel(ConvArgs a)
 #pragma unroll
     for (int it = 0; it < A_IT; ++it) {
         const int slot = tid + NT * it;
-        const int pos = slot >> 3;
-        const int chunk = (slot & 7) ^ swz8(pos);
+        const int pos = slot >> 2;
+        const int chunk = (slot & 3) ^ swz4(pos);
         const int op = p0 + pos;
         a_ch[it] = chunk * 8;
         a_off[it] = OOB;
@@ -184,21 +207,15 @@ __global__ __launch_bounds__(512, 1) void conv_pw_kernel(ConvArgs a)
                          (char*)bbuf + RB16 * NT * 16 + (it * NT + wave * 64) * 4);
     };
 
-    // byte offsets of this lane's fragments for K half h = 0 (h = 1: chunk ^ 4)
+    // byte offsets of this lane's fragments: the chunk of K group g in row
+    // `row` is g ^ swz4(row); rows of one lane differ by multiples of 16, so
+    // swz4 is that of k16
+    const int co = (g ^ swz4(k16)) << 4;
     int a_frag[MW], b_frag[NFW];
 #pragma unroll
-    for (int m = 0; m < MW; ++m) {
-        const int pos = 64 * wm + 16 * m + k16;
-        a_frag[m] = pos * 128;
-    }
+    for (int m = 0; m < MW; ++m) a_frag[m] = (64 * wm + 16 * m + k16) * 64 + co;
 #pragma unroll
-    for (int f = 0; f < NFW; ++f) {
-        const int nl = 16 * (wn * NFW + f) + k16;
-        b_frag[f] = nl * 128;
-    }
-    // the chunk of K group g in half h of row `row`: (4h + g) ^ swz8(row); rows
-    // of one lane differ by multiples of 16, so swz8 is that of k16
-    const int c0 = (g ^ swz8(k16)) << 4, c1 = ((4 + g) ^ swz8(k16)) << 4;
+    for (int f = 0; f < NFW; ++f) b_frag[f] = (16 * (wn * NFW + f) + k16) * 64 + co;
 
     f32x4 acc[MW][NFW];
 #pragma unroll
@@ -206,41 +223,48 @@ __global__ __launch_bounds__(512, 1) void conv_pw_kernel(ConvArgs a)
 #pragma unroll
         for (int f = 0; f < NFW; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto mma = [&](const uint4* abuf, const uint4* bbuf) {
+    auto mma = [&](const uint4* ab, const uint4* bb) {
+        bf16x8 bq[NFW];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int co = h ? c1 : c0;
-            bf16x8 bq[NFW];
+        for (int f = 0; f < NFW; ++f) bq[f] = as_bf16x8(*(const uint4*)((const char*)bb + b_frag[f]));
 #pragma unroll
-            for (int f = 0; f < NFW; ++f) bq[f] = as_bf16x8(*(const uint4*)((const char*)bbuf + b_frag[f] + co));
+        for (int m = 0; m < MW; ++m) {
+            const bf16x8 av = as_bf16x8(*(const uint4*)((const char*)ab + a_frag[m]));
 #pragma unroll
-            for (int m = 0; m < MW; ++m) {
-                const bf16x8 av = as_bf16x8(*(const uint4*)((const char*)abuf + a_frag[m] + co));
-#pragma unroll
-                for (int f = 0; f < NFW; ++f)
-                    acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bq[f], av, acc[m][f], 0, 0, 0);
-            }
+            for (int f = 0; f < NFW; ++f)
+                acc[m][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bq[f], av, acc[m][f], 0, 0, 0);
         }
     };
 
-    issue(0, lds_a0, lds_b0);
-    wait_vmcnt0();
+    // Step s reads buffer set s % NB and fills set (s + NB - 1) % NB -- last read
+    // in step s - 1, retired by its barrier -- with step s + NB - 1.  Steps past
+    // the last reload the last one, so every load is unconditional and the
+    // compiler's own waits stay exact; steps go in groups of NB so that every
+    // buffer is a fixed LDS variable.
+    auto clamp = [&](int s_) { return s_ < nsteps ? s_ : nsteps - 1; };
+    issue(clamp(0), lds_a0, lds_b0);
+    issue(clamp(1), lds_a1, lds_b1);
+    issue(clamp(2), lds_a2, lds_b2);
+    issue(clamp(3), lds_a3, lds_b3);
+    wait_vmcnt<(NB - 2) * LI>();  // step 0 has landed
     __builtin_amdgcn_s_barrier();
-    // Step s reads buffer s % 2 and fills the other one (last read in step s - 1,
-    // retired by its barrier) with step s + 1 -- the last step reloads itself (an
-    // L2 hit), so every load is unconditional and the compiler's own waits stay
-    // exact.  Steps go in pairs so that every buffer is a fixed LDS variable.
-    auto k_step = [&](int step, const uint4* ar, const uint4* br, uint4* aw, uint4* bw) {
-        issue(step + 1 < nsteps ? step + 1 : nsteps - 1, aw, bw);
-        mma(ar, br);
-        wait_vmcnt0();
+    auto k_step = [&](int step, auto J) {
+        constexpr int j = decltype(J)::value;
+        issue(clamp(step + NB - 1), abuf(IC<(j + NB - 1) % NB>{}), bbuf(IC<(j + NB - 1) % NB>{}));
+        mma(abuf(J), bbuf(J));
+        // the next step's loads were issued NB - 1 steps ago; the NB - 2 later
+        // steps' may stay in flight
+        wait_vmcnt<(NB - 2) * LI>();
         // bare barrier: the loads it publishes were waited for just above and
         // the loop makes no LDS stores
         __builtin_amdgcn_s_barrier();
     };
-    for (int step = 0; step < nsteps; step += 2) {
-        k_step(step, lds_a0, lds_b0, lds_a1, lds_b1);
-        if (step + 1 < nsteps) k_step(step + 1, lds_a1, lds_b1, lds_a0, lds_b0);
+    for (int step = 0; step < nsteps; step += NB) {
+        k_step(step, IC<0>{});
+        if (step + 1 < nsteps) k_step(step + 1, IC<1>{});
+        if (step + 2 < nsteps) k_step(step + 2, IC<2>{});
+        if (step + 3 < nsteps) k_step(step + 3, IC<3>{});
+        if (step + 4 < nsteps) k_step(step + 4, IC<4>{});
     }
 
     // ---------------------------------------------------------------- epilogue
@@ -296,8 +320,8 @@ hipError_t launch_pw(const ConvArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
-// Packed layout per (channel block, temporal tap, 64-channel chunk): NTILE rows
-// of 64 channels, the 16-byte chunks of row nl swizzled by swz8(nl) as in LDS;
+// Packed layout per (channel block, temporal tap, 32-channel chunk): NTILE rows
+// of 32 channels, the 16-byte chunks of row nl swizzled by swz4(nl) as in LDS;
 // zero past cout and cin.
 __global__ void pack_pw_kernel(const uint16_t* w, uint16_t* wpk, int cout, int cin, int kt, int ntile,
                                int nblocks, int kc_n)
@@ -313,7 +337,7 @@ __global__ void pack_pw_kernel(const uint16_t* w, uint16_t* wpk, int cout, int c
         row /= kc_n;
         const int ta = (int)(row % kt);
         const int nb = (int)(row / kt);
-        const int chunk = (e >> 3) ^ swz8(nl);
+        const int chunk = (e >> 3) ^ swz4(nl);
         const int c = kc * KC + chunk * 8 + (e & 7);
         const int n = nb * ntile + nl;
         uint16_t v = 0;
