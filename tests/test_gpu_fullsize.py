@@ -400,6 +400,32 @@ def test_c4_decoder_fullsize_sampled():
     assert torch.equal(torch.cat(outs), got), "production slot wiring differs from the unique-slot wiring"
 
 
+@pytest.mark.parametrize("fold", [False, True])
+def test_c4_decoder_whole_video_sampled(fold):
+    """The whole 91-latent video through the decoder at full size in the
+    benchmark's 15 clips (7, then 14 of 6 latents -> 361 frames at 1440x2560),
+    every cache carried through; every op of the last clip checked on sampled
+    positions against the oracle fed its own GPU input, the causal windows
+    carried along; with `fold`, the upsampling convs phase-folded."""
+    wl = synth.WORKLOADS[4]
+    say("full size c4, whole video (fold=%s)" % fold)
+    shapes = OM.decoder_layer_shapes()
+    dev, cpu = {}, {}
+    for i, (name, co, ci, kt, kh, kw, has_g) in enumerate(shapes):
+        d, c = _param_pair(co, ci, 4, i, has_g)
+        dev[name], cpu[name] = d, c
+    ops = S.decoder_ops(dev, unique_slots=True)
+    _gains_of_acts(ops, cpu)
+    splits = OM.clip_schedule(wl["t"], wl["first_clip"], wl["clip"])
+    assert len(splits) == 15 and OM.output_frames(sum(splits)) == 361
+    x = synth.bf16(synth.video(wl["c_latent"], sum(splits), wl["h"], wl["w"], synth.seed(4, 1)))
+    x_cl = x.permute(1, 2, 3, 0).contiguous().cuda()
+    got, worst = run_stack_sampled(ops, cpu, x_cl, wl["c_latent"], wl["h"], wl["w"], splits, seed=434,
+                                   max_pts_rows=8, fold_upsample=fold, check_from=len(splits) - 1)
+    assert got.shape == (24, 1440, 2560, 3)
+    assert all("%s.out" % k in worst for k in ("s0.up", "s1.up", "s2.up", "head"))
+
+
 def test_c4_decoder_fullsize_folded_sampled():
     """The whole decoder at full size with phase-folded upsample convs (the two
     that double time group their temporal taps): the first two clips, every op
