@@ -410,7 +410,7 @@ def cpu_baseline(workload, temporal_grow=None):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=15)
+    ap.add_argument("--steps", type=int, default=45)  # c4: three passes over the 15-clip video
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", choices=["c4", "c4tg", "c3"], default="c4")
     ap.add_argument("--tg-order", choices=["before", "after"], default="before",
