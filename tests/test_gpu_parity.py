@@ -119,6 +119,43 @@ def test_bf16_conv_vs_oracle(case):
     assert_bf16_close(got, ref, "bf16 conv")
 
 
+TINY_CASES = [
+    # cin, cout, k, up_s, up_t, h, w, splits, tpad, fold, kernel that must run:
+    # frames of one or two pixels -- a single tile mostly border and padding --
+    # through every kernel family, with growth, zero history and 1-frame chunks
+    (96, 96, (3, 3, 3), 1, 1, 1, 1, [1, 2], C.TPAD_REPLICATE, False, "conv_bf16_v2_up1_k3_n96"),
+    (64, 192, (3, 3, 3), 1, 2, 2, 1, [1, 1, 2], C.TPAD_ZERO, False, "conv_bf16_v2_up1_k3_n96"),
+    (96, 96, (3, 3, 3), 2, 1, 1, 2, [2, 1], C.TPAD_REPLICATE, False, "conv_bf16_v2_up2_k3_n96"),
+    (96, 96, (3, 3, 3), 2, 2, 1, 1, [1, 2, 1], C.TPAD_REPLICATE, True, "conv_bf16_phase_up2_k3_n96"),
+    (128, 96, (3, 3, 3), 2, 1, 2, 1, [1, 2], C.TPAD_ZERO, True, "conv_bf16_phase_up2_k3_n96"),
+    (96, 3, (3, 3, 3), 2, 1, 1, 1, [1, 2], C.TPAD_REPLICATE, False, "conv_bf16_head_up2_k3_c3"),
+    (64, 2, (3, 3, 3), 1, 1, 2, 1, [2, 1], C.TPAD_ZERO, False, "conv_bf16_head_up1_k3_c2"),
+    (96, 96, (1, 1, 1), 1, 1, 1, 1, [1, 1], C.TPAD_REPLICATE, False, "conv_bf16_pw_up1_kt1_n96"),
+    (192, 192, (3, 1, 1), 2, 2, 1, 1, [1, 2], C.TPAD_ZERO, False, "conv_bf16_pw_up2_kt3_n192"),
+    (16, 32, (3, 3, 3), 1, 1, 1, 1, [1, 2], C.TPAD_REPLICATE, False, "conv_bf16_up1_k3_n"),
+]
+
+
+@pytest.mark.parametrize("case", TINY_CASES, ids=lambda c: "%s_%dx%d" % (c[10], c[5], c[6]))
+def test_bf16_conv_tiny_frames(case):
+    """Degenerate frame sizes (1x1, 1x2, 2x1 pixels) through each kernel family
+    against the definition; the profiled kernel name shows which one ran."""
+    cin, cout, k, up_s, up_t, h, w, splits, tpad, fold, kname = case
+    say("bf16 conv, tiny frame %s" % (case,))
+    x = synth.bf16(synth.video(cin, sum(splits), h, w, synth.seed(5, 41)))
+    wt = synth.bf16(synth.conv_weight(cout, cin, *k, synth.seed(5, 42)))
+    b = synth.bias(cout, synth.seed(5, 43))
+    ref = O.one_shot(to_oracle(x), to_oracle(wt), to_oracle(b), TP[tpad], up_s, up_t)
+    plan = P.conv_plan(wt.cuda(), h, w, bias=b.cuda(), up_s=up_s, up_t=up_t, max_chunk_t=max(splits), tpad=tpad,
+                       fold_upsample=fold)
+    C.check(C.lib().cc3d_profile_enable(plan._h, 1), "profile_enable")
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits))
+    pr = C.OpProfile()
+    C.check(C.lib().cc3d_profile_read(plan._h, 0, 0, ctypes.byref(pr)), "profile_read")
+    assert pr.kernel.decode().startswith(kname), pr.kernel
+    assert_bf16_close(got, ref, "tiny frame conv")
+
+
 @pytest.mark.parametrize("k,up_s", [((1, 1, 1), 2), ((3, 1, 1), 1)])
 def test_bf16_pointwise_conv_residual(k, up_s):
     """The pointwise kernel's epilogue: + bias + residual, stored as bf16."""
