@@ -53,6 +53,23 @@ def test_c0_fp32_conv_chunked(tpad, splits):
     assert_fp32_close(got, ref, "c0")
 
 
+@pytest.mark.parametrize("h,w,k,up_s,up_t,tpad", [
+    (1, 1, (3, 3, 3), 1, 1, C.TPAD_REPLICATE),
+    (1, 2, (3, 3, 3), 2, 2, C.TPAD_ZERO),
+    (2, 1, (2, 1, 3), 2, 1, C.TPAD_REPLICATE),
+])
+def test_fp32_conv_tiny_frames(h, w, k, up_s, up_t, tpad):
+    """fp32 convs on frames of one or two pixels, 1-frame chunks included."""
+    say("fp32 tiny frame %dx%d k=%s up=%d/%d" % (h, w, k, up_s, up_t))
+    x = synth.video(8, 5, h, w, synth.seed(0, 31))
+    wt = synth.conv_weight(4, 8, *k, synth.seed(0, 32))
+    b = synth.bias(4, synth.seed(0, 33))
+    ref = O.one_shot(to_oracle(x), to_oracle(wt), to_oracle(b), TP[tpad], up_s, up_t)
+    plan = P.conv_plan(wt.cuda(), h, w, bias=b.cuda(), up_s=up_s, up_t=up_t, max_chunk_t=3, tpad=tpad)
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), [1, 3, 1]))
+    assert_fp32_close(got, ref, "fp32 tiny frame")
+
+
 def test_fp32_memoryblock_zero_history_with_bias_and_upsample():
     say("fp32 memoryblock kt=2")
     x = synth.video(8, 5, 6, 7, synth.seed(0, 11))
