@@ -599,6 +599,18 @@ def test_decoder_temporal_grow_layerwise(order):
     assert_stack_close(got, ref, "decoder tg %s" % order)
 
 
+@pytest.mark.parametrize("fold", [False, True])
+def test_decoder_full_channels_one_latent_chunks(fold):
+    """Every chunk one latent (the first grows to 1 frame, the rest to 4): each
+    layer's window is mostly its cache, and the folded growing convs take their
+    history grouping on every chunk."""
+    say("decoder full channels, one-latent chunks, fold=%s" % fold)
+    got, ref, _ = _decoder_layerwise(48, OM.DECODER_STAGES, t=4, h=2, w=3, splits=[1, 1, 1, 1],
+                                     fold_upsample=fold)
+    assert got.shape == (3, OM.output_frames(4), 32, 48)
+    assert_stack_close(got, ref, "decoder one-latent chunks")
+
+
 def test_decoder_full_channels_two_clips():
     """The whole decoder end to end at reduced spatial size: latent 48 x 13 x
     4x6 in the benchmark's clips (7 then 6 latents) -> RGB 3 x 49 x 64x96, every
