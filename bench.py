@@ -232,8 +232,9 @@ def setup_c3(dev, torch, synth, P, S, fold=False):
 def _counter_record(kernel_name):
     """The fields of `kernel_name`'s record in a committed PMC summary in
     profiles/ (a "traffic_record:" line), or None when no record exists or a
-    source it names (comma-separated: the kernel, and the op list that sets its
-    launches) changed since the counters were taken."""
+    source it names (comma-separated: the kernel, the op list that sets its
+    launches, the build script that holds its compiler flags) changed since the
+    counters were taken."""
     import glob
     import hashlib
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
