@@ -173,6 +173,79 @@ def test_bf16_conv_tiny_frames(case):
     assert_bf16_close(got, ref, "tiny frame conv")
 
 
+def _random_conv_cases(n, seed):
+    """Seeded draws over what a bf16 conv plan accepts: channels (multiples of 8),
+    kernel shapes, nearest 2x in space and time, frame sizes, chunkings, history
+    fills and the folding request -- so that combinations the listed cases miss
+    still meet the definition."""
+    rng = np.random.RandomState(seed)
+    cases = []
+    for _ in range(n):
+        k = [(3, 3, 3), (3, 3, 3), (1, 1, 1), (3, 1, 1), (2, 3, 3), (1, 3, 3)][rng.randint(6)]
+        cin = int(rng.choice([8, 16, 32, 48, 64, 96, 128, 192]))
+        cout = int(rng.choice([1, 2, 3, 8, 16, 24, 96, 192]))
+        up_s, up_t = int(rng.randint(1, 3)), int(rng.randint(1, 3))
+        h, w = int(rng.randint(1, 14)), int(rng.randint(1, 40))
+        splits = [int(v) for v in rng.randint(1, 4, size=rng.randint(1, 4))]
+        tpad = [C.TPAD_REPLICATE, C.TPAD_ZERO][rng.randint(2)]
+        cases.append((cin, cout, k, up_s, up_t, h, w, splits, tpad, bool(rng.randint(2)), bool(rng.randint(2))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_conv_cases(24, 2026), ids=lambda c: "ci%d_co%d_k%d%d%d_up%d%d_%dx%d" % (
+    c[0], c[1], c[2][0], c[2][1], c[2][2], c[3], c[4], c[5], c[6]))
+def test_bf16_conv_random_shapes(case):
+    cin, cout, k, up_s, up_t, h, w, splits, tpad, with_bias, fold = case
+    say("bf16 conv, random shape %s" % (case,))
+    x = synth.bf16(synth.video(cin, sum(splits), h, w, synth.seed(5, 61)))
+    wt = synth.bf16(synth.conv_weight(cout, cin, *k, synth.seed(5, 62)))
+    b = synth.bias(cout, synth.seed(5, 63)) if with_bias else None
+    ref = O.one_shot(to_oracle(x), to_oracle(wt), None if b is None else to_oracle(b), TP[tpad], up_s, up_t)
+    plan = P.conv_plan(wt.cuda(), h, w, bias=None if b is None else b.cuda(), up_s=up_s, up_t=up_t,
+                       max_chunk_t=max(splits), tpad=tpad, fold_upsample=fold)
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits))
+    assert_bf16_close(got, ref, "random-shape conv")
+
+
+def _random_epilogue_cases(n, seed):
+    """Seeded draws as above with the epilogue as well: a residual added before
+    the store, the pre-activation of the stored sum, or both."""
+    rng = np.random.RandomState(seed)
+    cases = []
+    for _ in range(n):
+        k = [(3, 3, 3), (3, 3, 3), (1, 1, 1), (3, 1, 1)][rng.randint(4)]
+        cin = int(rng.choice([16, 32, 64, 96, 192]))
+        cout = int(rng.choice([8, 16, 24, 96, 96, 192, 256, 384]))
+        up_s, up_t = int(rng.randint(1, 3)), int(rng.randint(1, 3))
+        h, w = int(rng.randint(1, 12)), int(rng.randint(1, 36))
+        splits = [int(v) for v in rng.randint(1, 4, size=rng.randint(1, 4))]
+        tpad = [C.TPAD_REPLICATE, C.TPAD_ZERO][rng.randint(2)]
+        epi = [(True, False), (False, True), (True, True)][rng.randint(3)]
+        cases.append((cin, cout, k, up_s, up_t, h, w, splits, tpad, epi[0], epi[1], bool(rng.randint(2))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_epilogue_cases(16, 7), ids=lambda c: "ci%d_co%d_k%d%d%d_up%d%d_r%d_a%d" % (
+    c[0], c[1], c[2][0], c[2][1], c[2][2], c[3], c[4], c[9], c[10]))
+def test_bf16_conv_random_epilogues(case):
+    cin, cout, k, up_s, up_t, h, w, splits, tpad, residual, act, fold = case
+    say("bf16 conv, random epilogue %s" % (case,))
+    x = synth.bf16(synth.video(cin, sum(splits), h, w, synth.seed(5, 71)))
+    wt = synth.bf16(synth.conv_weight(cout, cin, *k, synth.seed(5, 72)))
+    b = synth.bias(cout, synth.seed(5, 73))
+    g = synth.gain(cout, synth.seed(5, 74))
+    v = O.one_shot(to_oracle(x), to_oracle(wt), to_oracle(b), TP[tpad], up_s, up_t)
+    r = synth.bf16(synth.video(cout, *v.shape[1:], synth.seed(5, 75))) if residual else None
+    if residual:
+        v = v + to_oracle(r)
+    ref = O.act(O.round_bf16(v), to_oracle(g), 1e-6) if act else v
+    plan = P.conv_plan(wt.cuda(), h, w, bias=b.cuda(), gamma=g.cuda() if act else None, up_s=up_s, up_t=up_t,
+                       max_chunk_t=max(splits), tpad=tpad, residual=residual, act=act, fold_upsample=fold)
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits,
+                                     residual_cl=to_device_cl(r) if residual else None))
+    assert_bf16_close(got, ref, "random epilogue")
+
+
 @pytest.mark.parametrize("k,up_s", [((1, 1, 1), 2), ((3, 1, 1), 1)])
 def test_bf16_pointwise_conv_residual(k, up_s):
     """The pointwise kernel's epilogue: + bias + residual, stored as bf16."""
