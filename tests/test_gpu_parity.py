@@ -684,6 +684,42 @@ def test_decoder_full_channels_one_latent_chunks(fold):
     assert_stack_close(got, ref, "decoder one-latent chunks")
 
 
+def _random_decoder_cases(n, seed):
+    """Seeded decoder configurations: two or three stages of random widths and
+    temporal factors, latent width, frame size, chunking, TemporalGrow order,
+    first-chunk growth rule and the folding request."""
+    rng = np.random.RandomState(seed)
+    cases = []
+    for _ in range(n):
+        nst = int(rng.randint(2, 4))
+        stages = tuple((int(rng.choice([16, 32, 64, 96, 128, 192])), int(rng.randint(1, 3))) for _ in range(nst))
+        c_lat = int(rng.choice([8, 16, 32, 48]))
+        t, h, w = int(rng.randint(2, 6)), int(rng.randint(1, 5)), int(rng.randint(1, 7))
+        splits, left = [], t
+        while left:
+            k = int(rng.randint(1, left + 1))
+            splits.append(k)
+            left -= k
+        tg = [None, "before", "after"][rng.randint(3)]
+        cases.append((c_lat, stages, t, h, w, splits, tg, bool(rng.randint(2)), bool(rng.randint(2))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_decoder_cases(8, 11), ids=lambda c: "cl%d_%s_t%d_%dx%d_tg%s_al%d_f%d" % (
+    c[0], "-".join("%dx%d" % s_ for s_ in c[1]), c[2], c[3], c[4], c[6], c[7], c[8]))
+def test_decoder_random_configs(case):
+    """Every layer of randomly drawn decoder configurations against the oracle,
+    the stack end to end, and the production slot wiring bitwise equal to the
+    unique-slot one."""
+    c_lat, stages, t, h, w, splits, tg, aligned, fold = case
+    say("decoder random config %s" % (case,))
+    got, ref, _ = _decoder_layerwise(c_lat, stages, t=t, h=h, w=w, splits=splits, cfg=9, temporal_grow=tg,
+                                     aligned=aligned, fold_upsample=fold)
+    up = 2 ** (len(stages) + 1)  # each stage and the head double the frame size
+    assert got.shape == (3, OM.output_frames(t, [f for _, f in stages], aligned=aligned), h * up, w * up)
+    assert_stack_close(got, ref, "decoder random config")
+
+
 def test_decoder_full_channels_two_clips():
     """The whole decoder end to end at reduced spatial size: latent 48 x 13 x
     4x6 in the benchmark's clips (7 then 6 latents) -> RGB 3 x 49 x 64x96, every
