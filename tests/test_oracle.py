@@ -295,6 +295,33 @@ def test_resblock_definition_and_chunking():
     assert np.max(np.abs(got - ref)) <= 1e-12
 
 
+def test_upstage_against_torch_primitives():
+    """UpStage = conv2(act(conv1(nearest 2x up of x))), the act taking conv2's
+    gain, rebuilt from torch primitives -- repeat_interleave for the nearest
+    upsample, the first frame repeated twice ahead of the sequence for the causal
+    temporal padding, F.conv3d with zero spatial padding, RMSNorm over channels
+    and x * sigmoid(x) written out -- and run by the oracle in uneven chunks."""
+    r = _rng(21)
+    cin, cmid, cout, t = 3, 5, 4, 6
+    p1 = _params(r, cmid, cin, gain=False, bias=True)
+    p2 = _params(r, cout, cmid, bias=True)
+    x = r.standard_normal((cin, t, 2, 3))
+    eps = 1e-6
+
+    def conv(v, p):
+        v = torch.cat([v[:, :1], v[:, :1], v], dim=1)
+        return F.conv3d(v[None], torch.from_numpy(p["w"]), torch.from_numpy(p["b"]), padding=(0, 1, 1))[0]
+
+    xt = torch.from_numpy(x).repeat_interleave(2, dim=2).repeat_interleave(2, dim=3)
+    h = conv(xt, p1)
+    nh = h / torch.sqrt((h * h).mean(dim=0, keepdim=True) + eps) * torch.from_numpy(p2["g"])[:, None, None, None]
+    ref = conv(nh * torch.sigmoid(nh), p2).numpy()
+    stage = M.UpStage(p1, p2, eps)
+    got = np.concatenate([stage.step(x[:, a:b]) for a, b in ((0, 1), (1, 4), (4, 6))], axis=1)
+    assert got.shape == (cout, t, 4, 6)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
 def test_decoder_shapes_and_causality():
     r = _rng(18)
     stages = ((6, 2), (5, 2), (4, 1))
