@@ -32,7 +32,9 @@ def _run_chunks(plan, x_cl, splits, residual_cl=None):
             tn = plan.output_shape(n, first)[0]
             res = residual_cl[r0:r0 + tn].clone()  # a fresh (16-byte aligned) buffer
             r0 += tn
-        outs.append(st.step(x_cl[t0:t0 + n].contiguous(), residual=res))
+        # a fresh buffer: a slice of frames whose byte size is not a multiple
+        # of 16 would break the library's 16-byte alignment rule
+        outs.append(st.step(x_cl[t0:t0 + n].clone(), residual=res))
         t0 += n
     torch.cuda.synchronize()
     return torch.cat(outs, dim=0)
@@ -68,6 +70,38 @@ def test_fp32_conv_tiny_frames(h, w, k, up_s, up_t, tpad):
     plan = P.conv_plan(wt.cuda(), h, w, bias=b.cuda(), up_s=up_s, up_t=up_t, max_chunk_t=3, tpad=tpad)
     got = from_device_cl(_run_chunks(plan, to_device_cl(x), [1, 3, 1]))
     assert_fp32_close(got, ref, "fp32 tiny frame")
+
+
+def _random_fp32_cases(n, seed):
+    """Seeded draws for the fp32 conv: any channel counts (no multiple-of-8
+    rule), kernel shapes, nearest 2x in space and time, frame sizes, chunkings,
+    history fills, with and without bias."""
+    rng = np.random.RandomState(seed)
+    cases = []
+    for _ in range(n):
+        k = [(3, 3, 3), (3, 3, 3), (1, 1, 1), (3, 1, 1), (2, 3, 3), (1, 3, 3), (2, 1, 3)][rng.randint(7)]
+        cin, cout = int(rng.randint(1, 40)), int(rng.randint(1, 40))
+        up_s, up_t = int(rng.randint(1, 3)), int(rng.randint(1, 3))
+        h, w = int(rng.randint(1, 12)), int(rng.randint(1, 30))
+        splits = [int(v) for v in rng.randint(1, 4, size=rng.randint(1, 4))]
+        tpad = [C.TPAD_REPLICATE, C.TPAD_ZERO][rng.randint(2)]
+        cases.append((cin, cout, k, up_s, up_t, h, w, splits, tpad, bool(rng.randint(2))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_fp32_cases(16, 5), ids=lambda c: "ci%d_co%d_k%d%d%d_up%d%d_%dx%d" % (
+    c[0], c[1], c[2][0], c[2][1], c[2][2], c[3], c[4], c[5], c[6]))
+def test_fp32_conv_random_shapes(case):
+    cin, cout, k, up_s, up_t, h, w, splits, tpad, with_bias = case
+    say("fp32 conv, random shape %s" % (case,))
+    x = synth.video(cin, sum(splits), h, w, synth.seed(0, 51))
+    wt = synth.conv_weight(cout, cin, *k, synth.seed(0, 52))
+    b = synth.bias(cout, synth.seed(0, 53)) if with_bias else None
+    ref = O.one_shot(to_oracle(x), to_oracle(wt), None if b is None else to_oracle(b), TP[tpad], up_s, up_t)
+    plan = P.conv_plan(wt.cuda(), h, w, bias=None if b is None else b.cuda(), up_s=up_s, up_t=up_t,
+                       max_chunk_t=max(splits), tpad=tpad)
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits))
+    assert_fp32_close(got, ref, "random-shape fp32 conv")
 
 
 def test_fp32_memoryblock_zero_history_with_bias_and_upsample():
@@ -480,6 +514,31 @@ def test_cache_in_untouched_and_aliasing_rejected():
     # host memory is refused
     with pytest.raises(ValueError):
         plan.forward_chunk(x[:1].cpu().contiguous(), s1, s2)
+
+
+def test_misaligned_chunk_rejected_state_unchanged():
+    """A chunk pointer off 16-byte alignment (31 fp32 channels: a 3x26 frame is
+    9672 bytes, so the slice from frame 1 starts 8 bytes off) is refused with
+    EINVAL before anything runs; the stream then continues from the same state
+    and matches the definition."""
+    say("boundary: misaligned chunk")
+    cin, cout, h, w = 31, 5, 3, 26
+    x = synth.video(cin, 4, h, w, synth.seed(7, 21))
+    wt = synth.conv_weight(cout, cin, 3, 3, 3, synth.seed(7, 22))
+    ref = O.causal_conv3d(to_oracle(x), to_oracle(wt), None, O.REPLICATE)
+    plan = P.conv_plan(wt.cuda(), h, w, max_chunk_t=3)
+    x_cl = to_device_cl(x)
+    st = P.Stream(plan)
+    y0 = st.step(x_cl[:1].clone())
+    bad = x_cl[1:4]
+    assert bad.data_ptr() % 16 == 8
+    with pytest.raises(C.Cc3dError) as e:
+        st.step(bad)
+    assert e.value.status == C.EINVAL and "16-byte" in str(e.value)
+    assert st.frames_seen == 1
+    y1 = st.step(bad.clone())
+    torch.cuda.synchronize()
+    assert_fp32_close(from_device_cl(torch.cat([y0, y1])), ref, "after a refused chunk")
 
 
 def test_transposes_roundtrip():
