@@ -535,3 +535,97 @@ def test_aligned_schedule_golden():
     assert M.output_frames(7, aligned=True) == int(g["first_chunk_read"])
     assert M.output_frames(7, aligned=True) - int(g["first_chunk_dropped"]) == M.output_frames(7)
     assert M.output_frames(6, aligned=True) == int(g["clip_len"])
+
+
+# ------------------------- the decoder's composition, rebuilt from primitives --
+
+def _t_causal(v, p, mode):
+    """One-shot causal conv of a [C][T][H][W] float64 tensor with torch's conv3d:
+    k_t-1 history frames (copies of frame 0, or zeros) ahead of the sequence,
+    zero spatial padding of (k-1)/2."""
+    w = torch.from_numpy(p["w"])
+    kt, kh, kw = w.shape[2:]
+    first = v[:, :1] if mode == O.REPLICATE else torch.zeros_like(v[:, :1])
+    v = torch.cat([first] * (kt - 1) + [v], dim=1)
+    b = None if p.get("b") is None else torch.from_numpy(p["b"])
+    return F.conv3d(v[None], w, b, padding=(0, (kh - 1) // 2, (kw - 1) // 2))[0]
+
+
+def _t_act(v, g, eps=1e-6):
+    n = v / torch.sqrt((v * v).mean(dim=0, keepdim=True) + eps) * torch.from_numpy(g)[:, None, None, None]
+    return n * torch.sigmoid(n)
+
+
+def _t_up2(v):
+    return v.repeat_interleave(2, dim=2).repeat_interleave(2, dim=3)
+
+
+def _t_grow(v, factor, aligned):
+    """Frame growth of the whole video: factor 1 keeps it; factor 2 doubles every
+    frame after the first (the first too under the aligned rule)."""
+    if factor == 1:
+        return v
+    if aligned:
+        return v.repeat_interleave(2, dim=1)
+    return torch.cat([v[:, :1], v[:, 1:].repeat_interleave(2, dim=1)], dim=1)
+
+
+def _t_decoder(params, x, stages, temporal_grow, aligned, mode):
+    """The decoder of reading B composed one-shot over the whole video from torch
+    primitives, written apart from oracle/model.py: conv_in; per stage [nearest
+    2x in space (and the stage's growth in time) -> conv -> two residual blocks
+    x + conv2(act(conv1(act(x))))], where a TemporalGrow (1x1x1 projection,
+    growth, causal 3x1x1 conv) takes over the stage's growth, either at the
+    stage's input size ("before") or on the upsampled positions ("after"); head:
+    act at the low size -> nearest 2x -> conv to RGB."""
+    h = _t_causal(torch.from_numpy(x), params["conv_in"], mode)
+    for si, (_, factor) in enumerate(stages):
+        if temporal_grow is None:
+            h = _t_causal(_t_grow(_t_up2(h), factor, aligned), params["s%d.up" % si], mode)
+        else:
+            if temporal_grow == "after":
+                h = _t_up2(h)
+            q = _t_causal(h, params["s%d.tg.p" % si], mode)
+            q = _t_causal(_t_grow(q, factor, aligned), params["s%d.tg.t" % si], mode)
+            h = _t_causal(q if temporal_grow == "after" else _t_up2(q), params["s%d.up" % si], mode)
+        for r in range(2):
+            p1, p2 = params["s%d.rb%d.c1" % (si, r)], params["s%d.rb%d.c2" % (si, r)]
+            h = h + _t_causal(_t_act(_t_causal(_t_act(h, p1["g"]), p1, mode), p2["g"]), p2, mode)
+    return _t_causal(_t_up2(_t_act(h, params["head"]["g"])), params["head"], mode).numpy()
+
+
+DECODER_PIN_CASES = [
+    # stages, temporal_grow, aligned, history, chunks
+    (((6, 2), (5, 2), (4, 1)), None, False, O.REPLICATE, (1, 2, 1)),
+    (((6, 2), (5, 2), (4, 1)), None, True, O.REPLICATE, (3, 1)),
+    (((5, 1), (4, 2)), None, False, O.ZERO, (2, 2)),
+    (((6, 2), (5, 2), (4, 1)), "before", False, O.REPLICATE, (2, 2)),
+    (((6, 2), (5, 2), (4, 1)), "after", False, O.REPLICATE, (1, 3)),
+    (((5, 2), (4, 1)), "before", True, O.ZERO, (1, 1, 2)),
+]
+
+
+@pytest.mark.parametrize("case", DECODER_PIN_CASES, ids=lambda c: "%dst_tg%s_al%d_%s" % (
+    len(c[0]), c[1], c[2], c[3]))
+def test_decoder_against_torch_primitives(case):
+    """oracle/model.py's Decoder, run chunk by chunk with per-layer caches, equals
+    the same decoder composed one-shot from torch primitives (F.conv3d on
+    explicitly padded input, repeat_interleave for the nearest upsample and the
+    frame growth, RMSNorm and x * sigmoid(x) written out) to 1e-12: a dropped or
+    misplaced act, residual, gain, stage or growth in the oracle's wiring fails."""
+    stages, tg, aligned, mode, chunks = case
+    r = _rng(40 + DECODER_PIN_CASES.index(case))
+    c_lat = 3
+    params = _decoder_params(r, stages, c_lat, tg)
+    x = r.standard_normal((c_lat, sum(chunks), 2, 3))
+    ref = _t_decoder(params, x, stages, tg, aligned, mode)
+    dec = M.Decoder(params, stages=stages, temporal_grow=tg, aligned=aligned, mode=mode)
+    got, t0 = [], 0
+    for n in chunks:
+        got.append(dec.step(x[:, t0:t0 + n]))
+        t0 += n
+    got = np.concatenate(got, axis=1)
+    up = 2 ** (len(stages) + 1)
+    assert got.shape == ref.shape == (3, M.output_frames(sum(chunks), [f for _, f in stages], aligned=aligned),
+                                      2 * up, 3 * up)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
