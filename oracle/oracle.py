@@ -254,16 +254,22 @@ class CausalConvStream:
             v = upsample_temporal(v, first=(self.frames_seen == 0), aligned=self.aligned)
         return v
 
-    def step(self, x: np.ndarray) -> np.ndarray:
-        v = self.logical_input(x)  # low spatial resolution, grown in time
+    def window(self, x: np.ndarray) -> np.ndarray:
+        """Z = cache || the chunk's logical input (low spatial resolution, grown in
+        time); the cache becomes the last k_t-1 frames of Z and the frame count
+        moves on by the chunk's frames."""
+        v = self.logical_input(x)
         if self.frames_seen == 0:
             self.cache = history(v[:, 0], self.kt - 1, self.mode)
         z = np.concatenate([self.cache, v], axis=1)
-        zs = upsample_spatial(z, self.up_s) if self.up_s > 1 else z
-        y = conv_valid(zs, self.w, self.bias, self.nthreads)
         self.cache = z[:, z.shape[1] - (self.kt - 1):].copy()
         self.frames_seen += x.shape[1]
-        return y
+        return z
+
+    def step(self, x: np.ndarray) -> np.ndarray:
+        z = self.window(x)
+        zs = upsample_spatial(z, self.up_s) if self.up_s > 1 else z
+        return conv_valid(zs, self.w, self.bias, self.nthreads)
 
 
 def one_shot(x, w, bias=None, mode=REPLICATE, up_s=1, up_t=1, nthreads=None, aligned=False):

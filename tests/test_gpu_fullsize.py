@@ -32,25 +32,31 @@ pytestmark = pytest.mark.gpu
 EPS = 1e-6
 
 
-def _grow(v, first):
-    """Nearest 2x in time on non-first frames, on a [T][H][W][C] device tensor."""
-    if first:
-        return torch.cat([v[:1], v[1:].repeat_interleave(2, dim=0)])
-    return v.repeat_interleave(2, dim=0)
-
-
 class Window:
-    """The causal window Z = history || V of one conv op, on the device."""
+    """The causal window Z = history || V of one conv op, on the device.  Which
+    input frame each window frame holds is the oracle's own stream rule
+    (oracle.CausalConvStream.window: history fill, temporal growth, cache of the
+    last k_t-1 frames) run on frame numbers (0 = a zero frame); the frames are
+    the op's GPU input frames, gathered on the device."""
 
-    def __init__(self, kt, up_t):
-        self.kt, self.up_t, self.hist = kt, up_t, None
+    def __init__(self, kt, up_t, mode=O.REPLICATE, aligned=False):
+        self.rule = O.CausalConvStream(np.zeros((1, 1, kt, 1, 1)), None, mode, 1, up_t, aligned=aligned)
+        self.frames, self.seen = {}, 0
 
     def step(self, x, first):
-        v = _grow(x, first) if self.up_t == 2 else x
-        if first:  # REPLICATE history: copies of the first frame
-            self.hist = v[:1].expand(self.kt - 1, *v.shape[1:])
-        z = torch.cat([self.hist, v])
-        self.hist = z[z.shape[0] - (self.kt - 1):].clone()
+        if first:
+            self.rule.reset()
+            self.frames, self.seen = {}, 0
+        n = x.shape[0]
+        nums = np.arange(self.seen + 1, self.seen + n + 1, dtype=np.float64).reshape(1, n, 1, 1)
+        for i in range(n):
+            self.frames[self.seen + 1 + i] = x[i]
+        self.seen += n
+        z_nums = [int(k) for k in self.rule.window(nums)[0, :, 0, 0]]
+        zero = torch.zeros_like(x[0])
+        z = torch.stack([self.frames[k] if k > 0 else zero for k in z_nums])
+        keep = [int(k) for k in self.rule.cache[0, :, 0, 0] if k > 0]
+        self.frames = {k: self.frames[k].clone() for k in keep}
         return z
 
 
