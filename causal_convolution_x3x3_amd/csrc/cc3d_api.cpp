@@ -960,8 +960,8 @@ cc3d_status cc3d_forward_chunk(const cc3d_plan* p, const void* x, int t_chunk, c
 cc3d_status cc3d_slot_shape(const cc3d_plan* p, int slot, int t_chunk, int first, int* c, int* t, int* h, int* w)
 {
     if (!plan_ok(p)) return fail(CC3D_EINVAL, "plan is NULL or destroyed");
-    if (slot <= CC3D_SLOT_AUX || slot >= CC3D_MAX_SLOTS || !p->slots[slot].defined)
-        return fail(CC3D_EINVAL, "slot %d is not an intermediate slot of this plan", slot);
+    if (slot < CC3D_SLOT_AUX || slot >= CC3D_MAX_SLOTS || !p->slots[slot].defined)
+        return fail(CC3D_EINVAL, "slot %d is not an intermediate or residual slot of this plan", slot);
     if (t_chunk < 1 || t_chunk > p->max_t) return fail(CC3D_ESHAPE, "t_chunk=%d not in [1, %d]", t_chunk, p->max_t);
     const Slot& s = p->slots[slot];
     if (s.grouped)
@@ -977,6 +977,7 @@ cc3d_status cc3d_slot_shape(const cc3d_plan* p, int slot, int t_chunk, int first
 cc3d_status cc3d_slot_read(const cc3d_plan* p, int slot, int t_chunk, int first, void* dst, size_t dst_bytes,
                            void* stream)
 {
+    if (slot == CC3D_SLOT_AUX) return fail(CC3D_EINVAL, "slot %d is the caller's residual argument", slot);
     int c = 0, t = 0, h = 0, w = 0;
     cc3d_status st = cc3d_slot_shape(p, slot, t_chunk, first, &c, &t, &h, &w);
     if (st != CC3D_OK) return st;

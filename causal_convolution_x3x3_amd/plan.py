@@ -87,16 +87,21 @@ class Op:
 
 
 class Plan:
-    """A created plan (single conv or stack) with its forward/reset calls."""
+    """A created plan (single conv or stack) with its forward/reset calls.
+    ``cin``, ``h``, ``w``: the chunk input's channels and frame size; x is
+    [T][h][w][cin] of the plan dtype."""
 
-    def __init__(self, handle: ctypes.c_void_p, dtype: int, device):
+    def __init__(self, handle: ctypes.c_void_p, dtype: int, device, cin: int, h: int, w: int):
         self._h = handle
         self.dtype = dtype
         self.device = device
+        self.in_shape = (int(h), int(w), int(cin))
         L = C.lib()
         self.state_bytes = int(L.cc3d_state_bytes(self._h))
         self.device_bytes = int(L.cc3d_plan_device_bytes(self._h))
         self.out_dtype = torch.uint8 if L.cc3d_output_elem_bytes(self._h) == 1 else _TD[dtype]
+        # whether forward_chunk reads a residual argument (the residual slot is defined)
+        self.takes_residual = L.cc3d_slot_shape(self._h, C.SLOT_AUX, 1, 1, None, None, None, None) == C.OK
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -139,8 +144,25 @@ class Plan:
     def forward_chunk(self, x: torch.Tensor, cache_in: State, cache_out: State,
                       residual: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
                       stream=None) -> torch.Tensor:
+        """Decode one chunk x [T][h][w][cin] (plan dtype).  The library sees only
+        pointers, so every tensor's shape and dtype is checked here, before any
+        call: a smaller or wrongly typed buffer would be read past its end.
+        Returns y viewed as the chunk's output shape."""
+        if x.dim() != 4 or tuple(x.shape[1:]) != self.in_shape or x.dtype != _TD[self.dtype]:
+            raise ValueError("x must be [T][%d][%d][%d] of %s, got %s of %s"
+                             % (self.in_shape + (_TD[self.dtype], tuple(x.shape), x.dtype)))
         t_chunk = x.shape[0]
-        shape = self.output_shape(t_chunk, cache_in.frames_seen == 0)
+        first = cache_in.frames_seen == 0
+        shape = self.output_shape(t_chunk, first)
+        if residual is not None or self.takes_residual:
+            if not self.takes_residual:
+                raise ValueError("this plan takes no residual")
+            if residual is None:
+                raise ValueError("this plan adds a residual; pass one")
+            rshape = self.slot_shape(C.SLOT_AUX, t_chunk, first)
+            if tuple(residual.shape) != rshape or residual.dtype != _TD[self.dtype]:
+                raise ValueError("residual must be %s of %s, got %s of %s"
+                                 % (rshape, _TD[self.dtype], tuple(residual.shape), residual.dtype))
         if y is None:
             y = torch.empty(shape, dtype=self.out_dtype, device=self.device)
         elif y.dtype != self.out_dtype or y.numel() < _numel(shape):
@@ -150,7 +172,7 @@ class Plan:
         C.check(C.lib().cc3d_forward_chunk(self._h, _ptr(x), t_chunk, ctypes.byref(ci), ctypes.byref(co),
                                            _ptr(residual), _ptr(y), _stream(stream)), "cc3d_forward_chunk")
         cache_out.frames_seen = co.frames_seen
-        return y
+        return y if tuple(y.shape) == shape else y.reshape(-1)[:_numel(shape)].view(shape)
 
 
 def conv_plan(w: torch.Tensor, h_in: int, w_in: int, *, bias=None, gamma=None, up_s=1, up_t=1,
@@ -160,6 +182,11 @@ def conv_plan(w: torch.Tensor, h_in: int, w_in: int, *, bias=None, gamma=None, u
     ``aligned``: the first chunk doubles every frame at up_t = 2 (CC3D_GROW_ALIGNED).
     ``fold_upsample``: phase-folded kernel for an upsampling 3x3 conv where it applies."""
     cout, cin, kt, kh, kw = w.shape
+    if w.dtype not in _DT:
+        raise ValueError("weights must be bfloat16 or float32, got %s" % w.dtype)
+    for name, v, n in (("bias", bias, cout), ("gamma", gamma, cout)):
+        if v is not None and (v.dtype != torch.float32 or v.numel() != n):
+            raise ValueError("%s must hold %d float32 values, got %d of %s" % (name, n, v.numel(), v.dtype))
     d = C.ConvDesc(cin=cin, cout=cout, kt=kt, kh=kh, kw=kw, h_in=h_in, w_in=w_in, up_s=up_s, up_t=up_t,
                    max_chunk_t=max_chunk_t, dtype=_DT[w.dtype], tpad=tpad,
                    epilogue=(C.EPI_RESIDUAL if residual else 0) | (C.EPI_ACT if act else 0) |
@@ -169,13 +196,20 @@ def conv_plan(w: torch.Tensor, h_in: int, w_in: int, *, bias=None, gamma=None, u
     with torch.cuda.device(w.device):
         C.check(C.lib().cc3d_plan_create(ctypes.byref(d), _ptr(w), _ptr(bias), _ptr(gamma), _stream(stream),
                                          ctypes.byref(h)), "cc3d_plan_create")
-    return Plan(h, d.dtype, w.device)
+    return Plan(h, d.dtype, w.device, cin, h_in, w_in)
 
 
-def _check_weights(ops: List[Op], cin: int):
+def _check_weights(ops: List[Op], cin: int, dtype):
     """Each CONV op's weights must hold exactly [cout][channels of its src][k]
-    (the library reads that many elements through the pointer)."""
+    of the plan dtype, and every bias and gain its channel count of float32 (the
+    library reads that many elements through the pointer)."""
     ch = {C.SLOT_X: cin}
+
+    def vec(i, o, name, v, n):
+        if v is not None and n is not None and (v.dtype != torch.float32 or v.numel() != n):
+            raise ValueError("op %d (%s): %s must hold %d float32 values, got %d of %s"
+                             % (i, o.name, name, n, v.numel(), v.dtype))
+
     for i, o in enumerate(ops):
         c_src = ch.get(o.src)
         if o.kind == C.OP_CONV:
@@ -184,9 +218,13 @@ def _check_weights(ops: List[Op], cin: int):
             want = (o.cout, c_src) + tuple(o.k)
             if c_src is not None and tuple(o.w.shape) != want:
                 raise ValueError("op %d (%s): weights %s, expected %s" % (i, o.name, tuple(o.w.shape), want))
+            if o.w.dtype != dtype:
+                raise ValueError("op %d (%s): weights are %s, the plan is %s" % (i, o.name, o.w.dtype, dtype))
+            vec(i, o, "bias", o.bias, o.cout)
             c_out = o.cout
         else:
             c_out = c_src
+        vec(i, o, "gamma", o.gamma, c_out)
         for sl in (o.out, o.act_out):
             if sl != C.SLOT_NONE and c_out is not None:
                 ch[sl] = c_out
@@ -199,7 +237,7 @@ def stack_plan(ops: List[Op], cin: int, h: int, w: int, *, dtype=torch.bfloat16,
     ``frame_batch`` > 0: ops[batch_from:] run in batches of that many frames of
     their input (frame batching, see cc3d_stack_desc).  ``fold_upsample``: the
     phase-folded kernel for every upsampling 3x3 conv it applies to."""
-    _check_weights(ops, cin)
+    _check_weights(ops, cin, dtype)
     arr = (C.OpDesc * len(ops))()
     for i, o in enumerate(ops):
         kt, kh, kw = o.k
@@ -215,7 +253,7 @@ def stack_plan(ops: List[Op], cin: int, h: int, w: int, *, dtype=torch.bfloat16,
     with torch.cuda.device(device):
         C.check(C.lib().cc3d_stack_plan_create(ctypes.byref(d), _stream(stream), ctypes.byref(hnd)),
                 "cc3d_stack_plan_create")
-    return Plan(hnd, d.dtype, device)
+    return Plan(hnd, d.dtype, device, cin, h, w)
 
 
 class Stream:

@@ -283,9 +283,11 @@ cc3d_status cc3d_to_channels_first(const void* src_thwc, void* dst_cthw, int c, 
 
 /* Intermediate slots (index >= 3) hold what the last forward_chunk wrote, until
  * the next forward_chunk on the plan.  cc3d_slot_shape gives a slot's shape for a
- * chunk of t_chunk input frames; cc3d_slot_read copies its contents for that
- * chunk (dst: device, at least c*t*h*w elements of the plan dtype) on stream.
- * Used to inspect every layer of a stack (layer-wise parity checks). */
+ * chunk of t_chunk input frames (also for CC3D_SLOT_AUX, the shape forward_chunk's
+ * residual must have, when the plan reads one); cc3d_slot_read copies an
+ * intermediate slot's contents for that chunk (dst: device, at least c*t*h*w
+ * elements of the plan dtype) on stream.  Used to inspect every layer of a stack
+ * (layer-wise parity checks). */
 cc3d_status cc3d_slot_shape(const cc3d_plan* plan, int slot, int t_chunk, int first, int* c, int* t,
                             int* h, int* w);
 cc3d_status cc3d_slot_read(const cc3d_plan* plan, int slot, int t_chunk, int first, void* dst,

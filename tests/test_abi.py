@@ -151,7 +151,7 @@ def test_decoder_wiring_passes_library_checks(temporal_grow, aligned):
         params[name] = {"w": torch.empty((co, ci, kt, kh, kw), dtype=torch.bfloat16),
                         "g": torch.empty(ci) if g else None}
     ops = S.decoder_ops(params, stages=stages, temporal_grow=temporal_grow)
-    P._check_weights(ops, 16)
+    P._check_weights(ops, 16, torch.bfloat16)
     tg_ops = [o for o in ops if ".tg." in o.name]
     assert len(tg_ops) == (6 if temporal_grow else 0)
     for o in tg_ops:
@@ -169,7 +169,7 @@ def test_weight_shape_mismatch_is_caught_by_the_binding():
     from causal_convolution_x3x3_amd import plan as P
     w = torch.empty((16, 8, 3, 3, 3), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
-        P._check_weights([P.Op(cout=16, w=w, out=C.SLOT_Y)], 16)
+        P._check_weights([P.Op(cout=16, w=w, out=C.SLOT_Y)], 16, torch.bfloat16)
     with pytest.raises(ValueError):
         P.Op(cout=8, w=w, out=C.SLOT_Y)
     assert P.Op(cout=16, w=torch.empty((16, 16, 3, 1, 1)), out=C.SLOT_Y).k == (3, 1, 1)
@@ -232,3 +232,29 @@ def test_valid_descriptors_pass_validation():
     d, keep = _stack([C.OpDesc(**dict(norm, src=C.SLOT_X, act_out=3)),
                       C.OpDesc(**dict(norm, src=3, res=C.SLOT_X, out=4, act_out=C.SLOT_Y))])
     assert L.cc3d_stack_plan_create(ctypes.byref(d), None, ctypes.byref(out)) == C.EDEVICE, C.last_error()
+
+
+def test_binding_refuses_misshaped_input_before_any_library_call(monkeypatch):
+    """The C ABI sees only pointers, so the binding checks x against the plan's
+    frame size, channels and dtype before it calls anything: a smaller or
+    wrongly typed x would otherwise be read past its end on the device."""
+    import torch
+
+    from causal_convolution_x3x3_amd import plan as P
+
+    def no_call():
+        raise AssertionError("the library was called")
+
+    plan = object.__new__(P.Plan)
+    plan._h, plan.dtype, plan.device = None, C.BF16, torch.device("cpu")
+    plan.in_shape, plan.takes_residual = (8, 6, 16), False
+    monkeypatch.setattr(P.C, "lib", no_call)
+    st_in, st_out = object.__new__(P.State), object.__new__(P.State)
+    st_in.frames_seen = st_out.frames_seen = 0
+    for bad in (torch.zeros(2, 8, 6, 8, dtype=torch.bfloat16),     # fewer channels
+                torch.zeros(2, 4, 6, 16, dtype=torch.bfloat16),    # fewer rows
+                torch.zeros(2, 8, 6, 16, dtype=torch.float32),     # fp32 to a bf16 plan
+                torch.zeros(8, 6, 16, dtype=torch.bfloat16)):      # no frame axis
+        with pytest.raises(ValueError, match="x must be"):
+            plan.forward_chunk(bad, st_in, st_out)
+    assert st_out.frames_seen == 0
