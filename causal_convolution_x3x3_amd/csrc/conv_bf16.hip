@@ -27,40 +27,10 @@
 // lane l holds rows 4*(l >> 4) + i, column (l & 15).
 #include <cstdlib>
 
-#include "cc3d_kernels.h"
+#include "cc3d_device.h"
 
 namespace cc3d {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
-// float -> bfloat16, round to nearest, ties to even (NaN stays NaN).
-__device__ __forceinline__ uint16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
-// 16-byte chunk swizzle inside a 64-byte LDS row (one pixel or one weight
-// column, 32 channels): spreads the rows read by one ds_read_b128 over the banks.
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
-
-__device__ __forceinline__ const uint16_t* zframe(const ZWindow& z, int zi) {
-    const int hist = z.kt - 1;
-    if (zi < hist) {
-        if (!z.first) return (const uint16_t*)z.cache + (int64_t)zi * z.frame_elems;
-        return z.zero_hist ? nullptr : (const uint16_t*)z.x;
-    }
-    const int u = zi - hist;
-    const int src = (z.up_t == 2) ? ((u + z.t_shift) >> 1) : u;
-    return (const uint16_t*)z.x + (int64_t)src * z.frame_elems;
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 template <int UP, int KS, int NF, int TS_H, int SW>
 __global__ __launch_bounds__(256) void conv_bf16_kernel(ConvArgs a)

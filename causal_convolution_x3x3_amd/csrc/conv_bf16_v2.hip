@@ -31,58 +31,10 @@
 // * Work items (tile, frame, channel block) are dealt to the 8 XCDs in contiguous
 //   ranges, so neighbouring tiles and consecutive frames (which share input rows
 //   and frames) run under the same L2.
-#include "cc3d_kernels.h"
+#include "cc3d_device.h"
 
 namespace cc3d {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
-__device__ __forceinline__ uint16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
-// Two floats to a bf16 pair (low half = lo), round to nearest even: gfx950's
-// v_cvt_pk_bf16_f32.
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
-{
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
-}
-
-// 1/sqrt(mean of squares + eps) and SiLU(z) = z / (1 + e^-z) on the hardware's
-// transcendental units (v_rsq_f32, v_exp_f32, v_rcp_f32; about 1 ulp of fp32
-// each, far below the bf16 rounding of the stored result).
-__device__ __forceinline__ float rms_scale(float mean_sq, float eps)
-{
-    return __builtin_amdgcn_rsqf(mean_sq + eps);
-}
-__device__ __forceinline__ float silu(float z)
-{
-    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
-}
-
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-__device__ __forceinline__ const uint16_t* zframe(const ZWindow& z, int zi) {
-    const int hist = z.kt - 1;
-    if (zi < hist) {
-        if (!z.first) return (const uint16_t*)z.cache + (int64_t)zi * z.frame_elems;
-        return z.zero_hist ? nullptr : (const uint16_t*)z.x;
-    }
-    const int u = zi - hist;
-    const int src = (z.up_t == 2) ? ((u + z.t_shift) >> 1) : u;
-    return (const uint16_t*)z.x + (int64_t)src * z.frame_elems;
-}
 
 // (tile, frame, channel block) of work item w; the channel block varies fastest.
 __device__ __forceinline__ void decode_item(int w, int t_out, int nblocks, int& tile, int& t, int& nb)
@@ -107,36 +59,6 @@ struct Geo<2, RH> {  // tile: 4 RH source rows x 16 source columns; M-wave w: so
     static constexpr int TS_H = 4 * RH, TS_W = 16;
     static constexpr int MF = 4 * RH;  // RH rows x 4 phases
 };
-
-// Raw buffer descriptor (gfx9 family word 3) over `bytes` bytes at `base`; a
-// load whose offset lies past the end returns zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-constexpr uint32_t OOB = 0x80000000u;  // an offset past every buffer used here
-
-// 16 bytes per lane from buffer offset `off` straight into LDS: lane l writes
-// the 16-byte slot lds_base + l (lds_base is the same for the whole wave).
-__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4* lds_base)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
-}
-
-// 4 bytes per lane from buffer offset `off` into LDS at lds_base + 4 * lane.
-__device__ __forceinline__ void load_to_lds4(__amdgpu_buffer_rsrc_t r, uint32_t off, char* lds_base)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4, off, 0, 0, 0);
-}
-
-// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // WN = waves along N: the workgroup has 4*WN waves (two per SIMD when WN = 2);
 // wave (wm, wn) computes M-wave wm's pixels for the NF/WN fragments of half wn.

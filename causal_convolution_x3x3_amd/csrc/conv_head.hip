@@ -31,13 +31,10 @@
 // accumulators in registers; output frame t
 // is complete, and stored (bf16, or the 8-bit code of the fp32 value), once
 // input frame t + 2 has been added.
-#include "cc3d_kernels.h"
+#include "cc3d_device.h"
 
 namespace cc3d {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TH = 8, TW = 16;                  // source tile
 constexpr int BH = TH + 2, BW = TW + 2;         // with the one-pixel border
@@ -46,31 +43,6 @@ constexpr int MFR = (BPIX + 15) / 16;           // 12 M fragments of 16 pixels
 constexpr int MFW = MFR / 4;                    // 3 per wave
 constexpr int NFR = 6;                          // 3 temporal taps x 32 columns
 constexpr int PSTR = 100;                       // floats per pixel in the P table (96 used)
-constexpr uint32_t OOB = 0x80000000u;           // an offset past every buffer used here
-
-__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
-__device__ __forceinline__ uint16_t bf16_rne(float f)
-{
-    return __builtin_bit_cast(uint16_t, (__bf16)f);
-}
-
-__device__ __forceinline__ const uint16_t* zframe(const ZWindow& z, int zi)
-{
-    const int hist = z.kt - 1;
-    if (zi < hist) {
-        if (!z.first) return (const uint16_t*)z.cache + (int64_t)zi * z.frame_elems;
-        return z.zero_hist ? nullptr : (const uint16_t*)z.x;
-    }
-    const int u = zi - hist;
-    const int src = (z.up_t == 2) ? ((u + z.t_shift) >> 1) : u;
-    return (const uint16_t*)z.x + (int64_t)src * z.frame_elems;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
 
 template <int UP, int KC>
 __global__ __launch_bounds__(256, 2) void conv_head_kernel(ConvArgs a, int fpw)
@@ -170,7 +142,7 @@ __global__ __launch_bounds__(256, 2) void conv_head_kernel(ConvArgs a, int fpw)
                 if (a.out_u8)
                     ((uint8_t*)a.out)[base + q * cout + o] = rgb8_code(y);
                 else
-                    out[base + q * cout + o] = bf16_rne(y);
+                    out[base + q * cout + o] = f2bf(y);
             }
         }
     };

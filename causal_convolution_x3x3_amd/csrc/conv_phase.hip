@@ -34,75 +34,10 @@
 // sub-step ahead for the weights), the temporal-tap rotation, the XCD work
 // order and the epilogue (bias, residual, bf16 store, fused RMSNorm + SiLU when
 // one block holds every channel) are those of the v2 kernel.
-#include "cc3d_kernels.h"
+#include "cc3d_device.h"
 
 namespace cc3d {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
-__device__ __forceinline__ uint16_t f2bf(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
-// Two floats to a bf16 pair (low half = lo), round to nearest even.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
-{
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
-}
-
-__device__ __forceinline__ float rms_scale(float mean_sq, float eps) { return __builtin_amdgcn_rsqf(mean_sq + eps); }
-__device__ __forceinline__ float silu(float z)
-{
-    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
-}
-
-// 16-byte chunk swizzle inside a 64-byte LDS row (one pixel or one weight row,
-// 32 channels), as in the other MFMA kernels.
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 3; }
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-__device__ __forceinline__ const uint16_t* zframe(const ZWindow& z, int zi)
-{
-    const int hist = z.kt - 1;
-    if (zi < hist) {
-        if (!z.first) return (const uint16_t*)z.cache + (int64_t)zi * z.frame_elems;
-        return z.zero_hist ? nullptr : (const uint16_t*)z.x;
-    }
-    const int u = zi - hist;
-    const int src = (z.up_t == 2) ? ((u + z.t_shift) >> 1) : u;
-    return (const uint16_t*)z.x + (int64_t)src * z.frame_elems;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-constexpr uint32_t OOB = 0x80000000u;  // an offset past every buffer used here
-
-__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4* lds_base)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
-}
-
-// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 template <int V>
 struct IC {

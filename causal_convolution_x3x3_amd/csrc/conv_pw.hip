@@ -31,71 +31,15 @@
 // * Epilogue: + bias, + residual, round to bf16 (nearest even) and store.  The
 //   op's act and 8-bit output are not done here; the host picks this family only
 //   for convs without them.
-#include "cc3d_kernels.h"
+#include "cc3d_device.h"
 
 namespace cc3d {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 template <int V>
 struct IC {
     static constexpr int value = V;
 };
-
-__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
-// Two floats to a bf16 pair (low half = lo), round to nearest even.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
-{
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-// 16-byte chunk swizzle inside a 64-byte LDS row (one position or one weight
-// row, 32 channels): the 16 rows one fragment read touches spread over the
-// banks.
-__device__ __forceinline__ int swz4(int row) { return (row >> 1) & 3; }
-
-__device__ __forceinline__ const uint16_t* zframe(const ZWindow& z, int zi)
-{
-    const int hist = z.kt - 1;
-    if (zi < hist) {
-        if (!z.first) return (const uint16_t*)z.cache + (int64_t)zi * z.frame_elems;
-        return z.zero_hist ? nullptr : (const uint16_t*)z.x;
-    }
-    const int u = zi - hist;
-    const int src = (z.up_t == 2) ? ((u + z.t_shift) >> 1) : u;
-    return (const uint16_t*)z.x + (int64_t)src * z.frame_elems;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-constexpr uint32_t OOB = 0x80000000u;  // an offset past every buffer used here
-
-// 16 (or 4) bytes per lane from buffer offset `off` into LDS slot lds_base + lane.
-__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4* lds_base)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
-}
-__device__ __forceinline__ void load_to_lds4(__amdgpu_buffer_rsrc_t r, uint32_t off, char* lds_base)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4, off, 0, 0, 0);
-}
-
-// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 constexpr int KC = 32;  // channels per K step
 constexpr int NB = 5;   // buffer sets in the ring: loads NB - 1 steps ahead
@@ -165,7 +109,7 @@ __global__ __launch_bounds__(512, 1) void conv_pw_kernel(ConvArgs a)
     for (int it = 0; it < A_IT; ++it) {
         const int slot = tid + NT * it;
         const int pos = slot >> 2;
-        const int chunk = (slot & 3) ^ swz4(pos);
+        const int chunk = (slot & 3) ^ swz(pos);
         const int op = p0 + pos;
         a_ch[it] = chunk * 8;
         a_off[it] = OOB;
@@ -208,9 +152,9 @@ __global__ __launch_bounds__(512, 1) void conv_pw_kernel(ConvArgs a)
     };
 
     // byte offsets of this lane's fragments: the chunk of K group g in row
-    // `row` is g ^ swz4(row); rows of one lane differ by multiples of 16, so
-    // swz4 is that of k16
-    const int co = (g ^ swz4(k16)) << 4;
+    // `row` is g ^ swz(row); rows of one lane differ by multiples of 16, so
+    // swz is that of k16
+    const int co = (g ^ swz(k16)) << 4;
     int a_frag[MW], b_frag[NFW];
 #pragma unroll
     for (int m = 0; m < MW; ++m) a_frag[m] = (64 * wm + 16 * m + k16) * 64 + co;
@@ -321,7 +265,7 @@ hipError_t launch_pw(const ConvArgs& a, hipStream_t s)
 }
 
 // Packed layout per (channel block, temporal tap, 32-channel chunk): NTILE rows
-// of 32 channels, the 16-byte chunks of row nl swizzled by swz4(nl) as in LDS;
+// of 32 channels, the 16-byte chunks of row nl swizzled by swz(nl) as in LDS;
 // zero past cout and cin.
 __global__ void pack_pw_kernel(const uint16_t* w, uint16_t* wpk, int cout, int cin, int kt, int ntile,
                                int nblocks, int kc_n)
@@ -337,7 +281,7 @@ __global__ void pack_pw_kernel(const uint16_t* w, uint16_t* wpk, int cout, int c
         row /= kc_n;
         const int ta = (int)(row % kt);
         const int nb = (int)(row / kt);
-        const int chunk = (e >> 3) ^ swz4(nl);
+        const int chunk = (e >> 3) ^ swz(nl);
         const int c = kc * KC + chunk * 8 + (e & 7);
         const int n = nb * ntile + nl;
         uint16_t v = 0;

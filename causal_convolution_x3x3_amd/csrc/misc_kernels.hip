@@ -1,33 +1,10 @@
 // Memory-bound kernels of the decode path: the fp32 direct conv (small fp32
 // layers), the standalone channel RMSNorm + SiLU (+ residual) epilogue, the
 // causal cache update, zero fill and the channels-first/last transposes.
-#include "cc3d_kernels.h"
+#include "cc3d_device.h"
 
 namespace cc3d {
 namespace {
-
-__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
-__device__ __forceinline__ uint16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
-// Frame zi of the causal window (see ZWindow), as bytes; null = a zero frame.
-__device__ __forceinline__ const char* zframe_bytes(const ZWindow& z, int zi, int eb)
-{
-    const int hist = z.kt - 1;
-    const int64_t fb = z.frame_elems * eb;
-    if (zi < hist) {
-        if (!z.first) return (const char*)z.cache + zi * fb;
-        return z.zero_hist ? nullptr : (const char*)z.x;
-    }
-    const int u = zi - hist;
-    const int src = (z.up_t == 2) ? ((u + z.t_shift) >> 1) : u;
-    return (const char*)z.x + src * fb;
-}
 
 // ------------------------------------------------------------ fp32 conv ----
 // One thread per output element (channel fastest, so neighbouring threads share
@@ -156,14 +133,6 @@ __global__ __launch_bounds__(256) void norm_act_kernel(NormArgs a)
 }
 
 // ----------------------------------------------------- norm_act (bf16) ---
-// Two floats to a bf16 pair (low half = lo), round to nearest even
-// (v_cvt_pk_bf16_f32).
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
-{
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
-}
 __device__ __forceinline__ void unpack8(const uint4& r, float v[8])
 {
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
@@ -177,12 +146,6 @@ __device__ __forceinline__ uint4 pack8(const float v[8])
 {
     return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                       pack_bf16x2(v[6], v[7]));
-}
-// SiLU on the hardware's exp and reciprocal (about 1 ulp of fp32 each, far
-// below the bf16 rounding of the stored result).
-__device__ __forceinline__ float silu_fast(float z)
-{
-    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
 }
 
 // LPP lanes per pixel, each holding U 16-byte chunks (8 channels) of it: chunk
@@ -239,7 +202,7 @@ __global__ __launch_bounds__(256) void norm_act_bf16_kernel(NormArgs a)
         const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
         float o[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = silu_fast(gm[i] * v[u][i] * inv);
+        for (int i = 0; i < 8; ++i) o[i] = silu(gm[i] * v[u][i] * inv);
         dst[l + LPP * u] = pack8(o);
     }
 }
