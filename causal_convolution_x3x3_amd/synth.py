@@ -77,6 +77,21 @@ def bf16(t: torch.Tensor) -> torch.Tensor:
     return t.to(torch.bfloat16)
 
 
+def layer_weights(shapes, cfg: int, gain_for, with_bias: bool = False):
+    """Seeded weights for a list of layers (name, cout, cin, kt, kh, kw): per
+    layer i the bf16 weight draws seed(cfg, 10 + 3i), the float32 RMSNorm gain
+    of its input (where ``gain_for(name)``) seed(cfg, 11 + 3i) and the float32
+    bias (with ``with_bias``) seed(cfg, 12 + 3i).  CPU tensors; absent ones None."""
+    out = {}
+    for i, (name, co, ci, kt, kh, kw) in enumerate(shapes):
+        out[name] = {
+            "w": bf16(conv_weight(co, ci, kt, kh, kw, seed(cfg, 10 + 3 * i))),
+            "g": gain(ci, seed(cfg, 11 + 3 * i)) if gain_for(name) else None,
+            "b": bias(co, seed(cfg, 12 + 3 * i)) if with_bias else None,
+        }
+    return out
+
+
 def video(c, t, h, w, s: int) -> torch.Tensor:
     """A [C][T][H][W] float32 N(0,1) video."""
     return normal((c, t, h, w), s)

@@ -1,0 +1,81 @@
+"""The whole-decoder configurations the GPU tests compare end to end, and their
+seeded inputs.  Shared by the GPU tests and by ``golden/make_stack_bounds.py``,
+which measures, per configuration, how far the storage-rounded oracle drifts
+from itself under rounding-level perturbations (the end-to-end bound).
+
+A case: latent channels, stages ((channels, temporal factor), ...), latent
+frames t, frame size h x w, chunk lengths, weight seed cfg, TemporalGrow order
+(None, "before", "after") and the aligned first-chunk rule.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from causal_convolution_x3x3_amd import synth
+from oracle import model as OM
+
+SMALL_STAGES = ((64, 2), (32, 2), (16, 1))
+FULL_STAGES = OM.DECODER_STAGES
+
+
+def case(c_lat, stages, t, h, w, splits, cfg=4, tg=None, aligned=False):
+    return dict(c_lat=c_lat, stages=tuple(tuple(s) for s in stages), t=t, h=h, w=w, splits=tuple(splits),
+                cfg=cfg, tg=tg, aligned=aligned)
+
+
+def random_decoder_cases(n, seed):
+    """Seeded decoder configurations: two or three stages of random widths and
+    temporal factors, latent width, frame size, chunking, TemporalGrow order,
+    first-chunk growth rule and the folding request (the last item)."""
+    rng = np.random.RandomState(seed)
+    cases = []
+    for _ in range(n):
+        nst = int(rng.randint(2, 4))
+        stages = tuple((int(rng.choice([16, 32, 64, 96, 128, 192])), int(rng.randint(1, 3))) for _ in range(nst))
+        c_lat = int(rng.choice([8, 16, 32, 48]))
+        t, h, w = int(rng.randint(2, 6)), int(rng.randint(1, 5)), int(rng.randint(1, 7))
+        splits, left = [], t
+        while left:
+            k = int(rng.randint(1, left + 1))
+            splits.append(k)
+            left -= k
+        tg = [None, "before", "after"][rng.randint(3)]
+        cases.append((c_lat, stages, t, h, w, splits, tg, bool(rng.randint(2)), bool(rng.randint(2))))
+    return cases
+
+
+RANDOM_CASES = random_decoder_cases(8, 11)
+
+STACK_CASES = {
+    "small": case(16, SMALL_STAGES, 6, 3, 5, (2, 3, 1)),
+    "small_t5": case(16, SMALL_STAGES, 5, 3, 5, (3, 2)),
+    "small_t5_aligned": case(16, SMALL_STAGES, 5, 3, 5, (3, 2), aligned=True),
+    "small_tg_before": case(16, SMALL_STAGES, 6, 3, 5, (2, 3, 1), tg="before"),
+    "small_tg_after": case(16, SMALL_STAGES, 6, 3, 5, (2, 3, 1), tg="after"),
+    "small_t5_tg_before": case(16, SMALL_STAGES, 5, 3, 5, (3, 2), tg="before"),
+    "small_t5_tg_before_aligned": case(16, SMALL_STAGES, 5, 3, 5, (3, 2), tg="before", aligned=True),
+    "full_tiny": case(48, FULL_STAGES, 5, 2, 3, (3, 2)),
+    "full_tiny_aligned": case(48, FULL_STAGES, 5, 2, 3, (3, 2), aligned=True),
+    "full_tiny_tg_before": case(48, FULL_STAGES, 5, 2, 3, (3, 2), tg="before"),
+    "full_one_latent": case(48, FULL_STAGES, 4, 2, 3, (1, 1, 1, 1)),
+    "full_two_clips": case(48, FULL_STAGES, 13, 4, 6, (7, 6)),
+    "smoke": case(48, FULL_STAGES, 3, 2, 3, (2, 1), cfg=9),
+}
+for _i, (_cl, _st, _t, _h, _w, _sp, _tg, _al, _fold) in enumerate(RANDOM_CASES):
+    STACK_CASES["random%d" % _i] = case(_cl, _st, _t, _h, _w, _sp, cfg=9, tg=_tg, aligned=_al)
+
+
+def layer_shapes(c):
+    return OM.decoder_layer_shapes(c_latent=c["c_lat"], stages=c["stages"], temporal_grow=c["tg"])
+
+
+def weights(c):
+    """The case's seeded layer weights (CPU tensors, see synth.layer_weights)."""
+    full = layer_shapes(c)
+    gains = {s[0]: s[6] for s in full}
+    return synth.layer_weights([s[:6] for s in full], c["cfg"], lambda n: gains[n])
+
+
+def latent(c):
+    """The case's seeded bf16 latent video [C][T][H][W] (CPU)."""
+    return synth.bf16(synth.video(c["c_lat"], c["t"], c["h"], c["w"], synth.seed(c["cfg"], 1)))
