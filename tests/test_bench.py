@@ -131,3 +131,19 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_video_steps_cover_each_workload():
+    """A whole video is the steps each workload's schedule gives: c4 the 15 clips,
+    c3 its 1 + 90 chunks, c2 and c1 their 24 and 16 frames in 4-frame chunks."""
+    from causal_convolution_x3x3_amd import synth
+    assert bench.VIDEO_STEPS["c4"] == bench.VIDEO_STEPS["c4tg"] == len(OM.clip_schedule(91))
+    wl = synth.WORKLOADS
+    assert bench.VIDEO_STEPS["c3"] == len(synth.chunk_lengths(wl[3]["t"], wl[3]["chunk"], wl[3]["first_chunk"]))
+    assert bench.VIDEO_STEPS["c2"] == len(synth.chunk_lengths(wl[2]["t"], wl[2]["chunk"]))
+    assert bench.VIDEO_STEPS["c1"] == len(synth.chunk_lengths(wl[1]["t"], wl[1]["chunk"]))
+
+
+def test_cpu_model_is_read():
+    m = bench.cpu_model()
+    assert m is None or (isinstance(m, str) and m)
