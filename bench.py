@@ -490,19 +490,19 @@ def cpu_baseline(workload, temporal_grow=None):
         sample = "residual block on its first 4-frame chunk at the full 90x160, fp64, %d threads" % threads
         frames_per_s = lt / dt
     else:
-        cin, cmid, rows, cols = 128, 96, 8, 64
+        cin, cmid, rows, cols, lt = 128, 96, 32, 320, 4  # about 15 s on 16 host threads
         w1 = synth.conv_weight(cmid, cin, 3, 3, 3, synth.seed(3, 10)).double().numpy()
         w2 = synth.conv_weight(3, cmid, 3, 3, 3, synth.seed(3, 13)).double().numpy()
         g2 = synth.gain(cmid, synth.seed(3, 14)).double().numpy()
         st = OM.UpStage({"w": w1, "b": None}, {"w": w2, "b": None, "g": g2}, nthreads=threads)
-        x = synth.video(cin, 1, rows, cols, synth.seed(3, 100)).double().numpy()
+        x = synth.video(cin, lt, rows, cols, synth.seed(3, 100)).double().numpy()
         t0 = time.perf_counter()
         y = st.step(x)
         dt = time.perf_counter() - t0
-        fl = (conv_flops_per_voxel(cin, cmid) + conv_flops_per_voxel(cmid, 3)) * y.shape[2] * y.shape[3]
-        sample = "1440p stage on one frame of a %dx%d crop (-> %dx%d), fp64, %d threads" % (
-            rows, cols, y.shape[2], y.shape[3], threads)
-        frames_per_s = 1.0 / dt * (y.shape[2] * y.shape[3]) / (1440 * 2560)
+        fl = (conv_flops_per_voxel(cin, cmid) + conv_flops_per_voxel(cmid, 3)) * y.shape[1] * y.shape[2] * y.shape[3]
+        sample = "1440p stage on one %d-frame chunk of a %dx%d crop (-> %dx%d), fp64, %d threads" % (
+            lt, rows, cols, y.shape[2], y.shape[3], threads)
+        frames_per_s = lt / dt * (y.shape[2] * y.shape[3]) / (1440 * 2560)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "cpu_model": cpu_model(), "sample": sample, "seconds": round(dt, 3),
             "frames_per_s_equiv": frames_per_s}

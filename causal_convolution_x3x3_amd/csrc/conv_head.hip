@@ -24,11 +24,15 @@
 // 8 x 16 with UP = 1) and a run of consecutive output frames.  Each window frame
 // of the run is loaded once: its tile plus a one-pixel border (18 x 10 pixels,
 // 12 M fragments) goes straight into MFMA operand registers, into a ring of
-// three frames (output frame t reads frames t, t+1, t+2; frame t+3 replaces
-// frame t as soon as t's products are formed).  P goes to one of two LDS
-// buffers: a thread gathers output frame t's taps from one buffer, then forms
-// the products of frame t+1 and writes them to the other; one barrier per
-// frame.
+// three frames (output frame t reads frames t, t+1, t+2; frame t+3 is requested
+// into frame t's slot as soon as t's products are formed).  The weights sit in
+// LDS (copied once per workgroup).  P goes to one of two LDS buffers: in the
+// step of output frame t a thread forms the products of frame t+1 with its
+// gather of frame t's taps interleaved, writes frame t+1's P to the other
+// buffer and stores frame t; one barrier per frame.  Measured on the 1440p
+// head (8 x 16 tiles over 26 window frames): the kernel takes within a few
+// percent of a copy of the same loads alone, which run at about 5 TB/s for this
+// tile shape (2-D tiles with a border read below the contiguous-stream rate).
 #include "cc3d_device.h"
 
 namespace cc3d {
@@ -48,10 +52,18 @@ constexpr int PBUF = MFR * 16 * PSTR;           // floats per P buffer
 // position stays a base plus a constant (one address register per pixel).
 __device__ __forceinline__ int pidx(int L, int n) { return L * PSTR + n; }
 
-template <int UP, int KC>
+constexpr int RING = 3;                         // window frames held in registers
+
+// Epilogue variants: the common RGB heads (three channels, no residual) store
+// without a runtime branch, which lets the compiler interleave one frame's
+// gather with the next frame's MFMAs; anything else takes the general path.
+enum { EPI_GENERAL = 0, EPI_RGB_BF16 = 1, EPI_RGB_U8 = 2 };
+
+template <int UP, int KC, int EPI>
 __global__ __launch_bounds__(256, 2) void conv_head_kernel(ConvArgs a, int fpw)
 {
     __shared__ float ptab[2 * PBUF];
+    __shared__ uint4 wlds[3 * KC * NFR * 64];
 
     const int tiles_w = (a.w_in + TW - 1) / TW;
     const int tiles_h = (a.h_in + TH - 1) / TH;
@@ -77,17 +89,12 @@ __global__ __launch_bounds__(256, 2) void conv_head_kernel(ConvArgs a, int fpw)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, k16 = lane & 15;
 
-    // weights (MFMA row operand): temporal tap ta, row 16 f + k16, channels
-    // 32 kc + 8 g .. + 7
-    bf16x8 wa[3][KC][NFR];
-    const uint4* wp = (const uint4*)a.wpk;
-#pragma unroll
-    for (int ta = 0; ta < 3; ++ta)
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-            for (int f = 0; f < NFR; ++f)
-                wa[ta][kc][f] = __builtin_bit_cast(bf16x8, wp[((ta * KC + kc) * NFR + f) * 64 + lane]);
+    // weights (MFMA row operand) to LDS: for temporal tap ta, chunk kc and
+    // fragment f, lane (g, k16) reads row 16 f + k16, channels 32 kc + 8 g .. + 7
+    {
+        const uint4* wp = (const uint4*)a.wpk;
+        for (int i = tid; i < 3 * KC * NFR * 64; i += 256) wlds[i] = wp[i];
+    }
 
     // this lane's pixel in each of the wave's M fragments: byte offset inside a
     // frame of its 8-channel group, OOB outside the image (loads return zeros)
@@ -102,9 +109,13 @@ __global__ __launch_bounds__(256, 2) void conv_head_kernel(ConvArgs a, int fpw)
                        : OOB;
     }
     const uint32_t frame_bytes = (uint32_t)(a.z.frame_elems * 2);
-    bf16x8 xb[3][KC][MFW];
+    bf16x8 xb[RING][KC][MFW];
+    // Every call issues its loads: a frame past the run's window reads through an
+    // empty descriptor (zeros, no memory traffic).  With no load behind a branch
+    // in the main loop, the compiler's wait counts follow the ring exactly
+    // (a conditional load makes it wait for every load still in flight).
     auto load_frame = [&](const int zi, const int slot) {
-        const uint16_t* fp = zframe(a.z, zi);
+        const uint16_t* fp = zi < z1 ? zframe(a.z, zi) : nullptr;
         const __amdgpu_buffer_rsrc_t r = make_rsrc(fp, fp ? frame_bytes : 0u);
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
@@ -114,24 +125,7 @@ __global__ __launch_bounds__(256, 2) void conv_head_kernel(ConvArgs a, int fpw)
                     bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(poff[mm] + (uint32_t)(kc * 64)), 0, 0));
     };
 
-    // P of one output frame whose window frame t sits in ring slot s0
-    f32x4 acc[MFW][NFR];
-    auto products = [&](const int s0) {
-#pragma unroll
-        for (int mm = 0; mm < MFW; ++mm)
-#pragma unroll
-            for (int f = 0; f < NFR; ++f) acc[mm][f] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ta = 0; ta < 3; ++ta)
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-                for (int mm = 0; mm < MFW; ++mm)
-#pragma unroll
-                    for (int f = 0; f < NFR; ++f)
-                        acc[mm][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ta][kc][f], xb[(s0 + ta) % 3][kc][mm],
-                                                                             acc[mm][f], 0, 0, 0);
-    };
+    f32x4 acc[MFW][NFR];  // P of one output frame
     // acc[mm][f] = D[n][pixel]: lane (g, k16) holds n = 16 f + 4 g .. + 3 of pixel k16
     auto write_p = [&](float* pb) {
 #pragma unroll
@@ -151,26 +145,53 @@ __global__ __launch_bounds__(256, 2) void conv_head_kernel(ConvArgs a, int fpw)
 
     // UP = 2: the two output pixels of this thread are row oy, columns 2 sj and
     // 2 sj + 1 of the 16 x 32 output tile (source row si, phase p = oy & 1).
-    // UP = 1: threads 0..127 own output pixel (si, sj) of the 8 x 16 tile.
+    // UP = 1: thread tid owns output pixel (si, sj) of the 8 x 16 tile, tid & 127
+    // (threads 128..255 repeat the gather of threads 0..127 and store nothing:
+    // the gather then has no branch around it).
     constexpr int NQ = UP;
-    const int oy = tid >> 4, sj = tid & 15;
+    const int oy = (UP == 2 ? tid : tid & 127) >> 4, sj = tid & 15;
     const int p = oy & 1, si = UP == 2 ? oy >> 1 : oy;
     const int Y = UP == 2 ? 2 * i0 + oy : i0 + oy, X = UP == 2 ? 2 * (j0 + sj) : j0 + sj;
     const bool mine = Y < a.h_out && X < a.w_out && (UP == 2 || tid < TH * TW);
 
-    // gather: UP = 2: tap (b, d) of output pixel (oy, 2 sj + q) reads
+    // products_gather: the products of the frame whose first window frame is in
+    // ring slot s0 (with `prod`), tap ta = i interleaved with row tap b = i of
+    // the gather from P buffer pb (with `gath`), so the gather's LDS reads and
+    // adds issue while the MFMAs run.
+    // Gather: UP = 2: tap (b, d) of output pixel (oy, 2 sj + q) reads
     // bordered-tile pixel (si + 1 + floor((p+b-1)/2), sj + 1 + floor((q+d-1)/2)):
     //   q = 0: d = 0 -> column sj, d = 1, 2 -> sj + 1;  q = 1: d = 0, 1 -> sj + 1, d = 2 -> sj + 2.
     // UP = 1: tap (b, d) of output pixel (si, sj) reads (si + b, sj + d).
-    auto gather_store = [&](const float* pb, const int t) {
-        if (!mine) return;
-        float v[NQ][3];
+    auto products_gather = [&](const int s0, const float* pb, float (&v)[NQ][3], const bool prod,
+                               const bool gath) {
+#pragma unroll
+        for (int mm = 0; mm < MFW; ++mm)
+#pragma unroll
+            for (int f = 0; f < NFR; ++f) acc[mm][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
 #pragma unroll
             for (int o = 0; o < 3; ++o) v[q][o] = bias[o];
 #pragma unroll
-        for (int b = 0; b < 3; ++b) {
+        for (int i = 0; i < 3; ++i) {
+            if (prod) {
+                bf16x8 wa[KC][NFR];  // temporal tap i's weights, read together
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+                    for (int f = 0; f < NFR; ++f)
+                        wa[kc][f] = __builtin_bit_cast(bf16x8, wlds[((i * KC + kc) * NFR + f) * 64 + lane]);
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+                    for (int f = 0; f < NFR; ++f)
+#pragma unroll
+                        for (int mm = 0; mm < MFW; ++mm)
+                            acc[mm][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                wa[kc][f], xb[(s0 + i) % RING][kc][mm], acc[mm][f], 0, 0, 0);
+            }
+            if (!gath) continue;
+            const int b = i;
             const int row = UP == 2 ? si + 1 + ((p + b - 1) >> 1) : si + b;
             const int L0 = row * BW + sj;
 #pragma unroll
@@ -185,73 +206,90 @@ __global__ __launch_bounds__(256, 2) void conv_head_kernel(ConvArgs a, int fpw)
                 }
             }
         }
+    };
+
+    auto store = [&](const int t, float (&v)[NQ][3]) {
+        if (!mine) return;
         const int64_t base = (((int64_t)t * a.h_out + Y) * a.w_out + X) * cout;
-        const uint16_t* res = (const uint16_t*)a.res;
-        if (res) {
-#pragma unroll
-            for (int q = 0; q < NQ; ++q)
-#pragma unroll
-                for (int o = 0; o < 3; ++o)
-                    if (o < cout && X + q < a.w_out) v[q][o] += bf2f(res[base + q * cout + o]);
-        }
-        if (UP == 2 && cout == 3) {
-            // 6 values of two neighbouring pixels, from an even element (X and
-            // w_out are even): three 4-byte (bf16) or 2-byte (8-bit) stores
-            if (a.out_u8) {
-                uint16_t* o8 = (uint16_t*)((uint8_t*)a.out + base);
-                o8[0] = (uint16_t)(rgb8_code(v[0][0]) | (rgb8_code(v[0][1]) << 8));
-                o8[1] = (uint16_t)(rgb8_code(v[0][2]) | (rgb8_code(v[NQ - 1][0]) << 8));
-                o8[2] = (uint16_t)(rgb8_code(v[NQ - 1][1]) | (rgb8_code(v[NQ - 1][2]) << 8));
-            } else {
-                uint32_t* o32 = (uint32_t*)((uint16_t*)a.out + base);
-                o32[0] = pack_bf16x2(v[0][0], v[0][1]);
-                o32[1] = pack_bf16x2(v[0][2], v[NQ - 1][0]);
-                o32[2] = pack_bf16x2(v[NQ - 1][1], v[NQ - 1][2]);
-            }
+        if (EPI == EPI_RGB_BF16 && UP == 2) {
+            // 6 values of two neighbouring pixels from an even element (X and
+            // w_out are even): three 4-byte stores
+            uint32_t* o32 = (uint32_t*)((uint16_t*)a.out + base);
+            o32[0] = pack_bf16x2(v[0][0], v[0][1]);
+            o32[1] = pack_bf16x2(v[0][2], v[NQ - 1][0]);
+            o32[2] = pack_bf16x2(v[NQ - 1][1], v[NQ - 1][2]);
             return;
         }
+        if (EPI == EPI_RGB_U8 && UP == 2) {
+            uint16_t* o8 = (uint16_t*)((uint8_t*)a.out + base);
+            o8[0] = (uint16_t)(rgb8_code(v[0][0]) | (rgb8_code(v[0][1]) << 8));
+            o8[1] = (uint16_t)(rgb8_code(v[0][2]) | (rgb8_code(v[NQ - 1][0]) << 8));
+            o8[2] = (uint16_t)(rgb8_code(v[NQ - 1][1]) | (rgb8_code(v[NQ - 1][2]) << 8));
+            return;
+        }
+        if (EPI == EPI_RGB_BF16) {
+#pragma unroll
+            for (int o = 0; o < 3; ++o) ((uint16_t*)a.out)[base + o] = f2bf(v[0][o]);
+            return;
+        }
+        if (EPI == EPI_RGB_U8) {
+#pragma unroll
+            for (int o = 0; o < 3; ++o) ((uint8_t*)a.out)[base + o] = rgb8_code(v[0][o]);
+            return;
+        }
+        const uint16_t* res = (const uint16_t*)a.res;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             if (X + q >= a.w_out) continue;
 #pragma unroll
             for (int o = 0; o < 3; ++o) {
                 if (o >= cout) continue;
+                float y = v[q][o];
+                if (res) y += bf2f(res[base + q * cout + o]);
                 if (a.out_u8)
-                    ((uint8_t*)a.out)[base + q * cout + o] = rgb8_code(v[q][o]);
+                    ((uint8_t*)a.out)[base + q * cout + o] = rgb8_code(y);
                 else
-                    ((uint16_t*)a.out)[base + q * cout + o] = f2bf(v[q][o]);
+                    ((uint16_t*)a.out)[base + q * cout + o] = f2bf(y);
             }
         }
     };
 
-    // Output frame t (ring slot of its first window frame: PH = (t - t0) mod 3).
-    // On entry P of frame t is being written to buffer (t - t0) & 1.  The two
-    // waves of each SIMD (two workgroups per CU) overlap one's gather with the
-    // other's MFMAs; within a wave the gather comes first, so the accumulators
-    // are not live beside the gathered values.
+    // Output frame t (ring slot of its first window frame: PH = (t - t0) mod RING).
+    // On entry P of frame t is being written to buffer (t - t0) & 1.  Every step
+    // but the run's last forms the products of frame t+1 (the MFMAs run while the
+    // same wave gathers frame t's taps from LDS), requests window frame t+1+RING
+    // into the slot frame t+1 leaves, writes frame t+1's P to the other buffer,
+    // and stores frame t.
     auto step = [&](const int t, const int PH) {
-        float* pb = ptab + ((t - t0) & 1) * PBUF;
-        float* pn = ptab + ((t + 1 - t0) & 1) * PBUF;
         __syncthreads();  // P of frame t is complete; every gather of frame t-1 is done
-        gather_store(pb, t);
-        if (t + 1 < t1) {
-            products((PH + 1) % 3);                           // frame t+1: window t+1 .. t+3
-            if (t + 4 < z1) load_frame(t + 4, (PH + 1) % 3);  // replaces window frame t+1
-            write_p(pn);
-        }
+        float v[NQ][3];
+        products_gather((PH + 1) % RING, ptab + ((t - t0) & 1) * PBUF, v, true, true);
+        load_frame(t + 1 + RING, (PH + 1) % RING);
+        write_p(ptab + ((t + 1 - t0) & 1) * PBUF);
+        store(t, v);
     };
 
-    load_frame(t0, 0);
-    load_frame(t0 + 1, 1);
-    load_frame(t0 + 2, 2);
-    products(0);
-    if (t0 + 3 < z1) load_frame(t0 + 3, 0);
-    write_p(ptab);
-    for (int tb = t0; tb < t1; tb += 3) {
-        step(tb, 0);
-        if (tb + 1 < t1) step(tb + 1, 1);
-        if (tb + 2 < t1) step(tb + 2, 2);
+#pragma unroll
+    for (int r = 0; r < RING; ++r) load_frame(t0 + r, r);
+    __syncthreads();  // the weights are in LDS
+    {
+        float unused[NQ][3];
+        products_gather(0, ptab, unused, true, false);  // the run's first frame
     }
+    load_frame(t0 + RING, 0);
+    write_p(ptab);
+    int tb = t0;
+    for (; tb + RING < t1; tb += RING) {  // whole groups of steps that have a next frame
+#pragma unroll
+        for (int r = 0; r < RING; ++r) step(tb + r, r);
+    }
+#pragma unroll
+    for (int r = 0; r < RING - 1; ++r)
+        if (tb + r < t1 - 1) step(tb + r, r);
+    __syncthreads();
+    float v[NQ][3];
+    products_gather(0, ptab + ((t1 - 1 - t0) & 1) * PBUF, v, false, true);  // the run's last frame
+    store(t1 - 1, v);
 }
 
 }  // namespace
@@ -318,17 +356,28 @@ hipError_t launch_conv_head(const ConvArgs& a, hipStream_t s)
     const int64_t grid = ((total + 7) / 8) * 8;
     const dim3 gd((unsigned)grid), bd(256);
     const int kc = a.cin / 32;
+    const int epi = (a.cout == 3 && !a.res) ? (a.out_u8 ? EPI_RGB_U8 : EPI_RGB_BF16) : EPI_GENERAL;
+#define CC3D_HEAD_LAUNCH(UPV, KCV, EPIV) \
+    hipLaunchKernelGGL((conv_head_kernel<UPV, KCV, EPIV>), gd, bd, 0, s, a, fpw)
+#define CC3D_HEAD_EPI(UPV, KCV)                                        \
+    do {                                                               \
+        if (epi == EPI_RGB_BF16) CC3D_HEAD_LAUNCH(UPV, KCV, EPI_RGB_BF16); \
+        else if (epi == EPI_RGB_U8) CC3D_HEAD_LAUNCH(UPV, KCV, EPI_RGB_U8); \
+        else CC3D_HEAD_LAUNCH(UPV, KCV, EPI_GENERAL);                  \
+    } while (0)
     if (a.up_s == 2) {
-        if (kc == 1) hipLaunchKernelGGL((conv_head_kernel<2, 1>), gd, bd, 0, s, a, fpw);
-        else if (kc == 2) hipLaunchKernelGGL((conv_head_kernel<2, 2>), gd, bd, 0, s, a, fpw);
-        else if (kc == 3) hipLaunchKernelGGL((conv_head_kernel<2, 3>), gd, bd, 0, s, a, fpw);
+        if (kc == 1) CC3D_HEAD_EPI(2, 1);
+        else if (kc == 2) CC3D_HEAD_EPI(2, 2);
+        else if (kc == 3) CC3D_HEAD_EPI(2, 3);
         else return hipErrorInvalidValue;
     } else {
-        if (kc == 1) hipLaunchKernelGGL((conv_head_kernel<1, 1>), gd, bd, 0, s, a, fpw);
-        else if (kc == 2) hipLaunchKernelGGL((conv_head_kernel<1, 2>), gd, bd, 0, s, a, fpw);
-        else if (kc == 3) hipLaunchKernelGGL((conv_head_kernel<1, 3>), gd, bd, 0, s, a, fpw);
+        if (kc == 1) CC3D_HEAD_EPI(1, 1);
+        else if (kc == 2) CC3D_HEAD_EPI(1, 2);
+        else if (kc == 3) CC3D_HEAD_EPI(1, 3);
         else return hipErrorInvalidValue;
     }
+#undef CC3D_HEAD_EPI
+#undef CC3D_HEAD_LAUNCH
     return hipGetLastError();
 }
 
