@@ -26,7 +26,9 @@ EXPORTS = (
     "cc3d_plan_device_bytes", "cc3d_output_elem_bytes", "cc3d_output_shape", "cc3d_reset", "cc3d_forward_chunk",
     "cc3d_to_channels_last", "cc3d_to_channels_first", "cc3d_last_error", "cc3d_version",
     "cc3d_profile_enable", "cc3d_plan_num_ops", "cc3d_profile_read", "cc3d_slot_shape", "cc3d_slot_read",
+    "cc3d_conv_forward_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class ConvDesc(ctypes.Structure):
@@ -95,6 +97,8 @@ def lib():
             "cc3d_profile_read": (i, [vp, i, i, ctypes.POINTER(OpProfile)]),
             "cc3d_slot_shape": (i, [vp, i, i, i, pi, pi, pi, pi]),
             "cc3d_slot_read": (i, [vp, i, i, i, vp, sz, vp]),
+            "cc3d_conv_forward_noalloc": (i, [ctypes.POINTER(ConvDesc), vp, vp, vp, vp, i, ctypes.POINTER(State),
+                                              ctypes.POINTER(State), vp, vp, vp]),
             "cc3d_last_error": (ctypes.c_char_p, []),
             "cc3d_version": (i, []),
         }

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -124,13 +125,31 @@ int test_fail_alloc_at()
     return s ? atoi(s) : 0;
 }
 
+// Device memory for a plan: hipMalloc'd blocks the plan owns, or (arena mode)
+// 256-byte-aligned ranges of a caller-given arena, reserved in order and never
+// freed (the no-alloc entry point's scratch).
 struct Allocator {
     cc3d_plan* p;
     int count = 0;
     int fail_at;
+    char* arena = nullptr;
+    size_t arena_cap = 0, arena_used = 0;
     explicit Allocator(cc3d_plan* plan) : p(plan), fail_at(test_fail_alloc_at()) {}
+    Allocator(cc3d_plan* plan, void* base, size_t cap) : p(plan), fail_at(0), arena((char*)base), arena_cap(cap) {}
     cc3d_status alloc(void** out, size_t bytes, const char* what) {
         ++count;
+        if (arena) {
+            const size_t need = align_up(bytes ? bytes : 1);
+            if (arena_used + need > arena_cap)
+                return fail(CC3D_ENOMEM,
+                            "this conv needs more than the %zu bytes of the no-alloc scratch (%s: %zu bytes "
+                            "after %zu already reserved); use cc3d_plan_create / cc3d_forward_chunk",
+                            arena_cap, what, bytes, arena_used);
+            *out = arena + arena_used;
+            arena_used += need;
+            p->device_bytes += bytes;
+            return CC3D_OK;
+        }
         void* d = nullptr;
         if (fail_at > 0 && count == fail_at)
             return fail(CC3D_ENOMEM, "allocation %d (%s, %zu bytes) failed (injected by CC3D_TEST_FAIL_ALLOC)",
@@ -474,9 +493,12 @@ struct DeviceGuard {
     }
 };
 
-cc3d_status materialise(const cc3d_stack_desc* d, cc3d_plan* p, hipStream_t stream)
+// Device memory of a plan and its contents: first every block is reserved (so
+// a plan that does not fit fails before any device work), then the weights are
+// repacked or copied and bias/gain copied on `stream`.  `sync`: wait for that
+// work (plan creation; the no-alloc path does not).
+cc3d_status materialise(const cc3d_stack_desc* d, cc3d_plan* p, hipStream_t stream, Allocator& al, bool sync)
 {
-    Allocator al(p);
     // intermediate slots
     for (int s = CC3D_SLOT_AUX + 1; s < CC3D_MAX_SLOTS; ++s) {
         Slot& sl = p->slots[s];
@@ -490,74 +512,71 @@ cc3d_status materialise(const cc3d_stack_desc* d, cc3d_plan* p, hipStream_t stre
     for (size_t i = 0; i < p->ops.size(); ++i) {
         OpRt& r = p->ops[i];
         const cc3d_op_desc& o = d->ops[i];
+        cc3d_status st = CC3D_OK;
         if (r.kind == CC3D_OP_CONV) {
-            const size_t wbytes = (size_t)r.cout * r.cin * r.kt * r.kh * r.kw * p->elem;
-            if (p->dtype == CC3D_BF16) {
-                const size_t pk = cc3d::bf16_packed_elems(r.cout, r.cin, r.kt, r.kh, r.kw, r.family) * 2;
-                cc3d_status st = al.alloc(&r.wpk, pk, "packed weights");
-                if (st != CC3D_OK) return st;
-                st = hip_status(cc3d::launch_pack_bf16(o.w, r.wpk, r.cout, r.cin, r.kt, r.kh, r.kw, r.family, stream),
-                                "weight repack launch");
-                if (st != CC3D_OK) return st;
-            } else {
-                cc3d_status st = al.alloc(&r.wpk, wbytes, "weights");
-                if (st != CC3D_OK) return st;
-                st = hip_status(hipMemcpyAsync(r.wpk, o.w, wbytes, hipMemcpyDeviceToDevice, stream), "weight copy");
-                if (st != CC3D_OK) return st;
-            }
+            const size_t wbytes = p->dtype == CC3D_BF16
+                                      ? cc3d::bf16_packed_elems(r.cout, r.cin, r.kt, r.kh, r.kw, r.family) * 2
+                                      : (size_t)r.cout * r.cin * r.kt * r.kh * r.kw * p->elem;
+            st = al.alloc(&r.wpk, wbytes, p->dtype == CC3D_BF16 ? "packed weights" : "weights");
+            if (st != CC3D_OK) return st;
             if (o.bias) {
                 void* b = nullptr;
-                cc3d_status st = al.alloc(&b, (size_t)r.cout * 4, "bias");
-                if (st != CC3D_OK) return st;
+                if ((st = al.alloc(&b, (size_t)r.cout * 4, "bias")) != CC3D_OK) return st;
                 r.bias = (float*)b;
+            }
+        }
+        if (r.act_out != CC3D_SLOT_NONE) {
+            void* g = nullptr;
+            if ((st = al.alloc(&g, (size_t)r.cout * 4, "gamma")) != CC3D_OK) return st;
+            r.gamma = (float*)g;
+        }
+    }
+    for (size_t i = 0; i < p->ops.size(); ++i) {
+        const OpRt& r = p->ops[i];
+        const cc3d_op_desc& o = d->ops[i];
+        cc3d_status st = CC3D_OK;
+        if (r.kind == CC3D_OP_CONV) {
+            if (p->dtype == CC3D_BF16)
+                st = hip_status(cc3d::launch_pack_bf16(o.w, r.wpk, r.cout, r.cin, r.kt, r.kh, r.kw, r.family, stream),
+                                "weight repack launch");
+            else
+                st = hip_status(hipMemcpyAsync(r.wpk, o.w, (size_t)r.cout * r.cin * r.kt * r.kh * r.kw * p->elem,
+                                               hipMemcpyDeviceToDevice, stream),
+                                "weight copy");
+            if (st != CC3D_OK) return st;
+            if (o.bias) {
                 st = hip_status(hipMemcpyAsync(r.bias, o.bias, (size_t)r.cout * 4, hipMemcpyDeviceToDevice, stream),
                                 "bias copy");
                 if (st != CC3D_OK) return st;
             }
         }
         if (r.act_out != CC3D_SLOT_NONE) {
-            void* g = nullptr;
-            cc3d_status st = al.alloc(&g, (size_t)r.cout * 4, "gamma");
-            if (st != CC3D_OK) return st;
-            r.gamma = (float*)g;
             st = hip_status(hipMemcpyAsync(r.gamma, o.gamma, (size_t)r.cout * 4, hipMemcpyDeviceToDevice, stream),
                             "gamma copy");
             if (st != CC3D_OK) return st;
         }
     }
-    return hip_status(hipStreamSynchronize(stream), "plan set-up");
+    return sync ? hip_status(hipStreamSynchronize(stream), "plan set-up") : CC3D_OK;
 }
 
 std::string conv_kernel_name(const cc3d_plan* p, const OpRt& r);
 
-cc3d_status create_common(const cc3d_stack_desc* d, void* stream, cc3d_plan** out)
+// The plan's graph, slots and op table, with no device work.
+cc3d_status build_plan(const cc3d_stack_desc* d, cc3d_plan* p)
 {
-    if (!out) return fail(CC3D_EINVAL, "out is NULL");
-    *out = nullptr;
-    cc3d_plan* p = new (std::nothrow) cc3d_plan();
-    if (!p) return fail(CC3D_ENOMEM, "host allocation of the plan failed");
     cc3d_status st = build_graph(d, p);
-    if (st != CC3D_OK) {
-        release(p);
-        return st;
-    }
+    if (st != CC3D_OK) return st;
     st = assign_norm_temps(p);
-    if (st != CC3D_OK) {
-        release(p);
-        return st;
-    }
+    if (st != CC3D_OK) return st;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) {
-        release(p);
-        return hip_status(e, "hipGetDevice");
-    }
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
     p->device = dev;
-    st = materialise(d, p, (hipStream_t)stream);
-    if (st != CC3D_OK) {
-        release(p);
-        return st;
-    }
+    return CC3D_OK;
+}
+
+void name_kernels(cc3d_plan* p)
+{
     p->prof.assign(p->ops.size() * 3, cc3d_plan::ProfPart());
     const char* norm_name = p->dtype == CC3D_BF16 ? "norm_act_bf16" : "norm_act_f32";
     for (size_t i = 0; i < p->ops.size(); ++i) {
@@ -570,6 +589,31 @@ cc3d_status create_common(const cc3d_stack_desc* d, void* stream, cc3d_plan** ou
             p->prof[i * 3 + 0].kernel = norm_name;
         }
     }
+}
+
+cc3d_status noalloc_scratch(int device, void** out);
+
+cc3d_status create_common(const cc3d_stack_desc* d, void* stream, cc3d_plan** out)
+{
+    if (!out) return fail(CC3D_EINVAL, "out is NULL");
+    *out = nullptr;
+    cc3d_plan* p = new (std::nothrow) cc3d_plan();
+    if (!p) return fail(CC3D_ENOMEM, "host allocation of the plan failed");
+    cc3d_status st = build_plan(d, p);
+    if (st == CC3D_OK) {
+        // set-up on this device: the no-alloc entry point's scratch address too
+        void* unused = nullptr;
+        st = noalloc_scratch(p->device, &unused);
+    }
+    if (st == CC3D_OK) {
+        Allocator al(p);
+        st = materialise(d, p, (hipStream_t)stream, al, true);
+    }
+    if (st != CC3D_OK) {
+        release(p);
+        return st;
+    }
+    name_kernels(p);
     *out = p;
     clear_err();
     return CC3D_OK;
@@ -651,6 +695,81 @@ std::string conv_kernel_name(const cc3d_plan* p, const OpRt& r)
     return buf;
 }
 
+// The one-op stack descriptor of a single-conv descriptor.
+cc3d_status conv_stack_desc(const cc3d_conv_desc* d, const void* w, const float* bias, const float* gamma,
+                            cc3d_op_desc* op, cc3d_stack_desc* sd)
+{
+    if (!d) return fail(CC3D_EINVAL, "conv desc is NULL");
+    if (d->epilogue & ~(CC3D_EPI_RESIDUAL | CC3D_EPI_ACT | CC3D_EPI_U8))
+        return fail(CC3D_EINVAL, "epilogue flags 0x%x; accepted CC3D_EPI_RESIDUAL | CC3D_EPI_ACT | CC3D_EPI_U8",
+                    d->epilogue);
+    if ((d->epilogue & CC3D_EPI_ACT) && (d->epilogue & CC3D_EPI_U8))
+        return fail(CC3D_EINVAL, "CC3D_EPI_U8 cannot be combined with CC3D_EPI_ACT");
+    if (d->cin <= 0) return fail(CC3D_ESHAPE, "cin=%d must be >= 1", d->cin);
+    memset(op, 0, sizeof *op);
+    op->kind = CC3D_OP_CONV;
+    op->cout = d->cout;
+    op->kt = d->kt;
+    op->kh = d->kh;
+    op->kw = d->kw;
+    op->up_s = d->up_s;
+    op->up_t = d->up_t;
+    op->tpad = d->tpad;
+    op->src = CC3D_SLOT_X;
+    op->res = (d->epilogue & CC3D_EPI_RESIDUAL) ? CC3D_SLOT_AUX : CC3D_SLOT_NONE;
+    op->out = (d->epilogue & CC3D_EPI_ACT) ? CC3D_SLOT_NONE : CC3D_SLOT_Y;
+    op->act_out = (d->epilogue & CC3D_EPI_ACT) ? CC3D_SLOT_Y : CC3D_SLOT_NONE;
+    op->w = w;
+    op->bias = bias;
+    op->gamma = gamma;
+    op->out_u8 = (d->epilogue & CC3D_EPI_U8) ? 1 : 0;
+    memset(sd, 0, sizeof *sd);
+    sd->dtype = d->dtype;
+    sd->cin = d->cin;
+    sd->h = d->h_in;
+    sd->w = d->w_in;
+    sd->max_chunk_t = d->max_chunk_t;
+    sd->eps = d->eps;
+    sd->grow = d->grow;
+    sd->fold_upsample = d->fold_upsample;
+    sd->n_ops = 1;
+    sd->ops = op;
+    return CC3D_OK;
+}
+
+// The no-alloc entry point's scratch: one array per device, in this file, of a
+// fixed size (CC3D_NOALLOC_SCRATCH_BYTES), held until the process ends.  Its
+// device address is looked up once per device (at the first plan creation or
+// no-alloc call there) and kept: in host code the array's name is not a device
+// address.
+__device__ __align__(256) unsigned char scratch[CC3D_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+cc3d_status noalloc_scratch(int device, void** out)
+{
+    if (device < 0 || device >= kMaxDevices) return fail(CC3D_EDEVICE, "device %d not in [0, %d)", device, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[device]) {
+        void* ptr = nullptr;
+        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return fail(CC3D_EDEVICE, "hipGetSymbolAddress of the no-alloc scratch on device %d failed: %s", device,
+                        hipGetErrorString(e));
+        }
+        g_scratch_ptr[device] = ptr;
+    }
+    *out = g_scratch_ptr[device];
+    return CC3D_OK;
+}
+
+// One chunk through a plan; with check_only, every argument check and nothing else.
+cc3d_status forward_impl(const cc3d_plan* p, const void* x, int t_chunk, const cc3d_state* cache_in,
+                         cc3d_state* cache_out, const void* residual, void* y, void* stream, bool check_only);
+
 }  // namespace
 
 extern "C" {
@@ -668,43 +787,10 @@ cc3d_status cc3d_plan_create(const cc3d_conv_desc* d, const void* w, const float
                              void* stream, cc3d_plan** out)
 {
     if (out) *out = nullptr;
-    if (!d) return fail(CC3D_EINVAL, "conv desc is NULL");
-    if (d->epilogue & ~(CC3D_EPI_RESIDUAL | CC3D_EPI_ACT | CC3D_EPI_U8))
-        return fail(CC3D_EINVAL, "epilogue flags 0x%x; accepted CC3D_EPI_RESIDUAL | CC3D_EPI_ACT | CC3D_EPI_U8",
-                    d->epilogue);
-    if ((d->epilogue & CC3D_EPI_ACT) && (d->epilogue & CC3D_EPI_U8))
-        return fail(CC3D_EINVAL, "CC3D_EPI_U8 cannot be combined with CC3D_EPI_ACT");
-    if (d->cin <= 0) return fail(CC3D_ESHAPE, "cin=%d must be >= 1", d->cin);
     cc3d_op_desc op;
-    memset(&op, 0, sizeof op);
-    op.kind = CC3D_OP_CONV;
-    op.cout = d->cout;
-    op.kt = d->kt;
-    op.kh = d->kh;
-    op.kw = d->kw;
-    op.up_s = d->up_s;
-    op.up_t = d->up_t;
-    op.tpad = d->tpad;
-    op.src = CC3D_SLOT_X;
-    op.res = (d->epilogue & CC3D_EPI_RESIDUAL) ? CC3D_SLOT_AUX : CC3D_SLOT_NONE;
-    op.out = (d->epilogue & CC3D_EPI_ACT) ? CC3D_SLOT_NONE : CC3D_SLOT_Y;
-    op.act_out = (d->epilogue & CC3D_EPI_ACT) ? CC3D_SLOT_Y : CC3D_SLOT_NONE;
-    op.w = w;
-    op.bias = bias;
-    op.gamma = gamma;
-    op.out_u8 = (d->epilogue & CC3D_EPI_U8) ? 1 : 0;
     cc3d_stack_desc sd;
-    memset(&sd, 0, sizeof sd);
-    sd.dtype = d->dtype;
-    sd.cin = d->cin;
-    sd.h = d->h_in;
-    sd.w = d->w_in;
-    sd.max_chunk_t = d->max_chunk_t;
-    sd.eps = d->eps;
-    sd.grow = d->grow;
-    sd.fold_upsample = d->fold_upsample;
-    sd.n_ops = 1;
-    sd.ops = &op;
+    cc3d_status st = conv_stack_desc(d, w, bias, gamma, &op, &sd);
+    if (st != CC3D_OK) return st;
     return create_common(&sd, stream, out);
 }
 
@@ -752,6 +838,159 @@ cc3d_status cc3d_reset(const cc3d_plan* p, cc3d_state* state, void* stream)
 cc3d_status cc3d_forward_chunk(const cc3d_plan* p, const void* x, int t_chunk, const cc3d_state* cache_in,
                                cc3d_state* cache_out, const void* residual, void* y, void* stream)
 {
+    return forward_impl(p, x, t_chunk, cache_in, cache_out, residual, y, stream, false);
+}
+
+cc3d_status cc3d_conv_forward_noalloc(const cc3d_conv_desc* d, const void* w, const float* bias,
+                                      const float* gamma, const void* x, int t_chunk,
+                                      const cc3d_state* cache_in, cc3d_state* cache_out, const void* residual,
+                                      void* y, void* stream)
+{
+    if (!w) return fail(CC3D_EINVAL, "w is NULL");
+    if (!x) return fail(CC3D_EINVAL, "x is NULL");
+    if (!y) return fail(CC3D_EINVAL, "y is NULL");
+    cc3d_op_desc op;
+    cc3d_stack_desc sd;
+    cc3d_status st = conv_stack_desc(d, w, bias, gamma, &op, &sd);
+    if (st != CC3D_OK) return st;
+    // a plan on the host whose device memory is ranges of this device's scratch
+    cc3d_plan plan;
+    if ((st = build_plan(&sd, &plan)) != CC3D_OK) return st;
+    if (t_chunk < 1 || t_chunk > plan.max_t)
+        return fail(CC3D_ESHAPE, "t_chunk=%d not in [1, %d] (the descriptor's max_chunk_t)", t_chunk, plan.max_t);
+    if ((st = check_ptr(w, plan.device, "w")) != CC3D_OK) return st;
+    if (bias && (st = check_ptr(bias, plan.device, "bias")) != CC3D_OK) return st;
+    if (gamma && (st = check_ptr(gamma, plan.device, "gamma")) != CC3D_OK) return st;
+    void* base = nullptr;
+    if ((st = noalloc_scratch(plan.device, &base)) != CC3D_OK) return st;
+    // The chunk's arguments are checked first (forward_impl, check only); then
+    // materialise reserves every block of the scratch before it launches
+    // anything (a conv that does not fit fails there, before any device work),
+    // repacks the weights into it, and the chunk runs, all on `stream`.
+    Allocator al(&plan, base, CC3D_NOALLOC_SCRATCH_BYTES);
+    plan.magic = kPlanMagic;
+    st = forward_impl(&plan, x, t_chunk, cache_in, cache_out, residual, y, nullptr, true);
+    if (st == CC3D_OK) st = materialise(&sd, &plan, (hipStream_t)stream, al, false);
+    if (st == CC3D_OK) st = forward_impl(&plan, x, t_chunk, cache_in, cache_out, residual, y, stream, false);
+    plan.magic = 0;
+    return st;
+}
+
+cc3d_status cc3d_slot_shape(const cc3d_plan* p, int slot, int t_chunk, int first, int* c, int* t, int* h, int* w)
+{
+    if (!plan_ok(p)) return fail(CC3D_EINVAL, "plan is NULL or destroyed");
+    if (slot < CC3D_SLOT_AUX || slot >= CC3D_MAX_SLOTS || !p->slots[slot].defined)
+        return fail(CC3D_EINVAL, "slot %d is not an intermediate or residual slot of this plan", slot);
+    if (t_chunk < 1 || t_chunk > p->max_t) return fail(CC3D_ESHAPE, "t_chunk=%d not in [1, %d]", t_chunk, p->max_t);
+    const Slot& s = p->slots[slot];
+    if (s.grouped)
+        return fail(CC3D_EINVAL, "slot %d belongs to the frame-batched group and holds only the last batch", slot);
+    if (c) *c = s.c;
+    if (t) *t = (int)s.tc.eval(t_chunk, first != 0);
+    if (h) *h = s.h;
+    if (w) *w = s.w;
+    clear_err();
+    return CC3D_OK;
+}
+
+cc3d_status cc3d_slot_read(const cc3d_plan* p, int slot, int t_chunk, int first, void* dst, size_t dst_bytes,
+                           void* stream)
+{
+    if (slot == CC3D_SLOT_AUX) return fail(CC3D_EINVAL, "slot %d is the caller's residual argument", slot);
+    int c = 0, t = 0, h = 0, w = 0;
+    cc3d_status st = cc3d_slot_shape(p, slot, t_chunk, first, &c, &t, &h, &w);
+    if (st != CC3D_OK) return st;
+    if (!dst) return fail(CC3D_EINVAL, "dst is NULL");
+    const size_t bytes = (size_t)c * t * h * w * p->elem;
+    if (dst_bytes < bytes) return fail(CC3D_EINVAL, "dst_bytes=%zu < %zu needed", dst_bytes, bytes);
+    DeviceGuard g(p->device);
+    st = hip_status(hipMemcpyAsync(dst, p->slots[slot].ptr, bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream),
+                    "slot copy");
+    if (st == CC3D_OK) clear_err();
+    return st;
+}
+
+cc3d_status cc3d_profile_enable(cc3d_plan* p, int enable)
+{
+    if (!plan_ok(p)) return fail(CC3D_EINVAL, "plan is NULL or destroyed");
+    DeviceGuard g(p->device);
+    for (auto& part : p->prof) {
+        for (auto& e : part.pending) {
+            (void)hipEventSynchronize(e.stop);
+            p->event_pool.push_back(e.start);
+            p->event_pool.push_back(e.stop);
+        }
+        part.pending.clear();
+        part.launches = 0;
+        part.ms = part.flops = part.bytes = 0.0;
+    }
+    p->prof_on = enable != 0;
+    clear_err();
+    return CC3D_OK;
+}
+
+int cc3d_plan_num_ops(const cc3d_plan* p) { return plan_ok(p) ? (int)p->ops.size() : 0; }
+
+cc3d_status cc3d_profile_read(const cc3d_plan* p, int op, int part, cc3d_op_profile* out)
+{
+    if (!plan_ok(p)) return fail(CC3D_EINVAL, "plan is NULL or destroyed");
+    if (op < 0 || op >= (int)p->ops.size()) return fail(CC3D_EINVAL, "op %d not in [0, %zu)", op, p->ops.size());
+    if (part < 0 || part > 2) return fail(CC3D_EINVAL, "part %d not in [0, 2]", part);
+    if (!out) return fail(CC3D_EINVAL, "out is NULL");
+    DeviceGuard g(p->device);
+    auto& pp = p->prof[(size_t)op * 3 + part];
+    for (auto& e : pp.pending) {
+        hipError_t err = hipEventSynchronize(e.stop);
+        float ms = 0.f;
+        if (err == hipSuccess) err = hipEventElapsedTime(&ms, e.start, e.stop);
+        if (err != hipSuccess) return hip_status(err, "profile event");
+        pp.launches += 1;
+        pp.ms += ms;
+        pp.flops += e.flops;
+        pp.bytes += e.bytes;
+        p->event_pool.push_back(e.start);
+        p->event_pool.push_back(e.stop);
+    }
+    pp.pending.clear();
+    memset(out, 0, sizeof *out);
+    snprintf(out->kernel, sizeof out->kernel, "%s", pp.kernel.c_str());
+    out->launches = pp.launches;
+    out->total_ms = pp.ms;
+    out->flops = pp.flops;
+    out->bytes = pp.bytes;
+    clear_err();
+    return CC3D_OK;
+}
+
+cc3d_status cc3d_to_channels_last(const void* src, void* dst, int c, int t, int h, int w, int eb, void* stream)
+{
+    if (!src || !dst) return fail(CC3D_EINVAL, "src or dst is NULL");
+    if (c < 1 || t < 1 || h < 1 || w < 1) return fail(CC3D_ESHAPE, "c=%d t=%d h=%d w=%d must be >= 1", c, t, h, w);
+    if (eb != 2 && eb != 4) return fail(CC3D_EDTYPE, "elem_bytes=%d; accepted 2 or 4", eb);
+    cc3d_status st = hip_status(cc3d::launch_transpose(src, dst, c, (int64_t)t * h * w, eb, (hipStream_t)stream),
+                                "transpose launch");
+    if (st == CC3D_OK) clear_err();
+    return st;
+}
+
+cc3d_status cc3d_to_channels_first(const void* src, void* dst, int c, int t, int h, int w, int eb, void* stream)
+{
+    if (!src || !dst) return fail(CC3D_EINVAL, "src or dst is NULL");
+    if (c < 1 || t < 1 || h < 1 || w < 1) return fail(CC3D_ESHAPE, "c=%d t=%d h=%d w=%d must be >= 1", c, t, h, w);
+    if (eb != 2 && eb != 4) return fail(CC3D_EDTYPE, "elem_bytes=%d; accepted 2 or 4", eb);
+    cc3d_status st = hip_status(cc3d::launch_transpose(src, dst, (int64_t)t * h * w, c, eb, (hipStream_t)stream),
+                                "transpose launch");
+    if (st == CC3D_OK) clear_err();
+    return st;
+}
+
+}  // extern "C"
+
+namespace {
+
+cc3d_status forward_impl(const cc3d_plan* p, const void* x, int t_chunk, const cc3d_state* cache_in,
+                         cc3d_state* cache_out, const void* residual, void* y, void* stream, bool check_only)
+{
     if (!plan_ok(p)) return fail(CC3D_EINVAL, "plan is NULL or destroyed");
     if (!x) return fail(CC3D_EINVAL, "x is NULL");
     if (!y) return fail(CC3D_EINVAL, "y is NULL");
@@ -788,6 +1027,10 @@ cc3d_status cc3d_forward_chunk(const cc3d_plan* p, const void* x, int t_chunk, c
     if ((st = check_ptr(cache_in->arena, p->device, "cache_in arena")) != CC3D_OK) return st;
     if ((st = check_ptr(cache_out->arena, p->device, "cache_out arena")) != CC3D_OK) return st;
     if (residual && (st = check_ptr(residual, p->device, "residual")) != CC3D_OK) return st;
+    if (check_only) {
+        clear_err();
+        return CC3D_OK;
+    }
 
     hipStream_t s = (hipStream_t)stream;
     // One pass of ops over `t` frames of their base input: the chunk input (the
@@ -957,112 +1200,4 @@ cc3d_status cc3d_forward_chunk(const cc3d_plan* p, const void* x, int t_chunk, c
     return CC3D_OK;
 }
 
-cc3d_status cc3d_slot_shape(const cc3d_plan* p, int slot, int t_chunk, int first, int* c, int* t, int* h, int* w)
-{
-    if (!plan_ok(p)) return fail(CC3D_EINVAL, "plan is NULL or destroyed");
-    if (slot < CC3D_SLOT_AUX || slot >= CC3D_MAX_SLOTS || !p->slots[slot].defined)
-        return fail(CC3D_EINVAL, "slot %d is not an intermediate or residual slot of this plan", slot);
-    if (t_chunk < 1 || t_chunk > p->max_t) return fail(CC3D_ESHAPE, "t_chunk=%d not in [1, %d]", t_chunk, p->max_t);
-    const Slot& s = p->slots[slot];
-    if (s.grouped)
-        return fail(CC3D_EINVAL, "slot %d belongs to the frame-batched group and holds only the last batch", slot);
-    if (c) *c = s.c;
-    if (t) *t = (int)s.tc.eval(t_chunk, first != 0);
-    if (h) *h = s.h;
-    if (w) *w = s.w;
-    clear_err();
-    return CC3D_OK;
-}
-
-cc3d_status cc3d_slot_read(const cc3d_plan* p, int slot, int t_chunk, int first, void* dst, size_t dst_bytes,
-                           void* stream)
-{
-    if (slot == CC3D_SLOT_AUX) return fail(CC3D_EINVAL, "slot %d is the caller's residual argument", slot);
-    int c = 0, t = 0, h = 0, w = 0;
-    cc3d_status st = cc3d_slot_shape(p, slot, t_chunk, first, &c, &t, &h, &w);
-    if (st != CC3D_OK) return st;
-    if (!dst) return fail(CC3D_EINVAL, "dst is NULL");
-    const size_t bytes = (size_t)c * t * h * w * p->elem;
-    if (dst_bytes < bytes) return fail(CC3D_EINVAL, "dst_bytes=%zu < %zu needed", dst_bytes, bytes);
-    DeviceGuard g(p->device);
-    st = hip_status(hipMemcpyAsync(dst, p->slots[slot].ptr, bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream),
-                    "slot copy");
-    if (st == CC3D_OK) clear_err();
-    return st;
-}
-
-cc3d_status cc3d_profile_enable(cc3d_plan* p, int enable)
-{
-    if (!plan_ok(p)) return fail(CC3D_EINVAL, "plan is NULL or destroyed");
-    DeviceGuard g(p->device);
-    for (auto& part : p->prof) {
-        for (auto& e : part.pending) {
-            (void)hipEventSynchronize(e.stop);
-            p->event_pool.push_back(e.start);
-            p->event_pool.push_back(e.stop);
-        }
-        part.pending.clear();
-        part.launches = 0;
-        part.ms = part.flops = part.bytes = 0.0;
-    }
-    p->prof_on = enable != 0;
-    clear_err();
-    return CC3D_OK;
-}
-
-int cc3d_plan_num_ops(const cc3d_plan* p) { return plan_ok(p) ? (int)p->ops.size() : 0; }
-
-cc3d_status cc3d_profile_read(const cc3d_plan* p, int op, int part, cc3d_op_profile* out)
-{
-    if (!plan_ok(p)) return fail(CC3D_EINVAL, "plan is NULL or destroyed");
-    if (op < 0 || op >= (int)p->ops.size()) return fail(CC3D_EINVAL, "op %d not in [0, %zu)", op, p->ops.size());
-    if (part < 0 || part > 2) return fail(CC3D_EINVAL, "part %d not in [0, 2]", part);
-    if (!out) return fail(CC3D_EINVAL, "out is NULL");
-    DeviceGuard g(p->device);
-    auto& pp = p->prof[(size_t)op * 3 + part];
-    for (auto& e : pp.pending) {
-        hipError_t err = hipEventSynchronize(e.stop);
-        float ms = 0.f;
-        if (err == hipSuccess) err = hipEventElapsedTime(&ms, e.start, e.stop);
-        if (err != hipSuccess) return hip_status(err, "profile event");
-        pp.launches += 1;
-        pp.ms += ms;
-        pp.flops += e.flops;
-        pp.bytes += e.bytes;
-        p->event_pool.push_back(e.start);
-        p->event_pool.push_back(e.stop);
-    }
-    pp.pending.clear();
-    memset(out, 0, sizeof *out);
-    snprintf(out->kernel, sizeof out->kernel, "%s", pp.kernel.c_str());
-    out->launches = pp.launches;
-    out->total_ms = pp.ms;
-    out->flops = pp.flops;
-    out->bytes = pp.bytes;
-    clear_err();
-    return CC3D_OK;
-}
-
-cc3d_status cc3d_to_channels_last(const void* src, void* dst, int c, int t, int h, int w, int eb, void* stream)
-{
-    if (!src || !dst) return fail(CC3D_EINVAL, "src or dst is NULL");
-    if (c < 1 || t < 1 || h < 1 || w < 1) return fail(CC3D_ESHAPE, "c=%d t=%d h=%d w=%d must be >= 1", c, t, h, w);
-    if (eb != 2 && eb != 4) return fail(CC3D_EDTYPE, "elem_bytes=%d; accepted 2 or 4", eb);
-    cc3d_status st = hip_status(cc3d::launch_transpose(src, dst, c, (int64_t)t * h * w, eb, (hipStream_t)stream),
-                                "transpose launch");
-    if (st == CC3D_OK) clear_err();
-    return st;
-}
-
-cc3d_status cc3d_to_channels_first(const void* src, void* dst, int c, int t, int h, int w, int eb, void* stream)
-{
-    if (!src || !dst) return fail(CC3D_EINVAL, "src or dst is NULL");
-    if (c < 1 || t < 1 || h < 1 || w < 1) return fail(CC3D_ESHAPE, "c=%d t=%d h=%d w=%d must be >= 1", c, t, h, w);
-    if (eb != 2 && eb != 4) return fail(CC3D_EDTYPE, "elem_bytes=%d; accepted 2 or 4", eb);
-    cc3d_status st = hip_status(cc3d::launch_transpose(src, dst, (int64_t)t * h * w, c, eb, (hipStream_t)stream),
-                                "transpose launch");
-    if (st == CC3D_OK) clear_err();
-    return st;
-}
-
-}  // extern "C"
+}  // namespace

@@ -199,6 +199,49 @@ def conv_plan(w: torch.Tensor, h_in: int, w_in: int, *, bias=None, gamma=None, u
     return Plan(h, d.dtype, w.device, cin, h_in, w_in)
 
 
+def conv_forward_noalloc(w: torch.Tensor, x: torch.Tensor, cache_in: State, cache_out: State, y: torch.Tensor,
+                         *, bias=None, gamma=None, residual=None, up_s=1, up_t=1, max_chunk_t=8,
+                         tpad=C.TPAD_REPLICATE, act=False, out_u8=False, eps=1e-6, aligned=False,
+                         fold_upsample=False, stream=None) -> torch.Tensor:
+    """One conv chunk through cc3d_conv_forward_noalloc: the result of
+    conv_plan(w, ...).forward_chunk(x, ...), with no device allocation (the
+    library repacks the weights into its fixed per-device scratch).  The
+    caller supplies y and the two state arenas (State objects sized by a plan
+    of the same conv); x is [T][h][w][cin] of w's dtype, y the chunk's output
+    shape.  Shapes and dtypes are checked here before the call."""
+    cout, cin, kt, kh, kw = w.shape
+    if w.dtype not in _DT:
+        raise ValueError("weights must be bfloat16 or float32, got %s" % w.dtype)
+    if x.dim() != 4 or x.shape[3] != cin or x.dtype != w.dtype:
+        raise ValueError("x must be [T][h][w][%d] of %s, got %s of %s" % (cin, w.dtype, tuple(x.shape), x.dtype))
+    for name, v, n in (("bias", bias, cout), ("gamma", gamma, cout)):
+        if v is not None and (v.dtype != torch.float32 or v.numel() != n):
+            raise ValueError("%s must hold %d float32 values, got %d of %s" % (name, n, v.numel(), v.dtype))
+    d = C.ConvDesc(cin=cin, cout=cout, kt=kt, kh=kh, kw=kw, h_in=x.shape[1], w_in=x.shape[2], up_s=up_s,
+                   up_t=up_t, max_chunk_t=max_chunk_t, dtype=_DT[w.dtype], tpad=tpad,
+                   epilogue=(C.EPI_RESIDUAL if residual is not None else 0) | (C.EPI_ACT if act else 0) |
+                   (C.EPI_U8 if out_u8 else 0), eps=eps, grow=C.GROW_ALIGNED if aligned else C.GROW_ONCE,
+                   fold_upsample=int(fold_upsample))
+    first = cache_in.frames_seen == 0
+    t = x.shape[0]
+    grow = up_t == 2 and first and not aligned
+    t_out = (2 * t - 1 if grow else 2 * t) if up_t == 2 else t
+    want = (t_out, x.shape[1] * up_s, x.shape[2] * up_s, cout)
+    out_dtype = torch.uint8 if out_u8 else w.dtype
+    if tuple(y.shape) != want or y.dtype != out_dtype:
+        raise ValueError("y must be %s of %s, got %s of %s" % (want, out_dtype, tuple(y.shape), y.dtype))
+    if residual is not None and (tuple(residual.shape) != want or residual.dtype != w.dtype):
+        raise ValueError("residual must be %s of %s, got %s of %s" % (want, w.dtype, tuple(residual.shape),
+                                                                       residual.dtype))
+    ci, co = cache_in._c(), cache_out._c()
+    with torch.cuda.device(x.device):
+        C.check(C.lib().cc3d_conv_forward_noalloc(ctypes.byref(d), _ptr(w), _ptr(bias), _ptr(gamma), _ptr(x), t,
+                                                  ctypes.byref(ci), ctypes.byref(co), _ptr(residual), _ptr(y),
+                                                  _stream(stream)), "cc3d_conv_forward_noalloc")
+    cache_out.frames_seen = co.frames_seen
+    return y
+
+
 def _check_weights(ops: List[Op], cin: int, dtype):
     """Each CONV op's weights must hold exactly [cout][channels of its src][k]
     of the plan dtype, and every bias and gain its channel count of float32 (the

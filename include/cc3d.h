@@ -273,6 +273,30 @@ cc3d_status cc3d_forward_chunk(const cc3d_plan* plan, const void* x, int t_chunk
                                const cc3d_state* cache_in, cc3d_state* cache_out,
                                const void* residual, void* y, void* stream);
 
+/* One conv chunk that allocates no device memory, for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments and result as cc3d_plan_create(desc, w,
+ * bias, gamma) followed by cc3d_forward_chunk(plan, x, t_chunk, cache_in,
+ * cache_out, residual, y) -- the same validation, kernels and output, bit for
+ * bit -- but the weights are repacked on every call, on `stream`, into a
+ * fixed scratch array of CC3D_NOALLOC_SCRATCH_BYTES that the library holds
+ * on each device it runs on until the process ends (with the intermediate of
+ * an act the conv's kernel does not fuse, and copies of bias and gamma).  A
+ * conv whose repacked weights and intermediates do not fit is rejected
+ * (CC3D_ENOMEM) before any device work.  The state arenas are the caller's,
+ * of cc3d_state_bytes of a plan made from the same descriptor (e.g. at set-up).
+ * No call synchronises or allocates; the first call on a device (or the first
+ * plan creation there) looks the scratch's address up.  Every call on a device
+ * shares that device's scratch: calls that overlap on one device (two streams,
+ * or two host threads) race and must be ordered by the caller.  Nothing in
+ * the scratch needs to start at zero (every byte a call reads it first
+ * writes). */
+#define CC3D_NOALLOC_SCRATCH_BYTES (64u << 20)
+cc3d_status cc3d_conv_forward_noalloc(const cc3d_conv_desc* desc, const void* w, const float* bias,
+                                      const float* gamma, const void* x, int t_chunk,
+                                      const cc3d_state* cache_in, cc3d_state* cache_out,
+                                      const void* residual, void* y, void* stream);
+
 /* Channels-first <-> channels-last copies of one video tensor (the boundary
  * between a [C][T][H][W] caller and this library's [T][H][W][C]); elem_bytes is
  * 2 or 4.  Enqueued on stream; src and dst must not overlap. */

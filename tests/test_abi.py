@@ -258,3 +258,20 @@ def test_binding_refuses_misshaped_input_before_any_library_call(monkeypatch):
         with pytest.raises(ValueError, match="x must be"):
             plan.forward_chunk(bad, st_in, st_out)
     assert st_out.frames_seen == 0
+
+
+def test_noalloc_entry_rejects_bad_arguments_before_device_work():
+    """The no-alloc conv entry point validates its descriptor and pointers
+    before any device call (no GPU is touched here)."""
+    L = C.lib()
+    si, so = C.State(DUMMY, 0), C.State(ctypes.c_void_p(0x2000), 0)
+    args = lambda d: (d, DUMMY, None, None, DUMMY, 1, ctypes.byref(si), ctypes.byref(so), None, DUMMY, None)
+    assert L.cc3d_conv_forward_noalloc(*args(None)) == C.EINVAL
+    assert L.cc3d_conv_forward_noalloc(ctypes.byref(_conv_desc(kt=4)), DUMMY, None, None, DUMMY, 1, ctypes.byref(si),
+                                       ctypes.byref(so), None, DUMMY, None) == C.ESHAPE
+    assert "kt" in C.last_error() or "kernel" in C.last_error()
+    assert L.cc3d_conv_forward_noalloc(ctypes.byref(_conv_desc()), None, None, None, DUMMY, 1, ctypes.byref(si),
+                                       ctypes.byref(so), None, DUMMY, None) == C.EINVAL
+    assert L.cc3d_conv_forward_noalloc(ctypes.byref(_conv_desc(epilogue=C.EPI_ACT | C.EPI_U8)), DUMMY, None, None,
+                                       DUMMY, 1, ctypes.byref(si), ctypes.byref(so), None, DUMMY, None) == C.EINVAL
+    assert C.NOALLOC_SCRATCH_BYTES == 64 << 20
