@@ -77,6 +77,11 @@ struct OpRt {
     int ntile = 0, nblocks = 0, kchunks = 0, family = 1;
     bool fused_act = false;
     bool out_u8 = false;  // y as 8-bit codes
+    // This op also writes the cache of op cache_to (a later conv whose input it
+    // produces) when the pass has enough frames: from its conv kernel or its
+    // norm pass (cache_norm), the result v or the act (cache_act).
+    int cache_to = -1;
+    bool cache_norm = false, cache_act = false;
 };
 
 }  // namespace
@@ -469,6 +474,41 @@ cc3d_status assign_norm_temps(cc3d_plan* p)
     return CC3D_OK;
 }
 
+// A conv's cache holds the last kt-1 frames of its window; when its input is a
+// slot an earlier op of the same pass writes and the conv does not grow time,
+// those are the slot's last kt-1 frames (whenever the pass has that many), so
+// the writing op can store them into the cache as it produces them instead of
+// a copy kernel reading them back.  Pairs each such conv with its input's
+// writer: the writer's conv kernel where it is one of the register-blocked
+// families (which take a cache destination) or its norm pass.  Ops of a
+// frame-batched group keep the copy (a batch continues its caches in place).
+void pair_cache_writers(cc3d_plan* p)
+{
+    const int n = (int)p->ops.size();
+    const int g0 = p->frame_batch > 0 ? p->batch_from : n;
+    for (int j = 0; j < n && j < g0; ++j) {
+        const OpRt& c = p->ops[j];
+        if (c.kind != CC3D_OP_CONV || c.kt < 2 || c.up_t != 1 || c.src <= CC3D_SLOT_AUX) continue;
+        int i = j - 1;
+        for (; i >= 0; --i) {
+            const OpRt& w = p->ops[i];
+            if (w.out == c.src || w.act_out == c.src) break;
+        }
+        if (i < 0) continue;
+        OpRt& w = p->ops[i];
+        if (w.cache_to >= 0) continue;  // one cache per writer
+        const bool act = w.act_out == c.src;
+        bool norm;
+        if (w.kind == CC3D_OP_NORM_ACT) norm = true;
+        else if (act) norm = !w.fused_act;
+        else norm = false;  // the conv kernel writes its result slot
+        if (!norm && !(p->dtype == CC3D_BF16 && (w.family == 2 || w.family == 5))) continue;
+        w.cache_to = j;
+        w.cache_norm = norm;
+        w.cache_act = act;
+    }
+}
+
 cc3d_status hip_status(hipError_t e, const char* what)
 {
     if (e == hipSuccess) return CC3D_OK;
@@ -568,6 +608,7 @@ cc3d_status build_plan(const cc3d_stack_desc* d, cc3d_plan* p)
     if (st != CC3D_OK) return st;
     st = assign_norm_temps(p);
     if (st != CC3D_OK) return st;
+    pair_cache_writers(p);
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_status(e, "hipGetDevice");
@@ -1058,6 +1099,20 @@ cc3d_status forward_impl(const cc3d_plan* p, const void* x, int t_chunk, const c
         if (ps.group && !sl.grouped) base += ps.in_off * ((int64_t)sl.h * sl.w * sl.c * p->elem);
         return base;
     };
+    // Caches written by the op that produces the conv's input (pair_cache_writers)
+    // in this pass: that conv skips its copy.
+    bool cache_written[CC3D_MAX_OPS] = {};
+    // Where op r stores the cache of its paired conv for an output of t_s frames
+    // (null when the pass has fewer than that conv's kt-1 frames), and the first
+    // output frame that goes there.
+    auto cache_dest = [&](const OpRt& r, const Pass& ps, int64_t t_s, int64_t* t0) -> void* {
+        if (r.cache_to < 0 || ps.group) return nullptr;
+        const OpRt& c = p->ops[r.cache_to];
+        if (t_s < c.kt - 1) return nullptr;
+        *t0 = t_s - (c.kt - 1);
+        cache_written[r.cache_to] = true;
+        return ps.cache_wr + c.cache_off;
+    };
     // rot0: frames of this op's output produced by earlier batches of the chunk
     // (the kernels' temporal-tap rotation follows the frame's place in the chunk,
     // so a batched run sums in the same order as a whole-chunk one)
@@ -1112,13 +1167,21 @@ cc3d_status forward_impl(const cc3d_plan* p, const void* x, int t_chunk, const c
             const double vox = (double)t_v * r.h_out * r.w_out;
             const double fr_in = (double)r.h_in * r.w_in * r.cin * p->elem;
             const double fr_out = (double)r.h_out * r.w_out * r.cout * p->elem;
+            int64_t c_t0 = 0;
+            void* cdst = cache_dest(r, ps, t_v, &c_t0);
+            if (cdst && !r.cache_norm) {
+                a.cache = cdst;
+                a.cache_t0 = (int)c_t0;
+                a.cache_act = r.cache_act ? 1 : 0;
+            }
             hipError_t e;
             {
                 const int nstore = (a.out ? 1 : 0) + (a.act_out ? 1 : 0);
                 const double store_scale = r.out_u8 ? 1.0 / p->elem : 1.0;  // 8-bit codes
                 const double by = fr_in * (t_in + (first ? 0 : r.kt - 1)) +
                                   (double)r.cout * r.cin * r.kt * r.kh * r.kw * p->elem +
-                                  t_v * fr_out * (nstore * store_scale + (a.res ? 1 : 0));
+                                  t_v * fr_out * (nstore * store_scale + (a.res ? 1 : 0)) +
+                                  (a.cache ? (t_v - c_t0) * fr_out : 0.0);
                 ProfScope prof(p, oi, 0, s, 2.0 * r.cin * r.cout * r.kt * r.kh * r.kw * vox, by);
                 e = p->dtype == CC3D_BF16 ? cc3d::launch_conv_bf16(a, s) : cc3d::launch_conv_f32(a, s);
             }
@@ -1132,13 +1195,18 @@ cc3d_status forward_impl(const cc3d_plan* p, const void* x, int t_chunk, const c
                 n.eps = p->eps;
                 n.n_pix = (int64_t)t_v * r.h_out * r.w_out;
                 n.c = r.cout;
+                if (cdst && r.cache_norm) {
+                    n.cache = cdst;
+                    n.cache_pix0 = c_t0 * r.h_out * r.w_out;
+                    n.cache_act = r.cache_act ? 1 : 0;
+                }
                 {
-                    ProfScope prof(p, oi, 1, s, 0.0, 2.0 * t_v * fr_out);
+                    ProfScope prof(p, oi, 1, s, 0.0, (2.0 * t_v + (n.cache ? t_v - c_t0 : 0)) * fr_out);
                     e = cc3d::launch_norm_act(n, p->elem, s);
                 }
                 if ((st = hip_status(e, "norm launch")) != CC3D_OK) return st;
             }
-            if (r.kt > 1) {
+            if (r.kt > 1 && !cache_written[oi]) {
                 {
                     ProfScope prof(p, oi, 2, s, 0.0, 2.0 * (r.kt - 1) * fr_in);
                     e = cc3d::launch_cache_update(a.z, t_v, ps.cache_wr + r.cache_off, p->elem, s);
@@ -1157,11 +1225,17 @@ cc3d_status forward_impl(const cc3d_plan* p, const void* x, int t_chunk, const c
             n.n_pix = (int64_t)t_in * r.h_in * r.w_in;
             n.c = r.cin;
             *frames_out = t_in;
+            int64_t c_t0 = 0;
+            if ((n.cache = cache_dest(r, ps, t_in, &c_t0)) != nullptr) {
+                n.cache_pix0 = c_t0 * r.h_in * r.w_in;
+                n.cache_act = r.cache_act ? 1 : 0;
+            }
             const size_t oi = (size_t)(&r - p->ops.data());
             const int nmove = 1 + (n.res ? 1 : 0) + (n.out ? 1 : 0) + (n.act_out ? 1 : 0);
             hipError_t e;
             {
-                ProfScope prof(p, oi, 0, s, 0.0, (double)n.n_pix * n.c * p->elem * nmove);
+                ProfScope prof(p, oi, 0, s, 0.0,
+                               (double)n.c * p->elem * (n.n_pix * nmove + (n.cache ? n.n_pix - n.cache_pix0 : 0)));
                 e = cc3d::launch_norm_act(n, p->elem, s);
             }
             if ((st = hip_status(e, "norm launch")) != CC3D_OK) return st;

@@ -41,6 +41,12 @@ struct ConvArgs {
     int rot_taps;         // bf16 v2 and pointwise: rotate the temporal-tap order by the output frame
     int t_rot0;           // ... counted from this frame (the launch's first frame in its chunk)
     int out_u8;           // bf16 families 1 and 3: out holds 8-bit codes of the fp32 result
+    // A later conv's cache written by this one (families 2 and 5): output frames
+    // t >= cache_t0 of the result (cache_act = 0) or of the act (1) are also
+    // stored as frame t - cache_t0 of `cache`, or null.
+    void* cache;
+    int cache_t0;
+    int cache_act;
 };
 
 // 8-bit output code of an fp32 result v: rint(clamp((v + 1) * 127.5, 0, 255)).
@@ -58,6 +64,12 @@ struct NormArgs {
     float eps;
     int64_t n_pix;
     int c;
+    // A later conv's cache written by this pass: positions >= cache_pix0 of v
+    // (cache_act = 0) or of the act (1) are also stored at position - cache_pix0
+    // of `cache`, or null.
+    void* cache;
+    int64_t cache_pix0;
+    int cache_act;
 };
 
 // bf16 implicit-GEMM conv on MFMA.  Returns hipErrorInvalidValue for a shape

@@ -298,6 +298,15 @@ __global__ __launch_bounds__(512, 1) void conv_phase_kernel(ConvArgs a)
     uint16_t* out = (uint16_t*)a.out;
     uint16_t* act = (uint16_t*)a.act_out;
     const uint16_t* res = (const uint16_t*)a.res;
+    // a later conv's cache: this frame's values also go to frame t - cache_t0 of
+    // a.cache (the base is shifted so the same per-pixel offset applies)
+    uint16_t* craw = nullptr;
+    uint16_t* cact = nullptr;
+    if (a.cache && t >= a.cache_t0) {
+        uint16_t* cb = (uint16_t*)a.cache - (int64_t)a.cache_t0 * a.h_out * a.w_out * a.cout;
+        if (a.cache_act) cact = cb;
+        else craw = cb;
+    }
     float* red = lds_red;
     const bool vec_ok = (a.cout & 3) == 0;
     auto pixel_base = [&](int m, bool& valid) -> int64_t {
@@ -348,6 +357,7 @@ __global__ __launch_bounds__(512, 1) void conv_phase_kernel(ConvArgs a)
                 v[2] = bf2f((uint16_t)(hb.y & 0xffffu));
                 v[3] = bf2f((uint16_t)(hb.y >> 16));
                 if (out && valid) *(uint2*)(out + pbase + n) = hb;
+                if (craw && valid) *(uint2*)(craw + pbase + n) = hb;
             } else if (n < a.cout) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -357,6 +367,7 @@ __global__ __launch_bounds__(512, 1) void conv_phase_kernel(ConvArgs a)
                     const uint16_t hb = f2bf(v[i]);
                     v[i] = bf2f(hb);
                     if (out && valid) out[pbase + n + i] = hb;
+                    if (craw && valid) craw[pbase + n + i] = hb;
                 }
             } else {
                 v[0] = v[1] = v[2] = v[3] = 0.f;
@@ -396,7 +407,9 @@ __global__ __launch_bounds__(512, 1) void conv_phase_kernel(ConvArgs a)
             if (!valid || n >= a.cout) continue;
             const float z0 = silu(gm[f].x * acc[m][f][0] * inv), z1 = silu(gm[f].y * acc[m][f][1] * inv);
             const float z2 = silu(gm[f].z * acc[m][f][2] * inv), z3 = silu(gm[f].w * acc[m][f][3] * inv);
-            *(uint2*)(act + pbase + n) = make_uint2(pack_bf16x2(z0, z1), pack_bf16x2(z2, z3));
+            const uint2 hv = make_uint2(pack_bf16x2(z0, z1), pack_bf16x2(z2, z3));
+            *(uint2*)(act + pbase + n) = hv;
+            if (cact) *(uint2*)(cact + pbase + n) = hv;
         }
     }
 }

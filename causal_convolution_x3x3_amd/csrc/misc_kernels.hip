@@ -119,7 +119,10 @@ __global__ __launch_bounds__(256) void norm_act_kernel(NormArgs a)
         const int unit = l32 + 32 * u;
         if (live && unit < nunits) {
             const int64_t e = pix * a.c + unit * 4;
+            const bool to_cache = a.cache && pix >= a.cache_pix0;
+            const int64_t ce = (pix - a.cache_pix0) * a.c + unit * 4;
             if (a.out) Vec4<T>::store(a.out, e, v[u]);
+            if (to_cache && !a.cache_act) Vec4<T>::store(a.cache, ce, v[u]);
             if (a.act_out) {
                 float o[4];
                 for (int i = 0; i < 4; ++i) {
@@ -127,6 +130,7 @@ __global__ __launch_bounds__(256) void norm_act_kernel(NormArgs a)
                     o[i] = z / (1.0f + expf(-z));
                 }
                 Vec4<T>::store(a.act_out, e, o);
+                if (to_cache && a.cache_act) Vec4<T>::store(a.cache, ce, o);
             }
         }
     }
@@ -186,10 +190,16 @@ __global__ __launch_bounds__(256) void norm_act_bf16_kernel(NormArgs a)
     }
 #pragma unroll
     for (int o = 1; o < LPP; o <<= 1) ss += __shfl_xor(ss, o, LPP);
+    const bool to_cache = a.cache && pix >= a.cache_pix0;
+    uint4* cdst = (uint4*)a.cache + (pix - a.cache_pix0) * (LPP * U);
     if (a.out) {
         uint4* dst = (uint4*)a.out + pix * (LPP * U);
 #pragma unroll
         for (int u = 0; u < U; ++u) dst[l + LPP * u] = r[u];
+    }
+    if (to_cache && !a.cache_act) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) cdst[l + LPP * u] = r[u];
     }
     if (!a.act_out) return;
     const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / (float)a.c) + a.eps);
@@ -203,7 +213,9 @@ __global__ __launch_bounds__(256) void norm_act_bf16_kernel(NormArgs a)
         float o[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[i] = silu(gm[i] * v[u][i] * inv);
-        dst[l + LPP * u] = pack8(o);
+        const uint4 h = pack8(o);
+        dst[l + LPP * u] = h;
+        if (to_cache && a.cache_act) cdst[l + LPP * u] = h;
     }
 }
 
@@ -322,7 +334,8 @@ hipError_t launch_norm_act(const NormArgs& a, int elem_bytes, hipStream_t s)
     const int64_t blocks = (threads + 255) / 256;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     int lpp = 0, u = 0;
-    const bool aligned = (((uintptr_t)a.src | (uintptr_t)a.res | (uintptr_t)a.out | (uintptr_t)a.act_out) & 15u) == 0;
+    const bool aligned =
+        (((uintptr_t)a.src | (uintptr_t)a.res | (uintptr_t)a.out | (uintptr_t)a.act_out | (uintptr_t)a.cache) & 15u) == 0;
     if (elem_bytes == 2 && aligned && norm_bf16_shape(a.c, lpp, u)) {
         if (lpp == 4) return launch_norm_bf16_u<4>(a, u, s);
         if (lpp == 8) return launch_norm_bf16_u<8>(a, u, s);
