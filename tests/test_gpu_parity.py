@@ -411,6 +411,51 @@ def test_bf16_conv_epilogue_act(cout, residual):
     assert_bf16_close(got, ref, "epilogue")
 
 
+WHOLE_TILE_CASES = [
+    # cin, cout, up_s, h, w, residual, act, kernel that must run: frames that
+    # the register-blocked kernel's tiles cover exactly (9x64 / 8x64 output
+    # tiles; 12x16 / 8x16 source tiles when upsampling), so its epilogue runs
+    # without bounds tests
+    (96, 96, 1, 18, 64, True, True, "conv_bf16_v2_up1_k3_n96"),
+    (64, 96, 1, 9, 128, False, True, "conv_bf16_v2_up1_k3_n96"),
+    (96, 128, 1, 16, 64, True, False, "conv_bf16_v2_up1_k3_n128"),
+    (96, 192, 1, 9, 64, True, True, "conv_bf16_v2_up1_k3_n96"),
+    (96, 96, 2, 12, 32, True, True, "conv_bf16_v2_up2_k3_n96"),
+    (64, 128, 2, 8, 16, False, False, "conv_bf16_v2_up2_k3_n128"),
+]
+
+
+@pytest.mark.parametrize("case", WHOLE_TILE_CASES, ids=lambda c: "ci%d_co%d_us%d_%dx%d_r%d_a%d" % c[:7])
+def test_bf16_conv_whole_tiles(case):
+    """The register-blocked conv on frames its tiles cover exactly (the
+    epilogue form without per-fragment bounds tests): v = conv + bias
+    (+ residual) stored as bf16, and SiLU(RMSNorm(v)) where asked, against the
+    oracle; the act is fused in the conv up to 96 channels, else the norm pass."""
+    cin, cout, up_s, h, w, residual, act, kname = case
+    say("bf16 whole tiles %s" % (case,))
+    splits = [1, 2]
+    t = sum(splits)
+    x = synth.bf16(synth.video(cin, t, h, w, synth.seed(30, cin + cout)))
+    wt = synth.bf16(synth.conv_weight(cout, cin, 3, 3, 3, synth.seed(30, 2)))
+    b = synth.bias(cout, synth.seed(30, 3))
+    g = synth.gain(cout, synth.seed(30, 4))
+    ho, wo = up_s * h, up_s * w
+    r = synth.bf16(synth.video(cout, t, ho, wo, synth.seed(30, 5))) if residual else None
+    v = O.one_shot(to_oracle(x), to_oracle(wt), to_oracle(b), O.REPLICATE, up_s, 1)
+    if residual:
+        v = v + to_oracle(r)
+    ref = O.act(O.round_bf16(v), to_oracle(g), 1e-6) if act else v
+    plan = P.conv_plan(wt.cuda(), h, w, bias=b.cuda(), gamma=g.cuda() if act else None, act=act,
+                       residual=residual, up_s=up_s, max_chunk_t=2)
+    C.check(C.lib().cc3d_profile_enable(plan._h, 1), "profile_enable")
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits,
+                                     residual_cl=to_device_cl(r) if residual else None))
+    pr = C.OpProfile()
+    C.check(C.lib().cc3d_profile_read(plan._h, 0, 0, ctypes.byref(pr)), "profile_read")
+    assert pr.kernel.decode().startswith(kname), pr.kernel
+    assert_bf16_close(got, ref, "whole tiles")
+
+
 @pytest.mark.parametrize("c", [16, 24, 32, 64, 96, 128, 192, 256, 320, 384, 512])
 def test_norm_act_pass_lane_layouts(c):
     """The standalone norm pass (NORM_ACT ops) in every layout it picks for c
