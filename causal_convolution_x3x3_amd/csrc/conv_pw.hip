@@ -12,16 +12,18 @@
 // position to its source position (identity, or the nearest 2x upsample).
 //
 // * A work item is (a run of TP consecutive output positions of frame t, a block
-//   of NTILE output channels).  8 waves, two per SIMD: four along M (16*MW
-//   positions each) and two along N.  The weights are the MFMA's row operand, so
+//   of NTILE output channels).  8 waves: four along M (16*MW positions each)
+//   and two along N; one workgroup per CU (two waves per SIMD) or, with a
+//   smaller tile and ring, two (four waves per SIMD, so that one workgroup's
+//   prologue and epilogue run beside the other's loop).  The weights are the MFMA's row operand, so
 //   a lane's accumulators are four consecutive channels of one position and the
 //   epilogue moves 8-byte vectors.
 // * K is walked in steps of (temporal tap, 32 channels): one MFMA deep.  Both
 //   operands go from global memory straight into LDS (buffer loads with the LDS
 //   flag), NB - 1 steps ahead into a ring of NB buffer sets; one barrier per
 //   step, which waits only for the next step's loads.  A step's MFMAs take well
-//   under a microsecond, less than the loads' latency, so a deep ring is what
-//   keeps the pipe fed.  Every lane's 16-byte slot of the position tile has a
+//   under a microsecond, less than the loads' latency, so a deep ring (or a
+//   second workgroup) is what keeps the pipe fed.  Every lane's 16-byte slot of the position tile has a
 //   fixed source offset, so the nearest upsample (and any ragged tail past the
 //   frame, read as zeros) costs nothing in the loop.
 // * Temporal taps are taken in an order rotated by the output frame, and work
@@ -42,10 +44,11 @@ struct IC {
 };
 
 constexpr int KC = 32;  // channels per K step
-constexpr int NB = 5;   // buffer sets in the ring: loads NB - 1 steps ahead
 
-template <int UP, int NF, int MW>
-__global__ __launch_bounds__(512, 1) void conv_pw_kernel(ConvArgs a)
+// NB = buffer sets in the ring (loads NB - 1 steps ahead, at most 5); OCC =
+// workgroups per CU the LDS and registers are sized for.
+template <int UP, int NF, int MW, int NB, int OCC>
+__global__ __launch_bounds__(512, 2 * OCC) void conv_pw_kernel(ConvArgs a)
 {
     constexpr int WN = 2, NT = 512;
     constexpr int NFW = NF / WN;          // N fragments per wave
@@ -62,12 +65,12 @@ __global__ __launch_bounds__(512, 1) void conv_pw_kernel(ConvArgs a)
     static_assert(NF % WN == 0, "N fragments split evenly over the N waves");
     constexpr int LI = A_IT + RB16 + RB4;  // load instructions per step and lane
     static_assert((NB - 2) * LI < 64, "vmcnt range");
-    static_assert(NB * (A_CH + B_CH) * 16 <= 160 * 1024, "LDS budget");
+    static_assert(NB * (A_CH + B_CH) * 16 <= 160 * 1024 / OCC, "LDS budget");
+    static_assert(NB >= 3 && NB <= 5, "three to five buffer sets");
 
     // one LDS variable per buffer (the compiler then sees which one a load fills)
-    __shared__ uint4 lds_a0[A_CH], lds_a1[A_CH], lds_a2[A_CH], lds_a3[A_CH], lds_a4[A_CH];
-    __shared__ uint4 lds_b0[B_CH], lds_b1[B_CH], lds_b2[B_CH], lds_b3[B_CH], lds_b4[B_CH];
-    static_assert(NB == 5, "five buffer sets declared");
+    __shared__ uint4 lds_a0[A_CH], lds_a1[A_CH], lds_a2[A_CH], lds_a3[NB > 3 ? A_CH : 1], lds_a4[NB > 4 ? A_CH : 1];
+    __shared__ uint4 lds_b0[B_CH], lds_b1[B_CH], lds_b2[B_CH], lds_b3[NB > 3 ? B_CH : 1], lds_b4[NB > 4 ? B_CH : 1];
     auto abuf = [&](auto J) -> uint4* {
         constexpr int j = decltype(J)::value;
         return j == 0 ? lds_a0 : j == 1 ? lds_a1 : j == 2 ? lds_a2 : j == 3 ? lds_a3 : lds_a4;
@@ -157,7 +160,7 @@ __global__ __launch_bounds__(512, 1) void conv_pw_kernel(ConvArgs a)
     const int co = (g ^ swz(k16)) << 4;
     int a_frag[MW], b_frag[NFW];
 #pragma unroll
-    for (int m = 0; m < MW; ++m) a_frag[m] = (64 * wm + 16 * m + k16) * 64 + co;
+    for (int m = 0; m < MW; ++m) a_frag[m] = (16 * MW * wm + 16 * m + k16) * 64 + co;
 #pragma unroll
     for (int f = 0; f < NFW; ++f) b_frag[f] = (16 * (wn * NFW + f) + k16) * 64 + co;
 
@@ -188,8 +191,8 @@ __global__ __launch_bounds__(512, 1) void conv_pw_kernel(ConvArgs a)
     auto clamp = [&](int s_) { return s_ < nsteps ? s_ : nsteps - 1; };
     issue(clamp(0), lds_a0, lds_b0);
     issue(clamp(1), lds_a1, lds_b1);
-    issue(clamp(2), lds_a2, lds_b2);
-    issue(clamp(3), lds_a3, lds_b3);
+    if (NB > 3) issue(clamp(2), lds_a2, lds_b2);
+    if (NB > 4) issue(clamp(3), lds_a3, lds_b3);
     wait_vmcnt<(NB - 2) * LI>();  // step 0 has landed
     __builtin_amdgcn_s_barrier();
     auto k_step = [&](int step, auto J) {
@@ -207,19 +210,23 @@ __global__ __launch_bounds__(512, 1) void conv_pw_kernel(ConvArgs a)
         k_step(step, IC<0>{});
         if (step + 1 < nsteps) k_step(step + 1, IC<1>{});
         if (step + 2 < nsteps) k_step(step + 2, IC<2>{});
-        if (step + 3 < nsteps) k_step(step + 3, IC<3>{});
-        if (step + 4 < nsteps) k_step(step + 4, IC<4>{});
+        if constexpr (NB > 3) {
+            if (step + 3 < nsteps) k_step(step + 3, IC<3>{});
+        }
+        if constexpr (NB > 4) {
+            if (step + 4 < nsteps) k_step(step + 4, IC<4>{});
+        }
     }
 
     // ---------------------------------------------------------------- epilogue
     // acc[m][f] holds D[channel][position]: lane (g, k16) has channels
-    // n0 + 16 f .. + 3 of position p0 + 64 wm + 16 m + k16.
+    // n0 + 16 f .. + 3 of position p0 + 16 MW wm + 16 m + k16.
     const int n0 = nb * NTILE + wn * NFW * 16 + 4 * g;
     uint16_t* out = (uint16_t*)a.out;
     const uint16_t* res = (const uint16_t*)a.res;
 #pragma unroll
     for (int m = 0; m < MW; ++m) {
-        const int pos = p0 + 64 * wm + 16 * m + k16;
+        const int pos = p0 + 16 * MW * wm + 16 * m + k16;
         if (pos >= hw_out) continue;
         const int64_t pbase = ((int64_t)t * hw_out + pos) * a.cout;
         // this row's residual before its stores (a load of `res` may not move
@@ -251,16 +258,15 @@ __global__ __launch_bounds__(512, 1) void conv_pw_kernel(ConvArgs a)
     }
 }
 
-template <int UP, int NF>
+template <int UP, int NF, int MW = 4, int NB = 5, int OCC = 1>
 hipError_t launch_pw(const ConvArgs& a, hipStream_t s)
 {
-    constexpr int MW = 4;
     constexpr int TP = 4 * 16 * MW;
     const int64_t hw = (int64_t)a.h_out * a.w_out;
     const int64_t total = (hw + TP - 1) / TP * a.t_out * a.nblocks;
     if (total <= 0 || total > (int64_t)0x7fffffff - 8) return hipErrorInvalidValue;
     const int64_t grid = ((total + 7) / 8) * 8;
-    hipLaunchKernelGGL((conv_pw_kernel<UP, NF, MW>), dim3((unsigned)grid), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((conv_pw_kernel<UP, NF, MW, NB, OCC>), dim3((unsigned)grid), dim3(512), 0, s, a);
     return hipGetLastError();
 }
 
@@ -326,7 +332,10 @@ hipError_t launch_pack_pw(const void* w, void* wpk, int cout, int cin, int kt, h
 hipError_t launch_conv_pw(const ConvArgs& a, hipStream_t s)
 {
     if (!pw_conv_applies(a.cout, a.kh, a.kw, a.up_s) || a.act_out || a.out_u8 || !a.out) return hipErrorInvalidValue;
-    if (a.ntile == 192) return a.up_s == 1 ? launch_pw<1, 12>(a, s) : launch_pw<2, 12>(a, s);
+    // 192-channel blocks: 128 positions per item, a ring of three buffer sets
+    // (60 KB), two workgroups per CU -- measured 0-4% faster on TemporalGrow's
+    // convs than 256 positions with five sets and one workgroup per CU
+    if (a.ntile == 192) return a.up_s == 1 ? launch_pw<1, 12, 2, 3, 2>(a, s) : launch_pw<2, 12, 2, 3, 2>(a, s);
     if (a.ntile == 96) return a.up_s == 1 ? launch_pw<1, 6>(a, s) : launch_pw<2, 6>(a, s);
     return hipErrorInvalidValue;
 }
