@@ -60,6 +60,7 @@ STACK_CASES = {
     "full_one_latent": case(48, FULL_STAGES, 4, 2, 3, (1, 1, 1, 1)),
     "full_two_clips": case(48, FULL_STAGES, 13, 4, 6, (7, 6)),
     "smoke": case(48, FULL_STAGES, 3, 2, 3, (2, 1), cfg=9),
+    "full_fused_cache": case(48, FULL_STAGES, 4, 2, 3, (2, 2), cfg=9),
 }
 for _i, (_cl, _st, _t, _h, _w, _sp, _tg, _al, _fold) in enumerate(RANDOM_CASES):
     STACK_CASES["random%d" % _i] = case(_cl, _st, _t, _h, _w, _sp, cfg=9, tg=_tg, aligned=_al)

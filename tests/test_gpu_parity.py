@@ -764,6 +764,47 @@ def test_decoder_full_channels_tiny_frame(aligned, fold):
     assert_stack_close(got, ref, case, "decoder full channels")
 
 
+def test_decoder_cache_writes_fused_into_producers():
+    """Where a conv's input is a slot an earlier op of the same pass writes (and
+    the conv does not grow time), that op stores the conv's cache as it writes
+    the slot and no copy kernel runs for it; convs that read x or grow time keep
+    the copy.  The full-channel decoder in chunks of two latents (every slot has
+    at least the k_t - 1 = 2 frames a cache holds), against the oracle too."""
+    say("decoder: cache writes fused into the producers")
+    c = SC.STACK_CASES["full_fused_cache"]
+    c_lat, h, w, splits = c["c_lat"], c["h"], c["w"], list(c["splits"])
+    assert splits == [2, 2] and c["stages"] == OM.DECODER_STAGES
+    params = SC.weights(c)
+    cpu = {n: {k: None if v is None else v.double().numpy() for k, v in p.items()} for n, p in params.items()}
+    gpu = {n: {k: None if v is None else v.cuda() for k, v in p.items()} for n, p in params.items()}
+    x = SC.latent(c)
+    dec = OM.Decoder(cpu, store=O.round_bf16)
+    xo = x.double().numpy()
+    ref = np.concatenate([dec.step(xo[:, :2]), dec.step(xo[:, 2:4])], axis=1)
+    ops = S.decoder_ops(gpu)
+    plan = P.stack_plan(ops, c_lat, h, w, max_chunk_t=2)
+    C.check(C.lib().cc3d_profile_enable(plan._h, 1), "profile_enable")
+    st = P.Stream(plan)
+    x_cl = to_device_cl(x)
+    y = torch.cat([st.step(x_cl[:2].contiguous()), st.step(x_cl[2:4].contiguous())])
+    torch.cuda.synchronize()
+    fused = copied = 0
+    for i, o in enumerate(ops):
+        if o.kind != C.OP_CONV or o.k[0] < 2:
+            continue
+        pr = C.OpProfile()
+        C.check(C.lib().cc3d_profile_read(plan._h, i, 2, ctypes.byref(pr)), "profile_read")
+        if o.src == C.SLOT_X or o.up_t == 2:
+            assert pr.launches == 2, "%s: expected the cache copy in both chunks, got %d" % (o.name, pr.launches)
+            copied += 1
+        else:
+            assert pr.launches == 0, "%s: cache copied %d times, expected it stored by the producer" % (
+                o.name, pr.launches)
+            fused += 1
+    assert fused >= 10 and copied >= 1, (fused, copied)
+    assert_stack_close(from_device_cl(y), ref, "full_fused_cache", "fused cache writes")
+
+
 @pytest.mark.parametrize("t_prime,aligned,fold", [(1, False, False), (3, False, False), (4, False, True),
                                                    (3, True, False), (2, True, True)])
 def test_decoder_causality_bitwise(t_prime, aligned, fold):
