@@ -130,6 +130,10 @@ BF16_CASES = [
     (96, 96, (3, 3, 3), 1, 1, 17, 131, [1, 2], C.TPAD_REPLICATE, False),
     (192, 96, (3, 3, 3), 2, 1, 9, 35, [2, 1], C.TPAD_REPLICATE, True),
     (384, 384, (3, 3, 3), 2, 2, 5, 6, [1, 1], C.TPAD_REPLICATE, False),
+    # eight 96-channel blocks: each block's items on its own XCD (the 4- and
+    # 8-block dealing), with and without nearest 2x
+    (32, 768, (3, 3, 3), 1, 1, 9, 20, [1, 2], C.TPAD_REPLICATE, True),
+    (32, 768, (3, 3, 3), 2, 1, 5, 7, [2, 1], C.TPAD_ZERO, True),
     (16, 32, (2, 1, 1), 1, 1, 7, 19, [1, 2, 2], C.TPAD_ZERO, False),
     (16, 64, (1, 3, 3), 2, 1, 7, 9, [2, 1], C.TPAD_REPLICATE, True),
     (24, 16, (3, 1, 1), 1, 2, 5, 17, [2, 1], C.TPAD_ZERO, False),
