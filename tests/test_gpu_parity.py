@@ -460,6 +460,45 @@ def test_bf16_conv_whole_tiles(case):
     assert_bf16_close(got, ref, "whole tiles")
 
 
+RESIDUAL_ROW_CASES = [
+    # cin, cout, h, w, splits, act: the register-blocked conv (no upsampling)
+    # with a residual, at odd and even K-step counts (cin 32: 3 steps; 64: 6),
+    # on the small-frame 5-row tiles and the 9-/8-row ones, with ragged bottom
+    # and right tiles, several and eight channel blocks, and a cout that is not
+    # a multiple of 8.
+    (32, 96, 130, 400, [3, 1], True),
+    (64, 192, 70, 300, [2, 1], False),
+    (32, 256, 66, 260, [2, 2], False),
+    (64, 128, 13, 70, [1, 2], False),
+    (32, 100, 30, 90, [1, 2], False),
+    (32, 768, 9, 20, [1, 2], False),
+]
+
+
+@pytest.mark.parametrize("case", RESIDUAL_ROW_CASES, ids=lambda c: "ci%d_co%d_%dx%d" % c[:4])
+def test_bf16_conv_residual_rows(case):
+    """v = conv + bias + residual (and SiLU(RMSNorm(v)) where asked) from the
+    register-blocked kernel, against the oracle."""
+    cin, cout, h, w, splits, act = case
+    say("bf16 residual rows %s" % (case,))
+    t = sum(splits)
+    x = synth.bf16(synth.video(cin, t, h, w, synth.seed(31, cin + cout)))
+    wt = synth.bf16(synth.conv_weight(cout, cin, 3, 3, 3, synth.seed(31, 2)))
+    b = synth.bias(cout, synth.seed(31, 3))
+    g = synth.gain(cout, synth.seed(31, 4))
+    r = synth.bf16(synth.video(cout, t, h, w, synth.seed(31, 5)))
+    v = O.causal_conv3d(to_oracle(x), to_oracle(wt), to_oracle(b), O.REPLICATE) + to_oracle(r)
+    ref = O.act(O.round_bf16(v), to_oracle(g), 1e-6) if act else v
+    plan = P.conv_plan(wt.cuda(), h, w, bias=b.cuda(), gamma=g.cuda() if act else None, act=act,
+                       residual=True, max_chunk_t=max(splits))
+    C.check(C.lib().cc3d_profile_enable(plan._h, 1), "profile_enable")
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits, residual_cl=to_device_cl(r)))
+    pr = C.OpProfile()
+    C.check(C.lib().cc3d_profile_read(plan._h, 0, 0, ctypes.byref(pr)), "profile_read")
+    assert pr.kernel.decode().startswith("conv_bf16_v2_up1_k3"), pr.kernel
+    assert_bf16_close(got, ref, "residual rows")
+
+
 @pytest.mark.parametrize("c", [16, 24, 32, 64, 96, 128, 192, 256, 320, 384, 512])
 def test_norm_act_pass_lane_layouts(c):
     """The standalone norm pass (NORM_ACT ops) in every layout it picks for c
