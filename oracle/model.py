@@ -25,6 +25,16 @@ workloads built from those pieces:
   runs it at the stage's input size, ahead of the upsample conv; "after" runs it
   on the upsampled positions, between the upsample and the spatial conv.
 
+* ``Encoder``   the decoder read backwards (the pages print no encoder layer;
+  "ReAE: Causal Halo Exchange" puts the ReAE encoder under the decoder's
+  causal-state rule, and "From Pixels to Latents and Back" has it map the
+  target-size video to the latents the decoder reads): a stride-2 conv from
+  the pixels, three stages of [two ResBlocks -> conv with spatial stride 2 and
+  the decoder stage's temporal factor as temporal stride], then act -> conv to
+  the latent channels.  Each strided conv mirrors one upsampling conv of the
+  decoder; 1 + 4n frames give 1 + n latents (the first frame on its own), or
+  4n give n with ``aligned``.
+
 ``store`` is the storage rounding: with ``store=round_bf16`` every tensor that
 passes between layers is rounded to bfloat16, as a bf16 pipeline stores it
 (the conv output after bias and residual; the activation, computed from the
@@ -48,8 +58,10 @@ def _keep(x, store):
 class Conv:
     """One causal conv layer with its cache (see oracle.CausalConvStream)."""
 
-    def __init__(self, p, mode=O.REPLICATE, up_s=1, up_t=1, nthreads=None, aligned=False):
-        self.s = O.CausalConvStream(p["w"], p.get("b"), mode, up_s, up_t, nthreads, aligned)
+    def __init__(self, p, mode=O.REPLICATE, up_s=1, up_t=1, nthreads=None, aligned=False,
+                 stride_s=1, stride_t=1):
+        self.s = O.CausalConvStream(p["w"], p.get("b"), mode, up_s, up_t, nthreads, aligned,
+                                    stride_s, stride_t)
 
     def reset(self):
         self.s.reset()
@@ -197,6 +209,65 @@ class Decoder:
                 h = b.step(h)
         a = _keep(O.act(h, self.g_head, self.eps), st)
         return _keep(self.head.step(a), st)
+
+
+def encoder_layer_shapes(c_in=3, stages=DECODER_STAGES, c_latent=48, k=3):
+    """(name, Cout, Cin, kt, kh, kw, has_gain, stride_s, stride_t) for every conv
+    of the encoder, in execution order: the decoder's stages taken from the
+    last, each strided conv going back to the channels the matching decoder
+    stage started from."""
+    widths = [stages[0][0]] + [c for c, _ in stages]  # the decoder's conv_in width, then each stage's
+    shapes = [("conv_in", stages[-1][0], c_in, k, k, k, False, 2, 1)]
+    for ei in range(len(stages)):
+        si = len(stages) - 1 - ei  # the decoder stage this one mirrors
+        c, f = stages[si]
+        for r in range(2):
+            shapes.append(("e%d.rb%d.c1" % (ei, r), c, c, k, k, k, True, 1, 1))
+            shapes.append(("e%d.rb%d.c2" % (ei, r), c, c, k, k, k, True, 1, 1))
+        shapes.append(("e%d.down" % ei, widths[si], c, k, k, k, False, 2, f))
+    shapes.append(("conv_out", c_latent, widths[0], k, k, k, True, 1, 1))
+    return shapes
+
+
+class Encoder:
+    """The encoder read of the module docstring; ``params`` keyed by the names
+    of encoder_layer_shapes.  ``aligned``: every latent takes four new frames
+    (the 28-frame first chunk); otherwise the first frame makes the first
+    latent on its own."""
+
+    def __init__(self, params, eps=1e-6, mode=O.ZERO, stages=DECODER_STAGES, store=None,
+                 nthreads=None, aligned=False):
+        self.eps, self.store = eps, store
+        self.conv_in = Conv(params["conv_in"], mode, nthreads=nthreads, stride_s=2)
+        self.blocks, self.downs = [], []
+        for ei in range(len(stages)):
+            f = stages[len(stages) - 1 - ei][1]
+            self.blocks.append([
+                ResBlock(params["e%d.rb%d.c1" % (ei, r)], params["e%d.rb%d.c2" % (ei, r)],
+                         eps, mode, store, nthreads) for r in range(2)])
+            self.downs.append(Conv(params["e%d.down" % ei], mode, nthreads=nthreads, aligned=aligned,
+                                   stride_s=2, stride_t=f))
+        self.conv_out = Conv(params["conv_out"], mode, nthreads=nthreads)
+        self.g_out = params["conv_out"]["g"]
+
+    def reset(self):
+        self.conv_in.reset()
+        self.conv_out.reset()
+        for d in self.downs:
+            d.reset()
+        for bl in self.blocks:
+            for b in bl:
+                b.reset()
+
+    def step(self, x):
+        st = self.store
+        h = _keep(self.conv_in.step(x), st)
+        for bl, down in zip(self.blocks, self.downs):
+            for b in bl:
+                h = b.step(h)
+            h = _keep(down.step(h), st)
+        a = _keep(O.act(h, self.g_out, self.eps), st)
+        return _keep(self.conv_out.step(a), st)
 
 
 def output_frames(n_latent: int, temporal_factors=(2, 2), aligned: bool = False) -> int:

@@ -29,6 +29,15 @@ float64 numpy arrays laid out [C][T][H][W] (one video, channels first):
   doubles every frame, the first chunk's included (``aligned=True``); with
   copies of the first frame as history it puts the first output frame three
   extra times in front of the other rule's output.
+* strided causal conv -- "ReAE: Causal Halo Exchange": the ReAE encoder keeps
+  the same per-layer causal state as the decoder.  The page prints no encoder
+  layer; an encoder that reduces frame size and frame rate is read here as the
+  causal conv taken at every s-th pixel (zero padding (k-1)/2, PyTorch's stride
+  convention) and at every s_t-th frame.  Output j's current frame is input
+  frame s_t*j + phase: phase 0 keeps the first frame on its own (1 + 4n frames
+  -> 1 + n after two 2x reductions, the mirror of growth on non-first frames),
+  phase s_t - 1 with ``aligned`` (every output consumes s_t new frames, the
+  mirror of the aligned growth).
 
 The dense sum itself runs in ``cc3d_oracle.c`` (plain nested loops, fp64).
 """
@@ -70,8 +79,10 @@ def _lib():
         i64 = ctypes.c_int64
         lib.cc3d_oracle_conv_valid.argtypes = [dp, i, i, i, i, dp, i, i, i, i, dp, dp, i]
         lib.cc3d_oracle_conv_valid.restype = i
+        lib.cc3d_oracle_conv_strided.argtypes = [dp, i, i, i, i, dp, i, i, i, i, dp, i, i, i, dp, i]
+        lib.cc3d_oracle_conv_strided.restype = i
         lib.cc3d_oracle_conv_points.argtypes = [
-            ctypes.POINTER(ctypes.c_float), i64, i64, i64, i64, i, i, i, i, i,
+            ctypes.POINTER(ctypes.c_float), i64, i64, i64, i64, i, i, i, i, i, i,
             dp, i, i, i, i, dp, ctypes.POINTER(ctypes.c_int32), i64, dp, i]
         lib.cc3d_oracle_conv_points.restype = i
         _lib_handle = lib
@@ -109,11 +120,40 @@ def conv_valid(xp: np.ndarray, w: np.ndarray, bias=None, nthreads: int | None = 
     return y
 
 
+def conv_strided(xp: np.ndarray, w: np.ndarray, bias=None, t0: int = 0, stride_t: int = 1,
+                 stride_s: int = 1, nthreads: int | None = None) -> np.ndarray:
+    """Y[o,j,h,w] = B[o] + sum W[o,c,a,b,d] Xp[c, t0+st*j+a, ss*h+b-ph, ss*w+d-pw]
+    over a temporally padded sequence Xp; spatial zero padding.  Every output
+    whose window lies inside Xp: (Tp - kt - t0) // st + 1 frames (none when
+    Tp < t0 + kt) of (H-1)//ss + 1 x (W-1)//ss + 1 pixels."""
+    xp = np.ascontiguousarray(xp, dtype=np.float64)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    cin, tp, h, wd = xp.shape
+    cout, cin_w, kt, kh, kw = w.shape
+    if cin_w != cin:
+        raise ValueError("weight Cin %d != input Cin %d" % (cin_w, cin))
+    if t0 < 0 or stride_t < 1 or stride_s < 1:
+        raise ValueError("t0 must be >= 0 and the strides >= 1")
+    ho, wo = (h - 1) // stride_s + 1, (wd - 1) // stride_s + 1
+    if tp < t0 + kt:
+        return np.zeros((cout, 0, ho, wo), dtype=np.float64)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float64)
+    y = np.empty((cout, (tp - kt - t0) // stride_t + 1, ho, wo), dtype=np.float64)
+    rc = _lib().cc3d_oracle_conv_strided(
+        _dptr(xp), cin, tp, h, wd, _dptr(w), cout, kt, kh, kw,
+        None if b is None else _dptr(b), t0, stride_t, stride_s, _dptr(y), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("cc3d_oracle_conv_strided rejected its arguments")
+    return y
+
+
 def conv_points(z: np.ndarray, w: np.ndarray, bias, pts: np.ndarray, up: int = 1,
-                nthreads: int | None = None) -> np.ndarray:
+                nthreads: int | None = None, down: int = 1) -> np.ndarray:
     """The conv sum at output positions pts (n x 3: t, y, x) of the conv applied to
     the nearest-upsampled (factor ``up``) padded sequence Z [Cin][Tz][H][W]
-    (any strides, float32 holding exact values).  Returns n x Cout fp64."""
+    (any strides, float32 holding exact values), or with spatial stride
+    ``down`` (output (y, x) centred on pixel (down*y, down*x)); t is the first
+    frame of the output's window in Z.  Returns n x Cout fp64."""
     if z.dtype != np.float32:
         raise TypeError("conv_points reads a float32 input")
     w = np.ascontiguousarray(w, dtype=np.float64)
@@ -127,7 +167,7 @@ def conv_points(z: np.ndarray, w: np.ndarray, bias, pts: np.ndarray, up: int = 1
     st = [s // z.itemsize for s in z.strides]
     rc = _lib().cc3d_oracle_conv_points(
         z.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), st[0], st[1], st[2], st[3],
-        cin, tz, hin, win, up, _dptr(w), cout, kt, kh, kw,
+        cin, tz, hin, win, up, down, _dptr(w), cout, kt, kh, kw,
         None if b is None else _dptr(b),
         pts.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), pts.shape[0], _dptr(out),
         nthreads or default_threads())
@@ -154,9 +194,29 @@ def temporal_pad(x: np.ndarray, kt: int, mode: str) -> np.ndarray:
 
 
 def causal_conv3d(x: np.ndarray, w: np.ndarray, bias=None, mode: str = REPLICATE,
-                  nthreads: int | None = None) -> np.ndarray:
-    """One-shot causal conv over the whole sequence: conv_valid(temporal_pad(x))."""
-    return conv_valid(temporal_pad(x, w.shape[2], mode), w, bias, nthreads)
+                  nthreads: int | None = None, stride_s: int = 1, stride_t: int = 1,
+                  aligned: bool = False) -> np.ndarray:
+    """One-shot causal conv over the whole sequence: conv_valid(temporal_pad(x)),
+    or with strides the outputs whose current frame is s_t*j + phase (see
+    temporal_phase) at every s-th pixel."""
+    if stride_s == 1 and stride_t == 1:
+        return conv_valid(temporal_pad(x, w.shape[2], mode), w, bias, nthreads)
+    return conv_strided(temporal_pad(x, w.shape[2], mode), w, bias, temporal_phase(stride_t, aligned),
+                        stride_t, stride_s, nthreads)
+
+
+def temporal_phase(stride_t: int, aligned: bool = False) -> int:
+    """Input frame of a strided conv's first output: 0 (the first frame on its
+    own), or s_t - 1 with ``aligned`` (the first s_t frames together)."""
+    return stride_t - 1 if aligned else 0
+
+
+def strided_frames(n: int, stride_t: int, aligned: bool = False, seen: int = 0) -> int:
+    """Outputs of a strided conv for input frames seen .. seen+n-1: the frames
+    tau of that range with tau = phase (mod s_t)."""
+    ph = temporal_phase(stride_t, aligned)
+    first = seen + (ph - seen) % stride_t
+    return 0 if first > seen + n - 1 else (seen + n - 1 - first) // stride_t + 1
 
 
 # ------------------------------------------------------- composed pieces --
@@ -229,17 +289,24 @@ class CausalConvStream:
     rule (zeros or copies of the chunk's first frame).  The cache is held at the
     input's own resolution; when ``up_s``/``up_t`` are set the chunk is first
     upsampled (nearest, spatial; temporal growth on non-first frames, or on
-    every frame with ``aligned``).
+    every frame with ``aligned``).  With ``stride_s``/``stride_t`` the chunk's
+    outputs are those of the strided one-shot conv whose current frame lies in
+    the chunk: any chunking gives the same frames.
     """
 
     def __init__(self, w, bias=None, mode: str = REPLICATE, up_s: int = 1, up_t: int = 1,
-                 nthreads: int | None = None, aligned: bool = False):
+                 nthreads: int | None = None, aligned: bool = False, stride_s: int = 1,
+                 stride_t: int = 1):
         self.w = np.asarray(w, dtype=np.float64)
         self.bias = None if bias is None else np.asarray(bias, dtype=np.float64)
         self.mode = mode
         self.up_s = up_s
         self.up_t = up_t
         self.aligned = aligned
+        if (up_s > 1 and stride_s > 1) or (up_t > 1 and stride_t > 1):
+            raise ValueError("a conv either upsamples or strides along an axis, not both")
+        self.stride_s = stride_s
+        self.stride_t = stride_t
         self.kt = self.w.shape[2]
         self.nthreads = nthreads
         self.reset()
@@ -267,25 +334,40 @@ class CausalConvStream:
         return z
 
     def step(self, x: np.ndarray) -> np.ndarray:
+        if x.shape[1] == 0:
+            # a chunk with no frames (a strided layer before it produced none):
+            # no output, and the cache and frame count stay as they are
+            c, _, h, w = x.shape
+            if self.up_s > 1:
+                h, w = h * self.up_s, w * self.up_s
+            h, w = (h - 1) // self.stride_s + 1, (w - 1) // self.stride_s + 1
+            return np.zeros((self.w.shape[0], 0, h, w), dtype=np.float64)
+        seen = self.frames_seen
         z = self.window(x)
         zs = upsample_spatial(z, self.up_s) if self.up_s > 1 else z
-        return conv_valid(zs, self.w, self.bias, self.nthreads)
+        if self.stride_s == 1 and self.stride_t == 1:
+            return conv_valid(zs, self.w, self.bias, self.nthreads)
+        # the chunk's first output: input frame tau = phase (mod s_t), tau >= seen,
+        # whose window starts at Z index tau - seen
+        t0 = (temporal_phase(self.stride_t, self.aligned) - seen) % self.stride_t
+        return conv_strided(zs, self.w, self.bias, t0, self.stride_t, self.stride_s, self.nthreads)
 
 
-def one_shot(x, w, bias=None, mode=REPLICATE, up_s=1, up_t=1, nthreads=None, aligned=False):
-    """Upsample the whole video, then the one-shot causal conv."""
+def one_shot(x, w, bias=None, mode=REPLICATE, up_s=1, up_t=1, nthreads=None, aligned=False,
+             stride_s=1, stride_t=1):
+    """Upsample the whole video, then the one-shot causal conv (with strides)."""
     v = np.asarray(x, dtype=np.float64)
     if up_t == 2:
         v = upsample_temporal(v, first=True, aligned=aligned)
     if up_s > 1:
         v = upsample_spatial(v, up_s)
-    return causal_conv3d(v, w, bias, mode, nthreads)
+    return causal_conv3d(v, w, bias, mode, nthreads, stride_s, stride_t, aligned)
 
 
 def chunked(x, w, bias=None, mode=REPLICATE, up_s=1, up_t=1, splits=None, nthreads=None,
-            aligned=False):
+            aligned=False, stride_s=1, stride_t=1):
     """Run the stream over chunk lengths ``splits`` and concatenate the outputs."""
-    s = CausalConvStream(w, bias, mode, up_s, up_t, nthreads, aligned)
+    s = CausalConvStream(w, bias, mode, up_s, up_t, nthreads, aligned, stride_s, stride_t)
     out, t0 = [], 0
     for n in splits:
         out.append(s.step(x[:, t0:t0 + n]))

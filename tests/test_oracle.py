@@ -271,6 +271,163 @@ def test_conv_points_matches_full():
     assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
 
 
+# ---------------------------------------------------------- strided conv --
+# The encoder side's strided causal conv: every s-th pixel, every s_t-th frame
+# from the phase (0: the first frame on its own; s_t - 1 with ``aligned``).
+
+STRIDES = [(1, 2), (2, 1), (2, 2)]  # (spatial, temporal)
+
+
+@pytest.mark.parametrize("k", [(1, 1, 1), (2, 3, 3), (3, 1, 1), (3, 3, 3)])
+@pytest.mark.parametrize("stride", STRIDES)
+@pytest.mark.parametrize("mode", [O.REPLICATE, O.ZERO])
+@pytest.mark.parametrize("aligned", [False, True])
+def test_strided_conv_matches_brute_force(k, stride, mode, aligned):
+    r = _rng(hash((k, stride, mode, aligned)) % 2**32)
+    cin, cout, t, h, w = 2, 3, 7, 5, 6  # odd and even frame sizes
+    x = r.standard_normal((cin, t, h, w))
+    wt = r.standard_normal((cout, cin) + k)
+    b = r.standard_normal(cout)
+    ss, st = stride
+    ref = brute.strided_causal_conv3d_brute(x, wt, b, mode, ss, st, st - 1 if aligned else 0)
+    got = O.causal_conv3d(x, wt, b, mode, stride_s=ss, stride_t=st, aligned=aligned)
+    assert got.shape == ref.shape
+    assert got.shape[2:] == ((h + ss - 1) // ss, (w + ss - 1) // ss)
+    assert np.max(np.abs(got - ref)) <= 1e-13 * max(1.0, np.max(np.abs(ref)))
+
+
+@pytest.mark.parametrize("stride", STRIDES)
+@pytest.mark.parametrize("aligned", [False, True])
+def test_strided_conv_matches_torch_conv3d(stride, aligned):
+    """Library routine: torch CPU float64 conv3d with stride (s_t, s, s) and
+    spatial padding 1 on the history-padded input, started at the phase."""
+    r = _rng(31)
+    cin, cout, t, h, w = 4, 5, 9, 10, 7
+    x = r.standard_normal((cin, t, h, w))
+    wt = r.standard_normal((cout, cin, 3, 3, 3))
+    b = r.standard_normal(cout)
+    ss, st = stride
+    xt = torch.from_numpy(x)
+    xp = torch.cat([xt[:, :1], xt[:, :1], xt], dim=1)[:, (st - 1 if aligned else 0):]
+    ref = F.conv3d(xp[None], torch.from_numpy(wt), torch.from_numpy(b), stride=(st, ss, ss),
+                   padding=(0, 1, 1))[0].numpy()
+    got = O.causal_conv3d(x, wt, b, O.REPLICATE, stride_s=ss, stride_t=st, aligned=aligned)
+    assert got.shape == ref.shape
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("stride", STRIDES)
+@pytest.mark.parametrize("aligned", [False, True])
+def test_strided_conv_is_the_subsampled_conv(stride, aligned):
+    """Striding takes the stride-1 outputs at frames phase + s_t j and pixels
+    (s y, s x), bit for bit (the same sum in the same order)."""
+    r = _rng(32)
+    x = r.standard_normal((3, 8, 7, 6))
+    wt = r.standard_normal((2, 3, 3, 3, 3))
+    ss, st = stride
+    full = O.causal_conv3d(x, wt, None, O.ZERO)
+    got = O.causal_conv3d(x, wt, None, O.ZERO, stride_s=ss, stride_t=st, aligned=aligned)
+    assert np.array_equal(got, full[:, (st - 1 if aligned else 0)::st, ::ss, ::ss])
+
+
+def test_strided_delta_picks_frames_and_pixels():
+    """A delta at the current frame and the centre pixel: Y[j,y,x] = X[phase +
+    s_t j, 2y, 2x]; at the oldest tap, the frame two before (history for j = 0)."""
+    x = _rng(33).standard_normal((2, 9, 6, 5))
+    for aligned in (False, True):
+        ph = 1 if aligned else 0
+        y = O.causal_conv3d(x, _delta(2, 3, 3, 3, 2, 1, 1), None, O.ZERO, stride_s=2, stride_t=2,
+                            aligned=aligned)
+        assert np.array_equal(y, x[:, ph::2, ::2, ::2])
+        y = O.causal_conv3d(x, _delta(2, 3, 3, 3, 0, 1, 1), None, O.ZERO, stride_s=2, stride_t=2,
+                            aligned=aligned)
+        cur = np.arange(ph, 9, 2)
+        for j, tau in enumerate(cur):
+            ref = x[:, tau - 2, ::2, ::2] if tau >= 2 else np.zeros_like(x[:, 0, ::2, ::2])
+            assert np.array_equal(y[:, j], ref)
+
+
+STRIDED_SPLITS = [[11], [1] * 11, [1, 4, 4, 2], [3, 2, 6], [2, 2, 2, 5], [5, 6]]
+
+
+@pytest.mark.parametrize("splits", STRIDED_SPLITS)
+@pytest.mark.parametrize("mode", [O.REPLICATE, O.ZERO])
+@pytest.mark.parametrize("aligned", [False, True])
+def test_strided_chunked_equals_one_shot(splits, mode, aligned):
+    """Any chunking, even chunks that hold no output frame, gives the one-shot
+    frames: the cache is the window's last k_t-1 input frames whatever the
+    stride, and each chunk takes the outputs whose current frame it holds."""
+    r = _rng(34)
+    x = r.standard_normal((3, 11, 5, 6))
+    w = r.standard_normal((2, 3, 3, 3, 3))
+    b = r.standard_normal(2)
+    ref = O.one_shot(x, w, b, mode, stride_s=2, stride_t=2, aligned=aligned)
+    s = O.CausalConvStream(w, b, mode, stride_s=2, stride_t=2, aligned=aligned)
+    outs, t0 = [], 0
+    for n in splits:
+        y = s.step(x[:, t0:t0 + n])
+        assert y.shape[1] == O.strided_frames(n, 2, aligned, seen=t0)
+        outs.append(y)
+        t0 += n
+    got = np.concatenate(outs, axis=1)
+    assert got.shape == ref.shape
+    assert np.array_equal(got, ref)
+
+
+def test_strided_frame_counts():
+    """1 + 4n frames -> 1 + 2n -> 1 + n with the first frame on its own (361 ->
+    181 -> 91, the pages' 91 latents of a 361-frame video); with ``aligned``
+    4n -> 2n -> n (28 + 14 x 24 = 364 frames, 91 latents; 7 from the first
+    28-frame chunk, 6 from each 24-frame chunk)."""
+    n = 361
+    for _ in range(2):
+        n = O.strided_frames(n, 2)
+    assert n == 91
+    first, seen1, seen2 = [25] + [24] * 14, 0, 0
+    lat = []
+    for c in first:
+        m = O.strided_frames(c, 2, seen=seen1)
+        lat.append(O.strided_frames(m, 2, seen=seen2))
+        seen1, seen2 = seen1 + c, seen2 + m
+    assert lat == [7] + [6] * 14
+    seen1, seen2, lat = 0, 0, []
+    for c in [28] + [24] * 14:
+        m = O.strided_frames(c, 2, True, seen=seen1)
+        lat.append(O.strided_frames(m, 2, True, seen=seen2))
+        seen1, seen2 = seen1 + c, seen2 + m
+    assert lat == [7] + [6] * 14 and sum(lat) == 91
+
+
+@pytest.mark.parametrize("aligned", [False, True])
+def test_strided_causality(aligned):
+    r = _rng(35)
+    x = r.standard_normal((2, 9, 4, 4))
+    w = r.standard_normal((2, 2, 3, 3, 3))
+    base = O.one_shot(x, w, None, O.REPLICATE, stride_s=2, stride_t=2, aligned=aligned)
+    cur = np.arange(1 if aligned else 0, 9, 2)  # current frame of each output
+    for tp in range(1, 9):
+        x2 = x.copy()
+        x2[:, tp] += 1.0
+        y2 = O.one_shot(x2, w, None, O.REPLICATE, stride_s=2, stride_t=2, aligned=aligned)
+        before = cur < tp
+        assert np.array_equal(base[:, before], y2[:, before])
+        if (~before).any():  # the first output whose current frame is tp or later sees it
+            assert not np.array_equal(base[:, ~before][:, :1], y2[:, ~before][:, :1])
+
+
+def test_conv_points_with_spatial_stride():
+    r = _rng(36)
+    x = r.standard_normal((3, 4, 7, 6)).astype(np.float32)
+    w = r.standard_normal((2, 3, 3, 3, 3))
+    b = r.standard_normal(2)
+    xp = O.temporal_pad(x.astype(np.float64), 3, O.ZERO)
+    full = O.conv_strided(xp, w, b, 0, 1, 2)
+    pts = np.array([[t, y, xx] for t in range(4) for y in (0, 1, 3) for xx in (0, 2)])
+    got = O.conv_points(xp.astype(np.float32), w, b, pts, down=2)
+    ref = np.stack([full[:, t, y, xx] for t, y, xx in pts])
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
 # ----------------------------------------------------------------- blocks --
 
 def _params(r, cout, cin, gain=True, bias=False):
@@ -629,3 +786,91 @@ def test_decoder_against_torch_primitives(case):
     assert got.shape == ref.shape == (3, M.output_frames(sum(chunks), [f for _, f in stages], aligned=aligned),
                                       2 * up, 3 * up)
     assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+# ------------------------- the encoder's composition, rebuilt from primitives --
+
+def _encoder_params(r, stages, c_in, c_latent):
+    shapes = M.encoder_layer_shapes(c_in=c_in, stages=stages, c_latent=c_latent)
+    return {n: {"w": r.standard_normal((co, ci, kt, kh, kw)) / np.sqrt(ci * kt * kh * kw),
+                "b": r.uniform(-0.1, 0.1, co), "g": r.uniform(0.5, 1.5, ci) if g else None}
+            for n, co, ci, kt, kh, kw, g, _, _ in shapes}
+
+
+def _t_strided(v, p, mode, ss, st, aligned):
+    """One-shot strided causal conv with torch's conv3d: the history frames ahead
+    of the sequence, the first window starting at the phase (0, or st - 1 with
+    the aligned rule), stride (st, ss, ss), zero spatial padding (k-1)/2."""
+    w = torch.from_numpy(p["w"])
+    kt, kh, kw = w.shape[2:]
+    first = v[:, :1] if mode == O.REPLICATE else torch.zeros_like(v[:, :1])
+    v = torch.cat([first] * (kt - 1) + [v], dim=1)[:, (st - 1 if aligned else 0):]
+    b = None if p.get("b") is None else torch.from_numpy(p["b"])
+    return F.conv3d(v[None], w, b, stride=(st, ss, ss), padding=(0, (kh - 1) // 2, (kw - 1) // 2))[0]
+
+
+def _t_encoder(params, x, stages, aligned, mode):
+    """The encoder read backwards from the decoder, one-shot from torch
+    primitives: stride-2 conv from the pixels; per stage, the decoder's stages
+    from the last, two residual blocks then a conv with spatial stride 2 and
+    the stage's temporal factor as temporal stride; act -> conv to the latent."""
+    h = _t_strided(torch.from_numpy(x), params["conv_in"], mode, 2, 1, aligned)
+    for ei in range(len(stages)):
+        factor = stages[len(stages) - 1 - ei][1]
+        for r in range(2):
+            p1, p2 = params["e%d.rb%d.c1" % (ei, r)], params["e%d.rb%d.c2" % (ei, r)]
+            h = h + _t_causal(_t_act(_t_causal(_t_act(h, p1["g"]), p1, mode), p2["g"]), p2, mode)
+        h = _t_strided(h, params["e%d.down" % ei], mode, 2, factor, aligned)
+    return _t_causal(_t_act(h, params["conv_out"]["g"]), params["conv_out"], mode).numpy()
+
+
+ENCODER_PIN_CASES = [
+    # stages (as the decoder lists them), aligned, history, chunks
+    (((6, 2), (5, 2), (4, 1)), False, O.ZERO, (5, 4)),
+    (((6, 2), (5, 2), (4, 1)), True, O.ZERO, (4, 8)),
+    (((6, 2), (5, 2), (4, 1)), False, O.REPLICATE, (1, 2, 3, 3)),
+    (((5, 1), (4, 2)), True, O.REPLICATE, (2, 3, 1)),
+]
+
+
+@pytest.mark.parametrize("case", ENCODER_PIN_CASES, ids=lambda c: "%dst_al%d_%s" % (len(c[0]), c[1], c[2]))
+def test_encoder_against_torch_primitives(case):
+    """oracle/model.py's Encoder, chunk by chunk with per-layer caches (chunks that
+    do not split evenly into the strides included), equals the same encoder
+    composed one-shot from torch primitives to 1e-12."""
+    stages, aligned, mode, chunks = case
+    r = _rng(60 + ENCODER_PIN_CASES.index(case))
+    c_in, c_lat = 3, 4
+    params = _encoder_params(r, stages, c_in, c_lat)
+    down = 2 ** (len(stages) + 1)
+    x = r.standard_normal((c_in, sum(chunks), 2 * down, 3 * down))
+    ref = _t_encoder(params, x, stages, aligned, mode)
+    enc = M.Encoder(params, stages=stages, aligned=aligned, mode=mode)
+    got, t0 = [], 0
+    for n in chunks:
+        got.append(enc.step(x[:, t0:t0 + n]))
+        t0 += n
+    got = np.concatenate(got, axis=1)
+    n = sum(chunks)
+    for _, f in reversed(stages):
+        n = O.strided_frames(n, f, aligned)
+    assert got.shape == ref.shape == (c_lat, n, 2, 3)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_encoder_causality():
+    """Perturbing input frame t' leaves every latent whose last input frame is
+    before t' bit for bit unchanged (latent j of the first-frame rule ends at
+    frame 4j with two 2x strides)."""
+    stages = ((5, 2), (4, 2), (3, 1))
+    r = _rng(70)
+    params = _encoder_params(r, stages, 3, 2)
+    x = r.standard_normal((3, 9, 16, 16))
+    base = M.Encoder(params, stages=stages).step(x)
+    for tp in (1, 4, 5, 8):
+        x2 = x.copy()
+        x2[:, tp] += 1.0
+        y2 = M.Encoder(params, stages=stages).step(x2)
+        keep = (tp + 3) // 4  # latents 0 .. keep-1 end before frame tp
+        assert np.array_equal(base[:, :keep], y2[:, :keep])
+        assert not np.array_equal(base[:, keep], y2[:, keep])
