@@ -35,7 +35,8 @@ class ConvDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "cin", "cout", "kt", "kh", "kw", "h_in", "w_in", "up_s", "up_t", "max_chunk_t",
         "dtype", "tpad", "epilogue")] + [("eps", ctypes.c_float), ("grow", ctypes.c_int),
-                                         ("fold_upsample", ctypes.c_int)]
+                                         ("fold_upsample", ctypes.c_int), ("stride_s", ctypes.c_int),
+                                         ("stride_t", ctypes.c_int)]
 
 
 class State(ctypes.Structure):
@@ -45,7 +46,8 @@ class State(ctypes.Structure):
 class OpDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "kind", "cout", "kt", "kh", "kw", "up_s", "up_t", "tpad", "src", "res", "out", "act_out")] + [
-        ("w", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("gamma", ctypes.c_void_p), ("out_u8", ctypes.c_int)]
+        ("w", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("gamma", ctypes.c_void_p), ("out_u8", ctypes.c_int),
+        ("stride_s", ctypes.c_int), ("stride_t", ctypes.c_int)]
 
 
 class StackDesc(ctypes.Structure):

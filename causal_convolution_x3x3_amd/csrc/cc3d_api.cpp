@@ -36,19 +36,36 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-// Frame count of a slot for one chunk: T = mul * t_chunk + (first ? add_first : add_rest).
+// Frame count of a slot for one chunk: T = (mul * t_chunk + (first ? add_first :
+// add_rest)) / div, a chunk length being valid only where that is a whole number
+// (strided convs halve the count).
 struct FrameCount {
-    int64_t mul = 0, add_first = 0, add_rest = 0;
+    int64_t mul = 0, add_first = 0, add_rest = 0, div = 1;
     bool operator==(const FrameCount& o) const {
-        return mul == o.mul && add_first == o.add_first && add_rest == o.add_rest;
+        return mul == o.mul && add_first == o.add_first && add_rest == o.add_rest && div == o.div;
     }
-    int64_t eval(int64_t t, bool first) const { return mul * t + (first ? add_first : add_rest); }
-    // nearest 2x in time on non-first frames (every frame with the aligned rule)
+    int64_t num(int64_t t, bool first) const { return mul * t + (first ? add_first : add_rest); }
+    bool whole(int64_t t, bool first) const { return num(t, first) % div == 0; }
+    int64_t eval(int64_t t, bool first) const { return num(t, first) / div; }
+    // an upper bound for chunks of up to t frames (buffer sizing)
+    int64_t bound(int64_t t) const {
+        return (std::max(num(t, true), num(t, false)) + div - 1) / div;
+    }
+    // nearest 2x in time on non-first frames (every frame with the aligned rule):
+    // 2T - 1 on the first chunk = (2 num - div) / div
     FrameCount grown(bool aligned) const {
-        FrameCount g;
+        FrameCount g = *this;
         g.mul = 2 * mul;
-        g.add_first = 2 * add_first - (aligned ? 0 : 1);
+        g.add_first = 2 * add_first - (aligned ? 0 : div);
         g.add_rest = 2 * add_rest;
+        return g;
+    }
+    // temporal stride 2: (T + 1) / 2 on the first chunk with the first frame on
+    // its own (phase 0), else T / 2
+    FrameCount halved(bool aligned) const {
+        FrameCount g = *this;
+        g.div = 2 * div;
+        if (!aligned) g.add_first = add_first + div;
         return g;
     }
 };
@@ -67,6 +84,7 @@ struct Slot {
 struct OpRt {
     int kind = 0;
     int cin = 0, cout = 0, kt = 1, kh = 1, kw = 1, up_s = 1, up_t = 1, tpad = 0;
+    int stride_s = 1, stride_t = 1;
     int src = -1, res = -1, out = -1, act_out = -1;
     int norm_src = -1;      // act computed by a separate norm pass reading this slot
     int h_in = 0, w_in = 0, h_out = 0, w_out = 0;
@@ -287,6 +305,16 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
                             o.kh, o.kw);
             if ((o.up_s != 1 && o.up_s != 2) || (o.up_t != 1 && o.up_t != 2))
                 return fail(CC3D_ESHAPE, "op %d: up_s=%d up_t=%d; accepted 1 or 2", i, o.up_s, o.up_t);
+            if (o.stride_s < 0 || o.stride_s > 2 || o.stride_t < 0 || o.stride_t > 2)
+                return fail(CC3D_ESHAPE, "op %d: stride_s=%d stride_t=%d; accepted 1 or 2 (0 reads as 1)", i,
+                            o.stride_s, o.stride_t);
+            r.stride_s = o.stride_s == 2 ? 2 : 1;
+            r.stride_t = o.stride_t == 2 ? 2 : 1;
+            if ((r.stride_s == 2 && o.up_s == 2) || (r.stride_t == 2 && o.up_t == 2))
+                return fail(CC3D_ESHAPE, "op %d: a conv either upsamples or strides along an axis (up_s=%d "
+                            "stride_s=%d, up_t=%d stride_t=%d)", i, o.up_s, r.stride_s, o.up_t, r.stride_t);
+            if ((r.stride_s == 2 || r.stride_t == 2) && o.out_u8)
+                return fail(CC3D_EINVAL, "op %d: 8-bit output is not taken by a strided conv", i);
             if (o.tpad != CC3D_TPAD_REPLICATE && o.tpad != CC3D_TPAD_ZERO)
                 return fail(CC3D_EINVAL, "op %d: tpad %d not accepted (0 = REPLICATE, 1 = ZERO)", i, o.tpad);
             if (o.cout < 1 || o.cout > 4096) return fail(CC3D_ESHAPE, "op %d: cout=%d not in [1, 4096]", i, o.cout);
@@ -311,9 +339,10 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
             r.up_s = o.up_s;
             r.up_t = o.up_t;
             r.tpad = o.tpad;
-            r.h_out = r.h_in * o.up_s;
-            r.w_out = r.w_in * o.up_s;
+            r.h_out = r.stride_s == 2 ? (r.h_in + 1) / 2 : r.h_in * o.up_s;
+            r.w_out = r.stride_s == 2 ? (r.w_in + 1) / 2 : r.w_in * o.up_s;
             if (o.up_t == 2) tc_out = src.tc.grown(p->grow_aligned);
+            if (r.stride_t == 2) tc_out = src.tc.halved(p->grow_aligned);
             r.cache_off = cache_off;
             r.cache_bytes = (size_t)(o.kt - 1) * r.h_in * r.w_in * r.cin * p->elem;
             cache_off += align_up(r.cache_bytes);
@@ -323,6 +352,7 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
                 const int plain = o.act_out == CC3D_SLOT_NONE && !o.out_u8;
                 r.family = cc3d::bf16_conv_family(o.cout, r.cin, o.kt, o.kh, o.kw, o.up_s, plain,
                                                   d->fold_upsample && !o.out_u8);
+                if (r.stride_s == 2 || r.stride_t == 2) r.family = 1;  // the generic kernel takes strides
                 if (r.family == 4) cc3d::pw_conv_tiling(o.cout, &r.ntile, &r.nblocks);
             }
         } else {
@@ -410,6 +440,8 @@ cc3d_status build_group(const cc3d_stack_desc* d, cc3d_plan* p)
     bool have = false;
     for (int i = d->batch_from; i < n; ++i) {
         const OpRt& r = p->ops[i];
+        if (r.stride_s != 1 || r.stride_t != 1)
+            return fail(CC3D_EINVAL, "op %d: a strided conv is not taken inside the frame-batched group", i);
         for (int sl : {r.src, r.res}) {
             if (sl == CC3D_SLOT_NONE) continue;
             if (sl == CC3D_SLOT_AUX)
@@ -543,8 +575,7 @@ cc3d_status materialise(const cc3d_stack_desc* d, cc3d_plan* p, hipStream_t stre
     for (int s = CC3D_SLOT_AUX + 1; s < CC3D_MAX_SLOTS; ++s) {
         Slot& sl = p->slots[s];
         if (!sl.defined) continue;
-        const int64_t tmax = sl.grouped ? std::max(sl.rel.eval(p->frame_batch, true), sl.rel.eval(p->frame_batch, false))
-                                        : std::max(sl.tc.eval(p->max_t, true), sl.tc.eval(p->max_t, false));
+        const int64_t tmax = sl.grouped ? sl.rel.bound(p->frame_batch) : sl.tc.bound(p->max_t);
         sl.bytes = (size_t)tmax * sl.h * sl.w * sl.c * p->elem;
         cc3d_status st = al.alloc(&sl.ptr, sl.bytes, "an intermediate slot");
         if (st != CC3D_OK) return st;
@@ -662,6 +693,22 @@ cc3d_status create_common(const cc3d_stack_desc* d, void* stream, cc3d_plan** ou
 
 bool plan_ok(const cc3d_plan* p) { return p && p->magic == kPlanMagic; }
 
+// A chunk of t_chunk frames must leave every slot a whole frame count (strided
+// convs halve it: see FrameCount).
+cc3d_status check_frames(const cc3d_plan* p, int t_chunk, bool first)
+{
+    for (int s = 0; s < CC3D_MAX_SLOTS; ++s) {
+        const Slot& sl = p->slots[s];
+        if (!sl.defined || sl.tc.whole(t_chunk, first)) continue;
+        return fail(CC3D_ESHAPE,
+                    "t_chunk=%d (%s chunk) leaves op %d's output a fractional frame count: a temporal stride of 2 "
+                    "needs an %s number of frames there",
+                    t_chunk, first ? "first" : "later", sl.writer,
+                    (first && !p->grow_aligned) ? "odd" : "even");
+    }
+    return CC3D_OK;
+}
+
 cc3d_status check_ptr(const void* ptr, int device, const char* what)
 {
     hipPointerAttribute_t at;
@@ -728,6 +775,8 @@ std::string conv_kernel_name(const cc3d_plan* p, const OpRt& r)
         snprintf(buf, sizeof buf, "conv_bf16_phase_up%d_k%d_n%d", r.up_s, r.kh, r.ntile);
     else if (p->dtype == CC3D_BF16 && r.family == 4)
         snprintf(buf, sizeof buf, "conv_bf16_pw_up%d_kt%d_n%d", r.up_s, r.kt, r.ntile);
+    else if (p->dtype == CC3D_BF16 && (r.stride_s > 1 || r.stride_t > 1))
+        snprintf(buf, sizeof buf, "conv_bf16_s%dt%d_k%d_n%d", r.stride_s, r.stride_t, r.kh, r.ntile);
     else if (p->dtype == CC3D_BF16)
         snprintf(buf, sizeof buf, "conv_bf16%s_up%d_k%d_n%d", r.family == 2 ? "_v2" : "", r.up_s, r.kh,
                  r.ntile);
@@ -764,6 +813,8 @@ cc3d_status conv_stack_desc(const cc3d_conv_desc* d, const void* w, const float*
     op->bias = bias;
     op->gamma = gamma;
     op->out_u8 = (d->epilogue & CC3D_EPI_U8) ? 1 : 0;
+    op->stride_s = d->stride_s;
+    op->stride_t = d->stride_t;
     memset(sd, 0, sizeof *sd);
     sd->dtype = d->dtype;
     sd->cin = d->cin;
@@ -851,6 +902,8 @@ cc3d_status cc3d_output_shape(const cc3d_plan* p, int t_chunk, int first, int* c
     if (!plan_ok(p)) return fail(CC3D_EINVAL, "plan is NULL or destroyed");
     if (t_chunk < 1 || t_chunk > p->max_t)
         return fail(CC3D_ESHAPE, "t_chunk=%d not in [1, %d]", t_chunk, p->max_t);
+    cc3d_status st = check_frames(p, t_chunk, first != 0);
+    if (st != CC3D_OK) return st;
     const Slot& y = p->slots[CC3D_SLOT_Y];
     if (c) *c = y.c;
     if (t) *t = (int)y.tc.eval(t_chunk, first != 0);
@@ -926,6 +979,8 @@ cc3d_status cc3d_slot_shape(const cc3d_plan* p, int slot, int t_chunk, int first
     const Slot& s = p->slots[slot];
     if (s.grouped)
         return fail(CC3D_EINVAL, "slot %d belongs to the frame-batched group and holds only the last batch", slot);
+    cc3d_status st = check_frames(p, t_chunk, first != 0);
+    if (st != CC3D_OK) return st;
     if (c) *c = s.c;
     if (t) *t = (int)s.tc.eval(t_chunk, first != 0);
     if (h) *h = s.h;
@@ -1054,6 +1109,8 @@ cc3d_status forward_impl(const cc3d_plan* p, const void* x, int t_chunk, const c
          (uintptr_t)cache_out->arena) & 15u)
         return fail(CC3D_EINVAL, "x, y, residual and the state arenas must be 16-byte aligned");
     const bool first = cache_in->frames_seen == 0;
+    cc3d_status fst = check_frames(p, t_chunk, first);
+    if (fst != CC3D_OK) return fst;
     const Slot& ys = p->slots[CC3D_SLOT_Y];
     const size_t y_bytes = (size_t)ys.tc.eval(t_chunk, first) * ys.h * ys.w * ys.c * p->y_elem;
     const size_t x_bytes = (size_t)t_chunk * p->h * p->w * p->cin * p->elem;
@@ -1131,7 +1188,20 @@ cc3d_status forward_impl(const cc3d_plan* p, const void* x, int t_chunk, const c
             a.z.first = first ? 1 : 0;
             a.z.zero_hist = r.tpad == CC3D_TPAD_ZERO ? 1 : 0;
             a.z.t_shift = (first && !p->grow_aligned) ? 1 : 0;
-            const int t_v = (r.up_t == 2) ? 2 * t_in - a.z.t_shift : t_in;
+            // frames of the window's input V, and of the output
+            const int t_zv = (r.up_t == 2) ? 2 * t_in - a.z.t_shift : t_in;
+            int t_v = t_zv;
+            a.down_s = r.stride_s;
+            a.t_stride = r.stride_t;
+            a.t_first = 0;
+            if (r.stride_t == 2) {
+                // outputs at input frames tau = phase (mod 2): the chunk's first one
+                // is its first frame only on the first chunk with phase 0 (whole
+                // counts: later chunks start at an odd frame for phase 0, an even
+                // one for phase 1)
+                a.t_first = (first && !p->grow_aligned) ? 0 : 1;
+                t_v = (t_zv - a.t_first + 1) / 2;
+            }
             *frames_out = t_v;
             a.wpk = r.wpk;
             a.bias = r.bias;
@@ -1209,7 +1279,7 @@ cc3d_status forward_impl(const cc3d_plan* p, const void* x, int t_chunk, const c
             if (r.kt > 1 && !cache_written[oi]) {
                 {
                     ProfScope prof(p, oi, 2, s, 0.0, 2.0 * (r.kt - 1) * fr_in);
-                    e = cc3d::launch_cache_update(a.z, t_v, ps.cache_wr + r.cache_off, p->elem, s);
+                    e = cc3d::launch_cache_update(a.z, t_zv, ps.cache_wr + r.cache_off, p->elem, s);
                 }
                 if ((st = hip_status(e, "cache update launch")) != CC3D_OK) return st;
             }

@@ -47,6 +47,12 @@ struct ConvArgs {
     void* cache;
     int cache_t0;
     int cache_act;
+    // Strided convs (bf16 family 1 and fp32): output pixel (y, x) is centred on
+    // input pixel (down_s*y, down_s*x); output frame t reads window frames
+    // t_stride*t + t_first + (0 .. kt-1) of Z.  1, 1, 0 for every other conv.
+    int down_s;
+    int t_stride;
+    int t_first;
 };
 
 // 8-bit output code of an fp32 result v: rint(clamp((v + 1) * 127.5, 0, 255)).

@@ -17,6 +17,14 @@
 // image is exactly "source pixel outside the image".  The temporal growth and the
 // causal history are resolved per frame by the ZWindow map.
 //
+// Strided convs (DOWN = 2, the encoder side): the tile is TS_H x TS_W *output*
+// pixels, which read input rows 2y-1 .. 2y+1 and columns 2x-1 .. 2x+1; the LDS
+// tile keeps the even input columns first and the odd ones after them, so the
+// 16 output columns of a fragment read 16 consecutive LDS pixels at every column
+// tap (columns 2x + d: even half at x + d/2 for d = 0, 2, odd half at x for
+// d = 1), as the unstrided reads do.  A temporal stride maps output frame t to
+// window frames t_stride*t + t_first + (0 .. kt-1).
+//
 // Epilogue (fp32): + bias, + residual, round to bf16 and store (or store the
 // 8-bit code of the fp32 result, see rgb8_code); optionally the
 // channel RMSNorm + SiLU of the stored value, reduced across the 16 lanes that
@@ -32,12 +40,15 @@
 namespace cc3d {
 namespace {
 
-template <int UP, int KS, int NF, int TS_H, int SW>
+template <int UP, int DOWN, int KS, int NF, int TS_H, int SW>
 __global__ __launch_bounds__(256) void conv_bf16_kernel(ConvArgs a)
 {
+    static_assert(UP == 1 || DOWN == 1, "a conv either upsamples or strides");
     constexpr int HALO = (KS - 1) / 2;
     constexpr int TS_W = 16 * SW;
-    constexpr int LH = TS_H + 2 * HALO, LW = TS_W + 2 * HALO;
+    // LDS tile: the input rows and columns the tile's outputs read
+    constexpr int LH = DOWN * (TS_H - 1) + 2 * HALO + 1, LW = DOWN * (TS_W - 1) + 2 * HALO + 1;
+    constexpr int NE = (LW + 1) / 2;  // DOWN = 2: even input columns, stored first
     constexpr int NPH = UP * UP;
     constexpr int NTILE = 16 * NF;
     constexpr int TAPS = KS * KS;
@@ -52,7 +63,8 @@ __global__ __launch_bounds__(256) void conv_bf16_kernel(ConvArgs a)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, k16 = lane & 15;
-    const int tiles_w = (a.w_in + TS_W - 1) / TS_W;
+    // tiles cover the source frame (UP = 2) or the output frame (strided or not)
+    const int tiles_w = ((UP == 2 ? a.w_in : a.w_out) + TS_W - 1) / TS_W;
     const int i0 = (blockIdx.x / tiles_w) * TS_H;
     const int j0 = (blockIdx.x % tiles_w) * TS_W;
     const int nb = blockIdx.y;
@@ -69,12 +81,13 @@ __global__ __launch_bounds__(256) void conv_bf16_kernel(ConvArgs a)
 
     for (int step = 0; step < nsteps; ++step) {
         const int ta = step / a.kchunks, kc = step - ta * a.kchunks;
-        const uint16_t* fp = zframe(a.z, t + ta);
+        const uint16_t* fp = zframe(a.z, a.t_stride * t + a.t_first + ta);
         __syncthreads();  // every wave is done reading the previous step
         for (int idx = tid; idx < A_CHUNKS; idx += 256) {
             const int pix = idx >> 2, gg = idx & 3;
-            const int r = pix / LW, c = pix - r * LW;
-            const int gy = i0 + r - HALO, gx = j0 + c - HALO;
+            const int r = pix / LW, lc = pix - r * LW;
+            const int c = DOWN == 1 ? lc : (lc < NE ? 2 * lc : 2 * (lc - NE) + 1);  // input column in the tile
+            const int gy = DOWN * i0 + r - HALO, gx = DOWN * j0 + c - HALO;
             const int ch = kc * 32 + gg * 8;
             uint4 v = make_uint4(0u, 0u, 0u, 0u);
             if (fp && gy >= 0 && gy < a.h_in && gx >= 0 && gx < a.w_in && ch < a.cin)
@@ -101,9 +114,12 @@ __global__ __launch_bounds__(256) void conv_bf16_kernel(ConvArgs a)
                     const int s = (m / NPH) % SW;
                     const int r = wave * RPW + m / (NPH * SW);
                     int ly, lx;
-                    if (UP == 1) {
+                    if (UP == 1 && DOWN == 1) {
                         ly = r + tb;
                         lx = 16 * s + k16 + td;
+                    } else if (DOWN == 2) {
+                        ly = 2 * r + tb;
+                        lx = (td & 1) ? NE + 16 * s + k16 + (td >> 1) : 16 * s + k16 + (td >> 1);
                     } else {
                         const int oy = ((ph >> 1) + tb - HALO) >> 1;  // floor((p + dy) / 2)
                         const int ox = ((ph & 1) + td - HALO) >> 1;
@@ -180,26 +196,27 @@ __global__ __launch_bounds__(256) void conv_bf16_kernel(ConvArgs a)
     }
 }
 
-template <int UP, int KS, int NF>
+template <int UP, int DOWN, int KS, int NF>
 hipError_t launch_cfg(const ConvArgs& a, hipStream_t s)
 {
     constexpr int TS_H = (UP == 2) ? 4 : 16;
     constexpr int SW = 1;
-    const int tiles = ((a.h_in + TS_H - 1) / TS_H) * ((a.w_in + 16 * SW - 1) / (16 * SW));
+    const int th = UP == 2 ? a.h_in : a.h_out, tw = UP == 2 ? a.w_in : a.w_out;
+    const int tiles = ((th + TS_H - 1) / TS_H) * ((tw + 16 * SW - 1) / (16 * SW));
     dim3 grid(tiles, a.nblocks, a.t_out);
-    hipLaunchKernelGGL((conv_bf16_kernel<UP, KS, NF, TS_H, SW>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((conv_bf16_kernel<UP, DOWN, KS, NF, TS_H, SW>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
-template <int UP, int KS>
+template <int UP, int DOWN, int KS>
 hipError_t launch_nf(const ConvArgs& a, hipStream_t s)
 {
     switch (a.ntile) {
-    case 16: return launch_cfg<UP, KS, 1>(a, s);
-    case 32: return launch_cfg<UP, KS, 2>(a, s);
-    case 64: return launch_cfg<UP, KS, 4>(a, s);
-    case 96: return launch_cfg<UP, KS, 6>(a, s);
-    case 128: return launch_cfg<UP, KS, 8>(a, s);
+    case 16: return launch_cfg<UP, DOWN, KS, 1>(a, s);
+    case 32: return launch_cfg<UP, DOWN, KS, 2>(a, s);
+    case 64: return launch_cfg<UP, DOWN, KS, 4>(a, s);
+    case 96: return launch_cfg<UP, DOWN, KS, 6>(a, s);
+    case 128: return launch_cfg<UP, DOWN, KS, 8>(a, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -311,10 +328,13 @@ hipError_t launch_conv_bf16(const ConvArgs& a, hipStream_t s)
     if (a.family == 4) return launch_conv_pw(a, s);
     if (a.family == 5) return launch_conv_phase(a, s);
     if (a.family == 2) return launch_conv_bf16_v2(a, s);
-    if (a.up_s == 1 && a.kh == 3) return launch_nf<1, 3>(a, s);
-    if (a.up_s == 2 && a.kh == 3) return launch_nf<2, 3>(a, s);
-    if (a.up_s == 1 && a.kh == 1) return launch_nf<1, 1>(a, s);
-    if (a.up_s == 2 && a.kh == 1) return launch_nf<2, 1>(a, s);
+    if (a.t_stride < 1 || a.t_stride > 2 || (a.down_s != 1 && a.down_s != 2) || (a.down_s == 2 && a.up_s != 1))
+        return hipErrorInvalidValue;
+    if (a.down_s == 2) return a.kh == 3 ? launch_nf<1, 2, 3>(a, s) : launch_nf<1, 2, 1>(a, s);
+    if (a.up_s == 1 && a.kh == 3) return launch_nf<1, 1, 3>(a, s);
+    if (a.up_s == 2 && a.kh == 3) return launch_nf<2, 1, 3>(a, s);
+    if (a.up_s == 1 && a.kh == 1) return launch_nf<1, 1, 1>(a, s);
+    if (a.up_s == 2 && a.kh == 1) return launch_nf<2, 1, 1>(a, s);
     return hipErrorInvalidValue;
 }
 

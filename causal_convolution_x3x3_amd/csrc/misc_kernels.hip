@@ -8,11 +8,15 @@ namespace {
 
 // ------------------------------------------------------------ fp32 conv ----
 // One thread per output element (channel fastest, so neighbouring threads share
-// their input reads); fp32 accumulation over taps, then channels.
+// their input reads); fp32 accumulation over taps, then channels.  Upsampled
+// convs read source pixel floor(u / up_s) of upsampled pixel u; strided ones
+// centre output (y, x) on input pixel (down_s*y, down_s*x) and output frame t on
+// window frames t_stride*t + t_first + (0 .. kt-1).
 __global__ __launch_bounds__(256) void conv_f32_kernel(ConvArgs a)
 {
     const int64_t total = (int64_t)a.t_out * a.h_out * a.w_out * a.cout;
     const int ph = (a.kh - 1) / 2, pw = (a.kw - 1) / 2;
+    const int hu = a.h_in * a.up_s, wu = a.w_in * a.up_s;  // the conv's input size
     const int kvol = a.kt * a.kh * a.kw;
     const float* w = (const float*)a.wpk;
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
@@ -25,15 +29,15 @@ __global__ __launch_bounds__(256) void conv_f32_kernel(ConvArgs a)
         const int t = (int)(p / a.h_out);
         float s = 0.f;
         for (int ta = 0; ta < a.kt; ++ta) {
-            const float* fp = (const float*)zframe_bytes(a.z, t + ta, 4);
+            const float* fp = (const float*)zframe_bytes(a.z, a.t_stride * t + a.t_first + ta, 4);
             if (!fp) continue;
             for (int tb = 0; tb < a.kh; ++tb) {
-                const int yu = y + tb - ph;
-                if (yu < 0 || yu >= a.h_out) continue;
+                const int yu = a.down_s * y + tb - ph;
+                if (yu < 0 || yu >= hu) continue;
                 const int sy = yu / a.up_s;
                 for (int td = 0; td < a.kw; ++td) {
-                    const int xu = x + td - pw;
-                    if (xu < 0 || xu >= a.w_out) continue;
+                    const int xu = a.down_s * x + td - pw;
+                    if (xu < 0 || xu >= wu) continue;
                     const int sx = xu / a.up_s;
                     const float* px = fp + ((int64_t)sy * a.w_in + sx) * a.cin;
                     const float* wp = w + (int64_t)o * a.cin * kvol + (ta * a.kh + tb) * a.kw + td;

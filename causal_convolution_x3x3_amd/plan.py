@@ -76,6 +76,8 @@ class Op:
     bias: Optional[torch.Tensor] = None
     gamma: Optional[torch.Tensor] = None
     out_u8: bool = False  # CONV writing the output slot: y as 8-bit codes
+    stride_s: int = 1     # CONV: spatial stride (1 or 2; see cc3d_op_desc)
+    stride_t: int = 1     # CONV: temporal stride (1 or 2)
     name: str = field(default="")
 
     def __post_init__(self):
@@ -100,8 +102,11 @@ class Plan:
         self.state_bytes = int(L.cc3d_state_bytes(self._h))
         self.device_bytes = int(L.cc3d_plan_device_bytes(self._h))
         self.out_dtype = torch.uint8 if L.cc3d_output_elem_bytes(self._h) == 1 else _TD[dtype]
-        # whether forward_chunk reads a residual argument (the residual slot is defined)
-        self.takes_residual = L.cc3d_slot_shape(self._h, C.SLOT_AUX, 1, 1, None, None, None, None) == C.OK
+        # whether forward_chunk reads a residual argument (the residual slot is
+        # defined; ESHAPE: defined, but a one-frame first chunk is not a whole
+        # count for the plan's strided convs)
+        self.takes_residual = L.cc3d_slot_shape(self._h, C.SLOT_AUX, 1, 1, None, None, None, None) in (C.OK,
+                                                                                                     C.ESHAPE)
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -177,10 +182,12 @@ class Plan:
 
 def conv_plan(w: torch.Tensor, h_in: int, w_in: int, *, bias=None, gamma=None, up_s=1, up_t=1,
               max_chunk_t=8, tpad=C.TPAD_REPLICATE, residual=False, act=False, out_u8=False, eps=1e-6,
-              aligned=False, fold_upsample=False, stream=None) -> Plan:
+              aligned=False, fold_upsample=False, stride_s=1, stride_t=1, stream=None) -> Plan:
     """Plan for one causal conv; w is [Cout][Cin][kt][kh][kw] on the GPU (bf16 or fp32).
-    ``aligned``: the first chunk doubles every frame at up_t = 2 (CC3D_GROW_ALIGNED).
-    ``fold_upsample``: phase-folded kernel for an upsampling 3x3 conv where it applies."""
+    ``aligned``: the first chunk doubles every frame at up_t = 2 (CC3D_GROW_ALIGNED),
+    and a temporal stride takes every output from two new frames (phase 1).
+    ``fold_upsample``: phase-folded kernel for an upsampling 3x3 conv where it applies.
+    ``stride_s``, ``stride_t``: a strided conv (1 or 2 each)."""
     cout, cin, kt, kh, kw = w.shape
     if w.dtype not in _DT:
         raise ValueError("weights must be bfloat16 or float32, got %s" % w.dtype)
@@ -191,7 +198,7 @@ def conv_plan(w: torch.Tensor, h_in: int, w_in: int, *, bias=None, gamma=None, u
                    max_chunk_t=max_chunk_t, dtype=_DT[w.dtype], tpad=tpad,
                    epilogue=(C.EPI_RESIDUAL if residual else 0) | (C.EPI_ACT if act else 0) |
                    (C.EPI_U8 if out_u8 else 0), eps=eps, grow=C.GROW_ALIGNED if aligned else C.GROW_ONCE,
-                   fold_upsample=int(fold_upsample))
+                   fold_upsample=int(fold_upsample), stride_s=stride_s, stride_t=stride_t)
     h = ctypes.c_void_p()
     with torch.cuda.device(w.device):
         C.check(C.lib().cc3d_plan_create(ctypes.byref(d), _ptr(w), _ptr(bias), _ptr(gamma), _stream(stream),
@@ -286,7 +293,8 @@ def stack_plan(ops: List[Op], cin: int, h: int, w: int, *, dtype=torch.bfloat16,
         kt, kh, kw = o.k
         arr[i] = C.OpDesc(kind=o.kind, cout=o.cout, kt=kt, kh=kh, kw=kw, up_s=o.up_s, up_t=o.up_t,
                           tpad=o.tpad, src=o.src, res=o.res, out=o.out, act_out=o.act_out,
-                          w=_ptr(o.w), bias=_ptr(o.bias), gamma=_ptr(o.gamma), out_u8=int(o.out_u8))
+                          w=_ptr(o.w), bias=_ptr(o.bias), gamma=_ptr(o.gamma), out_u8=int(o.out_u8),
+                          stride_s=o.stride_s, stride_t=o.stride_t)
     d = C.StackDesc(dtype=_DT[dtype], cin=cin, h=h, w=w, max_chunk_t=max_chunk_t, eps=eps, n_ops=len(ops),
                     ops=arr, grow=C.GROW_ALIGNED if aligned else C.GROW_ONCE, batch_from=batch_from,
                     frame_batch=frame_batch, fold_upsample=int(fold_upsample))

@@ -145,3 +145,65 @@ def decoder_ops(params: Dict[str, Dict], stages=DECODER_STAGES, c_out: int = 3,
     ops.append(Op(cout=c_out, w=head["w"], bias=head.get("b"), up_s=2, src=last_act, out=Y, out_u8=out_u8,
                   name="head"))
     return ops
+
+
+def encoder_ops(params: Dict[str, Dict], stages=DECODER_STAGES, c_latent: int = 48,
+                unique_slots: bool = False) -> List[Op]:
+    """The encoder side (SwiftVR page, "ReAE: Causal Halo Exchange": the encoder
+    keeps the decoder's per-layer causal state; the page prints no encoder
+    layer): the decoder read backwards.  conv_in with spatial stride 2 from the
+    pixels -> per stage, the decoder's stages from the last, [two residual
+    blocks, then a conv with spatial stride 2 and the stage's temporal factor as
+    temporal stride, back to the channels the decoder stage started from] ->
+    act -> conv_out to the latent channels.  Params are keyed as
+    oracle/model.py's encoder_layer_shapes ("conv_in", "e<i>.rb<r>.c1|c2",
+    "e<i>.down", "conv_out"); conv_in's weights take the plan's input channels
+    (pixels padded with zero channels to a multiple of 8).
+
+    Slots per stage e (base = 3 + 5 e): raw A, raw B, act A, act B, inner act;
+    slot 3 + 5*len(stages) holds the act conv_out reads.  ``unique_slots`` as in
+    decoder_ops."""
+    nxt = [3]
+
+    def slot(fixed):
+        if not unique_slots:
+            return fixed
+        nxt[0] += 1
+        return nxt[0] - 1
+
+    n = len(stages)
+    widths = [stages[0][0]] + [c for c, _ in stages]  # the decoder's conv_in width, then each stage's
+    ops: List[Op] = []
+    raw_cur, act_cur = slot(3), slot(5)
+    ops.append(Op(cout=stages[-1][0], w=params["conv_in"]["w"], bias=params["conv_in"].get("b"), stride_s=2,
+                  src=X, out=raw_cur, act_out=act_cur, gamma=params["e0.rb0.c1"]["g"], name="conv_in"))
+    for ei in range(n):
+        si = n - 1 - ei  # the decoder stage this one mirrors
+        c, factor = stages[si]
+        base = 3 + 5 * ei
+        raw_fixed, act_fixed = [base, base + 1], [base + 2, base + 3]
+        cur = 0
+        for r in range(2):
+            p1, p2 = params["e%d.rb%d.c1" % (ei, r)], params["e%d.rb%d.c2" % (ei, r)]
+            inner = slot(base + 4)
+            ops.append(Op(cout=c, w=p1["w"], bias=p1.get("b"), src=act_cur, act_out=inner, gamma=p2["g"],
+                          name="e%d.rb%d.c1" % (ei, r)))
+            # block 0 hands act(y) to block 1; the down conv reads the raw stream
+            need_act = r == 0
+            new_raw = slot(raw_fixed[1 - cur])
+            new_act = slot(act_fixed[1 - cur]) if need_act else NONE
+            ops.append(Op(cout=c, w=p2["w"], bias=p2.get("b"), src=inner, res=raw_cur, out=new_raw,
+                          act_out=new_act, gamma=params["e%d.rb1.c1" % ei]["g"] if need_act else None,
+                          name="e%d.rb%d.c2" % (ei, r)))
+            raw_cur, act_cur, cur = new_raw, new_act, 1 - cur
+        down = params["e%d.down" % ei]
+        if ei == n - 1:  # only conv_out's act is read after the last stage
+            d_raw, d_act, g = NONE, slot(3 + 5 * n), params["conv_out"]["g"]
+        else:
+            d_raw, d_act, g = slot(base + 5), slot(base + 7), params["e%d.rb0.c1" % (ei + 1)]["g"]
+        ops.append(Op(cout=widths[si], w=down["w"], bias=down.get("b"), stride_s=2, stride_t=factor, src=raw_cur,
+                      out=d_raw, act_out=d_act, gamma=g, name="e%d.down" % ei))
+        raw_cur, act_cur = d_raw, d_act
+    out = params["conv_out"]
+    ops.append(Op(cout=c_latent, w=out["w"], bias=out.get("b"), src=act_cur, out=Y, name="conv_out"))
+    return ops

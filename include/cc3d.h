@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define CC3D_VERSION 104 /* 1.0.4: phase-folded upsample convs */
+#define CC3D_VERSION 105 /* 1.0.5: strided convs (the encoder side) */
 
 typedef enum {
     CC3D_OK = 0,
@@ -130,6 +130,8 @@ typedef struct {
     float eps;            /* RMSNorm epsilon (CC3D_EPI_ACT) */
     int grow;             /* cc3d_grow (first chunk at up_t = 2) */
     int fold_upsample;    /* 1: phase-folded upsample conv where it applies (see below) */
+    int stride_s, stride_t; /* strided conv (see "Strided convs" below): 1 or 2 each;
+                               0 reads as 1 */
 } cc3d_conv_desc;
 
 typedef struct cc3d_plan cc3d_plan;
@@ -185,6 +187,7 @@ typedef struct {
     const float* bias; /* CONV: device float32 [cout] or NULL */
     const float* gamma;/* device float32 [channels of v]; required when act_out is set */
     int out_u8;        /* CONV writing CC3D_SLOT_Y only: 1 = y as 8-bit codes (CC3D_EPI_U8) */
+    int stride_s, stride_t; /* CONV only: 1 or 2 each (0 reads as 1); see "Strided convs" */
 } cc3d_op_desc;
 
 typedef struct {
@@ -228,6 +231,24 @@ typedef struct {
  * residual argument or write a slot written before it; cc3d_slot_shape and
  * cc3d_slot_read reject the group's slots (CC3D_EINVAL). */
 
+/* Strided convs (stride_s, stride_t = 2; the encoder side: the SwiftVR page,
+ * "ReAE: Causal Halo Exchange", puts the ReAE encoder under the decoder's
+ * causal-state rule, and "From Pixels to Latents and Back" has it map the video
+ * to latents; the page prints no encoder layer).  stride_s = 2: output pixel
+ * (y, x) is the conv centred on input pixel (2y, 2x), zero padding (k-1)/2, so
+ * an H x W input gives ceil(H/2) x ceil(W/2) (PyTorch's stride convention).
+ * stride_t = 2: the outputs are those whose current frame is an input frame
+ * tau = phase (mod 2), counted over the whole video; phase 0 (CC3D_GROW_ONCE:
+ * the first frame on its own, 1 + 2n frames -> 1 + n) or 1 (CC3D_GROW_ALIGNED:
+ * every output takes two new frames, 2n -> n).  The cache is the last kt-1
+ * input frames, as for any conv.  Chunks must keep the count whole at every
+ * strided layer: with phase 0 the video's first chunk brings an odd number of
+ * frames to that layer and later chunks an even number; with phase 1 every
+ * chunk an even number (forward_chunk, cc3d_output_shape: CC3D_ESHAPE
+ * otherwise).  Not with up_s = 2 (stride_s) or up_t = 2 (stride_t) on the same
+ * conv, not inside a frame-batched group, not with 8-bit output; bf16 strided
+ * convs take kh = kw in {1, 3}. */
+
 /* Create a stack plan (same ownership, failure and synchronisation rules as
  * cc3d_plan_create).  The plan allocates its intermediate slots for
  * max_chunk_t input frames. */
@@ -249,7 +270,8 @@ int cc3d_output_elem_bytes(const cc3d_plan* plan);
 
 /* Output shape of one forward_chunk: y is [*t][*h][*w][*c].  first != 0 for the
  * video's first chunk (frames grow by 2t-1 instead of 2t at each up_t = 2, unless
- * the plan uses CC3D_GROW_ALIGNED). */
+ * the plan uses CC3D_GROW_ALIGNED; strided convs: see "Strided convs").
+ * CC3D_ESHAPE when t_chunk leaves a strided conv a fractional frame count. */
 cc3d_status cc3d_output_shape(const cc3d_plan* plan, int t_chunk, int first, int* c, int* t,
                               int* h, int* w);
 

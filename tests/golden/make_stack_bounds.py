@@ -1,5 +1,6 @@
-"""Writes stack_bounds.txt: the end-to-end bound of every whole-decoder
-configuration the GPU tests compare with the storage-rounded oracle.
+"""Writes stack_bounds.txt: the end-to-end bound of every whole-decoder (and
+whole-encoder) configuration the GPU tests compare with the storage-rounded
+oracle.
 
 Calls only the oracle (and the seeded input generators).  For each case of
 ``tests/stack_cases.py`` the decoder runs chunk by chunk in the oracle with every
@@ -42,8 +43,12 @@ OUT = os.path.join(HERE, "stack_bounds.txt")
 def run_oracle(c, store):
     cpu = {n: {k: None if v is None else v.double().numpy() for k, v in p.items()}
            for n, p in SC.weights(c).items()}
-    x = SC.latent(c).double().numpy()
-    dec = OM.Decoder(cpu, stages=c["stages"], store=store, temporal_grow=c["tg"], aligned=c["aligned"])
+    if c["kind"] == "encoder":
+        x = SC.pixels(c).double().numpy()
+        dec = OM.Encoder(cpu, stages=c["stages"], store=store, aligned=c["aligned"], mode=c["mode"])
+    else:
+        x = SC.latent(c).double().numpy()
+        dec = OM.Decoder(cpu, stages=c["stages"], store=store, temporal_grow=c["tg"], aligned=c["aligned"])
     out, t0 = [], 0
     for n in c["splits"]:
         out.append(dec.step(x[:, t0:t0 + n]))

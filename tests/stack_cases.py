@@ -1,11 +1,14 @@
-"""The whole-decoder configurations the GPU tests compare end to end, and their
-seeded inputs.  Shared by the GPU tests and by ``golden/make_stack_bounds.py``,
+"""The whole-decoder (and whole-encoder) configurations the GPU tests compare
+end to end, and their seeded inputs.  Shared by the GPU tests and by ``golden/make_stack_bounds.py``,
 which measures, per configuration, how far the storage-rounded oracle drifts
 from itself under rounding-level perturbations (the end-to-end bound).
 
 A case: latent channels, stages ((channels, temporal factor), ...), latent
 frames t, frame size h x w, chunk lengths, weight seed cfg, TemporalGrow order
-(None, "before", "after") and the aligned first-chunk rule.
+(None, "before", "after") and the aligned first-chunk rule.  An encoder case
+(kind "encoder") has the pixel channels c_in, frames t of the video, its frame
+size h x w, the stages as the decoder lists them, and history mode (zeros: the
+ReAE rule of the SwiftVR page, "ReAE: Causal Halo Exchange").
 """
 from __future__ import annotations
 
@@ -19,8 +22,13 @@ FULL_STAGES = OM.DECODER_STAGES
 
 
 def case(c_lat, stages, t, h, w, splits, cfg=4, tg=None, aligned=False):
-    return dict(c_lat=c_lat, stages=tuple(tuple(s) for s in stages), t=t, h=h, w=w, splits=tuple(splits),
-                cfg=cfg, tg=tg, aligned=aligned)
+    return dict(kind="decoder", c_lat=c_lat, stages=tuple(tuple(s) for s in stages), t=t, h=h, w=w,
+                splits=tuple(splits), cfg=cfg, tg=tg, aligned=aligned)
+
+
+def enc_case(c_in, c_lat, stages, t, h, w, splits, cfg=5, aligned=False):
+    return dict(kind="encoder", c_in=c_in, c_lat=c_lat, stages=tuple(tuple(s) for s in stages), t=t, h=h, w=w,
+                splits=tuple(splits), cfg=cfg, tg=None, aligned=aligned, mode="zero")
 
 
 def random_decoder_cases(n, seed):
@@ -64,9 +72,20 @@ STACK_CASES = {
 }
 for _i, (_cl, _st, _t, _h, _w, _sp, _tg, _al, _fold) in enumerate(RANDOM_CASES):
     STACK_CASES["random%d" % _i] = case(_cl, _st, _t, _h, _w, _sp, cfg=9, tg=_tg, aligned=_al)
+STACK_CASES.update({
+    # 1 + 4n frames with the first frame on its own (an odd first chunk, even later
+    # ones at every temporal stride), or 4n with the aligned rule
+    "enc_small": enc_case(3, 16, SMALL_STAGES, 9, 16, 24, (5, 4)),
+    "enc_small_aligned": enc_case(3, 16, SMALL_STAGES, 8, 16, 24, (4, 4), aligned=True),
+    "enc_full_tiny": enc_case(3, 48, FULL_STAGES, 5, 16, 16, (1, 4), cfg=9),
+    "enc_full_aligned": enc_case(3, 48, FULL_STAGES, 8, 16, 24, (4, 4), cfg=9, aligned=True),
+})
 
 
 def layer_shapes(c):
+    """(name, Cout, Cin, kt, kh, kw, has_gain, ...) of every conv of the case."""
+    if c["kind"] == "encoder":
+        return OM.encoder_layer_shapes(c_in=c["c_in"], stages=c["stages"], c_latent=c["c_lat"])
     return OM.decoder_layer_shapes(c_latent=c["c_lat"], stages=c["stages"], temporal_grow=c["tg"])
 
 
@@ -80,3 +99,8 @@ def weights(c):
 def latent(c):
     """The case's seeded bf16 latent video [C][T][H][W] (CPU)."""
     return synth.bf16(synth.video(c["c_lat"], c["t"], c["h"], c["w"], synth.seed(c["cfg"], 1)))
+
+
+def pixels(c):
+    """An encoder case's seeded bf16 input video [c_in][T][H][W] (CPU)."""
+    return synth.bf16(synth.video(c["c_in"], c["t"], c["h"], c["w"], synth.seed(c["cfg"], 2)))

@@ -24,7 +24,7 @@ def test_library_exports_every_declared_function():
     assert sorted(declared) == sorted(C.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.cc3d_version() == 104
+    assert L.cc3d_version() == 105
 
 
 def _conv_desc(**kw):
@@ -44,6 +44,9 @@ DUMMY = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
     (dict(epilogue=8), C.EINVAL), (dict(epilogue=C.EPI_ACT | C.EPI_U8), C.EINVAL), (dict(kh=3, kw=1), C.ESHAPE), (dict(eps=-1.0), C.EINVAL),
     (dict(grow=2), C.EINVAL), (dict(grow=-1), C.EINVAL), (dict(fold_upsample=2), C.EINVAL),
     (dict(cin=384, h_in=1440, w_in=1942), C.ESHAPE),  # 2^30 elements per input frame or more
+    # strides: 1 or 2 (0 reads as 1), never with an upsample on the same axis, no 8-bit output
+    (dict(stride_s=3), C.ESHAPE), (dict(stride_t=-1), C.ESHAPE), (dict(stride_s=2, up_s=2), C.ESHAPE),
+    (dict(stride_t=2, up_t=2), C.ESHAPE), (dict(stride_s=2, epilogue=C.EPI_U8), C.EINVAL),
 ])
 def test_plan_create_rejects_bad_descriptor(bad, status):
     L = C.lib()
@@ -275,3 +278,29 @@ def test_noalloc_entry_rejects_bad_arguments_before_device_work():
     assert L.cc3d_conv_forward_noalloc(ctypes.byref(_conv_desc(epilogue=C.EPI_ACT | C.EPI_U8)), DUMMY, None, None,
                                        DUMMY, 1, ctypes.byref(si), ctypes.byref(so), None, DUMMY, None) == C.EINVAL
     assert C.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+def test_descriptor_structs_match_the_header(tmp_path):
+    """The binding's ctypes structures have the header's sizes and field offsets
+    (a C program built against include/cc3d.h prints them)."""
+    fields = {"cc3d_conv_desc": C.ConvDesc, "cc3d_op_desc": C.OpDesc, "cc3d_stack_desc": C.StackDesc,
+              "cc3d_state": C.State, "cc3d_op_profile": C.OpProfile}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "cc3d.h"', "int main(void) {"]
+    for cname, py in fields.items():
+        lines.append('printf("%s size %%zu\\n", sizeof(%s));' % (cname, cname))
+        for f, _ in py._fields_:
+            lines.append('printf("%s %s %%zu\\n", offsetof(%s, %s));' % (cname, f, cname, f))
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.check_call(["gcc", "-I" + os.path.join(ROOT, "include"), "-o", str(exe), str(src)])
+    got = {}
+    for line in subprocess.check_output([str(exe)], text=True).splitlines():
+        a, b, v = line.split()
+        got[(a, b)] = int(v)
+    for cname, py in fields.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)

@@ -1263,3 +1263,188 @@ def test_decoder_rgb8_output_matches_bf16_head():
         assert np.abs(O.quantize_rgb8(from_device_cl(yb)).astype(int) -
                       y8.cpu().permute(3, 0, 1, 2).numpy().astype(int)).max() <= 1
         t0 += n
+
+
+# ------------------------------------------------------------ strided convs --
+# The encoder side: spatial stride 2 (outputs centred on even input pixels) and
+# temporal stride 2 (outputs at input frames tau = phase mod 2 over the video),
+# against the oracle's strided stream.
+
+STRIDED_CASES = [
+    # cin, cout, k, stride_s, stride_t, h, w, splits, tpad, aligned, bias, residual, act
+    (32, 96, (3, 3, 3), 2, 1, 17, 35, [2, 3], C.TPAD_REPLICATE, False, True, False, False),
+    (32, 128, (3, 3, 3), 2, 2, 16, 34, [1, 2, 4], C.TPAD_ZERO, False, False, False, False),
+    (32, 128, (3, 3, 3), 2, 2, 15, 33, [2, 4], C.TPAD_REPLICATE, True, True, False, False),
+    (64, 192, (3, 3, 3), 2, 2, 9, 20, [3, 2], C.TPAD_ZERO, False, True, False, False),
+    (16, 32, (3, 1, 1), 1, 2, 7, 9, [1, 2, 2], C.TPAD_ZERO, False, False, False, False),
+    (32, 64, (1, 1, 1), 2, 1, 10, 33, [2, 1], C.TPAD_REPLICATE, False, True, False, False),
+    (8, 96, (3, 3, 3), 2, 1, 36, 70, [1, 2], C.TPAD_ZERO, False, True, True, True),
+    (96, 192, (2, 3, 3), 2, 2, 11, 21, [1, 2], C.TPAD_ZERO, False, False, False, True),
+    (384, 384, (3, 3, 3), 2, 2, 4, 6, [2, 2], C.TPAD_ZERO, True, False, False, False),
+    (16, 16, (3, 3, 3), 2, 2, 1, 1, [1, 2], C.TPAD_REPLICATE, False, True, False, False),
+]
+
+
+def _strided_ref(x, wt, b, tpad, splits, ss, st, aligned, r=None, g=None):
+    v = O.chunked(to_oracle(x), to_oracle(wt), None if b is None else to_oracle(b), TP[tpad], splits=splits,
+                  aligned=aligned, stride_s=ss, stride_t=st)
+    if r is not None:
+        v = v + to_oracle(r)
+    return v if g is None else O.act(O.round_bf16(v), to_oracle(g), 1e-6)
+
+
+@pytest.mark.parametrize("case", STRIDED_CASES, ids=lambda c: "ci%d_co%d_k%s_s%d_t%d_%dx%d_al%d" % (
+    c[0], c[1], "".join(map(str, c[2])), c[3], c[4], c[5], c[6], c[9]))
+def test_bf16_strided_conv_vs_oracle(case):
+    cin, cout, k, ss, st, h, w, splits, tpad, aligned, with_bias, residual, act = case
+    say("bf16 strided conv %s" % (case,))
+    t = sum(splits)
+    x = synth.bf16(synth.video(cin, t, h, w, synth.seed(40, cin + cout)))
+    wt = synth.bf16(synth.conv_weight(cout, cin, *k, synth.seed(40, 2)))
+    b = synth.bias(cout, synth.seed(40, 3)) if with_bias else None
+    g = synth.gain(cout, synth.seed(40, 4)) if act else None
+    t_out = sum(O.strided_frames(n, st, aligned, seen=sum(splits[:i])) for i, n in enumerate(splits))
+    ho, wo = (h + ss - 1) // ss, (w + ss - 1) // ss
+    r = synth.bf16(synth.video(cout, t_out, ho, wo, synth.seed(40, 5))) if residual else None
+    ref = _strided_ref(x, wt, b, tpad, splits, ss, st, aligned, r, g)
+    plan = P.conv_plan(wt.cuda(), h, w, bias=None if b is None else b.cuda(), gamma=None if g is None else g.cuda(),
+                       act=act, residual=residual, max_chunk_t=max(splits), tpad=tpad, aligned=aligned,
+                       stride_s=ss, stride_t=st)
+    C.check(C.lib().cc3d_profile_enable(plan._h, 1), "profile_enable")
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits,
+                                     residual_cl=to_device_cl(r) if residual else None))
+    pr = C.OpProfile()
+    C.check(C.lib().cc3d_profile_read(plan._h, 0, 0, ctypes.byref(pr)), "profile_read")
+    assert pr.kernel.decode().startswith("conv_bf16_s%dt%d_k%d" % (ss, st, k[1])), pr.kernel
+    assert got.shape == (cout, t_out, ho, wo)
+    assert_bf16_close(got, ref, "strided conv")
+
+
+@pytest.mark.parametrize("case", [
+    # cin, cout, k, stride_s, stride_t, h, w, splits, tpad, aligned
+    (16, 16, (3, 3, 3), 2, 2, 12, 13, [1, 2, 2], C.TPAD_ZERO, False),
+    (8, 24, (2, 3, 3), 2, 1, 9, 10, [3, 1], C.TPAD_REPLICATE, False),
+    (12, 8, (3, 1, 1), 1, 2, 5, 6, [4, 2], C.TPAD_REPLICATE, True),
+])
+def test_fp32_strided_conv_vs_oracle(case):
+    cin, cout, k, ss, st, h, w, splits, tpad, aligned = case
+    say("fp32 strided conv %s" % (case,))
+    x = synth.video(cin, sum(splits), h, w, synth.seed(41, 1))
+    wt = synth.conv_weight(cout, cin, *k, synth.seed(41, 2))
+    b = synth.bias(cout, synth.seed(41, 3))
+    ref = _strided_ref(x, wt, b, tpad, splits, ss, st, aligned)
+    plan = P.conv_plan(wt.cuda(), h, w, bias=b.cuda(), max_chunk_t=max(splits), tpad=tpad, aligned=aligned,
+                       stride_s=ss, stride_t=st)
+    got = from_device_cl(_run_chunks(plan, to_device_cl(x), splits))
+    assert_fp32_close(got, ref, "fp32 strided conv")
+
+
+@pytest.mark.parametrize("aligned", [False, True])
+def test_strided_chunk_lengths_checked_before_any_work(aligned):
+    """A chunk that would leave a temporal stride a fractional frame count is
+    refused (CC3D_ESHAPE) by the shape query and by forward_chunk, before any
+    device work: the state keeps its frame count and y is untouched."""
+    say("strided chunk rule aligned=%s" % aligned)
+    wt = synth.bf16(synth.conv_weight(32, 16, 3, 3, 3, synth.seed(42, 1))).cuda()
+    plan = P.conv_plan(wt, 6, 8, max_chunk_t=4, aligned=aligned, stride_s=2, stride_t=2)
+    c, t, h, w = (ctypes.c_int() for _ in range(4))
+    for tc, first, ok in [(1, 1, not aligned), (2, 1, aligned), (3, 1, not aligned), (2, 0, True), (3, 0, False)]:
+        st = C.lib().cc3d_output_shape(plan._h, tc, first, ctypes.byref(c), ctypes.byref(t), ctypes.byref(h),
+                                       ctypes.byref(w))
+        assert (st == C.OK) == ok, (tc, first, C.last_error())
+        if ok:
+            assert (t.value, h.value, w.value, c.value) == (
+                O.strided_frames(tc, 2, aligned, seen=0 if first else (2 if aligned else 1)), 3, 4, 32)
+    stream = P.Stream(plan)
+    bad = 1 if aligned else 2
+    x = torch.zeros((bad, 6, 8, 16), dtype=torch.bfloat16, device="cuda")
+    y = torch.full((4, 3, 4, 32), 7.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(C.Cc3dError):
+        plan.forward_chunk(x, stream.states[0], stream.states[1], y=y)
+    ci, co = stream.states[0]._c(), stream.states[1]._c()
+    co.frames_seen = 5
+    st = C.lib().cc3d_forward_chunk(plan._h, ctypes.c_void_p(x.data_ptr()), bad, ctypes.byref(ci),
+                                    ctypes.byref(co), None, ctypes.c_void_p(y.data_ptr()), None)
+    assert st == C.ESHAPE, C.last_error()
+    torch.cuda.synchronize()
+    assert co.frames_seen == 5 and stream.states[0].frames_seen == 0
+    assert bool((y == 7.0).all())
+
+
+def _encoder_case(name):
+    """Encoder of a stack_cases configuration, twice on the GPU (production and
+    unique-slot wiring, bitwise equal), every layer against the oracle fed that
+    layer's own GPU input, and the whole stack against the storage-rounded
+    oracle (the recorded end-to-end bound).  The pixels go in padded with zero
+    channels to 8 (bf16 inputs take multiples of 8), conv_in's weights likewise."""
+    c = SC.STACK_CASES[name]
+    full = SC.layer_shapes(c)
+    gains = {s_[0]: s_[6] for s_ in full}
+    cpu, dev = _params([s_[:6] for s_ in full], c["cfg"], lambda n: gains[n])
+    w_in = dev["conv_in"]["w"]
+    pad = torch.zeros((w_in.shape[0], 8) + tuple(w_in.shape[2:]), dtype=w_in.dtype, device=w_in.device)
+    pad[:, :c["c_in"]] = w_in
+    dev["conv_in"]["w"] = pad
+    x = SC.pixels(c)
+    x8 = torch.zeros((8,) + tuple(x.shape[1:]), dtype=x.dtype)
+    x8[:c["c_in"]] = x
+    x_cl = to_device_cl(x8)
+    mode = O.ZERO if c["mode"] == "zero" else O.REPLICATE
+    tpad = C.TPAD_ZERO if c["mode"] == "zero" else C.TPAD_REPLICATE
+    splits = list(c["splits"])
+    ops_u = S.encoder_ops(dev, stages=c["stages"], c_latent=c["c_lat"], unique_slots=True)
+    ops_p = S.encoder_ops(dev, stages=c["stages"], c_latent=c["c_lat"])
+    for o in ops_u + ops_p:
+        o.tpad = tpad
+    plan_u = P.stack_plan(ops_u, 8, c["h"], c["w"], max_chunk_t=max(splits), aligned=c["aligned"])
+    plan_p = P.stack_plan(ops_p, 8, c["h"], c["w"], max_chunk_t=max(splits), aligned=c["aligned"])
+    su, sp = P.Stream(plan_u), P.Stream(plan_p)
+    layer = {i: O.CausalConvStream(cpu[o.name]["w"], cpu[o.name]["b"], mode, aligned=c["aligned"],
+                                   stride_s=o.stride_s, stride_t=o.stride_t)
+             for i, o in enumerate(ops_u)}
+    outs, t0 = [], 0
+    for n in splits:
+        first = su.frames_seen == 0
+        xc = x_cl[t0:t0 + n].contiguous()
+        yu, yp = su.step(xc), sp.step(xc)
+        torch.cuda.synchronize()
+        assert torch.equal(yu, yp), "production wiring differs from the unique-slot wiring"
+        outs.append(yu)
+        ten = {C.SLOT_X: xc, C.SLOT_Y: yu}
+        for o in ops_u:
+            for sl in (o.out, o.act_out):
+                if sl > C.SLOT_AUX:
+                    ten[sl] = plan_u.read_slot(sl, n, first)
+        torch.cuda.synchronize()
+        for i, o in enumerate(ops_u):
+            src = from_device_cl(ten[o.src])
+            if o.name == "conv_in":
+                src = src[:c["c_in"]]
+            v = layer[i].step(src)
+            if o.res != C.SLOT_NONE:
+                v = v + from_device_cl(ten[o.res])
+            if o.out != C.SLOT_NONE:
+                assert_bf16_close(from_device_cl(ten[o.out]), v, "%s out (chunk at %d)" % (o.name, t0))
+            if o.act_out != C.SLOT_NONE:
+                ref_act = O.act(O.round_bf16(v), cpu_gain(cpu, ops_u, o), 1e-6)
+                assert_bf16_close(from_device_cl(ten[o.act_out]), ref_act, "%s act (chunk at %d)" % (o.name, t0))
+        t0 += n
+    got = from_device_cl(torch.cat(outs, dim=0))
+    enc = OM.Encoder(cpu, stages=c["stages"], store=O.round_bf16, aligned=c["aligned"], mode=mode)
+    ref, t0 = [], 0
+    for n in splits:
+        ref.append(enc.step(to_oracle(x)[:, t0:t0 + n]))
+        t0 += n
+    return got, np.concatenate(ref, axis=1)
+
+
+@pytest.mark.parametrize("name", ["enc_small", "enc_small_aligned", "enc_full_tiny", "enc_full_aligned"])
+def test_encoder_layerwise_and_end_to_end(name):
+    say("encoder %s" % name)
+    c = SC.STACK_CASES[name]
+    got, ref = _encoder_case(name)
+    n = c["t"]
+    for _, f in reversed(c["stages"]):
+        n = O.strided_frames(n, f, c["aligned"])
+    assert got.shape == (c["c_lat"], n, -(-c["h"] // 16), -(-c["w"] // 16))
+    assert_stack_close(got, ref, name, "encoder")
