@@ -1,6 +1,6 @@
 """Benchmark of the chunked causal Conv3d decode on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4|c4tg|c3|c2|c1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4|c4tg|c3|c2|c1|e4]
                     [--tg-order before|after] [--frame-batch B] [--fold-upsample] [--videos N]
                     [--no-cpu-baseline] [--no-delivery]
 
@@ -26,6 +26,13 @@ available):
       RMSNorm+SiLU -> conv 128->128 at 540x960, 24 frames in chunks of 4.
   c1: the residual block, 128 ch at 90x160, x + conv(act(conv(act(x)))), 16
       frames in chunks of 4.
+  e4: the encoder side, the decoder read backwards: pixels 3 x 361 x 1440x2560
+      (padded with zero channels to 8) -> conv_in 3->96 with spatial stride 2 ->
+      3 stages (96/192/384 ch; 2 residual blocks, then a conv with spatial
+      stride 2 and temporal stride 1/2/2) -> act -> conv 384->48: latents
+      48 x 91 x 90x160, in chunks of 25 then 24 frames (7, then 6 latents; zero
+      history).  One step = one chunk; value counts conv_in with its 3 real
+      input channels.
 Inputs are resident in HBM before timing; outputs go to a device ring.
 --videos N: whole videos (c4: the 15 clips of 361 frames; c3: 91 chunks; c2, c1:
       their 24 or 16 frames) decoded 1 + N times, the first untimed; the seconds
@@ -273,7 +280,87 @@ def setup_c1(dev, torch, synth, P, S):
     return plan, work, ring, desc
 
 
-VIDEO_STEPS = {"c4": 15, "c4tg": 15, "c3": 91, "c2": 6, "c1": 4}
+def encoder_layer_list(c_in=8, stages=((384, 2), (192, 2), (96, 1)), c_latent=48):
+    """(name, cout, cin, kt, kh, kw, has_gain, stride_s, stride_t) -- the
+    encoder's conv list: the decoder's stages from the last, each [two residual
+    blocks, a conv with spatial stride 2 and the stage's temporal factor as
+    temporal stride] between a stride-2 conv_in and conv_out."""
+    widths = [stages[0][0]] + [c for c, _ in stages]
+    out = [("conv_in", stages[-1][0], c_in, 3, 3, 3, False, 2, 1)]
+    n = len(stages)
+    for ei in range(n):
+        c, f = stages[n - 1 - ei]
+        for r in range(2):
+            out.append(("e%d.rb%d.c1" % (ei, r), c, c, 3, 3, 3, True, 1, 1))
+            out.append(("e%d.rb%d.c2" % (ei, r), c, c, 3, 3, 3, True, 1, 1))
+        out.append(("e%d.down" % ei, widths[n - 1 - ei], c, 3, 3, 3, False, 2, f))
+    out.append(("conv_out", c_latent, widths[0], 3, 3, 3, True, 1, 1))
+    return out
+
+
+def halved(n, first):
+    """Outputs of a temporal stride of 2 with the first frame on its own."""
+    return (n + 1) // 2 if first else n // 2
+
+
+def e4_step_flops(t_in, first, h=1440, w=2560, c_pix=3):
+    """Algorithmic conv FLOP of one encoder chunk of t_in frames (conv_in with
+    its c_pix real channels) and the latents it yields."""
+    f, t = 0.0, t_in
+    h, w = (h + 1) // 2, (w + 1) // 2
+    f += conv_flops_per_voxel(c_pix, 96) * t * h * w
+    for c, c_next, st in ((96, 192, 1), (192, 384, 2), (384, 384, 2)):
+        f += 4 * conv_flops_per_voxel(c, c) * t * h * w
+        h, w = (h + 1) // 2, (w + 1) // 2
+        if st == 2:
+            t = halved(t, first)
+        f += conv_flops_per_voxel(c, c_next) * t * h * w
+    f += conv_flops_per_voxel(384, 48) * t * h * w
+    return f, t
+
+
+def setup_e4(dev, torch, synth, P, S):
+    h, w, c_pix, c_in = 1440, 2560, 3, 8
+    params = {}
+    for i, (name, co, ci, kt, kh, kw, has_g, _, _) in enumerate(encoder_layer_list(c_in=c_pix)):
+        wt = synth.bf16(synth.conv_weight(co, ci, kt, kh, kw, synth.seed(6, 10 + 3 * i)))
+        if name == "conv_in":  # the pixels' zero channels get zero weights
+            wp = torch.zeros((co, c_in, kt, kh, kw), dtype=wt.dtype)
+            wp[:, :c_pix] = wt
+            wt = wp
+        params[name] = {"w": wt.to(dev), "b": None,
+                        "g": synth.gain(ci, synth.seed(6, 11 + 3 * i)).to(dev) if has_g else None}
+    ops = S.encoder_ops(params)
+    for o in ops:
+        o.tpad = S.C.TPAD_ZERO  # zero history: the ReAE rule
+    plan = P.stack_plan(ops, c_in, h, w, max_chunk_t=25, device=dev)
+    del params
+    log("e4 plan: %d ops, state %.2f GB, plan device memory %.2f GB" % (
+        len(ops), plan.state_bytes / 1e9, plan.device_bytes / 1e9))
+    pool = []
+    for k, n in enumerate((25, 24, 24)):  # distinct chunks, cycled (content does not change the time)
+        x = synth.bf16(synth.video(c_pix, n, h, w, synth.seed(6, 100 + k)))
+        xc = torch.zeros((n, h, w, c_in), dtype=torch.bfloat16, device=dev)
+        xc[..., :c_pix] = x.permute(1, 2, 3, 0).to(dev)
+        del x
+        pool.append(xc)
+    sched = [25] + [24] * 14
+    work = []
+    for i, n in enumerate(sched):
+        fl, lat = e4_step_flops(n, i == 0)
+        xc = pool[0] if i == 0 else pool[1 + i % 2]
+        work.append((xc, i == 0, fl, lat, fl))
+    ring = [torch.empty((7, 90, 160, 48), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    desc = {"workload": "e4_encoder_bf16: pixels 3x361x1440x2560 (zero-padded to 8 channels) -> conv_in 3->96 "
+                        "stride 2 -> 3 stages (96/192/384 ch; 2 residual blocks, then conv with spatial stride 2, "
+                        "temporal stride 1/2/2) -> act -> conv 384->48 at 90x160; chunks of 25+14x24 frames, "
+                        "zero history",
+            "output": "48x91x90x160 bf16", "step": "one chunk (24 input frames; 25 for the first)",
+            "frames": "frames_per_s counts input frames"}
+    return plan, work, ring, desc
+
+
+VIDEO_STEPS = {"c4": 15, "c4tg": 15, "c3": 91, "c2": 6, "c1": 4, "e4": 15}
 
 
 def video_times(torch, plan, work, ring, runs, warmup=1):
@@ -477,6 +564,23 @@ def cpu_baseline(workload, temporal_grow=None):
         sample = "1080p-class stage on one %d-frame chunk of a %dx%d crop (-> %dx%d), fp64, %d threads" % (
             lt, rows, cols, y.shape[2], y.shape[3], threads)
         frames_per_s = lt / dt * (y.shape[2] * y.shape[3]) / (540 * 960)
+    elif workload == "e4":
+        lt, rows, cols = 5, 64, 320  # about 15 s on 16 host threads
+        shapes = OM.encoder_layer_shapes()
+        params = {}
+        for i, (name, co, ci, kt, kh, kw, has_g, _, _) in enumerate(shapes):
+            params[name] = {"w": synth.conv_weight(co, ci, kt, kh, kw, synth.seed(6, 10 + 3 * i)).double().numpy(),
+                            "g": synth.gain(ci, synth.seed(6, 11 + 3 * i)).double().numpy() if has_g else None,
+                            "b": None}
+        x = synth.video(3, lt, rows, cols, synth.seed(6, 100)).double().numpy()
+        enc = OM.Encoder(params, nthreads=threads)
+        t0 = time.perf_counter()
+        y = enc.step(x)
+        dt = time.perf_counter() - t0
+        fl, _ = e4_step_flops(lt, True, rows, cols)
+        sample = ("whole encoder, one first chunk of %d frames on a %dx%d pixel crop (-> %d latents of %dx%d), "
+                  "fp64, %d threads" % (lt, rows, cols, y.shape[1], y.shape[2], y.shape[3], threads))
+        frames_per_s = lt / dt * (rows * cols) / (1440 * 2560)
     elif workload == "c1":
         c, rows, cols, lt = 128, 90, 160, 4  # one whole 4-frame chunk, about 10 s on 16 host threads
         p = [{"w": synth.conv_weight(c, c, 3, 3, 3, synth.seed(1, 10 + 3 * i)).double().numpy(), "b": None,
@@ -525,7 +629,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=45)  # c4: three passes over the 15-clip video
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", choices=["c4", "c4tg", "c3", "c2", "c1"], default="c4")
+    ap.add_argument("--workload", choices=["c4", "c4tg", "c3", "c2", "c1", "e4"], default="c4")
     ap.add_argument("--tg-order", choices=["before", "after"], default="before",
                     help="c4tg: TemporalGrow before (reordered) or after (original) the spatial upsample")
     ap.add_argument("--frame-batch", type=int, default=0,
@@ -560,6 +664,8 @@ def main():
         plan, work, ring, desc = setup_c2(dev, torch, synth, P, S)
     elif args.workload == "c1":
         plan, work, ring, desc = setup_c1(dev, torch, synth, P, S)
+    elif args.workload == "e4":
+        plan, work, ring, desc = setup_e4(dev, torch, synth, P, S)
     else:
         plan, work, ring, desc = setup_c4(dev, torch, synth, P, S, temporal_grow=tg, frame_batch=args.frame_batch,
                                           fold=args.fold_upsample)
@@ -568,6 +674,9 @@ def main():
         torch, plan, work, ring, args.steps, args.warmup,
         before_timed=lambda: C.check(C.lib().cc3d_profile_enable(plan._h, 1), "profile_enable"))
     log("timed %.3f s" % dt)
+    in_frames = None
+    if args.workload == "e4":  # an encoder's rate is in input frames; tout counts latents
+        in_frames = sum(work[i % len(work)][0].shape[0] for i in range(args.warmup, args.warmup + args.steps))
 
     # per-kernel event totals over the timed region
     import ctypes
@@ -639,7 +748,7 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(dt / args.steps * 1e3, 3), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": desc, "frames_per_s": round(frames / dt, 2),
+        "config": desc, "frames_per_s": round((in_frames if in_frames is not None else frames) / dt, 2),
         "mfma_frac": round(executed / dt / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": roof, "kernels": per_kernel,
         # per-step GPU time between events on the stream (the first clip is the
@@ -647,6 +756,8 @@ def main():
         "step_ms": {"min": round(step_ms[0], 3), "mean": round(sum(step_ms) / len(step_ms), 3),
                     "p99": round(step_ms[min(len(step_ms) - 1, int(0.99 * len(step_ms)))], 3)},
     }
+    if in_frames is not None:
+        out["latents_per_s"] = round(frames / dt, 2)
     if args.fold_upsample:
         out["executed_tflops"] = round(executed / dt / 1e12, 2)
     if args.videos > 0:
@@ -655,7 +766,7 @@ def main():
         assert len(work) == n_video
         log("%d whole videos (%d steps each) after one untimed" % (args.videos, n_video))
         vt = video_times(torch, plan, work, ring, args.videos)
-        v_frames = sum(wk[3] for wk in work)
+        v_frames = sum((wk[0].shape[0] if in_frames is not None else wk[3]) for wk in work)
         v_flops = sum(wk[2] for wk in work)
         mean = sum(vt) / len(vt)
         out["video"] = {"frames": v_frames, "steps": n_video, "warmup": 1, "runs": len(vt),

@@ -352,7 +352,11 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
                 const int plain = o.act_out == CC3D_SLOT_NONE && !o.out_u8;
                 r.family = cc3d::bf16_conv_family(o.cout, r.cin, o.kt, o.kh, o.kw, o.up_s, plain,
                                                   d->fold_upsample && !o.out_u8);
-                if (r.stride_s == 2 || r.stride_t == 2) r.family = 1;  // the generic kernel takes strides
+                if (r.stride_s == 2 || r.stride_t == 2) {
+                    // 3x3 spatial stride 2 in 96/128-channel blocks: the register-blocked
+                    // kernel's strided tile; any other strided conv: the generic kernel
+                    r.family = (r.family == 2 && r.stride_s == 2) ? 2 : 1;
+                }
                 if (r.family == 4) cc3d::pw_conv_tiling(o.cout, &r.ntile, &r.nblocks);
             }
         } else {
@@ -776,7 +780,8 @@ std::string conv_kernel_name(const cc3d_plan* p, const OpRt& r)
     else if (p->dtype == CC3D_BF16 && r.family == 4)
         snprintf(buf, sizeof buf, "conv_bf16_pw_up%d_kt%d_n%d", r.up_s, r.kt, r.ntile);
     else if (p->dtype == CC3D_BF16 && (r.stride_s > 1 || r.stride_t > 1))
-        snprintf(buf, sizeof buf, "conv_bf16_s%dt%d_k%d_n%d", r.stride_s, r.stride_t, r.kh, r.ntile);
+        snprintf(buf, sizeof buf, "conv_bf16%s_s%dt%d_k%d_n%d", r.family == 2 ? "_v2" : "", r.stride_s, r.stride_t,
+                 r.kh, r.ntile);
     else if (p->dtype == CC3D_BF16)
         snprintf(buf, sizeof buf, "conv_bf16%s_up%d_k%d_n%d", r.family == 2 ? "_v2" : "", r.up_s, r.kh,
                  r.ntile);

@@ -31,6 +31,14 @@
 // * Work items (tile, frame, channel block) are dealt to the 8 XCDs in contiguous
 //   ranges, so neighbouring tiles and consecutive frames (which share input rows
 //   and frames) run under the same L2.
+// * Strided convs (DOWN = 2, the encoder side): the tile is RH output rows x 64
+//   output columns, which read input rows 2y-1 .. 2y+1 and columns 2x-1 ..
+//   2x+1.  The LDS tile keeps the even input columns first and the odd ones
+//   after them, so a fragment's 16 output columns read 16 consecutive LDS
+//   pixels at every column tap (even half at x + d/2 for d = 0, 2; odd half at x
+//   for d = 1), and LDS row s serves output rows (s - b) / 2 for the row taps b
+//   of the same parity.  Output frame t reads window frames
+//   t_stride*t + t_first + (0 .. kt-1).
 #include "cc3d_device.h"
 
 namespace cc3d {
@@ -70,13 +78,17 @@ struct Geo<2, RH> {  // tile: 4 RH source rows x 16 source columns; M-wave w: so
 // is a base register plus a constant (the chunk swizzle depends on the column
 // only).  Weights are prefetched two sub-steps ahead (three LDS buffers; two,
 // one sub-step ahead, where three do not fit), the input tile one K step ahead.
-template <int UP, int NF, int WN, int RH>
+template <int UP, int NF, int WN, int RH, int DOWN>
 __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
 {
+    static_assert(DOWN == 1 || UP == 1, "a conv either upsamples or strides");
     using G = Geo<UP, RH>;
     constexpr int NT = 256 * WN;        // threads
     constexpr int NFW = NF / WN;        // N fragments per wave
-    constexpr int LH = G::TS_H + 2, LW = G::TS_W + 2;
+    // LDS tile: the input rows and columns the tile's outputs read
+    constexpr int LH = DOWN == 2 ? 2 * G::TS_H + 1 : G::TS_H + 2;
+    constexpr int LW = DOWN == 2 ? 2 * G::TS_W + 1 : G::TS_W + 2;
+    constexpr int NE = (LW + 1) / 2;  // DOWN = 2: even input columns, stored first
     constexpr int LWP = (LW + 1) / 2 * 2;  // row pitch (pixels)
     constexpr int ROWB = LWP * 64;          // bytes per LDS row
     constexpr int NTILE = 16 * NF;
@@ -108,16 +120,20 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     __shared__ uint4 lds_b2[NBB == 3 ? B_CH : 1];
     __shared__ float lds_red[RED];  // epilogue: per-pixel partial sums of squares
 
-    const int tiles_w = (a.w_in + G::TS_W - 1) / G::TS_W;
-    const int tiles_h = (a.h_in + G::TS_H - 1) / G::TS_H;
+    // tiles cover the output frame (DOWN = 2) or the source frame (the output
+    // frame too for UP = 1)
+    const int tiles_w = ((DOWN == 2 ? a.w_out : a.w_in) + G::TS_W - 1) / G::TS_W;
+    const int tiles_h = ((DOWN == 2 ? a.h_out : a.h_in) + G::TS_H - 1) / G::TS_H;
     const int total = tiles_w * tiles_h * a.t_out * a.nblocks;
 
   // One work item (tile, frame, channel block): main loop and epilogue.
   auto process = [&](const int w) {
     int tile, t, nb;
     decode_item(w, a.t_out, a.nblocks, tile, t, nb);
-    const int i0 = (tile / tiles_w) * G::TS_H;  // source tile origin
+    const int i0 = (tile / tiles_w) * G::TS_H;  // tile origin (source frame for UP = 2, else output)
     const int j0 = (tile % tiles_w) * G::TS_W;
+    // first window frame of output frame t
+    const int tz0 = DOWN == 2 ? a.t_stride * t + a.t_first : t;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 3, wn = wave >> 2;
@@ -150,7 +166,9 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
             const int r = pix / LWP, c = pix - r * LWP;
             const int gg = (slot & 3) ^ swz(c);
             a_ch[it] = gg * 8;
-            const int gy = i0 + r - 1, gx = j0 + c - 1;
+            // input column of LDS column c (DOWN = 2: even columns, then odd)
+            const int ci = DOWN == 2 ? (c < NE ? 2 * c : 2 * (c - NE) + 1) : c;
+            const int gy = DOWN * i0 + r - 1, gx = DOWN * j0 + ci - 1;
             if (c < LW && gy >= 0 && gy < a.h_in && gx >= 0 && gx < a.w_in)
                 a_off[it] = (uint32_t)(((gy * a.w_in + gx) * a.cin + gg * 8) * 2);
         }
@@ -162,7 +180,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     // order as a whole-chunk one), so the
     // workgroups of frames t, t+1, t+2 -- which run at the same time -- read the
     // same input frame in the same step and share it in L2.
-    const int rot = a.rot_taps ? (a.kt - (a.t_rot0 + t) % a.kt) % a.kt : 0;
+    const int rot = a.rot_taps ? (a.kt - (a.t_rot0 + tz0) % a.kt) % a.kt : 0;
     auto phys_step = [&](int step) -> int {
         const int ta = step / a.kchunks, kc = step - ta * a.kchunks;
         const int tr = ta + rot < a.kt ? ta + rot : ta + rot - a.kt;
@@ -172,7 +190,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     auto issue_a = [&](int lstep, uint4* buf) {
         const int step = phys_step(lstep);
         const int ta = step / a.kchunks, kc = step - ta * a.kchunks;
-        const uint16_t* fp = zframe(a.z, t + ta);
+        const uint16_t* fp = zframe(a.z, tz0 + ta);
         const __amdgpu_buffer_rsrc_t r = make_rsrc(fp, fp ? frame_bytes : 0u);
         const int ch0 = kc * 32;
 #pragma unroll
@@ -208,7 +226,23 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     // The MFMAs of one sub-step (column tap d) from input buffer `aread` and the
     // B fragments bq[b][f] of taps (b, d).
     auto mma = [&](const int d, const uint4* aread, const bf16x8 (&bq)[3][NFW]) {
-        if (UP == 1) {
+        if (DOWN == 2) {
+            // LDS row s holds input row 2*i0 + s - 1; output row r reads rows 2r + b.
+            const int base = col_off((d & 1) ? NE + 16 * wm + k16 : 16 * wm + k16 + (d >> 1));
+#pragma unroll
+            for (int s = 0; s < LH; ++s) {
+                const bf16x8 av = lds_frag(aread, base + s * ROWB);
+#pragma unroll
+                for (int b = 0; b < 3; ++b) {
+                    const int r = (s - b) >> 1;
+                    if (((s - b) & 1) == 0 && s >= b && r < G::TS_H) {
+#pragma unroll
+                        for (int f = 0; f < NFW; ++f)
+                            acc[r][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bq[b][f], av, acc[r][f], 0, 0, 0);
+                    }
+                }
+            }
+        } else if (UP == 1) {
             // LDS row s holds source row i0 + s - 1; output row r reads rows r+b.
             const int base = col_off(16 * wm + k16 + d);
 #pragma unroll
@@ -503,15 +537,16 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     if (live) process(w);
 }
 
-template <int UP, int NF, int WN, int RH>
+template <int UP, int NF, int WN, int RH, int DOWN = 1>
 hipError_t launch_v2(const ConvArgs& a, hipStream_t s)
 {
     using G = Geo<UP, RH>;
-    const int tiles = ((a.h_in + G::TS_H - 1) / G::TS_H) * ((a.w_in + G::TS_W - 1) / G::TS_W);
+    const int th = DOWN == 2 ? a.h_out : a.h_in, tw = DOWN == 2 ? a.w_out : a.w_in;
+    const int tiles = ((th + G::TS_H - 1) / G::TS_H) * ((tw + G::TS_W - 1) / G::TS_W);
     const int64_t total = (int64_t)tiles * a.t_out * a.nblocks;
     if (total <= 0 || total > (int64_t)0x7fffffff - 8) return hipErrorInvalidValue;
     const int64_t grid = ((total + 7) / 8) * 8;
-    hipLaunchKernelGGL((conv3_v2_kernel<UP, NF, WN, RH>), dim3((unsigned)grid), dim3(256 * WN), 0, s, a);
+    hipLaunchKernelGGL((conv3_v2_kernel<UP, NF, WN, RH, DOWN>), dim3((unsigned)grid), dim3(256 * WN), 0, s, a);
     return hipGetLastError();
 }
 
@@ -525,6 +560,13 @@ bool v2_conv_applies(int ntile, int kh, int kw, int up_s)
 hipError_t launch_conv_bf16_v2(const ConvArgs& a, hipStream_t s)
 {
     if (!v2_conv_applies(a.ntile, a.kh, a.kw, a.up_s)) return hipErrorInvalidValue;
+    if (a.down_s == 2) {
+        // spatial stride 2: 2 output rows x 64 columns per tile (5 x 130 input
+        // pixels in LDS, double-buffered, beside the weight buffers)
+        if (a.up_s != 1 || a.t_stride < 1 || a.t_stride > 2) return hipErrorInvalidValue;
+        return a.ntile == 96 ? launch_v2<1, 6, 2, 2, 2>(a, s) : launch_v2<1, 8, 2, 2, 2>(a, s);
+    }
+    if (a.t_stride != 1 || a.t_first != 0) return hipErrorInvalidValue;  // temporal stride: family 1
     // up_s = 1, 96-channel blocks: 9 output rows per wave (a 9 x 64 tile per
     // workgroup, weights three buffers deep in LDS).  Measured against 8 rows
     // (4-10% slower: fewer pixels per weight fetch, larger border share) and 10

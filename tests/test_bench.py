@@ -147,3 +147,32 @@ def test_video_steps_cover_each_workload():
 def test_cpu_model_is_read():
     m = bench.cpu_model()
     assert m is None or (isinstance(m, str) and m)
+
+
+def test_encoder_layer_list_is_the_oracles():
+    assert bench.encoder_layer_list(c_in=3) == OM.encoder_layer_shapes(c_in=3)
+
+
+@pytest.mark.parametrize("t_in,first", [(25, True), (24, False), (1, True), (4, False)])
+def test_encoder_step_flops_match_a_per_layer_count(t_in, first):
+    """The e4 step's FLOP, summed here layer by layer over the oracle's layer list
+    with the oracle's strided frame counts and ceil(H/2) frame sizes."""
+    from oracle import oracle as O
+    h, w, t = 1440, 2560, t_in
+    seen = 0 if first else 25 + 24 * 3  # a later chunk starts at an odd frame
+    want = 0.0
+    for name, co, ci, kt, kh, kw, _, ss, st in OM.encoder_layer_shapes(c_in=3):
+        if ss == 2:
+            h, w = (h + 1) // 2, (w + 1) // 2
+        if st == 2:
+            t_new = O.strided_frames(t, 2, seen=seen)
+            seen = O.strided_frames(seen, 2)  # frames this layer's output held before the chunk
+            t = t_new
+        want += 2.0 * ci * co * kt * kh * kw * t * h * w
+    got, lat = bench.e4_step_flops(t_in, first)
+    assert got == want and lat == t
+
+
+def test_encoder_schedule_covers_the_video():
+    lats = [bench.e4_step_flops(n, i == 0)[1] for i, n in enumerate([25] + [24] * 14)]
+    assert lats == [7] + [6] * 14 and sum(lats) == 91 and bench.VIDEO_STEPS["e4"] == 15

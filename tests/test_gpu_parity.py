@@ -1282,7 +1282,30 @@ STRIDED_CASES = [
     (96, 192, (2, 3, 3), 2, 2, 11, 21, [1, 2], C.TPAD_ZERO, False, False, False, True),
     (384, 384, (3, 3, 3), 2, 2, 4, 6, [2, 2], C.TPAD_ZERO, True, False, False, False),
     (16, 16, (3, 3, 3), 2, 2, 1, 1, [1, 2], C.TPAD_REPLICATE, False, True, False, False),
+    # the register-blocked strided tile (2 output rows x 64 columns): several
+    # column and row tiles with ragged ends, two 128-channel blocks, frames that
+    # the tiles cover exactly (with residual and act), one-pixel frames
+    (64, 96, (3, 3, 3), 2, 2, 13, 261, [3, 2], C.TPAD_REPLICATE, False, True, False, False),
+    (32, 256, (3, 3, 3), 2, 1, 10, 140, [2, 2], C.TPAD_ZERO, False, False, True, False),
+    (96, 96, (3, 3, 3), 2, 2, 8, 256, [1, 2], C.TPAD_ZERO, False, True, True, True),
+    (64, 128, (3, 3, 3), 2, 2, 1, 2, [2, 2], C.TPAD_REPLICATE, True, True, False, False),
+    (192, 384, (3, 3, 3), 2, 2, 6, 9, [1, 4], C.TPAD_ZERO, False, True, False, True),
 ]
+
+
+def _ntile(cout):
+    """Output channels per workgroup of the bf16 conv kernels."""
+    if cout <= 16:
+        return 16
+    if cout <= 32:
+        return 32
+    if cout <= 64:
+        return 64
+    if cout <= 96:
+        return 96
+    if cout <= 128:
+        return 128
+    return 96 if cout % 96 == 0 else (128 if cout % 128 == 0 else 64)
 
 
 def _strided_ref(x, wt, b, tpad, splits, ss, st, aligned, r=None, g=None):
@@ -1315,7 +1338,9 @@ def test_bf16_strided_conv_vs_oracle(case):
                                      residual_cl=to_device_cl(r) if residual else None))
     pr = C.OpProfile()
     C.check(C.lib().cc3d_profile_read(plan._h, 0, 0, ctypes.byref(pr)), "profile_read")
-    assert pr.kernel.decode().startswith("conv_bf16_s%dt%d_k%d" % (ss, st, k[1])), pr.kernel
+    # 3x3 spatial stride 2 in 96/128-channel blocks: the register-blocked kernel
+    v2 = ss == 2 and k[1:] == (3, 3) and _ntile(cout) in (96, 128)
+    assert pr.kernel.decode().startswith("conv_bf16%s_s%dt%d_k%d" % ("_v2" if v2 else "", ss, st, k[1])), pr.kernel
     assert got.shape == (cout, t_out, ho, wo)
     assert_bf16_close(got, ref, "strided conv")
 
