@@ -389,12 +389,12 @@ def video_times(torch, plan, work, ring, runs, warmup=1):
     return sorted(marks[r].elapsed_time(marks[r + 1]) * 1e-3 for r in range(runs))
 
 
-def _counter_record(kernel_name):
+def _counter_record(kernel_name, workload=None):
     """The fields of `kernel_name`'s record in a committed PMC summary in
-    profiles/ (a "traffic_record:" line), or None when no record exists or a
-    source it names (comma-separated: the kernel, the op list that sets its
-    launches, the build script that holds its compiler flags) changed since the
-    counters were taken."""
+    profiles/ (a "traffic_record:" line; one that names a workload counts for
+    that workload only), or None when no record exists or a source it names
+    (comma-separated: the kernel, the op list that sets its launches, the build
+    script that holds its compiler flags) changed since the counters were taken."""
     import glob
     import hashlib
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
@@ -403,6 +403,8 @@ def _counter_record(kernel_name):
                 continue
             kv = dict(item.split("=", 1) for item in line.split()[1:])
             if kv.get("kernel") != kernel_name:
+                continue
+            if "workload" in kv and workload is not None and kv["workload"] != workload:
                 continue
             srcs = [os.path.join(ROOT, f) for f in kv["source"].split(",")]
             if not all(os.path.exists(f) for f in srcs):
@@ -415,17 +417,17 @@ def _counter_record(kernel_name):
     return None
 
 
-def recorded_traffic(kernel_name):
-    """HBM bytes per launch of `kernel_name` (FETCH_SIZE + WRITE_SIZE runs,
-    copy-calibrated), or None (see _counter_record)."""
-    kv = _counter_record(kernel_name)
+def recorded_traffic(kernel_name, workload=None):
+    """HBM bytes per launch of `kernel_name` in `workload` (FETCH_SIZE +
+    WRITE_SIZE runs, copy-calibrated), or None (see _counter_record)."""
+    kv = _counter_record(kernel_name, workload)
     return float(kv["bytes_per_launch"]) if kv else None
 
 
-def recorded_clock(kernel_name):
+def recorded_clock(kernel_name, workload=None):
     """Mean shader clock in GHz over `kernel_name`'s dispatches in the counter
     run (GRBM_GUI_ACTIVE per XCD / dispatch time), or None."""
-    kv = _counter_record(kernel_name)
+    kv = _counter_record(kernel_name, workload)
     return float(kv["clock_ghz"]) if kv and "clock_ghz" in kv else None
 
 
@@ -711,7 +713,8 @@ def main():
         achieved = dom["bytes"] / dom["launches"] / (avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    clock = recorded_clock(dom_name)
+    wl_key = args.workload + ("_" + tg if tg else "")
+    clock = recorded_clock(dom_name, wl_key)
     if clock and roof["bound"] == "mfma":
         # the part runs below its 2.4 GHz peak clock under this load (power): the
         # same rate against the dense peak at the clock the counters saw
@@ -721,7 +724,7 @@ def main():
     if dom["exec_flops"] != dom["flops"]:
         roof["flop_basis"] = "the folded kernel's own MFMA work (27-tap equivalent: %.1f TFLOP/s)" % (
             dom["flops"] / dom["launches"] / (avg_ms * 1e-3) / 1e12)
-    roof.update({"traffic": recorded_traffic(dom_name), "kernel": dom_name, "launches": dom["launches"],
+    roof.update({"traffic": recorded_traffic(dom_name, wl_key), "kernel": dom_name, "launches": dom["launches"],
                  "avg_launch_ms": round(avg_ms, 4), "share_of_kernel_time": round(dom["ms"] / total_kernel_ms, 3)})
     # per kernel: algorithmic rates and the fraction of the roof that bounds it
     # (MFMA where its FLOP per algorithmic byte reach the ridge point, else HBM)

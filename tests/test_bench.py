@@ -124,6 +124,14 @@ def test_traffic_record_follows_the_source(tmp_path, monkeypatch):
     (prof / "x.md").write_text("traffic_record: kernel=kk source=k.hip,ops.py source_sha256_16=%s "
                                "bytes_per_launch=7 clock_ghz=1.994\n" % sha3)
     assert bench.recorded_clock("kk") == 1.994 and bench.recorded_traffic("kk") == 7.0
+    # a record that names its workload counts for that workload only (one kernel
+    # can dominate two workloads with different bytes per launch)
+    (prof / "x.md").write_text("traffic_record: kernel=kk workload=c4 source=k.hip,ops.py source_sha256_16=%s "
+                               "bytes_per_launch=7\n"
+                               "traffic_record: kernel=kk workload=e4 source=k.hip,ops.py source_sha256_16=%s "
+                               "bytes_per_launch=9\n" % (sha3, sha3))
+    assert bench.recorded_traffic("kk", "c4") == 7.0 and bench.recorded_traffic("kk", "e4") == 9.0
+    assert bench.recorded_traffic("kk", "c3") is None
 
 
 def test_more_than_one_gpu_is_refused():
