@@ -567,7 +567,7 @@ def cpu_baseline(workload, temporal_grow=None):
             lt, rows, cols, y.shape[2], y.shape[3], threads)
         frames_per_s = lt / dt * (y.shape[2] * y.shape[3]) / (540 * 960)
     elif workload == "e4":
-        lt, rows, cols = 5, 64, 320  # about 15 s on 16 host threads
+        lt, rows, cols = 5, 96, 480  # about 11 s on 16 host threads
         shapes = OM.encoder_layer_shapes()
         params = {}
         for i, (name, co, ci, kt, kh, kw, has_g, _, _) in enumerate(shapes):

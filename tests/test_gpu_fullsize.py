@@ -96,17 +96,26 @@ def _gather(y, ts, row, cols):
     return y[ti, row][torch.arange(ti.numel(), device=y.device), ci].double().cpu().numpy()
 
 
-def check_conv(z, w, b, up, ts, rows, cols, out=None, res=None, act=None, gamma=None, tallies=None):
+def check_conv(z, w, b, up, ts, rows, cols, out=None, res=None, act=None, gamma=None, tallies=None,
+               down=1, t_stride=1, t_first=0):
     """Compare the op's stored result (out = conv + bias (+ res), bf16) and/or
     its act (SiLU(RMSNorm(rounded result))) with the oracle at the sampled
-    positions.  z: [Tz][Hin][Win][Cin] device window; w, b: float64 numpy."""
+    positions.  z: [Tz][Hin][Win][Cin] device window; w, b: float64 numpy.
+    A strided conv (down, t_stride): output frame t's window starts at window
+    frame t_stride*t + t_first; output pixel y is centred on input row down*y."""
     hin = z.shape[1]
     for y in rows:
-        r0 = max(0, (y - 1) // up)
-        r1 = min(hin - 1, (y + 1) // up)
+        if down == 1:
+            r0 = max(0, (y - 1) // up)
+            r1 = min(hin - 1, (y + 1) // up)
+            yl = y - up * r0
+        else:  # an even first row, so the output row stays on the stride grid
+            r0 = max(0, down * y - 2)
+            r1 = min(hin - 1, down * y + 1)
+            yl = (down * y - r0) // down
         zc = z[:, r0:r1 + 1].float().cpu().numpy().transpose(3, 0, 1, 2)  # [C][T][rows][W], a view
-        pts = np.array([(t, y - up * r0, c) for t in ts for c in cols], dtype=np.int32)
-        v = O.conv_points(zc, w, b, pts, up)  # n x Cout
+        pts = np.array([(t_stride * t + t_first, yl, c) for t in ts for c in cols], dtype=np.int32)
+        v = O.conv_points(zc, w, b, pts, up, down=down)  # n x Cout
         if res is not None:
             v = v + _gather(res, ts, y, cols)
         if out is not None:
@@ -134,7 +143,8 @@ def run_stack_sampled(ops, params_cpu, x_cl, cin, h, w, splits, seed, max_pts_ro
     unchecked, and their outputs are not kept."""
     plan = P.stack_plan(ops, cin, h, w, max_chunk_t=max(splits), fold_upsample=fold_upsample)
     st = P.Stream(plan)
-    wins = {i: Window(o.k[0], o.up_t) for i, o in enumerate(ops) if o.kind == C.OP_CONV}
+    wins = {i: Window(o.k[0], o.up_t, O.ZERO if o.tpad == C.TPAD_ZERO else O.REPLICATE)
+            for i, o in enumerate(ops) if o.kind == C.OP_CONV}
     rng = np.random.RandomState(seed)
     worst = {}
     outs, t0 = [], 0
@@ -175,8 +185,13 @@ def run_stack_sampled(ops, params_cpu, x_cl, cin, h, w, splits, seed, max_pts_ro
                 g = None
                 if act is not None:
                     g = params_cpu["__gain_of_act_%d" % o.act_out]
+                # a temporal stride's first output is the window's first frame only on
+                # the video's first chunk (the first frame on its own)
+                tf = 0 if (o.stride_t == 1 or first) else 1
+                if o.name == "conv_in" and p["w"].shape[1] != o.w.shape[1]:
+                    z = z[..., :p["w"].shape[1]]  # the pixels' real channels (the rest are zero)
                 check_conv(z, p["w"], p["b"], o.up_s, ts, rows, cols, out=out, res=res, act=act, gamma=g,
-                           tallies=tal)
+                           tallies=tal, down=o.stride_s, t_stride=o.stride_t, t_first=tf)
             else:
                 check_norm(src, act, to_oracle(o.gamma.cpu()), ts, rows, cols, res=res, out=out, tallies=tal)
             for k in ("out", "act"):
@@ -452,3 +467,45 @@ def test_c4_decoder_fullsize_folded_sampled():
                                    max_pts_rows=8, fold_upsample=True)
     assert got.shape == (OM.output_frames(sum(splits)), 1440, 2560, 3)
     assert all("%s.out" % k in worst for k in ("s0.up", "s1.up", "s2.up"))
+
+
+def test_e4_encoder_fullsize_sampled():
+    """The encoder at its full size, pixels 3 (+5 zero channels) x 1440x2560 ->
+    48 x 90x160 latents, zero history: the first two chunks (25 then 24 frames:
+    the first frame on its own, then pairs at each temporal stride), every op
+    checked on sampled outputs (the strided tile included); then the production
+    slot wiring must give bitwise the same latents."""
+    say("full size e4")
+    h, w, c_pix, c_in = 1440, 2560, 3, 8
+    dev, cpu = {}, {}
+    for i, (name, co, ci, kt, kh, kw, has_g, _, _) in enumerate(OM.encoder_layer_shapes(c_in=c_pix)):
+        d, c = _param_pair(co, ci, 6, i, has_g)
+        if name == "conv_in":
+            wp = torch.zeros((co, c_in, kt, kh, kw), dtype=d["w"].dtype, device=d["w"].device)
+            wp[:, :c_pix] = d["w"]
+            d["w"] = wp
+        dev[name], cpu[name] = d, c
+    ops = S.encoder_ops(dev, unique_slots=True)
+    for o in ops:
+        o.tpad = C.TPAD_ZERO
+    _gains_of_acts(ops, cpu)
+    splits = [25, 24]
+    x = synth.bf16(synth.video(c_pix, sum(splits), h, w, synth.seed(6, 1)))
+    x_cl = torch.zeros((sum(splits), h, w, c_in), dtype=torch.bfloat16, device="cuda")
+    x_cl[..., :c_pix] = x.permute(1, 2, 3, 0).cuda()
+    del x
+    got, worst = run_stack_sampled(ops, cpu, x_cl, c_in, h, w, splits, seed=606, max_pts_rows=6)
+    assert got.shape == (13, 90, 160, 48)  # 7 + 6 latents
+    torch.cuda.empty_cache()
+    say("  production wiring")
+    prod = S.encoder_ops(dev)
+    for o in prod:
+        o.tpad = C.TPAD_ZERO
+    plan = P.stack_plan(prod, c_in, h, w, max_chunk_t=max(splits))
+    st = P.Stream(plan)
+    t0, outs = 0, []
+    for n in splits:
+        outs.append(st.step(x_cl[t0:t0 + n].contiguous()).cpu())
+        t0 += n
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(outs), got), "production slot wiring differs from the unique-slot wiring"
