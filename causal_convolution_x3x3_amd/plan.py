@@ -209,7 +209,7 @@ def conv_plan(w: torch.Tensor, h_in: int, w_in: int, *, bias=None, gamma=None, u
 def conv_forward_noalloc(w: torch.Tensor, x: torch.Tensor, cache_in: State, cache_out: State, y: torch.Tensor,
                          *, bias=None, gamma=None, residual=None, up_s=1, up_t=1, max_chunk_t=8,
                          tpad=C.TPAD_REPLICATE, act=False, out_u8=False, eps=1e-6, aligned=False,
-                         fold_upsample=False, stream=None) -> torch.Tensor:
+                         fold_upsample=False, stride_s=1, stride_t=1, stream=None) -> torch.Tensor:
     """One conv chunk through cc3d_conv_forward_noalloc: the result of
     conv_plan(w, ...).forward_chunk(x, ...), with no device allocation (the
     library repacks the weights into its fixed per-device scratch).  The
@@ -228,12 +228,15 @@ def conv_forward_noalloc(w: torch.Tensor, x: torch.Tensor, cache_in: State, cach
                    up_t=up_t, max_chunk_t=max_chunk_t, dtype=_DT[w.dtype], tpad=tpad,
                    epilogue=(C.EPI_RESIDUAL if residual is not None else 0) | (C.EPI_ACT if act else 0) |
                    (C.EPI_U8 if out_u8 else 0), eps=eps, grow=C.GROW_ALIGNED if aligned else C.GROW_ONCE,
-                   fold_upsample=int(fold_upsample))
+                   fold_upsample=int(fold_upsample), stride_s=stride_s, stride_t=stride_t)
     first = cache_in.frames_seen == 0
     t = x.shape[0]
     grow = up_t == 2 and first and not aligned
     t_out = (2 * t - 1 if grow else 2 * t) if up_t == 2 else t
-    want = (t_out, x.shape[1] * up_s, x.shape[2] * up_s, cout)
+    if stride_t == 2:  # (a length that leaves half a frame is refused by the library)
+        t_out = (t + 1) // 2 if (first and not aligned) else t // 2
+    hw = (x.shape[1] * up_s, x.shape[2] * up_s) if stride_s == 1 else ((x.shape[1] + 1) // 2, (x.shape[2] + 1) // 2)
+    want = (t_out,) + hw + (cout,)
     out_dtype = torch.uint8 if out_u8 else w.dtype
     if tuple(y.shape) != want or y.dtype != out_dtype:
         raise ValueError("y must be %s of %s, got %s of %s" % (want, out_dtype, tuple(y.shape), y.dtype))

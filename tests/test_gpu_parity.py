@@ -1308,6 +1308,33 @@ def _ntile(cout):
     return 96 if cout % 96 == 0 else (128 if cout % 128 == 0 else 64)
 
 
+def _random_strided_cases(n, seed):
+    """Seeded strided convs: kernel shapes, channel counts (the register-blocked
+    strided tile and the generic kernel), spatial and/or temporal stride, both
+    temporal phases, frame sizes from one pixel, chunkings that keep every count
+    whole (phase 0: an odd first chunk, even later ones; phase 1: even chunks),
+    history fills, bias, residual and act."""
+    rng = np.random.RandomState(seed)
+    cases = []
+    for _ in range(n):
+        k = [(3, 3, 3), (3, 3, 3), (1, 1, 1), (3, 1, 1), (2, 3, 3)][rng.randint(5)]
+        cin = int(rng.choice([8, 16, 32, 64, 96]))
+        cout = int(rng.choice([8, 16, 24, 64, 96, 128, 192, 256]))
+        ss, st = [(2, 1), (1, 2), (2, 2), (2, 2)][rng.randint(4)]
+        aligned = bool(rng.randint(2)) if st == 2 else False
+        h, w = int(rng.randint(1, 20)), int(rng.randint(1, 80))
+        nch = int(rng.randint(1, 4))
+        if st == 2:
+            splits = [2 * int(rng.randint(1, 3)) - (0 if aligned else 1)] + [2 * int(rng.randint(1, 3))
+                                                                          for _ in range(nch - 1)]
+        else:
+            splits = [int(v) for v in rng.randint(1, 4, size=nch)]
+        tpad = [C.TPAD_REPLICATE, C.TPAD_ZERO][rng.randint(2)]
+        epi = [(False, False), (True, False), (False, True), (True, True)][rng.randint(4)]
+        cases.append((cin, cout, k, ss, st, h, w, splits, tpad, aligned, bool(rng.randint(2)), epi[0], epi[1]))
+    return cases
+
+
 def _strided_ref(x, wt, b, tpad, splits, ss, st, aligned, r=None, g=None):
     v = O.chunked(to_oracle(x), to_oracle(wt), None if b is None else to_oracle(b), TP[tpad], splits=splits,
                   aligned=aligned, stride_s=ss, stride_t=st)
@@ -1316,8 +1343,10 @@ def _strided_ref(x, wt, b, tpad, splits, ss, st, aligned, r=None, g=None):
     return v if g is None else O.act(O.round_bf16(v), to_oracle(g), 1e-6)
 
 
-@pytest.mark.parametrize("case", STRIDED_CASES, ids=lambda c: "ci%d_co%d_k%s_s%d_t%d_%dx%d_al%d" % (
-    c[0], c[1], "".join(map(str, c[2])), c[3], c[4], c[5], c[6], c[9]))
+@pytest.mark.parametrize("case", STRIDED_CASES + _random_strided_cases(16, 13),
+                         ids=lambda c: "ci%d_co%d_k%s_s%d_t%d_%dx%d_al%d_%s" % (
+                             c[0], c[1], "".join(map(str, c[2])), c[3], c[4], c[5], c[6], c[9],
+                             "-".join(map(str, c[7]))))
 def test_bf16_strided_conv_vs_oracle(case):
     cin, cout, k, ss, st, h, w, splits, tpad, aligned, with_bias, residual, act = case
     say("bf16 strided conv %s" % (case,))

@@ -99,3 +99,31 @@ def test_noalloc_refuses_a_conv_beyond_the_scratch():
     assert e.value.status == C.ENOMEM and "scratch" in str(e.value)
     torch.cuda.synchronize()
     assert bool((y == 3.0).all()) and b.frames_seen == 0
+
+
+def test_noalloc_strided_matches_the_plan_path():
+    """A strided conv (spatial and temporal stride 2, the register-blocked
+    kernel's strided tile, fused act) through the no-alloc entry point: a 3-frame
+    first chunk then a 2-frame one (smaller), bit for bit the plan path's."""
+    say("no-alloc: strided conv")
+    cin, cout, h, w, chunks = 64, 96, 14, 70, (3, 2)
+    wt, gamma, bias, x, _ = _inputs(cin, cout, h, w, sum(chunks), True, False, 1, 70)
+    plan = P.conv_plan(wt, h, w, bias=bias, gamma=gamma, max_chunk_t=3, act=True, stride_s=2, stride_t=2)
+    st = P.Stream(plan)
+    refs, t0 = [], 0
+    for n in chunks:
+        refs.append(st.step(x[t0:t0 + n].contiguous()).clone())
+        t0 += n
+    a, b = plan.new_state(), plan.new_state()
+    got, t0 = [], 0
+    for k, n in enumerate(chunks):
+        src, dst = (a, b) if k % 2 == 0 else (b, a)
+        y = torch.full(plan.output_shape(n, src.frames_seen == 0), -7.0, dtype=torch.bfloat16, device="cuda")
+        P.conv_forward_noalloc(wt, x[t0:t0 + n].contiguous(), src, dst, y, bias=bias, gamma=gamma, max_chunk_t=3,
+                               act=True, stride_s=2, stride_t=2)
+        got.append(y)
+        t0 += n
+    torch.cuda.synchronize()
+    assert got[0].shape == (2, 7, 35, 96) and got[1].shape == (1, 7, 35, 96)
+    for k in range(2):
+        assert torch.equal(got[k], refs[k]), "chunk %d differs from the plan path" % k
