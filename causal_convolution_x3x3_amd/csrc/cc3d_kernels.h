@@ -37,7 +37,7 @@ struct ConvArgs {
     int h_in, w_in, up_s, h_out, w_out, t_out;
     int kchunks;          // bf16: ceil(cin / 32)
     int ntile, nblocks;   // bf16: output channels per workgroup, number of such blocks
-    int family;           // bf16: kernel family (1 to 5) the weights were packed for
+    int family;           // bf16: kernel family (1 to 6) the weights were packed for
     int rot_taps;         // bf16 v2 and pointwise: rotate the temporal-tap order by the output frame
     int t_rot0;           // ... counted from this frame (the launch's first frame in its chunk)
     int out_u8;           // bf16 families 1 and 3: out holds 8-bit codes of the fp32 result

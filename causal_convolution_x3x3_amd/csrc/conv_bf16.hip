@@ -225,11 +225,14 @@ hipError_t launch_nf(const ConvArgs& a, hipStream_t s)
 // kh*kw spatial taps, each NTILE rows of 32 channels with the 16-byte chunks
 // swizzled as in LDS.  Spatial taps are ordered row-major (b, d), or column
 // major (d, b) for the v2 kernels, whose sub-steps take one column tap at a time.
+// tfold (8 input channels, family 6): one K step whose 8-channel group g holds
+// temporal tap g (K index 8 g + c = tap g, channel c; the fourth group zeros).
 __global__ void pack_bf16_kernel(const uint16_t* w, uint16_t* wpk, int cout, int cin, int kt,
-                                 int kh, int kw, int ntile, int nblocks, int kchunks, int dmajor)
+                                 int kh, int kw, int ntile, int nblocks, int kchunks, int dmajor, int tfold)
 {
     const int taps = kh * kw;
-    const int64_t total = (int64_t)nblocks * kt * kchunks * taps * ntile * 32;
+    const int kt_steps = tfold ? 1 : kt;
+    const int64_t total = (int64_t)nblocks * kt_steps * kchunks * taps * ntile * 32;
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * blockDim.x) {
         const int e = (int)(idx & 31);
@@ -240,16 +243,20 @@ __global__ void pack_bf16_kernel(const uint16_t* w, uint16_t* wpk, int cout, int
         row /= taps;
         const int kc = (int)(row % kchunks);
         row /= kchunks;
-        const int ta = (int)(row % kt);
-        const int nb = (int)(row / kt);
+        int ta = (int)(row % kt_steps);
+        const int nb = (int)(row / kt_steps);
         const int gphys = e >> 3, el = e & 7;
         const int glog = gphys ^ swz(nl);
         const int n = nb * ntile + nl;
-        const int c = kc * 32 + glog * 8 + el;
+        int c = kc * 32 + glog * 8 + el;
+        if (tfold) {
+            ta = glog;
+            c = el;
+        }
         const int b = dmajor ? tap % kh : tap / kw;
         const int d = dmajor ? tap / kh : tap % kw;
         uint16_t v = 0;
-        if (n < cout && c < cin) v = w[((((int64_t)n * cin + c) * kt + ta) * kh + b) * kw + d];
+        if (n < cout && c < cin && ta < kt) v = w[((((int64_t)n * cin + c) * kt + ta) * kh + b) * kw + d];
         wpk[idx] = v;
     }
 }
@@ -300,7 +307,7 @@ size_t bf16_packed_elems(int cout, int cin, int kt, int kh, int kw, int family)
     int nt, nb;
     bf16_conv_tiling(cout, &nt, &nb);
     const int kchunks = (cin + 31) / 32;
-    return (size_t)nb * kt * kchunks * kh * kw * nt * 32;
+    return (size_t)nb * (family == 6 ? 1 : kt) * kchunks * kh * kw * nt * 32;
 }
 
 hipError_t launch_pack_bf16(const void* w, void* wpk, int cout, int cin, int kt, int kh, int kw,
@@ -315,9 +322,9 @@ hipError_t launch_pack_bf16(const void* w, void* wpk, int cout, int cin, int kt,
     const size_t total = bf16_packed_elems(cout, cin, kt, kh, kw, family);
     int blocks = (int)((total + 255) / 256);
     if (blocks > 65536) blocks = 65536;
-    const int dmajor = family == 2 ? 1 : 0;
+    const int dmajor = (family == 2 || family == 6) ? 1 : 0;
     hipLaunchKernelGGL(pack_bf16_kernel, dim3(blocks), dim3(256), 0, s, (const uint16_t*)w,
-                       (uint16_t*)wpk, cout, cin, kt, kh, kw, nt, nb, kchunks, dmajor);
+                       (uint16_t*)wpk, cout, cin, kt, kh, kw, nt, nb, kchunks, dmajor, family == 6 ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -327,7 +334,7 @@ hipError_t launch_conv_bf16(const ConvArgs& a, hipStream_t s)
     if (a.family == 3) return launch_conv_head(a, s);
     if (a.family == 4) return launch_conv_pw(a, s);
     if (a.family == 5) return launch_conv_phase(a, s);
-    if (a.family == 2) return launch_conv_bf16_v2(a, s);
+    if (a.family == 2 || a.family == 6) return launch_conv_bf16_v2(a, s);
     if (a.t_stride < 1 || a.t_stride > 2 || (a.down_s != 1 && a.down_s != 2) || (a.down_s == 2 && a.up_s != 1))
         return hipErrorInvalidValue;
     if (a.down_s == 2) return a.kh == 3 ? launch_nf<1, 2, 3>(a, s) : launch_nf<1, 2, 1>(a, s);

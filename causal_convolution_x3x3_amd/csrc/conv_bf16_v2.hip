@@ -39,6 +39,11 @@
 //   for d = 1), and LDS row s serves output rows (s - b) / 2 for the row taps b
 //   of the same parity.  Output frame t reads window frames
 //   t_stride*t + t_first + (0 .. kt-1).
+// * Folded temporal taps (TF, 8 input channels: the pixels padded to 8): the
+//   K step's four 8-channel groups are the window frames t_stride*t + t_first
+//   + g (g < kt; the fourth is zero), so the whole K is one step.  The LDS tile
+//   is then planar, one plane of pixels per group, each plane a whole number of
+//   64-slot rounds so that every wave's load reads one frame.
 #include "cc3d_device.h"
 
 namespace cc3d {
@@ -78,10 +83,11 @@ struct Geo<2, RH> {  // tile: 4 RH source rows x 16 source columns; M-wave w: so
 // is a base register plus a constant (the chunk swizzle depends on the column
 // only).  Weights are prefetched two sub-steps ahead (three LDS buffers; two,
 // one sub-step ahead, where three do not fit), the input tile one K step ahead.
-template <int UP, int NF, int WN, int RH, int DOWN>
+template <int UP, int NF, int WN, int RH, int DOWN, int TF>
 __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
 {
     static_assert(DOWN == 1 || UP == 1, "a conv either upsamples or strides");
+    static_assert(TF == 0 || DOWN == 2, "folded temporal taps: the strided tile only");
     using G = Geo<UP, RH>;
     constexpr int NT = 256 * WN;        // threads
     constexpr int NFW = NF / WN;        // N fragments per wave
@@ -90,9 +96,10 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     constexpr int LW = DOWN == 2 ? 2 * G::TS_W + 1 : G::TS_W + 2;
     constexpr int NE = (LW + 1) / 2;  // DOWN = 2: even input columns, stored first
     constexpr int LWP = (LW + 1) / 2 * 2;  // row pitch (pixels)
-    constexpr int ROWB = LWP * 64;          // bytes per LDS row
+    constexpr int PL = (LH * LWP + 63) / 64 * 64;  // TF: pixels per plane, whole 64-slot rounds
+    constexpr int ROWB = TF ? LWP * 16 : LWP * 64;  // bytes per LDS row (TF: of one plane)
     constexpr int NTILE = 16 * NF;
-    constexpr int A_CH = LH * LWP * 4;      // 16-byte slots of one LDS tile buffer
+    constexpr int A_CH = TF ? 4 * PL : LH * LWP * 4;  // 16-byte slots of one LDS tile buffer
     constexpr int B_CH = 3 * NTILE * 4;     // 16-byte slots of one column tap's weights
     constexpr int A_IT = (A_CH + NT - 1) / NT;  // tile load rounds (16 bytes per lane)
     constexpr int A_PAD = A_IT * NT;            // tile buffer slots: whole rounds
@@ -145,7 +152,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
 #pragma unroll
         for (int f = 0; f < NFW; ++f) acc[m][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nsteps = a.kt * a.kchunks;
+    const int nsteps = TF ? 1 : a.kt * a.kchunks;
     const int nsub = nsteps * 3;
     const uint32_t frame_bytes = (uint32_t)(a.z.frame_elems * 2);
     const __amdgpu_buffer_rsrc_t wr =
@@ -161,7 +168,16 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
         const int slot = tid + NT * it;
         a_off[it] = OOB;
         a_ch[it] = 0;
-        if (slot < A_CH) {
+        if (TF && slot < A_CH) {
+            // plane gg = window frame gg (the pixel's 8 channels)
+            const int gg = slot / PL, pix = slot - gg * PL;
+            const int r = pix / LWP, c = pix - r * LWP;
+            a_ch[it] = gg;
+            const int ci = c < NE ? 2 * c : 2 * (c - NE) + 1;
+            const int gy = DOWN * i0 + r - 1, gx = DOWN * j0 + ci - 1;
+            if (pix < LH * LWP && c < LW && gy >= 0 && gy < a.h_in && gx >= 0 && gx < a.w_in)
+                a_off[it] = (uint32_t)((gy * a.w_in + gx) * a.cin * 2);
+        } else if (!TF && slot < A_CH) {
             const int pix = slot >> 2;
             const int r = pix / LWP, c = pix - r * LWP;
             const int gg = (slot & 3) ^ swz(c);
@@ -180,7 +196,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     // order as a whole-chunk one), so the
     // workgroups of frames t, t+1, t+2 -- which run at the same time -- read the
     // same input frame in the same step and share it in L2.
-    const int rot = a.rot_taps ? (a.kt - (a.t_rot0 + tz0) % a.kt) % a.kt : 0;
+    const int rot = (!TF && a.rot_taps) ? (a.kt - (a.t_rot0 + tz0) % a.kt) % a.kt : 0;  // TF: one step
     auto phys_step = [&](int step) -> int {
         const int ta = step / a.kchunks, kc = step - ta * a.kchunks;
         const int tr = ta + rot < a.kt ? ta + rot : ta + rot - a.kt;
@@ -188,6 +204,16 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     };
     auto phys_sub = [&](int sub) -> int { return phys_step(sub / 3) * 3 + sub % 3; };
     auto issue_a = [&](int lstep, uint4* buf) {
+        if (TF) {
+            // one frame per load round and wave (the plane of its 64 slots)
+#pragma unroll
+            for (int it = 0; it < A_IT; ++it) {
+                const int f = __builtin_amdgcn_readfirstlane(a_ch[it]);
+                const uint16_t* fp = f < a.kt ? zframe(a.z, tz0 + f) : nullptr;
+                load_to_lds(make_rsrc(fp, fp ? frame_bytes : 0u), a_off[it], buf + NT * it + wave * 64);
+            }
+            return;
+        }
         const int step = phys_step(lstep);
         const int ta = step / a.kchunks, kc = step - ta * a.kchunks;
         const uint16_t* fp = zframe(a.z, tz0 + ta);
@@ -212,7 +238,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
                          (char*)buf + RB16 * NT * 16 + (it * NT + wave * 64) * 4);
     };
     // byte offset of this lane's 16-byte chunk at LDS column `col` of row 0
-    auto col_off = [&](int col) -> int { return col * 64 + ((g ^ swz(col)) << 4); };
+    auto col_off = [&](int col) -> int { return TF ? (g * PL + col) * 16 : col * 64 + ((g ^ swz(col)) << 4); };
     auto lds_frag = [&](const uint4* base, int byte_off) -> bf16x8 {
         return as_bf16x8(*(const uint4*)((const char*)base + byte_off));
     };
@@ -537,7 +563,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     if (live) process(w);
 }
 
-template <int UP, int NF, int WN, int RH, int DOWN = 1>
+template <int UP, int NF, int WN, int RH, int DOWN = 1, int TF = 0>
 hipError_t launch_v2(const ConvArgs& a, hipStream_t s)
 {
     using G = Geo<UP, RH>;
@@ -546,7 +572,7 @@ hipError_t launch_v2(const ConvArgs& a, hipStream_t s)
     const int64_t total = (int64_t)tiles * a.t_out * a.nblocks;
     if (total <= 0 || total > (int64_t)0x7fffffff - 8) return hipErrorInvalidValue;
     const int64_t grid = ((total + 7) / 8) * 8;
-    hipLaunchKernelGGL((conv3_v2_kernel<UP, NF, WN, RH, DOWN>), dim3((unsigned)grid), dim3(256 * WN), 0, s, a);
+    hipLaunchKernelGGL((conv3_v2_kernel<UP, NF, WN, RH, DOWN, TF>), dim3((unsigned)grid), dim3(256 * WN), 0, s, a);
     return hipGetLastError();
 }
 
@@ -564,8 +590,13 @@ hipError_t launch_conv_bf16_v2(const ConvArgs& a, hipStream_t s)
         // spatial stride 2: 2 output rows x 64 columns per tile (5 x 130 input
         // pixels in LDS, double-buffered, beside the weight buffers)
         if (a.up_s != 1 || a.t_stride < 1 || a.t_stride > 2) return hipErrorInvalidValue;
+        if (a.family == 6) {  // 8 input channels, temporal taps folded into the K step
+            if (a.cin != 8 || a.kt > 3) return hipErrorInvalidValue;
+            return a.ntile == 96 ? launch_v2<1, 6, 2, 2, 2, 1>(a, s) : launch_v2<1, 8, 2, 2, 2, 1>(a, s);
+        }
         return a.ntile == 96 ? launch_v2<1, 6, 2, 2, 2>(a, s) : launch_v2<1, 8, 2, 2, 2>(a, s);
     }
+    if (a.family == 6) return hipErrorInvalidValue;
     if (a.t_stride != 1 || a.t_first != 0) return hipErrorInvalidValue;  // temporal stride: family 1
     // up_s = 1, 96-channel blocks: 9 output rows per wave (a 9 x 64 tile per
     // workgroup, weights three buffers deep in LDS).  Measured against 8 rows

@@ -1290,6 +1290,11 @@ STRIDED_CASES = [
     (96, 96, (3, 3, 3), 2, 2, 8, 256, [1, 2], C.TPAD_ZERO, False, True, True, True),
     (64, 128, (3, 3, 3), 2, 2, 1, 2, [2, 2], C.TPAD_REPLICATE, True, True, False, False),
     (192, 384, (3, 3, 3), 2, 2, 6, 9, [1, 4], C.TPAD_ZERO, False, True, False, True),
+    # 8 input channels (pixels padded to 8): temporal taps folded into one K step,
+    # k_t 3 and 2, both phases, 96 and 128 channels, ragged tiles, one-frame chunks
+    (8, 96, (3, 3, 3), 2, 1, 19, 133, [1, 1, 2], C.TPAD_REPLICATE, False, True, True, True),
+    (8, 128, (2, 3, 3), 2, 2, 9, 70, [3, 2], C.TPAD_ZERO, False, False, False, False),
+    (8, 256, (3, 3, 3), 2, 2, 8, 64, [2, 2], C.TPAD_ZERO, True, True, False, False),
 ]
 
 
@@ -1368,8 +1373,10 @@ def test_bf16_strided_conv_vs_oracle(case):
     pr = C.OpProfile()
     C.check(C.lib().cc3d_profile_read(plan._h, 0, 0, ctypes.byref(pr)), "profile_read")
     # 3x3 spatial stride 2 in 96/128-channel blocks: the register-blocked kernel
+    # (with 8 input channels, its temporal taps folded into one K step)
     v2 = ss == 2 and k[1:] == (3, 3) and _ntile(cout) in (96, 128)
-    assert pr.kernel.decode().startswith("conv_bf16%s_s%dt%d_k%d" % ("_v2" if v2 else "", ss, st, k[1])), pr.kernel
+    fam = ("_v2tf" if cin == 8 else "_v2") if v2 else ""
+    assert pr.kernel.decode().startswith("conv_bf16%s_s%dt%d_k%d" % (fam, ss, st, k[1])), pr.kernel
     assert got.shape == (cout, t_out, ho, wo)
     assert_bf16_close(got, ref, "strided conv")
 
