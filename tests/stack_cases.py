@@ -72,6 +72,30 @@ STACK_CASES = {
 }
 for _i, (_cl, _st, _t, _h, _w, _sp, _tg, _al, _fold) in enumerate(RANDOM_CASES):
     STACK_CASES["random%d" % _i] = case(_cl, _st, _t, _h, _w, _sp, cfg=9, tg=_tg, aligned=_al)
+def random_encoder_cases(n, seed):
+    """Seeded encoder configurations: two or three stages of random widths and
+    temporal factors, latent width, frame size, history fill, phase, and chunks
+    that keep every strided layer's count whole (with m = 2^(temporal strides):
+    a first chunk of 1 mod m frames then multiples of m; all multiples of m with
+    the aligned rule)."""
+    rng = np.random.RandomState(seed)
+    cases = []
+    for _ in range(n):
+        nst = int(rng.randint(2, 4))
+        stages = tuple((int(rng.choice([16, 32, 64, 96, 128, 192])), int(rng.randint(1, 3))) for _ in range(nst))
+        m = 2 ** sum(1 for _, f in stages if f == 2)
+        aligned = bool(rng.randint(2))
+        first = m * int(rng.randint(1, 3)) if aligned else 1 + m * int(rng.randint(0, 2))
+        splits = [first] + [m * int(rng.randint(1, 3)) for _ in range(int(rng.randint(0, 3)))]
+        c_lat = int(rng.choice([8, 16, 48]))
+        h, w = int(rng.randint(1, 40)), int(rng.randint(1, 60))
+        mode = ["zero", "replicate"][rng.randint(2)]
+        c = enc_case(3, c_lat, stages, sum(splits), h, w, splits, cfg=7, aligned=aligned)
+        c["mode"] = mode
+        cases.append(c)
+    return cases
+
+
 STACK_CASES.update({
     # 1 + 4n frames with the first frame on its own (an odd first chunk, even later
     # ones at every temporal stride), or 4n with the aligned rule
@@ -80,6 +104,8 @@ STACK_CASES.update({
     "enc_full_tiny": enc_case(3, 48, FULL_STAGES, 5, 16, 16, (1, 4), cfg=9),
     "enc_full_aligned": enc_case(3, 48, FULL_STAGES, 8, 16, 24, (4, 4), cfg=9, aligned=True),
 })
+for _i, _c in enumerate(random_encoder_cases(6, 17)):
+    STACK_CASES["enc_random%d" % _i] = _c
 
 
 def layer_shapes(c):

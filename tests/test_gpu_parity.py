@@ -1098,7 +1098,7 @@ def test_conv_family_override_keeps_v1(monkeypatch):
     assert names[None] == "conv_bf16_v2_up1_k3_n96" and names["1"] == "conv_bf16_up1_k3_n96", names
 
 
-@pytest.mark.parametrize("kind", ["resblock", "growing_folded"])
+@pytest.mark.parametrize("kind", ["resblock", "growing_folded", "strided"])
 def test_graph_capture_replays_chunks(kind):
     """CDA-VSR page, "CUDA Graph inference": a chunk decode captured into a graph
     (fixed shapes, the two state arenas used alternately, no allocation, no host
@@ -1106,12 +1106,17 @@ def test_graph_capture_replays_chunks(kind):
     eagerly (its first-chunk rule is fixed when a launch is recorded); two graphs
     (state A -> B and B -> A) are then replayed in turn, with eager copies and a
     synchronisation between replays, and every replay is checked.  Stacks: a
-    residual block, and a phase-folded conv that doubles space and time."""
+    residual block, a phase-folded conv that doubles space and time, and a conv
+    that halves them (strides, every output from two new frames)."""
     say("graph capture of forward_chunk: %s" % kind)
     c, h, w, n, nch = 96, 10, 40, 4, 7
     if kind == "resblock":
         cpu, dev = _params([("c1", c, c, 3, 3, 3), ("c2", c, c, 3, 3, 3)], 12, lambda n_: True, with_bias=True)
         plan = P.stack_plan(S.resblock_ops(c, dev["c1"], dev["c2"]), c, h, w, max_chunk_t=n)
+    elif kind == "strided":
+        wt = synth.bf16(synth.conv_weight(c, c, 3, 3, 3, synth.seed(12, 8))).cuda()
+        ops = [P.Op(cout=c, w=wt, stride_s=2, stride_t=2, src=C.SLOT_X, out=C.SLOT_Y, name="down")]
+        plan = P.stack_plan(ops, c, h, w, max_chunk_t=n, aligned=True)
     else:
         wt = synth.bf16(synth.conv_weight(c, c, 3, 3, 3, synth.seed(12, 7))).cuda()
         ops = [P.Op(cout=c, w=wt, up_s=2, up_t=2, src=C.SLOT_X, out=C.SLOT_Y, name="up")]
@@ -1499,13 +1504,15 @@ def _encoder_case(name):
     return got, np.concatenate(ref, axis=1)
 
 
-@pytest.mark.parametrize("name", ["enc_small", "enc_small_aligned", "enc_full_tiny", "enc_full_aligned"])
+@pytest.mark.parametrize("name", [k for k in SC.STACK_CASES if k.startswith("enc_")])
 def test_encoder_layerwise_and_end_to_end(name):
     say("encoder %s" % name)
     c = SC.STACK_CASES[name]
     got, ref = _encoder_case(name)
-    n = c["t"]
+    n, h, w = c["t"], c["h"], c["w"]
+    for _ in range(len(c["stages"]) + 1):  # conv_in and every stage's down conv halve the frame
+        h, w = (h + 1) // 2, (w + 1) // 2
     for _, f in reversed(c["stages"]):
         n = O.strided_frames(n, f, c["aligned"])
-    assert got.shape == (c["c_lat"], n, -(-c["h"] // 16), -(-c["w"] // 16))
+    assert got.shape == (c["c_lat"], n, h, w)
     assert_stack_close(got, ref, name, "encoder")
