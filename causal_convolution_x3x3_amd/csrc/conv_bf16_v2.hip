@@ -112,7 +112,9 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     constexpr int RED = WN * 4 * MF * 16;       // epilogue reduction floats
     // weight buffers: 3 (prefetch distance 2) when they fit in LDS with the
     // double-buffered tile, else 2 (distance 1)
-    constexpr int NBB = (2 * A_PAD + 3 * B_CH) * 16 + RED * 4 <= 160 * 1024 ? 3 : 2;
+    // TF: one K step, so no tile is prefetched and the second tile buffer is unused
+    constexpr int NA = TF ? 1 : 2;
+    constexpr int NBB = (NA * A_PAD + 3 * B_CH) * 16 + RED * 4 <= 160 * 1024 ? 3 : 2;
     static_assert(NF % WN == 0, "N fragments split evenly over the N waves");
 
     // One LDS variable per buffer, and every load of the main loop issued
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     // the compiler's own waits then see exactly which loads are in flight, know
     // that the buffer being read is not one being filled, and add no waits.
     __shared__ uint4 lds_a0[A_PAD];
-    __shared__ uint4 lds_a1[A_PAD];
+    __shared__ uint4 lds_a1[TF ? 1 : A_PAD];
     __shared__ uint4 lds_b0[B_CH];
     __shared__ uint4 lds_b1[B_CH];
     __shared__ uint4 lds_b2[NBB == 3 ? B_CH : 1];
@@ -345,7 +347,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
             const uint4* bread = bcur == 0 ? lds_b0 : (bcur == 1 ? lds_b1 : lds_b2);
             uint4* bwrite = bnext == 0 ? lds_b0 : (bnext == 1 ? lds_b1 : lds_b2);
             issue_b(sub + NBB - 1 < nsub ? sub + NBB - 1 : nsub - 1, bwrite);
-            if (d == 0) issue_a(next_a, awrite);
+            if (!TF && d == 0) issue_a(next_a, awrite);
 
             // B fragments of taps (b, d), b = 0..2, for this wave's channels
             bf16x8 bq[3][NFW];
@@ -358,14 +360,16 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
             // Before the barrier: the weights of sub + 1 and, at d == 2, the
             // next tile must have landed.  Loads complete in issue order; the
             // loads issued after the ones needed may stay in flight.
+            // (TF issues no tile in the loop: AT = 0)
+            constexpr int AT = TF ? 0 : A_IT;
             if (NBB == 3) {
                 // the weights of sub + 1 were issued in sub - 1, before
-                // sub's weights (RB) and, at d <= 1, before the tile (A_IT)
+                // sub's weights (RB) and, at d <= 1, before the tile (AT)
                 if (d == 2) wait_vmcnt<RB>();
-                else wait_vmcnt<RB + A_IT>();
+                else wait_vmcnt<RB + AT>();
             } else {
                 // the weights of sub + 1 were issued in this sub-step, before the tile
-                if (d == 0) wait_vmcnt<A_IT>();
+                if (d == 0) wait_vmcnt<AT>();
                 else wait_vmcnt<0>();
             }
             // A bare barrier: the loads this barrier publishes were waited for
@@ -592,7 +596,8 @@ hipError_t launch_conv_bf16_v2(const ConvArgs& a, hipStream_t s)
         if (a.up_s != 1 || a.t_stride < 1 || a.t_stride > 2) return hipErrorInvalidValue;
         if (a.family == 6) {  // 8 input channels, temporal taps folded into the K step
             if (a.cin != 8 || a.kt > 3) return hipErrorInvalidValue;
-            return a.ntile == 96 ? launch_v2<1, 6, 2, 2, 2, 1>(a, s) : launch_v2<1, 8, 2, 2, 2, 1>(a, s);
+            // one K step: the tile is single-buffered, which leaves room for 4 rows
+            return a.ntile == 96 ? launch_v2<1, 6, 2, 4, 2, 1>(a, s) : launch_v2<1, 8, 2, 4, 2, 1>(a, s);
         }
         return a.ntile == 96 ? launch_v2<1, 6, 2, 2, 2>(a, s) : launch_v2<1, 8, 2, 2, 2>(a, s);
     }
