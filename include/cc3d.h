@@ -290,6 +290,8 @@ cc3d_status cc3d_reset(const cc3d_plan* plan, cc3d_state* state, void* stream);
  *            CC3D_EPI_RESIDUAL: shape of y), else must be NULL
  * y        : device output, shape from cc3d_output_shape; must not overlap x
  * x, y, residual and both arenas must be 16-byte aligned (CC3D_EINVAL otherwise).
+ * A t_chunk that would leave a strided conv a fractional frame count is refused
+ * (CC3D_ESHAPE; see "Strided convs"), like every other check before any work.
  * Returns without synchronising; later calls never modify a returned y. */
 cc3d_status cc3d_forward_chunk(const cc3d_plan* plan, const void* x, int t_chunk,
                                const cc3d_state* cache_in, cc3d_state* cache_out,
@@ -333,7 +335,8 @@ cc3d_status cc3d_to_channels_first(const void* src_thwc, void* dst_cthw, int c, 
  * residual must have, when the plan reads one); cc3d_slot_read copies an
  * intermediate slot's contents for that chunk (dst: device, at least c*t*h*w
  * elements of the plan dtype) on stream.  Used to inspect every layer of a stack
- * (layer-wise parity checks). */
+ * (layer-wise parity checks).  CC3D_ESHAPE for a t_chunk a strided conv of the
+ * plan cannot take. */
 cc3d_status cc3d_slot_shape(const cc3d_plan* plan, int slot, int t_chunk, int first, int* c, int* t,
                             int* h, int* w);
 cc3d_status cc3d_slot_read(const cc3d_plan* plan, int slot, int t_chunk, int first, void* dst,
