@@ -203,6 +203,9 @@ def _group_desc(ops, batch_from, frame_batch):
      C.EINVAL, "also written before"),
     # the group reads the residual argument
     (1, 2, [_conv_op(out=3), _conv_op(src=3, res=C.SLOT_AUX, out=C.SLOT_Y)], C.EINVAL, "residual argument"),
+    # a strided conv inside the group
+    (1, 2, [_conv_op(out=3), _conv_op(src=3, out=C.SLOT_Y, stride_s=2)], C.EINVAL, "strided"),
+    (1, 2, [_conv_op(out=3), _conv_op(src=3, out=C.SLOT_Y, stride_t=2)], C.EINVAL, "strided"),
 ])
 def test_frame_batch_rejects_bad_groups(batch_from, frame_batch, ops, status, needle):
     L = C.lib()
@@ -223,7 +226,9 @@ def test_valid_descriptors_pass_validation():
         pytest.skip("placeholder pointers: run without a GPU")
     L = C.lib()
     out = ctypes.c_void_p()
-    for kw in (dict(), dict(up_s=2, up_t=2, grow=C.GROW_ALIGNED), dict(kt=3, kh=1, kw=1, cout=192, cin=96)):
+    for kw in (dict(), dict(up_s=2, up_t=2, grow=C.GROW_ALIGNED), dict(kt=3, kh=1, kw=1, cout=192, cin=96),
+               dict(stride_s=2, stride_t=2), dict(stride_s=0, stride_t=0), dict(cin=8, cout=96, stride_s=2),
+               dict(kh=1, kw=1, stride_s=2, up_t=2)):
         st = L.cc3d_plan_create(ctypes.byref(_conv_desc(**kw)), DUMMY, None, None, None, ctypes.byref(out))
         assert st == C.EDEVICE, C.last_error()
     d, keep = _stack([_conv_op(out=3), _conv_op(src=3, out=C.SLOT_Y)], batch_from=1, frame_batch=2)
