@@ -132,7 +132,8 @@ def _op_descs(ops):
         kt, kh, kw = o.k
         arr[i] = C.OpDesc(kind=o.kind, cout=o.cout, kt=kt, kh=kh, kw=kw, up_s=o.up_s, up_t=o.up_t, tpad=o.tpad,
                           src=o.src, res=o.res, out=o.out, act_out=o.act_out, w=DUMMY if o.w is not None else None,
-                          bias=None, gamma=DUMMY if o.gamma is not None else None, out_u8=int(o.out_u8))
+                          bias=None, gamma=DUMMY if o.gamma is not None else None, out_u8=int(o.out_u8),
+                          stride_s=o.stride_s, stride_t=o.stride_t)
     arr[len(ops)] = _conv_op(kind=9)
     return arr
 
@@ -161,6 +162,34 @@ def test_decoder_wiring_passes_library_checks(temporal_grow, aligned):
         assert o.k == ((1, 1, 1) if o.name.endswith(".p") else (3, 1, 1))
     arr = _op_descs(ops)
     d = C.StackDesc(dtype=C.BF16, cin=16, h=3, w=5, max_chunk_t=4, eps=1e-6, n_ops=len(ops) + 1, ops=arr,
+                    grow=C.GROW_ALIGNED if aligned else C.GROW_ONCE)
+    out = ctypes.c_void_p()
+    st = C.lib().cc3d_stack_plan_create(ctypes.byref(d), None, ctypes.byref(out))
+    assert st == C.EINVAL and ("op %d: kind 9" % len(ops)) in C.last_error(), C.last_error()
+
+
+@pytest.mark.parametrize("stages", [((64, 2), (32, 2), (16, 1)), ((384, 2), (192, 2), (96, 1)), ((32, 1), (16, 2))])
+@pytest.mark.parametrize("aligned", [False, True])
+def test_encoder_wiring_passes_library_checks(stages, aligned):
+    """The encoder op lists (the decoder read backwards: stride-2 convs, temporal
+    strides, 8-channel pixels) pass every shape and wiring check of the library
+    under either temporal phase: creation fails only at the bad op appended
+    after them."""
+    import torch
+    from causal_convolution_x3x3_amd import plan as P
+    from causal_convolution_x3x3_amd import stacks as S
+    from oracle import model as OM
+    params = {}
+    for name, co, ci, kt, kh, kw, g, _, _ in OM.encoder_layer_shapes(c_in=8, stages=stages, c_latent=16):
+        params[name] = {"w": torch.empty((co, ci, kt, kh, kw), dtype=torch.bfloat16),
+                        "g": torch.empty(ci) if g else None}
+    ops = S.encoder_ops(params, stages=stages, c_latent=16)
+    P._check_weights(ops, 8, torch.bfloat16)
+    strided = [o for o in ops if o.stride_s == 2]
+    assert [o.name for o in strided] == ["conv_in"] + ["e%d.down" % i for i in range(len(stages))]
+    assert [o.stride_t for o in strided[1:]] == [f for _, f in reversed(stages)]
+    arr = _op_descs(ops)
+    d = C.StackDesc(dtype=C.BF16, cin=8, h=37, w=50, max_chunk_t=9, eps=1e-6, n_ops=len(ops) + 1, ops=arr,
                     grow=C.GROW_ALIGNED if aligned else C.GROW_ONCE)
     out = ctypes.c_void_p()
     st = C.lib().cc3d_stack_plan_create(ctypes.byref(d), None, ctypes.byref(out))
