@@ -359,6 +359,13 @@ cc3d_status build_graph(const cc3d_stack_desc* d, cc3d_plan* p)
                     // 8 input channels (pixels padded to 8): the temporal taps fold into
                     // one 32-channel K step
                     if (r.family == 2 && r.cin == 8 && o.kt <= 3) r.family = 6;
+                    // output channels a multiple of 192: the strided tile in 192-channel
+                    // blocks (twice the MFMAs per LDS fragment read of the 96-channel one)
+                    if (r.family == 2 && o.cout % 192 == 0) {
+                        r.family = 7;
+                        r.ntile = 192;
+                        r.nblocks = o.cout / 192;
+                    }
                 }
                 if (r.family == 4) cc3d::pw_conv_tiling(o.cout, &r.ntile, &r.nblocks);
             }
@@ -541,7 +548,8 @@ void pair_cache_writers(cc3d_plan* p)
         if (w.kind == CC3D_OP_NORM_ACT) norm = true;
         else if (act) norm = !w.fused_act;
         else norm = false;  // the conv kernel writes its result slot
-        if (!norm && !(p->dtype == CC3D_BF16 && (w.family == 2 || w.family == 5 || w.family == 6))) continue;
+        if (!norm && !(p->dtype == CC3D_BF16 && (w.family == 2 || w.family == 5 || w.family == 6 ||
+                                                  w.family == 7))) continue;
         w.cache_to = j;
         w.cache_norm = norm;
         w.cache_act = act;
@@ -784,7 +792,8 @@ std::string conv_kernel_name(const cc3d_plan* p, const OpRt& r)
         snprintf(buf, sizeof buf, "conv_bf16_pw_up%d_kt%d_n%d", r.up_s, r.kt, r.ntile);
     else if (p->dtype == CC3D_BF16 && (r.stride_s > 1 || r.stride_t > 1))
         snprintf(buf, sizeof buf, "conv_bf16%s_s%dt%d_k%d_n%d",
-                 r.family == 6 ? "_v2tf" : (r.family == 2 ? "_v2" : ""), r.stride_s, r.stride_t, r.kh, r.ntile);
+                 r.family == 6 ? "_v2tf" : ((r.family == 2 || r.family == 7) ? "_v2" : ""), r.stride_s, r.stride_t,
+                 r.kh, r.ntile);
     else if (p->dtype == CC3D_BF16)
         snprintf(buf, sizeof buf, "conv_bf16%s_up%d_k%d_n%d", r.family == 2 ? "_v2" : "", r.up_s, r.kh,
                  r.ntile);

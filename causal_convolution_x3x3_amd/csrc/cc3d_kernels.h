@@ -37,17 +37,17 @@ struct ConvArgs {
     int h_in, w_in, up_s, h_out, w_out, t_out;
     int kchunks;          // bf16: ceil(cin / 32)
     int ntile, nblocks;   // bf16: output channels per workgroup, number of such blocks
-    int family;           // bf16: kernel family (1 to 6) the weights were packed for
+    int family;           // bf16: kernel family (1 to 7) the weights were packed for
     int rot_taps;         // bf16 v2 and pointwise: rotate the temporal-tap order by the output frame
     int t_rot0;           // ... counted from this frame (the launch's first frame in its chunk)
     int out_u8;           // bf16 families 1 and 3: out holds 8-bit codes of the fp32 result
-    // A later conv's cache written by this one (families 2 and 5): output frames
+    // A later conv's cache written by this one (families 2, 5, 6, 7): output frames
     // t >= cache_t0 of the result (cache_act = 0) or of the act (1) are also
     // stored as frame t - cache_t0 of `cache`, or null.
     void* cache;
     int cache_t0;
     int cache_act;
-    // Strided convs (bf16 family 1 and fp32): output pixel (y, x) is centred on
+    // Strided convs (bf16 families 1, 2, 6, 7 and fp32): output pixel (y, x) is centred on
     // input pixel (down_s*y, down_s*x); output frame t reads window frames
     // t_stride*t + t_first + (0 .. kt-1) of Z.  1, 1, 0 for every other conv.
     int down_s;
@@ -97,7 +97,10 @@ bool v2_conv_applies(int ntile, int kh, int kw, int up_s);
 // where it applies and `fold` != 0, 2 = v2 where it applies, 4 = the pointwise
 // kernel (conv_pw.hip) for 1x1 spatial kernels whose epilogue is plain (no act,
 // no 8-bit output: `plain` != 0), else 1.  CC3D_CONV_FAMILY=1 in the environment
-// at plan creation keeps every conv on v1.
+// at plan creation keeps every conv on v1.  Strided convs are assigned by the
+// host: 2 = v2's strided tile (96/128-channel blocks), 6 = the same with the
+// temporal taps folded into one K step (8 input channels), 7 = v2's strided
+// tile in 192-channel blocks (cout a multiple of 192), else 1.
 int bf16_conv_family(int cout, int cin, int kt, int kh, int kw, int up_s, int plain, int fold);
 hipError_t launch_conv_bf16_v2(const ConvArgs& a, hipStream_t s);
 

@@ -306,6 +306,10 @@ size_t bf16_packed_elems(int cout, int cin, int kt, int kh, int kw, int family)
     if (family == 5) return phase_packed_elems(cout, cin, kt);
     int nt, nb;
     bf16_conv_tiling(cout, &nt, &nb);
+    if (family == 7) {  // the strided tile in 192-channel blocks
+        nt = 192;
+        nb = (cout + 191) / 192;
+    }
     const int kchunks = (cin + 31) / 32;
     return (size_t)nb * (family == 6 ? 1 : kt) * kchunks * kh * kw * nt * 32;
 }
@@ -318,11 +322,15 @@ hipError_t launch_pack_bf16(const void* w, void* wpk, int cout, int cin, int kt,
     if (family == 5) return launch_pack_phase(w, wpk, cout, cin, kt, s);
     int nt, nb;
     bf16_conv_tiling(cout, &nt, &nb);
+    if (family == 7) {
+        nt = 192;
+        nb = (cout + 191) / 192;
+    }
     const int kchunks = (cin + 31) / 32;
     const size_t total = bf16_packed_elems(cout, cin, kt, kh, kw, family);
     int blocks = (int)((total + 255) / 256);
     if (blocks > 65536) blocks = 65536;
-    const int dmajor = (family == 2 || family == 6) ? 1 : 0;
+    const int dmajor = (family == 2 || family == 6 || family == 7) ? 1 : 0;
     hipLaunchKernelGGL(pack_bf16_kernel, dim3(blocks), dim3(256), 0, s, (const uint16_t*)w,
                        (uint16_t*)wpk, cout, cin, kt, kh, kw, nt, nb, kchunks, dmajor, family == 6 ? 1 : 0);
     return hipGetLastError();
@@ -334,7 +342,7 @@ hipError_t launch_conv_bf16(const ConvArgs& a, hipStream_t s)
     if (a.family == 3) return launch_conv_head(a, s);
     if (a.family == 4) return launch_conv_pw(a, s);
     if (a.family == 5) return launch_conv_phase(a, s);
-    if (a.family == 2 || a.family == 6) return launch_conv_bf16_v2(a, s);
+    if (a.family == 2 || a.family == 6 || a.family == 7) return launch_conv_bf16_v2(a, s);
     if (a.t_stride < 1 || a.t_stride > 2 || (a.down_s != 1 && a.down_s != 2) || (a.down_s == 2 && a.up_s != 1))
         return hipErrorInvalidValue;
     if (a.down_s == 2) return a.kh == 3 ? launch_nf<1, 2, 3>(a, s) : launch_nf<1, 2, 1>(a, s);

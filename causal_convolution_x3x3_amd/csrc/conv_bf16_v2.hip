@@ -58,23 +58,25 @@ __device__ __forceinline__ void decode_item(int w, int t_out, int nblocks, int& 
     tile = rest / t_out;
 }
 
-// Geometry of the two variants (per group of four waves along M); RH = output
+// Geometry of the two variants (per group of MW waves along M); RH = output
 // rows per wave for up_s = 1, source rows per wave for up_s = 2.
-template <int UP, int RH>
+template <int UP, int RH, int MW>
 struct Geo;
-template <int RH>
-struct Geo<1, RH> {  // tile: RH output rows x 64 columns; M-wave w: columns 16w..16w+15
-    static constexpr int TS_H = RH, TS_W = 64;
+template <int RH, int MW>
+struct Geo<1, RH, MW> {  // tile: RH output rows x 16 MW columns; M-wave w: columns 16w..16w+15
+    static constexpr int TS_H = RH, TS_W = 16 * MW;
     static constexpr int MF = RH;  // M fragments per wave: one per row
 };
-template <int RH>
-struct Geo<2, RH> {  // tile: 4 RH source rows x 16 source columns; M-wave w: source rows RH w .. RH w + RH-1
+template <int RH, int MW>
+struct Geo<2, RH, MW> {  // tile: 4 RH source rows x 16 source columns; M-wave w: source rows RH w .. RH w + RH-1
+    static_assert(MW == 4, "the upsampling tile has four waves along M");
     static constexpr int TS_H = 4 * RH, TS_W = 16;
     static constexpr int MF = 4 * RH;  // RH rows x 4 phases
 };
 
-// WN = waves along N: the workgroup has 4*WN waves (two per SIMD when WN = 2);
-// wave (wm, wn) computes M-wave wm's pixels for the NF/WN fragments of half wn.
+// MW = waves along M, WN = waves along N: the workgroup has MW*WN waves (8:
+// two per SIMD); wave (wm, wn) computes M-wave wm's pixels for the NF/WN
+// fragments of part wn.
 //
 // Staging: the input tile and the weights go from global memory straight into
 // LDS (buffer loads with the LDS flag), so no registers or LDS stores are spent
@@ -83,13 +85,14 @@ struct Geo<2, RH> {  // tile: 4 RH source rows x 16 source columns; M-wave w: so
 // is a base register plus a constant (the chunk swizzle depends on the column
 // only).  Weights are prefetched two sub-steps ahead (three LDS buffers; two,
 // one sub-step ahead, where three do not fit), the input tile one K step ahead.
-template <int UP, int NF, int WN, int RH, int DOWN, int TF>
-__global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
+template <int UP, int NF, int WN, int RH, int DOWN, int TF, int MW>
+__global__ __launch_bounds__(64 * MW * WN, 1) void conv3_v2_kernel(ConvArgs a)
 {
     static_assert(DOWN == 1 || UP == 1, "a conv either upsamples or strides");
     static_assert(TF == 0 || DOWN == 2, "folded temporal taps: the strided tile only");
-    using G = Geo<UP, RH>;
-    constexpr int NT = 256 * WN;        // threads
+    static_assert(MW == 2 || MW == 4, "two or four waves along M");
+    using G = Geo<UP, RH, MW>;
+    constexpr int NT = 64 * MW * WN;    // threads
     constexpr int NFW = NF / WN;        // N fragments per wave
     // LDS tile: the input rows and columns the tile's outputs read
     constexpr int LH = DOWN == 2 ? 2 * G::TS_H + 1 : G::TS_H + 2;
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     static_assert(RB4 * NT * 4 == (B_CH % NT) * 16, "weight blocks split into whole load rounds");
     constexpr int RB = RB16 + RB4;              // weight load instructions per wave
     constexpr int MF = G::MF;
-    constexpr int RED = WN * 4 * MF * 16;       // epilogue reduction floats
+    constexpr int RED = WN * MW * MF * 16;      // epilogue reduction floats
     // weight buffers: 3 (prefetch distance 2) when they fit in LDS with the
     // double-buffered tile, else 2 (distance 1)
     // TF: one K step, so no tile is prefetched and the second tile buffer is unused
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     const int tz0 = DOWN == 2 ? a.t_stride * t + a.t_first : t;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 3, wn = wave >> 2;
+    const int wm = wave & (MW - 1), wn = wave / MW;
     const int g = lane >> 4, k16 = lane & 15;
 
     f32x4 acc[MF][NFW];
@@ -411,7 +414,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
         if (a.cache_act) cact = cb;
         else craw = cb;
     }
-    float* red = lds_red;  // [WN][4 M-waves][MF][16 pixels]
+    float* red = lds_red;  // [WN][MW][MF][16 pixels]
     const bool vec_ok = (a.cout & 3) == 0;  // 4-channel groups never straddle cout
 
     auto pixel_of = [&](int m, int& y, int& x) {
@@ -504,7 +507,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
         if (act) {
             ss += __shfl_xor(ss, 16, 64);
             ss += __shfl_xor(ss, 32, 64);
-            if (g == 0) red[((wn * 4 + wm) * MF + m) * 16 + k16] = ss;
+            if (g == 0) red[((wn * MW + wm) * MF + m) * 16 + k16] = ss;
         }
     }
     if (!act) return;
@@ -524,7 +527,7 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
         const int64_t pbase = pixel_base(m, valid);
         float ss = 0.f;
 #pragma unroll
-        for (int h = 0; h < WN; ++h) ss += red[((h * 4 + wm) * MF + m) * 16 + k16];
+        for (int h = 0; h < WN; ++h) ss += red[((h * MW + wm) * MF + m) * 16 + k16];
         const float inv = rms_scale(ss * inv_c, a.eps);
 #pragma unroll
         for (int f = 0; f < NFW; ++f) {
@@ -567,16 +570,17 @@ __global__ __launch_bounds__(256 * WN, 1) void conv3_v2_kernel(ConvArgs a)
     if (live) process(w);
 }
 
-template <int UP, int NF, int WN, int RH, int DOWN = 1, int TF = 0>
+template <int UP, int NF, int WN, int RH, int DOWN = 1, int TF = 0, int MW = 4>
 hipError_t launch_v2(const ConvArgs& a, hipStream_t s)
 {
-    using G = Geo<UP, RH>;
+    using G = Geo<UP, RH, MW>;
     const int th = DOWN == 2 ? a.h_out : a.h_in, tw = DOWN == 2 ? a.w_out : a.w_in;
     const int tiles = ((th + G::TS_H - 1) / G::TS_H) * ((tw + G::TS_W - 1) / G::TS_W);
     const int64_t total = (int64_t)tiles * a.t_out * a.nblocks;
     if (total <= 0 || total > (int64_t)0x7fffffff - 8) return hipErrorInvalidValue;
     const int64_t grid = ((total + 7) / 8) * 8;
-    hipLaunchKernelGGL((conv3_v2_kernel<UP, NF, WN, RH, DOWN, TF>), dim3((unsigned)grid), dim3(256 * WN), 0, s, a);
+    hipLaunchKernelGGL((conv3_v2_kernel<UP, NF, WN, RH, DOWN, TF, MW>), dim3((unsigned)grid), dim3(64 * MW * WN), 0,
+                       s, a);
     return hipGetLastError();
 }
 
@@ -589,6 +593,17 @@ bool v2_conv_applies(int ntile, int kh, int kw, int up_s)
 
 hipError_t launch_conv_bf16_v2(const ConvArgs& a, hipStream_t s)
 {
+    if (a.family == 7) {
+        // spatial stride 2 in 192-channel blocks: 4 output rows x 32 columns per
+        // tile (9 x 66 input pixels in LDS, double-buffered, beside two weight
+        // buffers), two waves along M and four along N, each wave 4 rows x 16
+        // columns x 48 channels: 18 fragment reads per 36 MFMAs per sub-step
+        // against 14 per 18 for the 2-row tile
+        if (a.ntile != 192 || a.kh != 3 || a.kw != 3 || a.down_s != 2 || a.up_s != 1 || a.t_stride < 1 ||
+            a.t_stride > 2)
+            return hipErrorInvalidValue;
+        return launch_v2<1, 12, 4, 4, 2, 0, 2>(a, s);
+    }
     if (!v2_conv_applies(a.ntile, a.kh, a.kw, a.up_s)) return hipErrorInvalidValue;
     if (a.down_s == 2) {
         // spatial stride 2: 2 output rows x 64 columns per tile (5 x 130 input

@@ -1300,6 +1300,14 @@ STRIDED_CASES = [
     (8, 96, (3, 3, 3), 2, 1, 19, 133, [1, 1, 2], C.TPAD_REPLICATE, False, True, True, True),
     (8, 128, (2, 3, 3), 2, 2, 9, 70, [3, 2], C.TPAD_ZERO, False, False, False, False),
     (8, 256, (3, 3, 3), 2, 2, 8, 64, [2, 2], C.TPAD_ZERO, True, True, False, False),
+    # output channels a multiple of 192: the strided tile in 192-channel blocks
+    # (4 output rows x 32 columns): ragged row and column tiles, tiles covered
+    # exactly, two blocks, act fused over one block, k_t 2, one-pixel frames
+    (96, 192, (3, 3, 3), 2, 2, 19, 75, [3, 2], C.TPAD_REPLICATE, False, True, True, True),
+    (64, 192, (3, 3, 3), 2, 1, 16, 128, [1, 2], C.TPAD_ZERO, True, True, False, True),
+    (192, 384, (3, 3, 3), 2, 2, 17, 66, [2, 2], C.TPAD_ZERO, True, True, True, False),
+    (32, 192, (2, 3, 3), 2, 2, 9, 33, [1, 2, 2], C.TPAD_REPLICATE, False, False, False, False),
+    (128, 384, (3, 3, 3), 2, 1, 1, 1, [2, 1], C.TPAD_REPLICATE, False, True, False, True),
 ]
 
 
@@ -1378,10 +1386,12 @@ def test_bf16_strided_conv_vs_oracle(case):
     pr = C.OpProfile()
     C.check(C.lib().cc3d_profile_read(plan._h, 0, 0, ctypes.byref(pr)), "profile_read")
     # 3x3 spatial stride 2 in 96/128-channel blocks: the register-blocked kernel
-    # (with 8 input channels, its temporal taps folded into one K step)
+    # (with 8 input channels, its temporal taps folded into one K step; with
+    # output channels a multiple of 192, in 192-channel blocks)
     v2 = ss == 2 and k[1:] == (3, 3) and _ntile(cout) in (96, 128)
     fam = ("_v2tf" if cin == 8 else "_v2") if v2 else ""
-    assert pr.kernel.decode().startswith("conv_bf16%s_s%dt%d_k%d" % (fam, ss, st, k[1])), pr.kernel
+    nt = 192 if v2 and cin != 8 and cout % 192 == 0 else _ntile(cout)
+    assert pr.kernel.decode() == "conv_bf16%s_s%dt%d_k%d_n%d" % (fam, ss, st, k[1], nt), pr.kernel
     assert got.shape == (cout, t_out, ho, wo)
     assert_bf16_close(got, ref, "strided conv")
 
