@@ -101,12 +101,14 @@ def test_noalloc_refuses_a_conv_beyond_the_scratch():
     assert bool((y == 3.0).all()) and b.frames_seen == 0
 
 
-def test_noalloc_strided_matches_the_plan_path():
+@pytest.mark.parametrize("cin,cout", [(64, 96), (96, 192)])
+def test_noalloc_strided_matches_the_plan_path(cin, cout):
     """A strided conv (spatial and temporal stride 2, the register-blocked
-    kernel's strided tile, fused act) through the no-alloc entry point: a 3-frame
-    first chunk then a 2-frame one (smaller), bit for bit the plan path's."""
-    say("no-alloc: strided conv")
-    cin, cout, h, w, chunks = 64, 96, 14, 70, (3, 2)
+    kernel's strided tile in 96- and 192-channel blocks, fused act) through the
+    no-alloc entry point: a 3-frame first chunk then a 2-frame one (smaller),
+    bit for bit the plan path's."""
+    say("no-alloc: strided conv %d -> %d" % (cin, cout))
+    h, w, chunks = 14, 70, (3, 2)
     wt, gamma, bias, x, _ = _inputs(cin, cout, h, w, sum(chunks), True, False, 1, 70)
     plan = P.conv_plan(wt, h, w, bias=bias, gamma=gamma, max_chunk_t=3, act=True, stride_s=2, stride_t=2)
     st = P.Stream(plan)
@@ -124,6 +126,6 @@ def test_noalloc_strided_matches_the_plan_path():
         got.append(y)
         t0 += n
     torch.cuda.synchronize()
-    assert got[0].shape == (2, 7, 35, 96) and got[1].shape == (1, 7, 35, 96)
+    assert got[0].shape == (2, 7, 35, cout) and got[1].shape == (1, 7, 35, cout)
     for k in range(2):
         assert torch.equal(got[k], refs[k]), "chunk %d differs from the plan path" % k
