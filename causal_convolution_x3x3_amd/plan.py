@@ -35,6 +35,15 @@ def _ptr(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _check_arena(s: "State", nbytes: int, what: str):
+    """A state's arena must hold the plan's cc3d_state_bytes: the library writes
+    the caches through the bare pointer."""
+    a = s.arena
+    if a.dtype != torch.uint8 or a.dim() != 1 or a.numel() < nbytes or not a.is_contiguous():
+        raise ValueError("%s must be a contiguous byte arena of at least %d bytes, got %s of %s"
+                         % (what, nbytes, tuple(a.shape), a.dtype))
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -142,6 +151,7 @@ class Plan:
         return out
 
     def reset(self, state: State, stream=None):
+        _check_arena(state, self.state_bytes, "state")
         cs = state._c()
         C.check(C.lib().cc3d_reset(self._h, ctypes.byref(cs), _stream(stream)), "cc3d_reset")
         state.frames_seen = cs.frames_seen
@@ -156,6 +166,8 @@ class Plan:
         if x.dim() != 4 or tuple(x.shape[1:]) != self.in_shape or x.dtype != _TD[self.dtype]:
             raise ValueError("x must be [T][%d][%d][%d] of %s, got %s of %s"
                              % (self.in_shape + (_TD[self.dtype], tuple(x.shape), x.dtype)))
+        _check_arena(cache_in, self.state_bytes, "cache_in")
+        _check_arena(cache_out, self.state_bytes, "cache_out")
         t_chunk = x.shape[0]
         first = cache_in.frames_seen == 0
         shape = self.output_shape(t_chunk, first)
@@ -206,6 +218,12 @@ def conv_plan(w: torch.Tensor, h_in: int, w_in: int, *, bias=None, gamma=None, u
     return Plan(h, d.dtype, w.device, cin, h_in, w_in)
 
 
+def conv_state_bytes(kt: int, h_in: int, w_in: int, cin: int, elem_bytes: int) -> int:
+    """State bytes of one conv: its cache of kt - 1 input frames, in 256-byte
+    units (what cc3d_state_bytes reports for a plan of that conv)."""
+    return max(256, -(-(kt - 1) * h_in * w_in * cin * elem_bytes // 256) * 256)
+
+
 def conv_forward_noalloc(w: torch.Tensor, x: torch.Tensor, cache_in: State, cache_out: State, y: torch.Tensor,
                          *, bias=None, gamma=None, residual=None, up_s=1, up_t=1, max_chunk_t=8,
                          tpad=C.TPAD_REPLICATE, act=False, out_u8=False, eps=1e-6, aligned=False,
@@ -243,6 +261,9 @@ def conv_forward_noalloc(w: torch.Tensor, x: torch.Tensor, cache_in: State, cach
     if residual is not None and (tuple(residual.shape) != want or residual.dtype != w.dtype):
         raise ValueError("residual must be %s of %s, got %s of %s" % (want, w.dtype, tuple(residual.shape),
                                                                        residual.dtype))
+    need = conv_state_bytes(kt, x.shape[1], x.shape[2], cin, w.element_size())
+    _check_arena(cache_in, need, "cache_in")
+    _check_arena(cache_out, need, "cache_out")
     ci, co = cache_in._c(), cache_out._c()
     with torch.cuda.device(x.device):
         C.check(C.lib().cc3d_conv_forward_noalloc(ctypes.byref(d), _ptr(w), _ptr(bias), _ptr(gamma), _ptr(x), t,

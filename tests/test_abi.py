@@ -295,6 +295,43 @@ def test_binding_refuses_misshaped_input_before_any_library_call(monkeypatch):
         with pytest.raises(ValueError, match="x must be"):
             plan.forward_chunk(bad, st_in, st_out)
     assert st_out.frames_seen == 0
+    # state arenas smaller than the plan's state bytes (the caches are written
+    # through the bare pointer)
+    plan.state_bytes = 1024
+    good = torch.zeros(2, 8, 6, 16, dtype=torch.bfloat16)
+    st_in.arena, st_out.arena = torch.zeros(1024, dtype=torch.uint8), torch.zeros(512, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="cache_out must be"):
+        plan.forward_chunk(good, st_in, st_out)
+    with pytest.raises(ValueError, match="state must be"):
+        plan.reset(st_out)
+    st_out.arena = torch.zeros(256, dtype=torch.int32)  # 1024 bytes, but not a byte arena
+    with pytest.raises(ValueError, match="cache_out must be"):
+        plan.forward_chunk(good, st_in, st_out)
+
+
+def test_noalloc_binding_refuses_small_state_before_any_library_call(monkeypatch):
+    """conv_forward_noalloc sizes the conv's state (its cache of kt - 1 input
+    frames, in 256-byte units) and refuses smaller arenas before calling in."""
+    import torch
+
+    from causal_convolution_x3x3_amd import plan as P
+
+    def no_call():
+        raise AssertionError("the library was called")
+
+    monkeypatch.setattr(P.C, "lib", no_call)
+    w = torch.zeros(16, 8, 3, 3, 3, dtype=torch.bfloat16)
+    x = torch.zeros(2, 10, 12, 8, dtype=torch.bfloat16)
+    y = torch.zeros(2, 10, 12, 16, dtype=torch.bfloat16)
+    need = 2 * 10 * 12 * 8 * 2  # 3840 bytes -> 3840 (a multiple of 256)
+    st_in, st_out = object.__new__(P.State), object.__new__(P.State)
+    st_in.frames_seen = st_out.frames_seen = 0
+    st_in.arena, st_out.arena = torch.zeros(need, dtype=torch.uint8), torch.zeros(need - 256, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="cache_out must be"):
+        P.conv_forward_noalloc(w, x, st_in, st_out, y)
+    st_in.arena = torch.zeros(need - 1, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="cache_in must be"):
+        P.conv_forward_noalloc(w, x, st_in, st_out, y)
 
 
 def test_noalloc_entry_rejects_bad_arguments_before_device_work():

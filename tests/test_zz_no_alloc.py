@@ -45,6 +45,8 @@ def test_noalloc_matches_the_plan_path():
         wt, gamma, bias, x, r = _inputs(cin, cout, h, w, sum(chunks), act, res, up_s, 10 * ci)
         plan = P.conv_plan(wt, h, w, bias=bias, gamma=gamma, up_s=up_s, max_chunk_t=max(chunks), act=act,
                            residual=res)
+        # the binding's size check of the states uses the library's own figure
+        assert P.conv_state_bytes(3, h, w, cin, 2) == plan.state_bytes
         runs.append((plan, wt, gamma, bias, x, r, chunks, act, up_s))
     # the plan path: every case's chunks
     refs = []
@@ -111,6 +113,7 @@ def test_noalloc_strided_matches_the_plan_path(cin, cout):
     h, w, chunks = 14, 70, (3, 2)
     wt, gamma, bias, x, _ = _inputs(cin, cout, h, w, sum(chunks), True, False, 1, 70)
     plan = P.conv_plan(wt, h, w, bias=bias, gamma=gamma, max_chunk_t=3, act=True, stride_s=2, stride_t=2)
+    assert P.conv_state_bytes(3, h, w, cin, 2) == plan.state_bytes
     st = P.Stream(plan)
     refs, t0 = [], 0
     for n in chunks:
