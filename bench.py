@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4|c4tg|c3|c2|c1|e4]
                     [--tg-order before|after] [--frame-batch B] [--fold-upsample] [--videos N]
-                    [--no-cpu-baseline] [--no-delivery]
+                    [--no-cpu-baseline] [--no-delivery] [--per-op FILE]
 
 Workloads (synthetic, seeded; the pages' test videos and trained weights are not
 available):
@@ -38,6 +38,11 @@ Inputs are resident in HBM before timing; outputs go to a device ring.
       their 24 or 16 frames) decoded 1 + N times, the first untimed; the seconds
       per video (min / mean / p99 over the N timed ones) go in `video`, the
       protocol of the Synthesia digest ("Summary": 1 warmup + 10 runs).
+
+--per-op FILE: one JSON line per launch kind of every op over the timed steps
+      (op name; part: main = the op's own kernel, norm = a conv's separate norm
+      pass, cache = its cache copy; kernel, launches, ms per launch, algorithmic
+      TFLOP/s and GB/s) from the library's event profile.
 
 Prints one JSON line: value = algorithmic conv TFLOP/s (2*Cin*Cout*27 FLOP per
 output voxel of every conv) over the timed steps; plus output frames/s, the
@@ -643,6 +648,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-delivery", action="store_true",
                     help="skip the host-delivery measurement (c4: output copied to pinned host memory)")
+    ap.add_argument("--per-op", metavar="FILE", default=None,
+                    help="write the timed steps' per-op event profile to FILE (one JSON line per op and part)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this decode path has no multi-GPU mode; "
@@ -683,18 +690,29 @@ def main():
     # per-kernel event totals over the timed region
     import ctypes
     kern = {}
+    per_op = []
     for op in range(C.lib().cc3d_plan_num_ops(plan._h)):
         for part in range(3):
             pr = C.OpProfile()
             C.check(C.lib().cc3d_profile_read(plan._h, op, part, ctypes.byref(pr)), "profile_read")
             if pr.launches == 0:
                 continue
+            ms = pr.total_ms / pr.launches
+            per_op.append({"op": op, "name": plan.op_names[op] if op < len(plan.op_names) else "op%d" % op,
+                           "part": ("main", "norm", "cache")[part], "kernel": pr.kernel.decode(),
+                           "launches": pr.launches, "ms_per_launch": round(ms, 4),
+                           "tflops": round(pr.flops / pr.launches / (ms * 1e-3) / 1e12, 1),
+                           "gbs": round(pr.bytes / pr.launches / (ms * 1e-3) / 1e9, 1)})
             k = kern.setdefault(pr.kernel.decode(), {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
             k["launches"] += pr.launches
             k["ms"] += pr.total_ms
             k["flops"] += pr.flops
             k["bytes"] += pr.bytes
     C.check(C.lib().cc3d_profile_enable(plan._h, 0), "profile_enable")
+    if args.per_op:
+        with open(args.per_op, "w") as f:
+            for row in per_op:
+                f.write(json.dumps(row) + "\n")
     # MFMA work a kernel executes: the definition's count, except for the
     # phase-folded upsample convs, which execute fewer MFMAs -- all of the
     # timed steps' difference between algorithmic and executed FLOP is theirs

@@ -102,8 +102,9 @@ class Plan:
     ``cin``, ``h``, ``w``: the chunk input's channels and frame size; x is
     [T][h][w][cin] of the plan dtype."""
 
-    def __init__(self, handle: ctypes.c_void_p, dtype: int, device, cin: int, h: int, w: int):
+    def __init__(self, handle: ctypes.c_void_p, dtype: int, device, cin: int, h: int, w: int, op_names=None):
         self._h = handle
+        self.op_names = list(op_names or [])  # per op of the library's list (profiles name them)
         self.dtype = dtype
         self.device = device
         self.in_shape = (int(h), int(w), int(cin))
@@ -215,7 +216,7 @@ def conv_plan(w: torch.Tensor, h_in: int, w_in: int, *, bias=None, gamma=None, u
     with torch.cuda.device(w.device):
         C.check(C.lib().cc3d_plan_create(ctypes.byref(d), _ptr(w), _ptr(bias), _ptr(gamma), _stream(stream),
                                          ctypes.byref(h)), "cc3d_plan_create")
-    return Plan(h, d.dtype, w.device, cin, h_in, w_in)
+    return Plan(h, d.dtype, w.device, cin, h_in, w_in, ["conv"])
 
 
 def conv_state_bytes(kt: int, h_in: int, w_in: int, cin: int, elem_bytes: int) -> int:
@@ -328,7 +329,7 @@ def stack_plan(ops: List[Op], cin: int, h: int, w: int, *, dtype=torch.bfloat16,
     with torch.cuda.device(device):
         C.check(C.lib().cc3d_stack_plan_create(ctypes.byref(d), _stream(stream), ctypes.byref(hnd)),
                 "cc3d_stack_plan_create")
-    return Plan(hnd, d.dtype, device, cin, h, w)
+    return Plan(hnd, d.dtype, device, cin, h, w, [o.name or "op%d" % i for i, o in enumerate(ops)])
 
 
 class Stream:
