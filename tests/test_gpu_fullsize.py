@@ -509,3 +509,38 @@ def test_e4_encoder_fullsize_sampled():
         t0 += n
     torch.cuda.synchronize()
     assert torch.equal(torch.cat(outs), got), "production slot wiring differs from the unique-slot wiring"
+
+
+def test_e4_encoder_whole_video_sampled():
+    """The whole 361-frame video through the encoder at full size in the
+    benchmark's chunks (25, then 14 of 24 frames -> 91 latents), every cache
+    and temporal-stride phase carried through 15 chunks; every op of the last
+    chunk checked on sampled outputs against the oracle fed its own GPU input."""
+    say("full size e4, whole video")
+    h, w, c_pix, c_in = 1440, 2560, 3, 8
+    dev, cpu = {}, {}
+    for i, (name, co, ci, kt, kh, kw, has_g, _, _) in enumerate(OM.encoder_layer_shapes(c_in=c_pix)):
+        d, c = _param_pair(co, ci, 6, i, has_g)
+        if name == "conv_in":
+            wp = torch.zeros((co, c_in, kt, kh, kw), dtype=d["w"].dtype, device=d["w"].device)
+            wp[:, :c_pix] = d["w"]
+            d["w"] = wp
+        dev[name], cpu[name] = d, c
+    ops = S.encoder_ops(dev, unique_slots=True)
+    for o in ops:
+        o.tpad = C.TPAD_ZERO
+    _gains_of_acts(ops, cpu)
+    splits = [25] + [24] * 14
+    assert sum(splits) == 361
+
+    def chunk_of(k, n):  # chunk k of the pixels, padded with zero channels to 8
+        x = synth.bf16(synth.video(c_pix, n, h, w, synth.seed(6, 100 + k)))
+        xc = torch.zeros((n, h, w, c_in), dtype=torch.bfloat16, device="cuda")
+        xc[..., :c_pix] = x.permute(1, 2, 3, 0).cuda()
+        return xc
+
+    got, worst = run_stack_sampled(ops, cpu, None, c_in, h, w, splits, seed=616, max_pts_rows=6,
+                                   chunk_of=chunk_of, check_from=len(splits) - 1)
+    assert got.shape == (6, 90, 160, 48)  # the last chunk's 6 latents (91 = 7 + 14 x 6)
+    # every strided conv was checked (the last down conv stores only its act)
+    assert all(k in worst for k in ("conv_in.out", "e0.down.out", "e1.down.out", "e2.down.act", "conv_out.out"))
