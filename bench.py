@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4|c4tg|c3|c2|c1|e4]
                     [--tg-order before|after] [--frame-batch B] [--fold-upsample] [--videos N]
-                    [--no-cpu-baseline] [--no-delivery] [--per-op FILE]
+                    [--no-cpu-baseline] [--no-delivery] [--per-op FILE] [--band N]
 
 Workloads (synthetic, seeded; the pages' test videos and trained weights are not
 available):
@@ -39,6 +39,9 @@ Inputs are resident in HBM before timing; outputs go to a device ring.
       per video (min / mean / p99 over the N timed ones) go in `video`, the
       protocol of the Synthesia digest ("Summary": 1 warmup + 10 runs).
 
+--band N (c3): one GPU's share when the frame is split into N bands of rows (the
+      design's multi-GPU split): 720/N low-resolution rows plus a halo row on each
+      side, timed alone.
 --per-op FILE: one JSON line per launch kind of every op over the timed steps
       (op name; part: main = the op's own kernel, norm = a conv's separate norm
       pass, cache = its cache copy; kernel, launches, ms per launch, algorithmic
@@ -222,8 +225,13 @@ def setup_c4(dev, torch, synth, P, S, out_u8=False, temporal_grow=None, frame_ba
     return plan, work, ring, desc
 
 
-def setup_c3(dev, torch, synth, P, S, fold=False):
+def setup_c3(dev, torch, synth, P, S, fold=False, band=1):
+    """band > 1: one GPU's share when the frame is split into `band` bands of
+    rows: 720/band low-resolution rows plus one halo row on each side, so that
+    both convs' outputs over the band's own 2*720/band rows are exact."""
     cin, cmid, cout, h, w = 128, 96, 3, 720, 1280
+    if band > 1:
+        h = 720 // band + 2
     w1 = synth.bf16(synth.conv_weight(cmid, cin, 3, 3, 3, synth.seed(3, 10))).to(dev)
     w2 = synth.bf16(synth.conv_weight(cout, cmid, 3, 3, 3, synth.seed(3, 13))).to(dev)
     g2 = synth.gain(cmid, synth.seed(3, 14)).to(dev)
@@ -234,16 +242,20 @@ def setup_c3(dev, torch, synth, P, S, fold=False):
         x = synth.bf16(synth.video(cin, 4, h, w, synth.seed(3, 100 + k)))
         pool.append(x.permute(1, 2, 3, 0).contiguous().to(dev))
     sched = [1] + [4] * 90
-    fl_up = conv_flops_per_voxel(cin, cmid) * 1440 * 2560
-    fl_frame = fl_up + conv_flops_per_voxel(cmid, cout) * 1440 * 2560
+    fl_up = conv_flops_per_voxel(cin, cmid) * (2 * h) * 2560
+    fl_frame = fl_up + conv_flops_per_voxel(cmid, cout) * (2 * h) * 2560
     ex_frame = fl_frame - (2.0 / 9.0) * fl_up if fold else fl_frame
     work = []
     for i, n in enumerate(sched):
         work.append((pool[i % 8][:n], i == 0, fl_frame * n, n, ex_frame * n))
-    ring = [torch.empty((4, 1440, 2560, 3), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    ring = [torch.empty((4, 2 * h, 2 * w, 3), dtype=torch.bfloat16, device=dev) for _ in range(2)]
     desc = {"workload": "c3_stage1440_bf16: 128x720x1280 -> nearest 2x -> conv 128->96 -> RMSNorm+SiLU -> "
                         "conv 96->3 at 1440x2560; 361 frames as 1+90x4 chunks with caches",
             "output": "3x361x1440x2560 bf16", "step": "one 4-frame chunk"}
+    if band > 1:
+        desc["band"] = {"of": band, "input_rows": h, "computed_rows": 2 * h, "own_rows": 2 * (h - 2),
+                        "note": "one GPU's share of a frame split by rows (frames_per_s counts band frames; "
+                                "the algorithmic FLOP are those of the computed rows)"}
     if fold:
         desc["fold_upsample"] = "the upsampling conv phase-folded (hi/lo bf16 weights, 7/9 of its MFMA work)"
     return plan, work, ring, desc
@@ -648,6 +660,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-delivery", action="store_true",
                     help="skip the host-delivery measurement (c4: output copied to pinned host memory)")
+    ap.add_argument("--band", type=int, default=1,
+                    help="c3: one GPU's share of the frame split into this many bands of rows (halo included)")
     ap.add_argument("--per-op", metavar="FILE", default=None,
                     help="write the timed steps' per-op event profile to FILE (one JSON line per op and part)")
     args = ap.parse_args()
@@ -667,8 +681,11 @@ def main():
     torch.cuda.set_device(dev)
     C.lib()
     tg = args.tg_order if args.workload == "c4tg" else None
+    if args.band != 1 and (args.workload != "c3" or args.band < 1 or 720 % args.band):
+        print("--band applies to --workload c3 and must divide 720", file=sys.stderr)
+        sys.exit(2)
     if args.workload == "c3":
-        plan, work, ring, desc = setup_c3(dev, torch, synth, P, S, fold=args.fold_upsample)
+        plan, work, ring, desc = setup_c3(dev, torch, synth, P, S, fold=args.fold_upsample, band=args.band)
     elif args.workload == "c2":
         plan, work, ring, desc = setup_c2(dev, torch, synth, P, S)
     elif args.workload == "c1":
@@ -731,7 +748,8 @@ def main():
         achieved = dom["bytes"] / dom["launches"] / (avg_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    wl_key = args.workload + ("_" + tg if tg else "")
+    # counter records are per workload shape (none for a band)
+    wl_key = args.workload + ("_" + tg if tg else "") + ("_band%d" % args.band if args.band > 1 else "")
     clock = recorded_clock(dom_name, wl_key)
     if clock and roof["bound"] == "mfma":
         # the part runs below its 2.4 GHz peak clock under this load (power): the
