@@ -669,6 +669,9 @@ def main():
         print("bench.py measures one GPU only: this decode path has no multi-GPU mode; "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.band != 1 and (args.workload != "c3" or args.band < 1 or 720 % args.band):
+        print("--band applies to --workload c3 and must divide 720", file=sys.stderr)
+        sys.exit(2)
 
     import torch
 
@@ -681,9 +684,6 @@ def main():
     torch.cuda.set_device(dev)
     C.lib()
     tg = args.tg_order if args.workload == "c4tg" else None
-    if args.band != 1 and (args.workload != "c3" or args.band < 1 or 720 % args.band):
-        print("--band applies to --workload c3 and must divide 720", file=sys.stderr)
-        sys.exit(2)
     if args.workload == "c3":
         plan, work, ring, desc = setup_c3(dev, torch, synth, P, S, fold=args.fold_upsample, band=args.band)
     elif args.workload == "c2":

@@ -141,6 +141,16 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr and r.stdout == ""
 
 
+@pytest.mark.parametrize("args", [["--band", "8"], ["--workload", "c3", "--band", "7"],
+                                  ["--workload", "c3", "--band", "0"]])
+def test_band_is_refused_off_the_1440p_stage_or_off_its_rows(args):
+    """--band splits the 1440p stage's 720 low-resolution rows: other workloads
+    and counts that do not divide 720 are refused before any GPU work."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + args, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2 and "--band" in r.stderr and r.stdout == ""
+
+
 def test_video_steps_cover_each_workload():
     """A whole video is the steps each workload's schedule gives: c4 the 15 clips,
     c3 its 1 + 90 chunks, c2 and c1 their 24 and 16 frames in 4-frame chunks."""
